@@ -1,0 +1,165 @@
+"""CPU oracle for the N:M bitmask decode path -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the benchmark's ``cpu_baseline``
+leg may import this package.  The product library (``bitmask_spmv_amd``) never
+imports it, and it never imports the product library: the two share no code.
+
+The arithmetic lives in ``nm_oracle.c`` (plain C, IEEE fp64, built with
+``-ffp-contract=off``); this module only marshals numpy arrays to it.  The function
+list and the passages each follows:
+
+* ``col_norm``   -- Wanda activation norm n_j = sqrt(sum_t X[t][j]^2)
+                    ("SparseDecoding：只用解码激活校准的稀疏推理", 核心公式)
+* ``prune_pack`` -- score |W_ij| * n_j, keep the top N of every M columns (ties to
+                    the lower column), one uint32 mask word per 32 columns (bit b <->
+                    column 32w+b), kept values in increasing column order
+                    ("SparseDecoding: Decoding-Aware Pruning ...", Methodology Steps 2-3;
+                    "SparseDecoding:解码感知的准确高效大模型剪枝框架", 前置知识 N:M, 方法步骤详情 第三步)
+* ``unpack``     -- inverse of the packing: dense pruned matrix, zeros elsewhere
+* ``spmv``       -- fp64 matvec of the unpacked pruned matrix (+ sum of |products|)
+* ``dense``      -- fp64 matvec of the dense matrix (+ sum of |products|)
+
+Pins (tests that tie the oracle to something other than itself) live in
+``tests/test_oracle_pins.py``; every function above has at least one.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "nm_oracle.c")
+_LIB = os.path.join(_HERE, "libnmoracle.so")
+
+_lib = None
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+_ERRS = {1: "bad argument", 2: "non-finite input", 3: "mask word without exactly 16 set bits",
+         4: "out of memory"}
+
+
+def build(force: bool = True) -> str:
+    """Compile nm_oracle.c into a host-only shared library next to it."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + f".tmp{os.getpid()}"
+        cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+               "-pthread", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB):
+        build(force=True)
+    lib = ctypes.CDLL(_LIB)
+    i64, p = ctypes.c_int64, ctypes.c_void_p
+    lib.nmo_col_norm.argtypes = [p, i64, i64, i64, p]
+    lib.nmo_prune_pack.argtypes = [p, i64, i64, i64, p, ctypes.c_int, ctypes.c_int, p, p]
+    lib.nmo_unpack.argtypes = [p, p, i64, i64, p]
+    lib.nmo_spmv.argtypes = [p, p, i64, i64, p, i64, ctypes.c_int, p, p, ctypes.c_int]
+    lib.nmo_dense.argtypes = [p, i64, i64, i64, p, i64, ctypes.c_int, p, p, ctypes.c_int]
+    for f in (lib.nmo_col_norm, lib.nmo_prune_pack, lib.nmo_unpack, lib.nmo_spmv, lib.nmo_dense):
+        f.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise OracleError(f"{what}: {_ERRS.get(rc, rc)}")
+
+
+def _u16(a) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.uint16:
+        raise TypeError("expected raw bfloat16 patterns as uint16")
+    return a
+
+
+def col_norm(X) -> np.ndarray:
+    """X: uint16 bf16 patterns [T, K] -> float32 [K]."""
+    X = _u16(X)
+    T, K = X.shape
+    n = np.empty(K, dtype=np.float32)
+    _check(_load().nmo_col_norm(_ptr(X), T, K, K, _ptr(n)), "col_norm")
+    return n
+
+
+def prune_pack(W, n, N: int, M: int):
+    """W: uint16 [R, K]; n: float32 [K] -> (masks uint32 [R, K/32], values uint16 [R, K/2])."""
+    W = _u16(W)
+    n = np.ascontiguousarray(n, dtype=np.float32)
+    R, K = W.shape
+    if n.shape != (K,):
+        raise ValueError("col_norm length must equal K")
+    if K % 32:
+        raise OracleError("prune_pack: bad argument")
+    masks = np.empty((R, K // 32), dtype=np.uint32)
+    values = np.empty((R, K // 2), dtype=np.uint16)
+    _check(_load().nmo_prune_pack(_ptr(W), K, R, K, _ptr(n), int(N), int(M), _ptr(masks), _ptr(values)),
+           "prune_pack")
+    return masks, values
+
+
+def unpack(masks, values, K: int) -> np.ndarray:
+    masks = np.ascontiguousarray(masks, dtype=np.uint32)
+    values = _u16(values)
+    R = masks.shape[0]
+    out = np.empty((R, K), dtype=np.uint16)
+    _check(_load().nmo_unpack(_ptr(masks), _ptr(values), R, K, _ptr(out)), "unpack")
+    return out
+
+
+def spmv(masks, values, x, K: int, nthreads: int = 1):
+    """-> (y fp64 [B, R], absum fp64 [B, R]) for the packed pruned matrix."""
+    masks = np.ascontiguousarray(masks, dtype=np.uint32)
+    values = _u16(values)
+    x = _u16(x)
+    if x.ndim == 1:
+        x = x[None, :]
+    R = masks.shape[0]
+    B = x.shape[0]
+    if x.shape[1] != K or masks.shape != (R, K // 32) or values.shape != (R, K // 2):
+        raise ValueError("shape mismatch")
+    y = np.empty((B, R), dtype=np.float64)
+    a = np.empty((B, R), dtype=np.float64)
+    _check(_load().nmo_spmv(_ptr(masks), _ptr(values), R, K, _ptr(x), K, B, _ptr(y), _ptr(a), int(nthreads)),
+           "spmv")
+    return y, a
+
+
+def dense(W, x, nthreads: int = 1):
+    """-> (y fp64 [B, R], absum fp64 [B, R]) for the dense matrix."""
+    W = _u16(W)
+    x = _u16(x)
+    if x.ndim == 1:
+        x = x[None, :]
+    R, K = W.shape
+    B = x.shape[0]
+    if x.shape[1] != K:
+        raise ValueError("shape mismatch")
+    y = np.empty((B, R), dtype=np.float64)
+    a = np.empty((B, R), dtype=np.float64)
+    _check(_load().nmo_dense(_ptr(W), K, R, K, _ptr(x), K, B, _ptr(y), _ptr(a), int(nthreads)), "dense")
+    return y, a
+
+
+def within_tolerance(y_test, y_ref, absum, rel: float = 1e-2, abs_frac: float = 1e-3) -> np.ndarray:
+    """Element-wise acceptance |y - y_ref| <= rel*|y_ref| + abs_frac*sum_j|W_ij x_j|."""
+    y_test = np.asarray(y_test, dtype=np.float64)
+    return np.abs(y_test - y_ref) <= rel * np.abs(y_ref) + abs_frac * absum
