@@ -1,0 +1,208 @@
+"""bitmask_spmv_amd -- N:M bitmask sparse decode kernels for AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``include/nm_spmv.h`` (``libnmspmv.so``, built
+in-tree by ``bitmask_spmv_amd._build``).  Every function has the C entry point's name
+and only marshals arguments: it checks dtypes, devices, shapes and strides of torch
+tensors, passes their device pointers and the current HIP stream, and turns a
+non-zero status into :class:`NmError`.  All arithmetic runs in the HIP kernels; there
+is no CPU fallback, and importing this package fails loudly when the library has not
+been built.
+
+PyTorch is used only for device memory and streams.  ``masks`` are carried in int32
+tensors that hold the raw uint32 mask words; bf16 tensors are passed as raw patterns.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "NmError", "LIB_PATH", "lib", "nm_version", "nm_col_norm", "nm_prune_pack", "nm_spmv",
+    "nm_spmv_workspace_bytes", "dense_gemv", "dense_gemv_workspace_bytes", "nm_unpack",
+    "NM_PATTERNS",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnmspmv.so")
+NM_PATTERNS = ((2, 4), (4, 8), (8, 16), (16, 32))
+
+_STATUS = {0: "NM_OK", 1: "NM_ERR_NULL", 2: "NM_ERR_SHAPE", 3: "NM_ERR_PATTERN", 4: "NM_ERR_ALIGN",
+           5: "NM_ERR_WORKSPACE", 6: "NM_ERR_HIP"}
+
+
+class NmError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__(f"{_STATUS.get(status, status)}: {detail}")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
+            "(or python bitmask_spmv_amd/_build.py); there is no fallback path")
+    L = ctypes.CDLL(LIB_PATH)
+    i64, p, i32, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    L.nm_status_str.argtypes, L.nm_status_str.restype = [i32], ctypes.c_char_p
+    L.nm_last_error.argtypes, L.nm_last_error.restype = [], ctypes.c_char_p
+    L.nm_version.argtypes, L.nm_version.restype = [], i32
+    L.nm_col_norm.argtypes = [p, i64, i64, i64, p, p]
+    L.nm_prune_pack.argtypes = [p, i64, i64, i64, p, i32, i32, p, p, p]
+    L.nm_spmv_workspace_bytes.argtypes, L.nm_spmv_workspace_bytes.restype = [i64, i64, i32], sz
+    L.nm_spmv.argtypes = [p, p, i64, i64, p, i64, i32, p, i64, p, sz, p]
+    L.dense_gemv_workspace_bytes.argtypes, L.dense_gemv_workspace_bytes.restype = [i64, i64, i32], sz
+    L.dense_gemv.argtypes = [p, i64, i64, i64, p, i64, i32, p, i64, p, sz, p]
+    L.nm_unpack.argtypes = [p, p, i64, i64, p, i64, p]
+    for f in (L.nm_col_norm, L.nm_prune_pack, L.nm_spmv, L.dense_gemv, L.nm_unpack):
+        f.restype = i32
+    return L
+
+
+lib = _load()
+
+
+def _check(status: int):
+    if status != 0:
+        raise NmError(status, lib.nm_last_error().decode(errors="replace"))
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live on a HIP device (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must be {ndim}-D (got shape {tuple(t.shape)})")
+    if t.stride(-1) != 1:
+        raise ValueError(f"{name} must be contiguous in its last dimension")
+
+
+def _ld(t: torch.Tensor) -> int:
+    return t.stride(0) if t.dim() == 2 and t.shape[0] > 1 else t.shape[-1]
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def nm_version() -> int:
+    return int(lib.nm_version())
+
+
+def nm_col_norm(X: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """X: bf16 [T, K] calibration activations -> fp32 [K] column norms."""
+    _dev(X, "X", torch.bfloat16, 2)
+    T, K = X.shape
+    if out is None:
+        out = torch.empty(K, dtype=torch.float32, device=X.device)
+    _dev(out, "out", torch.float32, 1)
+    _check(lib.nm_col_norm(_ptr(X), T, K, _ld(X), _ptr(out), _stream(X)))
+    return out
+
+
+def nm_prune_pack(W: torch.Tensor, col_norm: torch.Tensor, N: int, M: int, masks: torch.Tensor | None = None,
+                  values: torch.Tensor | None = None):
+    """W: bf16 [R, K]; col_norm: fp32 [K] -> (masks int32 [R, K/32], values bf16 [R, K/2])."""
+    _dev(W, "W", torch.bfloat16, 2)
+    _dev(col_norm, "col_norm", torch.float32, 1)
+    R, K = W.shape
+    if col_norm.shape[0] != K:
+        raise ValueError("col_norm must have K entries")
+    if masks is None:
+        masks = torch.empty((R, max(K // 32, 1)), dtype=torch.int32, device=W.device)
+    if values is None:
+        values = torch.empty((R, max(K // 2, 1)), dtype=torch.bfloat16, device=W.device)
+    _dev(masks, "masks", torch.int32, 2)
+    _dev(values, "values", torch.bfloat16, 2)
+    if not (masks.is_contiguous() and values.is_contiguous()):
+        raise ValueError("masks and values must be contiguous")
+    if K % 32 == 0 and (masks.shape != (R, K // 32) or values.shape != (R, K // 2)):
+        raise ValueError("masks must be [R, K/32] and values [R, K/2]")
+    _check(lib.nm_prune_pack(_ptr(W), _ld(W), R, K, _ptr(col_norm), int(N), int(M), _ptr(masks), _ptr(values),
+                             _stream(W)))
+    return masks, values
+
+
+def nm_spmv_workspace_bytes(R: int, K: int, B: int) -> int:
+    return int(lib.nm_spmv_workspace_bytes(R, K, B))
+
+
+def dense_gemv_workspace_bytes(R: int, K: int, B: int) -> int:
+    return int(lib.dense_gemv_workspace_bytes(R, K, B))
+
+
+def _workspace(nbytes: int, ref: torch.Tensor, workspace: torch.Tensor | None):
+    if nbytes == 0:
+        return workspace, 0
+    if workspace is None:
+        workspace = torch.empty((nbytes + 3) // 4, dtype=torch.float32, device=ref.device)
+    if workspace.device != ref.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the same device")
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def _x_y(x: torch.Tensor, R: int, K: int, out: torch.Tensor | None):
+    squeeze = x.dim() == 1
+    if squeeze:
+        x = x.unsqueeze(0)
+    _dev(x, "x", torch.bfloat16, 2)
+    B = x.shape[0]
+    if x.shape[1] != K:
+        raise ValueError(f"x has {x.shape[1]} columns, expected K={K}")
+    if out is None:
+        out = torch.empty((B, R), dtype=torch.bfloat16, device=x.device)
+    o2 = out.unsqueeze(0) if out.dim() == 1 else out
+    _dev(o2, "out", torch.bfloat16, 2)
+    if o2.shape != (B, R):
+        raise ValueError(f"out must be [{B}, {R}]")
+    return x, B, o2, out, squeeze
+
+
+def nm_spmv(masks: torch.Tensor, values: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None,
+            workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """y = W_sparse x for packed (masks, values); x: bf16 [B, K] or [K] -> bf16 [B, R] (or [R])."""
+    _dev(masks, "masks", torch.int32, 2)
+    _dev(values, "values", torch.bfloat16, 2)
+    if not (masks.is_contiguous() and values.is_contiguous()):
+        raise ValueError("masks and values must be contiguous")
+    R = masks.shape[0]
+    K = masks.shape[1] * 32
+    if values.shape != (R, K // 2):
+        raise ValueError("values must be [R, K/2] with K = 32 * masks.shape[1]")
+    x2, B, o2, out, squeeze = _x_y(x, R, K, out)
+    ws, ws_bytes = _workspace(nm_spmv_workspace_bytes(R, K, B), x2, workspace)
+    _check(lib.nm_spmv(_ptr(masks), _ptr(values), R, K, _ptr(x2), _ld(x2), B, _ptr(o2), _ld(o2), _ptr(ws),
+                       ws_bytes, _stream(x2)))
+    return out[0] if squeeze and out.dim() == 2 else out
+
+
+def dense_gemv(W: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None,
+               workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """y = W x; W: bf16 [R, K]; x: bf16 [B, K] or [K] -> bf16 [B, R] (or [R])."""
+    _dev(W, "W", torch.bfloat16, 2)
+    R, K = W.shape
+    x2, B, o2, out, squeeze = _x_y(x, R, K, out)
+    ws, ws_bytes = _workspace(dense_gemv_workspace_bytes(R, K, B), x2, workspace)
+    _check(lib.dense_gemv(_ptr(W), _ld(W), R, K, _ptr(x2), _ld(x2), B, _ptr(o2), _ld(o2), _ptr(ws), ws_bytes,
+                          _stream(x2)))
+    return out[0] if squeeze and out.dim() == 2 else out
+
+
+def nm_unpack(masks: torch.Tensor, values: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Packed (masks, values) -> dense pruned bf16 [R, K] (zeros where bits are clear)."""
+    _dev(masks, "masks", torch.int32, 2)
+    _dev(values, "values", torch.bfloat16, 2)
+    R = masks.shape[0]
+    K = masks.shape[1] * 32
+    if out is None:
+        out = torch.empty((R, K), dtype=torch.bfloat16, device=masks.device)
+    _dev(out, "out", torch.bfloat16, 2)
+    _check(lib.nm_unpack(_ptr(masks), _ptr(values), R, K, _ptr(out), _ld(out), _stream(masks)))
+    return out

@@ -1,0 +1,248 @@
+// api.cpp -- the C ABI of include/nm_spmv.h: argument validation, error reporting,
+// per-device properties and kernel dispatch.  Every argument check runs before the
+// first HIP call, so invalid calls never touch the GPU.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "../../include/nm_spmv.h"
+#include "nm_kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+nm_status fail(nm_status s, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+nm_status hip_fail(const char *what, hipError_t e) {
+    return fail(NM_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu[kMaxDevices];
+std::atomic<int> g_lds[kMaxDevices];
+
+// Properties of the current device (cached).  Falls back to gfx950 figures when no
+// device is visible, which only matters for the size queries.
+nmk::DeviceInfo device_info() {
+    nmk::DeviceInfo d;
+    d.num_cu = 256;
+    d.max_lds_per_block = 160 * 1024;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return d;
+    }
+    int cu = g_cu[dev].load(std::memory_order_relaxed);
+    int lds = g_lds[dev].load(std::memory_order_relaxed);
+    if (cu <= 0) {
+        if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0) {
+            (void)hipGetLastError();
+            cu = 256;
+        }
+        if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || lds <= 0) {
+            (void)hipGetLastError();
+            lds = 64 * 1024;
+        }
+        g_lds[dev].store(lds, std::memory_order_relaxed);
+        g_cu[dev].store(cu, std::memory_order_relaxed);
+    }
+    d.num_cu = cu;
+    d.max_lds_per_block = lds;
+    return d;
+}
+
+// Optional launch-plan override for tuning sweeps: "<splits>,<grid_x>,<unroll>"
+// (0 keeps the planner's choice for that field).  The slice length follows from splits.
+void apply_override(const char *env, int64_t units, int64_t R, int B, size_t unit_lds, nmk::MvPlan &p) {
+    const char *s = std::getenv(env);
+    if (!s || !*s) return;
+    int sp = 0, gx = 0, un = 0;
+    if (std::sscanf(s, "%d,%d,%d", &sp, &gx, &un) < 1) return;
+    if (sp > 0) {
+        int64_t slice = (units + sp - 1) / sp;
+        p.slice = (int)slice;
+        p.splits = (int)((units + slice - 1) / slice);
+        p.lds_bytes = (size_t)slice * unit_lds;
+        p.ws_bytes = p.splits > 1 ? (size_t)p.splits * B * R * sizeof(float) : 0;
+    }
+    if (gx > 0) p.grid_x = gx;
+    if (un == 1 || un == 2 || un == 4) p.unroll = un;
+}
+
+nmk::MvPlan spmv_plan(int64_t R, int64_t K, int B) {
+    nmk::MvPlan p = nmk::plan_spmv(R, K, B, device_info());
+    apply_override("NM_SPMV_PLAN", K / 32, R, B, (size_t)B * 17 * 4, p);
+    return p;
+}
+
+nmk::MvPlan dense_plan(int64_t R, int64_t K, int B) {
+    nmk::MvPlan p = nmk::plan_dense(R, K, B, device_info());
+    apply_override("NM_DENSE_PLAN", K / 8, R, B, (size_t)B * 16, p);
+    return p;
+}
+
+constexpr int64_t kMaxDim = (int64_t)1 << 30;
+
+nm_status check_mv_common(int64_t R, int64_t K, int B, int64_t ldx, int64_t ldy, const void *x, const void *y) {
+    if (R < 1 || R > kMaxDim) return fail(NM_ERR_SHAPE, "R=%lld out of range [1, 2^30]", (long long)R);
+    if (B < 1 || B > 8) return fail(NM_ERR_SHAPE, "B=%d out of range [1, 8]", B);
+    if (ldx < K) return fail(NM_ERR_SHAPE, "ldx=%lld < K=%lld", (long long)ldx, (long long)K);
+    if (ldy < R) return fail(NM_ERR_SHAPE, "ldy=%lld < R=%lld", (long long)ldy, (long long)R);
+    if (ldx % 8) return fail(NM_ERR_ALIGN, "ldx=%lld is not a multiple of 8", (long long)ldx);
+    if (!aligned(x, 16)) return fail(NM_ERR_ALIGN, "x is not 16-byte aligned");
+    if (!aligned(y, 2)) return fail(NM_ERR_ALIGN, "y is not 2-byte aligned");
+    return NM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *nm_status_str(int s) {
+    switch (s) {
+    case NM_OK: return "NM_OK";
+    case NM_ERR_NULL: return "NM_ERR_NULL";
+    case NM_ERR_SHAPE: return "NM_ERR_SHAPE";
+    case NM_ERR_PATTERN: return "NM_ERR_PATTERN";
+    case NM_ERR_ALIGN: return "NM_ERR_ALIGN";
+    case NM_ERR_WORKSPACE: return "NM_ERR_WORKSPACE";
+    case NM_ERR_HIP: return "NM_ERR_HIP";
+    default: return "NM_ERR_UNKNOWN";
+    }
+}
+
+const char *nm_last_error(void) { return g_err; }
+
+int nm_version(void) { return 100; }
+
+nm_status nm_col_norm(const nm_bf16 *X, int64_t T, int64_t K, int64_t ldx, float *col_norm, void *hip_stream) {
+    try {
+        g_err[0] = 0;
+        if (!X || !col_norm) return fail(NM_ERR_NULL, "nm_col_norm: NULL pointer");
+        if (T < 1 || T > kMaxDim || K < 1 || K > kMaxDim || ldx < K)
+            return fail(NM_ERR_SHAPE, "nm_col_norm: bad sizes T=%lld K=%lld ldx=%lld", (long long)T, (long long)K,
+                        (long long)ldx);
+        if (!aligned(X, 2) || !aligned(col_norm, 4)) return fail(NM_ERR_ALIGN, "nm_col_norm: misaligned pointer");
+        hipError_t e = nmk::launch_col_norm(X, T, K, ldx, col_norm, (hipStream_t)hip_stream);
+        if (e != hipSuccess) return hip_fail("nm_col_norm launch", e);
+        return NM_OK;
+    } catch (...) {
+        return fail(NM_ERR_HIP, "nm_col_norm: internal error");
+    }
+}
+
+nm_status nm_prune_pack(const nm_bf16 *W, int64_t ldw, int64_t R, int64_t K, const float *col_norm, int N, int M,
+                        uint32_t *masks, nm_bf16 *values, void *hip_stream) {
+    try {
+        g_err[0] = 0;
+        if (!W || !col_norm || !masks || !values) return fail(NM_ERR_NULL, "nm_prune_pack: NULL pointer");
+        if (!(M == 4 || M == 8 || M == 16 || M == 32) || 2 * N != M)
+            return fail(NM_ERR_PATTERN, "nm_prune_pack: %d:%d is not a 50%% pattern with M in {4,8,16,32}", N, M);
+        if (R < 1 || R > kMaxDim || K < 32 || K > kMaxDim || K % 32 != 0 || ldw < K)
+            return fail(NM_ERR_SHAPE, "nm_prune_pack: bad sizes R=%lld K=%lld ldw=%lld (K must be a multiple of 32)",
+                        (long long)R, (long long)K, (long long)ldw);
+        if (ldw % 8 || !aligned(W, 16) || !aligned(col_norm, 16) || !aligned(masks, 4) || !aligned(values, 16))
+            return fail(NM_ERR_ALIGN, "nm_prune_pack: W/values/col_norm need 16-byte alignment, ldw a multiple of 8");
+        hipError_t e = nmk::launch_prune_pack(W, ldw, R, K, col_norm, N, M, masks, values, (hipStream_t)hip_stream);
+        if (e != hipSuccess) return hip_fail("nm_prune_pack launch", e);
+        return NM_OK;
+    } catch (...) {
+        return fail(NM_ERR_HIP, "nm_prune_pack: internal error");
+    }
+}
+
+size_t nm_spmv_workspace_bytes(int64_t R, int64_t K, int B) {
+    if (R < 1 || R > kMaxDim || K < 32 || K % 32 != 0 || K > kMaxDim || B < 1 || B > 8) return 0;
+    return spmv_plan(R, K, B).ws_bytes;
+}
+
+nm_status nm_spmv(const uint32_t *masks, const nm_bf16 *values, int64_t R, int64_t K, const nm_bf16 *x, int64_t ldx,
+                  int B, nm_bf16 *y, int64_t ldy, void *workspace, size_t workspace_bytes, void *hip_stream) {
+    try {
+        g_err[0] = 0;
+        if (!masks || !values || !x || !y) return fail(NM_ERR_NULL, "nm_spmv: NULL pointer");
+        if (K < 32 || K > kMaxDim || K % 32 != 0)
+            return fail(NM_ERR_SHAPE, "nm_spmv: K=%lld must be a positive multiple of 32", (long long)K);
+        nm_status st = check_mv_common(R, K, B, ldx, ldy, x, y);
+        if (st != NM_OK) return st;
+        if (!aligned(masks, 4) || !aligned(values, 16))
+            return fail(NM_ERR_ALIGN, "nm_spmv: masks need 4-byte and values 16-byte alignment");
+        const nmk::MvPlan p = spmv_plan(R, K, B);
+        if (p.ws_bytes > 0) {
+            if (!workspace || workspace_bytes < p.ws_bytes || !aligned(workspace, 4))
+                return fail(NM_ERR_WORKSPACE, "nm_spmv: workspace of %zu bytes required, %zu given", p.ws_bytes,
+                            workspace ? workspace_bytes : (size_t)0);
+        }
+        hipError_t e = nmk::launch_spmv(p, masks, values, R, K, x, ldx, B, y, ldy, (float *)workspace,
+                                        (hipStream_t)hip_stream);
+        if (e != hipSuccess) return hip_fail("nm_spmv launch", e);
+        return NM_OK;
+    } catch (...) {
+        return fail(NM_ERR_HIP, "nm_spmv: internal error");
+    }
+}
+
+size_t dense_gemv_workspace_bytes(int64_t R, int64_t K, int B) {
+    if (R < 1 || R > kMaxDim || K < 8 || K % 8 != 0 || K > kMaxDim || B < 1 || B > 8) return 0;
+    return dense_plan(R, K, B).ws_bytes;
+}
+
+nm_status dense_gemv(const nm_bf16 *W, int64_t ldw, int64_t R, int64_t K, const nm_bf16 *x, int64_t ldx, int B,
+                     nm_bf16 *y, int64_t ldy, void *workspace, size_t workspace_bytes, void *hip_stream) {
+    try {
+        g_err[0] = 0;
+        if (!W || !x || !y) return fail(NM_ERR_NULL, "dense_gemv: NULL pointer");
+        if (K < 8 || K > kMaxDim || K % 8 != 0 || ldw < K)
+            return fail(NM_ERR_SHAPE, "dense_gemv: bad sizes K=%lld ldw=%lld (K must be a multiple of 8)",
+                        (long long)K, (long long)ldw);
+        nm_status st = check_mv_common(R, K, B, ldx, ldy, x, y);
+        if (st != NM_OK) return st;
+        if (ldw % 8 || !aligned(W, 16))
+            return fail(NM_ERR_ALIGN, "dense_gemv: W needs 16-byte alignment and ldw a multiple of 8");
+        const nmk::MvPlan p = dense_plan(R, K, B);
+        if (p.ws_bytes > 0) {
+            if (!workspace || workspace_bytes < p.ws_bytes || !aligned(workspace, 4))
+                return fail(NM_ERR_WORKSPACE, "dense_gemv: workspace of %zu bytes required, %zu given", p.ws_bytes,
+                            workspace ? workspace_bytes : (size_t)0);
+        }
+        hipError_t e =
+            nmk::launch_dense(p, W, ldw, R, K, x, ldx, B, y, ldy, (float *)workspace, (hipStream_t)hip_stream);
+        if (e != hipSuccess) return hip_fail("dense_gemv launch", e);
+        return NM_OK;
+    } catch (...) {
+        return fail(NM_ERR_HIP, "dense_gemv: internal error");
+    }
+}
+
+nm_status nm_unpack(const uint32_t *masks, const nm_bf16 *values, int64_t R, int64_t K, nm_bf16 *W_out, int64_t ldw,
+                    void *hip_stream) {
+    try {
+        g_err[0] = 0;
+        if (!masks || !values || !W_out) return fail(NM_ERR_NULL, "nm_unpack: NULL pointer");
+        if (R < 1 || R > kMaxDim || K < 32 || K > kMaxDim || K % 32 != 0 || ldw < K)
+            return fail(NM_ERR_SHAPE, "nm_unpack: bad sizes R=%lld K=%lld ldw=%lld", (long long)R, (long long)K,
+                        (long long)ldw);
+        if (ldw % 8 || !aligned(W_out, 16) || !aligned(values, 16) || !aligned(masks, 4))
+            return fail(NM_ERR_ALIGN, "nm_unpack: W_out/values need 16-byte alignment, ldw a multiple of 8");
+        hipError_t e = nmk::launch_unpack(masks, values, R, K, W_out, ldw, (hipStream_t)hip_stream);
+        if (e != hipSuccess) return hip_fail("nm_unpack launch", e);
+        return NM_OK;
+    } catch (...) {
+        return fail(NM_ERR_HIP, "nm_unpack: internal error");
+    }
+}
+
+}  // extern "C"

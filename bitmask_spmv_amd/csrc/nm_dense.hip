@@ -1,0 +1,198 @@
+// nm_dense.hip -- same-GPU dense bf16 GEMV baseline on gfx950.
+//
+// The decode step is a memory-bound matrix-vector product that rereads every weight
+// per token ("SparseDecoding:解码感知的准确高效大模型剪枝框架", 前置知识 Prefill 与
+// Decoding); this kernel is the dense reference point the sparse kernel is compared
+// against, built with the same structure so that the comparison isolates the format:
+//   * x staged once per workgroup in LDS (contiguous, read back with 16-byte LDS loads);
+//   * a wave owns whole rows (or row slices); lane l reads 16-byte chunk l, l+64, ... of
+//     the row with non-temporal loads, so each wave iteration streams 1 KiB contiguously;
+//   * four v_dot2_f32_bf16 per chunk per token, fp32 accumulate, wave64 reduction,
+//     bf16 round-to-nearest-even store; deterministic split rows as in the sparse kernel.
+#include <atomic>
+
+#include "nm_device.h"
+#include "nm_kernels.h"
+
+namespace nmk {
+namespace {
+
+constexpr int kThreads = 512;
+constexpr size_t kLdsCap = 80 * 1024;
+constexpr size_t kLdsPerCu = 160 * 1024;
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+template <int B, int U>
+__global__ __launch_bounds__(kThreads) void dense_kernel(const u32x4 *__restrict__ W, int64_t ldw8, int R, int KC,
+                                                         const uint16_t *__restrict__ x, int64_t ldx,
+                                                         uint16_t *__restrict__ y, int64_t ldy,
+                                                         float *__restrict__ partial, int slice) {
+    extern __shared__ u32x4 xs4[];  // [B][ncs]
+    const int s = blockIdx.y;
+    const int c0 = s * slice;
+    const int ncs = min(slice, KC - c0);
+    for (int i = threadIdx.x; i < B * ncs; i += kThreads) {
+        const int b = i / ncs;
+        const int c = i - b * ncs;
+        xs4[i] = reinterpret_cast<const u32x4 *>(x + (int64_t)b * ldx)[c0 + c];
+    }
+    __syncthreads();
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    constexpr int kWaves = kThreads / kWave;
+    for (int row = blockIdx.x * kWaves + wave; row < R; row += gridDim.x * kWaves) {
+        const u32x4 *wrow = W + (int64_t)row * ldw8 + c0;
+        float acc[B];
+#pragma unroll
+        for (int b = 0; b < B; ++b) acc[b] = 0.f;
+        for (int base = 0; base < ncs; base += kWave * U) {
+            u32x4 wv[U];
+            int lc[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int c = base + u * kWave + lane;
+                const bool ok = c < ncs;
+                wv[u] = ok ? __builtin_nontemporal_load(wrow + c) : u32x4{0u, 0u, 0u, 0u};
+                lc[u] = ok ? c : 0;
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+#pragma unroll
+                for (int b = 0; b < B; ++b) {
+                    const u32x4 xv = xs4[b * ncs + lc[u]];
+                    float a = acc[b];
+                    a = dot2_bf16(wv[u].x, xv.x, a);
+                    a = dot2_bf16(wv[u].y, xv.y, a);
+                    a = dot2_bf16(wv[u].z, xv.z, a);
+                    a = dot2_bf16(wv[u].w, xv.w, a);
+                    acc[b] = a;
+                }
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            const float t = wave_sum(acc[b]);
+            if (lane == 0) {
+                if (gridDim.y == 1)
+                    y[(int64_t)b * ldy + row] = f32_to_bf16_rne(t);
+                else
+                    partial[((int64_t)s * B + b) * R + row] = t;
+            }
+        }
+    }
+}
+
+template <int B>
+__global__ __launch_bounds__(256) void dense_finish_kernel(const float *__restrict__ partial, int S, int R,
+                                                           uint16_t *__restrict__ y, int64_t ldy) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= R) return;
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+        float t = 0.f;
+        for (int s = 0; s < S; ++s) t += partial[((int64_t)s * B + b) * R + i];
+        y[(int64_t)b * ldy + i] = f32_to_bf16_rne(t);
+    }
+}
+
+template <int B, int U>
+hipError_t allow_lds(size_t bytes) {
+    static std::atomic<uint64_t> done{0};
+    if (bytes <= 64 * 1024) return hipSuccess;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = 1ull << (dev & 63);
+    if (done.load(std::memory_order_acquire) & bit) return hipSuccess;
+    e = hipFuncSetAttribute((const void *)dense_kernel<B, U>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)kLdsCap);
+    if (e == hipSuccess) done.fetch_or(bit, std::memory_order_acq_rel);
+    return e;
+}
+
+template <int B, int U>
+hipError_t launch_bu(const MvPlan &p, const uint16_t *W, int64_t ldw, int64_t R, int64_t K, const uint16_t *x,
+                     int64_t ldx, uint16_t *y, int64_t ldy, float *ws, hipStream_t st) {
+    hipError_t e = allow_lds<B, U>(p.lds_bytes);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((dense_kernel<B, U>), dim3(p.grid_x, p.splits), dim3(kThreads), p.lds_bytes, st,
+                       reinterpret_cast<const u32x4 *>(W), ldw / 8, (int)R, (int)(K / 8), x, ldx, y, ldy, ws,
+                       p.slice);
+    e = hipGetLastError();
+    if (e != hipSuccess || p.splits == 1) return e;
+    hipLaunchKernelGGL(dense_finish_kernel<B>, dim3((unsigned)((R + 255) / 256)), dim3(256), 0, st, ws, p.splits,
+                       (int)R, y, ldy);
+    return hipGetLastError();
+}
+
+template <int B>
+hipError_t launch_b(const MvPlan &p, const uint16_t *W, int64_t ldw, int64_t R, int64_t K, const uint16_t *x,
+                    int64_t ldx, uint16_t *y, int64_t ldy, float *ws, hipStream_t st) {
+    if (p.unroll >= 4) return launch_bu<B, 4>(p, W, ldw, R, K, x, ldx, y, ldy, ws, st);
+    if (p.unroll == 2) return launch_bu<B, 2>(p, W, ldw, R, K, x, ldx, y, ldy, ws, st);
+    return launch_bu<B, 1>(p, W, ldw, R, K, x, ldx, y, ldy, ws, st);
+}
+
+}  // namespace
+
+MvPlan plan_dense(int64_t R, int64_t K, int B, const DeviceInfo &dev) {
+    MvPlan p;
+    p.threads = kThreads;
+    const int64_t KC = K / 8;  // 16-byte chunks per row
+    const int64_t bytes_per_chunk = (int64_t)B * 16;
+    size_t cap = kLdsCap;
+    if (dev.max_lds_per_block > 0 && (size_t)dev.max_lds_per_block < cap) cap = (size_t)dev.max_lds_per_block;
+    int64_t max_slice = (int64_t)cap / bytes_per_chunk;
+    if (max_slice >= kWave) max_slice -= max_slice % kWave;
+    if (max_slice < 1) max_slice = 1;
+    const int64_t cu = dev.num_cu > 0 ? dev.num_cu : 256;
+    const int64_t want_tasks = cu * 16;
+    int64_t splits = (KC + max_slice - 1) / max_slice;
+    int64_t by_tasks = (want_tasks + R - 1) / R;
+    // no slice shorter than four wave iterations (4 KiB of a row per wave)
+    int64_t max_by_len = KC / (4 * kWave) > 0 ? KC / (4 * kWave) : 1;
+    if (by_tasks > max_by_len) by_tasks = max_by_len;
+    if (splits < by_tasks) splits = by_tasks;
+    int64_t slice = (KC + splits - 1) / splits;
+    if (slice > kWave) slice = (slice + kWave - 1) / kWave * kWave;
+    if (slice > max_slice) slice = max_slice;
+    splits = (KC + slice - 1) / slice;
+    p.splits = (int)splits;
+    p.slice = (int)slice;
+    p.lds_bytes = (size_t)slice * bytes_per_chunk;
+    int per_cu = (int)(kLdsPerCu / (p.lds_bytes > 0 ? p.lds_bytes : 1));
+    if (per_cu > 4) per_cu = 4;
+    if (per_cu < 1) per_cu = 1;
+    const int64_t waves = kThreads / kWave;
+    int64_t gx = (R + waves - 1) / waves;
+    int64_t cap_x = (per_cu * cu + splits - 1) / splits;
+    if (gx > cap_x) gx = cap_x;
+    if (gx < 1) gx = 1;
+    p.grid_x = (int)gx;
+    p.unroll = slice >= 4 * kWave ? 4 : (slice > kWave ? 2 : 1);
+    p.ws_bytes = splits > 1 ? (size_t)splits * B * R * sizeof(float) : 0;
+    return p;
+}
+
+hipError_t launch_dense(const MvPlan &p, const uint16_t *W, int64_t ldw, int64_t R, int64_t K, const uint16_t *x,
+                        int64_t ldx, int B, uint16_t *y, int64_t ldy, float *ws, hipStream_t st) {
+    switch (B) {
+    case 1: return launch_b<1>(p, W, ldw, R, K, x, ldx, y, ldy, ws, st);
+    case 2: return launch_b<2>(p, W, ldw, R, K, x, ldx, y, ldy, ws, st);
+    case 3: return launch_b<3>(p, W, ldw, R, K, x, ldx, y, ldy, ws, st);
+    case 4: return launch_b<4>(p, W, ldw, R, K, x, ldx, y, ldy, ws, st);
+    case 5: return launch_b<5>(p, W, ldw, R, K, x, ldx, y, ldy, ws, st);
+    case 6: return launch_b<6>(p, W, ldw, R, K, x, ldx, y, ldy, ws, st);
+    case 7: return launch_b<7>(p, W, ldw, R, K, x, ldx, y, ldy, ws, st);
+    case 8: return launch_b<8>(p, W, ldw, R, K, x, ldx, y, ldy, ws, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace nmk

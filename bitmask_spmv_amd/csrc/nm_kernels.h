@@ -1,0 +1,45 @@
+// nm_kernels.h -- internal launch interface between the C ABI (api.cpp) and the
+// gfx950 kernels.  Not installed; callers use include/nm_spmv.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace nmk {
+
+struct DeviceInfo {
+    int num_cu = 0;            // compute units on the current device
+    int max_lds_per_block = 0; // bytes of LDS one workgroup may allocate
+};
+
+// Launch plan of the split-row matrix-vector kernels.  Each row's reduction range
+// (mask words for the sparse kernel, 8-column chunks for the dense one) is cut into
+// `splits` contiguous slices of at most `slice` units.  grid = (grid_x, splits);
+// workgroup w of slice s stages that slice of x in LDS once and then walks rows
+// w*waves + wave, stepping by grid_x*waves.  With splits > 1 the slices write fp32
+// partial sums to the workspace and a second kernel adds them in slice order.
+struct MvPlan {
+    int splits = 1;
+    int slice = 0;          // units per slice
+    int grid_x = 1;
+    int threads = 512;      // workgroup size
+    int unroll = 2;         // wave iterations whose loads are issued together
+    size_t lds_bytes = 0;   // dynamic LDS per workgroup
+    size_t ws_bytes = 0;    // workspace bytes (0 when splits == 1)
+};
+
+MvPlan plan_spmv(int64_t R, int64_t K, int B, const DeviceInfo &dev);
+MvPlan plan_dense(int64_t R, int64_t K, int B, const DeviceInfo &dev);
+
+hipError_t launch_col_norm(const uint16_t *X, int64_t T, int64_t K, int64_t ldx, float *n, hipStream_t st);
+hipError_t launch_prune_pack(const uint16_t *W, int64_t ldw, int64_t R, int64_t K, const float *n, int N, int M,
+                             uint32_t *masks, uint16_t *values, hipStream_t st);
+hipError_t launch_unpack(const uint32_t *masks, const uint16_t *values, int64_t R, int64_t K, uint16_t *W,
+                         int64_t ldw, hipStream_t st);
+hipError_t launch_spmv(const MvPlan &p, const uint32_t *masks, const uint16_t *values, int64_t R, int64_t K,
+                       const uint16_t *x, int64_t ldx, int B, uint16_t *y, int64_t ldy, float *ws, hipStream_t st);
+hipError_t launch_dense(const MvPlan &p, const uint16_t *W, int64_t ldw, int64_t R, int64_t K, const uint16_t *x,
+                        int64_t ldx, int B, uint16_t *y, int64_t ldy, float *ws, hipStream_t st);
+
+}  // namespace nmk

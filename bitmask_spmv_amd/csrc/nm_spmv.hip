@@ -1,0 +1,235 @@
+// nm_spmv.hip -- batch-one / small-batch N:M bitmask SpMV on gfx950.
+//
+// What it computes (pages cited by title and section):
+//   "SparseDecoding: Decoding-Aware Pruning ..." (ai.info summary), Methodology Steps 2-3:
+//     each 32-bit mask word marks the kept columns of 32 consecutive inputs; its set
+//     bits pair one-to-one, in increasing column order, with the stored values; at 50%
+//     N:M with M <= 32 every aligned word has exactly 16 set bits, so the walk over a
+//     word is a fixed 16-step loop of "lowest set bit -> column, clear it".
+//   "SparseDecoding:解码感知的准确高效大模型剪枝框架" (paper.rainbus.top), 方法步骤详情
+//     第四步: the input vector is the reused operand and weights/masks are streamed;
+//     rows may be split with a reduction of the pieces.
+//
+// gfx950 design (what differs from the pages' A100/Triton kernel):
+//   * x lives in LDS for the whole workgroup: each 32-column block of x occupies 17
+//     dwords (16 data + 1 pad), so lanes that walk consecutive words land on different
+//     banks even when their bit positions agree.
+//   * word-per-lane mapping on the canonical row-major layout: lane l of a wave takes
+//     word w0+l of the row, so one wave iteration loads 256 contiguous bytes of masks
+//     and 2 KiB of contiguous values (two 16-byte loads per lane), all non-temporal.
+//   * 16 steps per word = 8 pairs; each pair gathers two bf16 inputs from LDS into one
+//     dword and feeds v_dot2_f32_bf16 with the matching packed value pair.
+//   * each wave owns whole rows (or row slices); the row total is a wave64 reduction.
+//     Slices of a row (when splits > 1) go to fp32 workspace and are added in slice
+//     order by a second kernel (deterministic, no atomics).
+//   * one kernel serves every 50% pattern (2:4 ... 16:32): the M of the pattern never
+//     enters the traversal.
+#include <atomic>
+
+#include "nm_device.h"
+#include "nm_kernels.h"
+
+namespace nmk {
+namespace {
+
+constexpr int kXPad = 17;         // dwords per 32-column block of x in LDS
+constexpr int kThreads = 512;     // 8 waves
+constexpr size_t kLdsCap = 80 * 1024;     // keeps two workgroups resident per CU
+constexpr size_t kLdsPerCu = 160 * 1024;  // gfx950 LDS per compute unit
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+template <int B, int U>
+__global__ __launch_bounds__(kThreads) void spmv_kernel(const uint32_t *__restrict__ masks,
+                                                        const u32x4 *__restrict__ values, int R, int KW,
+                                                        const uint16_t *__restrict__ x, int64_t ldx,
+                                                        uint16_t *__restrict__ y, int64_t ldy,
+                                                        float *__restrict__ partial, int slice) {
+    extern __shared__ uint32_t xs[];  // [B][nws * kXPad]
+    const int s = blockIdx.y;
+    const int w0 = s * slice;
+    const int nws = min(slice, KW - w0);
+    const int plane = nws * kXPad;
+
+    // Stage this slice of x (B tokens) into LDS.
+    for (int i = threadIdx.x; i < B * nws * 16; i += kThreads) {
+        const int b = i / (nws * 16);
+        const int r = i - b * nws * 16;
+        const uint32_t *xb = reinterpret_cast<const uint32_t *>(x + (int64_t)b * ldx) + (int64_t)w0 * 16;
+        xs[b * plane + (r >> 4) * kXPad + (r & 15)] = xb[r];
+    }
+    __syncthreads();
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    constexpr int kWaves = kThreads / kWave;
+    const uint16_t *xs16 = reinterpret_cast<const uint16_t *>(xs);
+
+    for (int row = blockIdx.x * kWaves + wave; row < R; row += gridDim.x * kWaves) {
+        const uint32_t *mrow = masks + (int64_t)row * KW + w0;
+        const u32x4 *vrow = values + ((int64_t)row * KW + w0) * 2;
+        float acc[B];
+#pragma unroll
+        for (int b = 0; b < B; ++b) acc[b] = 0.f;
+
+        for (int base = 0; base < nws; base += kWave * U) {
+            uint32_t m[U];
+            u32x4 va[U], vb[U];
+            int lw[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int w = base + u * kWave + lane;
+                const bool ok = w < nws;
+                // Lanes past the end walk a dummy word: 16 low bits set, zero values.
+                m[u] = ok ? __builtin_nontemporal_load(mrow + w) : 0xFFFFu;
+                va[u] = ok ? __builtin_nontemporal_load(vrow + 2 * w) : u32x4{0u, 0u, 0u, 0u};
+                vb[u] = ok ? __builtin_nontemporal_load(vrow + 2 * w + 1) : u32x4{0u, 0u, 0u, 0u};
+                lw[u] = ok ? w : 0;
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t v[8] = {va[u].x, va[u].y, va[u].z, va[u].w, vb[u].x, vb[u].y, vb[u].z, vb[u].w};
+                const uint16_t *xw = xs16 + 2 * lw[u] * kXPad;  // this word's 32 columns
+                uint32_t mm = m[u];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const int c0 = __builtin_ctz(mm);
+                    mm &= mm - 1;
+                    const int c1 = __builtin_ctz(mm);
+                    mm &= mm - 1;
+#pragma unroll
+                    for (int b = 0; b < B; ++b) {
+                        const uint16_t *xp = xw + 2 * b * plane;
+                        const uint32_t pr = (uint32_t)xp[c0] | ((uint32_t)xp[c1] << 16);
+                        acc[b] = dot2_bf16(v[k], pr, acc[b]);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            const float t = wave_sum(acc[b]);
+            if (lane == 0) {
+                if (gridDim.y == 1)
+                    y[(int64_t)b * ldy + row] = f32_to_bf16_rne(t);
+                else
+                    partial[((int64_t)s * B + b) * R + row] = t;
+            }
+        }
+    }
+}
+
+// Second pass of split rows: add the slices in order, round once to bf16.
+template <int B>
+__global__ __launch_bounds__(256) void split_finish_kernel(const float *__restrict__ partial, int S, int R,
+                                                           uint16_t *__restrict__ y, int64_t ldy) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= R) return;
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+        float t = 0.f;
+        for (int s = 0; s < S; ++s) t += partial[((int64_t)s * B + b) * R + i];
+        y[(int64_t)b * ldy + i] = f32_to_bf16_rne(t);
+    }
+}
+
+// Raise the dynamic-LDS limit of one kernel instance once per device.
+template <int B, int U>
+hipError_t allow_lds(size_t bytes) {
+    static std::atomic<uint64_t> done{0};
+    if (bytes <= 64 * 1024) return hipSuccess;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = 1ull << (dev & 63);
+    if (done.load(std::memory_order_acquire) & bit) return hipSuccess;
+    e = hipFuncSetAttribute((const void *)spmv_kernel<B, U>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)kLdsCap);
+    if (e == hipSuccess) done.fetch_or(bit, std::memory_order_acq_rel);
+    return e;
+}
+
+template <int B, int U>
+hipError_t launch_bu(const MvPlan &p, const uint32_t *masks, const uint16_t *values, int64_t R, int64_t K,
+                     const uint16_t *x, int64_t ldx, uint16_t *y, int64_t ldy, float *ws, hipStream_t st) {
+    hipError_t e = allow_lds<B, U>(p.lds_bytes);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((spmv_kernel<B, U>), dim3(p.grid_x, p.splits), dim3(kThreads), p.lds_bytes, st, masks,
+                       reinterpret_cast<const u32x4 *>(values), (int)R, (int)(K / 32), x, ldx, y, ldy, ws, p.slice);
+    e = hipGetLastError();
+    if (e != hipSuccess || p.splits == 1) return e;
+    hipLaunchKernelGGL(split_finish_kernel<B>, dim3((unsigned)((R + 255) / 256)), dim3(256), 0, st, ws, p.splits,
+                       (int)R, y, ldy);
+    return hipGetLastError();
+}
+
+template <int B>
+hipError_t launch_b(const MvPlan &p, const uint32_t *masks, const uint16_t *values, int64_t R, int64_t K,
+                    const uint16_t *x, int64_t ldx, uint16_t *y, int64_t ldy, float *ws, hipStream_t st) {
+    if (p.unroll >= 4) return launch_bu<B, 4>(p, masks, values, R, K, x, ldx, y, ldy, ws, st);
+    if (p.unroll == 2) return launch_bu<B, 2>(p, masks, values, R, K, x, ldx, y, ldy, ws, st);
+    return launch_bu<B, 1>(p, masks, values, R, K, x, ldx, y, ldy, ws, st);
+}
+
+}  // namespace
+
+MvPlan plan_spmv(int64_t R, int64_t K, int B, const DeviceInfo &dev) {
+    MvPlan p;
+    p.threads = kThreads;
+    const int64_t KW = K / 32;
+    const int64_t bytes_per_word = (int64_t)B * kXPad * 4;
+    size_t cap = kLdsCap;
+    if (dev.max_lds_per_block > 0 && (size_t)dev.max_lds_per_block < cap) cap = (size_t)dev.max_lds_per_block;
+    int64_t max_slice = (int64_t)cap / bytes_per_word;
+    if (max_slice >= kWave) max_slice -= max_slice % kWave;
+    if (max_slice < 1) max_slice = 1;
+    // Enough (row, slice) tasks to give every resident wave work, but no slice shorter
+    // than one wave iteration.
+    const int64_t cu = dev.num_cu > 0 ? dev.num_cu : 256;
+    const int64_t want_tasks = cu * 16;
+    int64_t splits = (KW + max_slice - 1) / max_slice;
+    int64_t by_tasks = (want_tasks + R - 1) / R;
+    int64_t max_by_len = KW / kWave > 0 ? KW / kWave : 1;
+    if (by_tasks > max_by_len) by_tasks = max_by_len;
+    if (splits < by_tasks) splits = by_tasks;
+    int64_t slice = (KW + splits - 1) / splits;
+    if (slice > kWave) slice = (slice + kWave - 1) / kWave * kWave;
+    if (slice > max_slice) slice = max_slice;
+    splits = (KW + slice - 1) / slice;
+    p.splits = (int)splits;
+    p.slice = (int)slice;
+    p.lds_bytes = (size_t)slice * bytes_per_word;
+    int per_cu = (int)(kLdsPerCu / (p.lds_bytes > 0 ? p.lds_bytes : 1));
+    if (per_cu > 4) per_cu = 4;
+    if (per_cu < 1) per_cu = 1;
+    const int64_t waves = kThreads / kWave;
+    int64_t gx = (R + waves - 1) / waves;
+    int64_t cap_x = (per_cu * cu + splits - 1) / splits;
+    if (gx > cap_x) gx = cap_x;
+    if (gx < 1) gx = 1;
+    p.grid_x = (int)gx;
+    p.unroll = slice > kWave ? 2 : 1;
+    p.ws_bytes = splits > 1 ? (size_t)splits * B * R * sizeof(float) : 0;
+    return p;
+}
+
+hipError_t launch_spmv(const MvPlan &p, const uint32_t *masks, const uint16_t *values, int64_t R, int64_t K,
+                       const uint16_t *x, int64_t ldx, int B, uint16_t *y, int64_t ldy, float *ws, hipStream_t st) {
+    switch (B) {
+    case 1: return launch_b<1>(p, masks, values, R, K, x, ldx, y, ldy, ws, st);
+    case 2: return launch_b<2>(p, masks, values, R, K, x, ldx, y, ldy, ws, st);
+    case 3: return launch_b<3>(p, masks, values, R, K, x, ldx, y, ldy, ws, st);
+    case 4: return launch_b<4>(p, masks, values, R, K, x, ldx, y, ldy, ws, st);
+    case 5: return launch_b<5>(p, masks, values, R, K, x, ldx, y, ldy, ws, st);
+    case 6: return launch_b<6>(p, masks, values, R, K, x, ldx, y, ldy, ws, st);
+    case 7: return launch_b<7>(p, masks, values, R, K, x, ldx, y, ldy, ws, st);
+    case 8: return launch_b<8>(p, masks, values, R, K, x, ldx, y, ldy, ws, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace nmk

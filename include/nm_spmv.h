@@ -1,0 +1,148 @@
+/*
+ * nm_spmv.h -- C ABI of the N:M bitmask sparse decode library for AMD MI355X (gfx950).
+ *
+ * The library computes, on one GPU, the decode-time hot path of N:M-pruned linear
+ * layers described on these pages (cited by title and section):
+ *
+ *   [SD-en]    "SparseDecoding: Decoding-Aware Pruning for Accurate and Efficient LLM
+ *              Inference" (ai.info AI summary): Key Contributions 2; Main Findings
+ *              (metadata reduction, identical traffic across patterns); Methodology in
+ *              Plain English, Steps 2 and 3.
+ *   [SD-cn]    "SparseDecoding:解码感知的准确高效大模型剪枝框架" (paper.rainbus.top):
+ *              前置知识 (Prefill 与 Decoding; N:M 半结构化稀疏; SpMM 与 SpMV);
+ *              核心方法 (核心创新二); 方法步骤详情 (第三步, 第四步).
+ *   [SD-repro] "SparseDecoding：只用解码激活校准的稀疏推理" (daiwk.github.io):
+ *              核心公式; 背景与主要改动.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers are DEVICE pointers owned by the caller unless stated otherwise.  The
+ *    library never allocates or frees device memory and keeps no per-call state.
+ *  - bf16 tensors are passed as raw 16-bit patterns (nm_bf16).
+ *  - Matrices are row-major; ld* arguments are row strides in ELEMENTS.
+ *  - Every call is asynchronous on `hip_stream` (a hipStream_t; NULL = the default
+ *    stream) and returns once the work is enqueued.  Argument errors are reported
+ *    synchronously, before any HIP call is made; a fault inside a kernel surfaces at
+ *    the caller's next synchronisation, as usual in HIP.
+ *  - Inputs must be finite.  Behaviour on NaN/Inf inputs is unspecified.
+ *  - Sizes (R, K, T) are limited to 2^30.
+ *  - Alignment: the base pointers of W, values, x and col_norm (pack input) must be
+ *    16-byte aligned and ldw, ldx must be multiples of 8 elements, else NM_ERR_ALIGN.
+ *    masks and workspace must be 4-byte aligned, y 2-byte aligned (ldy is free).
+ *  - Entry points are thread-safe and reentrant.  nm_last_error() returns a
+ *    thread-local description of the last failure on the calling thread.
+ *  - No C++ exception crosses this boundary.
+ */
+#ifndef NM_SPMV_H
+#define NM_SPMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t nm_bf16; /* raw bfloat16 bits */
+
+typedef enum {
+    NM_OK = 0,
+    NM_ERR_NULL = 1,      /* a required pointer is NULL                              */
+    NM_ERR_SHAPE = 2,     /* sizes out of range / inconsistent (e.g. K % 32 != 0)    */
+    NM_ERR_PATTERN = 3,   /* N:M not one of 2:4, 4:8, 8:16, 16:32                    */
+    NM_ERR_ALIGN = 4,     /* pointer or leading dimension misaligned                 */
+    NM_ERR_WORKSPACE = 5, /* workspace NULL or smaller than *_workspace_bytes()      */
+    NM_ERR_HIP = 6        /* a HIP runtime call failed (message in nm_last_error)    */
+} nm_status;
+
+/* Static string naming a status code. */
+const char *nm_status_str(int status);
+
+/* Thread-local text of the last failure on this thread ("" if none). */
+const char *nm_last_error(void);
+
+/* Library ABI version (major * 10000 + minor * 100 + patch). */
+int nm_version(void);
+
+/*
+ * nm_col_norm -- Wanda's per-input-channel activation norm [SD-repro, 核心公式]:
+ *     col_norm[j] = sqrt( sum_{t < T} X[t][j]^2 ).
+ * X: bf16 [T][ldx] calibration activations (one row per calibration token).
+ * col_norm: fp32 [K] output.
+ * The sum runs in fp64 in token order, the square root is the correctly rounded fp64
+ * one, and the result is rounded once (to nearest even) to fp32.  The result is
+ * therefore fully determined by X (bit-reproducible).
+ * Requires 1 <= T <= 2^30, 1 <= K <= 2^30, ldx >= K.
+ */
+nm_status nm_col_norm(const nm_bf16 *X, int64_t T, int64_t K, int64_t ldx, float *col_norm,
+                      void *hip_stream);
+
+/*
+ * nm_prune_pack -- Wanda-style N:M selection and bitmask packing.
+ * Score [SD-repro, 核心公式]: s_ij = |W_ij| * col_norm[j], evaluated exactly (fp64
+ * product of an 8-bit and a 24-bit significand).  In every group of M consecutive
+ * input columns of a row the N highest scores are kept [SD-cn, 前置知识 N:M]; equal
+ * scores keep the lower column.  Only 50% patterns are accepted: (N, M) in
+ * {(2,4), (4,8), (8,16), (16,32)}, so that every aligned 32-column word holds exactly
+ * 16 kept weights [SD-en, Methodology Step 3].
+ *
+ * Outputs (canonical packed layout [SD-en, Methodology Step 2]):
+ *   masks  uint32 [R][K/32]: bit b of word w is set iff column 32w+b is kept.
+ *   values bf16   [R][K/2] : values[i][16w+t] is the raw W pattern of the t-th kept
+ *                            column of word w, in increasing column order (the order
+ *                            a lowest-set-bit-first scan visits them).  A kept weight
+ *                            whose value is zero still sets its bit.
+ * W: bf16 [R][ldw], col_norm: fp32 [K] (non-negative, e.g. from nm_col_norm).
+ * Requires R >= 1, K >= 32, K % 32 == 0, ldw >= K.
+ */
+nm_status nm_prune_pack(const nm_bf16 *W, int64_t ldw, int64_t R, int64_t K, const float *col_norm,
+                        int N, int M, uint32_t *masks, nm_bf16 *values, void *hip_stream);
+
+/*
+ * nm_spmv -- batch-one (B <= 8) N:M sparse matrix-vector product of a packed matrix
+ * [SD-en, Methodology Steps 2-3; SD-cn, 方法步骤详情 第四步]:
+ *     y[b][i] = sum_j Wsparse[i][j] * x[b][j],   0 <= b < B, 0 <= i < R.
+ * Each mask word is walked with a fixed 16-step loop (find lowest set bit -> column,
+ * clear it), pairing the t-th set bit with values[16w+t].  The kernel does not depend
+ * on M: every 50% pattern has 16 set bits per word.  Products and sums are fp32; y is
+ * rounded to nearest even bf16.
+ *
+ * masks/values: canonical layout as produced by nm_prune_pack (rows contiguous).
+ * x: bf16 [B][ldx]; y: bf16 [B][ldy] (ldy >= R).
+ * workspace: device scratch of at least nm_spmv_workspace_bytes(R, K, B) bytes (may
+ * be NULL when that size is 0).  It holds fp32 partial sums of split rows; the
+ * second pass adds them in a fixed order, so results are bit-reproducible run to run.
+ * Requires R >= 1, K >= 32, K % 32 == 0, 1 <= B <= 8, ldx >= K, ldy >= R, and every
+ * mask word to hold exactly 16 set bits (not re-checked on the device).
+ */
+size_t nm_spmv_workspace_bytes(int64_t R, int64_t K, int B);
+nm_status nm_spmv(const uint32_t *masks, const nm_bf16 *values, int64_t R, int64_t K, const nm_bf16 *x,
+                  int64_t ldx, int B, nm_bf16 *y, int64_t ldy, void *workspace, size_t workspace_bytes,
+                  void *hip_stream);
+
+/*
+ * dense_gemv -- same-GPU dense baseline for the same product with an unpruned bf16
+ * matrix (decode is a memory-bound matrix-vector product [SD-cn, 前置知识 Prefill 与
+ * Decoding]):  y[b][i] = sum_j W[i][j] * x[b][j], fp32 accumulate, bf16 RNE store.
+ * W: bf16 [R][ldw]; x: bf16 [B][ldx]; y: bf16 [B][ldy].
+ * workspace: at least dense_gemv_workspace_bytes(R, K, B) bytes (NULL if 0).
+ * Requires R >= 1, K >= 8, K % 8 == 0, 1 <= B <= 8, ldw >= K, ldx >= K, ldy >= R.
+ */
+size_t dense_gemv_workspace_bytes(int64_t R, int64_t K, int B);
+nm_status dense_gemv(const nm_bf16 *W, int64_t ldw, int64_t R, int64_t K, const nm_bf16 *x, int64_t ldx,
+                     int B, nm_bf16 *y, int64_t ldy, void *workspace, size_t workspace_bytes,
+                     void *hip_stream);
+
+/*
+ * nm_unpack -- inverse of the packing: W_out[i][j] = kept value of column j, or +0.0
+ * where the bit is clear.  W_out: bf16 [R][ldw] (ldw >= K, multiple of 8).
+ * Requires R >= 1, K >= 32, K % 32 == 0 and 16 set bits per mask word.
+ */
+nm_status nm_unpack(const uint32_t *masks, const nm_bf16 *values, int64_t R, int64_t K, nm_bf16 *W_out,
+                    int64_t ldw, void *hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NM_SPMV_H */

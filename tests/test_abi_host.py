@@ -1,0 +1,128 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every
+function that include/*.h declares, and rejects invalid arguments synchronously
+with the documented status codes before making any HIP call."""
+from __future__ import annotations
+
+import ctypes
+import glob
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "bitmask_spmv_amd", "libnmspmv.so")
+
+NM_OK, NM_ERR_NULL, NM_ERR_SHAPE, NM_ERR_PATTERN, NM_ERR_ALIGN, NM_ERR_WORKSPACE, NM_ERR_HIP = range(7)
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([A-Za-z_]\w*)\s*\(", text, flags=re.M):
+            name = m.group(1)
+            if name not in ("if", "while", "defined"):
+                names.add(name)
+    return sorted(names)
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(LIB):
+        pytest.fail(f"{LIB} not built: run __graft_entry__.build() first")
+    lib = ctypes.CDLL(LIB)
+    i64, p, i32, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.nm_status_str.argtypes, lib.nm_status_str.restype = [i32], ctypes.c_char_p
+    lib.nm_last_error.restype = ctypes.c_char_p
+    lib.nm_col_norm.argtypes = [p, i64, i64, i64, p, p]
+    lib.nm_prune_pack.argtypes = [p, i64, i64, i64, p, i32, i32, p, p, p]
+    lib.nm_spmv.argtypes = [p, p, i64, i64, p, i64, i32, p, i64, p, sz, p]
+    lib.dense_gemv.argtypes = [p, i64, i64, i64, p, i64, i32, p, i64, p, sz, p]
+    lib.nm_unpack.argtypes = [p, p, i64, i64, p, i64, p]
+    return lib
+
+
+def test_header_declares_the_expected_entry_points():
+    names = declared_functions()
+    for n in ("nm_col_norm", "nm_prune_pack", "nm_spmv", "nm_spmv_workspace_bytes", "dense_gemv",
+              "dense_gemv_workspace_bytes", "nm_unpack", "nm_status_str", "nm_last_error", "nm_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, missing
+    for n in declared_functions():
+        getattr(L, n)  # resolvable through dlsym
+
+
+def test_status_strings(L):
+    assert L.nm_status_str(0) == b"NM_OK"
+    assert L.nm_status_str(3) == b"NM_ERR_PATTERN"
+    assert L.nm_status_str(99) == b"NM_ERR_UNKNOWN"
+    assert L.nm_version() >= 100
+
+
+# Fake, never-dereferenced addresses: validation must reject the call before any use.
+A16 = 0x10000
+A4 = 0x10004
+A2 = 0x10002
+
+
+def test_null_pointers_rejected(L):
+    assert L.nm_spmv(None, A16, 4, 64, A16, 64, 1, A16, 4, None, 0, None) == NM_ERR_NULL
+    assert L.dense_gemv(A16, 64, 4, 64, None, 64, 1, A16, 4, None, 0, None) == NM_ERR_NULL
+    assert L.nm_prune_pack(A16, 64, 4, 64, None, 2, 4, A16, A16, None) == NM_ERR_NULL
+    assert L.nm_col_norm(None, 16, 64, 64, A16, None) == NM_ERR_NULL
+    assert L.nm_unpack(A16, None, 4, 64, A16, 64, None) == NM_ERR_NULL
+    assert b"NULL" in L.nm_last_error()
+
+
+@pytest.mark.parametrize("N,M", [(1, 4), (3, 4), (2, 2), (4, 6), (32, 64), (0, 0), (8, 8)])
+def test_patterns_other_than_half_rejected(L, N, M):
+    assert L.nm_prune_pack(A16, 64, 4, 64, A16, N, M, A16, A16, None) == NM_ERR_PATTERN
+
+
+@pytest.mark.parametrize("R,K,B", [(0, 64, 1), (4, 48, 1), (4, 16, 1), (4, 0, 1), (4, 64, 0), (4, 64, 9),
+                                   (-1, 64, 1), (1 << 31, 64, 1)])
+def test_bad_spmv_shapes_rejected(L, R, K, B):
+    assert L.nm_spmv(A4, A16, R, K, A16, max(K, 8), B, A16, max(R, 1), None, 0, None) == NM_ERR_SHAPE
+
+
+def test_bad_leading_dims_rejected(L):
+    assert L.nm_spmv(A4, A16, 4, 64, A16, 32, 1, A16, 4, None, 0, None) == NM_ERR_SHAPE  # ldx < K
+    assert L.nm_spmv(A4, A16, 4, 64, A16, 64, 1, A16, 3, None, 0, None) == NM_ERR_SHAPE  # ldy < R
+    assert L.dense_gemv(A16, 60, 4, 64, A16, 64, 1, A16, 4, None, 0, None) == NM_ERR_SHAPE  # ldw < K
+    assert L.dense_gemv(A16, 64, 4, 60, A16, 64, 1, A16, 4, None, 0, None) == NM_ERR_SHAPE  # K % 8
+    assert L.nm_prune_pack(A16, 64, 4, 96, A16, 2, 4, A16, A16, None) == NM_ERR_SHAPE  # ldw < K
+
+
+def test_misalignment_rejected(L):
+    assert L.nm_spmv(A4, A4, 4, 64, A16, 64, 1, A16, 4, None, 0, None) == NM_ERR_ALIGN  # values
+    assert L.nm_spmv(A4, A16, 4, 64, A4, 64, 1, A16, 4, None, 0, None) == NM_ERR_ALIGN  # x
+    assert L.nm_spmv(A4, A16, 4, 64, A16, 68, 2, A16, 4, None, 0, None) == NM_ERR_ALIGN  # ldx % 8
+    assert L.nm_spmv(A2, A16, 4, 64, A16, 64, 1, A16, 4, None, 0, None) == NM_ERR_ALIGN  # masks
+    assert L.nm_spmv(A4, A16, 4, 64, A16, 64, 1, 0x10001, 4, None, 0, None) == NM_ERR_ALIGN  # y
+    assert L.dense_gemv(A4, 64, 4, 64, A16, 64, 1, A16, 4, None, 0, None) == NM_ERR_ALIGN  # W
+    assert L.dense_gemv(A16, 68, 4, 64, A16, 64, 1, A16, 4, None, 0, None) == NM_ERR_ALIGN  # ldw
+    assert L.nm_prune_pack(A16, 64, 4, 64, A4, 2, 4, A16, A16, None) == NM_ERR_ALIGN  # col_norm
+    assert L.nm_unpack(A4, A16, 4, 64, A4, 64, None) == NM_ERR_ALIGN  # W_out
+
+
+def test_workspace_size_queries_are_consistent(L):
+    L.nm_spmv_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int]
+    L.nm_spmv_workspace_bytes.restype = ctypes.c_size_t
+    L.dense_gemv_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int]
+    L.dense_gemv_workspace_bytes.restype = ctypes.c_size_t
+    assert L.nm_spmv_workspace_bytes(4, 48, 1) == 0  # invalid shape -> 0
+    # split rows need R * B fp32 per slice; a whole-row plan needs nothing
+    for R, K, B in [(1024, 4096, 1), (8192, 28672, 8), (4096, 4096, 1)]:
+        ws = L.nm_spmv_workspace_bytes(R, K, B)
+        assert ws % (4 * R * B) == 0
+        ws = L.dense_gemv_workspace_bytes(R, K, B)
+        assert ws % (4 * R * B) == 0

@@ -1,0 +1,332 @@
+"""GPU parity: the HIP path (through the C ABI, via the thin binding) against the CPU
+oracle on the same seeded inputs.
+
+Bars: bit-exact column norms, masks, packed values and unpacked matrices; SpMV and
+GEMV outputs within |y - y_ref| <= 1e-2 |y_ref| + 1e-3 sum_j |W_ij x_j| element by
+element; exact equality where the result is an integer or a power-of-two rescaling.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests import pins
+from tests.gpu_util import (bf16_as_f64, dev_bf16, dev_f32, dev_u32, host_bf16, host_f32, host_u32, say)
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("needs a HIP GPU", allow_module_level=True)
+
+import bitmask_spmv_amd as nm  # noqa: E402  (fails loudly if the library is missing)
+
+PATTERNS = [(2, 4), (4, 8), (8, 16), (16, 32)]
+RTOL, ATOL_FRAC = 1e-2, 1e-3
+
+
+def assert_within(y_gpu_bits, y_ref, absum, what):
+    y = bf16_as_f64(y_gpu_bits)
+    ok = oracle.within_tolerance(y, y_ref, absum, RTOL, ATOL_FRAC)
+    if not ok.all():
+        idx = np.argwhere(~ok)[:5]
+        raise AssertionError(f"{what}: {int((~ok).sum())} of {ok.size} outside tolerance, e.g. "
+                             + ", ".join(f"{tuple(i)}: gpu={y[tuple(i)]!r} ref={y_ref[tuple(i)]!r}" for i in idx))
+
+
+def gpu_pack(W_bits, X_bits, N, M):
+    n = nm.nm_col_norm(dev_bf16(X_bits))
+    masks, values = nm.nm_prune_pack(dev_bf16(W_bits), n, N, M)
+    torch.cuda.synchronize()
+    return host_f32(n), host_u32(masks), host_bf16(values), masks, values
+
+
+# ------------------------------------------------------------------ column norm
+@pytest.mark.parametrize("T,K", [(16, 512), (16, 4096), (7, 1000), (1, 33), (16, 28672)])
+def test_col_norm_bit_exact(T, K):
+    say("col_norm", T, K)
+    X = synth.calib_acts(K, 0, T, K, T=T)
+    got = host_f32(nm.nm_col_norm(dev_bf16(X)))
+    ref = oracle.col_norm(X)
+    assert (got.view(np.uint32) == ref.view(np.uint32)).all()
+
+
+def test_col_norm_closed_forms_and_tiny_values():
+    say("col_norm closed forms")
+    X = np.zeros((16, 64), np.float32)
+    X[0, 0], X[1, 0] = 3.0, 4.0
+    X[:, 1] = -3.0
+    X[5, 3] = -2.0 ** -100
+    X[2, 5] = 2.0 ** -130  # bf16 subnormal input
+    Xb = synth.to_bf16_bits(X)
+    got = host_f32(nm.nm_col_norm(dev_bf16(Xb)))
+    assert got[0] == 5.0 and got[1] == 12.0 and got[2] == 0.0 and got[3] == 2.0 ** -100
+    assert (got.view(np.uint32) == oracle.col_norm(Xb).view(np.uint32)).all()
+
+
+# ------------------------------------------------------------------ select + pack
+@pytest.mark.parametrize("N,M", PATTERNS)
+@pytest.mark.parametrize("R,K", [(256, 512), (37, 1024), (1, 32), (300, 4096)])
+def test_prune_pack_bit_exact(N, M, R, K):
+    say("prune_pack", N, M, R, K)
+    W = synth.weights(R, K, 1, R, K, M)
+    X = synth.calib_acts(K, 1, R, K, M)
+    n, m, v, _, _ = gpu_pack(W, X, N, M)
+    nref = oracle.col_norm(X)
+    mref, vref = oracle.prune_pack(W, nref, N, M)
+    assert (n.view(np.uint32) == nref.view(np.uint32)).all()
+    assert (m == mref).all()
+    assert (v == vref).all()
+    assert pins.certificate_ok(W, n, m, N, M).all()
+
+
+@pytest.mark.parametrize("N,M", PATTERNS)
+def test_prune_pack_tie_stress_and_signed_zero(N, M):
+    say("prune_pack ties", N, M)
+    R, K = 64, 1024
+    W, n = synth.tie_stress(R, K, 2, M)
+    masks, values = nm.nm_prune_pack(dev_bf16(W), dev_f32(n), N, M)
+    mref, vref = oracle.prune_pack(W, n, N, M)
+    assert (host_u32(masks) == mref).all()
+    assert (host_bf16(values) == vref).all()
+
+
+def test_prune_pack_subnormal_weights_and_norms():
+    """Exact scores must not flush: tiny bf16 weights and fp32 subnormal norms."""
+    say("prune_pack subnormal")
+    R, K = 8, 256
+    g = synth.rng(3, 3)
+    W = synth.to_bf16_bits((g.standard_normal((R, K)) * 2.0 ** -128).astype(np.float32))
+    n = (g.random(K) * 2.0 ** -140).astype(np.float32)
+    n[::5] = np.float32(1e-45)
+    masks, values = nm.nm_prune_pack(dev_bf16(W), dev_f32(n), 4, 8)
+    mref, vref = oracle.prune_pack(W, n, 4, 8)
+    assert (host_u32(masks) == mref).all() and (host_bf16(values) == vref).all()
+
+
+def test_prune_pack_strided_input():
+    say("prune_pack strided W")
+    R, K, ld = 48, 512, 640
+    Wfull = synth.weights(R, ld, 4)
+    X = synth.calib_acts(K, 4)
+    Wd = dev_bf16(Wfull)[:, :K]
+    n = nm.nm_col_norm(dev_bf16(X))
+    masks, values = nm.nm_prune_pack(Wd, n, 8, 16)
+    mref, vref = oracle.prune_pack(np.ascontiguousarray(Wfull[:, :K]), oracle.col_norm(X), 8, 16)
+    assert (host_u32(masks) == mref).all() and (host_bf16(values) == vref).all()
+
+
+# ------------------------------------------------------------------ unpack
+@pytest.mark.parametrize("N,M", [(2, 4), (16, 32)])
+def test_unpack_bit_exact(N, M):
+    say("unpack", N, M)
+    R, K = 200, 2048
+    W = synth.weights(R, K, 5)
+    mref, vref = oracle.prune_pack(W, oracle.col_norm(synth.calib_acts(K, 5)), N, M)
+    Wp = nm.nm_unpack(dev_u32(mref), dev_bf16(vref))
+    assert (host_bf16(Wp) == oracle.unpack(mref, vref, K)).all()
+
+
+# ------------------------------------------------------------------ SpMV
+SPMV_SHAPES = [
+    (256, 512),     # tiny workload shape
+    (1000, 4096),   # ragged row count, k/v-like split rows
+    (1024, 4096),   # k/v 8B: rows split into slices (workspace path)
+    (513, 5120),    # words per row not a multiple of 64
+    (96, 14336),    # long rows (down projection shape)
+    (17, 8192),     # few rows: many slices per row
+    (1, 32),        # smallest legal matrix
+    (3, 28672),     # longest rows, x = 56 KB
+]
+
+
+@pytest.mark.parametrize("R,K", SPMV_SHAPES)
+@pytest.mark.parametrize("B", [1, 2, 8])
+def test_spmv_within_tolerance(R, K, B):
+    say("spmv", R, K, B)
+    M = 8
+    W = synth.weights(R, K, 6, R, K)
+    mref, vref = oracle.prune_pack(W, oracle.col_norm(synth.calib_acts(K, 6, R, K)), M // 2, M)
+    x = synth.decode_x(B, K, 6, R, K, B)
+    y = nm.nm_spmv(dev_u32(mref), dev_bf16(vref), dev_bf16(x))
+    torch.cuda.synchronize()
+    yref, absum = oracle.spmv(mref, vref, x, K, nthreads=4)
+    assert_within(host_bf16(y), yref, absum, f"spmv R={R} K={K} B={B}")
+
+
+@pytest.mark.parametrize("B", [3, 4, 5, 6, 7])
+def test_spmv_every_batch_size(B):
+    say("spmv batch", B)
+    R, K = 384, 8192
+    W = synth.weights(R, K, 7, B)
+    mref, vref = oracle.prune_pack(W, oracle.col_norm(synth.calib_acts(K, 7, B)), 16, 32)
+    x = synth.decode_x(B, K, 7, B)
+    y = nm.nm_spmv(dev_u32(mref), dev_bf16(vref), dev_bf16(x))
+    yref, absum = oracle.spmv(mref, vref, x, K, nthreads=4)
+    assert_within(host_bf16(y), yref, absum, f"spmv B={B}")
+
+
+@pytest.mark.parametrize("N,M", PATTERNS)
+def test_spmv_integer_exact(N, M):
+    """Ternary weights and inputs: every partial sum is an integer <= K/2 in
+    magnitude, exact in fp32 and representable in bf16 up to 256, so the GPU result
+    must equal the oracle's bit for bit whatever the summation order."""
+    say("spmv integer exact", N, M)
+    R, K, B = 300, 512, 4
+    W = synth.ternary((R, K), 8, M)
+    x = synth.ternary((B, K), 9, M)
+    mref, vref = oracle.prune_pack(W, oracle.col_norm(synth.calib_acts(K, 8)), N, M)
+    y = nm.nm_spmv(dev_u32(mref), dev_bf16(vref), dev_bf16(x))
+    yref, _ = oracle.spmv(mref, vref, x, K)
+    assert np.abs(yref).max() <= 256
+    assert (bf16_as_f64(host_bf16(y)) == yref).all()
+
+
+def test_spmv_one_hot_reads_columns():
+    say("spmv one-hot")
+    R, K = 512, 4096
+    W = synth.weights(R, K, 10)
+    mref, vref = oracle.prune_pack(W, oracle.col_norm(synth.calib_acts(K, 10)), 2, 4)
+    Wp = oracle.unpack(mref, vref, K)
+    cols = [0, 1, 31, 32, 2047, 4095]
+    x = np.zeros((len(cols), K), np.uint16)
+    for b, j in enumerate(cols):
+        x[b, j] = 0x3F80
+    y = host_bf16(nm.nm_spmv(dev_u32(mref), dev_bf16(vref), dev_bf16(x)))
+    for b, j in enumerate(cols):
+        assert (y[b] == Wp[:, j]).all()
+
+
+def test_spmv_power_of_two_scaling_and_determinism():
+    say("spmv scaling + determinism")
+    R, K = 2048, 4096
+    W = synth.weights(R, K, 11)
+    mref, vref = oracle.prune_pack(W, oracle.col_norm(synth.calib_acts(K, 11)), 4, 8)
+    m, v = dev_u32(mref), dev_bf16(vref)
+    x = synth.decode_x(1, K, 11)
+    x4 = synth.to_bf16_bits(synth.bf16_bits_to_f32(x) * 4.0)
+    y1 = host_bf16(nm.nm_spmv(m, v, dev_bf16(x)))
+    y1b = host_bf16(nm.nm_spmv(m, v, dev_bf16(x)))
+    y4 = host_bf16(nm.nm_spmv(m, v, dev_bf16(x4)))
+    assert (y1 == y1b).all()  # run-to-run bit reproducibility (no atomics)
+    assert (bf16_as_f64(y4) == 4.0 * bf16_as_f64(y1)).all()
+
+
+def test_spmv_pattern_agnostic_kernel():
+    """Same bytes, four patterns: each result matches its own oracle."""
+    R, K = 640, 4096
+    W = synth.weights(R, K, 12)
+    n = oracle.col_norm(synth.calib_acts(K, 12))
+    x = synth.decode_x(1, K, 12)
+    for N, M in PATTERNS:
+        say("spmv pattern", N, M)
+        mref, vref = oracle.prune_pack(W, n, N, M)
+        y = nm.nm_spmv(dev_u32(mref), dev_bf16(vref), dev_bf16(x))
+        yref, absum = oracle.spmv(mref, vref, x, K)
+        assert_within(host_bf16(y), yref, absum, f"{N}:{M}")
+
+
+def test_spmv_strided_x_and_y():
+    say("spmv strided x/y")
+    R, K, B = 700, 4096, 3
+    W = synth.weights(R, K, 13)
+    mref, vref = oracle.prune_pack(W, oracle.col_norm(synth.calib_acts(K, 13)), 2, 4)
+    xfull = synth.decode_x(B, K + 64, 13)
+    xd = dev_bf16(xfull)[:, :K]
+    yfull = torch.zeros((B, R + 40), dtype=torch.bfloat16, device="cuda")
+    nm.nm_spmv(dev_u32(mref), dev_bf16(vref), xd, out=yfull[:, :R])
+    yh = host_bf16(yfull)
+    yref, absum = oracle.spmv(mref, vref, np.ascontiguousarray(xfull[:, :K]), K)
+    assert_within(yh[:, :R], yref, absum, "strided")
+    assert (yh[:, R:] == 0).all()  # nothing written past ldy's row
+
+
+def test_spmv_workspace_errors():
+    say("spmv workspace errors")
+    R, K = 1024, 4096
+    need = nm.nm_spmv_workspace_bytes(R, K, 1)
+    assert need > 0  # this shape splits rows on a 256-CU part
+    m = torch.zeros((R, K // 32), dtype=torch.int32, device="cuda")
+    v = torch.zeros((R, K // 2), dtype=torch.bfloat16, device="cuda")
+    x = torch.zeros((1, K), dtype=torch.bfloat16, device="cuda")
+    small = torch.empty(need // 4 - 1, dtype=torch.float32, device="cuda")
+    with pytest.raises(nm.NmError) as e:
+        nm.nm_spmv(m, v, x, workspace=small)
+    assert e.value.status == 5
+
+
+# ------------------------------------------------------------------ dense GEMV
+@pytest.mark.parametrize("R,K", [(256, 512), (1000, 4096), (96, 14336), (5, 28672), (1, 8), (77, 1000)])
+@pytest.mark.parametrize("B", [1, 4, 8])
+def test_dense_within_tolerance(R, K, B):
+    say("dense", R, K, B)
+    W = synth.weights(R, K, 14, R, K)
+    x = synth.decode_x(B, K, 14, R, K, B)
+    y = nm.dense_gemv(dev_bf16(W), dev_bf16(x))
+    yref, absum = oracle.dense(W, x, nthreads=4)
+    assert_within(host_bf16(y), yref, absum, f"dense R={R} K={K} B={B}")
+
+
+def test_dense_integer_exact():
+    say("dense integer exact")
+    R, K, B = 200, 256, 2
+    W = synth.ternary((R, K), 15)
+    x = synth.ternary((B, K), 16)
+    y = nm.dense_gemv(dev_bf16(W), dev_bf16(x))
+    yref, _ = oracle.dense(W, x)
+    assert (bf16_as_f64(host_bf16(y)) == yref).all()
+
+
+def test_sparse_equals_dense_of_unpacked():
+    say("spmv vs dense(unpack)")
+    R, K = 1536, 4096
+    W = synth.weights(R, K, 17)
+    X = synth.calib_acts(K, 17)
+    x = synth.decode_x(1, K, 17)
+    n = nm.nm_col_norm(dev_bf16(X))
+    masks, values = nm.nm_prune_pack(dev_bf16(W), n, 8, 16)
+    ys = host_bf16(nm.nm_spmv(masks, values, dev_bf16(x)))
+    yd = host_bf16(nm.dense_gemv(nm.nm_unpack(masks, values), dev_bf16(x)))
+    mref, vref = oracle.prune_pack(W, oracle.col_norm(X), 8, 16)
+    yref, absum = oracle.spmv(mref, vref, x, K)
+    assert_within(ys, yref, absum, "sparse")
+    assert_within(yd, yref, absum, "dense of unpacked")
+
+
+# ------------------------------------------------------------------ full-size layers
+# Llama-3.1-8B / Qwen3 / Llama-3.3-70B layer shapes, weights generated on the device,
+# packed by the GPU; a sample of rows is rebuilt by the oracle from the same inputs.
+FULL = [
+    ("8b-q", 4096, 4096, 2, 4, 1), ("8b-kv", 1024, 4096, 16, 32, 1), ("8b-up", 14336, 4096, 2, 4, 1),
+    ("8b-down", 4096, 14336, 16, 32, 1), ("14b-up", 17408, 5120, 4, 8, 1), ("32b-q", 8192, 5120, 4, 8, 1),
+    ("70b-kv", 1024, 8192, 8, 16, 8), ("70b-down", 8192, 28672, 8, 16, 1), ("70b-down-b4", 8192, 28672, 8, 16, 4),
+]
+
+
+@pytest.mark.parametrize("name,R,K,N,M,B", FULL, ids=[f[0] for f in FULL])
+def test_full_size_sampled(name, R, K, N, M, B):
+    say("full", name, R, K, N, M, B)
+    Wd = synth.device_weights(R, K, 0, R, K)
+    Xd = synth.device_calib_acts(K, 0, K)
+    xd = synth.device_decode_x(B, K, 0, K, B)
+    n = nm.nm_col_norm(Xd)
+    masks, values = nm.nm_prune_pack(Wd, n, N, M)
+    y = nm.nm_spmv(masks, values, xd)
+    yd = nm.dense_gemv(Wd, xd)
+    torch.cuda.synchronize()
+    nref = oracle.col_norm(host_bf16(Xd))
+    assert (host_f32(n).view(np.uint32) == nref.view(np.uint32)).all()
+    g = np.random.default_rng(R * 7 + K)
+    rows = np.unique(np.concatenate([[0, R - 1], g.choice(R, size=min(R, 192), replace=False)]))
+    ridx = torch.from_numpy(rows).cuda()
+    Ws = host_bf16(Wd.index_select(0, ridx))
+    ms, vs = oracle.prune_pack(Ws, nref, N, M)
+    assert (host_u32(masks.index_select(0, ridx)) == ms).all()
+    assert (host_bf16(values.index_select(0, ridx)) == vs).all()
+    xh = host_bf16(xd)
+    yref, absum = oracle.spmv(ms, vs, xh, K, nthreads=4)
+    assert_within(host_bf16(y)[:, rows], yref, absum, f"{name} sparse")
+    ydref, adabs = oracle.dense(Ws, xh, nthreads=4)
+    assert_within(host_bf16(yd)[:, rows], ydref, adabs, f"{name} dense")
