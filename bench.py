@@ -1,0 +1,393 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the N:M bitmask SpMV against the same-GPU dense bf16 GEMV.
+
+A step is one decode token (batch B, default 1) through a stack of synthetic decoder
+layers -- every projection of every layer is one nm_spmv call on its own packed
+weights -- for each N:M pattern of the workload.  The dense baseline runs the same
+stack with dense_gemv on the unpruned weights.  Inputs are generated and packed on
+the GPU before the timed region (column norms -> N:M select + pack), spot-checked
+against the CPU oracle, and every timed launch reads weights already resident in HBM.
+
+Printed (one JSON line on stdout): aggregate effective GB/s of the sparse step
+(algorithmic bytes: packed values + masks + x + y per call), a per-projection table
+(us, GB/s, % of the 8 TB/s HBM peak, dense us, speedup, hipBLASLt us), the roofline
+of the dominant kernel and the CPU oracle timed on the host cores.
+
+Cache defeat: every per-projection timing rotates over >= 512 MB of distinct buffers
+(twice the 256 MB Infinity Cache), and the step itself walks all layers of all
+patterns in decode order (several GB between reuses).
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config 8b] [--layers 8]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+ROTATE_BYTES = 512e6
+METRIC = "nm_spmv GB/s and % HBM peak per layer; speedup vs dense bf16 GEMV, batch 1"
+
+# Layer shapes (rows R = outputs, K = inputs) of the models the pages evaluate.
+# group = which activation feeds the projection (projections of one group share x).
+CONFIGS = {
+    "tiny": dict(workload="tiny: one 256x512 matrix, 2:4", batch=(1,),
+                 projs=[("w", 256, 512, "in")], patterns=[(2, 4)]),
+    "8b": dict(workload="Llama-3.1-8B-shaped decode layer set, 2:4 and 16:32",
+               projs=[("q", 4096, 4096, "attn"), ("k", 1024, 4096, "attn"), ("v", 1024, 4096, "attn"),
+                      ("o", 4096, 4096, "attn_out"), ("gate", 14336, 4096, "mlp"), ("up", 14336, 4096, "mlp"),
+                      ("down", 4096, 14336, "mlp_mid")],
+               patterns=[(2, 4), (16, 32)], batch=(1,)),
+    "8b-sweep": dict(workload="Llama-3.1-8B-shaped decode layer set, all four 50% patterns",
+                     projs=None, patterns=[(2, 4), (4, 8), (8, 16), (16, 32)], batch=(1,), base="8b"),
+    "qwen14b": dict(workload="Qwen3-14B-shaped layers, 4:8",
+                    projs=[("q", 5120, 5120, "attn"), ("gate", 17408, 5120, "mlp"), ("up", 17408, 5120, "mlp"),
+                           ("down", 5120, 17408, "mlp_mid")], patterns=[(4, 8)], batch=(1,)),
+    "qwen32b": dict(workload="Qwen3-32B-shaped layers, 4:8",
+                    projs=[("q", 8192, 5120, "attn"), ("gate", 25600, 5120, "mlp"), ("up", 25600, 5120, "mlp"),
+                           ("down", 5120, 25600, "mlp_mid")], patterns=[(4, 8)], batch=(1,)),
+    "70b": dict(workload="Llama-3.3-70B-shaped single-GPU layers, 8:16",
+                projs=[("q", 8192, 8192, "attn"), ("k", 1024, 8192, "attn"), ("v", 1024, 8192, "attn"),
+                       ("o", 8192, 8192, "attn_out"), ("gate", 28672, 8192, "mlp"), ("up", 28672, 8192, "mlp"),
+                       ("down", 8192, 28672, "mlp_mid")], patterns=[(8, 16)], batch=(1, 2, 4, 8)),
+}
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def sparse_bytes(R, K, B):
+    """Algorithmic bytes of one nm_spmv call: values R*K + masks R*K/8 + x 2BK + y 2BR."""
+    return R * K + R * K // 8 + 2 * B * K + 2 * B * R
+
+
+def dense_bytes(R, K, B):
+    return 2 * R * K + 2 * B * K + 2 * B * R
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="8b", choices=sorted(CONFIGS))
+    ap.add_argument("--layers", type=int, default=8, help="decoder layers of distinct buffers in a step")
+    ap.add_argument("--batch", type=int, default=1, help="tokens per step (B)")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-reps", type=int, default=12)
+    ap.add_argument("--skip-check", action="store_true", help="skip the oracle spot check")
+    return ap.parse_args()
+
+
+class Timer:
+    """HIP events on the current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def time_graph(self, g, reps):
+        t = self.torch
+        e0, e1 = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        t.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps  # ms per replay
+
+
+def capture(torch, fns):
+    """Capture a list of launches into one HIP graph (launch overhead off the clock)."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for f in fns:  # eager pass: first-call setup happens outside the capture
+            f()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    return g
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import bitmask_spmv_amd as nm
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a HIP GPU"
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    cfg = dict(CONFIGS[args.config])
+    if cfg.get("projs") is None:
+        cfg["projs"] = CONFIGS[cfg["base"]]["projs"]
+    B = args.batch
+    L = args.layers
+    projs, patterns = cfg["projs"], cfg["patterns"]
+    props = torch.cuda.get_device_properties(0)
+    log(f"device {props.name} CUs={props.multi_processor_count} config={args.config} layers={L} B={B}")
+
+    # ---------------------------------------------------------------- inputs
+    # Per projection a pool of distinct weight buffers of >= 512 MB (and >= L); the
+    # step uses the first L of each pool as the L decoder layers.
+    t0 = time.time()
+    pool_sparse = {}  # (pattern, proj) -> list of (masks, values)
+    pool_dense = {}   # proj -> list of W
+    pack_ms = 0.0
+    pack_bytes = 0
+    norm_ms = 0.0
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for pi, (name, R, K, group) in enumerate(projs):
+        ns = max(L, math.ceil(ROTATE_BYTES / sparse_bytes(R, K, B)))
+        nd = max(L, math.ceil(ROTATE_BYTES / dense_bytes(R, K, B)))
+        for (N, M) in patterns:
+            pool_sparse[(N, M), name] = []
+        pool_dense[name] = []
+        for c in range(max(ns, nd)):
+            W = synth.device_weights(R, K, args.seed, 100 + pi, c)
+            X = synth.device_calib_acts(K, args.seed, 200 + pi, c)
+            ev0.record()
+            n = nm.nm_col_norm(X)
+            ev1.record()
+            torch.cuda.synchronize()
+            norm_ms += ev0.elapsed_time(ev1)
+            for (N, M) in patterns:
+                if c < ns:
+                    ev0.record()
+                    pk = nm.nm_prune_pack(W, n, N, M)
+                    ev1.record()
+                    torch.cuda.synchronize()
+                    pack_ms += ev0.elapsed_time(ev1)
+                    pack_bytes += 2 * R * K + sparse_bytes(R, K, 0)
+                    pool_sparse[(N, M), name].append(pk)
+            if c < nd:
+                pool_dense[name].append(W)
+            del X, n
+    xs = {}
+    for gi, group in enumerate(sorted({p[3] for p in projs})):
+        K = [p[2] for p in projs if p[3] == group][0]
+        xs[group] = [synth.device_decode_x(B, K, args.seed, 300 + gi, l) for l in range(L)]
+    ys = {name: torch.empty((B, R), dtype=torch.bfloat16, device=dev) for name, R, K, _ in projs}
+    ws_bytes = max([nm.nm_spmv_workspace_bytes(R, K, B) for _, R, K, _ in projs]
+                   + [nm.dense_gemv_workspace_bytes(R, K, B) for _, R, K, _ in projs] + [4])
+    ws = torch.empty((ws_bytes + 3) // 4, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    log(f"inputs generated and packed in {time.time() - t0:.1f}s "
+        f"(pack {pack_bytes / pack_ms / 1e6:.0f} GB/s, col_norm {norm_ms:.2f} ms total)")
+
+    # ---------------------------------------------------------------- oracle spot check
+    parity = "skipped"
+    if not args.skip_check:
+        import oracle
+
+        def host_u16(t):
+            return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+        g = np.random.default_rng(args.seed)
+        for pi, (name, R, K, group) in enumerate(projs):
+            rows = np.unique(np.concatenate([[0, R - 1], g.choice(R, size=min(R, 6), replace=False)]))
+            ridx = torch.from_numpy(rows).to(dev)
+            W = pool_dense[name][0]
+            X = synth.device_calib_acts(K, args.seed, 200 + pi, 0)
+            nref = oracle.col_norm(host_u16(X))
+            assert (nm.nm_col_norm(X).cpu().numpy().view(np.uint32) == nref.view(np.uint32)).all(), "col_norm"
+            Ws = host_u16(W.index_select(0, ridx))
+            x = xs[group][0]
+            xh = host_u16(x)
+            for (N, M) in patterns:
+                masks, values = pool_sparse[(N, M), name][0]
+                mref, vref = oracle.prune_pack(Ws, nref, N, M)
+                assert (masks.index_select(0, ridx).cpu().numpy().view(np.uint32) == mref).all(), f"masks {name}"
+                assert (host_u16(values.index_select(0, ridx)) == vref).all(), f"values {name}"
+                y = nm.nm_spmv(masks, values, x, workspace=ws)
+                yref, absum = oracle.spmv(mref, vref, xh, K)
+                yg = (host_u16(y)[:, rows].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+                assert oracle.within_tolerance(yg, yref, absum).all(), f"spmv {name} {N}:{M}"
+            yd = nm.dense_gemv(W, x, workspace=ws)
+            ydref, dabs = oracle.dense(Ws, xh)
+            ydg = (host_u16(yd)[:, rows].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+            assert oracle.within_tolerance(ydg, ydref, dabs).all(), f"dense {name}"
+        parity = "ok"
+        log("oracle spot check ok (col_norm, masks, values bit-exact; spmv/dense within tolerance)")
+
+    # ---------------------------------------------------------------- step graphs
+    def spmv_call(pk, x, y):
+        m, v = pk
+        return lambda: nm.nm_spmv(m, v, x, out=y, workspace=ws)
+
+    def dense_call(W, x, y):
+        return lambda: nm.dense_gemv(W, x, out=y, workspace=ws)
+
+    sparse_fns, dense_fns = [], []
+    step_sparse_bytes = 0
+    step_dense_bytes = 0
+    for (N, M) in patterns:
+        for l in range(L):
+            for name, R, K, group in projs:
+                sparse_fns.append(spmv_call(pool_sparse[(N, M), name][l], xs[group][l], ys[name]))
+                step_sparse_bytes += sparse_bytes(R, K, B)
+    for l in range(L):
+        for name, R, K, group in projs:
+            dense_fns.append(dense_call(pool_dense[name][l], xs[group][l], ys[name]))
+            step_dense_bytes += dense_bytes(R, K, B)
+    g_sparse = capture(torch, sparse_fns)
+    g_dense = capture(torch, dense_fns)
+    timer = Timer(torch)
+
+    for _ in range(args.warmup):
+        g_sparse.replay()
+        g_dense.replay()
+    torch.cuda.synchronize()
+    ms_sparse = timer.time_graph(g_sparse, args.steps)
+    ms_dense = timer.time_graph(g_dense, args.steps)
+    log(f"step: sparse {ms_sparse * 1e3:.1f} us ({len(sparse_fns)} launches), dense {ms_dense * 1e3:.1f} us "
+        f"({len(dense_fns)} launches, {len(patterns)} pattern(s) share it)")
+
+    # ---------------------------------------------------------------- per projection
+    per = {}
+    reps = 3
+    for (N, M) in patterns:
+        for name, R, K, group in projs:
+            pool = pool_sparse[(N, M), name]
+            fns = [spmv_call(pk, xs[group][i % L], ys[name]) for i, pk in enumerate(pool)]
+            g = capture(torch, fns)
+            g.replay()
+            us = min(timer.time_graph(g, 1) for _ in range(reps)) * 1e3 / len(fns)
+            per.setdefault(name, {"R": R, "K": K})[f"{N}:{M}"] = {
+                "us": round(us, 2), "GBs": round(sparse_bytes(R, K, B) / us / 1e3, 1),
+                "pct_peak": round(100 * sparse_bytes(R, K, B) / us / 1e3 / HBM_PEAK_GBS, 1),
+                "rotation_MB": round(len(fns) * sparse_bytes(R, K, B) / 1e6)}
+            del g
+    for name, R, K, group in projs:
+        pool = pool_dense[name]
+        fns = [dense_call(W, xs[group][i % L], ys[name]) for i, W in enumerate(pool)]
+        g = capture(torch, fns)
+        g.replay()
+        us = min(timer.time_graph(g, 1) for _ in range(reps)) * 1e3 / len(fns)
+        lin = [(lambda W=W, x=xs[group][i % L]: torch.nn.functional.linear(x, W)) for i, W in enumerate(pool)]
+        gl = capture(torch, lin)
+        gl.replay()
+        us_lin = min(timer.time_graph(gl, 1) for _ in range(reps)) * 1e3 / len(lin)
+        d = per[name]
+        d["dense_us"] = round(us, 2)
+        d["dense_GBs"] = round(dense_bytes(R, K, B) / us / 1e3, 1)
+        d["hipblaslt_us"] = round(us_lin, 2)
+        for (N, M) in patterns:
+            d[f"{N}:{M}"]["speedup_vs_dense"] = round(us / d[f"{N}:{M}"]["us"], 3)
+            d[f"{N}:{M}"]["speedup_vs_hipblaslt"] = round(us_lin / d[f"{N}:{M}"]["us"], 3)
+        del g, gl
+    torch.cuda.synchronize()
+
+    # Dominant kernel: the launch shape (R x K) whose launches take the largest share of
+    # the step (projections of equal shape, e.g. gate and up, are one launch shape).
+    share = {}
+    for name, R, K, _ in projs:
+        share[(R, K)] = share.get((R, K), 0.0) + sum(per[name][f"{N}:{M}"]["us"] for (N, M) in patterns)
+    dR, dK = max(share, key=share.get)
+    dom_names = [name for name, R, K, _ in projs if (R, K) == (dR, dK)]
+    dom = dom_names[0]
+    dom_us = sum(per[n][f"{N}:{M}"]["us"] for n in dom_names for (N, M) in patterns) / (len(dom_names) * len(patterns))
+    dom_bytes = sparse_bytes(dR, dK, B)
+    achieved = dom_bytes / dom_us / 1e3  # GB/s
+    traffic = None
+    tf = os.path.join(ROOT, "profiles", "traffic.json")
+    if os.path.exists(tf):
+        try:
+            with open(tf) as f:
+                tj = json.load(f)
+            key = f"{args.config}:{dom}:B{B}"
+            if key in tj and tj[key].get("kernel_sha") == kernel_fingerprint():
+                traffic = tj[key]["bytes_per_launch"]
+        except (OSError, ValueError, KeyError):
+            traffic = None
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": f"nm_spmv on {'/'.join(dom_names)} {dR}x{dK}, B={B}", "algorithmic_bytes_per_launch": dom_bytes,
+                "avg_launch_us": round(dom_us, 3)}
+
+    # ---------------------------------------------------------------- CPU oracle baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        cores = len(os.sched_getaffinity(0))
+        (N, M) = patterns[0]
+        host = []
+        sb = 0
+        for name, R, K, group in projs:
+            masks, values = pool_sparse[(N, M), name][0]
+            host.append((masks.cpu().numpy().view(np.uint32), values.contiguous().view(torch.int16).cpu().numpy()
+                         .view(np.uint16), xs[group][0].contiguous().view(torch.int16).cpu().numpy().view(np.uint16), K))
+            sb += sparse_bytes(R, K, B)
+        t1 = time.time()
+        for _ in range(args.cpu_reps):
+            for m_h, v_h, x_h, K in host:
+                oracle.spmv(m_h, v_h, x_h, K, nthreads=cores)
+        dt = time.time() - t1
+        cpu = {"value": round(sb * args.cpu_reps / dt / 1e9, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
+               "sample": f"layer 0 of the set ({', '.join(p[0] for p in projs)}), {N}:{M}, B={B}, "
+                         f"x{args.cpu_reps} reps, {dt:.1f}s wall"}
+
+    value = step_sparse_bytes / (ms_sparse * 1e-3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_sparse, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg["workload"], "layers": L, "batch": B,
+                   "patterns": [f"{N}:{M}" for N, M in patterns], "parallelism": "single GPU"},
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1),
+        "dense_ms_per_step": round(ms_dense, 4),
+        "dense_GBs": round(step_dense_bytes / (ms_dense * 1e-3) / 1e9, 1),
+        "step_speedup_vs_dense": round(ms_dense * len(patterns) / ms_sparse, 3),
+        "per_layer": per,
+        "pack_GBs": round(pack_bytes / pack_ms / 1e6, 1),
+        "parity": parity,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def kernel_fingerprint() -> str:
+    """Hash of the SpMV kernel source: counters recorded for an older kernel are not reused."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in ("nm_spmv.hip", "nm_device.h"):
+        with open(os.path.join(ROOT, "bitmask_spmv_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+if __name__ == "__main__":
+    main()

@@ -36,10 +36,7 @@ def sources():
 def _compile(src: str) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *COMMON]
-    if src.endswith(".hip"):
-        cmd += ["-x", "hip", *HIP_FLAGS]
-    cmd += ["-c", src, "-o", obj]
+    cmd = [_hipcc(), *COMMON, "-x", "hip", *HIP_FLAGS, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

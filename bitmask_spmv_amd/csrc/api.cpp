@@ -9,7 +9,7 @@
 #include <cstdlib>
 #include <cstring>
 
-#include "../../include/nm_spmv.h"
+#include "nm_spmv.h"
 #include "nm_kernels.h"
 
 namespace {

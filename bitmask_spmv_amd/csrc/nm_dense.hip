@@ -27,6 +27,59 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
 }
 
+template <int U>
+struct DBatch {
+    u32x4 w[U];
+    int lc[U];
+};
+
+// One batch of U 16-byte chunks per lane through a raw buffer descriptor covering the
+// row slice's `chunks` chunks (0 = nothing to load; the loads return zeros).
+template <int U>
+__device__ __forceinline__ void load_dbatch(DBatch<U> &bt, const u32x4 *wrow, int chunks, int base, int lane) {
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(wrow, (int64_t)chunks * 16);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int c = base + u * kWave + lane;
+        bt.w[u] = __builtin_amdgcn_raw_buffer_load_b128(rw, c * 16, 0, kLoadNT);
+        bt.lc[u] = c;
+    }
+}
+
+template <int B, int U>
+__device__ __forceinline__ void dot_dbatch(const DBatch<U> &bt, const u32x4 *xs4, int ncs, float (&acc)[B]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int lc = bt.lc[u] < ncs ? bt.lc[u] : 0;  // padding lanes carry zero weights
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            const u32x4 xv = xs4[b * ncs + lc];
+            float a = acc[b];
+            a = dot2_bf16(bt.w[u].x, xv.x, a);
+            a = dot2_bf16(bt.w[u].y, xv.y, a);
+            a = dot2_bf16(bt.w[u].z, xv.z, a);
+            a = dot2_bf16(bt.w[u].w, xv.w, a);
+            acc[b] = a;
+        }
+    }
+}
+
+template <int B>
+__device__ __forceinline__ void finish_drow(float (&acc)[B], int row, int s, int R, int lane, uint16_t *y,
+                                            int64_t ldy, float *partial) {
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+        const float tot = wave_sum(acc[b]);
+        acc[b] = 0.f;
+        if (lane == 0) {
+            if (gridDim.y == 1)
+                y[(int64_t)b * ldy + row] = f32_to_bf16_rne(tot);
+            else
+                partial[((int64_t)s * B + b) * R + row] = tot;
+        }
+    }
+}
+
 template <int B, int U>
 __global__ __launch_bounds__(kThreads) void dense_kernel(const u32x4 *__restrict__ W, int64_t ldw8, int R, int KC,
                                                          const uint16_t *__restrict__ x, int64_t ldx,
@@ -36,55 +89,68 @@ __global__ __launch_bounds__(kThreads) void dense_kernel(const u32x4 *__restrict
     const int s = blockIdx.y;
     const int c0 = s * slice;
     const int ncs = min(slice, KC - c0);
-    for (int i = threadIdx.x; i < B * ncs; i += kThreads) {
-        const int b = i / ncs;
-        const int c = i - b * ncs;
-        xs4[i] = reinterpret_cast<const u32x4 *>(x + (int64_t)b * ldx)[c0 + c];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    constexpr int kWaves = kThreads / kWave;
+
+    // Same flat, software-pipelined walk over (row, batch) as the sparse kernel.
+    const int first_row = blockIdx.x * kWaves + wave;
+    const int row_step = gridDim.x * kWaves;
+    const int nb = (ncs + kWave * U - 1) / (kWave * U);
+    const int my_rows = first_row < R ? (R - 1 - first_row) / row_step + 1 : 0;
+    const int total = my_rows * nb;
+
+    DBatch<U> bufA, bufB;
+    int rowA = first_row, biA = 0, rowB = first_row, biB = 0;
+    load_dbatch<U>(bufA, W + (int64_t)min(rowA, R - 1) * ldw8 + c0, total > 0 ? ncs : 0, 0, lane);
+
+    {
+        constexpr int kStage = 4;
+        const int chunks = B * ncs;
+        for (int i0 = 0; i0 < chunks; i0 += kThreads * kStage) {
+            u32x4 r[kStage];
+#pragma unroll
+            for (int j = 0; j < kStage; ++j) {
+                const int i = i0 + j * kThreads + (int)threadIdx.x;
+                if (i < chunks) {
+                    const int b = i / ncs;
+                    r[j] = reinterpret_cast<const u32x4 *>(x + (int64_t)b * ldx)[c0 + (i - b * ncs)];
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < kStage; ++j) {
+                const int i = i0 + j * kThreads + (int)threadIdx.x;
+                if (i < chunks) xs4[i] = r[j];
+            }
+        }
     }
     __syncthreads();
 
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
-    constexpr int kWaves = kThreads / kWave;
-    for (int row = blockIdx.x * kWaves + wave; row < R; row += gridDim.x * kWaves) {
-        const u32x4 *wrow = W + (int64_t)row * ldw8 + c0;
-        float acc[B];
+    float acc[B];
 #pragma unroll
-        for (int b = 0; b < B; ++b) acc[b] = 0.f;
-        for (int base = 0; base < ncs; base += kWave * U) {
-            u32x4 wv[U];
-            int lc[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int c = base + u * kWave + lane;
-                const bool ok = c < ncs;
-                wv[u] = ok ? __builtin_nontemporal_load(wrow + c) : u32x4{0u, 0u, 0u, 0u};
-                lc[u] = ok ? c : 0;
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-#pragma unroll
-                for (int b = 0; b < B; ++b) {
-                    const u32x4 xv = xs4[b * ncs + lc[u]];
-                    float a = acc[b];
-                    a = dot2_bf16(wv[u].x, xv.x, a);
-                    a = dot2_bf16(wv[u].y, xv.y, a);
-                    a = dot2_bf16(wv[u].z, xv.z, a);
-                    a = dot2_bf16(wv[u].w, xv.w, a);
-                    acc[b] = a;
-                }
-            }
+    for (int b = 0; b < B; ++b) acc[b] = 0.f;
+    for (int t = 0; t < total; t += 2) {
+        rowB = rowA;
+        biB = biA + 1;
+        if (biB == nb) {
+            biB = 0;
+            rowB += row_step;
         }
-#pragma unroll
-        for (int b = 0; b < B; ++b) {
-            const float t = wave_sum(acc[b]);
-            if (lane == 0) {
-                if (gridDim.y == 1)
-                    y[(int64_t)b * ldy + row] = f32_to_bf16_rne(t);
-                else
-                    partial[((int64_t)s * B + b) * R + row] = t;
-            }
+        load_dbatch<U>(bufB, W + (int64_t)min(rowB, R - 1) * ldw8 + c0, t + 1 < total ? ncs : 0, biB * kWave * U,
+                       lane);
+        dot_dbatch<B, U>(bufA, xs4, ncs, acc);
+        if (biA == nb - 1) finish_drow<B>(acc, rowA, s, R, lane, y, ldy, partial);
+        if (t + 1 >= total) break;
+        rowA = rowB;
+        biA = biB + 1;
+        if (biA == nb) {
+            biA = 0;
+            rowA += row_step;
         }
+        load_dbatch<U>(bufA, W + (int64_t)min(rowA, R - 1) * ldw8 + c0, t + 2 < total ? ncs : 0, biA * kWave * U,
+                       lane);
+        dot_dbatch<B, U>(bufB, xs4, ncs, acc);
+        if (biB == nb - 1) finish_drow<B>(acc, rowB, s, R, lane, y, ldy, partial);
     }
 }
 
@@ -151,11 +217,13 @@ MvPlan plan_dense(int64_t R, int64_t K, int B, const DeviceInfo &dev) {
     int64_t max_slice = (int64_t)cap / bytes_per_chunk;
     if (max_slice >= kWave) max_slice -= max_slice % kWave;
     if (max_slice < 1) max_slice = 1;
+    // Split rows across workgroups only when the matrix has too few rows to give
+    // every CU a couple of waves: the split costs a second launch, which outweighs
+    // the extra parallelism on anything but very short, wide matrices.
     const int64_t cu = dev.num_cu > 0 ? dev.num_cu : 256;
-    const int64_t want_tasks = cu * 16;
+    const int64_t want_rows = cu * 2;
     int64_t splits = (KC + max_slice - 1) / max_slice;
-    int64_t by_tasks = (want_tasks + R - 1) / R;
-    // no slice shorter than four wave iterations (4 KiB of a row per wave)
+    int64_t by_tasks = R >= want_rows ? 1 : (want_rows + R - 1) / R;
     int64_t max_by_len = KC / (4 * kWave) > 0 ? KC / (4 * kWave) : 1;
     if (by_tasks > max_by_len) by_tasks = max_by_len;
     if (splits < by_tasks) splits = by_tasks;

@@ -11,6 +11,16 @@ constexpr int kWave = 64;  // CDNA wavefront width
 // Native 4 x 32-bit vector (16-byte global / LDS accesses, non-temporal builtins).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// Raw buffer resources: loads past num_records return zero without touching memory,
+// so a wave can always issue the same number of loads (the in-order vmcnt counter
+// then lets one batch be awaited while the next is still in flight).
+constexpr int kRsrcWord3 = 0x00020000;  // gfx9 raw (untyped) buffer descriptor word 3
+constexpr int kLoadNT = 2;              // cache policy: non-temporal (streamed once)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+
 // bf16 pattern -> fp32 (exact: bf16 is the upper half of binary32).
 __device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
@@ -77,11 +87,25 @@ __device__ __forceinline__ double sqrt_rn_f64(double s) {
     return r;
 }
 
-// Sum over the 64 lanes of a wavefront; every lane receives the total.
+// Sum over the 64 lanes of a wavefront, returned in every lane.  Four DPP steps
+// (quad swaps, half-row and row mirrors) leave each 16-lane row holding its row sum;
+// the four row sums are then read out and added in a fixed order, so the result does
+// not depend on timing.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_add(float v) {
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) v += __shfl_xor(v, off, kWave);
-    return v;
+    v = dpp_add<0xB1>(v);   // quad_perm(1,0,3,2)
+    v = dpp_add<0x4E>(v);   // quad_perm(2,3,0,1)
+    v = dpp_add<0x141>(v);  // row_half_mirror
+    v = dpp_add<0x140>(v);  // row_mirror
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return (r0 + r1) + (r2 + r3);
 }
 
 }  // namespace nmk

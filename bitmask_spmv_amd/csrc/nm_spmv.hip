@@ -43,6 +43,102 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
 }
 
+// One wave-iteration batch: U consecutive 64-word strips of one row slice, per lane one
+// mask word and its 16 packed values (two 16-byte loads).
+template <int U>
+struct Batch {
+    uint32_t m[U];
+    u32x4 va[U], vb[U];
+    int lw[U];
+};
+
+// Loads one batch through raw buffer descriptors covering the row slice's `words`
+// words (0 = nothing to load: the loads still issue and return zeros, as do lanes
+// past the end of the slice).
+//
+// Lane mapping of a 64-word strip: each 16-byte value load is contiguous across the
+// wave (lane l reads chunk l of the strip's first KiB, then chunk l of its second
+// KiB), which halves the cache lines each load instruction touches compared with one
+// lane reading a whole 32-byte word.  A quad-permute then swaps halves between lane
+// pairs so that lane 2i ends up with word i and lane 2i+1 with word 32+i; each lane
+// also loads its own word's mask.
+template <int U>
+__device__ __forceinline__ void load_batch(Batch<U> &bt, const uint32_t *mrow, const u32x4 *vrow, int words,
+                                           int base, int lane) {
+    const __amdgpu_buffer_rsrc_t rm = make_rsrc(mrow, (int64_t)words * 4);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vrow, (int64_t)words * 32);
+    const int my_word = (lane & 1) ? 32 + (lane >> 1) : (lane >> 1);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int s0 = base + u * kWave;  // first word of the strip
+        bt.m[u] = __builtin_amdgcn_raw_buffer_load_b32(rm, (s0 + my_word) * 4, 0, kLoadNT);
+        bt.va[u] = __builtin_amdgcn_raw_buffer_load_b128(rv, s0 * 32 + lane * 16, 0, kLoadNT);
+        bt.vb[u] = __builtin_amdgcn_raw_buffer_load_b128(rv, s0 * 32 + 1024 + lane * 16, 0, kLoadNT);
+        bt.lw[u] = s0 + my_word;
+    }
+}
+
+// Swap one dword with the neighbouring lane of the pair (lane ^ 1).
+__device__ __forceinline__ uint32_t pair_swap(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);  // quad_perm(1,0,3,2)
+}
+
+// The fixed 16-step walk of each mask word: lowest set bit -> column, clear it.
+template <int B, int U>
+__device__ __forceinline__ void walk_batch(const Batch<U> &bt, const uint16_t *xs16, int plane, int nws,
+                                           float (&acc)[B]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        // A padding lane (past the slice) holds zero values: walk 16 fixed columns of
+        // block 0 so every LDS address stays inside the staged x.
+        const bool ok = bt.lw[u] < nws;
+        const int lw = ok ? bt.lw[u] : 0;
+        // Reassemble this lane's 16 values (see load_batch): even lanes keep their first
+        // chunk and receive the partner's first chunk; odd lanes receive the partner's
+        // second chunk and keep their own second chunk.
+        const bool odd = threadIdx.x & 1;
+        const uint32_t s_x = odd ? bt.va[u].x : bt.vb[u].x, s_y = odd ? bt.va[u].y : bt.vb[u].y;
+        const uint32_t s_z = odd ? bt.va[u].z : bt.vb[u].z, s_w = odd ? bt.va[u].w : bt.vb[u].w;
+        const uint32_t r_x = pair_swap(s_x), r_y = pair_swap(s_y), r_z = pair_swap(s_z), r_w = pair_swap(s_w);
+        const uint32_t v[8] = {odd ? r_x : bt.va[u].x, odd ? r_y : bt.va[u].y,
+                               odd ? r_z : bt.va[u].z, odd ? r_w : bt.va[u].w,
+                               odd ? bt.vb[u].x : r_x, odd ? bt.vb[u].y : r_y,
+                               odd ? bt.vb[u].z : r_z, odd ? bt.vb[u].w : r_w};
+        const uint16_t *xw = xs16 + 2 * lw * kXPad;  // this word's 32 columns
+        uint32_t mm = ok ? bt.m[u] : 0xFFFFu;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int c0 = __builtin_ctz(mm);
+            mm &= mm - 1;
+            const int c1 = __builtin_ctz(mm);
+            mm &= mm - 1;
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                const uint16_t *xp = xw + 2 * b * plane;
+                const uint32_t pr = (uint32_t)xp[c0] | ((uint32_t)xp[c1] << 16);
+                acc[b] = dot2_bf16(v[k], pr, acc[b]);
+            }
+        }
+    }
+}
+
+// Row finished: wave reduction, then either the bf16 result or this slice's fp32 partial.
+template <int B>
+__device__ __forceinline__ void finish_row(float (&acc)[B], int row, int s, int R, int lane, uint16_t *y,
+                                           int64_t ldy, float *partial) {
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+        const float tot = wave_sum(acc[b]);
+        acc[b] = 0.f;
+        if (lane == 0) {
+            if (gridDim.y == 1)
+                y[(int64_t)b * ldy + row] = f32_to_bf16_rne(tot);
+            else
+                partial[((int64_t)s * B + b) * R + row] = tot;
+        }
+    }
+}
+
 template <int B, int U>
 __global__ __launch_bounds__(kThreads) void spmv_kernel(const uint32_t *__restrict__ masks,
                                                         const u32x4 *__restrict__ values, int R, int KW,
@@ -54,72 +150,95 @@ __global__ __launch_bounds__(kThreads) void spmv_kernel(const uint32_t *__restri
     const int w0 = s * slice;
     const int nws = min(slice, KW - w0);
     const int plane = nws * kXPad;
-
-    // Stage this slice of x (B tokens) into LDS.
-    for (int i = threadIdx.x; i < B * nws * 16; i += kThreads) {
-        const int b = i / (nws * 16);
-        const int r = i - b * nws * 16;
-        const uint32_t *xb = reinterpret_cast<const uint32_t *>(x + (int64_t)b * ldx) + (int64_t)w0 * 16;
-        xs[b * plane + (r >> 4) * kXPad + (r & 15)] = xb[r];
-    }
-    __syncthreads();
-
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
+    // wave-uniform by construction; readfirstlane lets the compiler keep the row loop
+    // in scalar registers and branch on it without exec masking
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     constexpr int kWaves = kThreads / kWave;
-    const uint16_t *xs16 = reinterpret_cast<const uint16_t *>(xs);
 
-    for (int row = blockIdx.x * kWaves + wave; row < R; row += gridDim.x * kWaves) {
-        const uint32_t *mrow = masks + (int64_t)row * KW + w0;
-        const u32x4 *vrow = values + ((int64_t)row * KW + w0) * 2;
-        float acc[B];
-#pragma unroll
-        for (int b = 0; b < B; ++b) acc[b] = 0.f;
+    // This wave's rows: first_row, first_row + row_step, ...; each row slice is cut
+    // into nb batches, walked as one flat sequence so the next batch's loads are in
+    // flight while the current one is computed, across row boundaries too.
+    const int first_row = blockIdx.x * kWaves + wave;
+    const int row_step = gridDim.x * kWaves;
+    const int nb = (nws + kWave * U - 1) / (kWave * U);
+    const int my_rows = first_row < R ? (R - 1 - first_row) / row_step + 1 : 0;
+    const int total = my_rows * nb;
 
-        for (int base = 0; base < nws; base += kWave * U) {
-            uint32_t m[U];
-            u32x4 va[U], vb[U];
-            int lw[U];
+    // Two batch buffers used in turn (no register copies, so the wait for one batch
+    // never covers the loads of the other).
+    Batch<U> bufA, bufB;
+    int rowA = first_row, biA = 0, rowB = first_row, biB = 0;
+    load_batch<U>(bufA, masks + (int64_t)min(rowA, R - 1) * KW + w0, values + ((int64_t)min(rowA, R - 1) * KW + w0) * 2,
+                  total > 0 ? nws : 0, 0, lane);
+
+    // Stage this slice of x (B tokens) into LDS with 16-byte loads, all issued before
+    // the first LDS store; 8 bf16 per chunk, 4 chunks per 32-column block.
+    {
+        constexpr int kStage = 4;
+        const int chunks = B * nws * 4;
+        for (int i0 = 0; i0 < chunks; i0 += kThreads * kStage) {
+            u32x4 r[kStage];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int w = base + u * kWave + lane;
-                const bool ok = w < nws;
-                // Lanes past the end walk a dummy word: 16 low bits set, zero values.
-                m[u] = ok ? __builtin_nontemporal_load(mrow + w) : 0xFFFFu;
-                va[u] = ok ? __builtin_nontemporal_load(vrow + 2 * w) : u32x4{0u, 0u, 0u, 0u};
-                vb[u] = ok ? __builtin_nontemporal_load(vrow + 2 * w + 1) : u32x4{0u, 0u, 0u, 0u};
-                lw[u] = ok ? w : 0;
+            for (int j = 0; j < kStage; ++j) {
+                const int i = i0 + j * kThreads + (int)threadIdx.x;
+                if (i < chunks) {
+                    const int b = i / (nws * 4);
+                    const int c = i - b * nws * 4;
+                    r[j] = reinterpret_cast<const u32x4 *>(x + (int64_t)b * ldx + (int64_t)w0 * 32)[c];
+                }
             }
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const uint32_t v[8] = {va[u].x, va[u].y, va[u].z, va[u].w, vb[u].x, vb[u].y, vb[u].z, vb[u].w};
-                const uint16_t *xw = xs16 + 2 * lw[u] * kXPad;  // this word's 32 columns
-                uint32_t mm = m[u];
-#pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    const int c0 = __builtin_ctz(mm);
-                    mm &= mm - 1;
-                    const int c1 = __builtin_ctz(mm);
-                    mm &= mm - 1;
-#pragma unroll
-                    for (int b = 0; b < B; ++b) {
-                        const uint16_t *xp = xw + 2 * b * plane;
-                        const uint32_t pr = (uint32_t)xp[c0] | ((uint32_t)xp[c1] << 16);
-                        acc[b] = dot2_bf16(v[k], pr, acc[b]);
-                    }
+            for (int j = 0; j < kStage; ++j) {
+                const int i = i0 + j * kThreads + (int)threadIdx.x;
+                if (i < chunks) {
+                    const int b = i / (nws * 4);
+                    const int c = i - b * nws * 4;
+                    uint32_t *d = xs + b * plane + (c >> 2) * kXPad + (c & 3) * 4;
+                    d[0] = r[j].x;
+                    d[1] = r[j].y;
+                    d[2] = r[j].z;
+                    d[3] = r[j].w;
                 }
             }
         }
+    }
+    __syncthreads();
+    const uint16_t *xs16 = reinterpret_cast<const uint16_t *>(xs);
+
+    float acc[B];
 #pragma unroll
-        for (int b = 0; b < B; ++b) {
-            const float t = wave_sum(acc[b]);
-            if (lane == 0) {
-                if (gridDim.y == 1)
-                    y[(int64_t)b * ldy + row] = f32_to_bf16_rne(t);
-                else
-                    partial[((int64_t)s * B + b) * R + row] = t;
-            }
+    for (int b = 0; b < B; ++b) acc[b] = 0.f;
+    for (int t = 0; t < total; t += 2) {
+        // B <- batch t+1, walk A (batch t)
+        rowB = rowA;
+        biB = biA + 1;
+        if (biB == nb) {
+            biB = 0;
+            rowB += row_step;
         }
+        {
+            const int r = min(rowB, R - 1);
+            load_batch<U>(bufB, masks + (int64_t)r * KW + w0, values + ((int64_t)r * KW + w0) * 2,
+                          t + 1 < total ? nws : 0, biB * kWave * U, lane);
+        }
+        walk_batch<B, U>(bufA, xs16, plane, nws, acc);
+        if (biA == nb - 1) finish_row<B>(acc, rowA, s, R, lane, y, ldy, partial);
+        if (t + 1 >= total) break;
+        // A <- batch t+2, walk B (batch t+1)
+        rowA = rowB;
+        biA = biB + 1;
+        if (biA == nb) {
+            biA = 0;
+            rowA += row_step;
+        }
+        {
+            const int r = min(rowA, R - 1);
+            load_batch<U>(bufA, masks + (int64_t)r * KW + w0, values + ((int64_t)r * KW + w0) * 2,
+                          t + 2 < total ? nws : 0, biA * kWave * U, lane);
+        }
+        walk_batch<B, U>(bufB, xs16, plane, nws, acc);
+        if (biB == nb - 1) finish_row<B>(acc, rowB, s, R, lane, y, ldy, partial);
     }
 }
 
@@ -189,10 +308,13 @@ MvPlan plan_spmv(int64_t R, int64_t K, int B, const DeviceInfo &dev) {
     if (max_slice < 1) max_slice = 1;
     // Enough (row, slice) tasks to give every resident wave work, but no slice shorter
     // than one wave iteration.
+    // Split rows across workgroups only when the matrix has too few rows to give
+    // every CU a couple of waves: the split costs a second launch, which outweighs
+    // the extra parallelism on anything but very short, wide matrices.
     const int64_t cu = dev.num_cu > 0 ? dev.num_cu : 256;
-    const int64_t want_tasks = cu * 16;
+    const int64_t want_rows = cu * 2;
     int64_t splits = (KW + max_slice - 1) / max_slice;
-    int64_t by_tasks = (want_tasks + R - 1) / R;
+    int64_t by_tasks = R >= want_rows ? 1 : (want_rows + R - 1) / R;
     int64_t max_by_len = KW / kWave > 0 ? KW / kWave : 1;
     if (by_tasks > max_by_len) by_tasks = max_by_len;
     if (splits < by_tasks) splits = by_tasks;
@@ -212,7 +334,7 @@ MvPlan plan_spmv(int64_t R, int64_t K, int B, const DeviceInfo &dev) {
     if (gx > cap_x) gx = cap_x;
     if (gx < 1) gx = 1;
     p.grid_x = (int)gx;
-    p.unroll = slice > kWave ? 2 : 1;
+    p.unroll = 1;
     p.ws_bytes = splits > 1 ? (size_t)splits * B * R * sizeof(float) : 0;
     return p;
 }
