@@ -86,6 +86,15 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=12)
     ap.add_argument("--skip-check", action="store_true", help="skip the oracle spot check")
+    ap.add_argument("--profile-kernel", action="store_true",
+                    help="counter-collection mode: only the dominant launch shape (eager, rotated) plus a "
+                         "plain 256 MiB device copy used to calibrate the byte counters")
+    ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="host-only: turn two rocprofv3 --pmc runs of --profile-kernel (FETCH_SIZE, "
+                         "WRITE_SIZE) into profiles/traffic.json")
+    ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
+                    help="host-only: print a per-kernel / per-launch-shape summary of a rocprofv3 "
+                         "--kernel-trace --stats run")
     return ap.parse_args()
 
 
@@ -125,6 +134,10 @@ def capture(torch, fns):
 
 def main():
     args = parse()
+    if args.ingest_pmc:
+        return ingest_pmc(args, *args.ingest_pmc)
+    if args.summarize_trace:
+        return summarize_trace(args.summarize_trace)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
               "Run with --gpus 1.", file=sys.stderr)
@@ -147,6 +160,8 @@ def main():
     projs, patterns = cfg["projs"], cfg["patterns"]
     props = torch.cuda.get_device_properties(0)
     log(f"device {props.name} CUs={props.multi_processor_count} config={args.config} layers={L} B={B}")
+    if args.profile_kernel:
+        return profile_kernel(args, torch, nm, synth, cfg, dev)
 
     # ---------------------------------------------------------------- inputs
     # Per projection a pool of distinct weight buffers of >= 512 MB (and >= L); the
@@ -376,6 +391,115 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+DOMINANT = {"8b": ("gate", 14336, 4096), "tiny": ("w", 256, 512), "8b-sweep": ("gate", 14336, 4096),
+            "qwen14b": ("gate", 17408, 5120), "qwen32b": ("gate", 25600, 5120), "70b": ("gate", 28672, 8192)}
+COPY_BYTES = 256 << 20
+
+
+def profile_kernel(args, torch, nm, synth, cfg, dev):
+    """Eager launches of the dominant launch shape (first pattern), rotated over >= 512 MB,
+    then one plain device-to-device copy of COPY_BYTES: the reference for the counters."""
+    name, R, K = DOMINANT[args.config]
+    N, M = cfg["patterns"][0]
+    B = args.batch
+    n_pool = max(2, math.ceil(ROTATE_BYTES / sparse_bytes(R, K, B)))
+    pool = []
+    for c in range(n_pool):
+        W = synth.device_weights(R, K, args.seed, 400, c)
+        n = nm.nm_col_norm(synth.device_calib_acts(K, args.seed, 401, c))
+        pool.append(nm.nm_prune_pack(W, n, N, M))
+        del W, n
+    x = synth.device_decode_x(B, K, args.seed, 402)
+    y = torch.empty((B, R), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(1, nm.nm_spmv_workspace_bytes(R, K, B) // 4), dtype=torch.float32, device=dev)
+    src = torch.empty(COPY_BYTES // 2, dtype=torch.int16, device=dev).random_()
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        m, v = pool[i % n_pool]
+        nm.nm_spmv(m, v, x, out=y, workspace=ws)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"profile_kernel": f"nm_spmv {name} {R}x{K} {N}:{M} B={B}", "launches": args.steps,
+                      "copy_bytes": COPY_BYTES}), flush=True)
+
+
+def _pmc_rows(d):
+    import csv
+    import glob
+
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    per = {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            key = (r["Dispatch_Id"], r["Kernel_Name"], r["Grid_Size"], r["Counter_Name"])
+            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    return per
+
+
+def ingest_pmc(args, fetch_dir, write_dir):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the dominant SpMV launches, scaled by
+    what the same counters report for the plain copy of COPY_BYTES (which moves exactly
+    COPY_BYTES each way).  Writes profiles/traffic.json."""
+    name, R, K = DOMINANT[args.config]
+    out = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        per = _pmc_rows(d)
+        spmv = [v for (disp, kn, grid, cn), v in per.items() if cn == counter and "spmv_kernel" in kn]
+        copies = [v for (disp, kn, grid, cn), v in per.items()
+                  if cn == counter and "copy" in kn.lower() and "nmk" not in kn]
+        if not spmv or not copies:
+            raise SystemExit(f"{counter}: missing spmv ({len(spmv)}) or copy ({len(copies)}) dispatches")
+        copy_kib = max(copies)  # the 256 MiB copy is the largest copy dispatch
+        factor = COPY_BYTES / (copy_kib * 1024.0)
+        spmv.sort()
+        med = spmv[len(spmv) // 2]
+        out[counter] = {"counter_kib_median": med, "copy_counter_kib": copy_kib, "scale": factor,
+                        "bytes_per_launch": med * 1024.0 * factor, "dispatches": len(spmv)}
+    total = out["FETCH_SIZE"]["bytes_per_launch"] + out["WRITE_SIZE"]["bytes_per_launch"]
+    key = f"{args.config}:{name}:B{args.batch}"
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    data = {}
+    if os.path.exists(path):
+        with open(path) as f:
+            data = json.load(f)
+    data[key] = {"kernel": f"nm_spmv {R}x{K}", "bytes_per_launch": round(total),
+                 "algorithmic_bytes": sparse_bytes(R, K, args.batch), "kernel_sha": kernel_fingerprint(),
+                 "fetch": out["FETCH_SIZE"], "write": out["WRITE_SIZE"]}
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as f:
+        json.dump(data, f, indent=1)
+        f.write("\n")
+    print(json.dumps(data[key]))
+
+
+def summarize_trace(d):
+    import csv
+    import glob
+    import statistics
+
+    files = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_trace.csv under {d}")
+    groups = {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            kn = r["Kernel_Name"]
+            short = kn.replace("void nmk::(anonymous namespace)::", "").split("(")[0] if "nmk::" in kn else \
+                "torch/other: " + kn[:40]
+            wg = int(r["Workgroup_Size_X"]) * int(r.get("Workgroup_Size_Y", 1) or 1)
+            grid = (int(r["Grid_Size_X"]) * int(r.get("Grid_Size_Y", 1) or 1)) // max(wg, 1)
+            groups.setdefault((short, grid), []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    print("| kernel | workgroups | dispatches | avg us | median us | min us | total ms |")
+    print("|---|---|---|---|---|---|---|")
+    for (k, g), v in sorted(groups.items(), key=lambda kv: -sum(kv[1]))[:25]:
+        print(f"| {k} | {g} | {len(v)} | {statistics.mean(v):.2f} | {statistics.median(v):.2f} | {min(v):.2f} | "
+              f"{sum(v) / 1e3:.2f} |")
 
 
 def kernel_fingerprint() -> str:
