@@ -84,7 +84,7 @@ void apply_override(const char *env, int64_t units, int64_t R, int B, size_t uni
 
 nmk::MvPlan spmv_plan(int64_t R, int64_t K, int B) {
     nmk::MvPlan p = nmk::plan_spmv(R, K, B, device_info());
-    apply_override("NM_SPMV_PLAN", K / 32, R, B, (size_t)B * 17 * 4, p);
+    apply_override("NM_SPMV_PLAN", K / 32, R, B, nmk::spmv_lds_per_word(B), p);
     return p;
 }
 

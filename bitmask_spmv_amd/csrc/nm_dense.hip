@@ -102,12 +102,12 @@ __global__ __launch_bounds__(kThreads) void dense_kernel(const u32x4 *__restrict
 
     DBatch<U> bufA, bufB;
     int rowA = first_row, biA = 0, rowB = first_row, biB = 0;
-    load_dbatch<U>(bufA, W + (int64_t)min(rowA, R - 1) * ldw8 + c0, total > 0 ? ncs : 0, 0, lane);
-
+    // Stage x; the first round of x loads goes out before batch A's weight loads so that
+    // waiting for x never waits for the weights queued behind it.
     {
         constexpr int kStage = 4;
         const int chunks = B * ncs;
-        for (int i0 = 0; i0 < chunks; i0 += kThreads * kStage) {
+        for (int i0 = 0; i0 < chunks || i0 == 0; i0 += kThreads * kStage) {
             u32x4 r[kStage];
 #pragma unroll
             for (int j = 0; j < kStage; ++j) {
@@ -117,6 +117,7 @@ __global__ __launch_bounds__(kThreads) void dense_kernel(const u32x4 *__restrict
                     r[j] = reinterpret_cast<const u32x4 *>(x + (int64_t)b * ldx)[c0 + (i - b * ncs)];
                 }
             }
+            if (i0 == 0) load_dbatch<U>(bufA, W + (int64_t)min(rowA, R - 1) * ldw8 + c0, total > 0 ? ncs : 0, 0, lane);
 #pragma unroll
             for (int j = 0; j < kStage; ++j) {
                 const int i = i0 + j * kThreads + (int)threadIdx.x;

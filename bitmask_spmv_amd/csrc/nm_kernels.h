@@ -30,6 +30,7 @@ struct MvPlan {
 };
 
 MvPlan plan_spmv(int64_t R, int64_t K, int B, const DeviceInfo &dev);
+size_t spmv_lds_per_word(int B);  // LDS bytes of x per 32-column block
 MvPlan plan_dense(int64_t R, int64_t K, int B, const DeviceInfo &dev);
 
 hipError_t launch_col_norm(const uint16_t *X, int64_t T, int64_t K, int64_t ldx, float *n, hipStream_t st);

@@ -32,7 +32,22 @@
 namespace nmk {
 namespace {
 
-constexpr int kXPad = 17;         // dwords per 32-column block of x in LDS
+// LDS layout of x.  B = 1: each 32-column block is 16 dwords of bf16 pairs plus one pad
+// dword (17 dwords), so lanes walking different words spread over the banks.  B > 1:
+// tokens are interleaved per column -- column c holds S bf16 (S = B rounded up to 2, 4
+// or 8, zero-filled) -- so one 4/8/16-byte LDS load gathers a column for every token;
+// blocks are 16*S dwords plus S/2 pad dwords (keeping 8/16-byte alignment).
+template <int B>
+struct XLayout {
+    static constexpr int S = B == 1 ? 1 : (B <= 2 ? 2 : (B <= 4 ? 4 : 8));
+    static constexpr int kBlk = B == 1 ? 17 : 16 * S + S / 2;  // dwords per 32-column block
+};
+
+constexpr int blk_dwords(int B) {
+    return B == 1 ? 17 : (B <= 2 ? 33 : (B <= 4 ? 66 : 132));
+}
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kThreads = 512;     // 8 waves
 constexpr size_t kLdsCap = 80 * 1024;     // keeps two workgroups resident per CU
 constexpr size_t kLdsPerCu = 160 * 1024;  // gfx950 LDS per compute unit
@@ -83,10 +98,31 @@ __device__ __forceinline__ uint32_t pair_swap(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);  // quad_perm(1,0,3,2)
 }
 
-// The fixed 16-step walk of each mask word: lowest set bit -> column, clear it.
+// Gather of one column for the S token slots (S/2 dwords: token pairs).
+template <int S>
+__device__ __forceinline__ void gather_col(const uint32_t *blk, int c, uint32_t (&d)[S / 2]) {
+    if constexpr (S == 2) {
+        d[0] = blk[c];
+    } else if constexpr (S == 4) {
+        const u32x2 t = *reinterpret_cast<const u32x2 *>(blk + 2 * c);
+        d[0] = t.x;
+        d[1] = t.y;
+    } else {
+        const u32x4 t = *reinterpret_cast<const u32x4 *>(blk + 4 * c);
+        d[0] = t.x;
+        d[1] = t.y;
+        d[2] = t.z;
+        d[3] = t.w;
+    }
+}
+
+// The fixed 16-step walk of each mask word: lowest set bit -> column, clear it.  Steps
+// are taken in pairs so that the two gathered inputs meet the packed value pair in one
+// v_dot2_f32_bf16 (per token).
 template <int B, int U>
-__device__ __forceinline__ void walk_batch(const Batch<U> &bt, const uint16_t *xs16, int plane, int nws,
-                                           float (&acc)[B]) {
+__device__ __forceinline__ void walk_batch(const Batch<U> &bt, const uint32_t *xs, int nws, float (&acc)[B]) {
+    constexpr int S = XLayout<B>::S;
+    constexpr int kBlk = XLayout<B>::kBlk;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         // A padding lane (past the slice) holds zero values: walk 16 fixed columns of
@@ -104,7 +140,7 @@ __device__ __forceinline__ void walk_batch(const Batch<U> &bt, const uint16_t *x
                                odd ? r_z : bt.va[u].z, odd ? r_w : bt.va[u].w,
                                odd ? bt.vb[u].x : r_x, odd ? bt.vb[u].y : r_y,
                                odd ? bt.vb[u].z : r_z, odd ? bt.vb[u].w : r_w};
-        const uint16_t *xw = xs16 + 2 * lw * kXPad;  // this word's 32 columns
+        const uint32_t *blk = xs + lw * kBlk;  // this word's 32 columns
         uint32_t mm = ok ? bt.m[u] : 0xFFFFu;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
@@ -112,11 +148,21 @@ __device__ __forceinline__ void walk_batch(const Batch<U> &bt, const uint16_t *x
             mm &= mm - 1;
             const int c1 = __builtin_ctz(mm);
             mm &= mm - 1;
+            if constexpr (S == 1) {
+                const uint16_t *xw = reinterpret_cast<const uint16_t *>(blk);
+                const uint32_t pr = (uint32_t)xw[c0] | ((uint32_t)xw[c1] << 16);
+                acc[0] = dot2_bf16(v[k], pr, acc[0]);
+            } else {
+                uint32_t d0[S / 2], d1[S / 2];
+                gather_col<S>(blk, c0, d0);
+                gather_col<S>(blk, c1, d1);
 #pragma unroll
-            for (int b = 0; b < B; ++b) {
-                const uint16_t *xp = xw + 2 * b * plane;
-                const uint32_t pr = (uint32_t)xp[c0] | ((uint32_t)xp[c1] << 16);
-                acc[b] = dot2_bf16(v[k], pr, acc[b]);
+                for (int j = 0; j < S / 2; ++j) {
+                    // (token 2j of column c0, token 2j of column c1), then the same for 2j+1
+                    if (2 * j < B) acc[2 * j] = dot2_bf16(v[k], __builtin_amdgcn_perm(d1[j], d0[j], 0x05040100u), acc[2 * j]);
+                    if (2 * j + 1 < B)
+                        acc[2 * j + 1] = dot2_bf16(v[k], __builtin_amdgcn_perm(d1[j], d0[j], 0x07060302u), acc[2 * j + 1]);
+                }
             }
         }
     }
@@ -145,11 +191,10 @@ __global__ __launch_bounds__(kThreads) void spmv_kernel(const uint32_t *__restri
                                                         const uint16_t *__restrict__ x, int64_t ldx,
                                                         uint16_t *__restrict__ y, int64_t ldy,
                                                         float *__restrict__ partial, int slice) {
-    extern __shared__ uint32_t xs[];  // [B][nws * kXPad]
+    extern __shared__ uint32_t xs[];  // [nws][XLayout<B>::kBlk]
     const int s = blockIdx.y;
     const int w0 = s * slice;
     const int nws = min(slice, KW - w0);
-    const int plane = nws * kXPad;
     const int lane = threadIdx.x & (kWave - 1);
     // wave-uniform by construction; readfirstlane lets the compiler keep the row loop
     // in scalar registers and branch on it without exec masking
@@ -169,32 +214,28 @@ __global__ __launch_bounds__(kThreads) void spmv_kernel(const uint32_t *__restri
     // never covers the loads of the other).
     Batch<U> bufA, bufB;
     int rowA = first_row, biA = 0, rowB = first_row, biB = 0;
-    load_batch<U>(bufA, masks + (int64_t)min(rowA, R - 1) * KW + w0, values + ((int64_t)min(rowA, R - 1) * KW + w0) * 2,
-                  total > 0 ? nws : 0, 0, lane);
-
-    // Stage this slice of x (B tokens) into LDS with 16-byte loads, all issued before
-    // the first LDS store; 8 bf16 per chunk, 4 chunks per 32-column block.
-    {
+    // Stage this slice of x into LDS.  The first round of x loads is issued before batch
+    // A's weight loads, so waiting for x (an L2 hit after the first workgroup of an XCD)
+    // never waits for the weights queued behind it.
+    if constexpr (XLayout<B>::S == 1) {
+        // 16-byte loads; 8 bf16 per chunk, 4 chunks per 32-column block
         constexpr int kStage = 4;
-        const int chunks = B * nws * 4;
-        for (int i0 = 0; i0 < chunks; i0 += kThreads * kStage) {
+        const int chunks = nws * 4;
+        for (int i0 = 0; i0 < chunks || i0 == 0; i0 += kThreads * kStage) {
             u32x4 r[kStage];
 #pragma unroll
             for (int j = 0; j < kStage; ++j) {
                 const int i = i0 + j * kThreads + (int)threadIdx.x;
-                if (i < chunks) {
-                    const int b = i / (nws * 4);
-                    const int c = i - b * nws * 4;
-                    r[j] = reinterpret_cast<const u32x4 *>(x + (int64_t)b * ldx + (int64_t)w0 * 32)[c];
-                }
+                if (i < chunks) r[j] = reinterpret_cast<const u32x4 *>(x + (int64_t)w0 * 32)[i];
             }
+            if (i0 == 0)
+                load_batch<U>(bufA, masks + (int64_t)min(rowA, R - 1) * KW + w0,
+                              values + ((int64_t)min(rowA, R - 1) * KW + w0) * 2, total > 0 ? nws : 0, 0, lane);
 #pragma unroll
             for (int j = 0; j < kStage; ++j) {
                 const int i = i0 + j * kThreads + (int)threadIdx.x;
                 if (i < chunks) {
-                    const int b = i / (nws * 4);
-                    const int c = i - b * nws * 4;
-                    uint32_t *d = xs + b * plane + (c >> 2) * kXPad + (c & 3) * 4;
+                    uint32_t *d = xs + (i >> 2) * XLayout<B>::kBlk + (i & 3) * 4;
                     d[0] = r[j].x;
                     d[1] = r[j].y;
                     d[2] = r[j].z;
@@ -202,9 +243,49 @@ __global__ __launch_bounds__(kThreads) void spmv_kernel(const uint32_t *__restri
                 }
             }
         }
+    } else {
+        // One column pair per thread and round: a dword (2 columns) of every token,
+        // transposed with byte permutes into the interleaved per-column layout.
+        constexpr int S = XLayout<B>::S;
+        constexpr int kStage = 2;
+        const int pairs = nws * 16;
+        const uint32_t *x32 = reinterpret_cast<const uint32_t *>(x) + (int64_t)w0 * 16;
+        for (int i0 = 0; i0 < pairs || i0 == 0; i0 += kThreads * kStage) {
+            uint32_t r[kStage][S];
+#pragma unroll
+            for (int j = 0; j < kStage; ++j) {
+                const int i = i0 + j * kThreads + (int)threadIdx.x;
+#pragma unroll
+                for (int b = 0; b < S; ++b) r[j][b] = (b < B && i < pairs) ? x32[(int64_t)b * (ldx / 2) + i] : 0u;
+            }
+            if (i0 == 0)
+                load_batch<U>(bufA, masks + (int64_t)min(rowA, R - 1) * KW + w0,
+                              values + ((int64_t)min(rowA, R - 1) * KW + w0) * 2, total > 0 ? nws : 0, 0, lane);
+#pragma unroll
+            for (int j = 0; j < kStage; ++j) {
+                const int i = i0 + j * kThreads + (int)threadIdx.x;
+                if (i < pairs) {
+                    const int c = 2 * i;  // first column of the pair, within the slice
+                    uint32_t *d = xs + (c >> 5) * XLayout<B>::kBlk + (c & 31) * (S / 2);
+                    uint32_t col[S];  // column c: S/2 dwords, then column c+1: S/2 dwords
+#pragma unroll
+                    for (int t = 0; t < S / 2; ++t) {
+                        col[t] = __builtin_amdgcn_perm(r[j][2 * t + 1], r[j][2 * t], 0x05040100u);
+                        col[S / 2 + t] = __builtin_amdgcn_perm(r[j][2 * t + 1], r[j][2 * t], 0x07060302u);
+                    }
+                    if constexpr (S == 2) {
+                        *reinterpret_cast<u32x2 *>(d) = u32x2{col[0], col[1]};
+                    } else if constexpr (S == 4) {
+                        *reinterpret_cast<u32x4 *>(d) = u32x4{col[0], col[1], col[2], col[3]};
+                    } else {
+                        reinterpret_cast<u32x4 *>(d)[0] = u32x4{col[0], col[1], col[2], col[3]};
+                        reinterpret_cast<u32x4 *>(d)[1] = u32x4{col[4], col[5], col[6], col[7]};
+                    }
+                }
+            }
+        }
     }
     __syncthreads();
-    const uint16_t *xs16 = reinterpret_cast<const uint16_t *>(xs);
 
     float acc[B];
 #pragma unroll
@@ -222,7 +303,7 @@ __global__ __launch_bounds__(kThreads) void spmv_kernel(const uint32_t *__restri
             load_batch<U>(bufB, masks + (int64_t)r * KW + w0, values + ((int64_t)r * KW + w0) * 2,
                           t + 1 < total ? nws : 0, biB * kWave * U, lane);
         }
-        walk_batch<B, U>(bufA, xs16, plane, nws, acc);
+        walk_batch<B, U>(bufA, xs, nws, acc);
         if (biA == nb - 1) finish_row<B>(acc, rowA, s, R, lane, y, ldy, partial);
         if (t + 1 >= total) break;
         // A <- batch t+2, walk B (batch t+1)
@@ -237,7 +318,7 @@ __global__ __launch_bounds__(kThreads) void spmv_kernel(const uint32_t *__restri
             load_batch<U>(bufA, masks + (int64_t)r * KW + w0, values + ((int64_t)r * KW + w0) * 2,
                           t + 2 < total ? nws : 0, biA * kWave * U, lane);
         }
-        walk_batch<B, U>(bufB, xs16, plane, nws, acc);
+        walk_batch<B, U>(bufB, xs, nws, acc);
         if (biB == nb - 1) finish_row<B>(acc, rowB, s, R, lane, y, ldy, partial);
     }
 }
@@ -296,11 +377,13 @@ hipError_t launch_b(const MvPlan &p, const uint32_t *masks, const uint16_t *valu
 
 }  // namespace
 
+size_t spmv_lds_per_word(int B) { return (size_t)blk_dwords(B) * 4; }
+
 MvPlan plan_spmv(int64_t R, int64_t K, int B, const DeviceInfo &dev) {
     MvPlan p;
     p.threads = kThreads;
     const int64_t KW = K / 32;
-    const int64_t bytes_per_word = (int64_t)B * kXPad * 4;
+    const int64_t bytes_per_word = (int64_t)blk_dwords(B) * 4;
     size_t cap = kLdsCap;
     if (dev.max_lds_per_block > 0 && (size_t)dev.max_lds_per_block < cap) cap = (size_t)dev.max_lds_per_block;
     int64_t max_slice = (int64_t)cap / bytes_per_word;
