@@ -270,12 +270,49 @@ def main():
     g_dense = capture(torch, dense_fns)
     timer = Timer(torch)
 
+    # The same step with projections that read the same x (q|k|v, gate|up) fused into one
+    # launch each (nm_spmv_multi / dense_gemv_multi): x is staged once per group.
+    groups = []  # list of lists of projection tuples, in layer order
+    for proj in projs:
+        if groups and groups[-1][0][3] == proj[3]:
+            groups[-1].append(proj)
+        else:
+            groups.append([proj])
+    fused_fns, fused_dense_fns = [], []
+    for (N, M) in patterns:
+        for l in range(L):
+            for grp in groups:
+                if len(grp) == 1:
+                    name = grp[0][0]
+                    fused_fns.append(spmv_call(pool_sparse[(N, M), name][l], xs[grp[0][3]][l], ys[name]))
+                else:
+                    pk = [pool_sparse[(N, M), pr[0]][l] for pr in grp]
+                    outs = [ys[pr[0]] for pr in grp]
+                    fused_fns.append(lambda pk=pk, x=xs[grp[0][3]][l], outs=outs:
+                                     nm.nm_spmv_multi(pk, x, outs=outs, workspace=ws))
+    for l in range(L):
+        for grp in groups:
+            Wl = [pool_dense[pr[0]][l] for pr in grp]
+            outs = [ys[pr[0]] for pr in grp]
+            fused_dense_fns.append(lambda Wl=Wl, x=xs[grp[0][3]][l], outs=outs:
+                                   nm.dense_gemv_multi(Wl, x, outs=outs, workspace=ws))
+    g_fused = capture(torch, fused_fns)
+    g_fused_dense = capture(torch, fused_dense_fns)
+
     for _ in range(args.warmup):
         g_sparse.replay()
         g_dense.replay()
     torch.cuda.synchronize()
     ms_sparse = timer.time_graph(g_sparse, args.steps)
     ms_dense = timer.time_graph(g_dense, args.steps)
+    for _ in range(args.warmup):
+        g_fused.replay()
+        g_fused_dense.replay()
+    torch.cuda.synchronize()
+    ms_fused = timer.time_graph(g_fused, args.steps)
+    ms_fused_dense = timer.time_graph(g_fused_dense, args.steps)
+    log(f"fused step: sparse {ms_fused * 1e3:.1f} us ({len(fused_fns)} launches), dense "
+        f"{ms_fused_dense * 1e3:.1f} us ({len(fused_dense_fns)} launches)")
     log(f"step: sparse {ms_sparse * 1e3:.1f} us ({len(sparse_fns)} launches), dense {ms_dense * 1e3:.1f} us "
         f"({len(dense_fns)} launches, {len(patterns)} pattern(s) share it)")
 
@@ -384,6 +421,12 @@ def main():
         "dense_ms_per_step": round(ms_dense, 4),
         "dense_GBs": round(step_dense_bytes / (ms_dense * 1e-3) / 1e9, 1),
         "step_speedup_vs_dense": round(ms_dense * len(patterns) / ms_sparse, 3),
+        "fused_step": {"launches": len(fused_fns), "ms": round(ms_fused, 4),
+                       "GBs": round(step_sparse_bytes / (ms_fused * 1e-3) / 1e9, 1),
+                       "pct_hbm_peak": round(100 * step_sparse_bytes / (ms_fused * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
+                       "dense_ms": round(ms_fused_dense, 4),
+                       "speedup_vs_dense": round(ms_fused_dense * len(patterns) / ms_fused, 3),
+                       "groups": ["|".join(pr[0] for pr in grp) for grp in groups]},
         "per_layer": per,
         "pack_GBs": round(pack_bytes / pack_ms / 1e6, 1),
         "parity": parity,

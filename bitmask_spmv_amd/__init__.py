@@ -21,7 +21,8 @@ import torch
 __all__ = [
     "NmError", "LIB_PATH", "lib", "nm_version", "nm_col_norm", "nm_prune_pack", "nm_spmv",
     "nm_spmv_workspace_bytes", "dense_gemv", "dense_gemv_workspace_bytes", "nm_unpack",
-    "NM_PATTERNS",
+    "NM_PATTERNS", "nm_spmv_multi", "nm_spmv_multi_workspace_bytes", "dense_gemv_multi",
+    "dense_gemv_multi_workspace_bytes",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnmspmv.so")
@@ -35,6 +36,16 @@ class NmError(RuntimeError):
     def __init__(self, status: int, detail: str):
         self.status = status
         super().__init__(f"{_STATUS.get(status, status)}: {detail}")
+
+
+class _SpmvMatrix(ctypes.Structure):
+    _fields_ = [("masks", ctypes.c_void_p), ("values", ctypes.c_void_p), ("R", ctypes.c_int64),
+                ("y", ctypes.c_void_p), ("ldy", ctypes.c_int64)]
+
+
+class _DenseMatrix(ctypes.Structure):
+    _fields_ = [("W", ctypes.c_void_p), ("ldw", ctypes.c_int64), ("R", ctypes.c_int64),
+                ("y", ctypes.c_void_p), ("ldy", ctypes.c_int64)]
 
 
 def _load() -> ctypes.CDLL:
@@ -54,7 +65,14 @@ def _load() -> ctypes.CDLL:
     L.dense_gemv_workspace_bytes.argtypes, L.dense_gemv_workspace_bytes.restype = [i64, i64, i32], sz
     L.dense_gemv.argtypes = [p, i64, i64, i64, p, i64, i32, p, i64, p, sz, p]
     L.nm_unpack.argtypes = [p, p, i64, i64, p, i64, p]
-    for f in (L.nm_col_norm, L.nm_prune_pack, L.nm_spmv, L.dense_gemv, L.nm_unpack):
+    L.nm_spmv_multi_workspace_bytes.argtypes = [p, i32, i64, i32]
+    L.nm_spmv_multi_workspace_bytes.restype = sz
+    L.nm_spmv_multi.argtypes = [p, i32, i64, p, i64, i32, p, sz, p]
+    L.dense_gemv_multi_workspace_bytes.argtypes = [p, i32, i64, i32]
+    L.dense_gemv_multi_workspace_bytes.restype = sz
+    L.dense_gemv_multi.argtypes = [p, i32, i64, p, i64, i32, p, sz, p]
+    for f in (L.nm_col_norm, L.nm_prune_pack, L.nm_spmv, L.dense_gemv, L.nm_unpack, L.nm_spmv_multi,
+              L.dense_gemv_multi):
         f.restype = i32
     return L
 
@@ -206,3 +224,77 @@ def nm_unpack(masks: torch.Tensor, values: torch.Tensor, out: torch.Tensor | Non
     _dev(out, "out", torch.bfloat16, 2)
     _check(lib.nm_unpack(_ptr(masks), _ptr(values), R, K, _ptr(out), _ld(out), _stream(masks)))
     return out
+
+
+def _multi_outs(x2, Rs, outs):
+    B = x2.shape[0]
+    if outs is None:
+        outs = [torch.empty((B, R), dtype=torch.bfloat16, device=x2.device) for R in Rs]
+    if len(outs) != len(Rs):
+        raise ValueError("one output per matrix")
+    o2 = []
+    for o, R in zip(outs, Rs):
+        o = o.unsqueeze(0) if o.dim() == 1 else o
+        _dev(o, "out", torch.bfloat16, 2)
+        if o.shape != (B, R):
+            raise ValueError(f"out must be [{B}, {R}]")
+        o2.append(o)
+    return outs, o2
+
+
+def _multi_x(x):
+    x2 = x.unsqueeze(0) if x.dim() == 1 else x
+    _dev(x2, "x", torch.bfloat16, 2)
+    return x2
+
+
+def nm_spmv_multi_workspace_bytes(Rs, K: int, B: int) -> int:
+    arr = (_SpmvMatrix * len(Rs))(*[_SpmvMatrix(None, None, int(R), None, int(R)) for R in Rs])
+    return int(lib.nm_spmv_multi_workspace_bytes(ctypes.cast(arr, ctypes.c_void_p), len(Rs), K, B))
+
+
+def nm_spmv_multi(packed, x: torch.Tensor, outs=None, workspace: torch.Tensor | None = None):
+    """Several packed matrices [(masks, values), ...] sharing x, in one launch -> list of y."""
+    x2 = _multi_x(x)
+    K = x2.shape[1]
+    Rs = []
+    for i, (m, v) in enumerate(packed):
+        _dev(m, f"masks[{i}]", torch.int32, 2)
+        _dev(v, f"values[{i}]", torch.bfloat16, 2)
+        if not (m.is_contiguous() and v.is_contiguous()):
+            raise ValueError("masks and values must be contiguous")
+        if m.shape[1] * 32 != K or v.shape != (m.shape[0], K // 2):
+            raise ValueError(f"matrix {i} does not have K={K} columns")
+        Rs.append(m.shape[0])
+    outs, o2 = _multi_outs(x2, Rs, outs)
+    arr = (_SpmvMatrix * len(Rs))(*[_SpmvMatrix(m.data_ptr(), v.data_ptr(), R, o.data_ptr(), _ld(o))
+                                     for (m, v), R, o in zip(packed, Rs, o2)])
+    ws, ws_bytes = _workspace(int(lib.nm_spmv_multi_workspace_bytes(ctypes.cast(arr, ctypes.c_void_p), len(Rs), K,
+                                                                     x2.shape[0])), x2, workspace)
+    _check(lib.nm_spmv_multi(ctypes.cast(arr, ctypes.c_void_p), len(Rs), K, _ptr(x2), _ld(x2), x2.shape[0], _ptr(ws),
+                             ws_bytes, _stream(x2)))
+    return outs
+
+
+def dense_gemv_multi_workspace_bytes(Rs, K: int, B: int) -> int:
+    arr = (_DenseMatrix * len(Rs))(*[_DenseMatrix(None, K, int(R), None, int(R)) for R in Rs])
+    return int(lib.dense_gemv_multi_workspace_bytes(ctypes.cast(arr, ctypes.c_void_p), len(Rs), K, B))
+
+
+def dense_gemv_multi(Ws, x: torch.Tensor, outs=None, workspace: torch.Tensor | None = None):
+    """Several dense matrices sharing x, in one launch -> list of y."""
+    x2 = _multi_x(x)
+    K = x2.shape[1]
+    for i, W in enumerate(Ws):
+        _dev(W, f"W[{i}]", torch.bfloat16, 2)
+        if W.shape[1] != K:
+            raise ValueError(f"matrix {i} does not have K={K} columns")
+    Rs = [W.shape[0] for W in Ws]
+    outs, o2 = _multi_outs(x2, Rs, outs)
+    arr = (_DenseMatrix * len(Rs))(*[_DenseMatrix(W.data_ptr(), _ld(W), R, o.data_ptr(), _ld(o))
+                                     for W, R, o in zip(Ws, Rs, o2)])
+    ws, ws_bytes = _workspace(int(lib.dense_gemv_multi_workspace_bytes(ctypes.cast(arr, ctypes.c_void_p), len(Rs),
+                                                                       K, x2.shape[0])), x2, workspace)
+    _check(lib.dense_gemv_multi(ctypes.cast(arr, ctypes.c_void_p), len(Rs), K, _ptr(x2), _ld(x2), x2.shape[0],
+                                _ptr(ws), ws_bytes, _stream(x2)))
+    return outs

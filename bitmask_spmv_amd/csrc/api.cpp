@@ -169,6 +169,21 @@ size_t nm_spmv_workspace_bytes(int64_t R, int64_t K, int B) {
     return spmv_plan(R, K, B).ws_bytes;
 }
 
+// Shared body of nm_spmv / nm_spmv_multi once the matrices are validated into a set.
+static nm_status spmv_run(const nmk::SpmvSet &set, int64_t K, const nm_bf16 *x, int64_t ldx, int B,
+                          void *workspace, size_t workspace_bytes, void *hip_stream, const char *who) {
+    const int64_t R = set.row0[set.P];
+    const nmk::MvPlan p = spmv_plan(R, K, B);
+    if (p.ws_bytes > 0) {
+        if (!workspace || workspace_bytes < p.ws_bytes || !aligned(workspace, 4))
+            return fail(NM_ERR_WORKSPACE, "%s: workspace of %zu bytes required, %zu given", who, p.ws_bytes,
+                        workspace ? workspace_bytes : (size_t)0);
+    }
+    hipError_t e = nmk::launch_spmv(p, set, K, x, ldx, B, (float *)workspace, (hipStream_t)hip_stream);
+    if (e != hipSuccess) return hip_fail(who, e);
+    return NM_OK;
+}
+
 nm_status nm_spmv(const uint32_t *masks, const nm_bf16 *values, int64_t R, int64_t K, const nm_bf16 *x, int64_t ldx,
                   int B, nm_bf16 *y, int64_t ldy, void *workspace, size_t workspace_bytes, void *hip_stream) {
     try {
@@ -180,24 +195,93 @@ nm_status nm_spmv(const uint32_t *masks, const nm_bf16 *values, int64_t R, int64
         if (st != NM_OK) return st;
         if (!aligned(masks, 4) || !aligned(values, 16))
             return fail(NM_ERR_ALIGN, "nm_spmv: masks need 4-byte and values 16-byte alignment");
-        const nmk::MvPlan p = spmv_plan(R, K, B);
-        if (p.ws_bytes > 0) {
-            if (!workspace || workspace_bytes < p.ws_bytes || !aligned(workspace, 4))
-                return fail(NM_ERR_WORKSPACE, "nm_spmv: workspace of %zu bytes required, %zu given", p.ws_bytes,
-                            workspace ? workspace_bytes : (size_t)0);
-        }
-        hipError_t e = nmk::launch_spmv(p, masks, values, R, K, x, ldx, B, y, ldy, (float *)workspace,
-                                        (hipStream_t)hip_stream);
-        if (e != hipSuccess) return hip_fail("nm_spmv launch", e);
-        return NM_OK;
+        nmk::SpmvSet set;
+        set.P = 1;
+        set.row0[1] = (int)R;
+        set.masks[0] = masks;
+        set.values[0] = values;
+        set.y[0] = y;
+        set.ldy[0] = ldy;
+        return spmv_run(set, K, x, ldx, B, workspace, workspace_bytes, hip_stream, "nm_spmv");
     } catch (...) {
         return fail(NM_ERR_HIP, "nm_spmv: internal error");
+    }
+}
+
+// Validates a host array of matrices sharing K into a set; 0 rows in total is an error.
+static nm_status build_spmv_set(const nm_spmv_matrix *mats, int P, int64_t K, int B, nmk::SpmvSet &set,
+                                const char *who) {
+    if (!mats) return fail(NM_ERR_NULL, "%s: NULL matrix array", who);
+    if (P < 1 || P > nmk::kMaxMats) return fail(NM_ERR_SHAPE, "%s: P=%d out of range [1, %d]", who, P, nmk::kMaxMats);
+    if (K < 32 || K > kMaxDim || K % 32 != 0)
+        return fail(NM_ERR_SHAPE, "%s: K=%lld must be a positive multiple of 32", who, (long long)K);
+    int64_t total = 0;
+    set.P = P;
+    for (int i = 0; i < P; ++i) {
+        const nm_spmv_matrix &m = mats[i];
+        if (!m.masks || !m.values || !m.y) return fail(NM_ERR_NULL, "%s: NULL pointer in matrix %d", who, i);
+        if (m.R < 1 || m.R > kMaxDim) return fail(NM_ERR_SHAPE, "%s: matrix %d has R=%lld", who, i, (long long)m.R);
+        if (m.ldy < m.R) return fail(NM_ERR_SHAPE, "%s: matrix %d has ldy < R", who, i);
+        if (!aligned(m.masks, 4) || !aligned(m.values, 16) || !aligned(m.y, 2))
+            return fail(NM_ERR_ALIGN, "%s: matrix %d misaligned (masks 4, values 16, y 2 bytes)", who, i);
+        set.row0[i] = (int)total;
+        set.masks[i] = m.masks;
+        set.values[i] = m.values;
+        set.y[i] = m.y;
+        set.ldy[i] = m.ldy;
+        total += m.R;
+        if (total > kMaxDim) return fail(NM_ERR_SHAPE, "%s: more than 2^30 rows in total", who);
+    }
+    set.row0[P] = (int)total;
+    (void)B;
+    return NM_OK;
+}
+
+size_t nm_spmv_multi_workspace_bytes(const nm_spmv_matrix *mats, int P, int64_t K, int B) {
+    if (!mats || P < 1 || P > nmk::kMaxMats || K < 32 || K % 32 != 0 || K > kMaxDim || B < 1 || B > 8) return 0;
+    int64_t total = 0;
+    for (int i = 0; i < P; ++i) {
+        if (mats[i].R < 1) return 0;
+        total += mats[i].R;
+    }
+    if (total > kMaxDim) return 0;
+    return spmv_plan(total, K, B).ws_bytes;
+}
+
+nm_status nm_spmv_multi(const nm_spmv_matrix *mats, int P, int64_t K, const nm_bf16 *x, int64_t ldx, int B,
+                        void *workspace, size_t workspace_bytes, void *hip_stream) {
+    try {
+        g_err[0] = 0;
+        if (!x) return fail(NM_ERR_NULL, "nm_spmv_multi: NULL x");
+        nmk::SpmvSet set;
+        nm_status st = build_spmv_set(mats, P, K, B, set, "nm_spmv_multi");
+        if (st != NM_OK) return st;
+        if (B < 1 || B > 8) return fail(NM_ERR_SHAPE, "nm_spmv_multi: B=%d out of range [1, 8]", B);
+        if (ldx < K) return fail(NM_ERR_SHAPE, "nm_spmv_multi: ldx < K");
+        if (ldx % 8 || !aligned(x, 16)) return fail(NM_ERR_ALIGN, "nm_spmv_multi: x needs 16-byte alignment, ldx % 8 == 0");
+        return spmv_run(set, K, x, ldx, B, workspace, workspace_bytes, hip_stream, "nm_spmv_multi");
+    } catch (...) {
+        return fail(NM_ERR_HIP, "nm_spmv_multi: internal error");
     }
 }
 
 size_t dense_gemv_workspace_bytes(int64_t R, int64_t K, int B) {
     if (R < 1 || R > kMaxDim || K < 8 || K % 8 != 0 || K > kMaxDim || B < 1 || B > 8) return 0;
     return dense_plan(R, K, B).ws_bytes;
+}
+
+static nm_status dense_run(const nmk::DenseSet &set, int64_t K, const nm_bf16 *x, int64_t ldx, int B,
+                           void *workspace, size_t workspace_bytes, void *hip_stream, const char *who) {
+    const int64_t R = set.row0[set.P];
+    const nmk::MvPlan p = dense_plan(R, K, B);
+    if (p.ws_bytes > 0) {
+        if (!workspace || workspace_bytes < p.ws_bytes || !aligned(workspace, 4))
+            return fail(NM_ERR_WORKSPACE, "%s: workspace of %zu bytes required, %zu given", who, p.ws_bytes,
+                        workspace ? workspace_bytes : (size_t)0);
+    }
+    hipError_t e = nmk::launch_dense(p, set, K, x, ldx, B, (float *)workspace, (hipStream_t)hip_stream);
+    if (e != hipSuccess) return hip_fail(who, e);
+    return NM_OK;
 }
 
 nm_status dense_gemv(const nm_bf16 *W, int64_t ldw, int64_t R, int64_t K, const nm_bf16 *x, int64_t ldx, int B,
@@ -212,18 +296,62 @@ nm_status dense_gemv(const nm_bf16 *W, int64_t ldw, int64_t R, int64_t K, const 
         if (st != NM_OK) return st;
         if (ldw % 8 || !aligned(W, 16))
             return fail(NM_ERR_ALIGN, "dense_gemv: W needs 16-byte alignment and ldw a multiple of 8");
-        const nmk::MvPlan p = dense_plan(R, K, B);
-        if (p.ws_bytes > 0) {
-            if (!workspace || workspace_bytes < p.ws_bytes || !aligned(workspace, 4))
-                return fail(NM_ERR_WORKSPACE, "dense_gemv: workspace of %zu bytes required, %zu given", p.ws_bytes,
-                            workspace ? workspace_bytes : (size_t)0);
-        }
-        hipError_t e =
-            nmk::launch_dense(p, W, ldw, R, K, x, ldx, B, y, ldy, (float *)workspace, (hipStream_t)hip_stream);
-        if (e != hipSuccess) return hip_fail("dense_gemv launch", e);
-        return NM_OK;
+        nmk::DenseSet set;
+        set.P = 1;
+        set.row0[1] = (int)R;
+        set.W[0] = W;
+        set.ldw[0] = ldw;
+        set.y[0] = y;
+        set.ldy[0] = ldy;
+        return dense_run(set, K, x, ldx, B, workspace, workspace_bytes, hip_stream, "dense_gemv");
     } catch (...) {
         return fail(NM_ERR_HIP, "dense_gemv: internal error");
+    }
+}
+
+size_t dense_gemv_multi_workspace_bytes(const dense_matrix *mats, int P, int64_t K, int B) {
+    if (!mats || P < 1 || P > nmk::kMaxMats || K < 8 || K % 8 != 0 || K > kMaxDim || B < 1 || B > 8) return 0;
+    int64_t total = 0;
+    for (int i = 0; i < P; ++i) {
+        if (mats[i].R < 1) return 0;
+        total += mats[i].R;
+    }
+    if (total > kMaxDim) return 0;
+    return dense_plan(total, K, B).ws_bytes;
+}
+
+nm_status dense_gemv_multi(const dense_matrix *mats, int P, int64_t K, const nm_bf16 *x, int64_t ldx, int B,
+                           void *workspace, size_t workspace_bytes, void *hip_stream) {
+    try {
+        g_err[0] = 0;
+        if (!mats || !x) return fail(NM_ERR_NULL, "dense_gemv_multi: NULL pointer");
+        if (P < 1 || P > nmk::kMaxMats) return fail(NM_ERR_SHAPE, "dense_gemv_multi: P=%d out of range", P);
+        if (K < 8 || K > kMaxDim || K % 8 != 0) return fail(NM_ERR_SHAPE, "dense_gemv_multi: K=%lld", (long long)K);
+        if (B < 1 || B > 8) return fail(NM_ERR_SHAPE, "dense_gemv_multi: B=%d out of range [1, 8]", B);
+        if (ldx < K) return fail(NM_ERR_SHAPE, "dense_gemv_multi: ldx < K");
+        if (ldx % 8 || !aligned(x, 16)) return fail(NM_ERR_ALIGN, "dense_gemv_multi: x alignment");
+        nmk::DenseSet set;
+        int64_t total = 0;
+        set.P = P;
+        for (int i = 0; i < P; ++i) {
+            const dense_matrix &m = mats[i];
+            if (!m.W || !m.y) return fail(NM_ERR_NULL, "dense_gemv_multi: NULL pointer in matrix %d", i);
+            if (m.R < 1 || m.R > kMaxDim || m.ldw < K || m.ldy < m.R)
+                return fail(NM_ERR_SHAPE, "dense_gemv_multi: bad sizes in matrix %d", i);
+            if (m.ldw % 8 || !aligned(m.W, 16) || !aligned(m.y, 2))
+                return fail(NM_ERR_ALIGN, "dense_gemv_multi: matrix %d misaligned", i);
+            set.row0[i] = (int)total;
+            set.W[i] = m.W;
+            set.ldw[i] = m.ldw;
+            set.y[i] = m.y;
+            set.ldy[i] = m.ldy;
+            total += m.R;
+            if (total > kMaxDim) return fail(NM_ERR_SHAPE, "dense_gemv_multi: more than 2^30 rows");
+        }
+        set.row0[P] = (int)total;
+        return dense_run(set, K, x, ldx, B, workspace, workspace_bytes, hip_stream, "dense_gemv_multi");
+    } catch (...) {
+        return fail(NM_ERR_HIP, "dense_gemv_multi: internal error");
     }
 }
 

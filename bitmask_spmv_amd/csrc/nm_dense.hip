@@ -64,27 +64,43 @@ __device__ __forceinline__ void dot_dbatch(const DBatch<U> &bt, const u32x4 *xs4
     }
 }
 
+__device__ __forceinline__ int owner(const DenseSet &set, int r) {
+    int p = 0;
+#pragma unroll
+    for (int q = 1; q < kMaxMats; ++q)
+        if (q < set.P && r >= set.row0[q]) p = q;
+    return p;
+}
+
 template <int B>
-__device__ __forceinline__ void finish_drow(float (&acc)[B], int row, int s, int R, int lane, uint16_t *y,
-                                            int64_t ldy, float *partial) {
+__device__ __forceinline__ void finish_drow(float (&acc)[B], const DenseSet &set, int row, int s, int R, int lane,
+                                            float *partial) {
+    const int p = owner(set, row);
 #pragma unroll
     for (int b = 0; b < B; ++b) {
         const float tot = wave_sum(acc[b]);
         acc[b] = 0.f;
         if (lane == 0) {
             if (gridDim.y == 1)
-                y[(int64_t)b * ldy + row] = f32_to_bf16_rne(tot);
+                set.y[p][(int64_t)b * set.ldy[p] + (row - set.row0[p])] = f32_to_bf16_rne(tot);
             else
                 partial[((int64_t)s * B + b) * R + row] = tot;
         }
     }
 }
 
+template <int U>
+__device__ __forceinline__ void load_row_dbatch(DBatch<U> &bt, const DenseSet &set, int r, int c0, int chunks,
+                                                int base, int lane) {
+    const int p = owner(set, r);
+    const u32x4 *wrow = reinterpret_cast<const u32x4 *>(set.W[p]) + (int64_t)(r - set.row0[p]) * (set.ldw[p] / 8) + c0;
+    load_dbatch<U>(bt, wrow, chunks, base, lane);
+}
+
 template <int B, int U>
-__global__ __launch_bounds__(kThreads) void dense_kernel(const u32x4 *__restrict__ W, int64_t ldw8, int R, int KC,
-                                                         const uint16_t *__restrict__ x, int64_t ldx,
-                                                         uint16_t *__restrict__ y, int64_t ldy,
-                                                         float *__restrict__ partial, int slice) {
+__global__ __launch_bounds__(kThreads) void dense_kernel(const DenseSet set, int KC, const uint16_t *__restrict__ x,
+                                                         int64_t ldx, float *__restrict__ partial, int slice) {
+    const int R = set.row0[set.P];
     extern __shared__ u32x4 xs4[];  // [B][ncs]
     const int s = blockIdx.y;
     const int c0 = s * slice;
@@ -117,7 +133,7 @@ __global__ __launch_bounds__(kThreads) void dense_kernel(const u32x4 *__restrict
                     r[j] = reinterpret_cast<const u32x4 *>(x + (int64_t)b * ldx)[c0 + (i - b * ncs)];
                 }
             }
-            if (i0 == 0) load_dbatch<U>(bufA, W + (int64_t)min(rowA, R - 1) * ldw8 + c0, total > 0 ? ncs : 0, 0, lane);
+            if (i0 == 0) load_row_dbatch<U>(bufA, set, min(rowA, R - 1), c0, total > 0 ? ncs : 0, 0, lane);
 #pragma unroll
             for (int j = 0; j < kStage; ++j) {
                 const int i = i0 + j * kThreads + (int)threadIdx.x;
@@ -137,10 +153,9 @@ __global__ __launch_bounds__(kThreads) void dense_kernel(const u32x4 *__restrict
             biB = 0;
             rowB += row_step;
         }
-        load_dbatch<U>(bufB, W + (int64_t)min(rowB, R - 1) * ldw8 + c0, t + 1 < total ? ncs : 0, biB * kWave * U,
-                       lane);
+        load_row_dbatch<U>(bufB, set, min(rowB, R - 1), c0, t + 1 < total ? ncs : 0, biB * kWave * U, lane);
         dot_dbatch<B, U>(bufA, xs4, ncs, acc);
-        if (biA == nb - 1) finish_drow<B>(acc, rowA, s, R, lane, y, ldy, partial);
+        if (biA == nb - 1) finish_drow<B>(acc, set, rowA, s, R, lane, partial);
         if (t + 1 >= total) break;
         rowA = rowB;
         biA = biB + 1;
@@ -148,23 +163,26 @@ __global__ __launch_bounds__(kThreads) void dense_kernel(const u32x4 *__restrict
             biA = 0;
             rowA += row_step;
         }
-        load_dbatch<U>(bufA, W + (int64_t)min(rowA, R - 1) * ldw8 + c0, t + 2 < total ? ncs : 0, biA * kWave * U,
-                       lane);
+        load_row_dbatch<U>(bufA, set, min(rowA, R - 1), c0, t + 2 < total ? ncs : 0, biA * kWave * U, lane);
         dot_dbatch<B, U>(bufB, xs4, ncs, acc);
-        if (biB == nb - 1) finish_drow<B>(acc, rowB, s, R, lane, y, ldy, partial);
+        if (biB == nb - 1) finish_drow<B>(acc, set, rowB, s, R, lane, partial);
     }
 }
 
 template <int B>
-__global__ __launch_bounds__(256) void dense_finish_kernel(const float *__restrict__ partial, int S, int R,
-                                                           uint16_t *__restrict__ y, int64_t ldy) {
+__global__ __launch_bounds__(256) void dense_finish_kernel(const float *__restrict__ partial, int S,
+                                                           const DenseSet set) {
+    const int R = set.row0[set.P];
     const int i = blockIdx.x * 256 + threadIdx.x;
     if (i >= R) return;
+    int p = 0;
+    for (int q = 1; q < set.P; ++q)
+        if (i >= set.row0[q]) p = q;
 #pragma unroll
     for (int b = 0; b < B; ++b) {
         float t = 0.f;
         for (int s = 0; s < S; ++s) t += partial[((int64_t)s * B + b) * R + i];
-        y[(int64_t)b * ldy + i] = f32_to_bf16_rne(t);
+        set.y[p][(int64_t)b * set.ldy[p] + (i - set.row0[p])] = f32_to_bf16_rne(t);
     }
 }
 
@@ -184,26 +202,26 @@ hipError_t allow_lds(size_t bytes) {
 }
 
 template <int B, int U>
-hipError_t launch_bu(const MvPlan &p, const uint16_t *W, int64_t ldw, int64_t R, int64_t K, const uint16_t *x,
-                     int64_t ldx, uint16_t *y, int64_t ldy, float *ws, hipStream_t st) {
+hipError_t launch_bu(const MvPlan &p, const DenseSet &set, int64_t K, const uint16_t *x, int64_t ldx, float *ws,
+                     hipStream_t st) {
     hipError_t e = allow_lds<B, U>(p.lds_bytes);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((dense_kernel<B, U>), dim3(p.grid_x, p.splits), dim3(kThreads), p.lds_bytes, st,
-                       reinterpret_cast<const u32x4 *>(W), ldw / 8, (int)R, (int)(K / 8), x, ldx, y, ldy, ws,
-                       p.slice);
+    hipLaunchKernelGGL((dense_kernel<B, U>), dim3(p.grid_x, p.splits), dim3(kThreads), p.lds_bytes, st, set,
+                       (int)(K / 8), x, ldx, ws, p.slice);
     e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;
+    const int R = set.row0[set.P];
     hipLaunchKernelGGL(dense_finish_kernel<B>, dim3((unsigned)((R + 255) / 256)), dim3(256), 0, st, ws, p.splits,
-                       (int)R, y, ldy);
+                       set);
     return hipGetLastError();
 }
 
 template <int B>
-hipError_t launch_b(const MvPlan &p, const uint16_t *W, int64_t ldw, int64_t R, int64_t K, const uint16_t *x,
-                    int64_t ldx, uint16_t *y, int64_t ldy, float *ws, hipStream_t st) {
-    if (p.unroll >= 4) return launch_bu<B, 4>(p, W, ldw, R, K, x, ldx, y, ldy, ws, st);
-    if (p.unroll == 2) return launch_bu<B, 2>(p, W, ldw, R, K, x, ldx, y, ldy, ws, st);
-    return launch_bu<B, 1>(p, W, ldw, R, K, x, ldx, y, ldy, ws, st);
+hipError_t launch_b(const MvPlan &p, const DenseSet &set, int64_t K, const uint16_t *x, int64_t ldx, float *ws,
+                    hipStream_t st) {
+    if (p.unroll >= 4) return launch_bu<B, 4>(p, set, K, x, ldx, ws, st);
+    if (p.unroll == 2) return launch_bu<B, 2>(p, set, K, x, ldx, ws, st);
+    return launch_bu<B, 1>(p, set, K, x, ldx, ws, st);
 }
 
 }  // namespace
@@ -249,17 +267,17 @@ MvPlan plan_dense(int64_t R, int64_t K, int B, const DeviceInfo &dev) {
     return p;
 }
 
-hipError_t launch_dense(const MvPlan &p, const uint16_t *W, int64_t ldw, int64_t R, int64_t K, const uint16_t *x,
-                        int64_t ldx, int B, uint16_t *y, int64_t ldy, float *ws, hipStream_t st) {
+hipError_t launch_dense(const MvPlan &p, const DenseSet &set, int64_t K, const uint16_t *x, int64_t ldx, int B,
+                        float *ws, hipStream_t st) {
     switch (B) {
-    case 1: return launch_b<1>(p, W, ldw, R, K, x, ldx, y, ldy, ws, st);
-    case 2: return launch_b<2>(p, W, ldw, R, K, x, ldx, y, ldy, ws, st);
-    case 3: return launch_b<3>(p, W, ldw, R, K, x, ldx, y, ldy, ws, st);
-    case 4: return launch_b<4>(p, W, ldw, R, K, x, ldx, y, ldy, ws, st);
-    case 5: return launch_b<5>(p, W, ldw, R, K, x, ldx, y, ldy, ws, st);
-    case 6: return launch_b<6>(p, W, ldw, R, K, x, ldx, y, ldy, ws, st);
-    case 7: return launch_b<7>(p, W, ldw, R, K, x, ldx, y, ldy, ws, st);
-    case 8: return launch_b<8>(p, W, ldw, R, K, x, ldx, y, ldy, ws, st);
+    case 1: return launch_b<1>(p, set, K, x, ldx, ws, st);
+    case 2: return launch_b<2>(p, set, K, x, ldx, ws, st);
+    case 3: return launch_b<3>(p, set, K, x, ldx, ws, st);
+    case 4: return launch_b<4>(p, set, K, x, ldx, ws, st);
+    case 5: return launch_b<5>(p, set, K, x, ldx, ws, st);
+    case 6: return launch_b<6>(p, set, K, x, ldx, ws, st);
+    case 7: return launch_b<7>(p, set, K, x, ldx, ws, st);
+    case 8: return launch_b<8>(p, set, K, x, ldx, ws, st);
     default: return hipErrorInvalidValue;
     }
 }

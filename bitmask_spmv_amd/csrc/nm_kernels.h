@@ -29,6 +29,28 @@ struct MvPlan {
     size_t ws_bytes = 0;    // workspace bytes (0 when splits == 1)
 };
 
+// Matrices that read the same input x (q, k, v; gate, up) walked by one launch: global
+// row r belongs to matrix p when row0[p] <= r < row0[p + 1]; x is staged once.
+constexpr int kMaxMats = 8;
+
+struct SpmvSet {
+    int P = 0;
+    int row0[kMaxMats + 1] = {};
+    const uint32_t *masks[kMaxMats] = {};
+    const uint16_t *values[kMaxMats] = {};
+    uint16_t *y[kMaxMats] = {};
+    int64_t ldy[kMaxMats] = {};
+};
+
+struct DenseSet {
+    int P = 0;
+    int row0[kMaxMats + 1] = {};
+    const uint16_t *W[kMaxMats] = {};
+    int64_t ldw[kMaxMats] = {};
+    uint16_t *y[kMaxMats] = {};
+    int64_t ldy[kMaxMats] = {};
+};
+
 MvPlan plan_spmv(int64_t R, int64_t K, int B, const DeviceInfo &dev);
 size_t spmv_lds_per_word(int B);  // LDS bytes of x per 32-column block
 MvPlan plan_dense(int64_t R, int64_t K, int B, const DeviceInfo &dev);
@@ -38,9 +60,10 @@ hipError_t launch_prune_pack(const uint16_t *W, int64_t ldw, int64_t R, int64_t 
                              uint32_t *masks, uint16_t *values, hipStream_t st);
 hipError_t launch_unpack(const uint32_t *masks, const uint16_t *values, int64_t R, int64_t K, uint16_t *W,
                          int64_t ldw, hipStream_t st);
-hipError_t launch_spmv(const MvPlan &p, const uint32_t *masks, const uint16_t *values, int64_t R, int64_t K,
-                       const uint16_t *x, int64_t ldx, int B, uint16_t *y, int64_t ldy, float *ws, hipStream_t st);
-hipError_t launch_dense(const MvPlan &p, const uint16_t *W, int64_t ldw, int64_t R, int64_t K, const uint16_t *x,
-                        int64_t ldx, int B, uint16_t *y, int64_t ldy, float *ws, hipStream_t st);
+// R of the plan = total rows of the set (set.row0[set.P]).
+hipError_t launch_spmv(const MvPlan &p, const SpmvSet &set, int64_t K, const uint16_t *x, int64_t ldx, int B,
+                       float *ws, hipStream_t st);
+hipError_t launch_dense(const MvPlan &p, const DenseSet &set, int64_t K, const uint16_t *x, int64_t ldx, int B,
+                        float *ws, hipStream_t st);
 
 }  // namespace nmk

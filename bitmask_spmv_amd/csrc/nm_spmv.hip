@@ -48,7 +48,7 @@ constexpr int blk_dwords(int B) {
 }
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-constexpr int kThreads = 512;     // 8 waves
+constexpr int kThreads = 512;     // default workgroup: 8 waves (256 for matrices with few rows)
 constexpr size_t kLdsCap = 80 * 1024;     // keeps two workgroups resident per CU
 constexpr size_t kLdsPerCu = 160 * 1024;  // gfx950 LDS per compute unit
 
@@ -168,29 +168,47 @@ __device__ __forceinline__ void walk_batch(const Batch<U> &bt, const uint32_t *x
     }
 }
 
+// Matrix of the set that owns global row r (r is wave-uniform: scalar compares).
+__device__ __forceinline__ int owner(const SpmvSet &set, int r) {
+    int p = 0;
+#pragma unroll
+    for (int q = 1; q < kMaxMats; ++q)
+        if (q < set.P && r >= set.row0[q]) p = q;
+    return p;
+}
+
 // Row finished: wave reduction, then either the bf16 result or this slice's fp32 partial.
 template <int B>
-__device__ __forceinline__ void finish_row(float (&acc)[B], int row, int s, int R, int lane, uint16_t *y,
-                                           int64_t ldy, float *partial) {
+__device__ __forceinline__ void finish_row(float (&acc)[B], const SpmvSet &set, int row, int s, int R, int lane,
+                                           float *partial) {
+    const int p = owner(set, row);
 #pragma unroll
     for (int b = 0; b < B; ++b) {
         const float tot = wave_sum(acc[b]);
         acc[b] = 0.f;
         if (lane == 0) {
             if (gridDim.y == 1)
-                y[(int64_t)b * ldy + row] = f32_to_bf16_rne(tot);
+                set.y[p][(int64_t)b * set.ldy[p] + (row - set.row0[p])] = f32_to_bf16_rne(tot);
             else
                 partial[((int64_t)s * B + b) * R + row] = tot;
         }
     }
 }
 
-template <int B, int U>
-__global__ __launch_bounds__(kThreads) void spmv_kernel(const uint32_t *__restrict__ masks,
-                                                        const u32x4 *__restrict__ values, int R, int KW,
-                                                        const uint16_t *__restrict__ x, int64_t ldx,
-                                                        uint16_t *__restrict__ y, int64_t ldy,
-                                                        float *__restrict__ partial, int slice) {
+// Batch loads of global row r, word offset `base` within the slice.
+template <int U>
+__device__ __forceinline__ void load_row_batch(Batch<U> &bt, const SpmvSet &set, int r, int KW, int w0, int words,
+                                               int base, int lane) {
+    const int p = owner(set, r);
+    const int64_t off = (int64_t)(r - set.row0[p]) * KW + w0;
+    load_batch<U>(bt, set.masks[p] + off, reinterpret_cast<const u32x4 *>(set.values[p]) + off * 2, words, base,
+                  lane);
+}
+
+template <int B, int U, int NT>
+__global__ __launch_bounds__(NT) void spmv_kernel(const SpmvSet set, int KW, const uint16_t *__restrict__ x,
+                                                  int64_t ldx, float *__restrict__ partial, int slice) {
+    const int R = set.row0[set.P];
     extern __shared__ uint32_t xs[];  // [nws][XLayout<B>::kBlk]
     const int s = blockIdx.y;
     const int w0 = s * slice;
@@ -199,7 +217,7 @@ __global__ __launch_bounds__(kThreads) void spmv_kernel(const uint32_t *__restri
     // wave-uniform by construction; readfirstlane lets the compiler keep the row loop
     // in scalar registers and branch on it without exec masking
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    constexpr int kWaves = kThreads / kWave;
+    constexpr int kWaves = NT / kWave;
 
     // This wave's rows: first_row, first_row + row_step, ...; each row slice is cut
     // into nb batches, walked as one flat sequence so the next batch's loads are in
@@ -221,19 +239,18 @@ __global__ __launch_bounds__(kThreads) void spmv_kernel(const uint32_t *__restri
         // 16-byte loads; 8 bf16 per chunk, 4 chunks per 32-column block
         constexpr int kStage = 4;
         const int chunks = nws * 4;
-        for (int i0 = 0; i0 < chunks || i0 == 0; i0 += kThreads * kStage) {
+        for (int i0 = 0; i0 < chunks || i0 == 0; i0 += NT * kStage) {
             u32x4 r[kStage];
 #pragma unroll
             for (int j = 0; j < kStage; ++j) {
-                const int i = i0 + j * kThreads + (int)threadIdx.x;
+                const int i = i0 + j * NT + (int)threadIdx.x;
                 if (i < chunks) r[j] = reinterpret_cast<const u32x4 *>(x + (int64_t)w0 * 32)[i];
             }
             if (i0 == 0)
-                load_batch<U>(bufA, masks + (int64_t)min(rowA, R - 1) * KW + w0,
-                              values + ((int64_t)min(rowA, R - 1) * KW + w0) * 2, total > 0 ? nws : 0, 0, lane);
+                load_row_batch<U>(bufA, set, min(rowA, R - 1), KW, w0, total > 0 ? nws : 0, 0, lane);
 #pragma unroll
             for (int j = 0; j < kStage; ++j) {
-                const int i = i0 + j * kThreads + (int)threadIdx.x;
+                const int i = i0 + j * NT + (int)threadIdx.x;
                 if (i < chunks) {
                     uint32_t *d = xs + (i >> 2) * XLayout<B>::kBlk + (i & 3) * 4;
                     d[0] = r[j].x;
@@ -250,20 +267,19 @@ __global__ __launch_bounds__(kThreads) void spmv_kernel(const uint32_t *__restri
         constexpr int kStage = 2;
         const int pairs = nws * 16;
         const uint32_t *x32 = reinterpret_cast<const uint32_t *>(x) + (int64_t)w0 * 16;
-        for (int i0 = 0; i0 < pairs || i0 == 0; i0 += kThreads * kStage) {
+        for (int i0 = 0; i0 < pairs || i0 == 0; i0 += NT * kStage) {
             uint32_t r[kStage][S];
 #pragma unroll
             for (int j = 0; j < kStage; ++j) {
-                const int i = i0 + j * kThreads + (int)threadIdx.x;
+                const int i = i0 + j * NT + (int)threadIdx.x;
 #pragma unroll
                 for (int b = 0; b < S; ++b) r[j][b] = (b < B && i < pairs) ? x32[(int64_t)b * (ldx / 2) + i] : 0u;
             }
             if (i0 == 0)
-                load_batch<U>(bufA, masks + (int64_t)min(rowA, R - 1) * KW + w0,
-                              values + ((int64_t)min(rowA, R - 1) * KW + w0) * 2, total > 0 ? nws : 0, 0, lane);
+                load_row_batch<U>(bufA, set, min(rowA, R - 1), KW, w0, total > 0 ? nws : 0, 0, lane);
 #pragma unroll
             for (int j = 0; j < kStage; ++j) {
-                const int i = i0 + j * kThreads + (int)threadIdx.x;
+                const int i = i0 + j * NT + (int)threadIdx.x;
                 if (i < pairs) {
                     const int c = 2 * i;  // first column of the pair, within the slice
                     uint32_t *d = xs + (c >> 5) * XLayout<B>::kBlk + (c & 31) * (S / 2);
@@ -298,13 +314,9 @@ __global__ __launch_bounds__(kThreads) void spmv_kernel(const uint32_t *__restri
             biB = 0;
             rowB += row_step;
         }
-        {
-            const int r = min(rowB, R - 1);
-            load_batch<U>(bufB, masks + (int64_t)r * KW + w0, values + ((int64_t)r * KW + w0) * 2,
-                          t + 1 < total ? nws : 0, biB * kWave * U, lane);
-        }
+        load_row_batch<U>(bufB, set, min(rowB, R - 1), KW, w0, t + 1 < total ? nws : 0, biB * kWave * U, lane);
         walk_batch<B, U>(bufA, xs, nws, acc);
-        if (biA == nb - 1) finish_row<B>(acc, rowA, s, R, lane, y, ldy, partial);
+        if (biA == nb - 1) finish_row<B>(acc, set, rowA, s, R, lane, partial);
         if (t + 1 >= total) break;
         // A <- batch t+2, walk B (batch t+1)
         rowA = rowB;
@@ -313,32 +325,32 @@ __global__ __launch_bounds__(kThreads) void spmv_kernel(const uint32_t *__restri
             biA = 0;
             rowA += row_step;
         }
-        {
-            const int r = min(rowA, R - 1);
-            load_batch<U>(bufA, masks + (int64_t)r * KW + w0, values + ((int64_t)r * KW + w0) * 2,
-                          t + 2 < total ? nws : 0, biA * kWave * U, lane);
-        }
+        load_row_batch<U>(bufA, set, min(rowA, R - 1), KW, w0, t + 2 < total ? nws : 0, biA * kWave * U, lane);
         walk_batch<B, U>(bufB, xs, nws, acc);
-        if (biB == nb - 1) finish_row<B>(acc, rowB, s, R, lane, y, ldy, partial);
+        if (biB == nb - 1) finish_row<B>(acc, set, rowB, s, R, lane, partial);
     }
 }
 
 // Second pass of split rows: add the slices in order, round once to bf16.
 template <int B>
-__global__ __launch_bounds__(256) void split_finish_kernel(const float *__restrict__ partial, int S, int R,
-                                                           uint16_t *__restrict__ y, int64_t ldy) {
+__global__ __launch_bounds__(256) void split_finish_kernel(const float *__restrict__ partial, int S,
+                                                           const SpmvSet set) {
+    const int R = set.row0[set.P];
     const int i = blockIdx.x * 256 + threadIdx.x;
     if (i >= R) return;
+    int p = 0;
+    for (int q = 1; q < set.P; ++q)
+        if (i >= set.row0[q]) p = q;
 #pragma unroll
     for (int b = 0; b < B; ++b) {
         float t = 0.f;
         for (int s = 0; s < S; ++s) t += partial[((int64_t)s * B + b) * R + i];
-        y[(int64_t)b * ldy + i] = f32_to_bf16_rne(t);
+        set.y[p][(int64_t)b * set.ldy[p] + (i - set.row0[p])] = f32_to_bf16_rne(t);
     }
 }
 
 // Raise the dynamic-LDS limit of one kernel instance once per device.
-template <int B, int U>
+template <int B, int U, int NT>
 hipError_t allow_lds(size_t bytes) {
     static std::atomic<uint64_t> done{0};
     if (bytes <= 64 * 1024) return hipSuccess;
@@ -347,32 +359,36 @@ hipError_t allow_lds(size_t bytes) {
     if (e != hipSuccess) return e;
     const uint64_t bit = 1ull << (dev & 63);
     if (done.load(std::memory_order_acquire) & bit) return hipSuccess;
-    e = hipFuncSetAttribute((const void *)spmv_kernel<B, U>, hipFuncAttributeMaxDynamicSharedMemorySize,
+    e = hipFuncSetAttribute((const void *)spmv_kernel<B, U, NT>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)kLdsCap);
     if (e == hipSuccess) done.fetch_or(bit, std::memory_order_acq_rel);
     return e;
 }
 
-template <int B, int U>
-hipError_t launch_bu(const MvPlan &p, const uint32_t *masks, const uint16_t *values, int64_t R, int64_t K,
-                     const uint16_t *x, int64_t ldx, uint16_t *y, int64_t ldy, float *ws, hipStream_t st) {
-    hipError_t e = allow_lds<B, U>(p.lds_bytes);
+template <int B, int U, int NT>
+hipError_t launch_bu(const MvPlan &p, const SpmvSet &set, int64_t K, const uint16_t *x, int64_t ldx, float *ws,
+                     hipStream_t st) {
+    hipError_t e = allow_lds<B, U, NT>(p.lds_bytes);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((spmv_kernel<B, U>), dim3(p.grid_x, p.splits), dim3(kThreads), p.lds_bytes, st, masks,
-                       reinterpret_cast<const u32x4 *>(values), (int)R, (int)(K / 32), x, ldx, y, ldy, ws, p.slice);
+    hipLaunchKernelGGL((spmv_kernel<B, U, NT>), dim3(p.grid_x, p.splits), dim3(NT), p.lds_bytes, st, set,
+                       (int)(K / 32), x, ldx, ws, p.slice);
     e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;
+    const int R = set.row0[set.P];
     hipLaunchKernelGGL(split_finish_kernel<B>, dim3((unsigned)((R + 255) / 256)), dim3(256), 0, st, ws, p.splits,
-                       (int)R, y, ldy);
+                       set);
     return hipGetLastError();
 }
 
 template <int B>
-hipError_t launch_b(const MvPlan &p, const uint32_t *masks, const uint16_t *values, int64_t R, int64_t K,
-                    const uint16_t *x, int64_t ldx, uint16_t *y, int64_t ldy, float *ws, hipStream_t st) {
-    if (p.unroll >= 4) return launch_bu<B, 4>(p, masks, values, R, K, x, ldx, y, ldy, ws, st);
-    if (p.unroll == 2) return launch_bu<B, 2>(p, masks, values, R, K, x, ldx, y, ldy, ws, st);
-    return launch_bu<B, 1>(p, masks, values, R, K, x, ldx, y, ldy, ws, st);
+hipError_t launch_b(const MvPlan &p, const SpmvSet &set, int64_t K, const uint16_t *x, int64_t ldx, float *ws,
+                    hipStream_t st) {
+    if (p.threads == 256) {
+        if (p.unroll >= 2) return launch_bu<B, 2, 256>(p, set, K, x, ldx, ws, st);
+        return launch_bu<B, 1, 256>(p, set, K, x, ldx, ws, st);
+    }
+    if (p.unroll >= 2) return launch_bu<B, 2, 512>(p, set, K, x, ldx, ws, st);
+    return launch_bu<B, 1, 512>(p, set, K, x, ldx, ws, st);
 }
 
 }  // namespace
@@ -411,7 +427,10 @@ MvPlan plan_spmv(int64_t R, int64_t K, int B, const DeviceInfo &dev) {
     int per_cu = (int)(kLdsPerCu / (p.lds_bytes > 0 ? p.lds_bytes : 1));
     if (per_cu > 4) per_cu = 4;
     if (per_cu < 1) per_cu = 1;
-    const int64_t waves = kThreads / kWave;
+    // Matrices with too few rows to give every CU a 512-thread workgroup use 256-thread
+    // workgroups, which spreads them over twice as many CUs.
+    if ((R + kThreads / kWave - 1) / (kThreads / kWave) * splits < cu) p.threads = 256;
+    const int64_t waves = p.threads / kWave;
     int64_t gx = (R + waves - 1) / waves;
     int64_t cap_x = (per_cu * cu + splits - 1) / splits;
     if (gx > cap_x) gx = cap_x;
@@ -422,17 +441,17 @@ MvPlan plan_spmv(int64_t R, int64_t K, int B, const DeviceInfo &dev) {
     return p;
 }
 
-hipError_t launch_spmv(const MvPlan &p, const uint32_t *masks, const uint16_t *values, int64_t R, int64_t K,
-                       const uint16_t *x, int64_t ldx, int B, uint16_t *y, int64_t ldy, float *ws, hipStream_t st) {
+hipError_t launch_spmv(const MvPlan &p, const SpmvSet &set, int64_t K, const uint16_t *x, int64_t ldx, int B,
+                       float *ws, hipStream_t st) {
     switch (B) {
-    case 1: return launch_b<1>(p, masks, values, R, K, x, ldx, y, ldy, ws, st);
-    case 2: return launch_b<2>(p, masks, values, R, K, x, ldx, y, ldy, ws, st);
-    case 3: return launch_b<3>(p, masks, values, R, K, x, ldx, y, ldy, ws, st);
-    case 4: return launch_b<4>(p, masks, values, R, K, x, ldx, y, ldy, ws, st);
-    case 5: return launch_b<5>(p, masks, values, R, K, x, ldx, y, ldy, ws, st);
-    case 6: return launch_b<6>(p, masks, values, R, K, x, ldx, y, ldy, ws, st);
-    case 7: return launch_b<7>(p, masks, values, R, K, x, ldx, y, ldy, ws, st);
-    case 8: return launch_b<8>(p, masks, values, R, K, x, ldx, y, ldy, ws, st);
+    case 1: return launch_b<1>(p, set, K, x, ldx, ws, st);
+    case 2: return launch_b<2>(p, set, K, x, ldx, ws, st);
+    case 3: return launch_b<3>(p, set, K, x, ldx, ws, st);
+    case 4: return launch_b<4>(p, set, K, x, ldx, ws, st);
+    case 5: return launch_b<5>(p, set, K, x, ldx, ws, st);
+    case 6: return launch_b<6>(p, set, K, x, ldx, ws, st);
+    case 7: return launch_b<7>(p, set, K, x, ldx, ws, st);
+    case 8: return launch_b<8>(p, set, K, x, ldx, ws, st);
     default: return hipErrorInvalidValue;
     }
 }

@@ -134,6 +134,39 @@ nm_status dense_gemv(const nm_bf16 *W, int64_t ldw, int64_t R, int64_t K, const 
                      void *hip_stream);
 
 /*
+ * nm_spmv_multi -- several packed matrices that read the same input x in one launch,
+ * e.g. the q, k and v projections of an attention block, or gate and up of an MLP
+ * (each is one pruned linear of the decode step [SD-cn, 方法步骤详情 第四步]).  x is
+ * staged once and one grid walks the rows of all matrices; results are identical to P
+ * separate nm_spmv calls with the same x (the per-row arithmetic does not change).
+ * mats: HOST array of P descriptors (1 <= P <= 8), read during the call only; every
+ * matrix has K columns, its own R, canonical masks/values and output y [B][ldy].
+ * Total rows <= 2^30.  Workspace as for nm_spmv, sized by nm_spmv_multi_workspace_bytes.
+ */
+typedef struct {
+    const uint32_t *masks;  /* [R][K/32] */
+    const nm_bf16 *values;  /* [R][K/2]  */
+    int64_t R;
+    nm_bf16 *y;             /* [B][ldy], ldy >= R */
+    int64_t ldy;
+} nm_spmv_matrix;
+size_t nm_spmv_multi_workspace_bytes(const nm_spmv_matrix *mats, int P, int64_t K, int B);
+nm_status nm_spmv_multi(const nm_spmv_matrix *mats, int P, int64_t K, const nm_bf16 *x, int64_t ldx, int B,
+                        void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* dense_gemv_multi -- the dense baseline for the same grouping (same conventions). */
+typedef struct {
+    const nm_bf16 *W;  /* [R][ldw] */
+    int64_t ldw;
+    int64_t R;
+    nm_bf16 *y;        /* [B][ldy] */
+    int64_t ldy;
+} dense_matrix;
+size_t dense_gemv_multi_workspace_bytes(const dense_matrix *mats, int P, int64_t K, int B);
+nm_status dense_gemv_multi(const dense_matrix *mats, int P, int64_t K, const nm_bf16 *x, int64_t ldx, int B,
+                           void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/*
  * nm_unpack -- inverse of the packing: W_out[i][j] = kept value of column j, or +0.0
  * where the bit is clear.  W_out: bf16 [R][ldw] (ldw >= K, multiple of 8).
  * Requires R >= 1, K >= 32, K % 32 == 0 and 16 set bits per mask word.

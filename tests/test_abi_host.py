@@ -126,3 +126,34 @@ def test_workspace_size_queries_are_consistent(L):
         assert ws % (4 * R * B) == 0
         ws = L.dense_gemv_workspace_bytes(R, K, B)
         assert ws % (4 * R * B) == 0
+
+
+class _Mat(ctypes.Structure):
+    _fields_ = [("a", ctypes.c_void_p), ("b", ctypes.c_void_p), ("R", ctypes.c_int64), ("y", ctypes.c_void_p),
+                ("ldy", ctypes.c_int64)]
+
+
+def test_multi_entry_points_reject_bad_arguments(L):
+    p, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    L.nm_spmv_multi.argtypes = [p, i32, i64, p, i64, i32, p, sz, p]
+    L.dense_gemv_multi.argtypes = [p, i32, i64, p, i64, i32, p, sz, p]
+    good = (_Mat * 2)(_Mat(A4, A16, 8, A16, 8), _Mat(A4, A16, 8, A16, 8))
+    arr = ctypes.cast(good, ctypes.c_void_p)
+    assert L.nm_spmv_multi(None, 2, 64, A16, 64, 1, None, 0, None) == NM_ERR_NULL
+    assert L.nm_spmv_multi(arr, 2, 64, None, 64, 1, None, 0, None) == NM_ERR_NULL
+    assert L.nm_spmv_multi(arr, 0, 64, A16, 64, 1, None, 0, None) == NM_ERR_SHAPE
+    assert L.nm_spmv_multi(arr, 9, 64, A16, 64, 1, None, 0, None) == NM_ERR_SHAPE
+    assert L.nm_spmv_multi(arr, 2, 48, A16, 64, 1, None, 0, None) == NM_ERR_SHAPE
+    assert L.nm_spmv_multi(arr, 2, 64, A16, 64, 9, None, 0, None) == NM_ERR_SHAPE
+    assert L.nm_spmv_multi(arr, 2, 64, A4, 64, 1, None, 0, None) == NM_ERR_ALIGN
+    bad = (_Mat * 2)(_Mat(A4, A16, 8, A16, 8), _Mat(A4, None, 8, A16, 8))
+    assert L.nm_spmv_multi(ctypes.cast(bad, p), 2, 64, A16, 64, 1, None, 0, None) == NM_ERR_NULL
+    bad = (_Mat * 2)(_Mat(A4, A16, 8, A16, 8), _Mat(A4, A4, 8, A16, 8))
+    assert L.nm_spmv_multi(ctypes.cast(bad, p), 2, 64, A16, 64, 1, None, 0, None) == NM_ERR_ALIGN
+    bad = (_Mat * 2)(_Mat(A4, A16, 8, A16, 8), _Mat(A4, A16, 0, A16, 8))
+    assert L.nm_spmv_multi(ctypes.cast(bad, p), 2, 64, A16, 64, 1, None, 0, None) == NM_ERR_SHAPE
+    dgood = (_Mat * 1)(_Mat(A16, 64, 8, A16, 8))
+    assert L.dense_gemv_multi(ctypes.cast(dgood, p), 1, 64, None, 64, 1, None, 0, None) == NM_ERR_NULL
+    assert L.dense_gemv_multi(ctypes.cast(dgood, p), 1, 60, A16, 64, 1, None, 0, None) == NM_ERR_SHAPE
+    dbad = (_Mat * 1)(_Mat(A4, 64, 8, A16, 8))
+    assert L.dense_gemv_multi(ctypes.cast(dbad, p), 1, 64, A16, 64, 1, None, 0, None) == NM_ERR_ALIGN

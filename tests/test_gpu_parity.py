@@ -330,3 +330,58 @@ def test_full_size_sampled(name, R, K, N, M, B):
     assert_within(host_bf16(y)[:, rows], yref, absum, f"{name} sparse")
     ydref, adabs = oracle.dense(Ws, xh, nthreads=4)
     assert_within(host_bf16(yd)[:, rows], ydref, adabs, f"{name} dense")
+
+
+# ------------------------------------------------------------------ several matrices, one launch
+@pytest.mark.parametrize("B", [1, 4])
+def test_spmv_multi_matches_oracle_and_separate_calls(B):
+    say("spmv multi", B)
+    K = 4096
+    Rs = [640, 520, 1000]  # q/k/v-like group with ragged row counts
+    x = synth.decode_x(B, K, 18, B)
+    n = oracle.col_norm(synth.calib_acts(K, 18))
+    refs, packed = [], []
+    for i, R in enumerate(Rs):
+        W = synth.weights(R, K, 18, i)
+        mref, vref = oracle.prune_pack(W, n, 8, 16)
+        refs.append(oracle.spmv(mref, vref, x, K, nthreads=4))
+        packed.append((dev_u32(mref), dev_bf16(vref)))
+    xd = dev_bf16(x)
+    ys = nm.nm_spmv_multi(packed, xd)
+    singles = [nm.nm_spmv(m, v, xd) for m, v in packed]
+    for i, (y, (yref, absum)) in enumerate(zip(ys, refs)):
+        assert_within(host_bf16(y), yref, absum, f"multi matrix {i}")
+        # every matrix has >= 512 rows, so neither launch splits rows: identical arithmetic
+        assert (host_bf16(y) == host_bf16(singles[i])).all()
+
+
+def test_spmv_multi_split_rows_and_single_matrix():
+    say("spmv multi split rows")
+    K = 8192
+    Rs = [7, 33]
+    x = synth.decode_x(2, K, 19)
+    packed, refs = [], []
+    for i, R in enumerate(Rs):
+        W = synth.weights(R, K, 19, i)
+        mref, vref = oracle.prune_pack(W, oracle.col_norm(synth.calib_acts(K, 19, i)), 2, 4)
+        refs.append(oracle.spmv(mref, vref, x, K))
+        packed.append((dev_u32(mref), dev_bf16(vref)))
+    assert nm.nm_spmv_multi_workspace_bytes(Rs, K, 2) > 0
+    ys = nm.nm_spmv_multi(packed, dev_bf16(x))
+    for i, (y, (yref, absum)) in enumerate(zip(ys, refs)):
+        assert_within(host_bf16(y), yref, absum, f"split multi {i}")
+    y1 = nm.nm_spmv_multi(packed[:1], dev_bf16(x))[0]
+    assert_within(host_bf16(y1), *refs[0], "single-matrix multi")
+
+
+@pytest.mark.parametrize("B", [1, 8])
+def test_dense_multi_matches_oracle(B):
+    say("dense multi", B)
+    K = 4096
+    Rs = [700, 96, 1500]
+    x = synth.decode_x(B, K, 20, B)
+    Ws = [synth.weights(R, K, 20, i) for i, R in enumerate(Rs)]
+    ys = nm.dense_gemv_multi([dev_bf16(W) for W in Ws], dev_bf16(x))
+    for i, (y, W) in enumerate(zip(ys, Ws)):
+        yref, absum = oracle.dense(W, x, nthreads=4)
+        assert_within(host_bf16(y), yref, absum, f"dense multi {i}")
