@@ -70,6 +70,14 @@ def sparse_bytes(R, K, B):
     return R * K + R * K // 8 + 2 * B * K + 2 * B * R
 
 
+META_BYTES_PER_KEPT = {"bitmask": 0.25, "u8_offset": 1, "i32_index": 4}
+
+
+def meta_format_bytes(fmt, R, K, B):
+    """Algorithmic bytes of one SpMV call with the given metadata format."""
+    return R * K + int(META_BYTES_PER_KEPT[fmt] * R * K // 2) + 2 * B * K + 2 * B * R
+
+
 def dense_bytes(R, K, B):
     return 2 * R * K + 2 * B * K + 2 * B * R
 
@@ -86,6 +94,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=12)
     ap.add_argument("--skip-check", action="store_true", help="skip the oracle spot check")
+    ap.add_argument("--no-meta-formats", action="store_true",
+                    help="skip the bitmask vs uint8-offset vs int32-index comparison table")
     ap.add_argument("--profile-kernel", action="store_true",
                     help="counter-collection mode: only the dominant launch shape (eager, rotated) plus a "
                          "plain 256 MiB device copy used to calibrate the byte counters")
@@ -351,6 +361,42 @@ def main():
         del g, gl
     torch.cuda.synchronize()
 
+    # ---------------------------------------------------------------- metadata formats
+    # The same product over the first pattern's packs with the metadata as uint8 offsets
+    # and int32 column indices (converted on the device from the masks), each timed over
+    # >= 512 MB of distinct buffers like the table above.
+    meta_table = None
+    if not args.no_meta_formats:
+        meta_table = {}
+        (N, M) = patterns[0]
+        fmts = (("u8_offset", nm.NM_META_U8_OFFSET), ("i32_index", nm.NM_META_I32_INDEX))
+        for name, R, K, group in projs:
+            d = meta_table.setdefault(name, {"R": R, "K": K, "pattern": f"{N}:{M}"})
+            bm = per[name][f"{N}:{M}"]
+            d["bitmask"] = {"us": bm["us"], "GBs": bm["GBs"], "bytes": meta_format_bytes("bitmask", R, K, B)}
+            for key, fmt in fmts:
+                nb = meta_format_bytes(key, R, K, B)
+                cnt = min(len(pool_sparse[(N, M), name]), max(2, math.ceil(ROTATE_BYTES / nb)))
+                pool = [(nm.nm_meta_from_mask(mk, fmt), v) for mk, v in pool_sparse[(N, M), name][:cnt]]
+                # same arithmetic as the bitmask kernel: outputs must agree bit for bit
+                mk0, v0 = pool_sparse[(N, M), name][0]
+                yb = nm.nm_spmv(mk0, v0, xs[group][0], workspace=ws)
+                ym = nm.nm_spmv_meta(pool[0][0], fmt, v0, xs[group][0], workspace=ws)
+                assert torch.equal(yb.view(torch.int16), ym.view(torch.int16)), f"{key} {name} differs from bitmask"
+                fns = [(lambda mt=mt, v=v, x=xs[group][i % L]:
+                        nm.nm_spmv_meta(mt, fmt, v, x, out=ys[name], workspace=ws)) for i, (mt, v) in enumerate(pool)]
+                g = capture(torch, fns)
+                g.replay()
+                us = min(timer.time_graph(g, 1) for _ in range(reps)) * 1e3 / len(fns)
+                d[key] = {"us": round(us, 2), "GBs": round(nb / us / 1e3, 1), "bytes": nb,
+                          "slowdown_vs_bitmask": round(us / bm["us"], 3),
+                          "rotation_MB": round(len(fns) * nb / 1e6)}
+                del g, pool, fns
+            torch.cuda.synchronize()
+        log("metadata formats (us): " + "; ".join(
+            f"{n} bitmask {d['bitmask']['us']} u8 {d['u8_offset']['us']} i32 {d['i32_index']['us']}"
+            for n, d in meta_table.items()))
+
     # Dominant kernel: the launch shape (R x K) whose launches take the largest share of
     # the step (projections of equal shape, e.g. gate and up, are one launch shape).
     share = {}
@@ -428,6 +474,7 @@ def main():
                        "speedup_vs_dense": round(ms_fused_dense * len(patterns) / ms_fused, 3),
                        "groups": ["|".join(pr[0] for pr in grp) for grp in groups]},
         "per_layer": per,
+        "metadata_formats": meta_table,
         "pack_GBs": round(pack_bytes / pack_ms / 1e6, 1),
         "parity": parity,
         "roofline": roofline,

@@ -22,11 +22,13 @@ __all__ = [
     "NmError", "LIB_PATH", "lib", "nm_version", "nm_col_norm", "nm_prune_pack", "nm_spmv",
     "nm_spmv_workspace_bytes", "dense_gemv", "dense_gemv_workspace_bytes", "nm_unpack",
     "NM_PATTERNS", "nm_spmv_multi", "nm_spmv_multi_workspace_bytes", "dense_gemv_multi",
-    "dense_gemv_multi_workspace_bytes",
+    "dense_gemv_multi_workspace_bytes", "NM_META_BITMASK", "NM_META_U8_OFFSET", "NM_META_I32_INDEX",
+    "nm_meta_from_mask", "nm_spmv_meta",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnmspmv.so")
 NM_PATTERNS = ((2, 4), (4, 8), (8, 16), (16, 32))
+NM_META_BITMASK, NM_META_U8_OFFSET, NM_META_I32_INDEX = 0, 1, 2
 
 _STATUS = {0: "NM_OK", 1: "NM_ERR_NULL", 2: "NM_ERR_SHAPE", 3: "NM_ERR_PATTERN", 4: "NM_ERR_ALIGN",
            5: "NM_ERR_WORKSPACE", 6: "NM_ERR_HIP"}
@@ -65,6 +67,8 @@ def _load() -> ctypes.CDLL:
     L.dense_gemv_workspace_bytes.argtypes, L.dense_gemv_workspace_bytes.restype = [i64, i64, i32], sz
     L.dense_gemv.argtypes = [p, i64, i64, i64, p, i64, i32, p, i64, p, sz, p]
     L.nm_unpack.argtypes = [p, p, i64, i64, p, i64, p]
+    L.nm_meta_from_mask.argtypes = [p, i64, i64, i32, p, p]
+    L.nm_spmv_meta.argtypes = [p, i32, p, i64, i64, p, i64, i32, p, i64, p, sz, p]
     L.nm_spmv_multi_workspace_bytes.argtypes = [p, i32, i64, i32]
     L.nm_spmv_multi_workspace_bytes.restype = sz
     L.nm_spmv_multi.argtypes = [p, i32, i64, p, i64, i32, p, sz, p]
@@ -224,6 +228,52 @@ def nm_unpack(masks: torch.Tensor, values: torch.Tensor, out: torch.Tensor | Non
     _dev(out, "out", torch.bfloat16, 2)
     _check(lib.nm_unpack(_ptr(masks), _ptr(values), R, K, _ptr(out), _ld(out), _stream(masks)))
     return out
+
+
+def _meta_shape(fmt: int, R: int, K: int):
+    if fmt == NM_META_BITMASK:
+        return torch.int32, (R, K // 32)
+    if fmt == NM_META_U8_OFFSET:
+        return torch.uint8, (R, K // 2)
+    if fmt == NM_META_I32_INDEX:
+        return torch.int32, (R, K // 2)
+    raise ValueError(f"unknown metadata format {fmt}")
+
+
+def nm_meta_from_mask(masks: torch.Tensor, fmt: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Canonical masks int32 [R, K/32] -> uint8 offsets [R, K/2] (NM_META_U8_OFFSET) or int32
+    column indices [R, K/2] (NM_META_I32_INDEX), in the order of the packed values."""
+    _dev(masks, "masks", torch.int32, 2)
+    if not masks.is_contiguous():
+        raise ValueError("masks must be contiguous")
+    R, K = masks.shape[0], masks.shape[1] * 32
+    if fmt not in (NM_META_U8_OFFSET, NM_META_I32_INDEX):
+        raise ValueError("fmt must be NM_META_U8_OFFSET or NM_META_I32_INDEX")
+    dtype, shape = _meta_shape(fmt, R, K)
+    if out is None:
+        out = torch.empty(shape, dtype=dtype, device=masks.device)
+    _dev(out, "out", dtype, 2)
+    if out.shape != shape or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous {dtype} tensor of shape {shape}")
+    _check(lib.nm_meta_from_mask(_ptr(masks), R, K, int(fmt), _ptr(out), _stream(masks)))
+    return out
+
+
+def nm_spmv_meta(meta: torch.Tensor, fmt: int, values: torch.Tensor, x: torch.Tensor,
+                 out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """nm_spmv with metadata in any format: masks int32 [R, K/32] (NM_META_BITMASK), uint8 offsets
+    [R, K/2] (NM_META_U8_OFFSET) or int32 column indices [R, K/2] (NM_META_I32_INDEX)."""
+    _dev(values, "values", torch.bfloat16, 2)
+    R, K = values.shape[0], values.shape[1] * 2
+    dtype, shape = _meta_shape(fmt, R, K)
+    _dev(meta, "meta", dtype, 2)
+    if meta.shape != shape or not (meta.is_contiguous() and values.is_contiguous()):
+        raise ValueError(f"meta must be a contiguous {dtype} tensor of shape {shape}, values contiguous")
+    x2, B, o2, out, squeeze = _x_y(x, R, K, out)
+    ws, ws_bytes = _workspace(nm_spmv_workspace_bytes(R, K, B), x2, workspace)
+    _check(lib.nm_spmv_meta(_ptr(meta), int(fmt), _ptr(values), R, K, _ptr(x2), _ld(x2), B, _ptr(o2), _ld(o2),
+                            _ptr(ws), ws_bytes, _stream(x2)))
+    return out[0] if squeeze and out.dim() == 2 else out
 
 
 def _multi_outs(x2, Rs, outs):

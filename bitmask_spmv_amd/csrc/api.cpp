@@ -65,7 +65,7 @@ nmk::DeviceInfo device_info() {
 }
 
 // Optional launch-plan override for tuning sweeps: "<splits>,<grid_x>,<unroll>"
-// (0 keeps the planner's choice for that field).  The slice length follows from splits.
+// (0 keeps the planner's choice for that field; unroll only affects the dense kernel).  The slice length follows from splits.
 void apply_override(const char *env, int64_t units, int64_t R, int B, size_t unit_lds, nmk::MvPlan &p) {
     const char *s = std::getenv(env);
     if (!s || !*s) return;
@@ -170,7 +170,7 @@ size_t nm_spmv_workspace_bytes(int64_t R, int64_t K, int B) {
 }
 
 // Shared body of nm_spmv / nm_spmv_multi once the matrices are validated into a set.
-static nm_status spmv_run(const nmk::SpmvSet &set, int64_t K, const nm_bf16 *x, int64_t ldx, int B,
+static nm_status spmv_run(const nmk::SpmvSet &set, int fmt, int64_t K, const nm_bf16 *x, int64_t ldx, int B,
                           void *workspace, size_t workspace_bytes, void *hip_stream, const char *who) {
     const int64_t R = set.row0[set.P];
     const nmk::MvPlan p = spmv_plan(R, K, B);
@@ -179,32 +179,73 @@ static nm_status spmv_run(const nmk::SpmvSet &set, int64_t K, const nm_bf16 *x, 
             return fail(NM_ERR_WORKSPACE, "%s: workspace of %zu bytes required, %zu given", who, p.ws_bytes,
                         workspace ? workspace_bytes : (size_t)0);
     }
-    hipError_t e = nmk::launch_spmv(p, set, K, x, ldx, B, (float *)workspace, (hipStream_t)hip_stream);
+    hipError_t e = nmk::launch_spmv(p, set, fmt, K, x, ldx, B, (float *)workspace, (hipStream_t)hip_stream);
     if (e != hipSuccess) return hip_fail(who, e);
     return NM_OK;
+}
+
+// Shared body of nm_spmv / nm_spmv_meta (one matrix).
+static nm_status spmv_one(const void *meta, int fmt, const nm_bf16 *values, int64_t R, int64_t K, const nm_bf16 *x,
+                          int64_t ldx, int B, nm_bf16 *y, int64_t ldy, void *workspace, size_t workspace_bytes,
+                          void *hip_stream, const char *who) {
+    if (!meta || !values || !x || !y) return fail(NM_ERR_NULL, "%s: NULL pointer", who);
+    if (fmt != NM_META_BITMASK && fmt != NM_META_U8_OFFSET && fmt != NM_META_I32_INDEX)
+        return fail(NM_ERR_PATTERN, "%s: unknown metadata format %d", who, fmt);
+    if (K < 32 || K > kMaxDim || K % 32 != 0)
+        return fail(NM_ERR_SHAPE, "%s: K=%lld must be a positive multiple of 32", who, (long long)K);
+    nm_status st = check_mv_common(R, K, B, ldx, ldy, x, y);
+    if (st != NM_OK) return st;
+    if (!aligned(meta, fmt == NM_META_BITMASK ? 4 : 16) || !aligned(values, 16))
+        return fail(NM_ERR_ALIGN, "%s: metadata needs 4-byte (masks) or 16-byte (index formats) and values 16-byte "
+                                  "alignment", who);
+    nmk::SpmvSet set;
+    set.P = 1;
+    set.row0[1] = (int)R;
+    set.meta[0] = meta;
+    set.values[0] = values;
+    set.y[0] = y;
+    set.ldy[0] = ldy;
+    return spmv_run(set, fmt, K, x, ldx, B, workspace, workspace_bytes, hip_stream, who);
 }
 
 nm_status nm_spmv(const uint32_t *masks, const nm_bf16 *values, int64_t R, int64_t K, const nm_bf16 *x, int64_t ldx,
                   int B, nm_bf16 *y, int64_t ldy, void *workspace, size_t workspace_bytes, void *hip_stream) {
     try {
         g_err[0] = 0;
-        if (!masks || !values || !x || !y) return fail(NM_ERR_NULL, "nm_spmv: NULL pointer");
-        if (K < 32 || K > kMaxDim || K % 32 != 0)
-            return fail(NM_ERR_SHAPE, "nm_spmv: K=%lld must be a positive multiple of 32", (long long)K);
-        nm_status st = check_mv_common(R, K, B, ldx, ldy, x, y);
-        if (st != NM_OK) return st;
-        if (!aligned(masks, 4) || !aligned(values, 16))
-            return fail(NM_ERR_ALIGN, "nm_spmv: masks need 4-byte and values 16-byte alignment");
-        nmk::SpmvSet set;
-        set.P = 1;
-        set.row0[1] = (int)R;
-        set.masks[0] = masks;
-        set.values[0] = values;
-        set.y[0] = y;
-        set.ldy[0] = ldy;
-        return spmv_run(set, K, x, ldx, B, workspace, workspace_bytes, hip_stream, "nm_spmv");
+        return spmv_one(masks, NM_META_BITMASK, values, R, K, x, ldx, B, y, ldy, workspace, workspace_bytes,
+                        hip_stream, "nm_spmv");
     } catch (...) {
         return fail(NM_ERR_HIP, "nm_spmv: internal error");
+    }
+}
+
+nm_status nm_spmv_meta(const void *meta, int format, const nm_bf16 *values, int64_t R, int64_t K, const nm_bf16 *x,
+                       int64_t ldx, int B, nm_bf16 *y, int64_t ldy, void *workspace, size_t workspace_bytes,
+                       void *hip_stream) {
+    try {
+        g_err[0] = 0;
+        return spmv_one(meta, format, values, R, K, x, ldx, B, y, ldy, workspace, workspace_bytes, hip_stream,
+                        "nm_spmv_meta");
+    } catch (...) {
+        return fail(NM_ERR_HIP, "nm_spmv_meta: internal error");
+    }
+}
+
+nm_status nm_meta_from_mask(const uint32_t *masks, int64_t R, int64_t K, int format, void *meta, void *hip_stream) {
+    try {
+        g_err[0] = 0;
+        if (!masks || !meta) return fail(NM_ERR_NULL, "nm_meta_from_mask: NULL pointer");
+        if (format != NM_META_U8_OFFSET && format != NM_META_I32_INDEX)
+            return fail(NM_ERR_PATTERN, "nm_meta_from_mask: format %d is not an index format", format);
+        if (R < 1 || R > kMaxDim || K < 32 || K > kMaxDim || K % 32 != 0)
+            return fail(NM_ERR_SHAPE, "nm_meta_from_mask: bad sizes R=%lld K=%lld", (long long)R, (long long)K);
+        if (!aligned(masks, 4) || !aligned(meta, 16))
+            return fail(NM_ERR_ALIGN, "nm_meta_from_mask: masks need 4-byte and meta 16-byte alignment");
+        hipError_t e = nmk::launch_meta_from_mask(masks, R, K, format, meta, (hipStream_t)hip_stream);
+        if (e != hipSuccess) return hip_fail("nm_meta_from_mask launch", e);
+        return NM_OK;
+    } catch (...) {
+        return fail(NM_ERR_HIP, "nm_meta_from_mask: internal error");
     }
 }
 
@@ -225,7 +266,7 @@ static nm_status build_spmv_set(const nm_spmv_matrix *mats, int P, int64_t K, in
         if (!aligned(m.masks, 4) || !aligned(m.values, 16) || !aligned(m.y, 2))
             return fail(NM_ERR_ALIGN, "%s: matrix %d misaligned (masks 4, values 16, y 2 bytes)", who, i);
         set.row0[i] = (int)total;
-        set.masks[i] = m.masks;
+        set.meta[i] = m.masks;
         set.values[i] = m.values;
         set.y[i] = m.y;
         set.ldy[i] = m.ldy;
@@ -259,7 +300,7 @@ nm_status nm_spmv_multi(const nm_spmv_matrix *mats, int P, int64_t K, const nm_b
         if (B < 1 || B > 8) return fail(NM_ERR_SHAPE, "nm_spmv_multi: B=%d out of range [1, 8]", B);
         if (ldx < K) return fail(NM_ERR_SHAPE, "nm_spmv_multi: ldx < K");
         if (ldx % 8 || !aligned(x, 16)) return fail(NM_ERR_ALIGN, "nm_spmv_multi: x needs 16-byte alignment, ldx % 8 == 0");
-        return spmv_run(set, K, x, ldx, B, workspace, workspace_bytes, hip_stream, "nm_spmv_multi");
+        return spmv_run(set, NM_META_BITMASK, K, x, ldx, B, workspace, workspace_bytes, hip_stream, "nm_spmv_multi");
     } catch (...) {
         return fail(NM_ERR_HIP, "nm_spmv_multi: internal error");
     }

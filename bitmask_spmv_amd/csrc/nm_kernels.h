@@ -24,7 +24,7 @@ struct MvPlan {
     int slice = 0;          // units per slice
     int grid_x = 1;
     int threads = 512;      // workgroup size
-    int unroll = 2;         // wave iterations whose loads are issued together
+    int unroll = 1;         // dense kernel: 8-column chunks per lane and batch (1, 2 or 4)
     size_t lds_bytes = 0;   // dynamic LDS per workgroup
     size_t ws_bytes = 0;    // workspace bytes (0 when splits == 1)
 };
@@ -33,10 +33,16 @@ struct MvPlan {
 // row r belongs to matrix p when row0[p] <= r < row0[p + 1]; x is staged once.
 constexpr int kMaxMats = 8;
 
+// Metadata formats of the sparse kernel (values of nm_meta_format): per 32-column word,
+// a 32-bit mask, 16 uint8 offsets within the word, or 16 int32 column indices.
+constexpr int kMetaBitmask = 0;
+constexpr int kMetaU8 = 1;
+constexpr int kMetaI32 = 2;
+
 struct SpmvSet {
     int P = 0;
     int row0[kMaxMats + 1] = {};
-    const uint32_t *masks[kMaxMats] = {};
+    const void *meta[kMaxMats] = {};  // metadata in the launch's format
     const uint16_t *values[kMaxMats] = {};
     uint16_t *y[kMaxMats] = {};
     int64_t ldy[kMaxMats] = {};
@@ -60,9 +66,10 @@ hipError_t launch_prune_pack(const uint16_t *W, int64_t ldw, int64_t R, int64_t 
                              uint32_t *masks, uint16_t *values, hipStream_t st);
 hipError_t launch_unpack(const uint32_t *masks, const uint16_t *values, int64_t R, int64_t K, uint16_t *W,
                          int64_t ldw, hipStream_t st);
+hipError_t launch_meta_from_mask(const uint32_t *masks, int64_t R, int64_t K, int fmt, void *meta, hipStream_t st);
 // R of the plan = total rows of the set (set.row0[set.P]).
-hipError_t launch_spmv(const MvPlan &p, const SpmvSet &set, int64_t K, const uint16_t *x, int64_t ldx, int B,
-                       float *ws, hipStream_t st);
+hipError_t launch_spmv(const MvPlan &p, const SpmvSet &set, int fmt, int64_t K, const uint16_t *x, int64_t ldx,
+                       int B, float *ws, hipStream_t st);
 hipError_t launch_dense(const MvPlan &p, const DenseSet &set, int64_t K, const uint16_t *x, int64_t ldx, int B,
                         float *ws, hipStream_t st);
 

@@ -6,9 +6,11 @@
 //       |W_ij| * sqrt(sum_t X_jt^2), top N of every M columns, 32 columns per mask word.
 //   "SparseDecoding: Decoding-Aware Pruning ..." (ai.info summary), Methodology Step 2:
 //       one bit per column, 32 bits per word, values in increasing column order.
-//   "SparseDecoding:解码感知的准确高效大模型剪枝框架" (paper.rainbus.top), 前置知识 N:M.
+//   "SparseDecoding:解码感知的准确高效大模型剪枝框架" (paper.rainbus.top), 前置知识 N:M;
+//       核心方法 (核心创新二): the index formats that the bitmask replaces -- a uint8
+//       offset or an int32 column index per kept weight.
 //
-// All three kernels are offline (run once per weight matrix); they are written for
+// All four kernels are offline (run once per weight matrix); they are written for
 // bit-exact agreement with a scalar definition rather than for peak bandwidth, but
 // still read and write HBM with 16-byte accesses where the layout allows.
 #include "nm_device.h"
@@ -134,6 +136,37 @@ __global__ __launch_bounds__(kPackThreads) void unpack_kernel(const uint32_t *__
     for (int q = 0; q < 4; ++q) dst[q] = mine[q];
 }
 
+// ---------------------------------------------------------------- index metadata
+// One thread per (row, word): the word's 16 set bits, lowest first, become 16 uint8
+// offsets within the word (one 16-byte store) or 16 int32 column indices within the row
+// (four 16-byte stores).
+template <int FMT>
+__global__ __launch_bounds__(kPackThreads) void meta_from_mask_kernel(const uint32_t *__restrict__ masks, int64_t R,
+                                                                      int64_t KW, uint32_t *__restrict__ meta) {
+    const int64_t gid = (int64_t)blockIdx.x * kPackThreads + threadIdx.x;
+    if (gid >= R * KW) return;
+    const int64_t w = gid % KW;
+    uint32_t mm = masks[gid];
+    uint32_t c[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+        c[t] = (uint32_t)__builtin_ctz(mm) & 31u;  // a corrupt mask (< 16 bits) yields 31s
+        mm &= mm - 1;
+    }
+    if constexpr (FMT == kMetaU8) {
+        uint32_t o[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) o[q] = c[4 * q] | (c[4 * q + 1] << 8) | (c[4 * q + 2] << 16) | (c[4 * q + 3] << 24);
+        reinterpret_cast<uint4 *>(meta)[gid] = make_uint4(o[0], o[1], o[2], o[3]);
+    } else {
+        const uint32_t base = (uint32_t)(32 * w);
+        uint4 *dst = reinterpret_cast<uint4 *>(meta) + gid * 4;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            dst[q] = make_uint4(base + c[4 * q], base + c[4 * q + 1], base + c[4 * q + 2], base + c[4 * q + 3]);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_col_norm(const uint16_t *X, int64_t T, int64_t K, int64_t ldx, float *n, hipStream_t st) {
@@ -176,6 +209,20 @@ hipError_t launch_unpack(const uint32_t *masks, const uint16_t *values, int64_t 
     const int64_t KW = K / 32;
     const unsigned blocks = (unsigned)((R * KW + kPackThreads - 1) / kPackThreads);
     hipLaunchKernelGGL(unpack_kernel, dim3(blocks), dim3(kPackThreads), 0, st, masks, values, R, KW, W, ldw);
+    return hipGetLastError();
+}
+
+hipError_t launch_meta_from_mask(const uint32_t *masks, int64_t R, int64_t K, int fmt, void *meta, hipStream_t st) {
+    const int64_t KW = K / 32;
+    const unsigned blocks = (unsigned)((R * KW + kPackThreads - 1) / kPackThreads);
+    if (fmt == kMetaU8)
+        hipLaunchKernelGGL(meta_from_mask_kernel<kMetaU8>, dim3(blocks), dim3(kPackThreads), 0, st, masks, R, KW,
+                           (uint32_t *)meta);
+    else if (fmt == kMetaI32)
+        hipLaunchKernelGGL(meta_from_mask_kernel<kMetaI32>, dim3(blocks), dim3(kPackThreads), 0, st, masks, R, KW,
+                           (uint32_t *)meta);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

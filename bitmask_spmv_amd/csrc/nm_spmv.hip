@@ -1,4 +1,4 @@
-// nm_spmv.hip -- batch-one / small-batch N:M bitmask SpMV on gfx950.
+// nm_spmv.hip -- batch-one / small-batch N:M sparse matrix-vector product on gfx950.
 //
 // What it computes (pages cited by title and section):
 //   "SparseDecoding: Decoding-Aware Pruning ..." (ai.info summary), Methodology Steps 2-3:
@@ -8,7 +8,10 @@
 //     word is a fixed 16-step loop of "lowest set bit -> column, clear it".
 //   "SparseDecoding:解码感知的准确高效大模型剪枝框架" (paper.rainbus.top), 方法步骤详情
 //     第四步: the input vector is the reused operand and weights/masks are streamed;
-//     rows may be split with a reduction of the pieces.
+//     rows may be split with a reduction of the pieces.  核心方法 (核心创新二): the
+//     bitmask costs 2 bits per kept weight against 8 for a uint8 offset and 32 for an
+//     int32 column index; both index formats run on the same kernel skeleton (the
+//     metadata format is a template parameter) so the trade-off can be measured.
 //
 // gfx950 design (what differs from the pages' A100/Triton kernel):
 //   * x lives in LDS for the whole workgroup: each 32-column block of x occupies 17
@@ -23,7 +26,7 @@
 //     Slices of a row (when splits > 1) go to fp32 workspace and are added in slice
 //     order by a second kernel (deterministic, no atomics).
 //   * one kernel serves every 50% pattern (2:4 ... 16:32): the M of the pattern never
-//     enters the traversal.
+//     enters the traversal.  Several matrices that share x run in one launch (SpmvSet).
 #include <atomic>
 
 #include "nm_device.h"
@@ -58,13 +61,17 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
 }
 
-// One wave-iteration batch: U consecutive 64-word strips of one row slice, per lane one
-// mask word and its 16 packed values (two 16-byte loads).
-template <int U>
+// Metadata bytes per 32-column word (16 kept weights) of each format.
+constexpr int meta_bytes(int fmt) { return fmt == kMetaBitmask ? 4 : (fmt == kMetaU8 ? 16 : 64); }
+
+// One wave-iteration batch: a 64-word strip of one row slice.  Per lane: the 16 packed
+// values of its word (two 16-byte chunks, before the pair swap) and the word's
+// metadata -- the mask word, 16 uint8 offsets, or 16 int32 column indices.
+template <int FMT>
 struct Batch {
-    uint32_t m[U];
-    u32x4 va[U], vb[U];
-    int lw[U];
+    u32x4 va, vb;
+    u32x4 meta[FMT == kMetaI32 ? 4 : 1];
+    int lw;  // word index within the slice (>= the slice length marks a padding lane)
 };
 
 // Loads one batch through raw buffer descriptors covering the row slice's `words`
@@ -76,21 +83,24 @@ struct Batch {
 // KiB), which halves the cache lines each load instruction touches compared with one
 // lane reading a whole 32-byte word.  A quad-permute then swaps halves between lane
 // pairs so that lane 2i ends up with word i and lane 2i+1 with word 32+i; each lane
-// also loads its own word's mask.
-template <int U>
-__device__ __forceinline__ void load_batch(Batch<U> &bt, const uint32_t *mrow, const u32x4 *vrow, int words,
+// loads its own word's metadata.
+template <int FMT>
+__device__ __forceinline__ void load_batch(Batch<FMT> &bt, const uint8_t *mrow, const u32x4 *vrow, int words,
                                            int base, int lane) {
-    const __amdgpu_buffer_rsrc_t rm = make_rsrc(mrow, (int64_t)words * 4);
+    const __amdgpu_buffer_rsrc_t rm = make_rsrc(mrow, (int64_t)words * meta_bytes(FMT));
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vrow, (int64_t)words * 32);
-    const int my_word = (lane & 1) ? 32 + (lane >> 1) : (lane >> 1);
+    const int w = base + ((lane & 1) ? 32 + (lane >> 1) : (lane >> 1));
+    if constexpr (FMT == kMetaBitmask) {
+        bt.meta[0].x = __builtin_amdgcn_raw_buffer_load_b32(rm, w * 4, 0, kLoadNT);
+    } else if constexpr (FMT == kMetaU8) {
+        bt.meta[0] = __builtin_amdgcn_raw_buffer_load_b128(rm, w * 16, 0, kLoadNT);
+    } else {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int s0 = base + u * kWave;  // first word of the strip
-        bt.m[u] = __builtin_amdgcn_raw_buffer_load_b32(rm, (s0 + my_word) * 4, 0, kLoadNT);
-        bt.va[u] = __builtin_amdgcn_raw_buffer_load_b128(rv, s0 * 32 + lane * 16, 0, kLoadNT);
-        bt.vb[u] = __builtin_amdgcn_raw_buffer_load_b128(rv, s0 * 32 + 1024 + lane * 16, 0, kLoadNT);
-        bt.lw[u] = s0 + my_word;
+        for (int q = 0; q < 4; ++q) bt.meta[q] = __builtin_amdgcn_raw_buffer_load_b128(rm, w * 64 + 16 * q, 0, kLoadNT);
     }
+    bt.va = __builtin_amdgcn_raw_buffer_load_b128(rv, base * 32 + lane * 16, 0, kLoadNT);
+    bt.vb = __builtin_amdgcn_raw_buffer_load_b128(rv, base * 32 + 1024 + lane * 16, 0, kLoadNT);
+    bt.lw = w;
 }
 
 // Swap one dword with the neighbouring lane of the pair (lane ^ 1).
@@ -116,53 +126,65 @@ __device__ __forceinline__ void gather_col(const uint32_t *blk, int c, uint32_t 
     }
 }
 
-// The fixed 16-step walk of each mask word: lowest set bit -> column, clear it.  Steps
-// are taken in pairs so that the two gathered inputs meet the packed value pair in one
-// v_dot2_f32_bf16 (per token).
-template <int B, int U>
-__device__ __forceinline__ void walk_batch(const Batch<U> &bt, const uint32_t *xs, int nws, float (&acc)[B]) {
+// Column (0..31 within the word) of the t-th kept weight of a word.  Bitmask: the fixed
+// 16-step walk -- lowest set bit gives the column, then that bit is cleared.  uint8
+// offset: byte t.  int32 index: at 50% N:M an index of word w always lies in
+// [32w, 32w + 32), so its low five bits are the column within the word.  The index
+// formats are masked to five bits so that no metadata value can address outside the
+// word's block of x.
+template <int FMT>
+__device__ __forceinline__ int column_of(const Batch<FMT> &bt, uint32_t &mm, int t) {
+    if constexpr (FMT == kMetaBitmask) {
+        const int c = __builtin_ctz(mm);
+        mm &= mm - 1;
+        return c;
+    } else if constexpr (FMT == kMetaU8) {
+        return (int)((bt.meta[0][t >> 2] >> (8 * (t & 3))) & 31u);
+    } else {
+        return (int)(bt.meta[t >> 2][t & 3] & 31u);
+    }
+}
+
+// Walk of one word: 8 pairs of kept weights; the two gathered inputs of a pair meet the
+// packed value pair in one v_dot2_f32_bf16 (per token).
+template <int FMT, int B>
+__device__ __forceinline__ void walk_batch(const Batch<FMT> &bt, const uint32_t *xs, int nws, float (&acc)[B]) {
     constexpr int S = XLayout<B>::S;
     constexpr int kBlk = XLayout<B>::kBlk;
+    // A padding lane (past the slice) holds zero values: it walks 16 fixed columns of
+    // block 0 (index formats: zero metadata, column 0) so every LDS address stays inside
+    // the staged x.
+    const bool ok = bt.lw < nws;
+    const int lw = ok ? bt.lw : 0;
+    // Reassemble this lane's 16 values (see load_batch): even lanes keep their first
+    // chunk and receive the partner's first chunk; odd lanes receive the partner's
+    // second chunk and keep their own second chunk.
+    const bool odd = threadIdx.x & 1;
+    const uint32_t s_x = odd ? bt.va.x : bt.vb.x, s_y = odd ? bt.va.y : bt.vb.y;
+    const uint32_t s_z = odd ? bt.va.z : bt.vb.z, s_w = odd ? bt.va.w : bt.vb.w;
+    const uint32_t r_x = pair_swap(s_x), r_y = pair_swap(s_y), r_z = pair_swap(s_z), r_w = pair_swap(s_w);
+    const uint32_t v[8] = {odd ? r_x : bt.va.x, odd ? r_y : bt.va.y, odd ? r_z : bt.va.z, odd ? r_w : bt.va.w,
+                           odd ? bt.vb.x : r_x, odd ? bt.vb.y : r_y, odd ? bt.vb.z : r_z, odd ? bt.vb.w : r_w};
+    const uint32_t *blk = xs + lw * kBlk;  // this word's 32 columns
+    uint32_t mm = ok ? bt.meta[0].x : 0xFFFFu;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        // A padding lane (past the slice) holds zero values: walk 16 fixed columns of
-        // block 0 so every LDS address stays inside the staged x.
-        const bool ok = bt.lw[u] < nws;
-        const int lw = ok ? bt.lw[u] : 0;
-        // Reassemble this lane's 16 values (see load_batch): even lanes keep their first
-        // chunk and receive the partner's first chunk; odd lanes receive the partner's
-        // second chunk and keep their own second chunk.
-        const bool odd = threadIdx.x & 1;
-        const uint32_t s_x = odd ? bt.va[u].x : bt.vb[u].x, s_y = odd ? bt.va[u].y : bt.vb[u].y;
-        const uint32_t s_z = odd ? bt.va[u].z : bt.vb[u].z, s_w = odd ? bt.va[u].w : bt.vb[u].w;
-        const uint32_t r_x = pair_swap(s_x), r_y = pair_swap(s_y), r_z = pair_swap(s_z), r_w = pair_swap(s_w);
-        const uint32_t v[8] = {odd ? r_x : bt.va[u].x, odd ? r_y : bt.va[u].y,
-                               odd ? r_z : bt.va[u].z, odd ? r_w : bt.va[u].w,
-                               odd ? bt.vb[u].x : r_x, odd ? bt.vb[u].y : r_y,
-                               odd ? bt.vb[u].z : r_z, odd ? bt.vb[u].w : r_w};
-        const uint32_t *blk = xs + lw * kBlk;  // this word's 32 columns
-        uint32_t mm = ok ? bt.m[u] : 0xFFFFu;
+    for (int k = 0; k < 8; ++k) {
+        const int c0 = column_of<FMT>(bt, mm, 2 * k);
+        const int c1 = column_of<FMT>(bt, mm, 2 * k + 1);
+        if constexpr (S == 1) {
+            const uint16_t *xw = reinterpret_cast<const uint16_t *>(blk);
+            const uint32_t pr = (uint32_t)xw[c0] | ((uint32_t)xw[c1] << 16);
+            acc[0] = dot2_bf16(v[k], pr, acc[0]);
+        } else {
+            uint32_t d0[S / 2], d1[S / 2];
+            gather_col<S>(blk, c0, d0);
+            gather_col<S>(blk, c1, d1);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int c0 = __builtin_ctz(mm);
-            mm &= mm - 1;
-            const int c1 = __builtin_ctz(mm);
-            mm &= mm - 1;
-            if constexpr (S == 1) {
-                const uint16_t *xw = reinterpret_cast<const uint16_t *>(blk);
-                const uint32_t pr = (uint32_t)xw[c0] | ((uint32_t)xw[c1] << 16);
-                acc[0] = dot2_bf16(v[k], pr, acc[0]);
-            } else {
-                uint32_t d0[S / 2], d1[S / 2];
-                gather_col<S>(blk, c0, d0);
-                gather_col<S>(blk, c1, d1);
-#pragma unroll
-                for (int j = 0; j < S / 2; ++j) {
-                    // (token 2j of column c0, token 2j of column c1), then the same for 2j+1
-                    if (2 * j < B) acc[2 * j] = dot2_bf16(v[k], __builtin_amdgcn_perm(d1[j], d0[j], 0x05040100u), acc[2 * j]);
-                    if (2 * j + 1 < B)
-                        acc[2 * j + 1] = dot2_bf16(v[k], __builtin_amdgcn_perm(d1[j], d0[j], 0x07060302u), acc[2 * j + 1]);
-                }
+            for (int j = 0; j < S / 2; ++j) {
+                // (token 2j of column c0, token 2j of column c1), then the same for 2j+1
+                if (2 * j < B) acc[2 * j] = dot2_bf16(v[k], __builtin_amdgcn_perm(d1[j], d0[j], 0x05040100u), acc[2 * j]);
+                if (2 * j + 1 < B)
+                    acc[2 * j + 1] = dot2_bf16(v[k], __builtin_amdgcn_perm(d1[j], d0[j], 0x07060302u), acc[2 * j + 1]);
             }
         }
     }
@@ -196,16 +218,16 @@ __device__ __forceinline__ void finish_row(float (&acc)[B], const SpmvSet &set, 
 }
 
 // Batch loads of global row r, word offset `base` within the slice.
-template <int U>
-__device__ __forceinline__ void load_row_batch(Batch<U> &bt, const SpmvSet &set, int r, int KW, int w0, int words,
+template <int FMT>
+__device__ __forceinline__ void load_row_batch(Batch<FMT> &bt, const SpmvSet &set, int r, int KW, int w0, int words,
                                                int base, int lane) {
     const int p = owner(set, r);
-    const int64_t off = (int64_t)(r - set.row0[p]) * KW + w0;
-    load_batch<U>(bt, set.masks[p] + off, reinterpret_cast<const u32x4 *>(set.values[p]) + off * 2, words, base,
-                  lane);
+    const int64_t off = (int64_t)(r - set.row0[p]) * KW + w0;  // in words
+    load_batch<FMT>(bt, reinterpret_cast<const uint8_t *>(set.meta[p]) + off * meta_bytes(FMT),
+                    reinterpret_cast<const u32x4 *>(set.values[p]) + off * 2, words, base, lane);
 }
 
-template <int B, int U, int NT>
+template <int FMT, int B, int NT>
 __global__ __launch_bounds__(NT) void spmv_kernel(const SpmvSet set, int KW, const uint16_t *__restrict__ x,
                                                   int64_t ldx, float *__restrict__ partial, int slice) {
     const int R = set.row0[set.P];
@@ -219,18 +241,18 @@ __global__ __launch_bounds__(NT) void spmv_kernel(const SpmvSet set, int KW, con
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     constexpr int kWaves = NT / kWave;
 
-    // This wave's rows: first_row, first_row + row_step, ...; each row slice is cut
-    // into nb batches, walked as one flat sequence so the next batch's loads are in
+    // This wave's rows: first_row, first_row + row_step, ...; each row slice is cut into
+    // nb strips of 64 words, walked as one flat sequence so the next strip's loads are in
     // flight while the current one is computed, across row boundaries too.
     const int first_row = blockIdx.x * kWaves + wave;
     const int row_step = gridDim.x * kWaves;
-    const int nb = (nws + kWave * U - 1) / (kWave * U);
+    const int nb = (nws + kWave - 1) / kWave;
     const int my_rows = first_row < R ? (R - 1 - first_row) / row_step + 1 : 0;
     const int total = my_rows * nb;
 
     // Two batch buffers used in turn (no register copies, so the wait for one batch
     // never covers the loads of the other).
-    Batch<U> bufA, bufB;
+    Batch<FMT> bufA, bufB;
     int rowA = first_row, biA = 0, rowB = first_row, biB = 0;
     // Stage this slice of x into LDS.  The first round of x loads is issued before batch
     // A's weight loads, so waiting for x (an L2 hit after the first workgroup of an XCD)
@@ -246,8 +268,7 @@ __global__ __launch_bounds__(NT) void spmv_kernel(const SpmvSet set, int KW, con
                 const int i = i0 + j * NT + (int)threadIdx.x;
                 if (i < chunks) r[j] = reinterpret_cast<const u32x4 *>(x + (int64_t)w0 * 32)[i];
             }
-            if (i0 == 0)
-                load_row_batch<U>(bufA, set, min(rowA, R - 1), KW, w0, total > 0 ? nws : 0, 0, lane);
+            if (i0 == 0) load_row_batch<FMT>(bufA, set, min(rowA, R - 1), KW, w0, total > 0 ? nws : 0, 0, lane);
 #pragma unroll
             for (int j = 0; j < kStage; ++j) {
                 const int i = i0 + j * NT + (int)threadIdx.x;
@@ -276,7 +297,7 @@ __global__ __launch_bounds__(NT) void spmv_kernel(const SpmvSet set, int KW, con
                 for (int b = 0; b < S; ++b) r[j][b] = (b < B && i < pairs) ? x32[(int64_t)b * (ldx / 2) + i] : 0u;
             }
             if (i0 == 0)
-                load_row_batch<U>(bufA, set, min(rowA, R - 1), KW, w0, total > 0 ? nws : 0, 0, lane);
+                load_row_batch<FMT>(bufA, set, min(rowA, R - 1), KW, w0, total > 0 ? nws : 0, 0, lane);
 #pragma unroll
             for (int j = 0; j < kStage; ++j) {
                 const int i = i0 + j * NT + (int)threadIdx.x;
@@ -314,8 +335,8 @@ __global__ __launch_bounds__(NT) void spmv_kernel(const SpmvSet set, int KW, con
             biB = 0;
             rowB += row_step;
         }
-        load_row_batch<U>(bufB, set, min(rowB, R - 1), KW, w0, t + 1 < total ? nws : 0, biB * kWave * U, lane);
-        walk_batch<B, U>(bufA, xs, nws, acc);
+        load_row_batch<FMT>(bufB, set, min(rowB, R - 1), KW, w0, t + 1 < total ? nws : 0, biB * kWave, lane);
+        walk_batch<FMT, B>(bufA, xs, nws, acc);
         if (biA == nb - 1) finish_row<B>(acc, set, rowA, s, R, lane, partial);
         if (t + 1 >= total) break;
         // A <- batch t+2, walk B (batch t+1)
@@ -325,8 +346,8 @@ __global__ __launch_bounds__(NT) void spmv_kernel(const SpmvSet set, int KW, con
             biA = 0;
             rowA += row_step;
         }
-        load_row_batch<U>(bufA, set, min(rowA, R - 1), KW, w0, t + 2 < total ? nws : 0, biA * kWave * U, lane);
-        walk_batch<B, U>(bufB, xs, nws, acc);
+        load_row_batch<FMT>(bufA, set, min(rowA, R - 1), KW, w0, t + 2 < total ? nws : 0, biA * kWave, lane);
+        walk_batch<FMT, B>(bufB, xs, nws, acc);
         if (biB == nb - 1) finish_row<B>(acc, set, rowB, s, R, lane, partial);
     }
 }
@@ -350,7 +371,7 @@ __global__ __launch_bounds__(256) void split_finish_kernel(const float *__restri
 }
 
 // Raise the dynamic-LDS limit of one kernel instance once per device.
-template <int B, int U, int NT>
+template <int FMT, int B, int NT>
 hipError_t allow_lds(size_t bytes) {
     static std::atomic<uint64_t> done{0};
     if (bytes <= 64 * 1024) return hipSuccess;
@@ -359,18 +380,18 @@ hipError_t allow_lds(size_t bytes) {
     if (e != hipSuccess) return e;
     const uint64_t bit = 1ull << (dev & 63);
     if (done.load(std::memory_order_acquire) & bit) return hipSuccess;
-    e = hipFuncSetAttribute((const void *)spmv_kernel<B, U, NT>, hipFuncAttributeMaxDynamicSharedMemorySize,
+    e = hipFuncSetAttribute((const void *)spmv_kernel<FMT, B, NT>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)kLdsCap);
     if (e == hipSuccess) done.fetch_or(bit, std::memory_order_acq_rel);
     return e;
 }
 
-template <int B, int U, int NT>
-hipError_t launch_bu(const MvPlan &p, const SpmvSet &set, int64_t K, const uint16_t *x, int64_t ldx, float *ws,
-                     hipStream_t st) {
-    hipError_t e = allow_lds<B, U, NT>(p.lds_bytes);
+template <int FMT, int B, int NT>
+hipError_t launch_fbn(const MvPlan &p, const SpmvSet &set, int64_t K, const uint16_t *x, int64_t ldx, float *ws,
+                      hipStream_t st) {
+    hipError_t e = allow_lds<FMT, B, NT>(p.lds_bytes);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((spmv_kernel<B, U, NT>), dim3(p.grid_x, p.splits), dim3(NT), p.lds_bytes, st, set,
+    hipLaunchKernelGGL((spmv_kernel<FMT, B, NT>), dim3(p.grid_x, p.splits), dim3(NT), p.lds_bytes, st, set,
                        (int)(K / 32), x, ldx, ws, p.slice);
     e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;
@@ -380,15 +401,27 @@ hipError_t launch_bu(const MvPlan &p, const SpmvSet &set, int64_t K, const uint1
     return hipGetLastError();
 }
 
-template <int B>
-hipError_t launch_b(const MvPlan &p, const SpmvSet &set, int64_t K, const uint16_t *x, int64_t ldx, float *ws,
+template <int FMT, int B>
+hipError_t launch_fb(const MvPlan &p, const SpmvSet &set, int64_t K, const uint16_t *x, int64_t ldx, float *ws,
+                     hipStream_t st) {
+    if (p.threads == 256) return launch_fbn<FMT, B, 256>(p, set, K, x, ldx, ws, st);
+    return launch_fbn<FMT, B, 512>(p, set, K, x, ldx, ws, st);
+}
+
+template <int FMT>
+hipError_t launch_f(const MvPlan &p, const SpmvSet &set, int64_t K, const uint16_t *x, int64_t ldx, int B, float *ws,
                     hipStream_t st) {
-    if (p.threads == 256) {
-        if (p.unroll >= 2) return launch_bu<B, 2, 256>(p, set, K, x, ldx, ws, st);
-        return launch_bu<B, 1, 256>(p, set, K, x, ldx, ws, st);
+    switch (B) {
+    case 1: return launch_fb<FMT, 1>(p, set, K, x, ldx, ws, st);
+    case 2: return launch_fb<FMT, 2>(p, set, K, x, ldx, ws, st);
+    case 3: return launch_fb<FMT, 3>(p, set, K, x, ldx, ws, st);
+    case 4: return launch_fb<FMT, 4>(p, set, K, x, ldx, ws, st);
+    case 5: return launch_fb<FMT, 5>(p, set, K, x, ldx, ws, st);
+    case 6: return launch_fb<FMT, 6>(p, set, K, x, ldx, ws, st);
+    case 7: return launch_fb<FMT, 7>(p, set, K, x, ldx, ws, st);
+    case 8: return launch_fb<FMT, 8>(p, set, K, x, ldx, ws, st);
+    default: return hipErrorInvalidValue;
     }
-    if (p.unroll >= 2) return launch_bu<B, 2, 512>(p, set, K, x, ldx, ws, st);
-    return launch_bu<B, 1, 512>(p, set, K, x, ldx, ws, st);
 }
 
 }  // namespace
@@ -405,11 +438,10 @@ MvPlan plan_spmv(int64_t R, int64_t K, int B, const DeviceInfo &dev) {
     int64_t max_slice = (int64_t)cap / bytes_per_word;
     if (max_slice >= kWave) max_slice -= max_slice % kWave;
     if (max_slice < 1) max_slice = 1;
-    // Enough (row, slice) tasks to give every resident wave work, but no slice shorter
-    // than one wave iteration.
-    // Split rows across workgroups only when the matrix has too few rows to give
-    // every CU a couple of waves: the split costs a second launch, which outweighs
-    // the extra parallelism on anything but very short, wide matrices.
+    // Split rows across workgroups only when LDS cannot hold a row's x, or when the
+    // matrix has too few rows to give every CU a couple of waves: the split costs a
+    // second launch, which outweighs the extra parallelism on anything but very short,
+    // wide matrices.  No slice is shorter than one 64-word strip.
     const int64_t cu = dev.num_cu > 0 ? dev.num_cu : 256;
     const int64_t want_rows = cu * 2;
     int64_t splits = (KW + max_slice - 1) / max_slice;
@@ -441,17 +473,12 @@ MvPlan plan_spmv(int64_t R, int64_t K, int B, const DeviceInfo &dev) {
     return p;
 }
 
-hipError_t launch_spmv(const MvPlan &p, const SpmvSet &set, int64_t K, const uint16_t *x, int64_t ldx, int B,
+hipError_t launch_spmv(const MvPlan &p, const SpmvSet &set, int fmt, int64_t K, const uint16_t *x, int64_t ldx, int B,
                        float *ws, hipStream_t st) {
-    switch (B) {
-    case 1: return launch_b<1>(p, set, K, x, ldx, ws, st);
-    case 2: return launch_b<2>(p, set, K, x, ldx, ws, st);
-    case 3: return launch_b<3>(p, set, K, x, ldx, ws, st);
-    case 4: return launch_b<4>(p, set, K, x, ldx, ws, st);
-    case 5: return launch_b<5>(p, set, K, x, ldx, ws, st);
-    case 6: return launch_b<6>(p, set, K, x, ldx, ws, st);
-    case 7: return launch_b<7>(p, set, K, x, ldx, ws, st);
-    case 8: return launch_b<8>(p, set, K, x, ldx, ws, st);
+    switch (fmt) {
+    case kMetaBitmask: return launch_f<kMetaBitmask>(p, set, K, x, ldx, B, ws, st);
+    case kMetaU8: return launch_f<kMetaU8>(p, set, K, x, ldx, B, ws, st);
+    case kMetaI32: return launch_f<kMetaI32>(p, set, K, x, ldx, B, ws, st);
     default: return hipErrorInvalidValue;
     }
 }

@@ -28,7 +28,8 @@
  *  - Sizes (R, K, T) are limited to 2^30.
  *  - Alignment: the base pointers of W, values, x and col_norm (pack input) must be
  *    16-byte aligned and ldw, ldx must be multiples of 8 elements, else NM_ERR_ALIGN.
- *    masks and workspace must be 4-byte aligned, y 2-byte aligned (ldy is free).
+ *    masks and workspace must be 4-byte aligned, y 2-byte aligned (ldy is free);
+ *    index metadata (nm_spmv_meta) 16-byte aligned.
  *  - Entry points are thread-safe and reentrant.  nm_last_error() returns a
  *    thread-local description of the last failure on the calling thread.
  *  - No C++ exception crosses this boundary.
@@ -165,6 +166,50 @@ typedef struct {
 size_t dense_gemv_multi_workspace_bytes(const dense_matrix *mats, int P, int64_t K, int B);
 nm_status dense_gemv_multi(const dense_matrix *mats, int P, int64_t K, const nm_bf16 *x, int64_t ldx, int B,
                            void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/*
+ * Index-metadata formats [SD-en, Main Findings (metadata reduction); SD-cn, 核心方法
+ * (核心创新二)]: the pages price the bitmask (2 bits per kept weight at 50%) against a
+ * uint8 offset (8 bits) and an int32 column index (32 bits, the nmSPARSE format) per
+ * kept weight.  The library builds both index formats from a bitmask and runs the same
+ * product on them so the metadata cost can be measured on one kernel design.
+ *
+ *   NM_META_BITMASK    uint32 [R][K/32]: the canonical masks (as nm_spmv).
+ *   NM_META_U8_OFFSET  uint8  [R][K/2]:  for kept weight t of word w (the t-th set bit,
+ *                      lowest first), its column minus 32w, i.e. 0..31; 16 bytes per
+ *                      word, in the order of values.
+ *   NM_META_I32_INDEX  int32  [R][K/2]:  the same weight's column index within the row,
+ *                      32w + offset; 16 per word, in the order of values.
+ */
+typedef enum {
+    NM_META_BITMASK = 0,
+    NM_META_U8_OFFSET = 1,
+    NM_META_I32_INDEX = 2
+} nm_meta_format;
+
+/*
+ * nm_meta_from_mask -- converts canonical masks into NM_META_U8_OFFSET or
+ * NM_META_I32_INDEX metadata (format NM_META_BITMASK is rejected with NM_ERR_PATTERN:
+ * there is nothing to convert).  meta: device buffer of R*K/2 bytes (uint8) or 2*R*K
+ * bytes (int32), 16-byte aligned.  Requires R >= 1, K >= 32, K % 32 == 0 and 16 set
+ * bits per mask word.
+ */
+nm_status nm_meta_from_mask(const uint32_t *masks, int64_t R, int64_t K, int format, void *meta,
+                            void *hip_stream);
+
+/*
+ * nm_spmv_meta -- nm_spmv with the metadata in any nm_meta_format: the same product
+ * y[b][i] = sum_j Wsparse[i][j] * x[b][j] with the t-th kept weight of word w at the
+ * column the metadata gives.  Same arithmetic, pairing order, rounding, workspace
+ * (nm_spmv_workspace_bytes) and requirements as nm_spmv; meta must be 4-byte
+ * (bitmask) or 16-byte (index formats) aligned.  At 50% N:M every weight of word w lies
+ * in columns [32w, 32w+32); the kernel reads the low five bits of each offset/index
+ * (an entry that breaks this rule reads a wrong column of the same word, never memory
+ * outside x).  Unknown formats fail with NM_ERR_PATTERN.
+ */
+nm_status nm_spmv_meta(const void *meta, int format, const nm_bf16 *values, int64_t R, int64_t K,
+                       const nm_bf16 *x, int64_t ldx, int B, nm_bf16 *y, int64_t ldy, void *workspace,
+                       size_t workspace_bytes, void *hip_stream);
 
 /*
  * nm_unpack -- inverse of the packing: W_out[i][j] = kept value of column j, or +0.0

@@ -18,6 +18,12 @@ list and the passages each follows:
 * ``unpack``     -- inverse of the packing: dense pruned matrix, zeros elsewhere
 * ``spmv``       -- fp64 matvec of the unpacked pruned matrix (+ sum of |products|)
 * ``dense``      -- fp64 matvec of the dense matrix (+ sum of |products|)
+* ``meta_from_mask`` / ``spmv_index`` -- the index formats the bitmask is priced
+                    against (uint8 offset within the 32-column word, int32 column index
+                    within the row, one per kept weight in value order) and the fp64
+                    matvec defined directly over them
+                    ("SparseDecoding: Decoding-Aware Pruning ...", Main Findings;
+                    "SparseDecoding:解码感知的准确高效大模型剪枝框架", 核心方法 核心创新二)
 
 Pins (tests that tie the oracle to something other than itself) live in
 ``tests/test_oracle_pins.py``; every function above has at least one.
@@ -41,7 +47,7 @@ class OracleError(RuntimeError):
     pass
 
 
-_ERRS = {1: "bad argument", 2: "non-finite input", 3: "mask word without exactly 16 set bits",
+_ERRS = {1: "bad argument", 2: "non-finite input", 3: "mask word without exactly 16 set bits (or malformed index metadata)",
          4: "out of memory"}
 
 
@@ -69,7 +75,10 @@ def _load():
     lib.nmo_unpack.argtypes = [p, p, i64, i64, p]
     lib.nmo_spmv.argtypes = [p, p, i64, i64, p, i64, ctypes.c_int, p, p, ctypes.c_int]
     lib.nmo_dense.argtypes = [p, i64, i64, i64, p, i64, ctypes.c_int, p, p, ctypes.c_int]
-    for f in (lib.nmo_col_norm, lib.nmo_prune_pack, lib.nmo_unpack, lib.nmo_spmv, lib.nmo_dense):
+    lib.nmo_meta_from_mask.argtypes = [p, i64, i64, ctypes.c_int, p]
+    lib.nmo_spmv_index.argtypes = [p, ctypes.c_int, p, i64, i64, p, i64, ctypes.c_int, p, p, ctypes.c_int]
+    for f in (lib.nmo_col_norm, lib.nmo_prune_pack, lib.nmo_unpack, lib.nmo_spmv, lib.nmo_dense,
+              lib.nmo_meta_from_mask, lib.nmo_spmv_index):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -156,6 +165,41 @@ def dense(W, x, nthreads: int = 1):
     y = np.empty((B, R), dtype=np.float64)
     a = np.empty((B, R), dtype=np.float64)
     _check(_load().nmo_dense(_ptr(W), K, R, K, _ptr(x), K, B, _ptr(y), _ptr(a), int(nthreads)), "dense")
+    return y, a
+
+
+META_U8, META_I32 = 1, 2
+_META_DT = {META_U8: np.uint8, META_I32: np.int32}
+
+
+def meta_from_mask(masks, K: int, fmt: int) -> np.ndarray:
+    """masks uint32 [R, K/32] -> uint8 [R, K/2] offsets (META_U8) or int32 [R, K/2] indices (META_I32)."""
+    masks = np.ascontiguousarray(masks, dtype=np.uint32)
+    if fmt not in _META_DT:
+        raise OracleError("meta_from_mask: bad argument")
+    R = masks.shape[0]
+    out = np.empty((R, K // 2), dtype=_META_DT[fmt])
+    _check(_load().nmo_meta_from_mask(_ptr(masks), R, K, int(fmt), _ptr(out)), "meta_from_mask")
+    return out
+
+
+def spmv_index(meta, fmt: int, values, x, K: int, nthreads: int = 1):
+    """-> (y fp64 [B, R], absum fp64 [B, R]) with the kept weights placed by index metadata."""
+    if fmt not in _META_DT:
+        raise OracleError("spmv_index: bad argument")
+    meta = np.ascontiguousarray(meta, dtype=_META_DT[fmt])
+    values = _u16(values)
+    x = _u16(x)
+    if x.ndim == 1:
+        x = x[None, :]
+    R = values.shape[0]
+    B = x.shape[0]
+    if x.shape[1] != K or meta.shape != (R, K // 2) or values.shape != (R, K // 2):
+        raise ValueError("shape mismatch")
+    y = np.empty((B, R), dtype=np.float64)
+    a = np.empty((B, R), dtype=np.float64)
+    _check(_load().nmo_spmv_index(_ptr(meta), int(fmt), _ptr(values), R, K, _ptr(x), K, B, _ptr(y), _ptr(a),
+                                  int(nthreads)), "spmv_index")
     return y, a
 
 

@@ -173,6 +173,66 @@ int nmo_unpack(const uint32_t *masks, const uint16_t *values, int64_t R, int64_t
     return NMO_OK;
 }
 
+/* ------------------------------------------------------------------ index metadata
+ * The formats the bitmask is priced against [SD-en, Main Findings (metadata
+ * reduction); SD-cn, 核心方法 (核心创新二)]: 8 bits (a uint8 offset) or 32 bits (an
+ * int32 column index) per kept weight instead of 2.  The pages do not spell the
+ * layouts out; the readings taken: one entry per kept weight, in the order of the
+ * packed values; the uint8 entry of the t-th kept weight of word w is its column
+ * minus 32w (0..31), the int32 entry is its column within the row.
+ */
+#define NMO_META_U8 1
+#define NMO_META_I32 2
+
+/* Column of kept weight t (0 <= t < K/2) of row i. */
+static int64_t meta_column(const void *meta, int fmt, int64_t i, int64_t t, int64_t K)
+{
+    const int64_t nnz = K / 2;
+    if (fmt == NMO_META_U8) return 32 * (t / 16) + ((const uint8_t *)meta)[i * nnz + t];
+    return ((const int32_t *)meta)[i * nnz + t];
+}
+
+/* Metadata of canonical masks: the set bits of each word, lowest first. */
+int nmo_meta_from_mask(const uint32_t *masks, int64_t R, int64_t K, int fmt, void *meta)
+{
+    if (!masks || !meta || R < 1 || K < 32 || K % 32 != 0) return NMO_EARG;
+    if (fmt != NMO_META_U8 && fmt != NMO_META_I32) return NMO_EARG;
+    for (int64_t i = 0; i < R; ++i) {
+        for (int64_t w = 0; w < K / 32; ++w) {
+            uint32_t m = masks[i * (K / 32) + w];
+            int64_t t = 16 * w;
+            for (int b = 0; b < 32; ++b) {
+                if (!(m & (1u << b))) continue;
+                if (t >= 16 * w + 16) return NMO_EMASK;
+                if (fmt == NMO_META_U8)
+                    ((uint8_t *)meta)[i * (K / 2) + t] = (uint8_t)b;
+                else
+                    ((int32_t *)meta)[i * (K / 2) + t] = (int32_t)(32 * w + b);
+                ++t;
+            }
+            if (t != 16 * w + 16) return NMO_EMASK;
+        }
+    }
+    return NMO_OK;
+}
+
+/* Index metadata is well formed when the columns of each word's 16 kept weights lie in
+ * that word and strictly increase (the values are stored in column order). */
+static int check_meta(const void *meta, int fmt, int64_t R, int64_t K)
+{
+    for (int64_t i = 0; i < R; ++i) {
+        for (int64_t w = 0; w < K / 32; ++w) {
+            int64_t prev = -1;
+            for (int64_t t = 16 * w; t < 16 * w + 16; ++t) {
+                int64_t c = meta_column(meta, fmt, i, t, K);
+                if (c < 32 * w || c >= 32 * w + 32 || c <= prev) return NMO_EMASK;
+                prev = c;
+            }
+        }
+    }
+    return NMO_OK;
+}
+
 /* ------------------------------------------------------------------ matvec references
  * y[b][i] = sum_j Wp[i][j] * x[b][j] with Wp the unpacked pruned matrix (dense
  * reference) or W itself; every product of two bf16 values is exact in fp64 and the
@@ -181,6 +241,8 @@ int nmo_unpack(const uint32_t *masks, const uint16_t *values, int64_t R, int64_t
  * element is still one sequential fp64 sum, so the thread count never changes a bit.
  */
 typedef struct {
+    const void *meta;        /* index metadata (nmo_spmv_index), else NULL */
+    int fmt;                 /* NMO_META_U8 or NMO_META_I32 when meta is set */
     const uint32_t *masks;   /* NULL for the dense reference */
     const uint16_t *values;  /* packed values, or the dense W */
     int64_t ldw;             /* dense only */
@@ -204,6 +266,25 @@ static void *mv_worker(void *arg)
         }
     }
     jb->rc = NMO_OK;
+    if (jb->meta) {
+        /* direct definition over the kept weights of each row, in storage order */
+        const int64_t nnz = jb->K / 2;
+        for (int64_t i = jb->r0; i < jb->r1; ++i) {
+            for (int b = 0; b < jb->B; ++b) {
+                const uint16_t *xb = jb->x + (int64_t)b * jb->ldx;
+                double s = 0.0, a = 0.0;
+                for (int64_t t = 0; t < nnz; ++t) {
+                    int64_t col = meta_column(jb->meta, jb->fmt, i, t, jb->K);
+                    double p = bf16_val(jb->values[i * nnz + t]) * bf16_val(xb[col]);
+                    s = s + p;
+                    a = a + fabs(p);
+                }
+                jb->y[(int64_t)b * jb->R + i] = s;
+                jb->absum[(int64_t)b * jb->R + i] = a;
+            }
+        }
+        return NULL;
+    }
     for (int64_t i = jb->r0; i < jb->r1; ++i) {
         const uint16_t *w;
         if (jb->masks) {
@@ -313,6 +394,36 @@ int nmo_dense(const uint16_t *W, int64_t ldw, int64_t R, int64_t K, const uint16
     memset(&p, 0, sizeof p);
     p.values = W;
     p.ldw = ldw;
+    p.R = R;
+    p.K = K;
+    p.ldx = ldx;
+    p.x = x;
+    p.B = B;
+    p.y = y;
+    p.absum = absum;
+    return run_mv(p, nthreads);
+}
+
+/* Sparse reference over index metadata: y[b][i] = sum_t values[i][t] * x[b][col(i, t)],
+ * summed in storage order (which is ascending column order, so on metadata built from
+ * masks the result equals nmo_spmv's bit for bit). */
+int nmo_spmv_index(const void *meta, int fmt, const uint16_t *values, int64_t R, int64_t K, const uint16_t *x,
+                   int64_t ldx, int B, double *y, double *absum, int nthreads)
+{
+    if (!meta || !values || !x || !y || !absum) return NMO_EARG;
+    if (fmt != NMO_META_U8 && fmt != NMO_META_I32) return NMO_EARG;
+    if (R < 1 || K < 32 || K % 32 != 0 || B < 1 || ldx < K) return NMO_EARG;
+    int rc = check_x(x, K, ldx, B);
+    if (rc) return rc;
+    rc = check_meta(meta, fmt, R, K);
+    if (rc) return rc;
+    for (int64_t i = 0; i < R * (K / 2); ++i)
+        if (!bf16_finite(values[i])) return NMO_ENONFINITE;
+    mv_job p;
+    memset(&p, 0, sizeof p);
+    p.meta = meta;
+    p.fmt = fmt;
+    p.values = values;
     p.R = R;
     p.K = K;
     p.ldx = ldx;

@@ -48,7 +48,9 @@ def L():
 def test_header_declares_the_expected_entry_points():
     names = declared_functions()
     for n in ("nm_col_norm", "nm_prune_pack", "nm_spmv", "nm_spmv_workspace_bytes", "dense_gemv",
-              "dense_gemv_workspace_bytes", "nm_unpack", "nm_status_str", "nm_last_error", "nm_version"):
+              "dense_gemv_workspace_bytes", "nm_unpack", "nm_status_str", "nm_last_error", "nm_version",
+              "nm_spmv_multi", "nm_spmv_multi_workspace_bytes", "dense_gemv_multi",
+              "dense_gemv_multi_workspace_bytes", "nm_meta_from_mask", "nm_spmv_meta"):
         assert n in names
 
 
@@ -157,3 +159,28 @@ def test_multi_entry_points_reject_bad_arguments(L):
     assert L.dense_gemv_multi(ctypes.cast(dgood, p), 1, 60, A16, 64, 1, None, 0, None) == NM_ERR_SHAPE
     dbad = (_Mat * 1)(_Mat(A4, 64, 8, A16, 8))
     assert L.dense_gemv_multi(ctypes.cast(dbad, p), 1, 64, A16, 64, 1, None, 0, None) == NM_ERR_ALIGN
+
+
+def test_metadata_entry_points_reject_bad_arguments(L):
+    p, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    L.nm_meta_from_mask.argtypes = [p, i64, i64, i32, p, p]
+    L.nm_spmv_meta.argtypes = [p, i32, p, i64, i64, p, i64, i32, p, i64, p, sz, p]
+    # conversion
+    assert L.nm_meta_from_mask(None, 4, 64, 1, A16, None) == NM_ERR_NULL
+    assert L.nm_meta_from_mask(A4, 4, 64, 1, None, None) == NM_ERR_NULL
+    assert L.nm_meta_from_mask(A4, 4, 64, 0, A16, None) == NM_ERR_PATTERN  # bitmask: nothing to convert
+    assert L.nm_meta_from_mask(A4, 4, 64, 3, A16, None) == NM_ERR_PATTERN
+    assert L.nm_meta_from_mask(A4, 4, 48, 1, A16, None) == NM_ERR_SHAPE
+    assert L.nm_meta_from_mask(A4, 0, 64, 2, A16, None) == NM_ERR_SHAPE
+    assert L.nm_meta_from_mask(A2, 4, 64, 2, A16, None) == NM_ERR_ALIGN
+    assert L.nm_meta_from_mask(A4, 4, 64, 2, A4, None) == NM_ERR_ALIGN
+    # product
+    assert L.nm_spmv_meta(None, 1, A16, 4, 64, A16, 64, 1, A16, 4, None, 0, None) == NM_ERR_NULL
+    assert L.nm_spmv_meta(A16, 7, A16, 4, 64, A16, 64, 1, A16, 4, None, 0, None) == NM_ERR_PATTERN
+    assert L.nm_spmv_meta(A16, -1, A16, 4, 64, A16, 64, 1, A16, 4, None, 0, None) == NM_ERR_PATTERN
+    assert L.nm_spmv_meta(A16, 1, A16, 4, 48, A16, 64, 1, A16, 4, None, 0, None) == NM_ERR_SHAPE
+    assert L.nm_spmv_meta(A16, 2, A16, 4, 64, A16, 64, 9, A16, 4, None, 0, None) == NM_ERR_SHAPE
+    assert L.nm_spmv_meta(A4, 1, A16, 4, 64, A16, 64, 1, A16, 4, None, 0, None) == NM_ERR_ALIGN  # u8 meta
+    assert L.nm_spmv_meta(A4, 2, A16, 4, 64, A16, 64, 1, A16, 4, None, 0, None) == NM_ERR_ALIGN  # i32 meta
+    assert L.nm_spmv_meta(A2, 0, A16, 4, 64, A16, 64, 1, A16, 4, None, 0, None) == NM_ERR_ALIGN  # masks
+    assert L.nm_spmv_meta(A16, 1, A4, 4, 64, A16, 64, 1, A16, 4, None, 0, None) == NM_ERR_ALIGN  # values
