@@ -64,43 +64,57 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 // Metadata bytes per 32-column word (16 kept weights) of each format.
 constexpr int meta_bytes(int fmt) { return fmt == kMetaBitmask ? 4 : (fmt == kMetaU8 ? 16 : 64); }
 
-// One wave-iteration batch: a 64-word strip of one row slice.  Per lane: the 16 packed
-// values of its word (two 16-byte chunks, before the pair swap) and the word's
-// metadata -- the mask word, 16 uint8 offsets, or 16 int32 column indices.
+// One wave-iteration batch: a 64-word strip of one row slice.
+//
+// Bitmask and uint8 offsets -- one word per lane.  Each 16-byte value load is contiguous
+// across the wave (lane l reads chunk l of the strip's first KiB, then chunk l of its
+// second KiB), which halves the cache lines each load instruction touches compared with
+// one lane reading a whole 32-byte word; a quad-permute then swaps halves between lane
+// pairs so that lane 2i ends up with word i and lane 2i+1 with word 32+i.  Each lane
+// loads its own word's metadata (4 or 16 bytes; the 16-byte offset loads of the wave
+// cover one contiguous KiB).
+//
+// int32 indices -- one quarter-word per lane and load.  A word's 64 bytes of indices
+// would take four 16-byte loads per lane at a 64-byte lane stride; instead load q
+// (q = 0..3) gives lane l the indices of kept weights 4(l%4)..4(l%4)+3 of word
+// 16q + l/4 (contiguous 1 KiB across the wave) and the matching 8 bytes of values
+// (contiguous 512 bytes).  Every lane then walks four entries of four words of the
+// same row; the row total does not care which lane holds which product.
 template <int FMT>
 struct Batch {
-    u32x4 va, vb;
-    u32x4 meta[FMT == kMetaI32 ? 4 : 1];
-    int lw;  // word index within the slice (>= the slice length marks a padding lane)
+    u32x4 va, vb;                          // values: two 16-byte chunks, or four 8-byte pieces (int32)
+    u32x4 meta[FMT == kMetaI32 ? 4 : 1];   // mask (.x) / 16 offsets / four quarter-words of indices
+    int lw;  // (first) word of this lane within the slice; >= the slice length marks padding
 };
 
 // Loads one batch through raw buffer descriptors covering the row slice's `words`
 // words (0 = nothing to load: the loads still issue and return zeros, as do lanes
 // past the end of the slice).
-//
-// Lane mapping of a 64-word strip: each 16-byte value load is contiguous across the
-// wave (lane l reads chunk l of the strip's first KiB, then chunk l of its second
-// KiB), which halves the cache lines each load instruction touches compared with one
-// lane reading a whole 32-byte word.  A quad-permute then swaps halves between lane
-// pairs so that lane 2i ends up with word i and lane 2i+1 with word 32+i; each lane
-// loads its own word's metadata.
 template <int FMT>
 __device__ __forceinline__ void load_batch(Batch<FMT> &bt, const uint8_t *mrow, const u32x4 *vrow, int words,
                                            int base, int lane) {
     const __amdgpu_buffer_rsrc_t rm = make_rsrc(mrow, (int64_t)words * meta_bytes(FMT));
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vrow, (int64_t)words * 32);
-    const int w = base + ((lane & 1) ? 32 + (lane >> 1) : (lane >> 1));
-    if constexpr (FMT == kMetaBitmask) {
-        bt.meta[0].x = __builtin_amdgcn_raw_buffer_load_b32(rm, w * 4, 0, kLoadNT);
-    } else if constexpr (FMT == kMetaU8) {
-        bt.meta[0] = __builtin_amdgcn_raw_buffer_load_b128(rm, w * 16, 0, kLoadNT);
-    } else {
+    if constexpr (FMT == kMetaI32) {
+        u32x2 v[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) bt.meta[q] = __builtin_amdgcn_raw_buffer_load_b128(rm, w * 64 + 16 * q, 0, kLoadNT);
+        for (int q = 0; q < 4; ++q) {
+            bt.meta[q] = __builtin_amdgcn_raw_buffer_load_b128(rm, base * 64 + 1024 * q + 16 * lane, 0, kLoadNT);
+            v[q] = __builtin_amdgcn_raw_buffer_load_b64(rv, base * 32 + 512 * q + 8 * lane, 0, kLoadNT);
+        }
+        bt.va = u32x4{v[0].x, v[0].y, v[1].x, v[1].y};
+        bt.vb = u32x4{v[2].x, v[2].y, v[3].x, v[3].y};
+        bt.lw = base + (lane >> 2);
+    } else {
+        const int w = base + ((lane & 1) ? 32 + (lane >> 1) : (lane >> 1));
+        if constexpr (FMT == kMetaBitmask)
+            bt.meta[0].x = __builtin_amdgcn_raw_buffer_load_b32(rm, w * 4, 0, kLoadNT);
+        else
+            bt.meta[0] = __builtin_amdgcn_raw_buffer_load_b128(rm, w * 16, 0, kLoadNT);
+        bt.va = __builtin_amdgcn_raw_buffer_load_b128(rv, base * 32 + lane * 16, 0, kLoadNT);
+        bt.vb = __builtin_amdgcn_raw_buffer_load_b128(rv, base * 32 + 1024 + lane * 16, 0, kLoadNT);
+        bt.lw = w;
     }
-    bt.va = __builtin_amdgcn_raw_buffer_load_b128(rv, base * 32 + lane * 16, 0, kLoadNT);
-    bt.vb = __builtin_amdgcn_raw_buffer_load_b128(rv, base * 32 + 1024 + lane * 16, 0, kLoadNT);
-    bt.lw = w;
 }
 
 // Swap one dword with the neighbouring lane of the pair (lane ^ 1).
@@ -126,66 +140,79 @@ __device__ __forceinline__ void gather_col(const uint32_t *blk, int c, uint32_t 
     }
 }
 
-// Column (0..31 within the word) of the t-th kept weight of a word.  Bitmask: the fixed
-// 16-step walk -- lowest set bit gives the column, then that bit is cleared.  uint8
-// offset: byte t.  int32 index: at 50% N:M an index of word w always lies in
-// [32w, 32w + 32), so its low five bits are the column within the word.  The index
-// formats are masked to five bits so that no metadata value can address outside the
-// word's block of x.
-template <int FMT>
-__device__ __forceinline__ int column_of(const Batch<FMT> &bt, uint32_t &mm, int t) {
-    if constexpr (FMT == kMetaBitmask) {
-        const int c = __builtin_ctz(mm);
-        mm &= mm - 1;
-        return c;
-    } else if constexpr (FMT == kMetaU8) {
-        return (int)((bt.meta[0][t >> 2] >> (8 * (t & 3))) & 31u);
+// One pair of kept weights: the inputs of columns c0 and c1 of the word's block (per
+// token) meet the packed value pair v in one v_dot2_f32_bf16.
+template <int B>
+__device__ __forceinline__ void dot_pair(uint32_t v, const uint32_t *blk, int c0, int c1, float (&acc)[B]) {
+    constexpr int S = XLayout<B>::S;
+    if constexpr (S == 1) {
+        const uint16_t *xw = reinterpret_cast<const uint16_t *>(blk);
+        const uint32_t pr = (uint32_t)xw[c0] | ((uint32_t)xw[c1] << 16);
+        acc[0] = dot2_bf16(v, pr, acc[0]);
     } else {
-        return (int)(bt.meta[t >> 2][t & 3] & 31u);
+        uint32_t d0[S / 2], d1[S / 2];
+        gather_col<S>(blk, c0, d0);
+        gather_col<S>(blk, c1, d1);
+#pragma unroll
+        for (int j = 0; j < S / 2; ++j) {
+            // (token 2j of column c0, token 2j of column c1), then the same for 2j+1
+            if (2 * j < B) acc[2 * j] = dot2_bf16(v, __builtin_amdgcn_perm(d1[j], d0[j], 0x05040100u), acc[2 * j]);
+            if (2 * j + 1 < B)
+                acc[2 * j + 1] = dot2_bf16(v, __builtin_amdgcn_perm(d1[j], d0[j], 0x07060302u), acc[2 * j + 1]);
+        }
     }
 }
 
-// Walk of one word: 8 pairs of kept weights; the two gathered inputs of a pair meet the
-// packed value pair in one v_dot2_f32_bf16 (per token).
+// Walk of one batch: 8 pairs of kept weights per lane.
+//
+// Columns within the word: bitmask -- the fixed 16-step walk, lowest set bit gives the
+// column and is then cleared; uint8 -- byte t of the word's offsets; int32 -- at 50% N:M
+// an index of word w always lies in [32w, 32w + 32), so its low five bits are the column
+// within the word.  The index formats are masked to five bits so that no metadata value
+// can address outside the word's block of x.
+//
+// A padding lane (past the slice) holds zero values and walks fixed columns of block 0
+// (bitmask: the low 16 columns; index formats: zero metadata, column 0), so every LDS
+// address stays inside the staged x.
 template <int FMT, int B>
 __device__ __forceinline__ void walk_batch(const Batch<FMT> &bt, const uint32_t *xs, int nws, float (&acc)[B]) {
-    constexpr int S = XLayout<B>::S;
     constexpr int kBlk = XLayout<B>::kBlk;
-    // A padding lane (past the slice) holds zero values: it walks 16 fixed columns of
-    // block 0 (index formats: zero metadata, column 0) so every LDS address stays inside
-    // the staged x.
-    const bool ok = bt.lw < nws;
-    const int lw = ok ? bt.lw : 0;
-    // Reassemble this lane's 16 values (see load_batch): even lanes keep their first
-    // chunk and receive the partner's first chunk; odd lanes receive the partner's
-    // second chunk and keep their own second chunk.
-    const bool odd = threadIdx.x & 1;
-    const uint32_t s_x = odd ? bt.va.x : bt.vb.x, s_y = odd ? bt.va.y : bt.vb.y;
-    const uint32_t s_z = odd ? bt.va.z : bt.vb.z, s_w = odd ? bt.va.w : bt.vb.w;
-    const uint32_t r_x = pair_swap(s_x), r_y = pair_swap(s_y), r_z = pair_swap(s_z), r_w = pair_swap(s_w);
-    const uint32_t v[8] = {odd ? r_x : bt.va.x, odd ? r_y : bt.va.y, odd ? r_z : bt.va.z, odd ? r_w : bt.va.w,
-                           odd ? bt.vb.x : r_x, odd ? bt.vb.y : r_y, odd ? bt.vb.z : r_z, odd ? bt.vb.w : r_w};
-    const uint32_t *blk = xs + lw * kBlk;  // this word's 32 columns
-    uint32_t mm = ok ? bt.meta[0].x : 0xFFFFu;
+    if constexpr (FMT == kMetaI32) {
+        const uint32_t v[8] = {bt.va.x, bt.va.y, bt.va.z, bt.va.w, bt.vb.x, bt.vb.y, bt.vb.z, bt.vb.w};
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        const int c0 = column_of<FMT>(bt, mm, 2 * k);
-        const int c1 = column_of<FMT>(bt, mm, 2 * k + 1);
-        if constexpr (S == 1) {
-            const uint16_t *xw = reinterpret_cast<const uint16_t *>(blk);
-            const uint32_t pr = (uint32_t)xw[c0] | ((uint32_t)xw[c1] << 16);
-            acc[0] = dot2_bf16(v[k], pr, acc[0]);
-        } else {
-            uint32_t d0[S / 2], d1[S / 2];
-            gather_col<S>(blk, c0, d0);
-            gather_col<S>(blk, c1, d1);
+        for (int q = 0; q < 4; ++q) {
+            const int w = bt.lw + 16 * q;
+            const uint32_t *blk = xs + (w < nws ? w : 0) * kBlk;
+            dot_pair<B>(v[2 * q], blk, (int)(bt.meta[q].x & 31u), (int)(bt.meta[q].y & 31u), acc);
+            dot_pair<B>(v[2 * q + 1], blk, (int)(bt.meta[q].z & 31u), (int)(bt.meta[q].w & 31u), acc);
+        }
+    } else {
+        const bool ok = bt.lw < nws;
+        // Reassemble this lane's 16 values: even lanes keep their first chunk and receive
+        // the partner's first chunk; odd lanes receive the partner's second chunk and keep
+        // their own second chunk.
+        const bool odd = threadIdx.x & 1;
+        const uint32_t s_x = odd ? bt.va.x : bt.vb.x, s_y = odd ? bt.va.y : bt.vb.y;
+        const uint32_t s_z = odd ? bt.va.z : bt.vb.z, s_w = odd ? bt.va.w : bt.vb.w;
+        const uint32_t r_x = pair_swap(s_x), r_y = pair_swap(s_y), r_z = pair_swap(s_z), r_w = pair_swap(s_w);
+        const uint32_t v[8] = {odd ? r_x : bt.va.x, odd ? r_y : bt.va.y, odd ? r_z : bt.va.z, odd ? r_w : bt.va.w,
+                               odd ? bt.vb.x : r_x, odd ? bt.vb.y : r_y, odd ? bt.vb.z : r_z, odd ? bt.vb.w : r_w};
+        const uint32_t *blk = xs + (ok ? bt.lw : 0) * kBlk;  // this word's 32 columns
+        uint32_t mm = ok ? bt.meta[0].x : 0xFFFFu;
 #pragma unroll
-            for (int j = 0; j < S / 2; ++j) {
-                // (token 2j of column c0, token 2j of column c1), then the same for 2j+1
-                if (2 * j < B) acc[2 * j] = dot2_bf16(v[k], __builtin_amdgcn_perm(d1[j], d0[j], 0x05040100u), acc[2 * j]);
-                if (2 * j + 1 < B)
-                    acc[2 * j + 1] = dot2_bf16(v[k], __builtin_amdgcn_perm(d1[j], d0[j], 0x07060302u), acc[2 * j + 1]);
+        for (int k = 0; k < 8; ++k) {
+            int c0, c1;
+            if constexpr (FMT == kMetaBitmask) {
+                c0 = __builtin_ctz(mm);
+                mm &= mm - 1;
+                c1 = __builtin_ctz(mm);
+                mm &= mm - 1;
+            } else {
+                const uint32_t o = bt.meta[0][k >> 1] >> (16 * (k & 1));  // offsets 2k, 2k+1
+                c0 = (int)(o & 31u);
+                c1 = (int)((o >> 8) & 31u);
             }
+            dot_pair<B>(v[k], blk, c0, c1, acc);
         }
     }
 }

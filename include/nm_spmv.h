@@ -200,9 +200,11 @@ nm_status nm_meta_from_mask(const uint32_t *masks, int64_t R, int64_t K, int for
 /*
  * nm_spmv_meta -- nm_spmv with the metadata in any nm_meta_format: the same product
  * y[b][i] = sum_j Wsparse[i][j] * x[b][j] with the t-th kept weight of word w at the
- * column the metadata gives.  Same arithmetic, pairing order, rounding, workspace
- * (nm_spmv_workspace_bytes) and requirements as nm_spmv; meta must be 4-byte
- * (bitmask) or 16-byte (index formats) aligned.  At 50% N:M every weight of word w lies
+ * column the metadata gives.  Same precision (fp32 products and sums, bf16 RNE store),
+ * workspace (nm_spmv_workspace_bytes) and requirements as nm_spmv; meta must be 4-byte
+ * (bitmask) or 16-byte (index formats) aligned.  Bitmask and uint8 offsets also sum in
+ * nm_spmv's order (identical bits); int32 indices are walked a quarter-word per lane, a
+ * different fp32 summation order (deterministic run to run).  At 50% N:M every weight of word w lies
  * in columns [32w, 32w+32); the kernel reads the low five bits of each offset/index
  * (an entry that breaks this rule reads a wrong column of the same word, never memory
  * outside x).  Unknown formats fail with NM_ERR_PATTERN.

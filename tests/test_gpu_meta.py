@@ -1,7 +1,9 @@
 """GPU parity of the index-metadata path (uint8 offsets, int32 column indices): the
 conversion kernel bit-exact against the oracle, and the SpMV over each format within
-the SpMV tolerance of the oracle's direct index-metadata matvec -- and bit-identical to
-the bitmask SpMV, whose per-row arithmetic (pairing, order, rounding) it shares."""
+the SpMV tolerance of the oracle's direct index-metadata matvec.  The uint8 path walks
+each word in the same lane and order as the bitmask SpMV, so its outputs are also
+bit-identical to nm_spmv's; the int32 path spreads a word over four lanes (another
+fp32 summation order), so it is held to the tolerance and to run-to-run determinism."""
 from __future__ import annotations
 
 import numpy as np
@@ -57,13 +59,16 @@ def test_spmv_meta_matches_oracle_and_bitmask(fmt, ofmt, R, K, B):
     xd, vd = dev_bf16(x), dev_bf16(v)
     meta_d = torch.from_numpy(np.ascontiguousarray(meta)).cuda()
     y = nm.nm_spmv_meta(meta_d, fmt, vd, xd)
+    y2 = nm.nm_spmv_meta(meta_d, fmt, vd, xd)
     yb = nm.nm_spmv(dev_u32(m), vd, xd)
     torch.cuda.synchronize()
     yref, absum = oracle.spmv_index(meta, ofmt, v, x, K, nthreads=4)
     got = bf16_as_f64(host_bf16(y))
     ok = oracle.within_tolerance(got, yref, absum, RTOL, ATOL_FRAC)
     assert ok.all(), f"{int((~ok).sum())} of {ok.size} outside tolerance"
-    assert (host_bf16(y) == host_bf16(yb)).all()
+    assert (host_bf16(y) == host_bf16(y2)).all()
+    if fmt == nm.NM_META_U8_OFFSET:
+        assert (host_bf16(y) == host_bf16(yb)).all()
 
 
 def test_spmv_meta_bitmask_format_is_nm_spmv():
@@ -91,7 +96,8 @@ def test_spmv_meta_full_size_sampled(fmt, ofmt):
     y = nm.nm_spmv_meta(meta, fmt, values, xd)
     yb = nm.nm_spmv(masks, values, xd)
     torch.cuda.synchronize()
-    assert (host_bf16(y) == host_bf16(yb)).all()
+    if fmt == nm.NM_META_U8_OFFSET:
+        assert (host_bf16(y) == host_bf16(yb)).all()
     g = np.random.default_rng(5)
     rows = np.unique(np.concatenate([[0, R - 1], g.choice(R, size=128, replace=False)]))
     ridx = torch.from_numpy(rows).cuda()
