@@ -215,7 +215,11 @@ def main():
         xs[group] = [synth.device_decode_x(B, K, args.seed, 300 + gi, l) for l in range(L)]
     ys = {name: torch.empty((B, R), dtype=torch.bfloat16, device=dev) for name, R, K, _ in projs}
     ws_bytes = max([nm.nm_spmv_workspace_bytes(R, K, B) for _, R, K, _ in projs]
-                   + [nm.dense_gemv_workspace_bytes(R, K, B) for _, R, K, _ in projs] + [4])
+                   + [nm.dense_gemv_workspace_bytes(R, K, B) for _, R, K, _ in projs]
+                   + [nm.nm_spmv_swiglu_workspace_bytes(R, K, B) for _, R, K, _ in projs]
+                   + [nm.dense_gemv_swiglu_workspace_bytes(R, K, B) for _, R, K, _ in projs]
+                   + [nm.nm_spmv_multi_workspace_bytes([R] * 3, K, B) for _, R, K, _ in projs]
+                   + [nm.dense_gemv_multi_workspace_bytes([R] * 3, K, B) for _, R, K, _ in projs] + [4])
     ws = torch.empty((ws_bytes + 3) // 4, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
     log(f"inputs generated and packed in {time.time() - t0:.1f}s "
@@ -295,6 +299,10 @@ def main():
                 if len(grp) == 1:
                     name = grp[0][0]
                     fused_fns.append(spmv_call(pool_sparse[(N, M), name][l], xs[grp[0][3]][l], ys[name]))
+                elif [pr[0] for pr in grp] == ["gate", "up"]:
+                    # gated MLP: h = silu(gate x) * (up x) written by the launch's epilogue
+                    fused_fns.append(lambda g=pool_sparse[(N, M), "gate"][l], u=pool_sparse[(N, M), "up"][l],
+                                     x=xs[grp[0][3]][l]: nm.nm_spmv_swiglu(g, u, x, out=ys["gate"], workspace=ws))
                 else:
                     pk = [pool_sparse[(N, M), pr[0]][l] for pr in grp]
                     outs = [ys[pr[0]] for pr in grp]
@@ -302,6 +310,10 @@ def main():
                                      nm.nm_spmv_multi(pk, x, outs=outs, workspace=ws))
     for l in range(L):
         for grp in groups:
+            if [pr[0] for pr in grp] == ["gate", "up"]:
+                fused_dense_fns.append(lambda g=pool_dense["gate"][l], u=pool_dense["up"][l], x=xs[grp[0][3]][l]:
+                                       nm.dense_gemv_swiglu(g, u, x, out=ys["gate"], workspace=ws))
+                continue
             Wl = [pool_dense[pr[0]][l] for pr in grp]
             outs = [ys[pr[0]] for pr in grp]
             fused_dense_fns.append(lambda Wl=Wl, x=xs[grp[0][3]][l], outs=outs:
@@ -360,6 +372,40 @@ def main():
             d[f"{N}:{M}"]["speedup_vs_hipblaslt"] = round(us_lin / d[f"{N}:{M}"]["us"], 3)
         del g, gl
     torch.cuda.synchronize()
+
+    # ---------------------------------------------------------------- gated MLP in one launch
+    # gate and up of one layer walked by one launch whose epilogue writes silu(g) * u.
+    names = [p[0] for p in projs]
+    if "gate" in names and "up" in names:
+        (_, R, K, group) = projs[names.index("gate")]
+        fb = 2 * (R * K + R * K // 8) + 2 * B * K + 2 * B * R  # both packed matrices, x once, h
+        fdb = 4 * R * K + 2 * B * K + 2 * B * R
+        d = per.setdefault("gate|up+swiglu", {"R": R, "K": K})
+        for (N, M) in patterns:
+            pg, pu = pool_sparse[(N, M), "gate"], pool_sparse[(N, M), "up"]
+            fns = [(lambda g=g, u=u, x=xs[group][i % L]: nm.nm_spmv_swiglu(g, u, x, out=ys["gate"], workspace=ws))
+                   for i, (g, u) in enumerate(zip(pg, pu))]
+            g = capture(torch, fns)
+            g.replay()
+            us = min(timer.time_graph(g, 1) for _ in range(reps)) * 1e3 / len(fns)
+            d[f"{N}:{M}"] = {"us": round(us, 2), "GBs": round(fb / us / 1e3, 1),
+                             "pct_peak": round(100 * fb / us / 1e3 / HBM_PEAK_GBS, 1),
+                             "rotation_MB": round(len(fns) * fb / 1e6)}
+            del g
+        pg, pu = pool_dense["gate"], pool_dense["up"]
+        fns = [(lambda a=a, b=b, x=xs[group][i % L]: nm.dense_gemv_swiglu(a, b, x, out=ys["gate"], workspace=ws))
+               for i, (a, b) in enumerate(zip(pg, pu))]
+        g = capture(torch, fns)
+        g.replay()
+        us = min(timer.time_graph(g, 1) for _ in range(reps)) * 1e3 / len(fns)
+        d["dense_us"] = round(us, 2)
+        d["dense_GBs"] = round(fdb / us / 1e3, 1)
+        for (N, M) in patterns:
+            d[f"{N}:{M}"]["speedup_vs_dense"] = round(us / d[f"{N}:{M}"]["us"], 3)
+        del g
+        torch.cuda.synchronize()
+        log("gate|up+swiglu: " + ", ".join(f"{k} {v['us']} us ({v['pct_peak']}%)" for k, v in d.items()
+                                            if isinstance(v, dict)) + f"; dense {d['dense_us']} us")
 
     # ---------------------------------------------------------------- metadata formats
     # The same product over the first pattern's packs with the metadata as uint8 offsets
@@ -473,7 +519,9 @@ def main():
                        "pct_hbm_peak": round(100 * step_sparse_bytes / (ms_fused * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
                        "dense_ms": round(ms_fused_dense, 4),
                        "speedup_vs_dense": round(ms_fused_dense * len(patterns) / ms_fused, 3),
-                       "groups": ["|".join(pr[0] for pr in grp) for grp in groups]},
+                       "groups": ["|".join(pr[0] for pr in grp)
+                                  + ("+swiglu" if [pr[0] for pr in grp] == ["gate", "up"] else "")
+                                  for grp in groups]},
         "per_layer": per,
         "metadata_formats": meta_table,
         "pack_GBs": round(pack_bytes / pack_ms / 1e6, 1),

@@ -23,7 +23,8 @@ __all__ = [
     "nm_spmv_workspace_bytes", "dense_gemv", "dense_gemv_workspace_bytes", "nm_unpack",
     "NM_PATTERNS", "nm_spmv_multi", "nm_spmv_multi_workspace_bytes", "dense_gemv_multi",
     "dense_gemv_multi_workspace_bytes", "NM_META_BITMASK", "NM_META_U8_OFFSET", "NM_META_I32_INDEX",
-    "nm_meta_from_mask", "nm_spmv_meta",
+    "nm_meta_from_mask", "nm_spmv_meta", "nm_spmv_swiglu", "nm_spmv_swiglu_workspace_bytes", "dense_gemv_swiglu",
+    "dense_gemv_swiglu_workspace_bytes",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnmspmv.so")
@@ -68,6 +69,10 @@ def _load() -> ctypes.CDLL:
     L.dense_gemv.argtypes = [p, i64, i64, i64, p, i64, i32, p, i64, p, sz, p]
     L.nm_unpack.argtypes = [p, p, i64, i64, p, i64, p]
     L.nm_meta_from_mask.argtypes = [p, i64, i64, i32, p, p]
+    L.nm_spmv_swiglu_workspace_bytes.argtypes, L.nm_spmv_swiglu_workspace_bytes.restype = [i64, i64, i32], sz
+    L.nm_spmv_swiglu.argtypes = [p, p, p, p, i64, i64, p, i64, i32, p, i64, p, sz, p]
+    L.dense_gemv_swiglu_workspace_bytes.argtypes, L.dense_gemv_swiglu_workspace_bytes.restype = [i64, i64, i32], sz
+    L.dense_gemv_swiglu.argtypes = [p, p, i64, i64, i64, p, i64, i32, p, i64, p, sz, p]
     L.nm_spmv_meta.argtypes = [p, i32, p, i64, i64, p, i64, i32, p, i64, p, sz, p]
     L.nm_spmv_multi_workspace_bytes.argtypes = [p, i32, i64, i32]
     L.nm_spmv_multi_workspace_bytes.restype = sz
@@ -273,6 +278,49 @@ def nm_spmv_meta(meta: torch.Tensor, fmt: int, values: torch.Tensor, x: torch.Te
     ws, ws_bytes = _workspace(nm_spmv_workspace_bytes(R, K, B), x2, workspace)
     _check(lib.nm_spmv_meta(_ptr(meta), int(fmt), _ptr(values), R, K, _ptr(x2), _ld(x2), B, _ptr(o2), _ld(o2),
                             _ptr(ws), ws_bytes, _stream(x2)))
+    return out[0] if squeeze and out.dim() == 2 else out
+
+
+def nm_spmv_swiglu_workspace_bytes(R: int, K: int, B: int) -> int:
+    return int(lib.nm_spmv_swiglu_workspace_bytes(R, K, B))
+
+
+def dense_gemv_swiglu_workspace_bytes(R: int, K: int, B: int) -> int:
+    return int(lib.dense_gemv_swiglu_workspace_bytes(R, K, B))
+
+
+def nm_spmv_swiglu(gate, up, x: torch.Tensor, out: torch.Tensor | None = None,
+                   workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """h = silu(W_gate x) * (W_up x) for packed gate = (masks, values) and up = (masks, values),
+    both R x K; x: bf16 [B, K] or [K] -> bf16 [B, R] (or [R])."""
+    (gm, gv), (um, uv) = gate, up
+    for t, n, dt in ((gm, "gate masks", torch.int32), (gv, "gate values", torch.bfloat16),
+                     (um, "up masks", torch.int32), (uv, "up values", torch.bfloat16)):
+        _dev(t, n, dt, 2)
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+    R, K = gm.shape[0], gm.shape[1] * 32
+    if gv.shape != (R, K // 2) or um.shape != gm.shape or uv.shape != gv.shape:
+        raise ValueError("gate and up must both be packed R x K matrices")
+    x2, B, o2, out, squeeze = _x_y(x, R, K, out)
+    ws, ws_bytes = _workspace(nm_spmv_swiglu_workspace_bytes(R, K, B), x2, workspace)
+    _check(lib.nm_spmv_swiglu(_ptr(gm), _ptr(gv), _ptr(um), _ptr(uv), R, K, _ptr(x2), _ld(x2), B, _ptr(o2),
+                              _ld(o2), _ptr(ws), ws_bytes, _stream(x2)))
+    return out[0] if squeeze and out.dim() == 2 else out
+
+
+def dense_gemv_swiglu(W_gate: torch.Tensor, W_up: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None,
+                      workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Dense baseline of nm_spmv_swiglu: W_gate, W_up bf16 [R, K] with the same row stride."""
+    _dev(W_gate, "W_gate", torch.bfloat16, 2)
+    _dev(W_up, "W_up", torch.bfloat16, 2)
+    if W_gate.shape != W_up.shape or _ld(W_gate) != _ld(W_up):
+        raise ValueError("W_gate and W_up must have the same shape and row stride")
+    R, K = W_gate.shape
+    x2, B, o2, out, squeeze = _x_y(x, R, K, out)
+    ws, ws_bytes = _workspace(dense_gemv_swiglu_workspace_bytes(R, K, B), x2, workspace)
+    _check(lib.dense_gemv_swiglu(_ptr(W_gate), _ptr(W_up), _ld(W_gate), R, K, _ptr(x2), _ld(x2), B, _ptr(o2),
+                                 _ld(o2), _ptr(ws), ws_bytes, _stream(x2)))
     return out[0] if squeeze and out.dim() == 2 else out
 
 

@@ -306,6 +306,52 @@ nm_status nm_spmv_multi(const nm_spmv_matrix *mats, int P, int64_t K, const nm_b
     }
 }
 
+size_t nm_spmv_swiglu_workspace_bytes(int64_t R, int64_t K, int B) {
+    if (R < 1 || R > kMaxDim / 2 || K < 32 || K % 32 != 0 || K > kMaxDim || B < 1 || B > 8) return 0;
+    return spmv_plan(2 * R, K, B).ws_bytes;
+}
+
+nm_status nm_spmv_swiglu(const uint32_t *gate_masks, const nm_bf16 *gate_values, const uint32_t *up_masks,
+                         const nm_bf16 *up_values, int64_t R, int64_t K, const nm_bf16 *x, int64_t ldx, int B,
+                         nm_bf16 *h, int64_t ldh, void *workspace, size_t workspace_bytes, void *hip_stream) {
+    try {
+        g_err[0] = 0;
+        const char *who = "nm_spmv_swiglu";
+        if (!gate_masks || !gate_values || !up_masks || !up_values || !x || !h)
+            return fail(NM_ERR_NULL, "%s: NULL pointer", who);
+        if (K < 32 || K > kMaxDim || K % 32 != 0)
+            return fail(NM_ERR_SHAPE, "%s: K=%lld must be a positive multiple of 32", who, (long long)K);
+        if (R > kMaxDim / 2) return fail(NM_ERR_SHAPE, "%s: R=%lld above 2^29", who, (long long)R);
+        nm_status st = check_mv_common(R, K, B, ldx, ldh, x, h);
+        if (st != NM_OK) return st;
+        if (!aligned(gate_masks, 4) || !aligned(up_masks, 4) || !aligned(gate_values, 16) || !aligned(up_values, 16))
+            return fail(NM_ERR_ALIGN, "%s: masks need 4-byte and values 16-byte alignment", who);
+        nmk::SpmvSet set;
+        set.P = 2;
+        set.row0[1] = (int)R;
+        set.row0[2] = (int)(2 * R);
+        set.meta[0] = gate_masks;
+        set.values[0] = gate_values;
+        set.meta[1] = up_masks;
+        set.values[1] = up_values;
+        set.y[0] = h;
+        set.ldy[0] = ldh;
+        set.y[1] = h;  // unused: the epilogue writes matrix 0's output only
+        set.ldy[1] = ldh;
+        const nmk::MvPlan p = spmv_plan(2 * R, K, B);
+        if (p.ws_bytes > 0) {
+            if (!workspace || workspace_bytes < p.ws_bytes || !aligned(workspace, 4))
+                return fail(NM_ERR_WORKSPACE, "%s: workspace of %zu bytes required, %zu given", who, p.ws_bytes,
+                            workspace ? workspace_bytes : (size_t)0);
+        }
+        hipError_t e = nmk::launch_spmv_swiglu(p, set, K, x, ldx, B, (float *)workspace, (hipStream_t)hip_stream);
+        if (e != hipSuccess) return hip_fail(who, e);
+        return NM_OK;
+    } catch (...) {
+        return fail(NM_ERR_HIP, "nm_spmv_swiglu: internal error");
+    }
+}
+
 size_t dense_gemv_workspace_bytes(int64_t R, int64_t K, int B) {
     if (R < 1 || R > kMaxDim || K < 8 || K % 8 != 0 || K > kMaxDim || B < 1 || B > 8) return 0;
     return dense_plan(R, K, B).ws_bytes;
@@ -347,6 +393,48 @@ nm_status dense_gemv(const nm_bf16 *W, int64_t ldw, int64_t R, int64_t K, const 
         return dense_run(set, K, x, ldx, B, workspace, workspace_bytes, hip_stream, "dense_gemv");
     } catch (...) {
         return fail(NM_ERR_HIP, "dense_gemv: internal error");
+    }
+}
+
+size_t dense_gemv_swiglu_workspace_bytes(int64_t R, int64_t K, int B) {
+    if (R < 1 || R > kMaxDim / 2 || K < 8 || K % 8 != 0 || K > kMaxDim || B < 1 || B > 8) return 0;
+    return dense_plan(2 * R, K, B).ws_bytes;
+}
+
+nm_status dense_gemv_swiglu(const nm_bf16 *W_gate, const nm_bf16 *W_up, int64_t ldw, int64_t R, int64_t K,
+                            const nm_bf16 *x, int64_t ldx, int B, nm_bf16 *h, int64_t ldh, void *workspace,
+                            size_t workspace_bytes, void *hip_stream) {
+    try {
+        g_err[0] = 0;
+        const char *who = "dense_gemv_swiglu";
+        if (!W_gate || !W_up || !x || !h) return fail(NM_ERR_NULL, "%s: NULL pointer", who);
+        if (K < 8 || K > kMaxDim || K % 8 != 0 || ldw < K)
+            return fail(NM_ERR_SHAPE, "%s: bad sizes K=%lld ldw=%lld", who, (long long)K, (long long)ldw);
+        if (R > kMaxDim / 2) return fail(NM_ERR_SHAPE, "%s: R=%lld above 2^29", who, (long long)R);
+        nm_status st = check_mv_common(R, K, B, ldx, ldh, x, h);
+        if (st != NM_OK) return st;
+        if (ldw % 8 || !aligned(W_gate, 16) || !aligned(W_up, 16))
+            return fail(NM_ERR_ALIGN, "%s: W needs 16-byte alignment and ldw a multiple of 8", who);
+        nmk::DenseSet set;
+        set.P = 2;
+        set.row0[1] = (int)R;
+        set.row0[2] = (int)(2 * R);
+        set.W[0] = W_gate;
+        set.W[1] = W_up;
+        set.ldw[0] = set.ldw[1] = ldw;
+        set.y[0] = set.y[1] = h;
+        set.ldy[0] = set.ldy[1] = ldh;
+        const nmk::MvPlan p = dense_plan(2 * R, K, B);
+        if (p.ws_bytes > 0) {
+            if (!workspace || workspace_bytes < p.ws_bytes || !aligned(workspace, 4))
+                return fail(NM_ERR_WORKSPACE, "%s: workspace of %zu bytes required, %zu given", who, p.ws_bytes,
+                            workspace ? workspace_bytes : (size_t)0);
+        }
+        hipError_t e = nmk::launch_dense_swiglu(p, set, K, x, ldx, B, (float *)workspace, (hipStream_t)hip_stream);
+        if (e != hipSuccess) return hip_fail(who, e);
+        return NM_OK;
+    } catch (...) {
+        return fail(NM_ERR_HIP, "dense_gemv_swiglu: internal error");
     }
 }
 

@@ -72,32 +72,50 @@ __device__ __forceinline__ int owner(const DenseSet &set, int r) {
     return p;
 }
 
-template <int B>
-__device__ __forceinline__ void finish_drow(float (&acc)[B], const DenseSet &set, int row, int s, int R, int lane,
-                                            float *partial) {
-    const int p = owner(set, row);
+// Matrix and row within it of launch row r (see kEpiSwiGLU for the gated-MLP order).
+template <int EPI>
+__device__ __forceinline__ void locate(const DenseSet &set, int r, int &p, int &local) {
+    if constexpr (EPI == kEpiSwiGLU) {
+        p = r & 1;
+        local = r >> 1;
+    } else {
+        p = owner(set, r);
+        local = r - set.row0[p];
+    }
+}
+
+template <int B, int EPI>
+__device__ __forceinline__ void finish_drow(float (&acc)[B], float (&gsave)[B], const DenseSet &set, int row, int s,
+                                            int R, int lane, float *partial) {
+    int p, local;
+    locate<EPI>(set, row, p, local);
 #pragma unroll
     for (int b = 0; b < B; ++b) {
         const float tot = wave_sum(acc[b]);
         acc[b] = 0.f;
-        if (lane == 0) {
-            if (gridDim.y == 1)
-                set.y[p][(int64_t)b * set.ldy[p] + (row - set.row0[p])] = f32_to_bf16_rne(tot);
-            else
-                partial[((int64_t)s * B + b) * R + row] = tot;
+        if (gridDim.y != 1) {
+            if (lane == 0) partial[((int64_t)s * B + b) * R + row] = tot;
+        } else if constexpr (EPI == kEpiSwiGLU) {
+            if (p == 0)
+                gsave[b] = tot;
+            else if (lane == 0)
+                set.y[0][(int64_t)b * set.ldy[0] + local] = f32_to_bf16_rne(silu_mul(gsave[b], tot));
+        } else if (lane == 0) {
+            set.y[p][(int64_t)b * set.ldy[p] + local] = f32_to_bf16_rne(tot);
         }
     }
 }
 
-template <int U>
+template <int U, int EPI>
 __device__ __forceinline__ void load_row_dbatch(DBatch<U> &bt, const DenseSet &set, int r, int c0, int chunks,
                                                 int base, int lane) {
-    const int p = owner(set, r);
-    const u32x4 *wrow = reinterpret_cast<const u32x4 *>(set.W[p]) + (int64_t)(r - set.row0[p]) * (set.ldw[p] / 8) + c0;
+    int p, local;
+    locate<EPI>(set, r, p, local);
+    const u32x4 *wrow = reinterpret_cast<const u32x4 *>(set.W[p]) + (int64_t)local * (set.ldw[p] / 8) + c0;
     load_dbatch<U>(bt, wrow, chunks, base, lane);
 }
 
-template <int B, int U>
+template <int B, int U, int EPI>
 __global__ __launch_bounds__(kThreads) void dense_kernel(const DenseSet set, int KC, const uint16_t *__restrict__ x,
                                                          int64_t ldx, float *__restrict__ partial, int slice) {
     const int R = set.row0[set.P];
@@ -109,12 +127,19 @@ __global__ __launch_bounds__(kThreads) void dense_kernel(const DenseSet set, int
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     constexpr int kWaves = kThreads / kWave;
 
-    // Same flat, software-pipelined walk over (row, batch) as the sparse kernel.
-    const int first_row = blockIdx.x * kWaves + wave;
+    // Same flat, software-pipelined walk over (row, batch) as the sparse kernel, with the
+    // same row order (row pairs for the gated MLP).
+    const int unit = blockIdx.x * kWaves + wave;
     const int row_step = gridDim.x * kWaves;
+    const int first_row = EPI == kEpiSwiGLU ? 2 * unit : unit;
+    const int units = EPI == kEpiSwiGLU ? R / 2 : R;
+    const int my_rows = (unit < units ? (units - 1 - unit) / row_step + 1 : 0) * (EPI == kEpiSwiGLU ? 2 : 1);
     const int nb = (ncs + kWave * U - 1) / (kWave * U);
-    const int my_rows = first_row < R ? (R - 1 - first_row) / row_step + 1 : 0;
     const int total = my_rows * nb;
+    auto next_row = [&](int r) {
+        if constexpr (EPI == kEpiSwiGLU) return (r & 1) ? r - 1 + 2 * row_step : r + 1;
+        return r + row_step;
+    };
 
     DBatch<U> bufA, bufB;
     int rowA = first_row, biA = 0, rowB = first_row, biB = 0;
@@ -133,7 +158,7 @@ __global__ __launch_bounds__(kThreads) void dense_kernel(const DenseSet set, int
                     r[j] = reinterpret_cast<const u32x4 *>(x + (int64_t)b * ldx)[c0 + (i - b * ncs)];
                 }
             }
-            if (i0 == 0) load_row_dbatch<U>(bufA, set, min(rowA, R - 1), c0, total > 0 ? ncs : 0, 0, lane);
+            if (i0 == 0) load_row_dbatch<U, EPI>(bufA, set, min(rowA, R - 1), c0, total > 0 ? ncs : 0, 0, lane);
 #pragma unroll
             for (int j = 0; j < kStage; ++j) {
                 const int i = i0 + j * kThreads + (int)threadIdx.x;
@@ -143,29 +168,29 @@ __global__ __launch_bounds__(kThreads) void dense_kernel(const DenseSet set, int
     }
     __syncthreads();
 
-    float acc[B];
+    float acc[B], gsave[B];
 #pragma unroll
-    for (int b = 0; b < B; ++b) acc[b] = 0.f;
+    for (int b = 0; b < B; ++b) acc[b] = gsave[b] = 0.f;
     for (int t = 0; t < total; t += 2) {
         rowB = rowA;
         biB = biA + 1;
         if (biB == nb) {
             biB = 0;
-            rowB += row_step;
+            rowB = next_row(rowB);
         }
-        load_row_dbatch<U>(bufB, set, min(rowB, R - 1), c0, t + 1 < total ? ncs : 0, biB * kWave * U, lane);
+        load_row_dbatch<U, EPI>(bufB, set, min(rowB, R - 1), c0, t + 1 < total ? ncs : 0, biB * kWave * U, lane);
         dot_dbatch<B, U>(bufA, xs4, ncs, acc);
-        if (biA == nb - 1) finish_drow<B>(acc, set, rowA, s, R, lane, partial);
+        if (biA == nb - 1) finish_drow<B, EPI>(acc, gsave, set, rowA, s, R, lane, partial);
         if (t + 1 >= total) break;
         rowA = rowB;
         biA = biB + 1;
         if (biA == nb) {
             biA = 0;
-            rowA += row_step;
+            rowA = next_row(rowA);
         }
-        load_row_dbatch<U>(bufA, set, min(rowA, R - 1), c0, t + 2 < total ? ncs : 0, biA * kWave * U, lane);
+        load_row_dbatch<U, EPI>(bufA, set, min(rowA, R - 1), c0, t + 2 < total ? ncs : 0, biA * kWave * U, lane);
         dot_dbatch<B, U>(bufB, xs4, ncs, acc);
-        if (biB == nb - 1) finish_drow<B>(acc, set, rowB, s, R, lane, partial);
+        if (biB == nb - 1) finish_drow<B, EPI>(acc, gsave, set, rowB, s, R, lane, partial);
     }
 }
 
@@ -186,7 +211,24 @@ __global__ __launch_bounds__(256) void dense_finish_kernel(const float *__restri
     }
 }
 
-template <int B, int U>
+template <int B>
+__global__ __launch_bounds__(256) void dense_finish_swiglu_kernel(const float *__restrict__ partial, int S,
+                                                                  const DenseSet set) {
+    const int R2 = set.row0[set.P];
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= R2 / 2) return;
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+        float g = 0.f, u = 0.f;
+        for (int s = 0; s < S; ++s) {
+            g += partial[((int64_t)s * B + b) * R2 + 2 * i];
+            u += partial[((int64_t)s * B + b) * R2 + 2 * i + 1];
+        }
+        set.y[0][(int64_t)b * set.ldy[0] + i] = f32_to_bf16_rne(silu_mul(g, u));
+    }
+}
+
+template <int B, int U, int EPI>
 hipError_t allow_lds(size_t bytes) {
     static std::atomic<uint64_t> done{0};
     if (bytes <= 64 * 1024) return hipSuccess;
@@ -195,33 +237,53 @@ hipError_t allow_lds(size_t bytes) {
     if (e != hipSuccess) return e;
     const uint64_t bit = 1ull << (dev & 63);
     if (done.load(std::memory_order_acquire) & bit) return hipSuccess;
-    e = hipFuncSetAttribute((const void *)dense_kernel<B, U>, hipFuncAttributeMaxDynamicSharedMemorySize,
+    e = hipFuncSetAttribute((const void *)dense_kernel<B, U, EPI>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)kLdsCap);
     if (e == hipSuccess) done.fetch_or(bit, std::memory_order_acq_rel);
     return e;
 }
 
-template <int B, int U>
+template <int B, int U, int EPI>
 hipError_t launch_bu(const MvPlan &p, const DenseSet &set, int64_t K, const uint16_t *x, int64_t ldx, float *ws,
                      hipStream_t st) {
-    hipError_t e = allow_lds<B, U>(p.lds_bytes);
+    hipError_t e = allow_lds<B, U, EPI>(p.lds_bytes);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((dense_kernel<B, U>), dim3(p.grid_x, p.splits), dim3(kThreads), p.lds_bytes, st, set,
+    hipLaunchKernelGGL((dense_kernel<B, U, EPI>), dim3(p.grid_x, p.splits), dim3(kThreads), p.lds_bytes, st, set,
                        (int)(K / 8), x, ldx, ws, p.slice);
     e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;
     const int R = set.row0[set.P];
-    hipLaunchKernelGGL(dense_finish_kernel<B>, dim3((unsigned)((R + 255) / 256)), dim3(256), 0, st, ws, p.splits,
-                       set);
+    if constexpr (EPI == kEpiSwiGLU)
+        hipLaunchKernelGGL(dense_finish_swiglu_kernel<B>, dim3((unsigned)((R / 2 + 255) / 256)), dim3(256), 0, st,
+                           ws, p.splits, set);
+    else
+        hipLaunchKernelGGL(dense_finish_kernel<B>, dim3((unsigned)((R + 255) / 256)), dim3(256), 0, st, ws,
+                           p.splits, set);
     return hipGetLastError();
 }
 
-template <int B>
+template <int B, int EPI>
 hipError_t launch_b(const MvPlan &p, const DenseSet &set, int64_t K, const uint16_t *x, int64_t ldx, float *ws,
                     hipStream_t st) {
-    if (p.unroll >= 4) return launch_bu<B, 4>(p, set, K, x, ldx, ws, st);
-    if (p.unroll == 2) return launch_bu<B, 2>(p, set, K, x, ldx, ws, st);
-    return launch_bu<B, 1>(p, set, K, x, ldx, ws, st);
+    if (p.unroll >= 4) return launch_bu<B, 4, EPI>(p, set, K, x, ldx, ws, st);
+    if (p.unroll == 2) return launch_bu<B, 2, EPI>(p, set, K, x, ldx, ws, st);
+    return launch_bu<B, 1, EPI>(p, set, K, x, ldx, ws, st);
+}
+
+template <int EPI>
+hipError_t launch_e(const MvPlan &p, const DenseSet &set, int64_t K, const uint16_t *x, int64_t ldx, int B,
+                    float *ws, hipStream_t st) {
+    switch (B) {
+    case 1: return launch_b<1, EPI>(p, set, K, x, ldx, ws, st);
+    case 2: return launch_b<2, EPI>(p, set, K, x, ldx, ws, st);
+    case 3: return launch_b<3, EPI>(p, set, K, x, ldx, ws, st);
+    case 4: return launch_b<4, EPI>(p, set, K, x, ldx, ws, st);
+    case 5: return launch_b<5, EPI>(p, set, K, x, ldx, ws, st);
+    case 6: return launch_b<6, EPI>(p, set, K, x, ldx, ws, st);
+    case 7: return launch_b<7, EPI>(p, set, K, x, ldx, ws, st);
+    case 8: return launch_b<8, EPI>(p, set, K, x, ldx, ws, st);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
@@ -269,17 +331,13 @@ MvPlan plan_dense(int64_t R, int64_t K, int B, const DeviceInfo &dev) {
 
 hipError_t launch_dense(const MvPlan &p, const DenseSet &set, int64_t K, const uint16_t *x, int64_t ldx, int B,
                         float *ws, hipStream_t st) {
-    switch (B) {
-    case 1: return launch_b<1>(p, set, K, x, ldx, ws, st);
-    case 2: return launch_b<2>(p, set, K, x, ldx, ws, st);
-    case 3: return launch_b<3>(p, set, K, x, ldx, ws, st);
-    case 4: return launch_b<4>(p, set, K, x, ldx, ws, st);
-    case 5: return launch_b<5>(p, set, K, x, ldx, ws, st);
-    case 6: return launch_b<6>(p, set, K, x, ldx, ws, st);
-    case 7: return launch_b<7>(p, set, K, x, ldx, ws, st);
-    case 8: return launch_b<8>(p, set, K, x, ldx, ws, st);
-    default: return hipErrorInvalidValue;
-    }
+    return launch_e<kEpiNone>(p, set, K, x, ldx, B, ws, st);
+}
+
+hipError_t launch_dense_swiglu(const MvPlan &p, const DenseSet &set, int64_t K, const uint16_t *x, int64_t ldx, int B,
+                               float *ws, hipStream_t st) {
+    if (set.P != 2 || set.row0[2] != 2 * set.row0[1]) return hipErrorInvalidValue;
+    return launch_e<kEpiSwiGLU>(p, set, K, x, ldx, B, ws, st);
 }
 
 }  // namespace nmk

@@ -70,7 +70,13 @@ hipError_t launch_meta_from_mask(const uint32_t *masks, int64_t R, int64_t K, in
 // R of the plan = total rows of the set (set.row0[set.P]).
 hipError_t launch_spmv(const MvPlan &p, const SpmvSet &set, int fmt, int64_t K, const uint16_t *x, int64_t ldx,
                        int B, float *ws, hipStream_t st);
+// Gated MLP: set = {gate, up}, R rows each (row0 = {0, R, 2R}); y[0] receives
+// silu(gate x) * (up x).  Plan for 2R rows.
+hipError_t launch_spmv_swiglu(const MvPlan &p, const SpmvSet &set, int64_t K, const uint16_t *x, int64_t ldx, int B,
+                              float *ws, hipStream_t st);
 hipError_t launch_dense(const MvPlan &p, const DenseSet &set, int64_t K, const uint16_t *x, int64_t ldx, int B,
                         float *ws, hipStream_t st);
+hipError_t launch_dense_swiglu(const MvPlan &p, const DenseSet &set, int64_t K, const uint16_t *x, int64_t ldx, int B,
+                               float *ws, hipStream_t st);
 
 }  // namespace nmk

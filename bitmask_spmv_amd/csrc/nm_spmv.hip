@@ -226,35 +226,54 @@ __device__ __forceinline__ int owner(const SpmvSet &set, int r) {
     return p;
 }
 
-// Row finished: wave reduction, then either the bf16 result or this slice's fp32 partial.
-template <int B>
-__device__ __forceinline__ void finish_row(float (&acc)[B], const SpmvSet &set, int row, int s, int R, int lane,
-                                           float *partial) {
-    const int p = owner(set, row);
+// Matrix and row within it of launch row r.
+template <int EPI>
+__device__ __forceinline__ void locate(const SpmvSet &set, int r, int &p, int &local) {
+    if constexpr (EPI == kEpiSwiGLU) {
+        p = r & 1;
+        local = r >> 1;
+    } else {
+        p = owner(set, r);
+        local = r - set.row0[p];
+    }
+}
+
+// Row finished: wave reduction, then the bf16 result (or, for the gated MLP, the gate
+// total kept in gsave until its up row finishes), or this slice's fp32 partial.
+template <int B, int EPI>
+__device__ __forceinline__ void finish_row(float (&acc)[B], float (&gsave)[B], const SpmvSet &set, int row, int s,
+                                           int R, int lane, float *partial) {
+    int p, local;
+    locate<EPI>(set, row, p, local);
 #pragma unroll
     for (int b = 0; b < B; ++b) {
         const float tot = wave_sum(acc[b]);
         acc[b] = 0.f;
-        if (lane == 0) {
-            if (gridDim.y == 1)
-                set.y[p][(int64_t)b * set.ldy[p] + (row - set.row0[p])] = f32_to_bf16_rne(tot);
-            else
-                partial[((int64_t)s * B + b) * R + row] = tot;
+        if (gridDim.y != 1) {
+            if (lane == 0) partial[((int64_t)s * B + b) * R + row] = tot;
+        } else if constexpr (EPI == kEpiSwiGLU) {
+            if (p == 0)
+                gsave[b] = tot;
+            else if (lane == 0)
+                set.y[0][(int64_t)b * set.ldy[0] + local] = f32_to_bf16_rne(silu_mul(gsave[b], tot));
+        } else if (lane == 0) {
+            set.y[p][(int64_t)b * set.ldy[p] + local] = f32_to_bf16_rne(tot);
         }
     }
 }
 
-// Batch loads of global row r, word offset `base` within the slice.
-template <int FMT>
+// Batch loads of launch row r, word offset `base` within the slice.
+template <int FMT, int EPI>
 __device__ __forceinline__ void load_row_batch(Batch<FMT> &bt, const SpmvSet &set, int r, int KW, int w0, int words,
                                                int base, int lane) {
-    const int p = owner(set, r);
-    const int64_t off = (int64_t)(r - set.row0[p]) * KW + w0;  // in words
+    int p, local;
+    locate<EPI>(set, r, p, local);
+    const int64_t off = (int64_t)local * KW + w0;  // in words
     load_batch<FMT>(bt, reinterpret_cast<const uint8_t *>(set.meta[p]) + off * meta_bytes(FMT),
                     reinterpret_cast<const u32x4 *>(set.values[p]) + off * 2, words, base, lane);
 }
 
-template <int FMT, int B, int NT>
+template <int FMT, int B, int NT, int EPI>
 __global__ __launch_bounds__(NT) void spmv_kernel(const SpmvSet set, int KW, const uint16_t *__restrict__ x,
                                                   int64_t ldx, float *__restrict__ partial, int slice) {
     const int R = set.row0[set.P];
@@ -268,14 +287,21 @@ __global__ __launch_bounds__(NT) void spmv_kernel(const SpmvSet set, int KW, con
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     constexpr int kWaves = NT / kWave;
 
-    // This wave's rows: first_row, first_row + row_step, ...; each row slice is cut into
-    // nb strips of 64 words, walked as one flat sequence so the next strip's loads are in
-    // flight while the current one is computed, across row boundaries too.
-    const int first_row = blockIdx.x * kWaves + wave;
+    // This wave's rows: first_row, first_row + row_step, ... (gated MLP: the row pairs
+    // 2i, 2i+1 for i = first pair, first pair + pair step, ...); each row slice is cut
+    // into nb strips of 64 words, walked as one flat sequence so the next strip's loads
+    // are in flight while the current one is computed, across row boundaries too.
+    const int unit = blockIdx.x * kWaves + wave;
     const int row_step = gridDim.x * kWaves;
+    const int first_row = EPI == kEpiSwiGLU ? 2 * unit : unit;
+    const int units = EPI == kEpiSwiGLU ? R / 2 : R;
+    const int my_rows = (unit < units ? (units - 1 - unit) / row_step + 1 : 0) * (EPI == kEpiSwiGLU ? 2 : 1);
     const int nb = (nws + kWave - 1) / kWave;
-    const int my_rows = first_row < R ? (R - 1 - first_row) / row_step + 1 : 0;
     const int total = my_rows * nb;
+    auto next_row = [&](int r) {
+        if constexpr (EPI == kEpiSwiGLU) return (r & 1) ? r - 1 + 2 * row_step : r + 1;
+        return r + row_step;
+    };
 
     // Two batch buffers used in turn (no register copies, so the wait for one batch
     // never covers the loads of the other).
@@ -295,7 +321,7 @@ __global__ __launch_bounds__(NT) void spmv_kernel(const SpmvSet set, int KW, con
                 const int i = i0 + j * NT + (int)threadIdx.x;
                 if (i < chunks) r[j] = reinterpret_cast<const u32x4 *>(x + (int64_t)w0 * 32)[i];
             }
-            if (i0 == 0) load_row_batch<FMT>(bufA, set, min(rowA, R - 1), KW, w0, total > 0 ? nws : 0, 0, lane);
+            if (i0 == 0) load_row_batch<FMT, EPI>(bufA, set, min(rowA, R - 1), KW, w0, total > 0 ? nws : 0, 0, lane);
 #pragma unroll
             for (int j = 0; j < kStage; ++j) {
                 const int i = i0 + j * NT + (int)threadIdx.x;
@@ -324,7 +350,7 @@ __global__ __launch_bounds__(NT) void spmv_kernel(const SpmvSet set, int KW, con
                 for (int b = 0; b < S; ++b) r[j][b] = (b < B && i < pairs) ? x32[(int64_t)b * (ldx / 2) + i] : 0u;
             }
             if (i0 == 0)
-                load_row_batch<FMT>(bufA, set, min(rowA, R - 1), KW, w0, total > 0 ? nws : 0, 0, lane);
+                load_row_batch<FMT, EPI>(bufA, set, min(rowA, R - 1), KW, w0, total > 0 ? nws : 0, 0, lane);
 #pragma unroll
             for (int j = 0; j < kStage; ++j) {
                 const int i = i0 + j * NT + (int)threadIdx.x;
@@ -351,31 +377,31 @@ __global__ __launch_bounds__(NT) void spmv_kernel(const SpmvSet set, int KW, con
     }
     __syncthreads();
 
-    float acc[B];
+    float acc[B], gsave[B];
 #pragma unroll
-    for (int b = 0; b < B; ++b) acc[b] = 0.f;
+    for (int b = 0; b < B; ++b) acc[b] = gsave[b] = 0.f;
     for (int t = 0; t < total; t += 2) {
         // B <- batch t+1, walk A (batch t)
         rowB = rowA;
         biB = biA + 1;
         if (biB == nb) {
             biB = 0;
-            rowB += row_step;
+            rowB = next_row(rowB);
         }
-        load_row_batch<FMT>(bufB, set, min(rowB, R - 1), KW, w0, t + 1 < total ? nws : 0, biB * kWave, lane);
+        load_row_batch<FMT, EPI>(bufB, set, min(rowB, R - 1), KW, w0, t + 1 < total ? nws : 0, biB * kWave, lane);
         walk_batch<FMT, B>(bufA, xs, nws, acc);
-        if (biA == nb - 1) finish_row<B>(acc, set, rowA, s, R, lane, partial);
+        if (biA == nb - 1) finish_row<B, EPI>(acc, gsave, set, rowA, s, R, lane, partial);
         if (t + 1 >= total) break;
         // A <- batch t+2, walk B (batch t+1)
         rowA = rowB;
         biA = biB + 1;
         if (biA == nb) {
             biA = 0;
-            rowA += row_step;
+            rowA = next_row(rowA);
         }
-        load_row_batch<FMT>(bufA, set, min(rowA, R - 1), KW, w0, t + 2 < total ? nws : 0, biA * kWave, lane);
+        load_row_batch<FMT, EPI>(bufA, set, min(rowA, R - 1), KW, w0, t + 2 < total ? nws : 0, biA * kWave, lane);
         walk_batch<FMT, B>(bufB, xs, nws, acc);
-        if (biB == nb - 1) finish_row<B>(acc, set, rowB, s, R, lane, partial);
+        if (biB == nb - 1) finish_row<B, EPI>(acc, gsave, set, rowB, s, R, lane, partial);
     }
 }
 
@@ -397,8 +423,26 @@ __global__ __launch_bounds__(256) void split_finish_kernel(const float *__restri
     }
 }
 
+// The same for the gated MLP: gate and up totals of row i (launch rows 2i, 2i+1).
+template <int B>
+__global__ __launch_bounds__(256) void split_finish_swiglu_kernel(const float *__restrict__ partial, int S,
+                                                                  const SpmvSet set) {
+    const int R2 = set.row0[set.P];
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= R2 / 2) return;
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+        float g = 0.f, u = 0.f;
+        for (int s = 0; s < S; ++s) {
+            g += partial[((int64_t)s * B + b) * R2 + 2 * i];
+            u += partial[((int64_t)s * B + b) * R2 + 2 * i + 1];
+        }
+        set.y[0][(int64_t)b * set.ldy[0] + i] = f32_to_bf16_rne(silu_mul(g, u));
+    }
+}
+
 // Raise the dynamic-LDS limit of one kernel instance once per device.
-template <int FMT, int B, int NT>
+template <int FMT, int B, int NT, int EPI>
 hipError_t allow_lds(size_t bytes) {
     static std::atomic<uint64_t> done{0};
     if (bytes <= 64 * 1024) return hipSuccess;
@@ -407,46 +451,50 @@ hipError_t allow_lds(size_t bytes) {
     if (e != hipSuccess) return e;
     const uint64_t bit = 1ull << (dev & 63);
     if (done.load(std::memory_order_acquire) & bit) return hipSuccess;
-    e = hipFuncSetAttribute((const void *)spmv_kernel<FMT, B, NT>, hipFuncAttributeMaxDynamicSharedMemorySize,
+    e = hipFuncSetAttribute((const void *)spmv_kernel<FMT, B, NT, EPI>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)kLdsCap);
     if (e == hipSuccess) done.fetch_or(bit, std::memory_order_acq_rel);
     return e;
 }
 
-template <int FMT, int B, int NT>
+template <int FMT, int B, int NT, int EPI>
 hipError_t launch_fbn(const MvPlan &p, const SpmvSet &set, int64_t K, const uint16_t *x, int64_t ldx, float *ws,
                       hipStream_t st) {
-    hipError_t e = allow_lds<FMT, B, NT>(p.lds_bytes);
+    hipError_t e = allow_lds<FMT, B, NT, EPI>(p.lds_bytes);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((spmv_kernel<FMT, B, NT>), dim3(p.grid_x, p.splits), dim3(NT), p.lds_bytes, st, set,
+    hipLaunchKernelGGL((spmv_kernel<FMT, B, NT, EPI>), dim3(p.grid_x, p.splits), dim3(NT), p.lds_bytes, st, set,
                        (int)(K / 32), x, ldx, ws, p.slice);
     e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;
     const int R = set.row0[set.P];
-    hipLaunchKernelGGL(split_finish_kernel<B>, dim3((unsigned)((R + 255) / 256)), dim3(256), 0, st, ws, p.splits,
-                       set);
+    if constexpr (EPI == kEpiSwiGLU)
+        hipLaunchKernelGGL(split_finish_swiglu_kernel<B>, dim3((unsigned)((R / 2 + 255) / 256)), dim3(256), 0, st,
+                           ws, p.splits, set);
+    else
+        hipLaunchKernelGGL(split_finish_kernel<B>, dim3((unsigned)((R + 255) / 256)), dim3(256), 0, st, ws,
+                           p.splits, set);
     return hipGetLastError();
 }
 
-template <int FMT, int B>
+template <int FMT, int B, int EPI>
 hipError_t launch_fb(const MvPlan &p, const SpmvSet &set, int64_t K, const uint16_t *x, int64_t ldx, float *ws,
                      hipStream_t st) {
-    if (p.threads == 256) return launch_fbn<FMT, B, 256>(p, set, K, x, ldx, ws, st);
-    return launch_fbn<FMT, B, 512>(p, set, K, x, ldx, ws, st);
+    if (p.threads == 256) return launch_fbn<FMT, B, 256, EPI>(p, set, K, x, ldx, ws, st);
+    return launch_fbn<FMT, B, 512, EPI>(p, set, K, x, ldx, ws, st);
 }
 
-template <int FMT>
+template <int FMT, int EPI>
 hipError_t launch_f(const MvPlan &p, const SpmvSet &set, int64_t K, const uint16_t *x, int64_t ldx, int B, float *ws,
                     hipStream_t st) {
     switch (B) {
-    case 1: return launch_fb<FMT, 1>(p, set, K, x, ldx, ws, st);
-    case 2: return launch_fb<FMT, 2>(p, set, K, x, ldx, ws, st);
-    case 3: return launch_fb<FMT, 3>(p, set, K, x, ldx, ws, st);
-    case 4: return launch_fb<FMT, 4>(p, set, K, x, ldx, ws, st);
-    case 5: return launch_fb<FMT, 5>(p, set, K, x, ldx, ws, st);
-    case 6: return launch_fb<FMT, 6>(p, set, K, x, ldx, ws, st);
-    case 7: return launch_fb<FMT, 7>(p, set, K, x, ldx, ws, st);
-    case 8: return launch_fb<FMT, 8>(p, set, K, x, ldx, ws, st);
+    case 1: return launch_fb<FMT, 1, EPI>(p, set, K, x, ldx, ws, st);
+    case 2: return launch_fb<FMT, 2, EPI>(p, set, K, x, ldx, ws, st);
+    case 3: return launch_fb<FMT, 3, EPI>(p, set, K, x, ldx, ws, st);
+    case 4: return launch_fb<FMT, 4, EPI>(p, set, K, x, ldx, ws, st);
+    case 5: return launch_fb<FMT, 5, EPI>(p, set, K, x, ldx, ws, st);
+    case 6: return launch_fb<FMT, 6, EPI>(p, set, K, x, ldx, ws, st);
+    case 7: return launch_fb<FMT, 7, EPI>(p, set, K, x, ldx, ws, st);
+    case 8: return launch_fb<FMT, 8, EPI>(p, set, K, x, ldx, ws, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -503,11 +551,17 @@ MvPlan plan_spmv(int64_t R, int64_t K, int B, const DeviceInfo &dev) {
 hipError_t launch_spmv(const MvPlan &p, const SpmvSet &set, int fmt, int64_t K, const uint16_t *x, int64_t ldx, int B,
                        float *ws, hipStream_t st) {
     switch (fmt) {
-    case kMetaBitmask: return launch_f<kMetaBitmask>(p, set, K, x, ldx, B, ws, st);
-    case kMetaU8: return launch_f<kMetaU8>(p, set, K, x, ldx, B, ws, st);
-    case kMetaI32: return launch_f<kMetaI32>(p, set, K, x, ldx, B, ws, st);
+    case kMetaBitmask: return launch_f<kMetaBitmask, kEpiNone>(p, set, K, x, ldx, B, ws, st);
+    case kMetaU8: return launch_f<kMetaU8, kEpiNone>(p, set, K, x, ldx, B, ws, st);
+    case kMetaI32: return launch_f<kMetaI32, kEpiNone>(p, set, K, x, ldx, B, ws, st);
     default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_spmv_swiglu(const MvPlan &p, const SpmvSet &set, int64_t K, const uint16_t *x, int64_t ldx, int B,
+                              float *ws, hipStream_t st) {
+    if (set.P != 2 || set.row0[2] != 2 * set.row0[1]) return hipErrorInvalidValue;
+    return launch_f<kMetaBitmask, kEpiSwiGLU>(p, set, K, x, ldx, B, ws, st);
 }
 
 }  // namespace nmk

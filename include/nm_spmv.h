@@ -155,6 +155,31 @@ size_t nm_spmv_multi_workspace_bytes(const nm_spmv_matrix *mats, int P, int64_t 
 nm_status nm_spmv_multi(const nm_spmv_matrix *mats, int P, int64_t K, const nm_bf16 *x, int64_t ldx, int B,
                         void *workspace, size_t workspace_bytes, void *hip_stream);
 
+/*
+ * nm_spmv_swiglu -- the gate and up projections of a gated (SwiGLU) MLP block in one
+ * launch, with the activation fused into the epilogue:
+ *     h[b][i] = silu(g) * u,  g = sum_j Wgate[i][j] x[b][j],  u = sum_j Wup[i][j] x[b][j],
+ *     silu(g) = g / (1 + exp(-g)),
+ * for 0 <= i < R.  The models the pages evaluate (Llama-3.1-8B, Llama-3.3-70B, Qwen3)
+ * use this block; each projection is one pruned linear of the decode step [SD-cn,
+ * 方法步骤详情 第四步].  g and u are the fp32 row totals of the same walk as nm_spmv
+ * (never rounded to bf16); silu and the product are fp32, h is rounded once to bf16.
+ * Both packed matrices are R x K in the canonical layout; x: bf16 [B][ldx]; h: bf16
+ * [B][ldh].  Workspace: nm_spmv_swiglu_workspace_bytes(R, K, B).  Requires R <= 2^29 and
+ * the nm_spmv conditions otherwise.
+ */
+size_t nm_spmv_swiglu_workspace_bytes(int64_t R, int64_t K, int B);
+nm_status nm_spmv_swiglu(const uint32_t *gate_masks, const nm_bf16 *gate_values, const uint32_t *up_masks,
+                         const nm_bf16 *up_values, int64_t R, int64_t K, const nm_bf16 *x, int64_t ldx, int B,
+                         nm_bf16 *h, int64_t ldh, void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* dense_gemv_swiglu -- the dense baseline of nm_spmv_swiglu: unpruned bf16 gate and up
+ * matrices W_gate, W_up [R][ldw], same epilogue and conventions. */
+size_t dense_gemv_swiglu_workspace_bytes(int64_t R, int64_t K, int B);
+nm_status dense_gemv_swiglu(const nm_bf16 *W_gate, const nm_bf16 *W_up, int64_t ldw, int64_t R, int64_t K,
+                            const nm_bf16 *x, int64_t ldx, int B, nm_bf16 *h, int64_t ldh, void *workspace,
+                            size_t workspace_bytes, void *hip_stream);
+
 /* dense_gemv_multi -- the dense baseline for the same grouping (same conventions). */
 typedef struct {
     const nm_bf16 *W;  /* [R][ldw] */

@@ -25,6 +25,11 @@ list and the passages each follows:
                     ("SparseDecoding: Decoding-Aware Pruning ...", Main Findings;
                     "SparseDecoding:解码感知的准确高效大模型剪枝框架", 核心方法 核心创新二)
 
+* ``swiglu`` / ``swiglu_tolerance`` -- h = silu(g) * u, silu(g) = g / (1 + exp(-g)), on
+                    fp64 gate and up products (the gated MLP of the models the pages
+                    evaluate: Llama-3.1-8B, Llama-3.3-70B, Qwen3), and the error bound a
+                    result inherits from the matvec tolerance of g and u
+
 Pins (tests that tie the oracle to something other than itself) live in
 ``tests/test_oracle_pins.py``; every function above has at least one.
 """
@@ -201,6 +206,32 @@ def spmv_index(meta, fmt: int, values, x, K: int, nthreads: int = 1):
     _check(_load().nmo_spmv_index(_ptr(meta), int(fmt), _ptr(values), R, K, _ptr(x), K, B, _ptr(y), _ptr(a),
                                   int(nthreads)), "spmv_index")
     return y, a
+
+
+def swiglu(g, u) -> np.ndarray:
+    """fp64 h = silu(g) * u with silu(g) = g / (1 + exp(-g))."""
+    g = np.asarray(g, dtype=np.float64)
+    u = np.asarray(u, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g)) * u
+
+
+SILU_SLOPE_BOUND = 1.1  # sup |d silu / dg| = 1.0998... (pinned in the tests)
+
+
+def swiglu_tolerance(g, ag, u, au, rel: float = 1e-2, abs_frac: float = 1e-3) -> np.ndarray:
+    """Bound on |h_test - h_ref| when g and u each meet the matvec tolerance
+    e = rel*|ref| + abs_frac*sum|products| and h is rounded once to bf16:
+    |silu(g')u' - silu(g)u| <= L*eg*(|u| + eu) + |silu(g)|*eu, L = SILU_SLOPE_BOUND,
+    plus half-ulp-of-bf16 relative rounding (2^-8) on top of the result's magnitude."""
+    g = np.asarray(g, dtype=np.float64)
+    u = np.asarray(u, dtype=np.float64)
+    eg = rel * np.abs(g) + abs_frac * np.asarray(ag, dtype=np.float64)
+    eu = rel * np.abs(u) + abs_frac * np.asarray(au, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        sg = np.abs(g / (1.0 + np.exp(-g)))
+    pre = SILU_SLOPE_BOUND * eg * (np.abs(u) + eu) + sg * eu
+    return pre + 2.0 ** -8 * (sg * np.abs(u) + pre) + 1e-30
 
 
 def within_tolerance(y_test, y_ref, absum, rel: float = 1e-2, abs_frac: float = 1e-3) -> np.ndarray:

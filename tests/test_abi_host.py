@@ -50,7 +50,8 @@ def test_header_declares_the_expected_entry_points():
     for n in ("nm_col_norm", "nm_prune_pack", "nm_spmv", "nm_spmv_workspace_bytes", "dense_gemv",
               "dense_gemv_workspace_bytes", "nm_unpack", "nm_status_str", "nm_last_error", "nm_version",
               "nm_spmv_multi", "nm_spmv_multi_workspace_bytes", "dense_gemv_multi",
-              "dense_gemv_multi_workspace_bytes", "nm_meta_from_mask", "nm_spmv_meta"):
+              "dense_gemv_multi_workspace_bytes", "nm_meta_from_mask", "nm_spmv_meta", "nm_spmv_swiglu",
+              "nm_spmv_swiglu_workspace_bytes", "dense_gemv_swiglu", "dense_gemv_swiglu_workspace_bytes"):
         assert n in names
 
 
@@ -184,3 +185,23 @@ def test_metadata_entry_points_reject_bad_arguments(L):
     assert L.nm_spmv_meta(A4, 2, A16, 4, 64, A16, 64, 1, A16, 4, None, 0, None) == NM_ERR_ALIGN  # i32 meta
     assert L.nm_spmv_meta(A2, 0, A16, 4, 64, A16, 64, 1, A16, 4, None, 0, None) == NM_ERR_ALIGN  # masks
     assert L.nm_spmv_meta(A16, 1, A4, 4, 64, A16, 64, 1, A16, 4, None, 0, None) == NM_ERR_ALIGN  # values
+
+
+def test_swiglu_entry_points_reject_bad_arguments(L):
+    p, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    L.nm_spmv_swiglu.argtypes = [p, p, p, p, i64, i64, p, i64, i32, p, i64, p, sz, p]
+    L.dense_gemv_swiglu.argtypes = [p, p, i64, i64, i64, p, i64, i32, p, i64, p, sz, p]
+    L.nm_spmv_swiglu_workspace_bytes.argtypes = [i64, i64, i32]
+    L.nm_spmv_swiglu_workspace_bytes.restype = sz
+    assert L.nm_spmv_swiglu(A4, A16, None, A16, 4, 64, A16, 64, 1, A16, 4, None, 0, None) == NM_ERR_NULL
+    assert L.nm_spmv_swiglu(A4, A16, A4, A16, 4, 48, A16, 64, 1, A16, 4, None, 0, None) == NM_ERR_SHAPE
+    assert L.nm_spmv_swiglu(A4, A16, A4, A16, 1 << 29 + 1, 64, A16, 64, 1, A16, 1 << 30, None, 0, None) \
+        == NM_ERR_SHAPE
+    assert L.nm_spmv_swiglu(A4, A16, A4, A16, 4, 64, A16, 64, 0, A16, 4, None, 0, None) == NM_ERR_SHAPE
+    assert L.nm_spmv_swiglu(A4, A16, A4, A4, 4, 64, A16, 64, 1, A16, 4, None, 0, None) == NM_ERR_ALIGN
+    assert L.nm_spmv_swiglu(A4, A16, A2, A16, 4, 64, A16, 64, 1, A16, 4, None, 0, None) == NM_ERR_ALIGN
+    assert L.dense_gemv_swiglu(A16, None, 64, 4, 64, A16, 64, 1, A16, 4, None, 0, None) == NM_ERR_NULL
+    assert L.dense_gemv_swiglu(A16, A16, 60, 4, 64, A16, 64, 1, A16, 4, None, 0, None) == NM_ERR_SHAPE
+    assert L.dense_gemv_swiglu(A16, A4, 64, 4, 64, A16, 64, 1, A16, 4, None, 0, None) == NM_ERR_ALIGN
+    assert L.nm_spmv_swiglu_workspace_bytes(0, 64, 1) == 0
+    assert L.nm_spmv_swiglu_workspace_bytes(8, 8192, 1) % (4 * 16) == 0
