@@ -8,10 +8,16 @@ stack with dense_gemv on the unpruned weights.  Inputs are generated and packed 
 the GPU before the timed region (column norms -> N:M select + pack), spot-checked
 against the CPU oracle, and every timed launch reads weights already resident in HBM.
 
-Printed (one JSON line on stdout): aggregate effective GB/s of the sparse step
-(algorithmic bytes: packed values + masks + x + y per call), a per-projection table
-(us, GB/s, % of the 8 TB/s HBM peak, dense us, speedup, hipBLASLt us), the roofline
-of the dominant kernel and the CPU oracle timed on the host cores.
+The headline step runs the projections that read the same x as one launch each --
+q|k|v through nm_spmv_multi, gate|up through nm_spmv_swiglu (silu(g) * u written by the
+epilogue), o and down alone -- against the same grouping of dense launches; the step
+with one nm_spmv call per projection is reported beside it.
+
+Printed (one JSON line on stdout): effective GB/s of the step (algorithmic bytes:
+packed values + masks of every matrix, x once per launch, the launch's outputs), a
+per-projection and per-fused-launch table (us, GB/s, % of the 8 TB/s HBM peak, dense
+us, speedup, hipBLASLt us), the bitmask / uint8-offset / int32-index comparison, the
+roofline of the step's dominant launch and the CPU oracle timed on the host cores.
 
 Cache defeat: every per-projection timing rotates over >= 512 MB of distinct buffers
 (twice the 256 MB Infinity Cache), and the step itself walks all layers of all
@@ -80,6 +86,23 @@ def meta_format_bytes(fmt, R, K, B):
 
 def dense_bytes(R, K, B):
     return 2 * R * K + 2 * B * K + 2 * B * R
+
+
+def is_glu(grp):
+    return [pr[0] for pr in grp] == ["gate", "up"]
+
+
+def group_label(grp):
+    return "|".join(pr[0] for pr in grp) + ("+swiglu" if is_glu(grp) else "")
+
+
+def group_bytes(grp, B, dense):
+    """Algorithmic bytes of one fused launch: every matrix of the group once, x once, and
+    the outputs (one h of R rows for the gated MLP, else every matrix's y)."""
+    K = grp[0][2]
+    w = sum((2 if dense else 1.125) * R * K for _, R, _, _ in grp)
+    outs = grp[0][1] if is_glu(grp) else sum(R for _, R, _, _ in grp)
+    return int(w) + 2 * B * K + 2 * B * outs
 
 
 def parse():
@@ -293,6 +316,8 @@ def main():
         else:
             groups.append([proj])
     fused_fns, fused_dense_fns = [], []
+    fused_sparse_bytes = L * len(patterns) * sum(group_bytes(grp, B, False) for grp in groups)
+    fused_dense_bytes = L * sum(group_bytes(grp, B, True) for grp in groups)
     for (N, M) in patterns:
         for l in range(L):
             for grp in groups:
@@ -373,39 +398,51 @@ def main():
         del g, gl
     torch.cuda.synchronize()
 
-    # ---------------------------------------------------------------- gated MLP in one launch
-    # gate and up of one layer walked by one launch whose epilogue writes silu(g) * u.
-    names = [p[0] for p in projs]
-    if "gate" in names and "up" in names:
-        (_, R, K, group) = projs[names.index("gate")]
-        fb = 2 * (R * K + R * K // 8) + 2 * B * K + 2 * B * R  # both packed matrices, x once, h
-        fdb = 4 * R * K + 2 * B * K + 2 * B * R
-        d = per.setdefault("gate|up+swiglu", {"R": R, "K": K})
+    # ---------------------------------------------------------------- fused launches
+    # Every group of projections that read the same x as one launch (q|k|v through
+    # nm_spmv_multi, gate|up through nm_spmv_swiglu whose epilogue writes silu(g) * u),
+    # timed over >= 512 MB of distinct buffers like the table above.
+    def fused_call(grp, i, N=None, M=None):
+        x = xs[grp[0][3]][i % L]
+        if N is None:
+            Ws = [pool_dense[pr[0]][i % len(pool_dense[pr[0]])] for pr in grp]
+            if is_glu(grp):
+                return lambda: nm.dense_gemv_swiglu(Ws[0], Ws[1], x, out=ys["gate"], workspace=ws)
+            outs = [ys[pr[0]] for pr in grp]
+            return lambda: nm.dense_gemv_multi(Ws, x, outs=outs, workspace=ws)
+        pk = [pool_sparse[(N, M), pr[0]][i % len(pool_sparse[(N, M), pr[0]])] for pr in grp]
+        if is_glu(grp):
+            return lambda: nm.nm_spmv_swiglu(pk[0], pk[1], x, out=ys["gate"], workspace=ws)
+        outs = [ys[pr[0]] for pr in grp]
+        return lambda: nm.nm_spmv_multi(pk, x, outs=outs, workspace=ws)
+
+    for grp in groups:
+        if len(grp) == 1:
+            continue
+        label = group_label(grp)
+        fb, fdb = group_bytes(grp, B, False), group_bytes(grp, B, True)
+        d = per.setdefault(label, {"R": [pr[1] for pr in grp], "K": grp[0][2]})
         for (N, M) in patterns:
-            pg, pu = pool_sparse[(N, M), "gate"], pool_sparse[(N, M), "up"]
-            fns = [(lambda g=g, u=u, x=xs[group][i % L]: nm.nm_spmv_swiglu(g, u, x, out=ys["gate"], workspace=ws))
-                   for i, (g, u) in enumerate(zip(pg, pu))]
-            g = capture(torch, fns)
+            n_rot = min(len(pool_sparse[(N, M), pr[0]]) for pr in grp)
+            g = capture(torch, [fused_call(grp, i, N, M) for i in range(n_rot)])
             g.replay()
-            us = min(timer.time_graph(g, 1) for _ in range(reps)) * 1e3 / len(fns)
+            us = min(timer.time_graph(g, 1) for _ in range(reps)) * 1e3 / n_rot
             d[f"{N}:{M}"] = {"us": round(us, 2), "GBs": round(fb / us / 1e3, 1),
                              "pct_peak": round(100 * fb / us / 1e3 / HBM_PEAK_GBS, 1),
-                             "rotation_MB": round(len(fns) * fb / 1e6)}
+                             "rotation_MB": round(n_rot * fb / 1e6)}
             del g
-        pg, pu = pool_dense["gate"], pool_dense["up"]
-        fns = [(lambda a=a, b=b, x=xs[group][i % L]: nm.dense_gemv_swiglu(a, b, x, out=ys["gate"], workspace=ws))
-               for i, (a, b) in enumerate(zip(pg, pu))]
-        g = capture(torch, fns)
+        n_rot = min(len(pool_dense[pr[0]]) for pr in grp)
+        g = capture(torch, [fused_call(grp, i) for i in range(n_rot)])
         g.replay()
-        us = min(timer.time_graph(g, 1) for _ in range(reps)) * 1e3 / len(fns)
+        us = min(timer.time_graph(g, 1) for _ in range(reps)) * 1e3 / n_rot
         d["dense_us"] = round(us, 2)
         d["dense_GBs"] = round(fdb / us / 1e3, 1)
         for (N, M) in patterns:
             d[f"{N}:{M}"]["speedup_vs_dense"] = round(us / d[f"{N}:{M}"]["us"], 3)
         del g
         torch.cuda.synchronize()
-        log("gate|up+swiglu: " + ", ".join(f"{k} {v['us']} us ({v['pct_peak']}%)" for k, v in d.items()
-                                            if isinstance(v, dict)) + f"; dense {d['dense_us']} us")
+        log(f"{label}: " + ", ".join(f"{k} {v['us']} us ({v['pct_peak']}%)" for k, v in d.items()
+                                     if isinstance(v, dict)) + f"; dense {d['dense_us']} us")
 
     # ---------------------------------------------------------------- metadata formats
     # The same product over the first pattern's packs with the metadata as uint8 offsets
@@ -444,16 +481,16 @@ def main():
             f"{n} bitmask {d['bitmask']['us']} u8 {d['u8_offset']['us']} i32 {d['i32_index']['us']}"
             for n, d in meta_table.items()))
 
-    # Dominant kernel: the launch shape (R x K) whose launches take the largest share of
-    # the step (projections of equal shape, e.g. gate and up, are one launch shape).
+    # Dominant kernel: the launch of the (fused) step whose launches take the largest share
+    # of it; its algorithmic bytes over its average launch time is the roofline's achieved.
     share = {}
-    for name, R, K, _ in projs:
-        share[(R, K)] = share.get((R, K), 0.0) + sum(per[name][f"{N}:{M}"]["us"] for (N, M) in patterns)
-    dR, dK = max(share, key=share.get)
-    dom_names = [name for name, R, K, _ in projs if (R, K) == (dR, dK)]
-    dom = dom_names[0]
-    dom_us = sum(per[n][f"{N}:{M}"]["us"] for n in dom_names for (N, M) in patterns) / (len(dom_names) * len(patterns))
-    dom_bytes = sparse_bytes(dR, dK, B)
+    for grp in groups:
+        label = grp[0][0] if len(grp) == 1 else group_label(grp)
+        share[label] = sum(per[label][f"{N}:{M}"]["us"] for (N, M) in patterns)
+    dom = max(share, key=share.get)
+    dom_grp = next(grp for grp in groups if (grp[0][0] if len(grp) == 1 else group_label(grp)) == dom)
+    dom_us = share[dom] / len(patterns)
+    dom_bytes = group_bytes(dom_grp, B, False)
     achieved = dom_bytes / dom_us / 1e3  # GB/s
     traffic = None
     tf = os.path.join(ROOT, "profiles", "traffic.json")
@@ -466,9 +503,11 @@ def main():
                 traffic = tj[key]["bytes_per_launch"]
         except (OSError, ValueError, KeyError):
             traffic = None
+    dom_desc = (f"{'nm_spmv_swiglu' if is_glu(dom_grp) else ('nm_spmv_multi' if len(dom_grp) > 1 else 'nm_spmv')} "
+                f"on {dom} ({' + '.join(f'{pr[1]}x{pr[2]}' for pr in dom_grp)}), B={B}")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": f"nm_spmv on {'/'.join(dom_names)} {dR}x{dK}, B={B}", "algorithmic_bytes_per_launch": dom_bytes,
+                "kernel": dom_desc, "algorithmic_bytes_per_launch": dom_bytes,
                 "avg_launch_us": round(dom_us, 3)}
 
     # ---------------------------------------------------------------- CPU oracle baseline
@@ -494,7 +533,7 @@ def main():
                "sample": f"layer 0 of the set ({', '.join(p[0] for p in projs)}), {N}:{M}, B={B}, "
                          f"x{args.cpu_reps} reps, {dt:.1f}s wall"}
 
-    value = step_sparse_bytes / (ms_sparse * 1e-3) / 1e9
+    value = fused_sparse_bytes / (ms_fused * 1e-3) / 1e9
     out = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -502,7 +541,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_sparse, 4),
+        "ms_per_step": round(ms_fused, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -511,17 +550,16 @@ def main():
         "config": {"workload": cfg["workload"], "layers": L, "batch": B,
                    "patterns": [f"{N}:{M}" for N, M in patterns], "parallelism": "single GPU"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1),
-        "dense_ms_per_step": round(ms_dense, 4),
-        "dense_GBs": round(step_dense_bytes / (ms_dense * 1e-3) / 1e9, 1),
-        "step_speedup_vs_dense": round(ms_dense * len(patterns) / ms_sparse, 3),
-        "fused_step": {"launches": len(fused_fns), "ms": round(ms_fused, 4),
-                       "GBs": round(step_sparse_bytes / (ms_fused * 1e-3) / 1e9, 1),
-                       "pct_hbm_peak": round(100 * step_sparse_bytes / (ms_fused * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
-                       "dense_ms": round(ms_fused_dense, 4),
-                       "speedup_vs_dense": round(ms_fused_dense * len(patterns) / ms_fused, 3),
-                       "groups": ["|".join(pr[0] for pr in grp)
-                                  + ("+swiglu" if [pr[0] for pr in grp] == ["gate", "up"] else "")
-                                  for grp in groups]},
+        "step": {"launches": len(fused_fns), "groups": [group_label(grp) for grp in groups],
+                 "bytes": fused_sparse_bytes,
+                 "dense_ms": round(ms_fused_dense, 4),
+                 "dense_GBs": round(fused_dense_bytes / (ms_fused_dense * 1e-3) / 1e9, 1),
+                 "speedup_vs_dense": round(ms_fused_dense * len(patterns) / ms_fused, 3)},
+        "unfused_step": {"launches": len(sparse_fns), "ms": round(ms_sparse, 4), "bytes": step_sparse_bytes,
+                         "GBs": round(step_sparse_bytes / (ms_sparse * 1e-3) / 1e9, 1),
+                         "pct_hbm_peak": round(100 * step_sparse_bytes / (ms_sparse * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
+                         "dense_ms": round(ms_dense, 4),
+                         "speedup_vs_dense": round(ms_dense * len(patterns) / ms_sparse, 3)},
         "per_layer": per,
         "metadata_formats": meta_table,
         "pack_GBs": round(pack_bytes / pack_ms / 1e6, 1),
@@ -532,38 +570,54 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-DOMINANT = {"8b": ("gate", 14336, 4096), "tiny": ("w", 256, 512), "8b-sweep": ("gate", 14336, 4096),
-            "qwen14b": ("gate", 17408, 5120), "qwen32b": ("gate", 25600, 5120), "70b": ("gate", 28672, 8192)}
 COPY_BYTES = 256 << 20
 
 
 def profile_kernel(args, torch, nm, synth, cfg, dev):
-    """Eager launches of the dominant launch shape (first pattern), rotated over >= 512 MB,
-    then one plain device-to-device copy of COPY_BYTES: the reference for the counters."""
-    name, R, K = DOMINANT[args.config]
+    """Eager launches of the step's dominant launch (gate|up through nm_spmv_swiglu when the
+    layer set has them, else the largest single projection), first pattern, rotated over
+    >= 512 MB of distinct packed buffers, then one plain device-to-device copy of
+    COPY_BYTES: the reference for the counters."""
+    projs = cfg["projs"]
+    names = [p[0] for p in projs]
     N, M = cfg["patterns"][0]
     B = args.batch
-    n_pool = max(2, math.ceil(ROTATE_BYTES / sparse_bytes(R, K, B)))
+    glu = "gate" in names and "up" in names
+    if glu:
+        _, R, K, _ = projs[names.index("gate")]
+        label, mats = "gate|up+swiglu", 2
+    else:
+        _, R, K, _ = max(projs, key=lambda p: p[1] * p[2])
+        label, mats = max(projs, key=lambda p: p[1] * p[2])[0], 1
+    per_launch = mats * (R * K + R * K // 8)
+    n_pool = max(2, math.ceil(ROTATE_BYTES / per_launch))
     pool = []
     for c in range(n_pool):
-        W = synth.device_weights(R, K, args.seed, 400, c)
         n = nm.nm_col_norm(synth.device_calib_acts(K, args.seed, 401, c))
-        pool.append(nm.nm_prune_pack(W, n, N, M))
-        del W, n
+        packs = []
+        for m in range(mats):
+            W = synth.device_weights(R, K, args.seed, 400 + m, c)
+            packs.append(nm.nm_prune_pack(W, n, N, M))
+            del W
+        pool.append(packs)
     x = synth.device_decode_x(B, K, args.seed, 402)
     y = torch.empty((B, R), dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(max(1, nm.nm_spmv_workspace_bytes(R, K, B) // 4), dtype=torch.float32, device=dev)
+    wsb = nm.nm_spmv_swiglu_workspace_bytes(R, K, B) if glu else nm.nm_spmv_workspace_bytes(R, K, B)
+    ws = torch.empty(max(1, wsb // 4), dtype=torch.float32, device=dev)
     src = torch.empty(COPY_BYTES // 2, dtype=torch.int16, device=dev).random_()
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
     for i in range(args.steps):
-        m, v = pool[i % n_pool]
-        nm.nm_spmv(m, v, x, out=y, workspace=ws)
+        packs = pool[i % n_pool]
+        if glu:
+            nm.nm_spmv_swiglu(packs[0], packs[1], x, out=y, workspace=ws)
+        else:
+            nm.nm_spmv(*packs[0], x, out=y, workspace=ws)
     torch.cuda.synchronize()
     dst.copy_(src)
     torch.cuda.synchronize()
-    print(json.dumps({"profile_kernel": f"nm_spmv {name} {R}x{K} {N}:{M} B={B}", "launches": args.steps,
-                      "copy_bytes": COPY_BYTES}), flush=True)
+    print(json.dumps({"profile_kernel": f"{label} {mats}x {R}x{K} {N}:{M} B={B}", "label": label,
+                      "launches": args.steps, "copy_bytes": COPY_BYTES}), flush=True)
 
 
 def _pmc_rows(d):
@@ -585,7 +639,17 @@ def ingest_pmc(args, fetch_dir, write_dir):
     """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the dominant SpMV launches, scaled by
     what the same counters report for the plain copy of COPY_BYTES (which moves exactly
     COPY_BYTES each way).  Writes profiles/traffic.json."""
-    name, R, K = DOMINANT[args.config]
+    cfg = dict(CONFIGS[args.config])
+    if cfg.get("projs") is None:
+        cfg["projs"] = CONFIGS[cfg["base"]]["projs"]
+    names = [p[0] for p in cfg["projs"]]
+    if "gate" in names and "up" in names:
+        _, R, K, _ = cfg["projs"][names.index("gate")]
+        name, mats = "gate|up+swiglu", 2
+        grp = [p for p in cfg["projs"] if p[0] in ("gate", "up")]
+    else:
+        big = max(cfg["projs"], key=lambda p: p[1] * p[2])
+        name, R, K, mats, grp = big[0], big[1], big[2], 1, [big]
     out = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         per = _pmc_rows(d)
@@ -607,8 +671,8 @@ def ingest_pmc(args, fetch_dir, write_dir):
     if os.path.exists(path):
         with open(path) as f:
             data = json.load(f)
-    data[key] = {"kernel": f"nm_spmv {R}x{K}", "bytes_per_launch": round(total),
-                 "algorithmic_bytes": sparse_bytes(R, K, args.batch), "kernel_sha": kernel_fingerprint(),
+    data[key] = {"kernel": f"{name} {mats}x {R}x{K}", "bytes_per_launch": round(total),
+                 "algorithmic_bytes": group_bytes(grp, args.batch, False), "kernel_sha": kernel_fingerprint(),
                  "fetch": out["FETCH_SIZE"], "write": out["WRITE_SIZE"]}
     os.makedirs(os.path.dirname(path), exist_ok=True)
     with open(path, "w") as f:
