@@ -335,42 +335,43 @@ __global__ __launch_bounds__(NT) void spmv_kernel(const SpmvSet set, int KW, con
             }
         }
     } else {
-        // One column pair per thread and round: a dword (2 columns) of every token,
-        // transposed with byte permutes into the interleaved per-column layout.
+        // Eight columns per thread and round: one 16-byte load of every token, transposed
+        // with byte permutes into the interleaved per-column layout (the eight columns'
+        // 4*S dwords are contiguous in LDS: S 16-byte stores).
         constexpr int S = XLayout<B>::S;
-        constexpr int kStage = 2;
-        const int pairs = nws * 16;
-        const uint32_t *x32 = reinterpret_cast<const uint32_t *>(x) + (int64_t)w0 * 16;
-        for (int i0 = 0; i0 < pairs || i0 == 0; i0 += NT * kStage) {
-            uint32_t r[kStage][S];
+        constexpr int kStage = 8 / S;  // 8 x 16-byte loads in flight per thread and round
+        const int octs = nws * 4;
+        const uint16_t *xw = x + (int64_t)w0 * 32;
+        for (int i0 = 0; i0 < octs || i0 == 0; i0 += NT * kStage) {
+            u32x4 r[kStage][S];
 #pragma unroll
             for (int j = 0; j < kStage; ++j) {
                 const int i = i0 + j * NT + (int)threadIdx.x;
 #pragma unroll
-                for (int b = 0; b < S; ++b) r[j][b] = (b < B && i < pairs) ? x32[(int64_t)b * (ldx / 2) + i] : 0u;
+                for (int b = 0; b < S; ++b)
+                    r[j][b] = (b < B && i < octs) ? *reinterpret_cast<const u32x4 *>(xw + (int64_t)b * ldx + 8 * i)
+                                                  : u32x4{0u, 0u, 0u, 0u};
             }
             if (i0 == 0)
                 load_row_batch<FMT, EPI>(bufA, set, min(rowA, R - 1), KW, w0, total > 0 ? nws : 0, 0, lane);
 #pragma unroll
             for (int j = 0; j < kStage; ++j) {
                 const int i = i0 + j * NT + (int)threadIdx.x;
-                if (i < pairs) {
-                    const int c = 2 * i;  // first column of the pair, within the slice
-                    uint32_t *d = xs + (c >> 5) * XLayout<B>::kBlk + (c & 31) * (S / 2);
-                    uint32_t col[S];  // column c: S/2 dwords, then column c+1: S/2 dwords
+                if (i < octs) {
+                    const int c = 8 * i;  // first column of the eight, within the slice
+                    u32x4 *d = reinterpret_cast<u32x4 *>(xs + (c >> 5) * XLayout<B>::kBlk + (c & 31) * (S / 2));
+                    uint32_t col[4 * S];  // column c+k: dwords k*S/2 .. k*S/2 + S/2 - 1
 #pragma unroll
-                    for (int t = 0; t < S / 2; ++t) {
-                        col[t] = __builtin_amdgcn_perm(r[j][2 * t + 1], r[j][2 * t], 0x05040100u);
-                        col[S / 2 + t] = __builtin_amdgcn_perm(r[j][2 * t + 1], r[j][2 * t], 0x07060302u);
+                    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+                        for (int t = 0; t < S / 2; ++t) {
+                            col[(2 * q) * (S / 2) + t] = __builtin_amdgcn_perm(r[j][2 * t + 1][q], r[j][2 * t][q], 0x05040100u);
+                            col[(2 * q + 1) * (S / 2) + t] =
+                                __builtin_amdgcn_perm(r[j][2 * t + 1][q], r[j][2 * t][q], 0x07060302u);
+                        }
                     }
-                    if constexpr (S == 2) {
-                        *reinterpret_cast<u32x2 *>(d) = u32x2{col[0], col[1]};
-                    } else if constexpr (S == 4) {
-                        *reinterpret_cast<u32x4 *>(d) = u32x4{col[0], col[1], col[2], col[3]};
-                    } else {
-                        reinterpret_cast<u32x4 *>(d)[0] = u32x4{col[0], col[1], col[2], col[3]};
-                        reinterpret_cast<u32x4 *>(d)[1] = u32x4{col[4], col[5], col[6], col[7]};
-                    }
+#pragma unroll
+                    for (int v = 0; v < S; ++v) d[v] = u32x4{col[4 * v], col[4 * v + 1], col[4 * v + 2], col[4 * v + 3]};
                 }
             }
         }
