@@ -25,6 +25,11 @@ list and the passages each follows:
                     ("SparseDecoding: Decoding-Aware Pruning ...", Main Findings;
                     "SparseDecoding:解码感知的准确高效大模型剪枝框架", 核心方法 核心创新二)
 
+* ``prune_pack_unstructured`` / ``unpack_unstructured`` / ``spmv_unstructured`` -- the
+                    pages' 50% unstructured setting: each row keeps its K/2 highest scores
+                    (same score and tie rule), same bitmask + ascending-values encoding
+                    with a varying number of set bits per word
+                    ("SparseDecoding: Decoding-Aware Pruning ...", Methodology Steps 3-4)
 * ``swiglu`` / ``swiglu_tolerance`` -- h = silu(g) * u, silu(g) = g / (1 + exp(-g)), on
                     fp64 gate and up products (the gated MLP of the models the pages
                     evaluate: Llama-3.1-8B, Llama-3.3-70B, Qwen3), and the error bound a
@@ -81,9 +86,13 @@ def _load():
     lib.nmo_spmv.argtypes = [p, p, i64, i64, p, i64, ctypes.c_int, p, p, ctypes.c_int]
     lib.nmo_dense.argtypes = [p, i64, i64, i64, p, i64, ctypes.c_int, p, p, ctypes.c_int]
     lib.nmo_meta_from_mask.argtypes = [p, i64, i64, ctypes.c_int, p]
+    lib.nmo_prune_pack_unstructured.argtypes = [p, i64, i64, i64, p, p, p]
+    lib.nmo_unpack_unstructured.argtypes = [p, p, i64, i64, p]
+    lib.nmo_spmv_unstructured.argtypes = [p, p, i64, i64, p, i64, ctypes.c_int, p, p, ctypes.c_int]
     lib.nmo_spmv_index.argtypes = [p, ctypes.c_int, p, i64, i64, p, i64, ctypes.c_int, p, p, ctypes.c_int]
     for f in (lib.nmo_col_norm, lib.nmo_prune_pack, lib.nmo_unpack, lib.nmo_spmv, lib.nmo_dense,
-              lib.nmo_meta_from_mask, lib.nmo_spmv_index):
+              lib.nmo_meta_from_mask, lib.nmo_spmv_index, lib.nmo_prune_pack_unstructured,
+              lib.nmo_unpack_unstructured, lib.nmo_spmv_unstructured):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -170,6 +179,49 @@ def dense(W, x, nthreads: int = 1):
     y = np.empty((B, R), dtype=np.float64)
     a = np.empty((B, R), dtype=np.float64)
     _check(_load().nmo_dense(_ptr(W), K, R, K, _ptr(x), K, B, _ptr(y), _ptr(a), int(nthreads)), "dense")
+    return y, a
+
+
+def prune_pack_unstructured(W, n):
+    """W: uint16 [R, K]; n: float32 [K] -> (masks uint32 [R, K/32], values uint16 [R, K/2]), K/2 kept per row."""
+    W = _u16(W)
+    n = np.ascontiguousarray(n, dtype=np.float32)
+    R, K = W.shape
+    if n.shape != (K,):
+        raise ValueError("col_norm length must equal K")
+    if K % 32:
+        raise OracleError("prune_pack_unstructured: bad argument")
+    masks = np.empty((R, K // 32), dtype=np.uint32)
+    values = np.empty((R, K // 2), dtype=np.uint16)
+    _check(_load().nmo_prune_pack_unstructured(_ptr(W), K, R, K, _ptr(n), _ptr(masks), _ptr(values)),
+           "prune_pack_unstructured")
+    return masks, values
+
+
+def unpack_unstructured(masks, values, K: int) -> np.ndarray:
+    masks = np.ascontiguousarray(masks, dtype=np.uint32)
+    values = _u16(values)
+    R = masks.shape[0]
+    out = np.empty((R, K), dtype=np.uint16)
+    _check(_load().nmo_unpack_unstructured(_ptr(masks), _ptr(values), R, K, _ptr(out)), "unpack_unstructured")
+    return out
+
+
+def spmv_unstructured(masks, values, x, K: int, nthreads: int = 1):
+    """-> (y fp64 [B, R], absum fp64 [B, R]) for unstructured rows (K/2 set bits per row)."""
+    masks = np.ascontiguousarray(masks, dtype=np.uint32)
+    values = _u16(values)
+    x = _u16(x)
+    if x.ndim == 1:
+        x = x[None, :]
+    R = masks.shape[0]
+    B = x.shape[0]
+    if x.shape[1] != K or masks.shape != (R, K // 32) or values.shape != (R, K // 2):
+        raise ValueError("shape mismatch")
+    y = np.empty((B, R), dtype=np.float64)
+    a = np.empty((B, R), dtype=np.float64)
+    _check(_load().nmo_spmv_unstructured(_ptr(masks), _ptr(values), R, K, _ptr(x), K, B, _ptr(y), _ptr(a),
+                                         int(nthreads)), "spmv_unstructured")
     return y, a
 
 

@@ -143,6 +143,58 @@ int nmo_prune_pack(const uint16_t *W, int64_t ldw, int64_t R, int64_t K, const f
     return NMO_OK;
 }
 
+/* qsort order for a whole row: (score descending, column ascending). */
+static int cmp_scored(const void *a, const void *b)
+{
+    const scored_t *x = (const scored_t *)a, *y = (const scored_t *)b;
+    if (before(x, y)) return -1;
+    if (before(y, x)) return 1;
+    return 0;
+}
+
+/*
+ * 50% unstructured selection [SD-en, Methodology Step 4: "50% unstructured sparsity",
+ * retaining 50% of weights; SD-en, Step 3 on rows of a general sparse matrix].
+ * Reading taken: the comparison group is the whole output row (as in Wanda's
+ * unstructured setting), each row keeps exactly K/2 weights -- the first K/2 of the
+ * row under (score descending, column ascending), score s_ij = |W_ij| * n_j as above.
+ * Encoding is unchanged: one bit per column, kept values in increasing column order,
+ * now with a varying number of set bits per word (the t-th kept value of the row is
+ * values[t]).
+ */
+int nmo_prune_pack_unstructured(const uint16_t *W, int64_t ldw, int64_t R, int64_t K, const float *n,
+                                uint32_t *masks, uint16_t *values)
+{
+    if (!W || !n || !masks || !values) return NMO_EARG;
+    if (R < 1 || K < 32 || K % 32 != 0 || ldw < K) return NMO_EARG;
+    for (int64_t j = 0; j < K; ++j)
+        if (!isfinite(n[j]) || n[j] < 0.0f) return NMO_ENONFINITE;
+    scored_t *order = (scored_t *)malloc((size_t)K * sizeof(scored_t));
+    if (!order) return NMO_ENOMEM;
+    for (int64_t i = 0; i < R; ++i) {
+        const uint16_t *row = W + i * ldw;
+        for (int64_t j = 0; j < K; ++j) {
+            if (!bf16_finite(row[j])) {
+                free(order);
+                return NMO_ENONFINITE;
+            }
+            order[j].col = (int)j;
+            order[j].score = fabs(bf16_val(row[j])) * (double)n[j];
+        }
+        qsort(order, (size_t)K, sizeof(scored_t), cmp_scored);
+        for (int64_t w = 0; w < K / 32; ++w) masks[i * (K / 32) + w] = 0u;
+        for (int64_t k = 0; k < K / 2; ++k) {
+            int64_t c = order[k].col;
+            masks[i * (K / 32) + c / 32] |= 1u << (c % 32);
+        }
+        int64_t t = 0;
+        for (int64_t j = 0; j < K; ++j)
+            if (masks[i * (K / 32) + j / 32] & (1u << (j % 32))) values[i * (K / 2) + t++] = row[j];
+    }
+    free(order);
+    return NMO_OK;
+}
+
 /* Expand one packed row back to a dense row of bf16 patterns (zeros elsewhere). */
 static int unpack_row(const uint32_t *mrow, const uint16_t *vrow, int64_t K, uint16_t *out)
 {
@@ -159,6 +211,32 @@ static int unpack_row(const uint32_t *mrow, const uint16_t *vrow, int64_t K, uin
             }
         }
         if (t != 16) return NMO_EMASK;
+    }
+    return NMO_OK;
+}
+
+/* Unstructured rows: the t-th set bit of the row (words in order, lowest bit first) owns
+ * values[t]; a row must hold exactly K/2 set bits. */
+static int unpack_row_rowwise(const uint32_t *mrow, const uint16_t *vrow, int64_t K, uint16_t *out)
+{
+    int64_t t = 0;
+    for (int64_t j = 0; j < K; ++j) {
+        if (mrow[j / 32] & (1u << (j % 32))) {
+            if (t >= K / 2) return NMO_EMASK;
+            out[j] = vrow[t++];
+        } else {
+            out[j] = 0;
+        }
+    }
+    return t == K / 2 ? NMO_OK : NMO_EMASK;
+}
+
+int nmo_unpack_unstructured(const uint32_t *masks, const uint16_t *values, int64_t R, int64_t K, uint16_t *Wout)
+{
+    if (!masks || !values || !Wout || R < 1 || K < 32 || K % 32 != 0) return NMO_EARG;
+    for (int64_t i = 0; i < R; ++i) {
+        int rc = unpack_row_rowwise(masks + i * (K / 32), values + i * (K / 2), K, Wout + i * K);
+        if (rc) return rc;
     }
     return NMO_OK;
 }
@@ -244,6 +322,7 @@ typedef struct {
     const void *meta;        /* index metadata (nmo_spmv_index), else NULL */
     int fmt;                 /* NMO_META_U8 or NMO_META_I32 when meta is set */
     const uint32_t *masks;   /* NULL for the dense reference */
+    int rowwise;             /* masks with a varying count per word (unstructured rows) */
     const uint16_t *values;  /* packed values, or the dense W */
     int64_t ldw;             /* dense only */
     int64_t R, K, ldx;
@@ -288,7 +367,9 @@ static void *mv_worker(void *arg)
     for (int64_t i = jb->r0; i < jb->r1; ++i) {
         const uint16_t *w;
         if (jb->masks) {
-            int rc = unpack_row(jb->masks + i * (jb->K / 32), jb->values + i * (jb->K / 2), jb->K, row);
+            int rc = jb->rowwise
+                         ? unpack_row_rowwise(jb->masks + i * (jb->K / 32), jb->values + i * (jb->K / 2), jb->K, row)
+                         : unpack_row(jb->masks + i * (jb->K / 32), jb->values + i * (jb->K / 2), jb->K, row);
             if (rc) {
                 jb->rc = rc;
                 break;
@@ -423,6 +504,31 @@ int nmo_spmv_index(const void *meta, int fmt, const uint16_t *values, int64_t R,
     memset(&p, 0, sizeof p);
     p.meta = meta;
     p.fmt = fmt;
+    p.values = values;
+    p.R = R;
+    p.K = K;
+    p.ldx = ldx;
+    p.x = x;
+    p.B = B;
+    p.y = y;
+    p.absum = absum;
+    return run_mv(p, nthreads);
+}
+
+/* Sparse reference for unstructured rows: the matvec of the unpacked pruned matrix. */
+int nmo_spmv_unstructured(const uint32_t *masks, const uint16_t *values, int64_t R, int64_t K, const uint16_t *x,
+                          int64_t ldx, int B, double *y, double *absum, int nthreads)
+{
+    if (!masks || !values || !x || !y || !absum) return NMO_EARG;
+    if (R < 1 || K < 32 || K % 32 != 0 || B < 1 || ldx < K) return NMO_EARG;
+    int rc = check_x(x, K, ldx, B);
+    if (rc) return rc;
+    for (int64_t i = 0; i < R * (K / 2); ++i)
+        if (!bf16_finite(values[i])) return NMO_ENONFINITE;
+    mv_job p;
+    memset(&p, 0, sizeof p);
+    p.masks = masks;
+    p.rowwise = 1;
     p.values = values;
     p.R = R;
     p.K = K;
