@@ -119,6 +119,8 @@ def parse():
     ap.add_argument("--skip-check", action="store_true", help="skip the oracle spot check")
     ap.add_argument("--no-meta-formats", action="store_true",
                     help="skip the bitmask vs uint8-offset vs int32-index comparison table")
+    ap.add_argument("--no-unstructured", action="store_true",
+                    help="skip the 50%% unstructured vs N:M comparison table")
     ap.add_argument("--profile-kernel", action="store_true",
                     help="counter-collection mode: only the dominant launch shape (eager, rotated) plus a "
                          "plain 256 MiB device copy used to calibrate the byte counters")
@@ -481,6 +483,56 @@ def main():
             f"{n} bitmask {d['bitmask']['us']} u8 {d['u8_offset']['us']} i32 {d['i32_index']['us']}"
             for n, d in meta_table.items()))
 
+    # ---------------------------------------------------------------- 50% unstructured rows
+    # The pages' other 50% setting: each row keeps its K/2 highest scores, same encoding,
+    # a varying number of set bits per word.  Packed on the device from the same weights
+    # and timed like the N:M table (>= 512 MB of distinct buffers).
+    unstructured = None
+    if not args.no_unstructured:
+        import oracle
+
+        unstructured = {}
+        (N, M) = patterns[0]
+        for pi, (name, R, K, group) in enumerate(projs):
+            nb_ = sparse_bytes(R, K, B)
+            cnt = max(2, math.ceil(ROTATE_BYTES / nb_))
+            pool = []
+            for c in range(cnt):
+                W = synth.device_weights(R, K, args.seed, 100 + pi, c)
+                n = nm.nm_col_norm(synth.device_calib_acts(K, args.seed, 200 + pi, c))
+                pool.append(nm.nm_prune_pack_unstructured(W, n))
+                if c == 0:
+                    # spot check: masks/values bit-exact and the product within tolerance on sampled rows
+                    g = np.random.default_rng(args.seed + pi)
+                    rows = np.unique(np.concatenate([[0, R - 1], g.choice(R, size=min(R, 6), replace=False)]))
+                    ridx = torch.from_numpy(rows).to(dev)
+                    hu = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+                    nref = oracle.col_norm(hu(synth.device_calib_acts(K, args.seed, 200 + pi, c)))
+                    ms, vs = oracle.prune_pack_unstructured(hu(W.index_select(0, ridx)), nref)
+                    mk, vl = pool[0]
+                    assert (mk.index_select(0, ridx).cpu().numpy().view(np.uint32) == ms).all(), f"u masks {name}"
+                    assert (hu(vl.index_select(0, ridx)) == vs).all(), f"u values {name}"
+                    yu = nm.nm_spmv_unstructured(mk, vl, xs[group][0], workspace=ws)
+                    yref, absum = oracle.spmv_unstructured(ms, vs, hu(xs[group][0]), K)
+                    yg = (hu(yu)[:, rows].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+                    assert oracle.within_tolerance(yg, yref, absum).all(), f"unstructured spmv {name}"
+                del W, n
+            fns = [(lambda mk=mk, vl=vl, x=xs[group][i % L]:
+                    nm.nm_spmv_unstructured(mk, vl, x, out=ys[name], workspace=ws)) for i, (mk, vl) in enumerate(pool)]
+            g = capture(torch, fns)
+            g.replay()
+            us = min(timer.time_graph(g, 1) for _ in range(reps)) * 1e3 / len(fns)
+            nmus = per[name][f"{N}:{M}"]["us"]
+            unstructured[name] = {"R": R, "K": K, "us": round(us, 2), "GBs": round(nb_ / us / 1e3, 1),
+                                  "pct_peak": round(100 * nb_ / us / 1e3 / HBM_PEAK_GBS, 1),
+                                  f"nm_{N}:{M}_us": nmus, "slowdown_vs_nm": round(us / nmus, 3),
+                                  "speedup_vs_dense": round(per[name]["dense_us"] / us, 3),
+                                  "rotation_MB": round(len(fns) * nb_ / 1e6)}
+            del g, pool, fns
+            torch.cuda.synchronize()
+        log("unstructured 50% (us): " + "; ".join(f"{n} {d['us']} (N:M {d[f'nm_{N}:{M}_us']}, dense "
+                                                   f"x{d['speedup_vs_dense']})" for n, d in unstructured.items()))
+
     # Dominant kernel: the launch of the (fused) step whose launches take the largest share
     # of it; its algorithmic bytes over its average launch time is the roofline's achieved.
     share = {}
@@ -562,6 +614,7 @@ def main():
                          "speedup_vs_dense": round(ms_dense * len(patterns) / ms_sparse, 3)},
         "per_layer": per,
         "metadata_formats": meta_table,
+        "unstructured_50": unstructured,
         "pack_GBs": round(pack_bytes / pack_ms / 1e6, 1),
         "parity": parity,
         "roofline": roofline,

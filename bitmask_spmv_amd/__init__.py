@@ -24,7 +24,8 @@ __all__ = [
     "NM_PATTERNS", "nm_spmv_multi", "nm_spmv_multi_workspace_bytes", "dense_gemv_multi",
     "dense_gemv_multi_workspace_bytes", "NM_META_BITMASK", "NM_META_U8_OFFSET", "NM_META_I32_INDEX",
     "nm_meta_from_mask", "nm_spmv_meta", "nm_spmv_swiglu", "nm_spmv_swiglu_workspace_bytes", "dense_gemv_swiglu",
-    "dense_gemv_swiglu_workspace_bytes",
+    "dense_gemv_swiglu_workspace_bytes", "nm_prune_pack_unstructured", "nm_spmv_unstructured",
+    "nm_spmv_unstructured_workspace_bytes", "nm_unpack_unstructured",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnmspmv.so")
@@ -69,6 +70,11 @@ def _load() -> ctypes.CDLL:
     L.dense_gemv.argtypes = [p, i64, i64, i64, p, i64, i32, p, i64, p, sz, p]
     L.nm_unpack.argtypes = [p, p, i64, i64, p, i64, p]
     L.nm_meta_from_mask.argtypes = [p, i64, i64, i32, p, p]
+    L.nm_prune_pack_unstructured.argtypes = [p, i64, i64, i64, p, p, p, p]
+    L.nm_spmv_unstructured_workspace_bytes.argtypes = [i64, i64, i32]
+    L.nm_spmv_unstructured_workspace_bytes.restype = sz
+    L.nm_spmv_unstructured.argtypes = [p, p, i64, i64, p, i64, i32, p, i64, p, sz, p]
+    L.nm_unpack_unstructured.argtypes = [p, p, i64, i64, p, i64, p]
     L.nm_spmv_swiglu_workspace_bytes.argtypes, L.nm_spmv_swiglu_workspace_bytes.restype = [i64, i64, i32], sz
     L.nm_spmv_swiglu.argtypes = [p, p, p, p, i64, i64, p, i64, i32, p, i64, p, sz, p]
     L.dense_gemv_swiglu_workspace_bytes.argtypes, L.dense_gemv_swiglu_workspace_bytes.restype = [i64, i64, i32], sz
@@ -322,6 +328,62 @@ def dense_gemv_swiglu(W_gate: torch.Tensor, W_up: torch.Tensor, x: torch.Tensor,
     _check(lib.dense_gemv_swiglu(_ptr(W_gate), _ptr(W_up), _ld(W_gate), R, K, _ptr(x2), _ld(x2), B, _ptr(o2),
                                  _ld(o2), _ptr(ws), ws_bytes, _stream(x2)))
     return out[0] if squeeze and out.dim() == 2 else out
+
+
+def nm_prune_pack_unstructured(W: torch.Tensor, col_norm: torch.Tensor, masks: torch.Tensor | None = None,
+                               values: torch.Tensor | None = None):
+    """50% unstructured: W bf16 [R, K], col_norm fp32 [K] -> (masks int32 [R, K/32], values bf16 [R, K/2]),
+    each row keeping its K/2 highest scores."""
+    _dev(W, "W", torch.bfloat16, 2)
+    _dev(col_norm, "col_norm", torch.float32, 1)
+    R, K = W.shape
+    if col_norm.shape[0] != K:
+        raise ValueError("col_norm must have K entries")
+    if masks is None:
+        masks = torch.empty((R, max(K // 32, 1)), dtype=torch.int32, device=W.device)
+    if values is None:
+        values = torch.empty((R, max(K // 2, 1)), dtype=torch.bfloat16, device=W.device)
+    _dev(masks, "masks", torch.int32, 2)
+    _dev(values, "values", torch.bfloat16, 2)
+    if not (masks.is_contiguous() and values.is_contiguous()):
+        raise ValueError("masks and values must be contiguous")
+    if K % 32 == 0 and (masks.shape != (R, K // 32) or values.shape != (R, K // 2)):
+        raise ValueError("masks must be [R, K/32] and values [R, K/2]")
+    _check(lib.nm_prune_pack_unstructured(_ptr(W), _ld(W), R, K, _ptr(col_norm), _ptr(masks), _ptr(values),
+                                          _stream(W)))
+    return masks, values
+
+
+def nm_spmv_unstructured_workspace_bytes(R: int, K: int, B: int) -> int:
+    return int(lib.nm_spmv_unstructured_workspace_bytes(R, K, B))
+
+
+def nm_spmv_unstructured(masks: torch.Tensor, values: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None,
+                         workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """y = W_sparse x for 50% unstructured rows packed by nm_prune_pack_unstructured."""
+    _dev(masks, "masks", torch.int32, 2)
+    _dev(values, "values", torch.bfloat16, 2)
+    if not (masks.is_contiguous() and values.is_contiguous()):
+        raise ValueError("masks and values must be contiguous")
+    R, K = masks.shape[0], masks.shape[1] * 32
+    if values.shape != (R, K // 2):
+        raise ValueError("values must be [R, K/2] with K = 32 * masks.shape[1]")
+    x2, B, o2, out, squeeze = _x_y(x, R, K, out)
+    ws, ws_bytes = _workspace(nm_spmv_unstructured_workspace_bytes(R, K, B), x2, workspace)
+    _check(lib.nm_spmv_unstructured(_ptr(masks), _ptr(values), R, K, _ptr(x2), _ld(x2), B, _ptr(o2), _ld(o2),
+                                    _ptr(ws), ws_bytes, _stream(x2)))
+    return out[0] if squeeze and out.dim() == 2 else out
+
+
+def nm_unpack_unstructured(masks: torch.Tensor, values: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    _dev(masks, "masks", torch.int32, 2)
+    _dev(values, "values", torch.bfloat16, 2)
+    R, K = masks.shape[0], masks.shape[1] * 32
+    if out is None:
+        out = torch.empty((R, K), dtype=torch.bfloat16, device=masks.device)
+    _dev(out, "out", torch.bfloat16, 2)
+    _check(lib.nm_unpack_unstructured(_ptr(masks), _ptr(values), R, K, _ptr(out), _ld(out), _stream(masks)))
+    return out
 
 
 def _multi_outs(x2, Rs, outs):

@@ -88,6 +88,11 @@ nmk::MvPlan spmv_plan(int64_t R, int64_t K, int B) {
     return p;
 }
 
+nmk::MvPlan spmv_unstructured_plan(int64_t R, int64_t K, int B) {
+    nmk::MvPlan p = nmk::plan_spmv_unstructured(R, K, B, device_info());
+    return p;
+}
+
 nmk::MvPlan dense_plan(int64_t R, int64_t K, int B) {
     nmk::MvPlan p = nmk::plan_dense(R, K, B, device_info());
     apply_override("NM_DENSE_PLAN", K / 8, R, B, (size_t)B * 16, p);
@@ -349,6 +354,76 @@ nm_status nm_spmv_swiglu(const uint32_t *gate_masks, const nm_bf16 *gate_values,
         return NM_OK;
     } catch (...) {
         return fail(NM_ERR_HIP, "nm_spmv_swiglu: internal error");
+    }
+}
+
+nm_status nm_prune_pack_unstructured(const nm_bf16 *W, int64_t ldw, int64_t R, int64_t K, const float *col_norm,
+                                     uint32_t *masks, nm_bf16 *values, void *hip_stream) {
+    try {
+        g_err[0] = 0;
+        if (!W || !col_norm || !masks || !values) return fail(NM_ERR_NULL, "nm_prune_pack_unstructured: NULL pointer");
+        if (R < 1 || R > kMaxDim || K < 32 || K > kMaxDim || K % 32 != 0 || ldw < K)
+            return fail(NM_ERR_SHAPE, "nm_prune_pack_unstructured: bad sizes R=%lld K=%lld ldw=%lld", (long long)R,
+                        (long long)K, (long long)ldw);
+        if (ldw % 8 || !aligned(W, 16) || !aligned(col_norm, 16) || !aligned(masks, 4) || !aligned(values, 2))
+            return fail(NM_ERR_ALIGN, "nm_prune_pack_unstructured: W/col_norm need 16-byte alignment, ldw % 8 == 0");
+        hipError_t e = nmk::launch_prune_pack_unstructured(W, ldw, R, K, col_norm, masks, values,
+                                                           (hipStream_t)hip_stream);
+        if (e != hipSuccess) return hip_fail("nm_prune_pack_unstructured launch", e);
+        return NM_OK;
+    } catch (...) {
+        return fail(NM_ERR_HIP, "nm_prune_pack_unstructured: internal error");
+    }
+}
+
+size_t nm_spmv_unstructured_workspace_bytes(int64_t R, int64_t K, int B) {
+    if (R < 1 || R > kMaxDim || K < 32 || K % 32 != 0 || K > kMaxDim || B < 1 || B > 8) return 0;
+    return spmv_unstructured_plan(R, K, B).ws_bytes;
+}
+
+nm_status nm_spmv_unstructured(const uint32_t *masks, const nm_bf16 *values, int64_t R, int64_t K, const nm_bf16 *x,
+                               int64_t ldx, int B, nm_bf16 *y, int64_t ldy, void *workspace, size_t workspace_bytes,
+                               void *hip_stream) {
+    try {
+        g_err[0] = 0;
+        const char *who = "nm_spmv_unstructured";
+        if (!masks || !values || !x || !y) return fail(NM_ERR_NULL, "%s: NULL pointer", who);
+        if (K < 32 || K > kMaxDim || K % 32 != 0)
+            return fail(NM_ERR_SHAPE, "%s: K=%lld must be a positive multiple of 32", who, (long long)K);
+        nm_status st = check_mv_common(R, K, B, ldx, ldy, x, y);
+        if (st != NM_OK) return st;
+        if (!aligned(masks, 4) || !aligned(values, 16))
+            return fail(NM_ERR_ALIGN, "%s: masks need 4-byte and values 16-byte alignment", who);
+        const nmk::MvPlan p = spmv_unstructured_plan(R, K, B);
+        if (p.ws_bytes > 0) {
+            if (!workspace || workspace_bytes < p.ws_bytes || !aligned(workspace, 4))
+                return fail(NM_ERR_WORKSPACE, "%s: workspace of %zu bytes required, %zu given", who, p.ws_bytes,
+                            workspace ? workspace_bytes : (size_t)0);
+        }
+        hipError_t e = nmk::launch_spmv_unstructured(p, masks, values, R, K, x, ldx, B, y, ldy, (float *)workspace,
+                                                     (hipStream_t)hip_stream);
+        if (e != hipSuccess) return hip_fail(who, e);
+        return NM_OK;
+    } catch (...) {
+        return fail(NM_ERR_HIP, "nm_spmv_unstructured: internal error");
+    }
+}
+
+nm_status nm_unpack_unstructured(const uint32_t *masks, const nm_bf16 *values, int64_t R, int64_t K, nm_bf16 *W_out,
+                                 int64_t ldw, void *hip_stream) {
+    try {
+        g_err[0] = 0;
+        if (!masks || !values || !W_out) return fail(NM_ERR_NULL, "nm_unpack_unstructured: NULL pointer");
+        if (R < 1 || R > kMaxDim || K < 32 || K > kMaxDim || K % 32 != 0 || ldw < K)
+            return fail(NM_ERR_SHAPE, "nm_unpack_unstructured: bad sizes R=%lld K=%lld ldw=%lld", (long long)R,
+                        (long long)K, (long long)ldw);
+        if (ldw % 8 || !aligned(W_out, 16) || !aligned(values, 2) || !aligned(masks, 4))
+            return fail(NM_ERR_ALIGN, "nm_unpack_unstructured: W_out needs 16-byte alignment, ldw % 8 == 0");
+        hipError_t e = nmk::launch_unpack_unstructured(masks, values, R, K, W_out, ldw, (hipStream_t)hip_stream);
+        if (e != hipSuccess) return hip_fail("nm_unpack_unstructured launch", e);
+        return NM_OK;
+    } catch (...) {
+        return fail(NM_ERR_HIP, "nm_unpack_unstructured: internal error");
     }
 }
 

@@ -66,6 +66,15 @@ hipError_t launch_prune_pack(const uint16_t *W, int64_t ldw, int64_t R, int64_t 
                              uint32_t *masks, uint16_t *values, hipStream_t st);
 hipError_t launch_unpack(const uint32_t *masks, const uint16_t *values, int64_t R, int64_t K, uint16_t *W,
                          int64_t ldw, hipStream_t st);
+// 50% unstructured rows (K/2 kept per row; same encoding, varying set bits per word).
+hipError_t launch_prune_pack_unstructured(const uint16_t *W, int64_t ldw, int64_t R, int64_t K, const float *n,
+                                         uint32_t *masks, uint16_t *values, hipStream_t st);
+hipError_t launch_unpack_unstructured(const uint32_t *masks, const uint16_t *values, int64_t R, int64_t K,
+                                      uint16_t *W, int64_t ldw, hipStream_t st);
+MvPlan plan_spmv_unstructured(int64_t R, int64_t K, int B, const DeviceInfo &dev);
+hipError_t launch_spmv_unstructured(const MvPlan &p, const uint32_t *masks, const uint16_t *values, int64_t R,
+                                    int64_t K, const uint16_t *x, int64_t ldx, int B, uint16_t *y, int64_t ldy,
+                                    float *ws, hipStream_t st);
 hipError_t launch_meta_from_mask(const uint32_t *masks, int64_t R, int64_t K, int fmt, void *meta, hipStream_t st);
 // R of the plan = total rows of the set (set.row0[set.P]).
 hipError_t launch_spmv(const MvPlan &p, const SpmvSet &set, int fmt, int64_t K, const uint16_t *x, int64_t ldx,

@@ -31,35 +31,14 @@
 
 #include "nm_device.h"
 #include "nm_kernels.h"
+#include "nm_spmv_common.h"
 
 namespace nmk {
 namespace {
 
-// LDS layout of x.  B = 1: each 32-column block is 16 dwords of bf16 pairs plus one pad
-// dword (17 dwords), so lanes walking different words spread over the banks.  B > 1:
-// tokens are interleaved per column -- column c holds S bf16 (S = B rounded up to 2, 4
-// or 8, zero-filled) -- so one 4/8/16-byte LDS load gathers a column for every token;
-// blocks are 16*S dwords plus S/2 pad dwords (keeping 8/16-byte alignment).
-template <int B>
-struct XLayout {
-    static constexpr int S = B == 1 ? 1 : (B <= 2 ? 2 : (B <= 4 ? 4 : 8));
-    static constexpr int kBlk = B == 1 ? 17 : 16 * S + S / 2;  // dwords per 32-column block
-};
-
-constexpr int blk_dwords(int B) {
-    return B == 1 ? 17 : (B <= 2 ? 33 : (B <= 4 ? 66 : 132));
-}
-
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kThreads = 512;     // default workgroup: 8 waves (256 for matrices with few rows)
 constexpr size_t kLdsCap = 80 * 1024;     // keeps two workgroups resident per CU
 constexpr size_t kLdsPerCu = 160 * 1024;  // gfx950 LDS per compute unit
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
-}
 
 // Metadata bytes per 32-column word (16 kept weights) of each format.
 constexpr int meta_bytes(int fmt) { return fmt == kMetaBitmask ? 4 : (fmt == kMetaU8 ? 16 : 64); }
@@ -120,47 +99,6 @@ __device__ __forceinline__ void load_batch(Batch<FMT> &bt, const uint8_t *mrow, 
 // Swap one dword with the neighbouring lane of the pair (lane ^ 1).
 __device__ __forceinline__ uint32_t pair_swap(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);  // quad_perm(1,0,3,2)
-}
-
-// Gather of one column for the S token slots (S/2 dwords: token pairs).
-template <int S>
-__device__ __forceinline__ void gather_col(const uint32_t *blk, int c, uint32_t (&d)[S / 2]) {
-    if constexpr (S == 2) {
-        d[0] = blk[c];
-    } else if constexpr (S == 4) {
-        const u32x2 t = *reinterpret_cast<const u32x2 *>(blk + 2 * c);
-        d[0] = t.x;
-        d[1] = t.y;
-    } else {
-        const u32x4 t = *reinterpret_cast<const u32x4 *>(blk + 4 * c);
-        d[0] = t.x;
-        d[1] = t.y;
-        d[2] = t.z;
-        d[3] = t.w;
-    }
-}
-
-// One pair of kept weights: the inputs of columns c0 and c1 of the word's block (per
-// token) meet the packed value pair v in one v_dot2_f32_bf16.
-template <int B>
-__device__ __forceinline__ void dot_pair(uint32_t v, const uint32_t *blk, int c0, int c1, float (&acc)[B]) {
-    constexpr int S = XLayout<B>::S;
-    if constexpr (S == 1) {
-        const uint16_t *xw = reinterpret_cast<const uint16_t *>(blk);
-        const uint32_t pr = (uint32_t)xw[c0] | ((uint32_t)xw[c1] << 16);
-        acc[0] = dot2_bf16(v, pr, acc[0]);
-    } else {
-        uint32_t d0[S / 2], d1[S / 2];
-        gather_col<S>(blk, c0, d0);
-        gather_col<S>(blk, c1, d1);
-#pragma unroll
-        for (int j = 0; j < S / 2; ++j) {
-            // (token 2j of column c0, token 2j of column c1), then the same for 2j+1
-            if (2 * j < B) acc[2 * j] = dot2_bf16(v, __builtin_amdgcn_perm(d1[j], d0[j], 0x05040100u), acc[2 * j]);
-            if (2 * j + 1 < B)
-                acc[2 * j + 1] = dot2_bf16(v, __builtin_amdgcn_perm(d1[j], d0[j], 0x07060302u), acc[2 * j + 1]);
-        }
-    }
 }
 
 // Walk of one batch: 8 pairs of kept weights per lane.
@@ -307,75 +245,12 @@ __global__ __launch_bounds__(NT) void spmv_kernel(const SpmvSet set, int KW, con
     // never covers the loads of the other).
     Batch<FMT> bufA, bufB;
     int rowA = first_row, biA = 0, rowB = first_row, biB = 0;
-    // Stage this slice of x into LDS.  The first round of x loads is issued before batch
-    // A's weight loads, so waiting for x (an L2 hit after the first workgroup of an XCD)
-    // never waits for the weights queued behind it.
-    if constexpr (XLayout<B>::S == 1) {
-        // 16-byte loads; 8 bf16 per chunk, 4 chunks per 32-column block
-        constexpr int kStage = 4;
-        const int chunks = nws * 4;
-        for (int i0 = 0; i0 < chunks || i0 == 0; i0 += NT * kStage) {
-            u32x4 r[kStage];
-#pragma unroll
-            for (int j = 0; j < kStage; ++j) {
-                const int i = i0 + j * NT + (int)threadIdx.x;
-                if (i < chunks) r[j] = reinterpret_cast<const u32x4 *>(x + (int64_t)w0 * 32)[i];
-            }
-            if (i0 == 0) load_row_batch<FMT, EPI>(bufA, set, min(rowA, R - 1), KW, w0, total > 0 ? nws : 0, 0, lane);
-#pragma unroll
-            for (int j = 0; j < kStage; ++j) {
-                const int i = i0 + j * NT + (int)threadIdx.x;
-                if (i < chunks) {
-                    uint32_t *d = xs + (i >> 2) * XLayout<B>::kBlk + (i & 3) * 4;
-                    d[0] = r[j].x;
-                    d[1] = r[j].y;
-                    d[2] = r[j].z;
-                    d[3] = r[j].w;
-                }
-            }
-        }
-    } else {
-        // Eight columns per thread and round: one 16-byte load of every token, transposed
-        // with byte permutes into the interleaved per-column layout (the eight columns'
-        // 4*S dwords are contiguous in LDS: S 16-byte stores).
-        constexpr int S = XLayout<B>::S;
-        constexpr int kStage = 8 / S;  // 8 x 16-byte loads in flight per thread and round
-        const int octs = nws * 4;
-        const uint16_t *xw = x + (int64_t)w0 * 32;
-        for (int i0 = 0; i0 < octs || i0 == 0; i0 += NT * kStage) {
-            u32x4 r[kStage][S];
-#pragma unroll
-            for (int j = 0; j < kStage; ++j) {
-                const int i = i0 + j * NT + (int)threadIdx.x;
-#pragma unroll
-                for (int b = 0; b < S; ++b)
-                    r[j][b] = (b < B && i < octs) ? *reinterpret_cast<const u32x4 *>(xw + (int64_t)b * ldx + 8 * i)
-                                                  : u32x4{0u, 0u, 0u, 0u};
-            }
-            if (i0 == 0)
-                load_row_batch<FMT, EPI>(bufA, set, min(rowA, R - 1), KW, w0, total > 0 ? nws : 0, 0, lane);
-#pragma unroll
-            for (int j = 0; j < kStage; ++j) {
-                const int i = i0 + j * NT + (int)threadIdx.x;
-                if (i < octs) {
-                    const int c = 8 * i;  // first column of the eight, within the slice
-                    u32x4 *d = reinterpret_cast<u32x4 *>(xs + (c >> 5) * XLayout<B>::kBlk + (c & 31) * (S / 2));
-                    uint32_t col[4 * S];  // column c+k: dwords k*S/2 .. k*S/2 + S/2 - 1
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-#pragma unroll
-                        for (int t = 0; t < S / 2; ++t) {
-                            col[(2 * q) * (S / 2) + t] = __builtin_amdgcn_perm(r[j][2 * t + 1][q], r[j][2 * t][q], 0x05040100u);
-                            col[(2 * q + 1) * (S / 2) + t] =
-                                __builtin_amdgcn_perm(r[j][2 * t + 1][q], r[j][2 * t][q], 0x07060302u);
-                        }
-                    }
-#pragma unroll
-                    for (int v = 0; v < S; ++v) d[v] = u32x4{col[4 * v], col[4 * v + 1], col[4 * v + 2], col[4 * v + 3]};
-                }
-            }
-        }
-    }
+    // Stage this slice of x into LDS; batch A's loads go out right after the first round
+    // of x loads, so waiting for x (an L2 hit after the first workgroup of an XCD) never
+    // waits for the weights queued behind it.
+    stage_x<B, NT>(xs, x, ldx, w0, nws, [&] {
+        load_row_batch<FMT, EPI>(bufA, set, min(rowA, R - 1), KW, w0, total > 0 ? nws : 0, 0, lane);
+    });
     __syncthreads();
 
     float acc[B], gsave[B];

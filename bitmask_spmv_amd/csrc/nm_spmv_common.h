@@ -1,0 +1,150 @@
+// nm_spmv_common.h -- pieces shared by the sparse matrix-vector kernels (N:M with any
+// metadata format, and 50% unstructured rows): the LDS layout of x and its staging, and
+// the pair-of-kept-weights dot product.  Internal; included by .hip files only.
+#pragma once
+
+#include "nm_device.h"
+
+namespace nmk {
+namespace {
+
+// LDS layout of x.  B = 1: each 32-column block is 16 dwords of bf16 pairs plus one pad
+// dword (17 dwords), so lanes walking different words spread over the banks.  B > 1:
+// tokens are interleaved per column -- column c holds S bf16 (S = B rounded up to 2, 4
+// or 8, zero-filled) -- so one 4/8/16-byte LDS load gathers a column for every token;
+// blocks are 16*S dwords plus S/2 pad dwords (keeping 8/16-byte alignment).
+template <int B>
+struct XLayout {
+    static constexpr int S = B == 1 ? 1 : (B <= 2 ? 2 : (B <= 4 ? 4 : 8));
+    static constexpr int kBlk = B == 1 ? 17 : 16 * S + S / 2;  // dwords per 32-column block
+};
+
+constexpr int blk_dwords(int B) {
+    return B == 1 ? 17 : (B <= 2 ? 33 : (B <= 4 ? 66 : 132));
+}
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+// Gather of one column for the S token slots (S/2 dwords: token pairs).
+template <int S>
+__device__ __forceinline__ void gather_col(const uint32_t *blk, int c, uint32_t (&d)[S / 2]) {
+    if constexpr (S == 2) {
+        d[0] = blk[c];
+    } else if constexpr (S == 4) {
+        const u32x2 t = *reinterpret_cast<const u32x2 *>(blk + 2 * c);
+        d[0] = t.x;
+        d[1] = t.y;
+    } else {
+        const u32x4 t = *reinterpret_cast<const u32x4 *>(blk + 4 * c);
+        d[0] = t.x;
+        d[1] = t.y;
+        d[2] = t.z;
+        d[3] = t.w;
+    }
+}
+
+// One pair of kept weights: the inputs of columns c0 and c1 of the word's block (per
+// token) meet the packed value pair v in one v_dot2_f32_bf16.
+template <int B>
+__device__ __forceinline__ void dot_pair(uint32_t v, const uint32_t *blk, int c0, int c1, float (&acc)[B]) {
+    constexpr int S = XLayout<B>::S;
+    if constexpr (S == 1) {
+        const uint16_t *xw = reinterpret_cast<const uint16_t *>(blk);
+        const uint32_t pr = (uint32_t)xw[c0] | ((uint32_t)xw[c1] << 16);
+        acc[0] = dot2_bf16(v, pr, acc[0]);
+    } else {
+        uint32_t d0[S / 2], d1[S / 2];
+        gather_col<S>(blk, c0, d0);
+        gather_col<S>(blk, c1, d1);
+#pragma unroll
+        for (int j = 0; j < S / 2; ++j) {
+            // (token 2j of column c0, token 2j of column c1), then the same for 2j+1
+            if (2 * j < B) acc[2 * j] = dot2_bf16(v, __builtin_amdgcn_perm(d1[j], d0[j], 0x05040100u), acc[2 * j]);
+            if (2 * j + 1 < B)
+                acc[2 * j + 1] = dot2_bf16(v, __builtin_amdgcn_perm(d1[j], d0[j], 0x07060302u), acc[2 * j + 1]);
+        }
+    }
+}
+
+// Stages columns [32*w0, 32*(w0+nws)) of x (B tokens, row stride ldx) into LDS in the
+// XLayout<B> layout, all NT threads of the workgroup taking part; first_round() runs
+// once, right after the first round of x loads has been issued (callers put their first
+// weight loads there).  The caller synchronises the workgroup afterwards.
+template <int B, int NT, class F>
+__device__ __forceinline__ void stage_x(uint32_t *xs, const uint16_t *__restrict__ x, int64_t ldx, int w0, int nws,
+                                        F &&first_round) {
+    if constexpr (XLayout<B>::S == 1) {
+        // 16-byte loads; 8 bf16 per chunk, 4 chunks per 32-column block
+        constexpr int kStage = 4;
+        const int chunks = nws * 4;
+        for (int i0 = 0; i0 < chunks || i0 == 0; i0 += NT * kStage) {
+            u32x4 r[kStage];
+#pragma unroll
+            for (int j = 0; j < kStage; ++j) {
+                const int i = i0 + j * NT + (int)threadIdx.x;
+                if (i < chunks) r[j] = reinterpret_cast<const u32x4 *>(x + (int64_t)w0 * 32)[i];
+            }
+            if (i0 == 0) first_round();
+#pragma unroll
+            for (int j = 0; j < kStage; ++j) {
+                const int i = i0 + j * NT + (int)threadIdx.x;
+                if (i < chunks) {
+                    uint32_t *d = xs + (i >> 2) * XLayout<B>::kBlk + (i & 3) * 4;
+                    d[0] = r[j].x;
+                    d[1] = r[j].y;
+                    d[2] = r[j].z;
+                    d[3] = r[j].w;
+                }
+            }
+        }
+    } else {
+        // Eight columns per thread and round: one 16-byte load of every token, transposed
+        // with byte permutes into the interleaved per-column layout (the eight columns'
+        // 4*S dwords are contiguous in LDS: S 16-byte stores).
+        constexpr int S = XLayout<B>::S;
+        constexpr int kStage = 8 / S;  // 8 x 16-byte loads in flight per thread and round
+        const int octs = nws * 4;
+        const uint16_t *xw = x + (int64_t)w0 * 32;
+        for (int i0 = 0; i0 < octs || i0 == 0; i0 += NT * kStage) {
+            u32x4 r[kStage][S];
+#pragma unroll
+            for (int j = 0; j < kStage; ++j) {
+                const int i = i0 + j * NT + (int)threadIdx.x;
+#pragma unroll
+                for (int b = 0; b < S; ++b)
+                    r[j][b] = (b < B && i < octs) ? *reinterpret_cast<const u32x4 *>(xw + (int64_t)b * ldx + 8 * i)
+                                                  : u32x4{0u, 0u, 0u, 0u};
+            }
+            if (i0 == 0) first_round();
+#pragma unroll
+            for (int j = 0; j < kStage; ++j) {
+                const int i = i0 + j * NT + (int)threadIdx.x;
+                if (i < octs) {
+                    const int c = 8 * i;  // first column of the eight, within the slice
+                    u32x4 *d = reinterpret_cast<u32x4 *>(xs + (c >> 5) * XLayout<B>::kBlk + (c & 31) * (S / 2));
+                    uint32_t col[4 * S];  // column c+k: dwords k*S/2 .. k*S/2 + S/2 - 1
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+                        for (int t = 0; t < S / 2; ++t) {
+                            col[(2 * q) * (S / 2) + t] = __builtin_amdgcn_perm(r[j][2 * t + 1][q], r[j][2 * t][q], 0x05040100u);
+                            col[(2 * q + 1) * (S / 2) + t] =
+                                __builtin_amdgcn_perm(r[j][2 * t + 1][q], r[j][2 * t][q], 0x07060302u);
+                        }
+                    }
+#pragma unroll
+                    for (int v = 0; v < S; ++v) d[v] = u32x4{col[4 * v], col[4 * v + 1], col[4 * v + 2], col[4 * v + 3]};
+                }
+            }
+        }
+    }
+}
+
+}  // namespace
+}  // namespace nmk

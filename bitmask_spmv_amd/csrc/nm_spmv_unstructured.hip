@@ -1,0 +1,326 @@
+// nm_spmv_unstructured.hip -- matrix-vector product of 50% unstructured rows on gfx950.
+//
+// What it computes (pages cited by title and section):
+//   "SparseDecoding: Decoding-Aware Pruning ..." (ai.info summary), Methodology Steps 2-4:
+//     the same encoding as the N:M kernel (one bit per column, kept values in increasing
+//     column order) for the pages' other 50% setting, unstructured sparsity, where a row
+//     keeps half of its weights but a 32-bit word may hold anywhere from 0 to 32 of them.
+//     Step 3 names exactly this case as the one the fixed 16-step walk does not cover:
+//     the number of traversal steps now differs between words.
+//
+// gfx950 design:
+//   * x in LDS exactly as in the N:M kernel (shared staging and layout).
+//   * one mask word per lane (lane l <-> word l of a 64-word strip, in word order); the
+//     wave's popcounts are prefix-summed across lanes (shuffles) to give every lane the
+//     offset of its word's values, and their total is the strip's value count n.
+//   * a strip's values are one contiguous run of the row's packed values; it is loaded
+//     with 16-byte loads that are contiguous across the wave, through a buffer
+//     descriptor that ends at the run (loads past it return zeros and move no data), and
+//     written to a per-wave LDS window from which lanes read their own values.
+//   * each lane walks its word two set bits at a time (lowest set bit, clear it) and
+//     feeds v_dot2_f32_bf16 with the value pair; the wave runs as many pair steps as its
+//     fullest word needs (lanes whose word ran out contribute zeros).
+//   * software pipeline: while strip t is walked, the values of strip t+1 (whose masks
+//     arrived one iteration earlier) and the masks of strip t+2 are in flight.
+//   * rows are balanced by construction (K/2 kept per row); a wave owns whole rows (or
+//     row slices, whose value offset is the popcount of the masks before the slice).
+#include "nm_device.h"
+#include "nm_kernels.h"
+#include "nm_spmv_common.h"
+
+namespace nmk {
+namespace {
+
+constexpr int kUThreads = 512;                 // 8 waves per workgroup
+constexpr int kWinChunks = 260;                // per-wave window: 16-byte chunks (>= 2048 values + 7 + pad)
+constexpr int kWinBytes = kWinChunks * 16;
+constexpr int kValLoads = (kWinChunks + kWave - 1) / kWave;  // 16-byte loads per lane for one strip (5)
+constexpr size_t kULdsCap = 80 * 1024;
+constexpr size_t kULdsPerCu = 160 * 1024;
+
+// One strip of a row slice: which row and strip, where its values start (row-relative
+// value index), this lane's mask word and the offset of its values in the strip.
+struct Strip {
+    int row, bi;
+    int vb;      // row-relative index of the strip's first value
+    int n;       // values in the strip (sum of the wave's popcounts)
+    uint32_t m;  // this lane's mask word (0 past the slice)
+    int off;     // this lane's first value within the strip
+};
+
+__device__ __forceinline__ uint32_t load_mask(const uint32_t *masks, int row, int KW, int w0, int nws, int base,
+                                              int lane) {
+    const __amdgpu_buffer_rsrc_t rm = make_rsrc(masks + (int64_t)row * KW + w0, (int64_t)nws * 4);
+    return __builtin_amdgcn_raw_buffer_load_b32(rm, (base + lane) * 4, 0, kLoadNT);
+}
+
+// Exclusive prefix sum of v over the wave (lane order) and the wave total, with DPP:
+// shifts by 1, 2, 4, 8 inside each row of 16 lanes (lanes whose source lies outside the
+// row add 0), then lane 15 of rows 0 and 2 added into rows 1 and 3, then lane 31 into
+// rows 2 and 3.
+__device__ __forceinline__ int wave_excl_scan(int v, int lane, int &total) {
+    int incl = v;
+    incl += __builtin_amdgcn_update_dpp(0, incl, 0x111, 0xF, 0xF, true);  // row_shr:1
+    incl += __builtin_amdgcn_update_dpp(0, incl, 0x112, 0xF, 0xF, true);  // row_shr:2
+    incl += __builtin_amdgcn_update_dpp(0, incl, 0x114, 0xF, 0xF, true);  // row_shr:4
+    incl += __builtin_amdgcn_update_dpp(0, incl, 0x118, 0xF, 0xF, true);  // row_shr:8
+    incl += __builtin_amdgcn_update_dpp(0, incl, 0x142, 0xA, 0xF, false);  // row_bcast:15
+    incl += __builtin_amdgcn_update_dpp(0, incl, 0x143, 0xC, 0xF, false);  // row_bcast:31
+    (void)lane;
+    // the total is wave-uniform: keep it in a scalar register (buffer descriptors built
+    // from it stay scalar)
+    total = __builtin_amdgcn_readlane(incl, kWave - 1);
+    return incl - v;
+}
+
+// Issues the loads of a strip's values: [vb, vb + n) of the row's K/2 packed values,
+// from the enclosing 16-byte chunk on; chunk c goes to lane c % 64, load c / 64.  Only
+// the loads that can carry data are issued (the count is wave-uniform); registers of the
+// others are zeroed.
+__device__ __forceinline__ void load_values(u32x4 (&v)[kValLoads], const uint16_t *vrow, int half_k, int vb, int n,
+                                            int lane) {
+    const int a0 = vb & ~7;                                  // first value of the first chunk
+    int end = (vb + n - a0) * 2;                             // bytes needed from a0
+    end = (end + 15) & ~15;
+    const int room = (half_k - a0) * 2;                      // never past the row's values
+    if (end > room) end = room > 0 ? room : 0;
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vrow + a0, end);
+    const int loads = (end / 16 + kWave - 1) / kWave;
+#pragma unroll
+    for (int q = 0; q < kValLoads; ++q)
+        v[q] = q < loads ? __builtin_amdgcn_raw_buffer_load_b128(rv, (q * kWave + lane) * 16, 0, kLoadNT)
+                         : u32x4{0u, 0u, 0u, 0u};
+}
+
+// Value count offset of a row slice starting at word w0: popcount of the row's earlier
+// masks (only for split rows).
+__device__ __forceinline__ int slice_value_base(const uint32_t *masks, int row, int KW, int w0, int lane) {
+    int acc = 0;
+    for (int b = 0; b < w0; b += kWave) {
+        const uint32_t m = load_mask(masks, row, KW, 0, w0, b, lane);
+        acc += __builtin_popcount(m);
+    }
+    int total;
+    wave_excl_scan(acc, lane, total);
+    return total;
+}
+
+template <int B>
+__global__ __launch_bounds__(kUThreads) void spmv_unstructured_kernel(const uint32_t *__restrict__ masks,
+                                                                      const uint16_t *__restrict__ values, int R,
+                                                                      int KW, const uint16_t *__restrict__ x,
+                                                                      int64_t ldx, uint16_t *__restrict__ y,
+                                                                      int64_t ldy, float *__restrict__ partial,
+                                                                      int slice) {
+    constexpr int kBlk = XLayout<B>::kBlk;
+    constexpr int kWaves = kUThreads / kWave;
+    extern __shared__ uint32_t xs[];  // [nws][kBlk] x, then kWaves windows of kWinBytes
+    const int s = blockIdx.y;
+    const int w0 = s * slice;
+    const int nws = min(slice, KW - w0);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int half_k = KW * 16;
+    uint16_t *win = reinterpret_cast<uint16_t *>(
+        reinterpret_cast<uint8_t *>(xs) + (((size_t)nws * kBlk * 4 + 15) & ~(size_t)15) + (size_t)wave * kWinBytes);
+
+    const int first_row = blockIdx.x * kWaves + wave;
+    const int row_step = gridDim.x * kWaves;
+    const int nb = (nws + kWave - 1) / kWave;
+    const int my_rows = first_row < R ? (R - 1 - first_row) / row_step + 1 : 0;
+    const int total = my_rows * nb;
+
+    // Prologue: masks of strip 0 go out with the first round of x loads.
+    uint32_t m_next = 0;
+    stage_x<B, kUThreads>(xs, x, ldx, w0, nws, [&] {
+        if (total > 0) m_next = load_mask(masks, first_row, KW, w0, nws, 0, lane);
+    });
+    __syncthreads();
+    if (total == 0) return;
+
+    Strip cur;
+    u32x4 vals[kValLoads];
+    {
+        cur.row = first_row;
+        cur.bi = 0;
+        cur.vb = w0 > 0 ? slice_value_base(masks, first_row, KW, w0, lane) : 0;
+        cur.m = m_next;
+        cur.off = wave_excl_scan(__builtin_popcount(cur.m), lane, cur.n);
+        load_values(vals, values + (int64_t)cur.row * half_k, half_k, cur.vb, cur.n, lane);
+        if (total > 1) {
+            const int nrow = nb > 1 ? cur.row : cur.row + row_step;
+            m_next = load_mask(masks, nrow, KW, w0, nws, nb > 1 ? kWave : 0, lane);
+        }
+    }
+
+    float acc[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) acc[b] = 0.f;
+    for (int t = 0; t < total; ++t) {
+        // values of strip t: fill the window
+#pragma unroll
+        for (int q = 0; q < kValLoads; ++q) {
+            const int c = q * kWave + lane;
+            if (c < kWinChunks) reinterpret_cast<u32x4 *>(win)[c] = vals[q];
+        }
+        const int shift = cur.vb & 7;  // window element of the strip's first value
+        const uint32_t m_cur = cur.m;
+        const int off_cur = shift + cur.off;
+        const int word = cur.bi * kWave + lane;
+        const uint32_t *blk = xs + (word < nws ? word : 0) * kBlk;
+        const int row_cur = cur.row;
+        const bool row_ends = cur.bi == nb - 1;
+
+        // next strip: its masks are here; scan them and send out its value loads and the
+        // masks of the strip after it
+        if (t + 1 < total) {
+            Strip nx;
+            nx.bi = cur.bi + 1;
+            nx.row = cur.row;
+            nx.vb = cur.vb + cur.n;
+            if (nx.bi == nb) {
+                nx.bi = 0;
+                nx.row += row_step;
+                nx.vb = w0 > 0 ? slice_value_base(masks, nx.row, KW, w0, lane) : 0;
+            }
+            nx.m = m_next;
+            nx.off = wave_excl_scan(__builtin_popcount(nx.m), lane, nx.n);
+            load_values(vals, values + (int64_t)nx.row * half_k, half_k, nx.vb, nx.n, lane);
+            if (t + 2 < total) {
+                int r2 = nx.row, b2 = nx.bi + 1;
+                if (b2 == nb) {
+                    b2 = 0;
+                    r2 += row_step;
+                }
+                m_next = load_mask(masks, r2, KW, w0, nws, b2 * kWave, lane);
+            }
+            cur = nx;
+        }
+        // window writes before the reads of other lanes' chunks (one wave; the fence keeps
+        // the compiler from reordering the LDS accesses across it)
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+
+        // walk strip t: two set bits per step, values from the window
+        uint32_t mm = m_cur;
+        int vi = off_cur;
+        while (__builtin_amdgcn_ballot_w64(mm != 0)) {
+            const bool ok0 = mm != 0;
+            const int c0 = __builtin_ctz(mm) & 31;
+            mm &= mm - 1;
+            const bool ok1 = mm != 0;
+            const int c1 = __builtin_ctz(mm) & 31;
+            mm &= mm - 1;
+            // both window reads are unconditional (index kept inside the window); a lane
+            // past its word's last bit takes zeros instead of what the window holds there
+            const int i0 = min(vi, kWinChunks * 8 - 2);
+            const uint32_t lo = win[i0], hi = win[i0 + 1];
+            const uint32_t pr = (ok0 ? lo : 0u) | ((ok1 ? hi : 0u) << 16);
+            dot_pair<B>(pr, blk, c0, c1, acc);
+            vi += 2;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // reads before the next strip's writes
+
+        if (row_ends) {
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                const float tot = wave_sum(acc[b]);
+                acc[b] = 0.f;
+                if (lane == 0) {
+                    if (gridDim.y == 1)
+                        y[(int64_t)b * ldy + row_cur] = f32_to_bf16_rne(tot);
+                    else
+                        partial[((int64_t)s * B + b) * R + row_cur] = tot;
+                }
+            }
+        }
+    }
+}
+
+template <int B>
+__global__ __launch_bounds__(256) void unstructured_finish_kernel(const float *__restrict__ partial, int S, int R,
+                                                                  uint16_t *__restrict__ y, int64_t ldy) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= R) return;
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+        float t = 0.f;
+        for (int s = 0; s < S; ++s) t += partial[((int64_t)s * B + b) * R + i];
+        y[(int64_t)b * ldy + i] = f32_to_bf16_rne(t);
+    }
+}
+
+template <int B>
+hipError_t launch_u(const MvPlan &p, const uint32_t *masks, const uint16_t *values, int64_t R, int64_t K,
+                    const uint16_t *x, int64_t ldx, uint16_t *y, int64_t ldy, float *ws, hipStream_t st) {
+    if (p.lds_bytes > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute((const void *)spmv_unstructured_kernel<B>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)kULdsCap);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(spmv_unstructured_kernel<B>, dim3(p.grid_x, p.splits), dim3(kUThreads), p.lds_bytes, st,
+                       masks, values, (int)R, (int)(K / 32), x, ldx, y, ldy, ws, p.slice);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.splits == 1) return e;
+    hipLaunchKernelGGL(unstructured_finish_kernel<B>, dim3((unsigned)((R + 255) / 256)), dim3(256), 0, st, ws,
+                       p.splits, (int)R, y, ldy);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+MvPlan plan_spmv_unstructured(int64_t R, int64_t K, int B, const DeviceInfo &dev) {
+    MvPlan p;
+    p.threads = kUThreads;
+    const int64_t KW = K / 32;
+    const int64_t bytes_per_word = (int64_t)spmv_lds_per_word(B);
+    const int64_t windows = (int64_t)(kUThreads / kWave) * kWinBytes;
+    size_t cap = kULdsCap;
+    if (dev.max_lds_per_block > 0 && (size_t)dev.max_lds_per_block < cap) cap = (size_t)dev.max_lds_per_block;
+    int64_t max_slice = ((int64_t)cap - windows - 16) / bytes_per_word;
+    if (max_slice >= kWave) max_slice -= max_slice % kWave;
+    if (max_slice < 1) max_slice = 1;
+    // Same policy as the N:M planner: split only when LDS forces it or rows are few.
+    const int64_t cu = dev.num_cu > 0 ? dev.num_cu : 256;
+    int64_t splits = (KW + max_slice - 1) / max_slice;
+    int64_t by_tasks = R >= cu * 2 ? 1 : (cu * 2 + R - 1) / R;
+    const int64_t max_by_len = KW / kWave > 0 ? KW / kWave : 1;
+    if (by_tasks > max_by_len) by_tasks = max_by_len;
+    if (splits < by_tasks) splits = by_tasks;
+    int64_t slice = (KW + splits - 1) / splits;
+    if (slice > kWave) slice = (slice + kWave - 1) / kWave * kWave;
+    if (slice > max_slice) slice = max_slice;
+    splits = (KW + slice - 1) / slice;
+    p.splits = (int)splits;
+    p.slice = (int)slice;
+    p.lds_bytes = (((size_t)slice * bytes_per_word + 15) & ~(size_t)15) + (size_t)windows;
+    int per_cu = (int)(kULdsPerCu / p.lds_bytes);
+    if (per_cu > 8) per_cu = 8;
+    if (per_cu < 1) per_cu = 1;
+    const int64_t waves = kUThreads / kWave;
+    int64_t gx = (R + waves - 1) / waves;
+    const int64_t cap_x = (per_cu * cu + splits - 1) / splits;
+    if (gx > cap_x) gx = cap_x;
+    if (gx < 1) gx = 1;
+    p.grid_x = (int)gx;
+    p.unroll = 1;
+    p.ws_bytes = splits > 1 ? (size_t)splits * B * R * sizeof(float) : 0;
+    return p;
+}
+
+hipError_t launch_spmv_unstructured(const MvPlan &p, const uint32_t *masks, const uint16_t *values, int64_t R,
+                                    int64_t K, const uint16_t *x, int64_t ldx, int B, uint16_t *y, int64_t ldy,
+                                    float *ws, hipStream_t st) {
+    switch (B) {
+    case 1: return launch_u<1>(p, masks, values, R, K, x, ldx, y, ldy, ws, st);
+    case 2: return launch_u<2>(p, masks, values, R, K, x, ldx, y, ldy, ws, st);
+    case 3: return launch_u<3>(p, masks, values, R, K, x, ldx, y, ldy, ws, st);
+    case 4: return launch_u<4>(p, masks, values, R, K, x, ldx, y, ldy, ws, st);
+    case 5: return launch_u<5>(p, masks, values, R, K, x, ldx, y, ldy, ws, st);
+    case 6: return launch_u<6>(p, masks, values, R, K, x, ldx, y, ldy, ws, st);
+    case 7: return launch_u<7>(p, masks, values, R, K, x, ldx, y, ldy, ws, st);
+    case 8: return launch_u<8>(p, masks, values, R, K, x, ldx, y, ldy, ws, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace nmk

@@ -239,6 +239,37 @@ nm_status nm_spmv_meta(const void *meta, int format, const nm_bf16 *values, int6
                        size_t workspace_bytes, void *hip_stream);
 
 /*
+ * 50% unstructured rows [SD-en, Methodology Steps 3-4: the pages' other 50% setting,
+ * "50% unstructured sparsity", and the case the fixed-step walk does not cover].
+ *
+ * nm_prune_pack_unstructured -- the same Wanda score and tie rule as nm_prune_pack, with
+ * the whole row as the comparison group: row i keeps the K/2 columns that come first
+ * under (score descending, column ascending).  Same encoding: masks uint32 [R][K/32]
+ * (bit b of word w <-> column 32w+b), values bf16 [R][K/2] in increasing column order;
+ * a word may now hold 0..32 set bits, every row exactly K/2.  Alignment: W and col_norm
+ * 16 bytes (ldw % 8 == 0), masks 4, values 2.
+ *
+ * nm_spmv_unstructured -- y[b][i] = sum_j Wsparse[i][j] * x[b][j] for such rows: each
+ * word's set bits are walked lowest first and paired with the row's values in order (the
+ * value offset of a word is the popcount of the row's earlier words).  Same arithmetic,
+ * output rounding, shape/alignment rules and workspace protocol as nm_spmv (workspace:
+ * nm_spmv_unstructured_workspace_bytes).  Requires K/2 set bits per row (not re-checked
+ * on the device; a violating row gives undefined values but no access outside the
+ * row's values).
+ *
+ * nm_unpack_unstructured -- inverse of nm_prune_pack_unstructured (zeros where bits are
+ * clear); W_out bf16 [R][ldw], 16-byte aligned, ldw % 8 == 0.
+ */
+nm_status nm_prune_pack_unstructured(const nm_bf16 *W, int64_t ldw, int64_t R, int64_t K, const float *col_norm,
+                                     uint32_t *masks, nm_bf16 *values, void *hip_stream);
+size_t nm_spmv_unstructured_workspace_bytes(int64_t R, int64_t K, int B);
+nm_status nm_spmv_unstructured(const uint32_t *masks, const nm_bf16 *values, int64_t R, int64_t K, const nm_bf16 *x,
+                               int64_t ldx, int B, nm_bf16 *y, int64_t ldy, void *workspace, size_t workspace_bytes,
+                               void *hip_stream);
+nm_status nm_unpack_unstructured(const uint32_t *masks, const nm_bf16 *values, int64_t R, int64_t K, nm_bf16 *W_out,
+                                 int64_t ldw, void *hip_stream);
+
+/*
  * nm_unpack -- inverse of the packing: W_out[i][j] = kept value of column j, or +0.0
  * where the bit is clear.  W_out: bf16 [R][ldw] (ldw >= K, multiple of 8).
  * Requires R >= 1, K >= 32, K % 32 == 0 and 16 set bits per mask word.

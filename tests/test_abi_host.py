@@ -51,7 +51,9 @@ def test_header_declares_the_expected_entry_points():
               "dense_gemv_workspace_bytes", "nm_unpack", "nm_status_str", "nm_last_error", "nm_version",
               "nm_spmv_multi", "nm_spmv_multi_workspace_bytes", "dense_gemv_multi",
               "dense_gemv_multi_workspace_bytes", "nm_meta_from_mask", "nm_spmv_meta", "nm_spmv_swiglu",
-              "nm_spmv_swiglu_workspace_bytes", "dense_gemv_swiglu", "dense_gemv_swiglu_workspace_bytes"):
+              "nm_spmv_swiglu_workspace_bytes", "dense_gemv_swiglu", "dense_gemv_swiglu_workspace_bytes",
+              "nm_prune_pack_unstructured", "nm_spmv_unstructured", "nm_spmv_unstructured_workspace_bytes",
+              "nm_unpack_unstructured"):
         assert n in names
 
 
@@ -205,3 +207,27 @@ def test_swiglu_entry_points_reject_bad_arguments(L):
     assert L.dense_gemv_swiglu(A16, A4, 64, 4, 64, A16, 64, 1, A16, 4, None, 0, None) == NM_ERR_ALIGN
     assert L.nm_spmv_swiglu_workspace_bytes(0, 64, 1) == 0
     assert L.nm_spmv_swiglu_workspace_bytes(8, 8192, 1) % (4 * 16) == 0
+
+
+def test_unstructured_entry_points_reject_bad_arguments(L):
+    p, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    L.nm_prune_pack_unstructured.argtypes = [p, i64, i64, i64, p, p, p, p]
+    L.nm_spmv_unstructured.argtypes = [p, p, i64, i64, p, i64, i32, p, i64, p, sz, p]
+    L.nm_unpack_unstructured.argtypes = [p, p, i64, i64, p, i64, p]
+    L.nm_spmv_unstructured_workspace_bytes.argtypes = [i64, i64, i32]
+    L.nm_spmv_unstructured_workspace_bytes.restype = sz
+    assert L.nm_prune_pack_unstructured(A16, 64, 4, 64, None, A16, A16, None) == NM_ERR_NULL
+    assert L.nm_prune_pack_unstructured(A16, 64, 4, 48, A16, A16, A16, None) == NM_ERR_SHAPE
+    assert L.nm_prune_pack_unstructured(A16, 60, 4, 64, A16, A16, A16, None) == NM_ERR_SHAPE
+    assert L.nm_prune_pack_unstructured(A4, 64, 4, 64, A16, A16, A16, None) == NM_ERR_ALIGN
+    assert L.nm_prune_pack_unstructured(A16, 64, 4, 64, A4, A16, A16, None) == NM_ERR_ALIGN
+    assert L.nm_spmv_unstructured(None, A16, 4, 64, A16, 64, 1, A16, 4, None, 0, None) == NM_ERR_NULL
+    assert L.nm_spmv_unstructured(A4, A16, 4, 48, A16, 64, 1, A16, 4, None, 0, None) == NM_ERR_SHAPE
+    assert L.nm_spmv_unstructured(A4, A16, 0, 64, A16, 64, 1, A16, 4, None, 0, None) == NM_ERR_SHAPE
+    assert L.nm_spmv_unstructured(A4, A16, 4, 64, A16, 64, 9, A16, 4, None, 0, None) == NM_ERR_SHAPE
+    assert L.nm_spmv_unstructured(A4, A4, 4, 64, A16, 64, 1, A16, 4, None, 0, None) == NM_ERR_ALIGN
+    assert L.nm_spmv_unstructured(A2, A16, 4, 64, A16, 64, 1, A16, 4, None, 0, None) == NM_ERR_ALIGN
+    assert L.nm_unpack_unstructured(A4, A16, 4, 64, None, 64, None) == NM_ERR_NULL
+    assert L.nm_unpack_unstructured(A4, A16, 4, 64, A4, 64, None) == NM_ERR_ALIGN
+    assert L.nm_spmv_unstructured_workspace_bytes(4, 48, 1) == 0
+    assert L.nm_spmv_unstructured_workspace_bytes(16, 8192, 2) % (4 * 16 * 2) == 0
