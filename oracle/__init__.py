@@ -35,6 +35,9 @@ list and the passages each follows:
                     evaluate: Llama-3.1-8B, Llama-3.3-70B, Qwen3), and the error bound a
                     result inherits from the matvec tolerance of g and u
 
+The OBS / SparseGPT N:M solver oracle (Hessian, inverse factor, column-sequential
+selection and compensation) lives in ``oracle/sparsegpt.py`` (plain numpy, fp64).
+
 Pins (tests that tie the oracle to something other than itself) live in
 ``tests/test_oracle_pins.py``; every function above has at least one.
 """
