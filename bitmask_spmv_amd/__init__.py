@@ -25,7 +25,8 @@ __all__ = [
     "dense_gemv_multi_workspace_bytes", "NM_META_BITMASK", "NM_META_U8_OFFSET", "NM_META_I32_INDEX",
     "nm_meta_from_mask", "nm_spmv_meta", "nm_spmv_swiglu", "nm_spmv_swiglu_workspace_bytes", "dense_gemv_swiglu",
     "dense_gemv_swiglu_workspace_bytes", "nm_prune_pack_unstructured", "nm_spmv_unstructured",
-    "nm_spmv_unstructured_workspace_bytes", "nm_unpack_unstructured",
+    "nm_spmv_unstructured_workspace_bytes", "nm_unpack_unstructured", "nm_hessian", "nm_obs_inverse_factor",
+    "nm_obs_inverse_factor_workspace_bytes", "nm_sparsegpt_prune_pack", "nm_sparsegpt_workspace_bytes",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnmspmv.so")
@@ -70,6 +71,14 @@ def _load() -> ctypes.CDLL:
     L.dense_gemv.argtypes = [p, i64, i64, i64, p, i64, i32, p, i64, p, sz, p]
     L.nm_unpack.argtypes = [p, p, i64, i64, p, i64, p]
     L.nm_meta_from_mask.argtypes = [p, i64, i64, i32, p, p]
+    f64 = ctypes.c_double
+    L.nm_hessian.argtypes = [p, i64, i64, i64, p, i64, p]
+    L.nm_obs_inverse_factor_workspace_bytes.argtypes = [i64]
+    L.nm_obs_inverse_factor_workspace_bytes.restype = sz
+    L.nm_obs_inverse_factor.argtypes = [p, i64, i64, f64, p, i64, p, sz, p]
+    L.nm_sparsegpt_workspace_bytes.argtypes = [i64, i64]
+    L.nm_sparsegpt_workspace_bytes.restype = sz
+    L.nm_sparsegpt_prune_pack.argtypes = [p, i64, i64, i64, p, i64, i32, i32, f64, p, p, p, sz, p]
     L.nm_prune_pack_unstructured.argtypes = [p, i64, i64, i64, p, p, p, p]
     L.nm_spmv_unstructured_workspace_bytes.argtypes = [i64, i64, i32]
     L.nm_spmv_unstructured_workspace_bytes.restype = sz
@@ -384,6 +393,64 @@ def nm_unpack_unstructured(masks: torch.Tensor, values: torch.Tensor, out: torch
     _dev(out, "out", torch.bfloat16, 2)
     _check(lib.nm_unpack_unstructured(_ptr(masks), _ptr(values), R, K, _ptr(out), _ld(out), _stream(masks)))
     return out
+
+
+def nm_hessian(X: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """H = 2 X^T X: X bf16 [T, K] calibration activations -> fp64 [K, K]."""
+    _dev(X, "X", torch.bfloat16, 2)
+    T, K = X.shape
+    if out is None:
+        out = torch.empty((K, K), dtype=torch.float64, device=X.device)
+    _dev(out, "out", torch.float64, 2)
+    if out.shape != (K, K):
+        raise ValueError("out must be [K, K]")
+    _check(lib.nm_hessian(_ptr(X), T, K, _ld(X), _ptr(out), _ld(out), _stream(X)))
+    return out
+
+
+def nm_obs_inverse_factor_workspace_bytes(K: int) -> int:
+    return int(lib.nm_obs_inverse_factor_workspace_bytes(K))
+
+
+def nm_obs_inverse_factor(H: torch.Tensor, damp: float = 0.01, out: torch.Tensor | None = None,
+                          workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Upper U with U^T U = (H + damp * mean(diag H) * I)^-1 (fp64 [K, K])."""
+    _dev(H, "H", torch.float64, 2)
+    K = H.shape[0]
+    if H.shape != (K, K):
+        raise ValueError("H must be square")
+    if out is None:
+        out = torch.empty((K, K), dtype=torch.float64, device=H.device)
+    _dev(out, "out", torch.float64, 2)
+    ws, ws_bytes = _workspace(nm_obs_inverse_factor_workspace_bytes(K), H, workspace)
+    _check(lib.nm_obs_inverse_factor(_ptr(H), _ld(H), K, float(damp), _ptr(out), _ld(out), _ptr(ws), ws_bytes,
+                                     _stream(H)))
+    return out
+
+
+def nm_sparsegpt_workspace_bytes(R: int, K: int) -> int:
+    return int(lib.nm_sparsegpt_workspace_bytes(R, K))
+
+
+def nm_sparsegpt_prune_pack(W: torch.Tensor, H: torch.Tensor, N: int, M: int, damp: float = 0.01,
+                            masks: torch.Tensor | None = None, values: torch.Tensor | None = None,
+                            workspace: torch.Tensor | None = None):
+    """OBS / SparseGPT N:M solver: W bf16 [R, K], H fp64 [K, K] -> (masks int32 [R, K/32], values bf16 [R, K/2])."""
+    _dev(W, "W", torch.bfloat16, 2)
+    _dev(H, "H", torch.float64, 2)
+    R, K = W.shape
+    if H.shape != (K, K):
+        raise ValueError("H must be [K, K]")
+    if masks is None:
+        masks = torch.empty((R, max(K // 32, 1)), dtype=torch.int32, device=W.device)
+    if values is None:
+        values = torch.empty((R, max(K // 2, 1)), dtype=torch.bfloat16, device=W.device)
+    _dev(masks, "masks", torch.int32, 2)
+    _dev(values, "values", torch.bfloat16, 2)
+    ws, ws_bytes = _workspace(nm_sparsegpt_workspace_bytes(R, K), W, workspace)
+    _check(lib.nm_sparsegpt_prune_pack(_ptr(W), _ld(W), R, K, _ptr(H), _ld(H), int(N), int(M), float(damp),
+                                       _ptr(masks), _ptr(values), _ptr(ws), ws_bytes, _stream(W)))
+    return masks, values
 
 
 def _multi_outs(x2, Rs, outs):

@@ -427,6 +427,94 @@ nm_status nm_unpack_unstructured(const uint32_t *masks, const nm_bf16 *values, i
     }
 }
 
+// ---------------------------------------------------------------- OBS / SparseGPT solver
+constexpr int64_t kMaxSolverK = 65536;
+
+nm_status nm_hessian(const nm_bf16 *X, int64_t T, int64_t K, int64_t ldx, double *H, int64_t ldh, void *hip_stream) {
+    try {
+        g_err[0] = 0;
+        if (!X || !H) return fail(NM_ERR_NULL, "nm_hessian: NULL pointer");
+        if (T < 1 || T > kMaxDim || K < 1 || K > kMaxSolverK || ldx < K || ldh < K)
+            return fail(NM_ERR_SHAPE, "nm_hessian: bad sizes T=%lld K=%lld ldx=%lld ldh=%lld", (long long)T,
+                        (long long)K, (long long)ldx, (long long)ldh);
+        if (!aligned(X, 2) || !aligned(H, 8)) return fail(NM_ERR_ALIGN, "nm_hessian: misaligned pointer");
+        hipError_t e = nmk::launch_hessian(X, T, K, ldx, H, ldh, (hipStream_t)hip_stream);
+        if (e != hipSuccess) return hip_fail("nm_hessian launch", e);
+        return NM_OK;
+    } catch (...) {
+        return fail(NM_ERR_HIP, "nm_hessian: internal error");
+    }
+}
+
+size_t nm_obs_inverse_factor_workspace_bytes(int64_t K) {
+    if (K < 32 || K % 32 != 0 || K > kMaxSolverK) return 0;
+    return nmk::sparsegpt_factor_workspace(K);
+}
+
+static nm_status check_solver_h(const double *H, int64_t ldh, int64_t K, double damp, const char *who) {
+    if (!H) return fail(NM_ERR_NULL, "%s: NULL H", who);
+    if (K < 32 || K % 32 != 0 || K > kMaxSolverK || ldh < K)
+        return fail(NM_ERR_SHAPE, "%s: K=%lld must be a multiple of 32 in [32, 65536], ldh >= K", who, (long long)K);
+    if (!(damp >= 0.0) || damp > 1e30) return fail(NM_ERR_SHAPE, "%s: damp must be finite and >= 0", who);
+    if (!aligned(H, 8)) return fail(NM_ERR_ALIGN, "%s: H needs 8-byte alignment", who);
+    return NM_OK;
+}
+
+nm_status nm_obs_inverse_factor(const double *H, int64_t ldh, int64_t K, double damp, double *U, int64_t ldu,
+                                void *workspace, size_t workspace_bytes, void *hip_stream) {
+    try {
+        g_err[0] = 0;
+        const char *who = "nm_obs_inverse_factor";
+        nm_status st = check_solver_h(H, ldh, K, damp, who);
+        if (st != NM_OK) return st;
+        if (!U) return fail(NM_ERR_NULL, "%s: NULL U", who);
+        if (ldu < K) return fail(NM_ERR_SHAPE, "%s: ldu < K", who);
+        if (!aligned(U, 8)) return fail(NM_ERR_ALIGN, "%s: U needs 8-byte alignment", who);
+        const size_t need = nmk::sparsegpt_factor_workspace(K);
+        if (!workspace || workspace_bytes < need || !aligned(workspace, 8))
+            return fail(NM_ERR_WORKSPACE, "%s: workspace of %zu bytes required, %zu given", who, need,
+                        workspace ? workspace_bytes : (size_t)0);
+        hipError_t e = nmk::launch_inverse_factor(H, ldh, K, damp, U, ldu, workspace, (hipStream_t)hip_stream);
+        if (e != hipSuccess) return hip_fail(who, e);
+        return NM_OK;
+    } catch (...) {
+        return fail(NM_ERR_HIP, "nm_obs_inverse_factor: internal error");
+    }
+}
+
+size_t nm_sparsegpt_workspace_bytes(int64_t R, int64_t K) {
+    if (R < 1 || R > kMaxDim || K < 32 || K % 32 != 0 || K > kMaxSolverK) return 0;
+    return nmk::sparsegpt_workspace(R, K);
+}
+
+nm_status nm_sparsegpt_prune_pack(const nm_bf16 *W, int64_t ldw, int64_t R, int64_t K, const double *H, int64_t ldh,
+                                  int N, int M, double damp, uint32_t *masks, nm_bf16 *values, void *workspace,
+                                  size_t workspace_bytes, void *hip_stream) {
+    try {
+        g_err[0] = 0;
+        const char *who = "nm_sparsegpt_prune_pack";
+        if (!W || !masks || !values) return fail(NM_ERR_NULL, "%s: NULL pointer", who);
+        if (!(M == 4 || M == 8 || M == 16 || M == 32) || 2 * N != M)
+            return fail(NM_ERR_PATTERN, "%s: %d:%d is not a 50%% pattern with M in {4,8,16,32}", who, N, M);
+        nm_status st = check_solver_h(H, ldh, K, damp, who);
+        if (st != NM_OK) return st;
+        if (R < 1 || R > kMaxDim || ldw < K) return fail(NM_ERR_SHAPE, "%s: bad sizes R=%lld ldw=%lld", who,
+                                                         (long long)R, (long long)ldw);
+        if (!aligned(W, 2) || !aligned(masks, 4) || !aligned(values, 16))
+            return fail(NM_ERR_ALIGN, "%s: W 2-byte, masks 4-byte and values 16-byte alignment required", who);
+        const size_t need = nmk::sparsegpt_workspace(R, K);
+        if (!workspace || workspace_bytes < need || !aligned(workspace, 8))
+            return fail(NM_ERR_WORKSPACE, "%s: workspace of %zu bytes required, %zu given", who, need,
+                        workspace ? workspace_bytes : (size_t)0);
+        hipError_t e = nmk::launch_sparsegpt(W, ldw, R, K, H, ldh, N, M, damp, masks, values, workspace,
+                                             (hipStream_t)hip_stream);
+        if (e != hipSuccess) return hip_fail(who, e);
+        return NM_OK;
+    } catch (...) {
+        return fail(NM_ERR_HIP, "nm_sparsegpt_prune_pack: internal error");
+    }
+}
+
 size_t dense_gemv_workspace_bytes(int64_t R, int64_t K, int B) {
     if (R < 1 || R > kMaxDim || K < 8 || K % 8 != 0 || K > kMaxDim || B < 1 || B > 8) return 0;
     return dense_plan(R, K, B).ws_bytes;

@@ -75,6 +75,15 @@ MvPlan plan_spmv_unstructured(int64_t R, int64_t K, int B, const DeviceInfo &dev
 hipError_t launch_spmv_unstructured(const MvPlan &p, const uint32_t *masks, const uint16_t *values, int64_t R,
                                     int64_t K, const uint16_t *x, int64_t ldx, int B, uint16_t *y, int64_t ldy,
                                     float *ws, hipStream_t st);
+// OBS / SparseGPT solver (fp64).  Workspace sizes in bytes.
+size_t sparsegpt_factor_workspace(int64_t K);
+size_t sparsegpt_workspace(int64_t R, int64_t K);
+hipError_t launch_hessian(const uint16_t *X, int64_t T, int64_t K, int64_t ldx, double *H, int64_t ldh,
+                          hipStream_t st);
+hipError_t launch_inverse_factor(const double *H, int64_t ldh, int64_t K, double damp, double *U, int64_t ldu,
+                                 void *ws, hipStream_t st);
+hipError_t launch_sparsegpt(const uint16_t *W, int64_t ldw, int64_t R, int64_t K, const double *H, int64_t ldh,
+                            int N, int M, double damp, uint32_t *masks, uint16_t *values, void *ws, hipStream_t st);
 hipError_t launch_meta_from_mask(const uint32_t *masks, int64_t R, int64_t K, int fmt, void *meta, hipStream_t st);
 // R of the plan = total rows of the set (set.row0[set.P]).
 hipError_t launch_spmv(const MvPlan &p, const SpmvSet &set, int fmt, int64_t K, const uint16_t *x, int64_t ldx,

@@ -270,6 +270,43 @@ nm_status nm_unpack_unstructured(const uint32_t *masks, const nm_bf16 *values, i
                                  int64_t ldw, void *hip_stream);
 
 /*
+ * OBS / SparseGPT N:M solver [SD-cn, 前置知识 (训练后剪枝与OBS框架) and 方法步骤详情 第二步:
+ * H = 2 X X^T, saliency w_q^2 / (2 [H^-1]_qq), compensation
+ * delta_w = -(w_q / [H^-1]_qq) H^-1_{:,q}; SD-en, Methodology Step 1].  All in fp64.
+ *
+ * nm_hessian -- H = 2 X^T X for calibration activations X: bf16 [T][ldx] (tokens by the
+ * K input channels, the layout nm_col_norm takes); H: fp64 [K][ldh], full symmetric
+ * matrix.  Requires 1 <= T <= 2^30, 1 <= K <= 65536, ldx >= K, ldh >= K.
+ *
+ * nm_obs_inverse_factor -- U: fp64 [K][ldu], upper triangular with positive diagonal and
+ * U^T U = (H + lambda I)^-1, lambda = damp * mean(diag H) (entries below the diagonal
+ * are written as 0).  U[i][i]^2 is the inverse-Hessian entry of column i among the
+ * columns i.. (the quantity the column-sequential solver needs).  Requires K a multiple
+ * of 32 in [32, 65536], damp >= 0, H + lambda I positive definite (otherwise the
+ * results are NaN; nothing faults).  Workspace: nm_obs_inverse_factor_workspace_bytes(K)
+ * (about 16 K^2 bytes), 8-byte aligned.
+ *
+ * nm_sparsegpt_prune_pack -- the column-sequential solver (SparseGPT's schedule): columns
+ * are fixed left to right; at the first column of each group of M, every row keeps the
+ * N columns of largest w^2 / U[c][c]^2 (current, already compensated weights; ties keep
+ * the lower column); a pruned weight moves the later columns of its row by
+ * -(w / U[c][c]) * U[c][c+1:].  Output in the nm_prune_pack format (masks uint32
+ * [R][K/32], values bf16 [R][K/2] in increasing column order), the kept weights being
+ * the compensated ones rounded once to bf16 (nearest even).  W: bf16 [R][ldw] (not
+ * modified); H as for nm_obs_inverse_factor.  Only 50% patterns (N = M/2, M in
+ * {4, 8, 16, 32}).  Workspace: nm_sparsegpt_workspace_bytes(R, K) (about 16 K^2 + 8 R K
+ * bytes), 8-byte aligned; values 16-byte aligned.
+ */
+nm_status nm_hessian(const nm_bf16 *X, int64_t T, int64_t K, int64_t ldx, double *H, int64_t ldh, void *hip_stream);
+size_t nm_obs_inverse_factor_workspace_bytes(int64_t K);
+nm_status nm_obs_inverse_factor(const double *H, int64_t ldh, int64_t K, double damp, double *U, int64_t ldu,
+                                void *workspace, size_t workspace_bytes, void *hip_stream);
+size_t nm_sparsegpt_workspace_bytes(int64_t R, int64_t K);
+nm_status nm_sparsegpt_prune_pack(const nm_bf16 *W, int64_t ldw, int64_t R, int64_t K, const double *H, int64_t ldh,
+                                  int N, int M, double damp, uint32_t *masks, nm_bf16 *values, void *workspace,
+                                  size_t workspace_bytes, void *hip_stream);
+
+/*
  * nm_unpack -- inverse of the packing: W_out[i][j] = kept value of column j, or +0.0
  * where the bit is clear.  W_out: bf16 [R][ldw] (ldw >= K, multiple of 8).
  * Requires R >= 1, K >= 32, K % 32 == 0 and 16 set bits per mask word.

@@ -53,7 +53,8 @@ def test_header_declares_the_expected_entry_points():
               "dense_gemv_multi_workspace_bytes", "nm_meta_from_mask", "nm_spmv_meta", "nm_spmv_swiglu",
               "nm_spmv_swiglu_workspace_bytes", "dense_gemv_swiglu", "dense_gemv_swiglu_workspace_bytes",
               "nm_prune_pack_unstructured", "nm_spmv_unstructured", "nm_spmv_unstructured_workspace_bytes",
-              "nm_unpack_unstructured"):
+              "nm_unpack_unstructured", "nm_hessian", "nm_obs_inverse_factor",
+              "nm_obs_inverse_factor_workspace_bytes", "nm_sparsegpt_prune_pack", "nm_sparsegpt_workspace_bytes"):
         assert n in names
 
 
@@ -231,3 +232,35 @@ def test_unstructured_entry_points_reject_bad_arguments(L):
     assert L.nm_unpack_unstructured(A4, A16, 4, 64, A4, 64, None) == NM_ERR_ALIGN
     assert L.nm_spmv_unstructured_workspace_bytes(4, 48, 1) == 0
     assert L.nm_spmv_unstructured_workspace_bytes(16, 8192, 2) % (4 * 16 * 2) == 0
+
+
+def test_solver_entry_points_reject_bad_arguments(L):
+    p, i64, i32, sz, f64 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t, ctypes.c_double
+    L.nm_hessian.argtypes = [p, i64, i64, i64, p, i64, p]
+    L.nm_obs_inverse_factor.argtypes = [p, i64, i64, f64, p, i64, p, sz, p]
+    L.nm_obs_inverse_factor_workspace_bytes.argtypes = [i64]
+    L.nm_obs_inverse_factor_workspace_bytes.restype = sz
+    L.nm_sparsegpt_workspace_bytes.argtypes = [i64, i64]
+    L.nm_sparsegpt_workspace_bytes.restype = sz
+    L.nm_sparsegpt_prune_pack.argtypes = [p, i64, i64, i64, p, i64, i32, i32, f64, p, p, p, sz, p]
+    assert L.nm_hessian(None, 4, 64, 64, A16, 64, None) == NM_ERR_NULL
+    assert L.nm_hessian(A16, 0, 64, 64, A16, 64, None) == NM_ERR_SHAPE
+    assert L.nm_hessian(A16, 4, 64, 32, A16, 64, None) == NM_ERR_SHAPE
+    assert L.nm_hessian(A16, 4, 64, 64, A16, 63, None) == NM_ERR_SHAPE
+    assert L.nm_hessian(A16, 4, 64, 64, A4, 64, None) == NM_ERR_ALIGN
+    assert L.nm_obs_inverse_factor_workspace_bytes(48) == 0
+    wsb = L.nm_obs_inverse_factor_workspace_bytes(64)
+    assert wsb >= 2 * 64 * 64 * 8
+    assert L.nm_obs_inverse_factor(A16, 64, 48, 0.01, A16, 64, A16, wsb, None) == NM_ERR_SHAPE
+    assert L.nm_obs_inverse_factor(A16, 64, 64, -1.0, A16, 64, A16, wsb, None) == NM_ERR_SHAPE
+    assert L.nm_obs_inverse_factor(A16, 64, 64, float("nan"), A16, 64, A16, wsb, None) == NM_ERR_SHAPE
+    assert L.nm_obs_inverse_factor(A16, 64, 64, 0.01, None, 64, A16, wsb, None) == NM_ERR_NULL
+    assert L.nm_obs_inverse_factor(A16, 64, 64, 0.01, A16, 64, A16, wsb - 8, None) == NM_ERR_WORKSPACE
+    assert L.nm_obs_inverse_factor(A4, 64, 64, 0.01, A16, 64, A16, wsb, None) == NM_ERR_ALIGN
+    swb = L.nm_sparsegpt_workspace_bytes(8, 64)
+    assert swb >= wsb + 8 * 64 * 8
+    assert L.nm_sparsegpt_prune_pack(A16, 64, 8, 64, A16, 64, 3, 4, 0.01, A16, A16, A16, swb, None) == NM_ERR_PATTERN
+    assert L.nm_sparsegpt_prune_pack(A16, 64, 8, 48, A16, 64, 2, 4, 0.01, A16, A16, A16, swb, None) == NM_ERR_SHAPE
+    assert L.nm_sparsegpt_prune_pack(A16, 64, 8, 64, A16, 64, 2, 4, 0.01, A16, A4, A16, swb, None) == NM_ERR_ALIGN
+    assert L.nm_sparsegpt_prune_pack(A16, 64, 8, 64, A16, 64, 2, 4, 0.01, A16, A16, None, 0, None) == NM_ERR_WORKSPACE
+    assert L.nm_sparsegpt_prune_pack(None, 64, 8, 64, A16, 64, 2, 4, 0.01, A16, A16, A16, swb, None) == NM_ERR_NULL
