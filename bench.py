@@ -39,6 +39,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+FP64_MFMA_PEAK_TFLOPS = 78.6
 ROTATE_BYTES = 512e6
 METRIC = "nm_spmv GB/s and % HBM peak per layer; speedup vs dense bf16 GEMV, batch 1"
 
@@ -119,6 +120,8 @@ def parse():
     ap.add_argument("--skip-check", action="store_true", help="skip the oracle spot check")
     ap.add_argument("--no-meta-formats", action="store_true",
                     help="skip the bitmask vs uint8-offset vs int32-index comparison table")
+    ap.add_argument("--no-solver", action="store_true", help="skip the OBS / SparseGPT solver measurement")
+    ap.add_argument("--solver-tokens", type=int, default=4096, help="calibration tokens for the solver")
     ap.add_argument("--no-unstructured", action="store_true",
                     help="skip the 50%% unstructured vs N:M comparison table")
     ap.add_argument("--profile-kernel", action="store_true",
@@ -533,6 +536,57 @@ def main():
         log("unstructured 50% (us): " + "; ".join(f"{n} {d['us']} (N:M {d[f'nm_{N}:{M}_us']}, dense "
                                                    f"x{d['speedup_vs_dense']})" for n, d in unstructured.items()))
 
+    # ---------------------------------------------------------------- OBS / SparseGPT solver
+    # Offline: the Hessian of T synthetic calibration tokens (fp64 MFMA), the damped
+    # inverse factor and the column-sequential N:M solve of the largest MLP projection;
+    # quality as the relative reconstruction error on the calibration tokens, against
+    # the Wanda selection of the same weights.
+    solver = None
+    if not args.no_solver:
+        name_s, R_s, K_s, _ = max(projs, key=lambda p: p[1] * p[2])
+        T_s = args.solver_tokens
+        (N, M) = patterns[0]
+        W_s = synth.device_weights(R_s, K_s, args.seed, 600)
+        X_s = synth.device_calib_acts(K_s, args.seed, 601, T=T_s)
+
+        def timed(fn, reps=1):
+            fn()
+            torch.cuda.synchronize()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record()
+            for _ in range(reps):
+                out = fn()
+            ev[1].record()
+            torch.cuda.synchronize()
+            return ev[0].elapsed_time(ev[1]) / reps, out
+
+        h_ms, H_s = timed(lambda: nm.nm_hessian(X_s), reps=5)
+        f_ms, _ = timed(lambda: nm.nm_obs_inverse_factor(H_s, 0.01))
+        sg_ms, (m_s, v_s) = timed(lambda: nm.nm_sparsegpt_prune_pack(W_s, H_s, N, M, 0.01))
+        n_s = nm.nm_col_norm(X_s)
+        mw, vw = nm.nm_prune_pack(W_s, n_s, N, M)
+
+        def rel_err(mk, vl):
+            Wp = nm.nm_unpack(mk, vl).float()
+            Wf = W_s.float()
+            Xf = X_s.float()
+            num = ((Wf - Wp) @ Xf.T).pow(2).sum()
+            den = (Wf @ Xf.T).pow(2).sum()
+            return float(num / den)
+
+        flops = 2.0 * K_s * K_s * T_s
+        solver = {"shape": f"{name_s} {R_s}x{K_s}", "pattern": f"{N}:{M}", "tokens": T_s,
+                  "hessian_ms": round(h_ms, 3), "hessian_TFLOPs": round(flops / h_ms / 1e9, 2),
+                  "hessian_frac_fp64_mfma_peak": round(flops / h_ms / 1e9 / FP64_MFMA_PEAK_TFLOPS, 4),
+                  "inverse_factor_ms": round(f_ms, 2), "prune_pack_ms": round(sg_ms, 2),
+                  "rel_recon_error": {"wanda": rel_err(mw, vw), "sparsegpt": rel_err(m_s, v_s)}}
+        log(f"solver on {solver['shape']} {N}:{M}, {T_s} tokens: hessian {h_ms:.2f} ms "
+            f"({solver['hessian_TFLOPs']} TFLOP/s fp64), inverse factor {f_ms:.1f} ms, solve+pack {sg_ms:.1f} ms; "
+            f"rel. error wanda {solver['rel_recon_error']['wanda']:.4f} vs sparsegpt "
+            f"{solver['rel_recon_error']['sparsegpt']:.4f}")
+        del W_s, X_s, H_s, m_s, v_s, mw, vw
+        torch.cuda.synchronize()
+
     # Dominant kernel: the launch of the (fused) step whose launches take the largest share
     # of it; its algorithmic bytes over its average launch time is the roofline's achieved.
     share = {}
@@ -615,6 +669,7 @@ def main():
         "per_layer": per,
         "metadata_formats": meta_table,
         "unstructured_50": unstructured,
+        "solver": solver,
         "pack_GBs": round(pack_bytes / pack_ms / 1e6, 1),
         "parity": parity,
         "roofline": roofline,
@@ -746,8 +801,11 @@ def summarize_trace(d):
     for f in files:
         for r in csv.DictReader(open(f)):
             kn = r["Kernel_Name"]
-            short = kn.replace("void nmk::(anonymous namespace)::", "").split("(")[0] if "nmk::" in kn else \
-                "torch/other: " + kn[:40]
+            if "nmk::" in kn:
+                short = kn.replace("void ", "", 1) if kn.startswith("void ") else kn
+                short = short.replace("nmk::(anonymous namespace)::", "").split("(")[0]
+            else:
+                short = "torch/other: " + kn[:40]
             wg = int(r["Workgroup_Size_X"]) * int(r.get("Workgroup_Size_Y", 1) or 1)
             grid = (int(r["Grid_Size_X"]) * int(r.get("Grid_Size_Y", 1) or 1)) // max(wg, 1)
             groups.setdefault((short, grid), []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
@@ -759,11 +817,12 @@ def summarize_trace(d):
 
 
 def kernel_fingerprint() -> str:
-    """Hash of the SpMV kernel source: counters recorded for an older kernel are not reused."""
+    """Hash of the SpMV kernel source (kernel, shared staging/dot helpers, device helpers):
+    counters recorded for an older kernel are not reused."""
     import hashlib
 
     h = hashlib.sha256()
-    for f in ("nm_spmv.hip", "nm_device.h"):
+    for f in ("nm_spmv.hip", "nm_spmv_common.h", "nm_device.h"):
         with open(os.path.join(ROOT, "bitmask_spmv_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

@@ -118,4 +118,9 @@ constexpr int kEpiSwiGLU = 1;
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.f + __expf(-g)) * u; }
 
+// Position of the lowest set bit of m, and 31 when m has no bit set.  (__builtin_ctz is
+// undefined for 0, so a "& 31" applied to it may be folded away and the hardware's
+// bit scan then yields -1; or-ing in bit 31 keeps every result a valid column.)
+__device__ __forceinline__ int low_bit(uint32_t m) { return __builtin_ctz(m | 0x80000000u); }
+
 }  // namespace nmk

@@ -94,11 +94,11 @@ __global__ __launch_bounds__(kPackThreads) void prune_pack_kernel(const uint16_t
     uint32_t mm = mask;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-        // "& 31" keeps every access inside the word even for out-of-contract
+        // low_bit keeps every access inside the word even for out-of-contract
         // (non-finite) inputs that could leave fewer than 16 bits set.
-        const int c0 = __builtin_ctz(mm) & 31;
+        const int c0 = low_bit(mm);
         mm &= mm - 1;
-        const int c1 = __builtin_ctz(mm) & 31;
+        const int c1 = low_bit(mm);
         mm &= mm - 1;
         out[t] = (uint32_t)wrow[c0] | ((uint32_t)wrow[c1] << 16);
     }
@@ -127,9 +127,9 @@ __global__ __launch_bounds__(kPackThreads) void unpack_kernel(const uint32_t *__
     uint32_t mm = masks[gid];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-        const int c0 = __builtin_ctz(mm) & 31;  // stays in this thread's slot for corrupt masks
+        const int c0 = low_bit(mm);  // stays in this thread's slot for corrupt masks
         mm &= mm - 1;
-        const int c1 = __builtin_ctz(mm) & 31;
+        const int c1 = low_bit(mm);
         mm &= mm - 1;
         mine16[c0] = (uint16_t)(vv[t] & 0xFFFFu);
         mine16[c1] = (uint16_t)(vv[t] >> 16);
@@ -153,7 +153,7 @@ __global__ __launch_bounds__(kPackThreads) void meta_from_mask_kernel(const uint
     uint32_t c[16];
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
-        c[t] = (uint32_t)__builtin_ctz(mm) & 31u;  // a corrupt mask (< 16 bits) yields 31s
+        c[t] = (uint32_t)low_bit(mm);  // a corrupt mask (< 16 bits) yields 31s
         mm &= mm - 1;
     }
     if constexpr (FMT == kMetaU8) {

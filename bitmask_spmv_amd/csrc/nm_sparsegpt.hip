@@ -400,9 +400,9 @@ __global__ __launch_bounds__(kBlkThreads) void sgpt_block_kernel(const double *_
     uint32_t mm = keep;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-        const int ca = __builtin_ctz(mm) & 31;  // "& 31": stays in the slot for any mask
+        const int ca = low_bit(mm);  // stays in the slot for any mask
         mm &= mm - 1;
-        const int cb = __builtin_ctz(mm) & 31;
+        const int cb = low_bit(mm);
         mm &= mm - 1;
         out[t] = (uint32_t)f64_to_bf16_rne(w[ca]) | ((uint32_t)f64_to_bf16_rne(w[cb]) << 16);
     }

@@ -38,16 +38,6 @@ constexpr int kValLoads = (kWinChunks + kWave - 1) / kWave;  // 16-byte loads pe
 constexpr size_t kULdsCap = 80 * 1024;
 constexpr size_t kULdsPerCu = 160 * 1024;
 
-// One strip of a row slice: which row and strip, where its values start (row-relative
-// value index), this lane's mask word and the offset of its values in the strip.
-struct Strip {
-    int row, bi;
-    int vb;      // row-relative index of the strip's first value
-    int n;       // values in the strip (sum of the wave's popcounts)
-    uint32_t m;  // this lane's mask word (0 past the slice)
-    int off;     // this lane's first value within the strip
-};
-
 __device__ __forceinline__ uint32_t load_mask(const uint32_t *masks, int row, int KW, int w0, int nws, int base,
                                               int lane) {
     const __amdgpu_buffer_rsrc_t rm = make_rsrc(masks + (int64_t)row * KW + w0, (int64_t)nws * 4);
@@ -131,87 +121,81 @@ __global__ __launch_bounds__(kUThreads) void spmv_unstructured_kernel(const uint
     const int total = my_rows * nb;
 
     // Prologue: masks of strip 0 go out with the first round of x loads.
-    uint32_t m_next = 0;
+    uint32_t mA = 0, mB = 0;  // masks of the strips in turn (no register copies of loads)
     stage_x<B, kUThreads>(xs, x, ldx, w0, nws, [&] {
-        if (total > 0) m_next = load_mask(masks, first_row, KW, w0, nws, 0, lane);
+        if (total > 0) mA = load_mask(masks, first_row, KW, w0, nws, 0, lane);
     });
     __syncthreads();
     if (total == 0) return;
 
-    Strip cur;
+    // Strip bookkeeping: scalar (row, strip, value base, count) plus this lane's offset.
+    int row = first_row, bi = 0, vb = 0, n = 0, off = 0;
     u32x4 vals[kValLoads];
-    {
-        cur.row = first_row;
-        cur.bi = 0;
-        cur.vb = w0 > 0 ? slice_value_base(masks, first_row, KW, w0, lane) : 0;
-        cur.m = m_next;
-        cur.off = wave_excl_scan(__builtin_popcount(cur.m), lane, cur.n);
-        load_values(vals, values + (int64_t)cur.row * half_k, half_k, cur.vb, cur.n, lane);
-        if (total > 1) {
-            const int nrow = nb > 1 ? cur.row : cur.row + row_step;
-            m_next = load_mask(masks, nrow, KW, w0, nws, nb > 1 ? kWave : 0, lane);
-        }
-    }
+    vb = w0 > 0 ? slice_value_base(masks, row, KW, w0, lane) : 0;
+    off = wave_excl_scan(__builtin_popcount(mA), lane, n);
+    load_values(vals, values + (int64_t)row * half_k, half_k, vb, n, lane);
+    if (total > 1) mB = load_mask(masks, nb > 1 ? row : row + row_step, KW, w0, nws, nb > 1 ? kWave : 0, lane);
 
     float acc[B];
 #pragma unroll
     for (int b = 0; b < B; ++b) acc[b] = 0.f;
-    for (int t = 0; t < total; ++t) {
+
+    // One strip: m_this holds its mask (arrived), m_other the next strip's (in flight).
+    // The walk works on a copy of m_this, so m_this can take the masks of the strip
+    // after next before the walk starts.
+    auto step = [&](uint32_t &m_this, uint32_t &m_other, int t) {
         // values of strip t: fill the window
 #pragma unroll
         for (int q = 0; q < kValLoads; ++q) {
             const int c = q * kWave + lane;
             if (c < kWinChunks) reinterpret_cast<u32x4 *>(win)[c] = vals[q];
         }
-        const int shift = cur.vb & 7;  // window element of the strip's first value
-        const uint32_t m_cur = cur.m;
-        const int off_cur = shift + cur.off;
-        const int word = cur.bi * kWave + lane;
+        const uint32_t m_walk = m_this;
+        const int vi0 = (vb & 7) + off;  // window element of this lane's first value
+        const int word = bi * kWave + lane;
         const uint32_t *blk = xs + (word < nws ? word : 0) * kBlk;
-        const int row_cur = cur.row;
-        const bool row_ends = cur.bi == nb - 1;
+        const int row_cur = row;
+        const bool row_ends = bi == nb - 1;
 
-        // next strip: its masks are here; scan them and send out its value loads and the
-        // masks of the strip after it
+        // next strip: scan its masks, send out its value loads and the strip-after-next masks
         if (t + 1 < total) {
-            Strip nx;
-            nx.bi = cur.bi + 1;
-            nx.row = cur.row;
-            nx.vb = cur.vb + cur.n;
-            if (nx.bi == nb) {
-                nx.bi = 0;
-                nx.row += row_step;
-                nx.vb = w0 > 0 ? slice_value_base(masks, nx.row, KW, w0, lane) : 0;
+            int nbi = bi + 1, nrow = row, nvb = vb + n;
+            if (nbi == nb) {
+                nbi = 0;
+                nrow += row_step;
+                nvb = w0 > 0 ? slice_value_base(masks, nrow, KW, w0, lane) : 0;
             }
-            nx.m = m_next;
-            nx.off = wave_excl_scan(__builtin_popcount(nx.m), lane, nx.n);
-            load_values(vals, values + (int64_t)nx.row * half_k, half_k, nx.vb, nx.n, lane);
+            off = wave_excl_scan(__builtin_popcount(m_other), lane, n);
+            load_values(vals, values + (int64_t)nrow * half_k, half_k, nvb, n, lane);
             if (t + 2 < total) {
-                int r2 = nx.row, b2 = nx.bi + 1;
+                int r2 = nrow, b2 = nbi + 1;
                 if (b2 == nb) {
                     b2 = 0;
                     r2 += row_step;
                 }
-                m_next = load_mask(masks, r2, KW, w0, nws, b2 * kWave, lane);
+                m_this = load_mask(masks, r2, KW, w0, nws, b2 * kWave, lane);
             }
-            cur = nx;
+            row = nrow;
+            bi = nbi;
+            vb = nvb;
         }
         // window writes before the reads of other lanes' chunks (one wave; the fence keeps
         // the compiler from reordering the LDS accesses across it)
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 
-        // walk strip t: two set bits per step, values from the window
-        uint32_t mm = m_cur;
-        int vi = off_cur;
+        // walk strip t: two set bits per step, values from the window.  A lane past its
+        // word's last bit takes zero values at column 31 of its own block (low_bit), so
+        // every read stays inside data this launch wrote.
+        uint32_t mm = m_walk;
+        int vi = vi0;
         while (__builtin_amdgcn_ballot_w64(mm != 0)) {
             const bool ok0 = mm != 0;
-            const int c0 = __builtin_ctz(mm) & 31;
+            const int c0 = low_bit(mm);
             mm &= mm - 1;
             const bool ok1 = mm != 0;
-            const int c1 = __builtin_ctz(mm) & 31;
+            const int c1 = low_bit(mm);
             mm &= mm - 1;
-            // both window reads are unconditional (index kept inside the window); a lane
-            // past its word's last bit takes zeros instead of what the window holds there
+            // both window reads are unconditional (index kept inside the window)
             const int i0 = min(vi, kWinChunks * 8 - 2);
             const uint32_t lo = win[i0], hi = win[i0 + 1];
             const uint32_t pr = (ok0 ? lo : 0u) | ((ok1 ? hi : 0u) << 16);
@@ -233,6 +217,11 @@ __global__ __launch_bounds__(kUThreads) void spmv_unstructured_kernel(const uint
                 }
             }
         }
+    };
+    for (int t = 0; t < total; t += 2) {
+        step(mA, mB, t);
+        if (t + 1 >= total) break;
+        step(mB, mA, t + 1);
     }
 }
 
