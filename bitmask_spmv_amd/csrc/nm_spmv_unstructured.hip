@@ -32,9 +32,10 @@ namespace nmk {
 namespace {
 
 constexpr int kUThreads = 512;                 // 8 waves per workgroup
-constexpr int kWinChunks = 260;                // per-wave window: 16-byte chunks (>= 2048 values + 7 + pad)
+constexpr int kWinChunks = 264;                // per-wave window: 16-byte chunks (>= 7 + 2048 + 34 values)
 constexpr int kWinBytes = kWinChunks * 16;
 constexpr int kValLoads = (kWinChunks + kWave - 1) / kWave;  // 16-byte loads per lane for one strip (5)
+constexpr int kLead = 4;                       // zero dwords in front of x (see the walk)
 constexpr size_t kULdsCap = 80 * 1024;
 constexpr size_t kULdsPerCu = 160 * 1024;
 
@@ -104,15 +105,17 @@ __global__ __launch_bounds__(kUThreads) void spmv_unstructured_kernel(const uint
                                                                       int slice) {
     constexpr int kBlk = XLayout<B>::kBlk;
     constexpr int kWaves = kUThreads / kWave;
-    extern __shared__ uint32_t xs[];  // [nws][kBlk] x, then kWaves windows of kWinBytes
+    extern __shared__ uint32_t lds[];  // [kLead zeros][nws][kBlk] x, then kWaves windows of kWinBytes
+    uint32_t *xs = lds + kLead;
     const int s = blockIdx.y;
     const int w0 = s * slice;
     const int nws = min(slice, KW - w0);
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int half_k = KW * 16;
-    uint16_t *win = reinterpret_cast<uint16_t *>(
-        reinterpret_cast<uint8_t *>(xs) + (((size_t)nws * kBlk * 4 + 15) & ~(size_t)15) + (size_t)wave * kWinBytes);
+    uint16_t *win = reinterpret_cast<uint16_t *>(reinterpret_cast<uint8_t *>(xs) +
+                                                 (((size_t)nws * kBlk * 4 + 15) & ~(size_t)15) +
+                                                 (size_t)wave * kWinBytes);
 
     const int first_row = blockIdx.x * kWaves + wave;
     const int row_step = gridDim.x * kWaves;
@@ -125,6 +128,17 @@ __global__ __launch_bounds__(kUThreads) void spmv_unstructured_kernel(const uint
     stage_x<B, kUThreads>(xs, x, ldx, w0, nws, [&] {
         if (total > 0) mA = load_mask(masks, first_row, KW, w0, nws, 0, lane);
     });
+    // Zero the dwords in front of x and the pad dwords of every block: a lane whose word
+    // has run out of set bits scans -1, which addresses the pad just before its block
+    // (or the leading zeros), so it multiplies by an x of exactly 0.
+    {
+        constexpr int kData = XLayout<B>::S == 1 ? 16 : 16 * XLayout<B>::S;
+        constexpr int kPad = kBlk - kData;
+        if (threadIdx.x < kLead) lds[threadIdx.x] = 0u;
+        for (int w = threadIdx.x; w < nws; w += kUThreads)
+#pragma unroll
+            for (int q = 0; q < kPad; ++q) xs[w * kBlk + kData + q] = 0u;
+    }
     __syncthreads();
     if (total == 0) return;
 
@@ -184,21 +198,21 @@ __global__ __launch_bounds__(kUThreads) void spmv_unstructured_kernel(const uint
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 
         // walk strip t: two set bits per step, values from the window.  A lane past its
-        // word's last bit takes zero values at column 31 of its own block (low_bit), so
-        // every read stays inside data this launch wrote.
+        // word's last bit scans -1 (__builtin_ctzg with fallback -1 is the hardware's
+        // lowest-set-bit scan), reads the zero pad in front of its block as x and so adds
+        // exactly 0 whatever finite value the window holds at its (then foreign) index; the
+        // window is rewritten in full for every strip and sized for the largest index.
         uint32_t mm = m_walk;
         int vi = vi0;
         while (__builtin_amdgcn_ballot_w64(mm != 0)) {
-            const bool ok0 = mm != 0;
-            const int c0 = low_bit(mm);
+            const int c0 = __builtin_ctzg(mm, -1);
             mm &= mm - 1;
-            const bool ok1 = mm != 0;
-            const int c1 = low_bit(mm);
+            const int c1 = __builtin_ctzg(mm, -1);
             mm &= mm - 1;
-            // both window reads are unconditional (index kept inside the window)
-            const int i0 = min(vi, kWinChunks * 8 - 2);
-            const uint32_t lo = win[i0], hi = win[i0 + 1];
-            const uint32_t pr = (ok0 ? lo : 0u) | ((ok1 ? hi : 0u) << 16);
+            // the pair (vi, vi+1) from the two aligned dwords around it (a dword read at a
+            // 2-byte offset would be a slow misaligned LDS access)
+            const uint32_t *w32 = reinterpret_cast<const uint32_t *>(win) + (vi >> 1);
+            const uint32_t pr = __builtin_amdgcn_alignbit(w32[1], w32[0], (uint32_t)(vi & 1) * 16u);
             dot_pair<B>(pr, blk, c0, c1, acc);
             vi += 2;
         }
@@ -265,7 +279,7 @@ MvPlan plan_spmv_unstructured(int64_t R, int64_t K, int B, const DeviceInfo &dev
     const int64_t windows = (int64_t)(kUThreads / kWave) * kWinBytes;
     size_t cap = kULdsCap;
     if (dev.max_lds_per_block > 0 && (size_t)dev.max_lds_per_block < cap) cap = (size_t)dev.max_lds_per_block;
-    int64_t max_slice = ((int64_t)cap - windows - 16) / bytes_per_word;
+    int64_t max_slice = ((int64_t)cap - windows - 16 - kLead * 4) / bytes_per_word;
     if (max_slice >= kWave) max_slice -= max_slice % kWave;
     if (max_slice < 1) max_slice = 1;
     // Same policy as the N:M planner: split only when LDS forces it or rows are few.
@@ -281,7 +295,7 @@ MvPlan plan_spmv_unstructured(int64_t R, int64_t K, int B, const DeviceInfo &dev
     splits = (KW + slice - 1) / slice;
     p.splits = (int)splits;
     p.slice = (int)slice;
-    p.lds_bytes = (((size_t)slice * bytes_per_word + 15) & ~(size_t)15) + (size_t)windows;
+    p.lds_bytes = (size_t)kLead * 4 + (((size_t)slice * bytes_per_word + 15) & ~(size_t)15) + (size_t)windows;
     int per_cu = (int)(kULdsPerCu / p.lds_bytes);
     if (per_cu > 8) per_cu = 8;
     if (per_cu < 1) per_cu = 1;
