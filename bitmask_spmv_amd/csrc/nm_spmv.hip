@@ -155,12 +155,16 @@ __device__ __forceinline__ void walk_batch(const Batch<FMT> &bt, const uint32_t 
     }
 }
 
-// Matrix of the set that owns global row r (r is wave-uniform: scalar compares).
+// Matrix of the set that owns global row r (0 <= r < R).  The launcher pads row0 past
+// the last matrix with the total row count, so p counts the bounds row0[q] <= r.  The
+// test is the sign of row0[q] - 1 - r (no overflow for 0 <= r, row0[q] <= INT_MAX),
+// which keeps it in scalar integer arithmetic: a boolean compare is materialised
+// through a vector register here, and reusing that register makes the wave wait for
+// its in-flight loads.
 __device__ __forceinline__ int owner(const SpmvSet &set, int r) {
     int p = 0;
 #pragma unroll
-    for (int q = 1; q < kMaxMats; ++q)
-        if (q < set.P && r >= set.row0[q]) p = q;
+    for (int q = 1; q < kMaxMats; ++q) p += (int)((uint32_t)(set.row0[q] - 1 - r) >> 31);
     return p;
 }
 
@@ -176,28 +180,38 @@ __device__ __forceinline__ void locate(const SpmvSet &set, int r, int &p, int &l
     }
 }
 
-// Row finished: wave reduction, then the bf16 result (or, for the gated MLP, the gate
-// total kept in gsave until its up row finishes), or this slice's fp32 partial.
+// Row finished: wave reduction (uniform across the wave), then lane 0 writes the output
+// -- the bf16 row; for the gated MLP h = silu(g) * u once the up row of a pair is done,
+// the gate total kept in gsave until then; for a split launch the row's fp32 partial.
+// `split` (0 or 1) and the row parity are integers: a boolean here would be materialised
+// through a vector register, and the reuse of that register can make the wave wait for
+// its in-flight loads.
 template <int B, int EPI>
-__device__ __forceinline__ void finish_row(float (&acc)[B], float (&gsave)[B], const SpmvSet &set, int row, int s,
-                                           int R, int lane, float *partial) {
-    int p, local;
-    locate<EPI>(set, row, p, local);
+__device__ __forceinline__ void finish_row(float (&acc)[B], float (&gsave)[B], const SpmvSet &set, int row, int split,
+                                           int s, int R, int lane, float *partial) {
+    const int glu = EPI == kEpiSwiGLU ? 1 - split : 0;  // gated MLP without a split
+    const int up = row & 1;
+    float val[B];
 #pragma unroll
     for (int b = 0; b < B; ++b) {
         const float tot = wave_sum(acc[b]);
         acc[b] = 0.f;
-        if (gridDim.y != 1) {
-            if (lane == 0) partial[((int64_t)s * B + b) * R + row] = tot;
-        } else if constexpr (EPI == kEpiSwiGLU) {
-            if (p == 0)
-                gsave[b] = tot;
-            else if (lane == 0)
-                set.y[0][(int64_t)b * set.ldy[0] + local] = f32_to_bf16_rne(silu_mul(gsave[b], tot));
-        } else if (lane == 0) {
-            set.y[p][(int64_t)b * set.ldy[p] + local] = f32_to_bf16_rne(tot);
+        val[b] = tot;
+        if constexpr (EPI == kEpiSwiGLU) {
+            gsave[b] = up ? gsave[b] : tot;
+            val[b] = glu ? silu_mul(gsave[b], tot) : tot;
         }
     }
+    if ((glu & (up ^ 1)) | lane) return;  // a gate row waits for its up row; lane 0 writes
+    if (split) {
+#pragma unroll
+        for (int b = 0; b < B; ++b) partial[((int64_t)s * B + b) * R + row] = val[b];
+        return;
+    }
+    int p, local;
+    locate<EPI>(set, row, p, local);
+#pragma unroll
+    for (int b = 0; b < B; ++b) set.y[p][(int64_t)b * set.ldy[p] + local] = f32_to_bf16_rne(val[b]);
 }
 
 // Batch loads of launch row r, word offset `base` within the slice.
@@ -230,6 +244,7 @@ __global__ __launch_bounds__(NT) void spmv_kernel(const SpmvSet set, int KW, con
     // into nb strips of 64 words, walked as one flat sequence so the next strip's loads
     // are in flight while the current one is computed, across row boundaries too.
     const int unit = blockIdx.x * kWaves + wave;
+    const int split = gridDim.y != 1 ? 1 : 0;
     const int row_step = gridDim.x * kWaves;
     const int first_row = EPI == kEpiSwiGLU ? 2 * unit : unit;
     const int units = EPI == kEpiSwiGLU ? R / 2 : R;
@@ -241,11 +256,18 @@ __global__ __launch_bounds__(NT) void spmv_kernel(const SpmvSet set, int KW, con
         return r + row_step;
     };
 
-    // Two batch buffers used in turn (no register copies, so the wait for one batch
-    // never covers the loads of the other).
+    // Two batch buffers used in turn: the loads of the next batch go out before the walk
+    // of the current one.  No register copies, so the wait for one batch never covers
+    // the loads of the other.
     Batch<FMT> bufA, bufB;
+    auto step = [&](int &row, int &bi) {
+        if (++bi == nb) {
+            bi = 0;
+            row = next_row(row);
+        }
+    };
     int rowA = first_row, biA = 0, rowB = first_row, biB = 0;
-    // Stage this slice of x into LDS; batch A's loads go out right after the first round
+    // Stage this slice of x into LDS; batch 0's loads go out right after the first round
     // of x loads, so waiting for x (an L2 hit after the first workgroup of an XCD) never
     // waits for the weights queued behind it.
     stage_x<B, NT>(xs, x, ldx, w0, nws, [&] {
@@ -256,28 +278,33 @@ __global__ __launch_bounds__(NT) void spmv_kernel(const SpmvSet set, int KW, con
     float acc[B], gsave[B];
 #pragma unroll
     for (int b = 0; b < B; ++b) acc[b] = gsave[b] = 0.f;
-    for (int t = 0; t < total; t += 2) {
-        // B <- batch t+1, walk A (batch t)
+    // Whole pairs of batches per iteration and the odd last batch after the loop: an exit
+    // in the middle of the body would give the wait-count analysis a path back to the
+    // top with a batch's loads still in flight, and it would then wait for them there.
+    // The loads are unconditional (a conditional load makes every later wait a full
+    // one); the one batch past the end, when the count is even, has zero words -- no
+    // memory traffic -- and goes out before the last walk, which hides its round trip.
+    int t = 0;
+    for (; t + 1 < total; t += 2) {
         rowB = rowA;
-        biB = biA + 1;
-        if (biB == nb) {
-            biB = 0;
-            rowB = next_row(rowB);
-        }
-        load_row_batch<FMT, EPI>(bufB, set, min(rowB, R - 1), KW, w0, t + 1 < total ? nws : 0, biB * kWave, lane);
-        walk_batch<FMT, B>(bufA, xs, nws, acc);
-        if (biA == nb - 1) finish_row<B, EPI>(acc, gsave, set, rowA, s, R, lane, partial);
-        if (t + 1 >= total) break;
-        // A <- batch t+2, walk B (batch t+1)
+        biB = biA;
+        step(rowB, biB);
+        load_row_batch<FMT, EPI>(bufB, set, min(rowB, R - 1), KW, w0, nws, biB * kWave, lane);  // batch t+1
+        // keep the walk (which waits for batch A) after the issue of these loads
+        __builtin_amdgcn_sched_barrier(0);
+        walk_batch<FMT, B>(bufA, xs, nws, acc);  // batch t
+        if (biA == nb - 1) finish_row<B, EPI>(acc, gsave, set, rowA, split, s, R, lane, partial);
         rowA = rowB;
-        biA = biB + 1;
-        if (biA == nb) {
-            biA = 0;
-            rowA = next_row(rowA);
-        }
+        biA = biB;
+        step(rowA, biA);
         load_row_batch<FMT, EPI>(bufA, set, min(rowA, R - 1), KW, w0, t + 2 < total ? nws : 0, biA * kWave, lane);
-        walk_batch<FMT, B>(bufB, xs, nws, acc);
-        if (biB == nb - 1) finish_row<B, EPI>(acc, gsave, set, rowB, s, R, lane, partial);
+        __builtin_amdgcn_sched_barrier(0);
+        walk_batch<FMT, B>(bufB, xs, nws, acc);  // batch t+1
+        if (biB == nb - 1) finish_row<B, EPI>(acc, gsave, set, rowB, split, s, R, lane, partial);
+    }
+    if (t < total) {  // odd count: the last batch is in A
+        walk_batch<FMT, B>(bufA, xs, nws, acc);
+        if (biA == nb - 1) finish_row<B, EPI>(acc, gsave, set, rowA, split, s, R, lane, partial);
     }
 }
 
@@ -338,7 +365,9 @@ hipError_t launch_fbn(const MvPlan &p, const SpmvSet &set, int64_t K, const uint
                       hipStream_t st) {
     hipError_t e = allow_lds<FMT, B, NT, EPI>(p.lds_bytes);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((spmv_kernel<FMT, B, NT, EPI>), dim3(p.grid_x, p.splits), dim3(NT), p.lds_bytes, st, set,
+    SpmvSet padded = set;
+    for (int q = set.P + 1; q <= kMaxMats; ++q) padded.row0[q] = set.row0[set.P];
+    hipLaunchKernelGGL((spmv_kernel<FMT, B, NT, EPI>), dim3(p.grid_x, p.splits), dim3(NT), p.lds_bytes, st, padded,
                        (int)(K / 32), x, ldx, ws, p.slice);
     e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;
