@@ -30,27 +30,29 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 template <int U>
 struct DBatch {
     u32x4 w[U];
-    int lc[U];
+    int base;  // first chunk of the batch within the row slice (wave-uniform)
 };
 
-// One batch of U 16-byte chunks per lane through a raw buffer descriptor covering the
-// row slice's `chunks` chunks (0 = nothing to load; the loads return zeros).
+// One batch of U 16-byte chunks per lane (chunk base + u*64 + lane) through a raw buffer
+// descriptor that starts at the batch and ends at the row slice's `chunks` chunks
+// (0 = nothing to load; out-of-range lanes read zeros).  The batch position lives in the
+// scalar descriptor and the lane offsets are loop-invariant, so issuing a batch writes
+// no vector register but the load destinations.
 template <int U>
 __device__ __forceinline__ void load_dbatch(DBatch<U> &bt, const u32x4 *wrow, int chunks, int base, int lane) {
-    const __amdgpu_buffer_rsrc_t rw = make_rsrc(wrow, (int64_t)chunks * 16);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(wrow + base, (int64_t)max(chunks - base, 0) * 16);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int c = base + u * kWave + lane;
-        bt.w[u] = __builtin_amdgcn_raw_buffer_load_b128(rw, c * 16, 0, kLoadNT);
-        bt.lc[u] = c;
-    }
+    for (int u = 0; u < U; ++u)
+        bt.w[u] = __builtin_amdgcn_raw_buffer_load_b128(rw, (u * kWave + lane) * 16, 0, kLoadNT);
+    bt.base = base;
 }
 
 template <int B, int U>
 __device__ __forceinline__ void dot_dbatch(const DBatch<U> &bt, const u32x4 *xs4, int ncs, float (&acc)[B]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int lc = bt.lc[u] < ncs ? bt.lc[u] : 0;  // padding lanes carry zero weights
+        const int c = bt.base + u * kWave + (int)(threadIdx.x & (kWave - 1));
+        const int lc = c < ncs ? c : 0;  // padding lanes carry zero weights
 #pragma unroll
         for (int b = 0; b < B; ++b) {
             const u32x4 xv = xs4[b * ncs + lc];
@@ -64,11 +66,15 @@ __device__ __forceinline__ void dot_dbatch(const DBatch<U> &bt, const u32x4 *xs4
     }
 }
 
+// Matrix of the set that owns launch row r (0 <= r < R).  The launcher pads row0 past
+// the last matrix with the total row count, so p counts the bounds row0[q] <= r; the
+// test is the sign of row0[q] - 1 - r, kept in scalar integer arithmetic (a boolean
+// compare is materialised through a vector register, and reusing that register makes
+// the wave wait for its in-flight loads).
 __device__ __forceinline__ int owner(const DenseSet &set, int r) {
     int p = 0;
 #pragma unroll
-    for (int q = 1; q < kMaxMats; ++q)
-        if (q < set.P && r >= set.row0[q]) p = q;
+    for (int q = 1; q < kMaxMats; ++q) p += (int)((uint32_t)(set.row0[q] - 1 - r) >> 31);
     return p;
 }
 
@@ -84,26 +90,56 @@ __device__ __forceinline__ void locate(const DenseSet &set, int r, int &p, int &
     }
 }
 
+// Row finished: wave reduction, then lane 0 writes the bf16 row (gated MLP: h once the up
+// row of a pair is done, the gate total kept in gsave until then) or, for a split
+// launch, the row's fp32 partial.  `split` and the row parity are integers for the same
+// reason as in owner().
+//
+// The stored data (bf16 bits, or the fp32 bits of a partial) is built in `held`, which the
+// row loop pins in vector registers until after the next loads have gone out (hold()):
+// a store's data register may not be overwritten until the store has gone (this target
+// tracks that with the in-order load counter), so a recycled data register would make
+// the wave wait for every load issued before the store.
 template <int B, int EPI>
-__device__ __forceinline__ void finish_drow(float (&acc)[B], float (&gsave)[B], const DenseSet &set, int row, int s,
-                                            int R, int lane, float *partial) {
-    int p, local;
-    locate<EPI>(set, row, p, local);
+__device__ __forceinline__ void finish_drow(float (&acc)[B], float (&gsave)[B], uint32_t (&held)[B], const DenseSet &set,
+                                            int row, int split, int s, int R, int lane, float *partial) {
+    const int glu = EPI == kEpiSwiGLU ? 1 - split : 0;  // gated MLP without a split
+    const int up = row & 1;
+    float val[B];
 #pragma unroll
     for (int b = 0; b < B; ++b) {
         const float tot = wave_sum(acc[b]);
         acc[b] = 0.f;
-        if (gridDim.y != 1) {
-            if (lane == 0) partial[((int64_t)s * B + b) * R + row] = tot;
-        } else if constexpr (EPI == kEpiSwiGLU) {
-            if (p == 0)
-                gsave[b] = tot;
-            else if (lane == 0)
-                set.y[0][(int64_t)b * set.ldy[0] + local] = f32_to_bf16_rne(silu_mul(gsave[b], tot));
-        } else if (lane == 0) {
-            set.y[p][(int64_t)b * set.ldy[p] + local] = f32_to_bf16_rne(tot);
+        val[b] = tot;
+        if constexpr (EPI == kEpiSwiGLU) {
+            gsave[b] = up ? gsave[b] : tot;
+            val[b] = glu ? silu_mul(gsave[b], tot) : tot;
         }
     }
+    if ((glu & (up ^ 1)) | lane) return;  // a gate row waits for its up row; lane 0 writes
+    if (split) {
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            held[b] = __float_as_uint(val[b]);
+            reinterpret_cast<uint32_t *>(partial)[((int64_t)s * B + b) * R + row] = held[b];
+        }
+        return;
+    }
+    int p, local;
+    locate<EPI>(set, row, p, local);
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+        held[b] = f32_to_bf16_rne(val[b]);
+        set.y[p][(int64_t)b * set.ldy[p] + local] = (uint16_t)held[b];
+    }
+}
+
+// Pins the last stored data in vector registers up to this point, past the address
+// arithmetic of the loads just issued (see finish_drow).
+template <int B>
+__device__ __forceinline__ void hold(uint32_t (&held)[B]) {
+#pragma unroll
+    for (int b = 0; b < B; ++b) asm volatile("" : "+v"(held[b]));
 }
 
 template <int U, int EPI>
@@ -131,6 +167,7 @@ __global__ __launch_bounds__(kThreads) void dense_kernel(const DenseSet set, int
     // same row order (row pairs for the gated MLP).
     const int unit = blockIdx.x * kWaves + wave;
     const int row_step = gridDim.x * kWaves;
+    const int split = gridDim.y != 1 ? 1 : 0;
     const int first_row = EPI == kEpiSwiGLU ? 2 * unit : unit;
     const int units = EPI == kEpiSwiGLU ? R / 2 : R;
     const int my_rows = (unit < units ? (units - 1 - unit) / row_step + 1 : 0) * (EPI == kEpiSwiGLU ? 2 : 1);
@@ -169,28 +206,43 @@ __global__ __launch_bounds__(kThreads) void dense_kernel(const DenseSet set, int
     __syncthreads();
 
     float acc[B], gsave[B];
+    uint32_t held[B];
 #pragma unroll
-    for (int b = 0; b < B; ++b) acc[b] = gsave[b] = 0.f;
-    for (int t = 0; t < total; t += 2) {
+    for (int b = 0; b < B; ++b) {
+        acc[b] = gsave[b] = 0.f;
+        held[b] = 0u;
+    }
+    // Whole pairs of batches per iteration, the odd last batch after the loop, and the
+    // next batch's loads issued before the current walk waits: the same schedule as the
+    // sparse kernel, for the same reasons.
+    auto step = [&](int &row, int &bi) {
+        if (++bi == nb) {
+            bi = 0;
+            row = next_row(row);
+        }
+    };
+    int t = 0;
+    for (; t + 1 < total; t += 2) {
         rowB = rowA;
-        biB = biA + 1;
-        if (biB == nb) {
-            biB = 0;
-            rowB = next_row(rowB);
-        }
-        load_row_dbatch<U, EPI>(bufB, set, min(rowB, R - 1), c0, t + 1 < total ? ncs : 0, biB * kWave * U, lane);
+        biB = biA;
+        step(rowB, biB);
+        load_row_dbatch<U, EPI>(bufB, set, min(rowB, R - 1), c0, ncs, biB * kWave * U, lane);
+        hold(held);
+        __builtin_amdgcn_sched_barrier(0);
         dot_dbatch<B, U>(bufA, xs4, ncs, acc);
-        if (biA == nb - 1) finish_drow<B, EPI>(acc, gsave, set, rowA, s, R, lane, partial);
-        if (t + 1 >= total) break;
+        if (biA == nb - 1) finish_drow<B, EPI>(acc, gsave, held, set, rowA, split, s, R, lane, partial);
         rowA = rowB;
-        biA = biB + 1;
-        if (biA == nb) {
-            biA = 0;
-            rowA = next_row(rowA);
-        }
+        biA = biB;
+        step(rowA, biA);
         load_row_dbatch<U, EPI>(bufA, set, min(rowA, R - 1), c0, t + 2 < total ? ncs : 0, biA * kWave * U, lane);
+        hold(held);
+        __builtin_amdgcn_sched_barrier(0);
         dot_dbatch<B, U>(bufB, xs4, ncs, acc);
-        if (biB == nb - 1) finish_drow<B, EPI>(acc, gsave, set, rowB, s, R, lane, partial);
+        if (biB == nb - 1) finish_drow<B, EPI>(acc, gsave, held, set, rowB, split, s, R, lane, partial);
+    }
+    if (t < total) {
+        dot_dbatch<B, U>(bufA, xs4, ncs, acc);
+        if (biA == nb - 1) finish_drow<B, EPI>(acc, gsave, held, set, rowA, split, s, R, lane, partial);
     }
 }
 
@@ -248,7 +300,9 @@ hipError_t launch_bu(const MvPlan &p, const DenseSet &set, int64_t K, const uint
                      hipStream_t st) {
     hipError_t e = allow_lds<B, U, EPI>(p.lds_bytes);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((dense_kernel<B, U, EPI>), dim3(p.grid_x, p.splits), dim3(kThreads), p.lds_bytes, st, set,
+    DenseSet padded = set;  // row0 past the last matrix = the total (see owner())
+    for (int q = set.P + 1; q <= kMaxMats; ++q) padded.row0[q] = set.row0[set.P];
+    hipLaunchKernelGGL((dense_kernel<B, U, EPI>), dim3(p.grid_x, p.splits), dim3(kThreads), p.lds_bytes, st, padded,
                        (int)(K / 8), x, ldx, ws, p.slice);
     e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;
