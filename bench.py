@@ -247,7 +247,8 @@ def main():
                    + [nm.nm_spmv_swiglu_workspace_bytes(R, K, B) for _, R, K, _ in projs]
                    + [nm.dense_gemv_swiglu_workspace_bytes(R, K, B) for _, R, K, _ in projs]
                    + [nm.nm_spmv_multi_workspace_bytes([R] * 3, K, B) for _, R, K, _ in projs]
-                   + [nm.dense_gemv_multi_workspace_bytes([R] * 3, K, B) for _, R, K, _ in projs] + [4])
+                   + [nm.dense_gemv_multi_workspace_bytes([R] * 3, K, B) for _, R, K, _ in projs]
+                   + [nm.nm_spmv_unstructured_workspace_bytes(R, K, B) for _, R, K, _ in projs] + [4])
     ws = torch.empty((ws_bytes + 3) // 4, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
     log(f"inputs generated and packed in {time.time() - t0:.1f}s "
