@@ -302,6 +302,8 @@ FULL = [
     ("8b-q", 4096, 4096, 2, 4, 1), ("8b-kv", 1024, 4096, 16, 32, 1), ("8b-up", 14336, 4096, 2, 4, 1),
     ("8b-down", 4096, 14336, 16, 32, 1), ("14b-up", 17408, 5120, 4, 8, 1), ("32b-q", 8192, 5120, 4, 8, 1),
     ("70b-kv", 1024, 8192, 8, 16, 8), ("70b-down", 8192, 28672, 8, 16, 1), ("70b-down-b4", 8192, 28672, 8, 16, 4),
+    ("14b-down", 5120, 17408, 4, 8, 1), ("32b-down", 5120, 25600, 4, 8, 1), ("70b-q-b2", 8192, 8192, 8, 16, 2),
+    ("70b-up-b8", 28672, 8192, 8, 16, 8),
 ]
 
 
