@@ -124,6 +124,9 @@ def parse():
     ap.add_argument("--solver-tokens", type=int, default=4096, help="calibration tokens for the solver")
     ap.add_argument("--no-unstructured", action="store_true",
                     help="skip the 50%% unstructured vs N:M comparison table")
+    ap.add_argument("--profile-proj", default=None,
+                    help="with --profile-kernel: launch this projection alone through nm_spmv (e.g. gate) "
+                         "instead of the dominant launch")
     ap.add_argument("--profile-kernel", action="store_true",
                     help="counter-collection mode: only the dominant launch shape (eager, rotated) plus a "
                          "plain 256 MiB device copy used to calibrate the byte counters")
@@ -691,8 +694,13 @@ def profile_kernel(args, torch, nm, synth, cfg, dev):
     names = [p[0] for p in projs]
     N, M = cfg["patterns"][0]
     B = args.batch
-    glu = "gate" in names and "up" in names
-    if glu:
+    glu = "gate" in names and "up" in names and args.profile_proj is None
+    if args.profile_proj is not None:
+        if args.profile_proj not in names:
+            raise SystemExit(f"--profile-proj: no projection {args.profile_proj!r} in {names}")
+        _, R, K, _ = projs[names.index(args.profile_proj)]
+        label, mats = args.profile_proj, 1
+    elif glu:
         _, R, K, _ = projs[names.index("gate")]
         label, mats = "gate|up+swiglu", 2
     else:
