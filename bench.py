@@ -453,6 +453,37 @@ def main():
         log(f"{label}: " + ", ".join(f"{k} {v['us']} us ({v['pct_peak']}%)" for k, v in d.items()
                                      if isinstance(v, dict)) + f"; dense {d['dense_us']} us")
 
+    # ---------------------------------------------------------------- achievable read
+    # What a launch that only streams reaches on the same byte count under the same
+    # rotation (nm_stream_read over >= 512 MB of distinct buffers of that size): the rate
+    # each launch's % of the 8 TB/s peak is read against.
+    stream_us = {}
+
+    def time_stream_read(nbytes):
+        nbytes = (int(nbytes) + 15) // 16 * 16
+        if nbytes not in stream_us:
+            cnt = max(2, math.ceil(ROTATE_BYTES / nbytes))
+            bufs = [torch.empty(nbytes // 4, dtype=torch.int32, device=dev) for _ in range(cnt)]
+            sink = torch.empty(nm.nm_stream_read_sink_words(nbytes), dtype=torch.int32, device=dev)
+            g = capture(torch, [(lambda b=b: nm.nm_stream_read(b, sink=sink)) for b in bufs])
+            g.replay()
+            stream_us[nbytes] = min(timer.time_graph(g, 1) for _ in range(reps)) * 1e3 / cnt
+            del g, bufs
+        return nbytes, stream_us[nbytes]
+
+    first_pat = f"{patterns[0][0]}:{patterns[0][1]}"
+    stream_log = []
+    for grp in [[pr] for pr in projs] + [grp for grp in groups if len(grp) > 1]:
+        label = grp[0][0] if len(grp) == 1 else group_label(grp)
+        nbytes, us = time_stream_read(group_bytes(grp, B, False))
+        d = per[label]
+        d["stream_read"] = {"us": round(us, 2), "GBs": round(nbytes / us / 1e3, 1),
+                            "pct_peak": round(100 * nbytes / us / 1e3 / HBM_PEAK_GBS, 1),
+                            "spmv_over_stream_time": round(d[first_pat]["us"] / us, 3)}
+        stream_log.append(f"{label} {round(us, 2)} us ({d['stream_read']['pct_peak']}%)")
+    torch.cuda.synchronize()
+    log("stream read of the same bytes (achievable): " + ", ".join(stream_log))
+
     # ---------------------------------------------------------------- metadata formats
     # The same product over the first pattern's packs with the metadata as uint8 offsets
     # and int32 column indices (converted on the device from the masks), each timed over
@@ -639,9 +670,25 @@ def main():
             for m_h, v_h, x_h, K in host:
                 oracle.spmv(m_h, v_h, x_h, K, nthreads=cores)
         dt = time.time() - t1
+        # the same sample on one core (fewer repetitions: it is ~cores times slower)
+        reps1 = max(1, args.cpu_reps // 6)
+        t1 = time.time()
+        for _ in range(reps1):
+            for m_h, v_h, x_h, K in host:
+                oracle.spmv(m_h, v_h, x_h, K, nthreads=1)
+        dt1 = time.time() - t1
+        model = ""
+        try:
+            with open("/proc/cpuinfo") as f:
+                model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+        except OSError:
+            pass
         cpu = {"value": round(sb * args.cpu_reps / dt / 1e9, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
                "sample": f"layer 0 of the set ({', '.join(p[0] for p in projs)}), {N}:{M}, B={B}, "
-                         f"x{args.cpu_reps} reps, {dt:.1f}s wall"}
+                         f"x{args.cpu_reps} reps, {dt:.1f}s wall",
+               "one_core": {"value": round(sb * reps1 / dt1 / 1e9, 3), "unit": "GB/s",
+                            "sample": f"the same layer, x{reps1} reps, {dt1:.1f}s wall"},
+               "cpu_model": model}
 
     value = fused_sparse_bytes / (ms_fused * 1e-3) / 1e9
     out = {
@@ -818,11 +865,15 @@ def summarize_trace(d):
             wg = int(r["Workgroup_Size_X"]) * int(r.get("Workgroup_Size_Y", 1) or 1)
             grid = (int(r["Grid_Size_X"]) * int(r.get("Grid_Size_Y", 1) or 1)) // max(wg, 1)
             groups.setdefault((short, grid), []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-    print("| kernel | workgroups | dispatches | avg us | median us | min us | total ms |")
-    print("|---|---|---|---|---|---|---|")
+    def pct(v, q):  # nearest-rank percentile
+        s = sorted(v)
+        return s[min(len(s) - 1, max(0, int(round(q / 100 * len(s) + 0.5)) - 1))]
+
+    print("| kernel | workgroups | dispatches | avg us | median us | p10 us | p90 us | min us | total ms |")
+    print("|---|---|---|---|---|---|---|---|---|")
     for (k, g), v in sorted(groups.items(), key=lambda kv: -sum(kv[1]))[:25]:
-        print(f"| {k} | {g} | {len(v)} | {statistics.mean(v):.2f} | {statistics.median(v):.2f} | {min(v):.2f} | "
-              f"{sum(v) / 1e3:.2f} |")
+        print(f"| {k} | {g} | {len(v)} | {statistics.mean(v):.2f} | {statistics.median(v):.2f} | {pct(v, 10):.2f} | "
+              f"{pct(v, 90):.2f} | {min(v):.2f} | {sum(v) / 1e3:.2f} |")
 
 
 def kernel_fingerprint() -> str:

@@ -27,6 +27,7 @@ __all__ = [
     "dense_gemv_swiglu_workspace_bytes", "nm_prune_pack_unstructured", "nm_spmv_unstructured",
     "nm_spmv_unstructured_workspace_bytes", "nm_unpack_unstructured", "nm_hessian", "nm_obs_inverse_factor",
     "nm_obs_inverse_factor_workspace_bytes", "nm_sparsegpt_prune_pack", "nm_sparsegpt_workspace_bytes",
+    "nm_stream_read", "nm_stream_read_sink_words",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnmspmv.so")
@@ -95,6 +96,8 @@ def _load() -> ctypes.CDLL:
     L.dense_gemv_multi_workspace_bytes.argtypes = [p, i32, i64, i32]
     L.dense_gemv_multi_workspace_bytes.restype = sz
     L.dense_gemv_multi.argtypes = [p, i32, i64, p, i64, i32, p, sz, p]
+    L.nm_stream_read_sink_words.argtypes, L.nm_stream_read_sink_words.restype = [sz], sz
+    L.nm_stream_read.argtypes, L.nm_stream_read.restype = [p, sz, p, sz, p], i32
     for f in (L.nm_col_norm, L.nm_prune_pack, L.nm_spmv, L.dense_gemv, L.nm_unpack, L.nm_spmv_multi,
               L.dense_gemv_multi):
         f.restype = i32
@@ -525,3 +528,24 @@ def dense_gemv_multi(Ws, x: torch.Tensor, outs=None, workspace: torch.Tensor | N
     _check(lib.dense_gemv_multi(ctypes.cast(arr, ctypes.c_void_p), len(Rs), K, _ptr(x2), _ld(x2), x2.shape[0],
                                 _ptr(ws), ws_bytes, _stream(x2)))
     return outs
+
+
+def nm_stream_read_sink_words(nbytes: int) -> int:
+    return int(lib.nm_stream_read_sink_words(nbytes))
+
+
+def nm_stream_read(buf: torch.Tensor, sink: torch.Tensor | None = None) -> torch.Tensor:
+    """Measurement aid: one streaming read of a contiguous device tensor (its whole
+    storage, a multiple of 16 bytes); returns the per-workgroup XOR folds (int32) whose
+    XOR is the XOR of all dwords read."""
+    if not isinstance(buf, torch.Tensor) or buf.device.type != "cuda":
+        raise ValueError("buf must be a tensor on a HIP device")
+    if not buf.is_contiguous():
+        raise ValueError("buf must be contiguous")
+    nbytes = buf.numel() * buf.element_size()
+    words = nm_stream_read_sink_words(nbytes)
+    if sink is None:
+        sink = torch.empty(words, dtype=torch.int32, device=buf.device)
+    _dev(sink, "sink", torch.int32, 1)
+    _check(lib.nm_stream_read(_ptr(buf), nbytes, _ptr(sink), sink.numel(), _stream(buf)))
+    return sink

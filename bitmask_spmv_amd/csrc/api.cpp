@@ -665,4 +665,25 @@ nm_status nm_unpack(const uint32_t *masks, const nm_bf16 *values, int64_t R, int
     }
 }
 
+size_t nm_stream_read_sink_words(size_t bytes) { return nmk::stream_read_groups(bytes); }
+
+nm_status nm_stream_read(const void *buf, size_t bytes, uint32_t *sink, size_t sink_words, void *hip_stream) {
+    try {
+        g_err[0] = 0;
+        if (!buf || !sink) return fail(NM_ERR_NULL, "nm_stream_read: NULL pointer");
+        if (bytes < 16 || bytes % 16 != 0 || bytes > ((size_t)1 << 31))
+            return fail(NM_ERR_SHAPE, "nm_stream_read: bytes=%zu must be a multiple of 16 in [16, 2^31]", bytes);
+        if (!aligned(buf, 16) || !aligned(sink, 4))
+            return fail(NM_ERR_ALIGN, "nm_stream_read: buf needs 16-byte alignment");
+        const size_t need = nmk::stream_read_groups(bytes);
+        if (sink_words < need)
+            return fail(NM_ERR_WORKSPACE, "nm_stream_read: sink of %zu words required, %zu given", need, sink_words);
+        hipError_t e = nmk::launch_stream_read(buf, bytes, sink, (hipStream_t)hip_stream);
+        if (e != hipSuccess) return hip_fail("nm_stream_read launch", e);
+        return NM_OK;
+    } catch (...) {
+        return fail(NM_ERR_HIP, "nm_stream_read: internal error");
+    }
+}
+
 }  // extern "C"

@@ -96,5 +96,9 @@ hipError_t launch_dense(const MvPlan &p, const DenseSet &set, int64_t K, const u
                         float *ws, hipStream_t st);
 hipError_t launch_dense_swiglu(const MvPlan &p, const DenseSet &set, int64_t K, const uint16_t *x, int64_t ldx, int B,
                                float *ws, hipStream_t st);
+// Measurement aid: one streaming read of `bytes` bytes (multiple of 16, <= 2^31), one
+// XOR-fold per workgroup into sink[0 .. stream_read_groups(bytes)).
+size_t stream_read_groups(size_t bytes);
+hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t st);
 
 }  // namespace nmk

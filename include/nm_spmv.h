@@ -314,6 +314,23 @@ nm_status nm_sparsegpt_prune_pack(const nm_bf16 *W, int64_t ldw, int64_t R, int6
 nm_status nm_unpack(const uint32_t *masks, const nm_bf16 *values, int64_t R, int64_t K, nm_bf16 *W_out,
                     int64_t ldw, void *hip_stream);
 
+/*
+ * nm_stream_read -- measurement aid, not part of the method: reads `bytes` bytes at `buf`
+ * once, with the same 16-byte non-temporal loads and 512-thread workgroups as the
+ * matrix-vector kernels, and writes one XOR-fold of the dwords per workgroup to
+ * sink[0 .. nm_stream_read_sink_words(bytes)).  Timed under the same rotation of
+ * distinct buffers as the SpMV, it gives the rate a kernel that only streams reaches --
+ * the achievable figure the SpMV's % of the 8 TB/s peak is read against.  The XOR of all
+ * sink words equals the XOR of all dwords of the buffer.
+ *
+ * buf: device, 16-byte aligned, caller-owned, read only.  bytes: multiple of 16 in
+ * [16, 2^31] (else NM_ERR_SHAPE).  sink: device uint32 array, caller-owned, at least
+ * nm_stream_read_sink_words(bytes) words (else NM_ERR_WORKSPACE).  Asynchronous on
+ * hip_stream like every other entry point.
+ */
+size_t nm_stream_read_sink_words(size_t bytes);
+nm_status nm_stream_read(const void *buf, size_t bytes, uint32_t *sink, size_t sink_words, void *hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -264,3 +264,21 @@ def test_solver_entry_points_reject_bad_arguments(L):
     assert L.nm_sparsegpt_prune_pack(A16, 64, 8, 64, A16, 64, 2, 4, 0.01, A16, A4, A16, swb, None) == NM_ERR_ALIGN
     assert L.nm_sparsegpt_prune_pack(A16, 64, 8, 64, A16, 64, 2, 4, 0.01, A16, A16, None, 0, None) == NM_ERR_WORKSPACE
     assert L.nm_sparsegpt_prune_pack(None, 64, 8, 64, A16, 64, 2, 4, 0.01, A16, A16, A16, swb, None) == NM_ERR_NULL
+
+
+def test_stream_read_rejects_bad_arguments(L):
+    p, sz = ctypes.c_void_p, ctypes.c_size_t
+    L.nm_stream_read_sink_words.argtypes, L.nm_stream_read_sink_words.restype = [sz], sz
+    L.nm_stream_read.argtypes, L.nm_stream_read.restype = [p, sz, p, sz, p], ctypes.c_int
+    assert L.nm_stream_read_sink_words(16) == 1
+    assert L.nm_stream_read_sink_words(1 << 31) == 1024  # one fold per workgroup, at most 1024
+    assert L.nm_stream_read_sink_words(512 * 64 * 3) == 3  # at least four 16-byte chunks per thread
+    assert L.nm_stream_read_sink_words(512 * 64 * 3 + 16) == 4
+    words = L.nm_stream_read_sink_words(1 << 20)
+    assert L.nm_stream_read(None, 1 << 20, A16, words, None) == NM_ERR_NULL
+    assert L.nm_stream_read(A16, 1 << 20, None, words, None) == NM_ERR_NULL
+    assert L.nm_stream_read(A16, 0, A16, words, None) == NM_ERR_SHAPE
+    assert L.nm_stream_read(A16, 24, A16, words, None) == NM_ERR_SHAPE
+    assert L.nm_stream_read(A16, (1 << 31) + 16, A16, 1024, None) == NM_ERR_SHAPE
+    assert L.nm_stream_read(A4, 1 << 20, A16, words, None) == NM_ERR_ALIGN
+    assert L.nm_stream_read(A16, 1 << 20, A16, words - 1, None) == NM_ERR_WORKSPACE
