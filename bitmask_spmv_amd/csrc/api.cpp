@@ -82,8 +82,8 @@ void apply_override(const char *env, int64_t units, int64_t R, int B, size_t uni
     if (un == 1 || un == 2 || un == 4) p.unroll = un;
 }
 
-nmk::MvPlan spmv_plan(int64_t R, int64_t K, int B) {
-    nmk::MvPlan p = nmk::plan_spmv(R, K, B, device_info());
+nmk::MvPlan spmv_plan(int64_t R, int64_t K, int B, int fmt = nmk::kMetaBitmask) {
+    nmk::MvPlan p = nmk::plan_spmv(R, K, B, device_info(), fmt);
     apply_override("NM_SPMV_PLAN", K / 32, R, B, nmk::spmv_lds_per_word(B), p);
     return p;
 }
@@ -178,7 +178,7 @@ size_t nm_spmv_workspace_bytes(int64_t R, int64_t K, int B) {
 static nm_status spmv_run(const nmk::SpmvSet &set, int fmt, int64_t K, const nm_bf16 *x, int64_t ldx, int B,
                           void *workspace, size_t workspace_bytes, void *hip_stream, const char *who) {
     const int64_t R = set.row0[set.P];
-    const nmk::MvPlan p = spmv_plan(R, K, B);
+    const nmk::MvPlan p = spmv_plan(R, K, B, fmt);
     if (p.ws_bytes > 0) {
         if (!workspace || workspace_bytes < p.ws_bytes || !aligned(workspace, 4))
             return fail(NM_ERR_WORKSPACE, "%s: workspace of %zu bytes required, %zu given", who, p.ws_bytes,

@@ -57,7 +57,9 @@ struct DenseSet {
     int64_t ldy[kMaxMats] = {};
 };
 
-MvPlan plan_spmv(int64_t R, int64_t K, int B, const DeviceInfo &dev);
+// fmt: the launchs metadata format (the planner picks 1024-thread workgroups only for
+// kernels that fit them without spilling).
+MvPlan plan_spmv(int64_t R, int64_t K, int B, const DeviceInfo &dev, int fmt = kMetaBitmask);
 size_t spmv_lds_per_word(int B);  // LDS bytes of x per 32-column block
 MvPlan plan_dense(int64_t R, int64_t K, int B, const DeviceInfo &dev);
 

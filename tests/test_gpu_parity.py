@@ -168,6 +168,28 @@ def test_spmv_every_batch_size(B):
     assert_within(host_bf16(y), yref, absum, f"spmv B={B}")
 
 
+# x slices large enough that only two workgroups fit per CU at B = 3 and 4: the bitmask
+# kernel then runs 1024-thread workgroups (incl. split rows for K = 28672).
+WIDE = [(3000, 8192, 3), (2100, 8192, 4), (700, 28672, 4), (2049, 9216, 3)]
+
+
+@pytest.mark.parametrize("R,K,B", WIDE)
+def test_spmv_wide_workgroups(R, K, B):
+    say("spmv wide", R, K, B)
+    W = synth.weights(R, K, 21, R, K, B)
+    mref, vref = oracle.prune_pack(W, oracle.col_norm(synth.calib_acts(K, 21, R, K)), 8, 16)
+    x = synth.decode_x(B, K, 21, R, K, B)
+    md, vd, xd = dev_u32(mref), dev_bf16(vref), dev_bf16(x)
+    y = nm.nm_spmv(md, vd, xd)
+    y2 = nm.nm_spmv(md, vd, xd)
+    ys = nm.nm_spmv_multi([(md, vd), (md[: R // 3], vd[: R // 3])], xd)
+    yref, absum = oracle.spmv(mref, vref, x, K, nthreads=4)
+    assert_within(host_bf16(y), yref, absum, f"spmv wide R={R} K={K} B={B}")
+    assert (host_bf16(y) == host_bf16(y2)).all()
+    assert_within(host_bf16(ys[0]), yref, absum, "multi matrix 0")
+    assert_within(host_bf16(ys[1]), yref[:, : R // 3], absum[:, : R // 3], "multi matrix 1")
+
+
 @pytest.mark.parametrize("N,M", PATTERNS)
 def test_spmv_integer_exact(N, M):
     """Ternary weights and inputs: every partial sum is an integer <= K/2 in

@@ -29,10 +29,12 @@ def _assert_h(h_bits, g, ag, u, au, what):
 
 
 SHAPES = [(256, 512), (1000, 4096), (513, 5120), (17, 8192), (3, 28672), (1, 32)]
+# 2R launch rows with an x slice that leaves room for two workgroups per CU at B = 3/4:
+# the 1024-thread workgroup variant of the gated-MLP kernel
+WIDE = [(1500, 8192, 4), (1100, 9216, 3)]
 
 
-@pytest.mark.parametrize("R,K", SHAPES)
-@pytest.mark.parametrize("B", [1, 3, 8])
+@pytest.mark.parametrize("R,K,B", [(R, K, B) for R, K in SHAPES for B in (1, 3, 8)] + WIDE)
 def test_swiglu_sparse_and_dense(R, K, B):
     say("swiglu", R, K, B)
     n = oracle.col_norm(synth.calib_acts(K, 8, R, K))
