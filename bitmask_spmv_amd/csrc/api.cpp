@@ -93,8 +93,8 @@ nmk::MvPlan spmv_unstructured_plan(int64_t R, int64_t K, int B) {
     return p;
 }
 
-nmk::MvPlan dense_plan(int64_t R, int64_t K, int B) {
-    nmk::MvPlan p = nmk::plan_dense(R, K, B, device_info());
+nmk::MvPlan dense_plan(int64_t R, int64_t K, int B, int epi = nmk::kEpiNone) {
+    nmk::MvPlan p = nmk::plan_dense(R, K, B, device_info(), epi);
     apply_override("NM_DENSE_PLAN", K / 8, R, B, (size_t)B * 16, p);
     return p;
 }
@@ -561,7 +561,7 @@ nm_status dense_gemv(const nm_bf16 *W, int64_t ldw, int64_t R, int64_t K, const 
 
 size_t dense_gemv_swiglu_workspace_bytes(int64_t R, int64_t K, int B) {
     if (R < 1 || R > kMaxDim / 2 || K < 8 || K % 8 != 0 || K > kMaxDim || B < 1 || B > 8) return 0;
-    return dense_plan(2 * R, K, B).ws_bytes;
+    return dense_plan(2 * R, K, B, nmk::kEpiSwiGLU).ws_bytes;
 }
 
 nm_status dense_gemv_swiglu(const nm_bf16 *W_gate, const nm_bf16 *W_up, int64_t ldw, int64_t R, int64_t K,
@@ -587,7 +587,7 @@ nm_status dense_gemv_swiglu(const nm_bf16 *W_gate, const nm_bf16 *W_up, int64_t 
         set.ldw[0] = set.ldw[1] = ldw;
         set.y[0] = set.y[1] = h;
         set.ldy[0] = set.ldy[1] = ldh;
-        const nmk::MvPlan p = dense_plan(2 * R, K, B);
+        const nmk::MvPlan p = dense_plan(2 * R, K, B, nmk::kEpiSwiGLU);
         if (p.ws_bytes > 0) {
             if (!workspace || workspace_bytes < p.ws_bytes || !aligned(workspace, 4))
                 return fail(NM_ERR_WORKSPACE, "%s: workspace of %zu bytes required, %zu given", who, p.ws_bytes,

@@ -18,6 +18,14 @@ namespace nmk {
 namespace {
 
 constexpr int kThreads = 512;
+
+// 1024-thread workgroups (16 waves, at most 64 VGPRs so two fit per CU) when the x slice
+// leaves room for only two workgroups per CU, for the instantiations that fit that
+// register budget: B = 3 and 4, except the gated-MLP kernel with four chunks per lane at
+// B = 4.  The same rule as the sparse kernel's, so the baseline gets the same occupancy.
+constexpr bool dense_wide_ok(int B, int U, int EPI) {
+    return (B == 3 || B == 4) && !(EPI == kEpiSwiGLU && B == 4 && U == 4);
+}
 constexpr size_t kLdsCap = 80 * 1024;
 constexpr size_t kLdsPerCu = 160 * 1024;
 
@@ -151,8 +159,8 @@ __device__ __forceinline__ void load_row_dbatch(DBatch<U> &bt, const DenseSet &s
     load_dbatch<U>(bt, wrow, chunks, base, lane);
 }
 
-template <int B, int U, int EPI>
-__global__ __launch_bounds__(kThreads) void dense_kernel(const DenseSet set, int KC, const uint16_t *__restrict__ x,
+template <int B, int U, int EPI, int NT>
+__global__ __launch_bounds__(NT, NT == 1024 ? 8 : 1) void dense_kernel(const DenseSet set, int KC, const uint16_t *__restrict__ x,
                                                          int64_t ldx, float *__restrict__ partial, int slice) {
     const int R = set.row0[set.P];
     extern __shared__ u32x4 xs4[];  // [B][ncs]
@@ -161,7 +169,7 @@ __global__ __launch_bounds__(kThreads) void dense_kernel(const DenseSet set, int
     const int ncs = min(slice, KC - c0);
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    constexpr int kWaves = kThreads / kWave;
+    constexpr int kWaves = NT / kWave;
 
     // Same flat, software-pipelined walk over (row, batch) as the sparse kernel, with the
     // same row order (row pairs for the gated MLP).
@@ -185,11 +193,11 @@ __global__ __launch_bounds__(kThreads) void dense_kernel(const DenseSet set, int
     {
         constexpr int kStage = 4;
         const int chunks = B * ncs;
-        for (int i0 = 0; i0 < chunks || i0 == 0; i0 += kThreads * kStage) {
+        for (int i0 = 0; i0 < chunks || i0 == 0; i0 += NT * kStage) {
             u32x4 r[kStage];
 #pragma unroll
             for (int j = 0; j < kStage; ++j) {
-                const int i = i0 + j * kThreads + (int)threadIdx.x;
+                const int i = i0 + j * NT + (int)threadIdx.x;
                 if (i < chunks) {
                     const int b = i / ncs;
                     r[j] = reinterpret_cast<const u32x4 *>(x + (int64_t)b * ldx)[c0 + (i - b * ncs)];
@@ -198,7 +206,7 @@ __global__ __launch_bounds__(kThreads) void dense_kernel(const DenseSet set, int
             if (i0 == 0) load_row_dbatch<U, EPI>(bufA, set, min(rowA, R - 1), c0, total > 0 ? ncs : 0, 0, lane);
 #pragma unroll
             for (int j = 0; j < kStage; ++j) {
-                const int i = i0 + j * kThreads + (int)threadIdx.x;
+                const int i = i0 + j * NT + (int)threadIdx.x;
                 if (i < chunks) xs4[i] = r[j];
             }
         }
@@ -280,7 +288,7 @@ __global__ __launch_bounds__(256) void dense_finish_swiglu_kernel(const float *_
     }
 }
 
-template <int B, int U, int EPI>
+template <int B, int U, int EPI, int NT>
 hipError_t allow_lds(size_t bytes) {
     static std::atomic<uint64_t> done{0};
     if (bytes <= 64 * 1024) return hipSuccess;
@@ -289,20 +297,20 @@ hipError_t allow_lds(size_t bytes) {
     if (e != hipSuccess) return e;
     const uint64_t bit = 1ull << (dev & 63);
     if (done.load(std::memory_order_acquire) & bit) return hipSuccess;
-    e = hipFuncSetAttribute((const void *)dense_kernel<B, U, EPI>, hipFuncAttributeMaxDynamicSharedMemorySize,
+    e = hipFuncSetAttribute((const void *)dense_kernel<B, U, EPI, NT>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)kLdsCap);
     if (e == hipSuccess) done.fetch_or(bit, std::memory_order_acq_rel);
     return e;
 }
 
-template <int B, int U, int EPI>
-hipError_t launch_bu(const MvPlan &p, const DenseSet &set, int64_t K, const uint16_t *x, int64_t ldx, float *ws,
-                     hipStream_t st) {
-    hipError_t e = allow_lds<B, U, EPI>(p.lds_bytes);
+template <int B, int U, int EPI, int NT>
+hipError_t launch_bun(const MvPlan &p, const DenseSet &set, int64_t K, const uint16_t *x, int64_t ldx, float *ws,
+                      hipStream_t st) {
+    hipError_t e = allow_lds<B, U, EPI, NT>(p.lds_bytes);
     if (e != hipSuccess) return e;
     DenseSet padded = set;  // row0 past the last matrix = the total (see owner())
     for (int q = set.P + 1; q <= kMaxMats; ++q) padded.row0[q] = set.row0[set.P];
-    hipLaunchKernelGGL((dense_kernel<B, U, EPI>), dim3(p.grid_x, p.splits), dim3(kThreads), p.lds_bytes, st, padded,
+    hipLaunchKernelGGL((dense_kernel<B, U, EPI, NT>), dim3(p.grid_x, p.splits), dim3(NT), p.lds_bytes, st, padded,
                        (int)(K / 8), x, ldx, ws, p.slice);
     e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;
@@ -314,6 +322,14 @@ hipError_t launch_bu(const MvPlan &p, const DenseSet &set, int64_t K, const uint
         hipLaunchKernelGGL(dense_finish_kernel<B>, dim3((unsigned)((R + 255) / 256)), dim3(256), 0, st, ws,
                            p.splits, set);
     return hipGetLastError();
+}
+
+template <int B, int U, int EPI>
+hipError_t launch_bu(const MvPlan &p, const DenseSet &set, int64_t K, const uint16_t *x, int64_t ldx, float *ws,
+                     hipStream_t st) {
+    if constexpr (dense_wide_ok(B, U, EPI))
+        if (p.threads == 1024) return launch_bun<B, U, EPI, 1024>(p, set, K, x, ldx, ws, st);
+    return launch_bun<B, U, EPI, kThreads>(p, set, K, x, ldx, ws, st);
 }
 
 template <int B, int EPI>
@@ -342,7 +358,7 @@ hipError_t launch_e(const MvPlan &p, const DenseSet &set, int64_t K, const uint1
 
 }  // namespace
 
-MvPlan plan_dense(int64_t R, int64_t K, int B, const DeviceInfo &dev) {
+MvPlan plan_dense(int64_t R, int64_t K, int B, const DeviceInfo &dev, int epi) {
     MvPlan p;
     p.threads = kThreads;
     const int64_t KC = K / 8;  // 16-byte chunks per row
@@ -372,13 +388,16 @@ MvPlan plan_dense(int64_t R, int64_t K, int B, const DeviceInfo &dev) {
     int per_cu = (int)(kLdsPerCu / (p.lds_bytes > 0 ? p.lds_bytes : 1));
     if (per_cu > 4) per_cu = 4;
     if (per_cu < 1) per_cu = 1;
-    const int64_t waves = kThreads / kWave;
+    p.unroll = slice >= 4 * kWave ? 4 : (slice > kWave ? 2 : 1);
+    if (per_cu <= 2 && (R + kThreads / kWave - 1) / (kThreads / kWave) * splits >= cu &&
+        dense_wide_ok(B, p.unroll, epi))
+        p.threads = 1024;
+    const int64_t waves = p.threads / kWave;
     int64_t gx = (R + waves - 1) / waves;
     int64_t cap_x = (per_cu * cu + splits - 1) / splits;
     if (gx > cap_x) gx = cap_x;
     if (gx < 1) gx = 1;
     p.grid_x = (int)gx;
-    p.unroll = slice >= 4 * kWave ? 4 : (slice > kWave ? 2 : 1);
     p.ws_bytes = splits > 1 ? (size_t)splits * B * R * sizeof(float) : 0;
     return p;
 }

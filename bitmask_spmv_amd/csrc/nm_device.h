@@ -108,14 +108,7 @@ __device__ __forceinline__ float wave_sum(float v) {
     return (r0 + r1) + (r2 + r3);
 }
 
-// Row epilogues of the matrix-vector kernels.  kEpiNone: every row's total is one
-// output.  kEpiSwiGLU: the set is the gate (matrix 0) and up (matrix 1) projections of a
-// gated MLP with R rows each; launch row 2i is gate row i and 2i+1 up row i, a wave walks
-// the two back to back and writes h_i = silu(g_i) * u_i (fp32, one bf16 rounding) to
-// matrix 0's output.
-constexpr int kEpiNone = 0;
-constexpr int kEpiSwiGLU = 1;
-
+// Gated-MLP epilogue (kEpiSwiGLU, nm_kernels.h): h = silu(g) * u in fp32.
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.f + __expf(-g)) * u; }
 
 // Position of the lowest set bit of m, and 31 when m has no bit set.  (__builtin_ctz is

@@ -29,6 +29,14 @@ struct MvPlan {
     size_t ws_bytes = 0;    // workspace bytes (0 when splits == 1)
 };
 
+// Row epilogues of the matrix-vector kernels.  kEpiNone: every row's total is one
+// output.  kEpiSwiGLU: the set is the gate (matrix 0) and up (matrix 1) projections of a
+// gated MLP with R rows each; launch row 2i is gate row i and 2i+1 up row i, a wave walks
+// the two back to back and writes h_i = silu(g_i) * u_i (fp32, one bf16 rounding) to
+// matrix 0's output.
+constexpr int kEpiNone = 0;
+constexpr int kEpiSwiGLU = 1;
+
 // Matrices that read the same input x (q, k, v; gate, up) walked by one launch: global
 // row r belongs to matrix p when row0[p] <= r < row0[p + 1]; x is staged once.
 constexpr int kMaxMats = 8;
@@ -61,7 +69,9 @@ struct DenseSet {
 // kernels that fit them without spilling).
 MvPlan plan_spmv(int64_t R, int64_t K, int B, const DeviceInfo &dev, int fmt = kMetaBitmask);
 size_t spmv_lds_per_word(int B);  // LDS bytes of x per 32-column block
-MvPlan plan_dense(int64_t R, int64_t K, int B, const DeviceInfo &dev);
+// epi: the launch's epilogue, which decides whether the 1024-thread workgroup variant
+// fits without spilling.
+MvPlan plan_dense(int64_t R, int64_t K, int B, const DeviceInfo &dev, int epi = kEpiNone);
 
 hipError_t launch_col_norm(const uint16_t *X, int64_t T, int64_t K, int64_t ldx, float *n, hipStream_t st);
 hipError_t launch_prune_pack(const uint16_t *W, int64_t ldw, int64_t R, int64_t K, const float *n, int N, int M,

@@ -169,7 +169,8 @@ def test_spmv_every_batch_size(B):
 
 
 # x slices large enough that only two workgroups fit per CU at B = 3 and 4: the bitmask
-# kernel then runs 1024-thread workgroups (incl. split rows for K = 28672).
+# kernel and the dense GEMV then run 1024-thread workgroups (incl. split rows for
+# K = 28672).
 WIDE = [(3000, 8192, 3), (2100, 8192, 4), (700, 28672, 4), (2049, 9216, 3)]
 
 
@@ -188,6 +189,10 @@ def test_spmv_wide_workgroups(R, K, B):
     assert (host_bf16(y) == host_bf16(y2)).all()
     assert_within(host_bf16(ys[0]), yref, absum, "multi matrix 0")
     assert_within(host_bf16(ys[1]), yref[:, : R // 3], absum[:, : R // 3], "multi matrix 1")
+    # the dense baseline takes 1024-thread workgroups on the same shapes
+    yd = nm.dense_gemv(dev_bf16(W), xd)
+    ydref, adabs = oracle.dense(W, x, nthreads=4)
+    assert_within(host_bf16(yd), ydref, adabs, f"dense wide R={R} K={K} B={B}")
 
 
 @pytest.mark.parametrize("N,M", PATTERNS)
