@@ -6,7 +6,6 @@
 #include <atomic>
 #include <cstdarg>
 #include <cstdio>
-#include <cstdlib>
 #include <cstring>
 
 #include "nm_spmv.h"
@@ -64,28 +63,8 @@ nmk::DeviceInfo device_info() {
     return d;
 }
 
-// Optional launch-plan override for tuning sweeps: "<splits>,<grid_x>,<unroll>"
-// (0 keeps the planner's choice for that field; unroll only affects the dense kernel).  The slice length follows from splits.
-void apply_override(const char *env, int64_t units, int64_t R, int B, size_t unit_lds, nmk::MvPlan &p) {
-    const char *s = std::getenv(env);
-    if (!s || !*s) return;
-    int sp = 0, gx = 0, un = 0;
-    if (std::sscanf(s, "%d,%d,%d", &sp, &gx, &un) < 1) return;
-    if (sp > 0) {
-        int64_t slice = (units + sp - 1) / sp;
-        p.slice = (int)slice;
-        p.splits = (int)((units + slice - 1) / slice);
-        p.lds_bytes = (size_t)slice * unit_lds;
-        p.ws_bytes = p.splits > 1 ? (size_t)p.splits * B * R * sizeof(float) : 0;
-    }
-    if (gx > 0) p.grid_x = gx;
-    if (un == 1 || un == 2 || un == 4) p.unroll = un;
-}
-
 nmk::MvPlan spmv_plan(int64_t R, int64_t K, int B, int fmt = nmk::kMetaBitmask) {
-    nmk::MvPlan p = nmk::plan_spmv(R, K, B, device_info(), fmt);
-    apply_override("NM_SPMV_PLAN", K / 32, R, B, nmk::spmv_lds_per_word(B), p);
-    return p;
+    return nmk::plan_spmv(R, K, B, device_info(), fmt);
 }
 
 nmk::MvPlan spmv_unstructured_plan(int64_t R, int64_t K, int B) {
@@ -94,9 +73,7 @@ nmk::MvPlan spmv_unstructured_plan(int64_t R, int64_t K, int B) {
 }
 
 nmk::MvPlan dense_plan(int64_t R, int64_t K, int B, int epi = nmk::kEpiNone) {
-    nmk::MvPlan p = nmk::plan_dense(R, K, B, device_info(), epi);
-    apply_override("NM_DENSE_PLAN", K / 8, R, B, (size_t)B * 16, p);
-    return p;
+    return nmk::plan_dense(R, K, B, device_info(), epi);
 }
 
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
