@@ -17,9 +17,10 @@
 //   * x lives in LDS for the whole workgroup: each 32-column block of x occupies 17
 //     dwords (16 data + 1 pad), so lanes that walk consecutive words land on different
 //     banks even when their bit positions agree.
-//   * word-per-lane mapping on the canonical row-major layout: lane l of a wave takes
-//     word w0+l of the row, so one wave iteration loads 256 contiguous bytes of masks
-//     and 2 KiB of contiguous values (two 16-byte loads per lane), all non-temporal.
+//   * word-per-lane mapping on the canonical row-major layout: each lane of a wave takes
+//     one word of a 64-word strip of the row, so one wave iteration loads 256 contiguous
+//     bytes of masks and 2 KiB of contiguous values (two 16-byte loads per lane), all
+//     non-temporal; the next strip's loads go out before the current strip is walked.
 //   * 16 steps per word = 8 pairs; each pair gathers two bf16 inputs from LDS into one
 //     dword and feeds v_dot2_f32_bf16 with the matching packed value pair.
 //   * each wave owns whole rows (or row slices); the row total is a wave64 reduction.
