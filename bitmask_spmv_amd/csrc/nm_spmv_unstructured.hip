@@ -202,19 +202,25 @@ __global__ __launch_bounds__(kUThreads) void spmv_unstructured_kernel(const uint
         // lowest-set-bit scan), reads the zero pad in front of its block as x and so adds
         // exactly 0 whatever finite value the window holds at its (then foreign) index; the
         // window is rewritten in full for every strip and sized for the largest index.
+        // Four pairs per check of the wave's remaining bits, so the LDS reads of several
+        // pairs overlap; a word has at most 16 pairs, a multiple of four, so no lane reads
+        // past the index bound the window is sized for.
         uint32_t mm = m_walk;
         int vi = vi0;
         while (__builtin_amdgcn_ballot_w64(mm != 0)) {
-            const int c0 = __builtin_ctzg(mm, -1);
-            mm &= mm - 1;
-            const int c1 = __builtin_ctzg(mm, -1);
-            mm &= mm - 1;
-            // the pair (vi, vi+1) from the two aligned dwords around it (a dword read at a
-            // 2-byte offset would be a slow misaligned LDS access)
-            const uint32_t *w32 = reinterpret_cast<const uint32_t *>(win) + (vi >> 1);
-            const uint32_t pr = __builtin_amdgcn_alignbit(w32[1], w32[0], (uint32_t)(vi & 1) * 16u);
-            dot_pair<B>(pr, blk, c0, c1, acc);
-            vi += 2;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int c0 = __builtin_ctzg(mm, -1);
+                mm &= mm - 1;
+                const int c1 = __builtin_ctzg(mm, -1);
+                mm &= mm - 1;
+                // the pair (vi, vi+1) from the two aligned dwords around it (a dword read at
+                // a 2-byte offset would be a slow misaligned LDS access)
+                const uint32_t *w32 = reinterpret_cast<const uint32_t *>(win) + (vi >> 1);
+                const uint32_t pr = __builtin_amdgcn_alignbit(w32[1], w32[0], (uint32_t)(vi & 1) * 16u);
+                dot_pair<B>(pr, blk, c0, c1, acc);
+                vi += 2;
+            }
         }
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // reads before the next strip's writes
 
