@@ -403,6 +403,28 @@ def test_spmv_multi_split_rows_and_single_matrix():
     assert_within(host_bf16(y1), *refs[0], "single-matrix multi")
 
 
+@pytest.mark.parametrize("P", [7, 8])
+def test_spmv_multi_many_ragged_matrices(P):
+    """Up to the maximum of eight matrices per launch, with ragged row counts (1 row,
+    fewer rows than a workgroup's waves, rows not a multiple of 8): every launch row is
+    attributed to its own matrix and written to that matrix's output."""
+    say("spmv multi many", P)
+    K, B = 1024, 3
+    Rs = [5, 64, 1, 300, 17, 8, 129, 2][:P]
+    x = synth.decode_x(B, K, 20, P)
+    n = oracle.col_norm(synth.calib_acts(K, 20, P))
+    packed, refs = [], []
+    for i, R in enumerate(Rs):
+        W = synth.weights(R, K, 20, P, i)
+        mref, vref = oracle.prune_pack(W, n, 4, 8)
+        refs.append(oracle.spmv(mref, vref, x, K))
+        packed.append((dev_u32(mref), dev_bf16(vref)))
+    ys = nm.nm_spmv_multi(packed, dev_bf16(x))
+    for i, (y, (yref, absum)) in enumerate(zip(ys, refs)):
+        assert y.shape == (B, Rs[i])
+        assert_within(host_bf16(y), yref, absum, f"multi P={P} matrix {i}")
+
+
 @pytest.mark.parametrize("B", [1, 8])
 def test_dense_multi_matches_oracle(B):
     say("dense multi", B)
