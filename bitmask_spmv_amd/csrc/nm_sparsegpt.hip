@@ -36,6 +36,7 @@ namespace nmk {
 namespace {
 
 typedef double v4f64 __attribute__((ext_vector_type(4)));
+typedef double v2f64 __attribute__((ext_vector_type(2)));
 constexpr int kNB = 32;  // panel / column-block width
 
 __device__ __forceinline__ double bf16_to_f64(uint16_t b) { return (double)__uint_as_float((uint32_t)b << 16); }
@@ -254,12 +255,12 @@ __global__ __launch_bounds__(256) void syrk_kernel(double *__restrict__ A, int64
 }
 
 // ---------------------------------------------------------------- blocked lower-triangular inverse
-// Cinv[ib][ib] = inverse of the 32x32 lower block C[ib][ib]: column j of the inverse by
-// forward substitution (thread j).
+// Cinv[ib][ib] = inverse of the 32x32 lower block C[ib][ib] (ib = workgroup): column j of
+// the inverse by forward substitution (thread j).
 __global__ __launch_bounds__(64) void trtri_diag_kernel(const double *__restrict__ C, double *__restrict__ Ci,
-                                                        int64_t K, int ib) {
+                                                        int64_t K) {
     __shared__ double L[kNB][kNB + 1];
-    const int64_t o = (int64_t)ib * kNB;
+    const int64_t o = (int64_t)blockIdx.x * kNB;
     for (int e = threadIdx.x; e < kNB * kNB; e += 64) L[e / kNB][e % kNB] = C[(o + e / kNB) * K + o + e % kNB];
     __syncthreads();
     const int j = threadIdx.x;
@@ -276,47 +277,78 @@ __global__ __launch_bounds__(64) void trtri_diag_kernel(const double *__restrict
     for (int i = 0; i < kNB; ++i) Ci[(o + i) * K + o + j] = x[i];
 }
 
-// Off-diagonal blocks of block row ib: Cinv[ib][jb] = -Cinv[ib][ib] * sum_{kb=jb}^{ib-1}
-// C[ib][kb] Cinv[kb][jb]; one workgroup per jb < ib.  Also zeroes the strictly upper
-// blocks of the row (so Cinv is a clean lower-triangular matrix).
-__global__ __launch_bounds__(256) void trtri_row_kernel(const double *__restrict__ C, double *__restrict__ Ci,
-                                                        int64_t K, int ib) {
-    __shared__ double Cs[kNB][kNB + 1];
-    __shared__ double Ds[kNB][kNB + 1];
-    __shared__ double Ts[kNB][kNB + 1];
-    const int tid = threadIdx.x;
-    const int jb = blockIdx.x;
-    const int64_t oi = (int64_t)ib * kNB, oj = (int64_t)jb * kNB;
-    const int ti = tid >> 3, tj = (tid & 7) * 4;  // 32 rows x 8 groups of 4 columns
-    double acc[4] = {0.0, 0.0, 0.0, 0.0};
-    for (int kb = jb; kb < ib; ++kb) {
-        const int64_t ok = (int64_t)kb * kNB;
-        for (int e = tid; e < kNB * kNB; e += 256) {
-            Cs[e / kNB][e % kNB] = C[(oi + e / kNB) * K + ok + e % kNB];
-            Ds[e / kNB][e % kNB] = Ci[(ok + e / kNB) * K + oj + e % kNB];
+// Column block jb of Cinv = C^-1 by block forward substitution (C X = E_jb):
+//   X[ib][jb] = -Cinv[ib][ib] * sum_{kb=jb}^{ib-1} C[ib][kb] X[kb][jb],  ib = jb+1 .. nb-1,
+// with X[jb][jb] = Cinv[jb][jb] from trtri_diag_kernel.  Column blocks are independent, so
+// one launch runs all of them (workgroup jb), each reading C and only the blocks of its
+// own column that it wrote itself; the 32x32x32 block products run on fp64 MFMA, each of
+// the 4 waves computing one 16x16 quarter, with the next pair of tiles loaded into
+// registers while the current pair is multiplied.
+__global__ __launch_bounds__(256) void trtri_col_kernel(const double *__restrict__ C, double *__restrict__ Ci,
+                                                        int64_t K, int nb) {
+    __shared__ double As[kNB][kNB + 1];
+    __shared__ double Bs[kNB][kNB + 1];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t oj = (int64_t)blockIdx.x * kNB;
+    const int wi = (wave >> 1) * 16, wj = (wave & 1) * 16;  // this wave's quarter of a tile
+    const int lr = tid >> 3, lc = (tid & 7) * 4;             // tile loader: row, first of 4 columns
+    // D layout of a 16x16 f64 MFMA tile: lane l, element r -> row l/16 + 4*r, column l%16
+    const int dr = wi + (lane >> 4), dc = wj + (lane & 15);
+    for (int ib = (int)blockIdx.x + 1; ib < nb; ++ib) {
+        const int64_t oi = (int64_t)ib * kNB;
+        v2f64 c0, c1, x0, x1;  // 4 consecutive doubles of a C tile row and of an X tile row
+        auto load = [&](int kb) {
+            const int64_t ok = (int64_t)kb * kNB;
+            const v2f64 *pc = reinterpret_cast<const v2f64 *>(C + (oi + lr) * K + ok + lc);
+            const v2f64 *px = reinterpret_cast<const v2f64 *>(Ci + (ok + lr) * K + oj + lc);
+            c0 = pc[0];
+            c1 = pc[1];
+            x0 = px[0];
+            x1 = px[1];
+        };
+        load((int)blockIdx.x);
+        v4f64 acc = v4f64{0.0, 0.0, 0.0, 0.0};
+        for (int kb = (int)blockIdx.x; kb < ib; ++kb) {
+            __syncthreads();  // the previous products are done with As / Bs
+            As[lr][lc] = c0.x;
+            As[lr][lc + 1] = c0.y;
+            As[lr][lc + 2] = c1.x;
+            As[lr][lc + 3] = c1.y;
+            Bs[lr][lc] = x0.x;
+            Bs[lr][lc + 1] = x0.y;
+            Bs[lr][lc + 2] = x1.x;
+            Bs[lr][lc + 3] = x1.y;
+            __syncthreads();
+            if (kb + 1 < ib) load(kb + 1);
+#pragma unroll
+            for (int s = 0; s < kNB / 4; ++s) {
+                const int k = 4 * s + (lane >> 4);
+                acc = __builtin_amdgcn_mfma_f64_16x16x4f64(As[wi + (lane & 15)][k], Bs[k][wj + (lane & 15)], acc, 0, 0,
+                                                           0);
+            }
         }
+        // the sum to Bs, Cinv[ib][ib] to As, then X[ib][jb] = -Cinv[ib][ib] * sum
+        const v2f64 *pd = reinterpret_cast<const v2f64 *>(Ci + (oi + lr) * K + oi + lc);
+        const v2f64 d0 = pd[0], d1 = pd[1];
         __syncthreads();
-#pragma unroll 8
-        for (int k = 0; k < kNB; ++k) {
-            const double c = Cs[ti][k];
 #pragma unroll
-            for (int b = 0; b < 4; ++b) acc[b] = fma(c, Ds[k][tj + b], acc[b]);
+        for (int r = 0; r < 4; ++r) Bs[dr + 4 * r][dc] = acc[r];
+        As[lr][lc] = d0.x;
+        As[lr][lc + 1] = d0.y;
+        As[lr][lc + 2] = d1.x;
+        As[lr][lc + 3] = d1.y;
+        __syncthreads();
+        v4f64 out = v4f64{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+        for (int s = 0; s < kNB / 4; ++s) {
+            const int k = 4 * s + (lane >> 4);
+            out = __builtin_amdgcn_mfma_f64_16x16x4f64(As[wi + (lane & 15)][k], Bs[k][wj + (lane & 15)], out, 0, 0, 0);
         }
-        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Ci[(oi + dr + 4 * r) * K + oj + dc] = -out[r];
+        // the block is read back (through memory) by this workgroup's later rows
+        __threadfence();
     }
-#pragma unroll
-    for (int b = 0; b < 4; ++b) Ts[ti][tj + b] = acc[b];
-    for (int e = tid; e < kNB * kNB; e += 256) Ds[e / kNB][e % kNB] = Ci[(oi + e / kNB) * K + oi + e % kNB];
-    __syncthreads();
-    double out[4] = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll 8
-    for (int k = 0; k < kNB; ++k) {
-        const double d = Ds[ti][k];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) out[b] = fma(d, Ts[k][tj + b], out[b]);
-    }
-#pragma unroll
-    for (int b = 0; b < 4; ++b) Ci[(oi + ti) * K + oj + tj + b] = -out[b];
 }
 
 __global__ __launch_bounds__(256) void zero_upper_kernel(double *__restrict__ Ci, int64_t K) {
@@ -491,10 +523,8 @@ hipError_t launch_inverse_factor(const double *H, int64_t ldh, int64_t K, double
         }
     }
     hipLaunchKernelGGL(zero_upper_kernel, dim3(blocks_for(K * K)), dim3(256), 0, st, Ci, K);
-    for (int ib = 0; ib < nb; ++ib) {
-        hipLaunchKernelGGL(trtri_diag_kernel, dim3(1), dim3(64), 0, st, A, Ci, K, ib);
-        if (ib > 0) hipLaunchKernelGGL(trtri_row_kernel, dim3((unsigned)ib), dim3(256), 0, st, A, Ci, K, ib);
-    }
+    hipLaunchKernelGGL(trtri_diag_kernel, dim3((unsigned)nb), dim3(64), 0, st, A, Ci, K);
+    hipLaunchKernelGGL(trtri_col_kernel, dim3((unsigned)nb), dim3(256), 0, st, A, Ci, K, nb);
     hipLaunchKernelGGL(flip_kernel, dim3(blocks_for(K * K)), dim3(256), 0, st, Ci, K, U, ldu);
     return hipGetLastError();
 }
