@@ -67,6 +67,14 @@ nmk::MvPlan spmv_plan(int64_t R, int64_t K, int B, int fmt = nmk::kMetaBitmask) 
     return nmk::plan_spmv(R, K, B, device_info(), fmt);
 }
 
+// Plan of one launch over a validated set: the matrix-core tile kernel where it applies
+// (bitmask, B >= 5, K a multiple of 1024), else the word-per-lane kernel.
+nmk::MvPlan spmv_set_plan(const nmk::SpmvSet &set, int fmt, int64_t K, int64_t ldx, int B, int epi) {
+    if (nmk::spmv_tile_ok(set, K, ldx, B, fmt, epi))
+        return nmk::plan_spmv_tile(set.row0[set.P], B, device_info(), epi);
+    return spmv_plan(set.row0[set.P], K, B, fmt);
+}
+
 nmk::MvPlan spmv_unstructured_plan(int64_t R, int64_t K, int B) {
     nmk::MvPlan p = nmk::plan_spmv_unstructured(R, K, B, device_info());
     return p;
@@ -154,14 +162,14 @@ size_t nm_spmv_workspace_bytes(int64_t R, int64_t K, int B) {
 // Shared body of nm_spmv / nm_spmv_multi once the matrices are validated into a set.
 static nm_status spmv_run(const nmk::SpmvSet &set, int fmt, int64_t K, const nm_bf16 *x, int64_t ldx, int B,
                           void *workspace, size_t workspace_bytes, void *hip_stream, const char *who) {
-    const int64_t R = set.row0[set.P];
-    const nmk::MvPlan p = spmv_plan(R, K, B, fmt);
+    const nmk::MvPlan p = spmv_set_plan(set, fmt, K, ldx, B, nmk::kEpiNone);
     if (p.ws_bytes > 0) {
         if (!workspace || workspace_bytes < p.ws_bytes || !aligned(workspace, 4))
             return fail(NM_ERR_WORKSPACE, "%s: workspace of %zu bytes required, %zu given", who, p.ws_bytes,
                         workspace ? workspace_bytes : (size_t)0);
     }
-    hipError_t e = nmk::launch_spmv(p, set, fmt, K, x, ldx, B, (float *)workspace, (hipStream_t)hip_stream);
+    hipError_t e = p.tile ? nmk::launch_spmv_tile(p, set, K, x, ldx, B, nmk::kEpiNone, (hipStream_t)hip_stream)
+                          : nmk::launch_spmv(p, set, fmt, K, x, ldx, B, (float *)workspace, (hipStream_t)hip_stream);
     if (e != hipSuccess) return hip_fail(who, e);
     return NM_OK;
 }
@@ -320,13 +328,16 @@ nm_status nm_spmv_swiglu(const uint32_t *gate_masks, const nm_bf16 *gate_values,
         set.ldy[0] = ldh;
         set.y[1] = h;  // unused: the epilogue writes matrix 0's output only
         set.ldy[1] = ldh;
-        const nmk::MvPlan p = spmv_plan(2 * R, K, B);
+        const nmk::MvPlan p = spmv_set_plan(set, NM_META_BITMASK, K, ldx, B, nmk::kEpiSwiGLU);
         if (p.ws_bytes > 0) {
             if (!workspace || workspace_bytes < p.ws_bytes || !aligned(workspace, 4))
                 return fail(NM_ERR_WORKSPACE, "%s: workspace of %zu bytes required, %zu given", who, p.ws_bytes,
                             workspace ? workspace_bytes : (size_t)0);
         }
-        hipError_t e = nmk::launch_spmv_swiglu(p, set, K, x, ldx, B, (float *)workspace, (hipStream_t)hip_stream);
+        hipError_t e = p.tile
+                           ? nmk::launch_spmv_tile(p, set, K, x, ldx, B, nmk::kEpiSwiGLU, (hipStream_t)hip_stream)
+                           : nmk::launch_spmv_swiglu(p, set, K, x, ldx, B, (float *)workspace,
+                                                     (hipStream_t)hip_stream);
         if (e != hipSuccess) return hip_fail(who, e);
         return NM_OK;
     } catch (...) {

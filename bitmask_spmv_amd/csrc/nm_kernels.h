@@ -27,6 +27,8 @@ struct MvPlan {
     int unroll = 1;         // dense kernel: 8-column chunks per lane and batch (1, 2 or 4)
     size_t lds_bytes = 0;   // dynamic LDS per workgroup
     size_t ws_bytes = 0;    // workspace bytes (0 when splits == 1)
+    int tile = 0;           // 1: the matrix-core tile kernel (nm_spmv_tile.hip), 16-row tiles
+    int tiles = 0;          // tile kernel: number of 16-row tiles
 };
 
 // Row epilogues of the matrix-vector kernels.  kEpiNone: every row's total is one
@@ -104,6 +106,16 @@ hipError_t launch_spmv(const MvPlan &p, const SpmvSet &set, int fmt, int64_t K, 
 // silu(gate x) * (up x).  Plan for 2R rows.
 hipError_t launch_spmv_swiglu(const MvPlan &p, const SpmvSet &set, int64_t K, const uint16_t *x, int64_t ldx, int B,
                               float *ws, hipStream_t st);
+// Bitmask launches with B >= kTileMinB tokens can run on the matrix cores: each 16-row
+// tile of mask words is expanded into a dense tile in LDS and multiplied by the inputs
+// with MFMA.  spmv_tile_ok says whether a set qualifies (K a multiple of 1024, matrices
+// of a plain set starting at multiples of 16 rows, 32-bit buffer ranges); the tile plan
+// needs no workspace.  R = rows of the launch (gated MLP: 2 x the rows of each matrix).
+constexpr int kTileMinB = 5;
+bool spmv_tile_ok(const SpmvSet &set, int64_t K, int64_t ldx, int B, int fmt, int epi);
+MvPlan plan_spmv_tile(int64_t R, int B, const DeviceInfo &dev, int epi);
+hipError_t launch_spmv_tile(const MvPlan &p, const SpmvSet &set, int64_t K, const uint16_t *x, int64_t ldx, int B,
+                            int epi, hipStream_t st);
 hipError_t launch_dense(const MvPlan &p, const DenseSet &set, int64_t K, const uint16_t *x, int64_t ldx, int B,
                         float *ws, hipStream_t st);
 hipError_t launch_dense_swiglu(const MvPlan &p, const DenseSet &set, int64_t K, const uint16_t *x, int64_t ldx, int B,

@@ -162,19 +162,6 @@ __device__ __forceinline__ void walk_batch(const Batch<FMT> &bt, const uint32_t 
     }
 }
 
-// Matrix of the set that owns global row r (0 <= r < R).  The launcher pads row0 past
-// the last matrix with the total row count, so p counts the bounds row0[q] <= r.  The
-// test is the sign of row0[q] - 1 - r (no overflow for 0 <= r, row0[q] <= INT_MAX),
-// which keeps it in scalar integer arithmetic: a boolean compare is materialised
-// through a vector register here, and reusing that register makes the wave wait for
-// its in-flight loads.
-__device__ __forceinline__ int owner(const SpmvSet &set, int r) {
-    int p = 0;
-#pragma unroll
-    for (int q = 1; q < kMaxMats; ++q) p += (int)((uint32_t)(set.row0[q] - 1 - r) >> 31);
-    return p;
-}
-
 // Matrix and row within it of launch row r.
 template <int EPI>
 __device__ __forceinline__ void locate(const SpmvSet &set, int r, int &p, int &local) {

@@ -4,6 +4,7 @@
 #pragma once
 
 #include "nm_device.h"
+#include "nm_kernels.h"
 
 namespace nmk {
 namespace {
@@ -70,6 +71,19 @@ __device__ __forceinline__ void dot_pair(uint32_t v, const uint32_t *blk, int c0
                 acc[2 * j + 1] = dot2_bf16(v, __builtin_amdgcn_perm(d1[j], d0[j], 0x07060302u), acc[2 * j + 1]);
         }
     }
+}
+
+// Matrix of the set that owns global row r (0 <= r < R).  The launcher pads row0 past
+// the last matrix with the total row count, so p counts the bounds row0[q] <= r.  The
+// test is the sign of row0[q] - 1 - r (no overflow for 0 <= r, row0[q] <= INT_MAX),
+// which keeps it in scalar integer arithmetic: a boolean compare is materialised
+// through a vector register here, and reusing that register makes the wave wait for
+// its in-flight loads.
+__device__ __forceinline__ int owner(const SpmvSet &set, int r) {
+    int p = 0;
+#pragma unroll
+    for (int q = 1; q < kMaxMats; ++q) p += (int)((uint32_t)(set.row0[q] - 1 - r) >> 31);
+    return p;
 }
 
 // Stages columns [32*w0, 32*(w0+nws)) of x (B tokens, row stride ldx) into LDS in the
