@@ -502,11 +502,17 @@ def main():
                 cnt = min(len(pool_sparse[(N, M), name]), max(2, math.ceil(ROTATE_BYTES / nb)))
                 pool = [(nm.nm_meta_from_mask(mk, fmt), v) for mk, v in pool_sparse[(N, M), name][:cnt]]
                 if fmt == nm.NM_META_U8_OFFSET:
-                    # same lanes and summation order as the bitmask kernel: identical bits
+                    # same lanes and summation order as the word-per-lane bitmask kernel:
+                    # identical bits; the bitmask launch runs on the matrix cores instead
+                    # for B >= 5 and K a multiple of 1024 (other order: agreement only)
                     mk0, v0 = pool_sparse[(N, M), name][0]
                     yb = nm.nm_spmv(mk0, v0, xs[group][0], workspace=ws)
                     ym = nm.nm_spmv_meta(pool[0][0], fmt, v0, xs[group][0], workspace=ws)
-                    assert torch.equal(yb.view(torch.int16), ym.view(torch.int16)), f"{key} {name} != bitmask"
+                    if B < 5 or K % 1024:
+                        assert torch.equal(yb.view(torch.int16), ym.view(torch.int16)), f"{key} {name} != bitmask"
+                    else:
+                        yf, mf = yb.float(), ym.float()
+                        assert float((yf - mf).abs().max()) <= 1e-2 * float(yf.abs().max()), f"{key} {name} != bitmask"
                 fns = [(lambda mt=mt, v=v, x=xs[group][i % L]:
                         nm.nm_spmv_meta(mt, fmt, v, x, out=ys[name], workspace=ws)) for i, (mt, v) in enumerate(pool)]
                 g = capture(torch, fns)
