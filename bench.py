@@ -41,6 +41,12 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 FP64_MFMA_PEAK_TFLOPS = 78.6
 ROTATE_BYTES = 512e6
+# Launches per timed graph: a rotation pool is cycled (buffer i % pool) in whole passes
+# up to at least this many launches, so the cost of starting a graph replay is spread
+# over as many dispatches as the pages' protocol times (50), and every buffer -- also
+# across back-to-back replays -- is re-read only after the whole pool (>= 512 MB).
+TIMED_LAUNCHES = 64
+TIMED_REPLAYS = 5
 METRIC = "nm_spmv GB/s and % HBM peak per layer; speedup vs dense bf16 GEMV, batch 1"
 
 # Layer shapes (rows R = outputs, K = inputs) of the models the pages evaluate.
@@ -154,6 +160,18 @@ class Timer:
         e1.record()
         t.cuda.synchronize()
         return e0.elapsed_time(e1) / reps  # ms per replay
+
+
+def time_launches(torch, timer, fns):
+    """Average µs per launch of a rotation: one graph of whole passes over the pool's
+    launches (at least TIMED_LAUNCHES), replayed once untimed, then the median of
+    TIMED_REPLAYS event-timed replays."""
+    n = -(-TIMED_LAUNCHES // len(fns)) * len(fns)
+    g = capture(torch, [fns[i % len(fns)] for i in range(n)])
+    g.replay()
+    t = sorted(timer.time_graph(g, 1) for _ in range(TIMED_REPLAYS))
+    del g
+    return t[len(t) // 2] * 1e3 / n
 
 
 def capture(torch, fns):
@@ -374,29 +392,21 @@ def main():
 
     # ---------------------------------------------------------------- per projection
     per = {}
-    reps = 3
     for (N, M) in patterns:
         for name, R, K, group in projs:
             pool = pool_sparse[(N, M), name]
             fns = [spmv_call(pk, xs[group][i % L], ys[name]) for i, pk in enumerate(pool)]
-            g = capture(torch, fns)
-            g.replay()
-            us = min(timer.time_graph(g, 1) for _ in range(reps)) * 1e3 / len(fns)
+            us = time_launches(torch, timer, fns)
             per.setdefault(name, {"R": R, "K": K})[f"{N}:{M}"] = {
                 "us": round(us, 2), "GBs": round(sparse_bytes(R, K, B) / us / 1e3, 1),
                 "pct_peak": round(100 * sparse_bytes(R, K, B) / us / 1e3 / HBM_PEAK_GBS, 1),
                 "rotation_MB": round(len(fns) * sparse_bytes(R, K, B) / 1e6)}
-            del g
     for name, R, K, group in projs:
         pool = pool_dense[name]
         fns = [dense_call(W, xs[group][i % L], ys[name]) for i, W in enumerate(pool)]
-        g = capture(torch, fns)
-        g.replay()
-        us = min(timer.time_graph(g, 1) for _ in range(reps)) * 1e3 / len(fns)
+        us = time_launches(torch, timer, fns)
         lin = [(lambda W=W, x=xs[group][i % L]: torch.nn.functional.linear(x, W)) for i, W in enumerate(pool)]
-        gl = capture(torch, lin)
-        gl.replay()
-        us_lin = min(timer.time_graph(gl, 1) for _ in range(reps)) * 1e3 / len(lin)
+        us_lin = time_launches(torch, timer, lin)
         d = per[name]
         d["dense_us"] = round(us, 2)
         d["dense_GBs"] = round(dense_bytes(R, K, B) / us / 1e3, 1)
@@ -404,7 +414,6 @@ def main():
         for (N, M) in patterns:
             d[f"{N}:{M}"]["speedup_vs_dense"] = round(us / d[f"{N}:{M}"]["us"], 3)
             d[f"{N}:{M}"]["speedup_vs_hipblaslt"] = round(us_lin / d[f"{N}:{M}"]["us"], 3)
-        del g, gl
     torch.cuda.synchronize()
 
     # ---------------------------------------------------------------- fused launches
@@ -433,22 +442,16 @@ def main():
         d = per.setdefault(label, {"R": [pr[1] for pr in grp], "K": grp[0][2]})
         for (N, M) in patterns:
             n_rot = min(len(pool_sparse[(N, M), pr[0]]) for pr in grp)
-            g = capture(torch, [fused_call(grp, i, N, M) for i in range(n_rot)])
-            g.replay()
-            us = min(timer.time_graph(g, 1) for _ in range(reps)) * 1e3 / n_rot
+            us = time_launches(torch, timer, [fused_call(grp, i, N, M) for i in range(n_rot)])
             d[f"{N}:{M}"] = {"us": round(us, 2), "GBs": round(fb / us / 1e3, 1),
                              "pct_peak": round(100 * fb / us / 1e3 / HBM_PEAK_GBS, 1),
                              "rotation_MB": round(n_rot * fb / 1e6)}
-            del g
         n_rot = min(len(pool_dense[pr[0]]) for pr in grp)
-        g = capture(torch, [fused_call(grp, i) for i in range(n_rot)])
-        g.replay()
-        us = min(timer.time_graph(g, 1) for _ in range(reps)) * 1e3 / n_rot
+        us = time_launches(torch, timer, [fused_call(grp, i) for i in range(n_rot)])
         d["dense_us"] = round(us, 2)
         d["dense_GBs"] = round(fdb / us / 1e3, 1)
         for (N, M) in patterns:
             d[f"{N}:{M}"]["speedup_vs_dense"] = round(us / d[f"{N}:{M}"]["us"], 3)
-        del g
         torch.cuda.synchronize()
         log(f"{label}: " + ", ".join(f"{k} {v['us']} us ({v['pct_peak']}%)" for k, v in d.items()
                                      if isinstance(v, dict)) + f"; dense {d['dense_us']} us")
@@ -465,10 +468,9 @@ def main():
             cnt = max(2, math.ceil(ROTATE_BYTES / nbytes))
             bufs = [torch.empty(nbytes // 4, dtype=torch.int32, device=dev) for _ in range(cnt)]
             sink = torch.empty(nm.nm_stream_read_sink_words(nbytes), dtype=torch.int32, device=dev)
-            g = capture(torch, [(lambda b=b: nm.nm_stream_read(b, sink=sink)) for b in bufs])
-            g.replay()
-            stream_us[nbytes] = min(timer.time_graph(g, 1) for _ in range(reps)) * 1e3 / cnt
-            del g, bufs
+            stream_us[nbytes] = time_launches(torch, timer, [(lambda b=b: nm.nm_stream_read(b, sink=sink))
+                                                             for b in bufs])
+            del bufs
         return nbytes, stream_us[nbytes]
 
     first_pat = f"{patterns[0][0]}:{patterns[0][1]}"
@@ -515,13 +517,11 @@ def main():
                         assert float((yf - mf).abs().max()) <= 1e-2 * float(yf.abs().max()), f"{key} {name} != bitmask"
                 fns = [(lambda mt=mt, v=v, x=xs[group][i % L]:
                         nm.nm_spmv_meta(mt, fmt, v, x, out=ys[name], workspace=ws)) for i, (mt, v) in enumerate(pool)]
-                g = capture(torch, fns)
-                g.replay()
-                us = min(timer.time_graph(g, 1) for _ in range(reps)) * 1e3 / len(fns)
+                us = time_launches(torch, timer, fns)
                 d[key] = {"us": round(us, 2), "GBs": round(nb / us / 1e3, 1), "bytes": nb,
                           "slowdown_vs_bitmask": round(us / bm["us"], 3),
                           "rotation_MB": round(len(fns) * nb / 1e6)}
-                del g, pool, fns
+                del pool, fns
             torch.cuda.synchronize()
         log("metadata formats (us): " + "; ".join(
             f"{n} bitmask {d['bitmask']['us']} u8 {d['u8_offset']['us']} i32 {d['i32_index']['us']}"
@@ -563,16 +563,14 @@ def main():
                 del W, n
             fns = [(lambda mk=mk, vl=vl, x=xs[group][i % L]:
                     nm.nm_spmv_unstructured(mk, vl, x, out=ys[name], workspace=ws)) for i, (mk, vl) in enumerate(pool)]
-            g = capture(torch, fns)
-            g.replay()
-            us = min(timer.time_graph(g, 1) for _ in range(reps)) * 1e3 / len(fns)
+            us = time_launches(torch, timer, fns)
             nmus = per[name][f"{N}:{M}"]["us"]
             unstructured[name] = {"R": R, "K": K, "us": round(us, 2), "GBs": round(nb_ / us / 1e3, 1),
                                   "pct_peak": round(100 * nb_ / us / 1e3 / HBM_PEAK_GBS, 1),
                                   f"nm_{N}:{M}_us": nmus, "slowdown_vs_nm": round(us / nmus, 3),
                                   "speedup_vs_dense": round(per[name]["dense_us"] / us, 3),
                                   "rotation_MB": round(len(fns) * nb_ / 1e6)}
-            del g, pool, fns
+            del pool, fns
             torch.cuda.synchronize()
         log("unstructured 50% (us): " + "; ".join(f"{n} {d['us']} (N:M {d[f'nm_{N}:{M}_us']}, dense "
                                                    f"x{d['speedup_vs_dense']})" for n, d in unstructured.items()))
