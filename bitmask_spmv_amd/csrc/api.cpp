@@ -71,7 +71,7 @@ nmk::MvPlan spmv_plan(int64_t R, int64_t K, int B, int fmt = nmk::kMetaBitmask) 
 // (bitmask, B >= 5, K a multiple of 1024), else the word-per-lane kernel.
 nmk::MvPlan spmv_set_plan(const nmk::SpmvSet &set, int fmt, int64_t K, int64_t ldx, int B, int epi) {
     if (nmk::spmv_tile_ok(set, K, ldx, B, fmt, epi))
-        return nmk::plan_spmv_tile(set.row0[set.P], B, device_info(), epi);
+        return nmk::plan_spmv_tile(set, K, B, device_info(), epi);
     return spmv_plan(set.row0[set.P], K, B, fmt);
 }
 

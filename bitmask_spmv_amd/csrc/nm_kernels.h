@@ -24,11 +24,11 @@ struct MvPlan {
     int slice = 0;          // units per slice
     int grid_x = 1;
     int threads = 512;      // workgroup size
-    int unroll = 1;         // dense kernel: 8-column chunks per lane and batch (1, 2 or 4)
+    int unroll = 1;         // dense kernel: 8-column chunks per lane and batch (1, 2 or 4); tile kernel: tiles per step
     size_t lds_bytes = 0;   // dynamic LDS per workgroup
     size_t ws_bytes = 0;    // workspace bytes (0 when splits == 1)
-    int tile = 0;           // 1: the matrix-core tile kernel (nm_spmv_tile.hip), 16-row tiles
-    int tiles = 0;          // tile kernel: number of 16-row tiles
+    int tile = 0;           // 1: the matrix-core tile kernel (nm_spmv_tile.hip), 16-row tiles (threads / 64 waves)
+    int tiles = 0;          // tile kernel: number of units (16 or 32 rows; unroll = tiles per unit)
 };
 
 // Row epilogues of the matrix-vector kernels.  kEpiNone: every row's total is one
@@ -113,7 +113,7 @@ hipError_t launch_spmv_swiglu(const MvPlan &p, const SpmvSet &set, int64_t K, co
 // needs no workspace.  R = rows of the launch (gated MLP: 2 x the rows of each matrix).
 constexpr int kTileMinB = 5;
 bool spmv_tile_ok(const SpmvSet &set, int64_t K, int64_t ldx, int B, int fmt, int epi);
-MvPlan plan_spmv_tile(int64_t R, int B, const DeviceInfo &dev, int epi);
+MvPlan plan_spmv_tile(const SpmvSet &set, int64_t K, int B, const DeviceInfo &dev, int epi);
 hipError_t launch_spmv_tile(const MvPlan &p, const SpmvSet &set, int64_t K, const uint16_t *x, int64_t ldx, int B,
                             int epi, hipStream_t st);
 hipError_t launch_dense(const MvPlan &p, const DenseSet &set, int64_t K, const uint16_t *x, int64_t ldx, int B,

@@ -37,6 +37,8 @@
 // offset and whose size ends at the last valid row, so rows past the matrix, token lanes
 // past B and the one batch issued past the end of the work read zeros without touching
 // memory, and every wave issues the same loads in the same order.
+#include <atomic>
+
 #include "nm_device.h"
 #include "nm_kernels.h"
 #include "nm_spmv_common.h"
@@ -44,9 +46,7 @@
 namespace nmk {
 namespace {
 
-constexpr int kTWaves = 8;
-constexpr int kTThreads = kTWaves * kWave;
-constexpr int kTRows = 16;                        // rows per tile (the MFMA's M)
+constexpr int kTRows = 16;                        // rows per MFMA tile (the MFMA's M)
 constexpr int kTStep = 4;                         // words per row and step
 constexpr int kTRowBytes = 16 + kTStep * 64;      // tile row: 16-byte lead pad + 4 x 32 bf16
 constexpr int kTWaveBytes = kTRows * kTRowBytes + 16;  // one wave's dense tile + a 16-byte tail pad
@@ -55,48 +55,61 @@ constexpr uint32_t kXOut = 0x40000000u;           // x offset of token lanes >= 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// One step's loads (64 words: 4 words of each of the 16 rows).
+// LDS of a workgroup of W waves walking TT tiles per step: the waves' dense tiles, then
+// two buffers of the waves' partial sums ([W][B][16*TT] floats each).
+template <int B, int TT, int W>
+constexpr size_t tile_lds_bytes() {
+    return (size_t)W * kTWaveBytes + 2 * (size_t)W * B * kTRows * TT * 4;
+}
+
+// One step's loads: 4 words of each of the 16 rows of each of the TT tiles.
+template <int TT>
 struct TBatch {
-    u32x4 va, vb;      // 16-byte value chunk (lane & 7) of row (lane >> 3), of row 8 + (lane >> 3)
-    uint32_t ma, mb;   // mask word ((lane & 7) >> 1) of the same two rows
-    u32x4 xq[kTStep];  // MFMA input operand of the step's four word columns
+    u32x4 va[TT], vb[TT];  // 16-byte value chunk (lane & 7) of tile row (lane >> 3), of row 8 + (lane >> 3)
+    uint32_t ma[TT], mb[TT];  // mask word ((lane & 7) >> 1) of the same two rows
+    u32x4 xp[kTStep / 2];     // x of word columns 2p (lanes n < 8) and 2p+1 (lanes n >= 8), shared by the tiles
 };
 
-// Where a tile's rows live, and where its outputs go.
+// Where a unit's rows live (8-row quarters: tile t has quarters 2t and 2t+1), and where
+// its outputs go.
+template <int TT>
 struct TileRows {
-    const uint8_t *m[2];  // masks of the first row of each half
-    const uint8_t *v[2];  // values of the first row of each half
-    int valid[2];         // rows of each half inside the matrix (0..8)
-    int p;                // output matrix
-    int local;            // first output row of the tile within matrix p
-    int rows;             // rows of matrix p (plain launch) / of the gate matrix (gated MLP)
+    const uint8_t *m[2 * TT];  // masks of the first row of each quarter
+    const uint8_t *v[2 * TT];  // values of the first row of each quarter
+    int valid[2 * TT];         // rows of each quarter inside the matrix (0..8)
+    int p;                     // output matrix
+    int local;                 // first output row of the unit within matrix p
+    int rows;                  // rows of matrix p (plain launch) / of the gate matrix (gated MLP)
 };
 
-template <int EPI>
-__device__ __forceinline__ TileRows tile_rows(const SpmvSet &set, int tile, int KW) {
-    TileRows t;
+// Rows of unit u.  Plain launch: 16*TT consecutive rows of one matrix.  Gated MLP: gate
+// and up rows i0..i0+8*TT-1; tile t holds gate rows i0+8t..+7 in rows 0-7 and the same
+// up rows in rows 8-15.
+template <int EPI, int TT>
+__device__ __forceinline__ TileRows<TT> tile_rows(const SpmvSet &set, int unit, int KW) {
+    TileRows<TT> t;
     if constexpr (EPI == kEpiSwiGLU) {
-        const int i0 = tile * 8;
-        const int n = min(max(set.row0[1] - i0, 0), 8);
+        const int i0 = unit * 8 * TT;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            t.m[h] = static_cast<const uint8_t *>(set.meta[h]) + (int64_t)i0 * KW * 4;
-            t.v[h] = reinterpret_cast<const uint8_t *>(set.values[h]) + (int64_t)i0 * KW * 32;
-            t.valid[h] = n;
+        for (int q = 0; q < 2 * TT; ++q) {
+            const int r = i0 + 8 * (q >> 1);
+            t.m[q] = static_cast<const uint8_t *>(set.meta[q & 1]) + (int64_t)r * KW * 4;
+            t.v[q] = reinterpret_cast<const uint8_t *>(set.values[q & 1]) + (int64_t)r * KW * 32;
+            t.valid[q] = min(max(set.row0[1] - r, 0), 8);
         }
         t.p = 0;
         t.local = i0;
         t.rows = set.row0[1];
     } else {
-        const int tb = tile * kTRows;
-        const int p = owner(set, tb);  // a tile never straddles two matrices
+        const int tb = unit * kTRows * TT;
+        const int p = owner(set, tb);  // a unit never straddles two matrices
         const int lb = tb - set.row0[p];
         const int rp = set.row0[p + 1] - set.row0[p];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            t.m[h] = static_cast<const uint8_t *>(set.meta[p]) + (int64_t)(lb + 8 * h) * KW * 4;
-            t.v[h] = reinterpret_cast<const uint8_t *>(set.values[p]) + (int64_t)(lb + 8 * h) * KW * 32;
-            t.valid[h] = min(max(rp - lb - 8 * h, 0), 8);
+        for (int q = 0; q < 2 * TT; ++q) {
+            t.m[q] = static_cast<const uint8_t *>(set.meta[p]) + (int64_t)(lb + 8 * q) * KW * 4;
+            t.v[q] = reinterpret_cast<const uint8_t *>(set.values[p]) + (int64_t)(lb + 8 * q) * KW * 32;
+            t.valid[q] = min(max(rp - lb - 8 * q, 0), 8);
         }
         t.p = p;
         t.local = lb;
@@ -106,26 +119,33 @@ __device__ __forceinline__ TileRows tile_rows(const SpmvSet &set, int tile, int 
 }
 
 // Loads of one step at word column cw (live = false: the same loads with empty ranges).
-template <int B>
-__device__ __forceinline__ void load_tbatch(TBatch &bt, const TileRows &tr, int cw, int KW, const uint16_t *x,
-                                            int64_t ldx, uint32_t vo, uint32_t mo, uint32_t xo, bool live) {
+template <int B, int TT>
+__device__ __forceinline__ void load_tbatch(TBatch<TT> &bt, const TileRows<TT> &tr, int cw, int KW,
+                                            const uint16_t *x, int64_t ldx, uint32_t vo, uint32_t mo, uint32_t xo,
+                                            bool live) {
     const int64_t vrow = (int64_t)KW * 32, mrow = (int64_t)KW * 4;
-    const int64_t vn0 = live ? tr.valid[0] * vrow - (int64_t)cw * 32 : 0;
-    const int64_t vn1 = live ? tr.valid[1] * vrow - (int64_t)cw * 32 : 0;
-    const int64_t mn0 = live ? tr.valid[0] * mrow - (int64_t)cw * 4 : 0;
-    const int64_t mn1 = live ? tr.valid[1] * mrow - (int64_t)cw * 4 : 0;
-    const int64_t xn = live ? (int64_t)(B - 1) * ldx * 2 + (int64_t)(KW - cw) * 64 : 0;
-    const __amdgpu_buffer_rsrc_t rv0 = make_rsrc(tr.v[0] + (int64_t)cw * 32, vn0 > 0 ? vn0 : 0);
-    const __amdgpu_buffer_rsrc_t rv1 = make_rsrc(tr.v[1] + (int64_t)cw * 32, vn1 > 0 ? vn1 : 0);
-    const __amdgpu_buffer_rsrc_t rm0 = make_rsrc(tr.m[0] + (int64_t)cw * 4, mn0 > 0 ? mn0 : 0);
-    const __amdgpu_buffer_rsrc_t rm1 = make_rsrc(tr.m[1] + (int64_t)cw * 4, mn1 > 0 ? mn1 : 0);
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + (int64_t)cw * 32, xn);
-    bt.va = __builtin_amdgcn_raw_buffer_load_b128(rv0, vo, 0, kLoadNT);
-    bt.vb = __builtin_amdgcn_raw_buffer_load_b128(rv1, vo, 0, kLoadNT);
-    bt.ma = __builtin_amdgcn_raw_buffer_load_b32(rm0, mo, 0, kLoadNT);
-    bt.mb = __builtin_amdgcn_raw_buffer_load_b32(rm1, mo, 0, kLoadNT);
 #pragma unroll
-    for (int j = 0; j < kTStep; ++j) bt.xq[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, xo + j * 64u, 0, 0);
+    for (int q = 0; q < 2 * TT; ++q) {
+        const int64_t vn = live ? tr.valid[q] * vrow - (int64_t)cw * 32 : 0;
+        const int64_t mn = live ? tr.valid[q] * mrow - (int64_t)cw * 4 : 0;
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(tr.v[q] + (int64_t)cw * 32, vn > 0 ? vn : 0);
+        const __amdgpu_buffer_rsrc_t rm = make_rsrc(tr.m[q] + (int64_t)cw * 4, mn > 0 ? mn : 0);
+        // (the 16 bytes of masks per row and step are a part of a line the next steps
+        // read again: a default load keeps the line in the caches for them)
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rv, vo, 0, kLoadNT);
+        const uint32_t m = __builtin_amdgcn_raw_buffer_load_b32(rm, mo, 0, 0);
+        if (q & 1) {
+            bt.vb[q >> 1] = v;
+            bt.mb[q >> 1] = m;
+        } else {
+            bt.va[q >> 1] = v;
+            bt.ma[q >> 1] = m;
+        }
+    }
+    const int64_t xn = live ? (int64_t)(B - 1) * ldx * 2 + (int64_t)(KW - cw) * 64 : 0;
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + (int64_t)cw * 32, xn);
+#pragma unroll
+    for (int j = 0; j < kTStep / 2; ++j) bt.xp[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, xo + j * 128u, 0, 0);
 }
 
 // Swap one dword with the neighbouring lane of the pair (lane ^ 1).
@@ -133,7 +153,7 @@ __device__ __forceinline__ uint32_t tpair_swap(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);  // quad_perm(1,0,3,2)
 }
 
-// One step: expand the lane's word into the wave's dense tile, then four MFMAs.
+// One tile of one step: expand the lane's word into the wave's dense tile, then four MFMAs.
 //
 // Lane l's word: row (l & 1) * 8 + (l >> 3) of the tile, word column (l & 7) >> 1.  Its
 // 32 columns are zeroed and its 16 kept values written at their columns.  Even lanes
@@ -147,20 +167,22 @@ __device__ __forceinline__ uint32_t tpair_swap(uint32_t v) {
 // row's data or another wave's tile.  The zeroing writes of lanes with rows 8..15 take
 // the word's 16-byte chunks in the order 2, 3, 0, 1, so the 16 lanes of each group of a
 // 16-byte write cover distinct banks.  The wave's LDS operations execute in issue order,
-// so the expansion is complete before the operand reads that follow it.
-__device__ __forceinline__ void walk_tbatch(const TBatch &bt, uint8_t *tw, int lane, f32x4 &acc) {
+// so the expansion is complete before the operand reads that follow it, and the operand
+// reads of one tile before the expansion of the next tile into the same LDS.
+__device__ __forceinline__ void walk_tile(const u32x4 &va, const u32x4 &vb, uint32_t ma, uint32_t mb,
+                                          const u32x4 (&xq)[kTStep], uint8_t *tw, int lane, f32x4 &acc) {
     const bool odd = lane & 1;
-    const uint32_t s_x = odd ? bt.va.x : bt.vb.x, s_y = odd ? bt.va.y : bt.vb.y;
-    const uint32_t s_z = odd ? bt.va.z : bt.vb.z, s_w = odd ? bt.va.w : bt.vb.w;
+    const uint32_t s_x = odd ? va.x : vb.x, s_y = odd ? va.y : vb.y;
+    const uint32_t s_z = odd ? va.z : vb.z, s_w = odd ? va.w : vb.w;
     const uint32_t r_x = tpair_swap(s_x), r_y = tpair_swap(s_y), r_z = tpair_swap(s_z), r_w = tpair_swap(s_w);
     // the word's 16 values in walk order: even lanes ascending, odd lanes descending
     // (dword d of the odd lane = the two values of dword 7 - d, halves swapped)
-    const uint32_t od[8] = {bt.vb.w, bt.vb.z, bt.vb.y, bt.vb.x, r_w, r_z, r_y, r_x};
-    const uint32_t ev[8] = {bt.va.x, bt.va.y, bt.va.z, bt.va.w, r_x, r_y, r_z, r_w};
+    const uint32_t od[8] = {vb.w, vb.z, vb.y, vb.x, r_w, r_z, r_y, r_x};
+    const uint32_t ev[8] = {va.x, va.y, va.z, va.w, r_x, r_y, r_z, r_w};
     uint32_t v[8];
 #pragma unroll
     for (int d = 0; d < 8; ++d) v[d] = odd ? __builtin_amdgcn_alignbit(od[d], od[d], 16) : ev[d];
-    uint32_t m = odd ? __builtin_bitreverse32(bt.mb) : bt.ma;
+    uint32_t m = odd ? __builtin_bitreverse32(mb) : ma;
     uint8_t *ub = tw + ((lane & 1) * 8 + (lane >> 3)) * kTRowBytes + 16 + ((lane & 7) >> 1) * 64;
     uint8_t *wb = odd ? ub + 62 : ub;  // column c of the walk order sits at wb + step * c
     const int step = odd ? -2 : 2;
@@ -179,10 +201,34 @@ __device__ __forceinline__ void walk_tbatch(const TBatch &bt, uint8_t *tw, int l
 #pragma unroll
     for (int j = 0; j < kTStep; ++j) {
         const u32x4 a = *reinterpret_cast<const u32x4 *>(ar + 64 * j);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, bt.xq[j]),
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, xq[j]),
                                                       acc, 0, 0, 0);
     }
     __builtin_amdgcn_wave_barrier();
+}
+
+// Exchange of the two halves of every 16-lane row (row_ror:8).
+__device__ __forceinline__ u32x4 swap_row_halves(const u32x4 &v) {
+    return u32x4{(uint32_t)__builtin_amdgcn_update_dpp(0, (int)v.x, 0x128, 0xF, 0xF, false),
+                 (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v.y, 0x128, 0xF, 0xF, false),
+                 (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v.z, 0x128, 0xF, 0xF, false),
+                 (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v.w, 0x128, 0xF, 0xF, false)};
+}
+
+// The MFMA input operands of a step: word column 2p is the loaded pair register as it is,
+// word column 2p+1 the same register with its 16-lane row halves exchanged.  Either way
+// the lanes of tokens 8..15 hold x of other tokens or columns: they only feed output
+// columns 8..15 of the product, which no one reads.
+template <int TT>
+__device__ __forceinline__ void walk_tbatch(const TBatch<TT> &bt, uint8_t *tw, int lane, f32x4 (&acc)[TT]) {
+    u32x4 xq[kTStep];
+#pragma unroll
+    for (int j = 0; j < kTStep / 2; ++j) {
+        xq[2 * j] = bt.xp[j];
+        xq[2 * j + 1] = swap_row_halves(bt.xp[j]);
+    }
+#pragma unroll
+    for (int t = 0; t < TT; ++t) walk_tile(bt.va[t], bt.vb[t], bt.ma[t], bt.mb[t], xq, tw, lane, acc[t]);
 }
 
 // Workgroup barrier for LDS traffic only: the weight loads in flight stay in flight.
@@ -192,64 +238,82 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// End of a tile: the waves' partial sums go to LDS, are added in wave order and stored.
-template <int B, int EPI>
-__device__ __forceinline__ void finish_tile(f32x4 &acc, float (*red)[B][kTRows], const TileRows &tr,
+// End of a unit: the waves' partial sums go to LDS ([W][B][16*TT]), are added in wave
+// order and stored.
+template <int B, int EPI, int TT, int W>
+__device__ __forceinline__ void finish_tile(f32x4 (&acc)[TT], float *red, const TileRows<TT> &tr,
                                             const SpmvSet &set, int wave, int lane) {
+    constexpr int kR = kTRows * TT;  // partial sums per token and wave
     const int n = lane & 15, q = lane >> 4;
-    if (n < B) *reinterpret_cast<f32x4 *>(&red[wave][n][4 * q]) = acc;
-    acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+        if (n < B) *reinterpret_cast<f32x4 *>(red + (wave * B + n) * kR + kTRows * t + 4 * q) = acc[t];
+        acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     lds_barrier();
-    const int t = threadIdx.x;
+    const int th = threadIdx.x;
     if constexpr (EPI == kEpiSwiGLU) {
-        if (t < 8 * B) {
-            const int j = t & 7, b = t >> 3;
+        constexpr int kH = 8 * TT;  // outputs per token: gate/up row pairs of the unit
+        if (th < kH * B) {
+            const int j = th % kH, b = th / kH;
+            const int gi = kTRows * (j >> 3) + (j & 7);  // gate row j sits in tile j/8, row j%8; up at row + 8
             float g = 0.f, u = 0.f;
 #pragma unroll
-            for (int w = 0; w < kTWaves; ++w) {
-                g += red[w][b][j];
-                u += red[w][b][8 + j];
+            for (int w = 0; w < W; ++w) {
+                g += red[(w * B + b) * kR + gi];
+                u += red[(w * B + b) * kR + gi + 8];
             }
             if (tr.local + j < tr.rows) set.y[0][(int64_t)b * set.ldy[0] + tr.local + j] = f32_to_bf16_rne(silu_mul(g, u));
         }
     } else {
-        if (t < kTRows * B) {
-            const int i = t & 15, b = t >> 4;
-            float s = 0.f;
+        if (th < kR * B) {
+            const int i = th % kR, b = th / kR;
+            float sum = 0.f;
 #pragma unroll
-            for (int w = 0; w < kTWaves; ++w) s += red[w][b][i];
-            if (tr.local + i < tr.rows) set.y[tr.p][(int64_t)b * set.ldy[tr.p] + tr.local + i] = f32_to_bf16_rne(s);
+            for (int w = 0; w < W; ++w) sum += red[(w * B + b) * kR + i];
+            if (tr.local + i < tr.rows) set.y[tr.p][(int64_t)b * set.ldy[tr.p] + tr.local + i] = f32_to_bf16_rne(sum);
         }
     }
 }
 
-template <int B, int EPI>
-__global__ __launch_bounds__(kTThreads, 4) void spmv_tile_kernel(const SpmvSet set, int KW,
+// W waves per workgroup share a unit of TT tiles (16*TT rows) at a time: wave w walks
+// words [w*KW/W, (w+1)*KW/W) of the unit's rows in steps of 4 words, one word of each
+// tile per lane, all TT tiles of a step multiplied by the same x operand.
+template <int B, int EPI, int TT, int W>
+__global__ __launch_bounds__(W * kWave, 4) void spmv_tile_kernel(const SpmvSet set, int KW,
                                                                  const uint16_t *__restrict__ x, int64_t ldx,
-                                                                 int tiles) {
-    __shared__ __attribute__((aligned(16))) uint8_t dense[kTWaves * kTWaveBytes];
-    __shared__ __attribute__((aligned(16))) float red[2][kTWaves][B][kTRows];
+                                                                 int units) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t tlds[];
+    uint8_t *dense = tlds;
+    float *red0 = reinterpret_cast<float *>(tlds + (size_t)W * kTWaveBytes);
+    float *red1 = red0 + W * B * kTRows * TT;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int nwp = KW / kTWaves;  // words per wave and row; a multiple of kTStep
+    const int nwp = KW / W;  // words per wave and row; a multiple of kTStep
     const int steps = nwp / kTStep;
     const int wa = wave * nwp;
-    const int my_tiles = (int)blockIdx.x < tiles ? (tiles - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
-    const int total = my_tiles * steps;
+    const int my_units = (int)blockIdx.x < units ? (units - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
+    const int total = my_units * steps;
     const uint32_t vo = (uint32_t)((lane >> 3) * KW * 32 + (lane & 7) * 16);
     const uint32_t mo = (uint32_t)((lane >> 3) * KW * 4 + ((lane & 7) >> 1) * 4);
-    const int n = lane & 15;
-    const uint32_t xo = n < B ? (uint32_t)(n * ldx * 2 + (lane >> 4) * 16) : kXOut;
+    // x operand loads: lane l holds token (l & 7), k-block l >> 4 of word column 2p
+    // (l & 15 < 8) or 2p+1 (l & 15 >= 8) -- all 64 lanes load, half the instructions of
+    // one operand register per word column, and a token's two word columns are 128
+    // contiguous bytes
+    const int n = lane & 7;
+    const uint32_t xo = n < B ? (uint32_t)(n * ldx * 2 + (lane >> 4) * 16 + ((lane >> 3) & 1) * 64) : kXOut;
     uint8_t *tw = dense + wave * kTWaveBytes;
 
-    // Steps of this wave: (tile, step) for tiles blockIdx.x, + gridDim.x, ..., walked as
+    // Steps of this wave: (unit, step) for units blockIdx.x, + gridDim.x, ..., walked as
     // one flat sequence with the next step's loads in flight during the current one,
-    // across tile boundaries too (two buffers used in turn, as in nm_spmv.hip).
-    TBatch bA, bB;
+    // across unit boundaries too (two buffers used in turn, as in nm_spmv.hip).
+    TBatch<TT> bA, bB;
     int tA = blockIdx.x, sA = 0, tB = tA, sB = 0;
-    TileRows rA = tile_rows<EPI>(set, min(tA, tiles - 1), KW), rB = rA;
-    load_tbatch<B>(bA, rA, wa, KW, x, ldx, vo, mo, xo, total > 0);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    TileRows<TT> rA = tile_rows<EPI, TT>(set, min(tA, units - 1), KW), rB = rA;
+    load_tbatch<B, TT>(bA, rA, wa, KW, x, ldx, vo, mo, xo, total > 0);
+    f32x4 acc[TT];
+#pragma unroll
+    for (int t = 0; t < TT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     int buf = 0;
     int k = 0;
     for (; k + 1 < total; k += 2) {
@@ -258,15 +322,15 @@ __global__ __launch_bounds__(kTThreads, 4) void spmv_tile_kernel(const SpmvSet s
         if (sB == steps) {
             sB = 0;
             tB += gridDim.x;
-            rB = tile_rows<EPI>(set, min(tB, tiles - 1), KW);
+            rB = tile_rows<EPI, TT>(set, min(tB, units - 1), KW);
         } else {
             rB = rA;
         }
-        load_tbatch<B>(bB, rB, wa + kTStep * sB, KW, x, ldx, vo, mo, xo, true);
+        load_tbatch<B, TT>(bB, rB, wa + kTStep * sB, KW, x, ldx, vo, mo, xo, true);
         __builtin_amdgcn_sched_barrier(0);
-        walk_tbatch(bA, tw, lane, acc);
+        walk_tbatch<TT>(bA, tw, lane, acc);
         if (sA == steps - 1) {
-            finish_tile<B, EPI>(acc, red[buf], rA, set, wave, lane);
+            finish_tile<B, EPI, TT, W>(acc, buf ? red1 : red0, rA, set, wave, lane);
             buf ^= 1;
         }
         tA = tB;
@@ -274,32 +338,62 @@ __global__ __launch_bounds__(kTThreads, 4) void spmv_tile_kernel(const SpmvSet s
         if (sA == steps) {
             sA = 0;
             tA += gridDim.x;
-            rA = tile_rows<EPI>(set, min(tA, tiles - 1), KW);
+            rA = tile_rows<EPI, TT>(set, min(tA, units - 1), KW);
         } else {
             rA = rB;
         }
-        load_tbatch<B>(bA, rA, wa + kTStep * sA, KW, x, ldx, vo, mo, xo, k + 2 < total);
+        load_tbatch<B, TT>(bA, rA, wa + kTStep * sA, KW, x, ldx, vo, mo, xo, k + 2 < total);
         __builtin_amdgcn_sched_barrier(0);
-        walk_tbatch(bB, tw, lane, acc);
+        walk_tbatch<TT>(bB, tw, lane, acc);
         if (sB == steps - 1) {
-            finish_tile<B, EPI>(acc, red[buf], rB, set, wave, lane);
+            finish_tile<B, EPI, TT, W>(acc, buf ? red1 : red0, rB, set, wave, lane);
             buf ^= 1;
         }
     }
     if (k < total) {  // odd count: the last step is in A
-        walk_tbatch(bA, tw, lane, acc);
-        if (sA == steps - 1) finish_tile<B, EPI>(acc, red[buf], rA, set, wave, lane);
+        walk_tbatch<TT>(bA, tw, lane, acc);
+        if (sA == steps - 1) finish_tile<B, EPI, TT, W>(acc, buf ? red1 : red0, rA, set, wave, lane);
     }
+}
+
+// Raise the dynamic-LDS limit of one kernel instance once per device.
+template <int B, int EPI, int TT, int W>
+hipError_t allow_tile_lds() {
+    static std::atomic<uint64_t> done{0};
+    constexpr size_t bytes = tile_lds_bytes<B, TT, W>();
+    if (bytes <= 64 * 1024) return hipSuccess;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = 1ull << (dev & 63);
+    if (done.load(std::memory_order_acquire) & bit) return hipSuccess;
+    e = hipFuncSetAttribute((const void *)spmv_tile_kernel<B, EPI, TT, W>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)bytes);
+    if (e == hipSuccess) done.fetch_or(bit, std::memory_order_acq_rel);
+    return e;
+}
+
+template <int B, int EPI, int TT, int W>
+hipError_t launch_tbw(const MvPlan &p, const SpmvSet &set, int64_t K, const uint16_t *x, int64_t ldx,
+                      hipStream_t st) {
+    hipError_t e = allow_tile_lds<B, EPI, TT, W>();
+    if (e != hipSuccess) return e;
+    SpmvSet padded = set;
+    for (int q = set.P + 1; q <= kMaxMats; ++q) padded.row0[q] = set.row0[set.P];
+    hipLaunchKernelGGL((spmv_tile_kernel<B, EPI, TT, W>), dim3((unsigned)p.grid_x), dim3(W * kWave),
+                       (tile_lds_bytes<B, TT, W>()), st, padded, (int)(K / 32), x, ldx, p.tiles);
+    return hipGetLastError();
 }
 
 template <int B, int EPI>
 hipError_t launch_tb(const MvPlan &p, const SpmvSet &set, int64_t K, const uint16_t *x, int64_t ldx,
                      hipStream_t st) {
-    SpmvSet padded = set;
-    for (int q = set.P + 1; q <= kMaxMats; ++q) padded.row0[q] = set.row0[set.P];
-    hipLaunchKernelGGL((spmv_tile_kernel<B, EPI>), dim3((unsigned)p.grid_x), dim3(kTThreads), 0, st, padded,
-                       (int)(K / 32), x, ldx, p.tiles);
-    return hipGetLastError();
+    const int tt = p.unroll, w = p.threads / kWave;
+    if (tt == 2 && w == 16) return launch_tbw<B, EPI, 2, 16>(p, set, K, x, ldx, st);
+    if (tt == 2 && w == 8) return launch_tbw<B, EPI, 2, 8>(p, set, K, x, ldx, st);
+    if (tt == 1 && w == 16) return launch_tbw<B, EPI, 1, 16>(p, set, K, x, ldx, st);
+    if (tt == 1 && w == 8) return launch_tbw<B, EPI, 1, 8>(p, set, K, x, ldx, st);
+    return hipErrorInvalidValue;
 }
 
 template <int EPI>
@@ -318,7 +412,7 @@ hipError_t launch_te(const MvPlan &p, const SpmvSet &set, int64_t K, const uint1
 
 bool spmv_tile_ok(const SpmvSet &set, int64_t K, int64_t ldx, int B, int fmt, int epi) {
     if (fmt != kMetaBitmask || B < kTileMinB || B > 8) return false;
-    if (K % (32 * kTWaves * kTStep) != 0) return false;  // every wave gets whole steps
+    if (K % (32 * 8 * kTStep) != 0) return false;  // every wave of an 8-wave workgroup gets whole steps
     // 32-bit buffer offsets: 8 rows of values, and the x rows of all tokens
     if ((int64_t)8 * K > ((int64_t)1 << 30) || (int64_t)(B - 1) * ldx * 2 + K * 2 > ((int64_t)1 << 30)) return false;
     if (epi == kEpiSwiGLU) return set.P == 2 && set.row0[2] == 2 * set.row0[1];
@@ -327,17 +421,38 @@ bool spmv_tile_ok(const SpmvSet &set, int64_t K, int64_t ldx, int B, int fmt, in
     return true;
 }
 
-MvPlan plan_spmv_tile(int64_t R, int B, const DeviceInfo &dev, int epi) {
+MvPlan plan_spmv_tile(const SpmvSet &set, int64_t K, int B, const DeviceInfo &dev, int epi) {
     (void)B;
     MvPlan p;
     p.tile = 1;
-    p.threads = kTThreads;
-    const int64_t tiles = epi == kEpiSwiGLU ? (R / 2 + 7) / 8 : (R + kTRows - 1) / kTRows;
+    const int64_t R = set.row0[set.P];
     const int64_t cu = dev.num_cu > 0 ? dev.num_cu : 256;
-    int64_t gx = cu * 2;  // two 8-wave workgroups per CU (LDS and register budget)
-    if (gx > tiles) gx = tiles;
+    const int64_t tiles = epi == kEpiSwiGLU ? (R / 2 + 7) / 8 : (R + kTRows - 1) / kTRows;
+    // Two 8-wave workgroups per CU (LDS and register budget).  With fewer tiles than
+    // that, one 16-wave workgroup per CU keeps as many waves in flight, where K still
+    // gives every wave at least four steps per tile.
+    const int w = (tiles < 2 * cu && K % (32 * 16 * kTStep) == 0 && K / (32 * 16 * kTStep) >= 4) ? 16 : 8;
+    const int64_t slots = cu * (16 / w);  // resident workgroups
+    // Two tiles per step (one x operand for 32 rows, half the x loads per weight byte)
+    // when that leaves the CUs as evenly loaded as one tile per step does: the units of
+    // work per CU are whole, and a CU's last unit is the launch's tail.
+    bool two = (tiles + 1) / 2 >= slots;
+    if (epi != kEpiSwiGLU)
+        for (int q = 1; q < set.P; ++q)
+            if (set.row0[q] % (2 * kTRows)) two = false;  // units must not straddle two matrices
+    if (two) {
+        const int64_t u1 = tiles, u2 = (tiles + 1) / 2;
+        // ceil(u / cu) / (u / cu): compare ceil(u2/cu) * u1 with ceil(u1/cu) * u2
+        if ((u2 + cu - 1) / cu * u1 > (u1 + cu - 1) / cu * u2) two = false;
+    }
+    const int tt = two ? 2 : 1;
+    const int64_t units = (tiles + tt - 1) / tt;
+    int64_t gx = slots;
+    if (gx > units) gx = units;
     p.grid_x = (int)(gx < 1 ? 1 : gx);
-    p.tiles = (int)tiles;
+    p.tiles = (int)units;
+    p.unroll = tt;
+    p.threads = w * kWave;
     p.splits = 1;
     p.ws_bytes = 0;
     return p;

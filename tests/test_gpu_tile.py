@@ -147,3 +147,43 @@ def test_tile_swiglu(R, K, B):
     ref = oracle.swiglu(g, u)
     ok = np.abs(bf16_as_f64(h) - ref) <= oracle.swiglu_tolerance(g, ag, u, au)
     assert ok.all(), f"swiglu R={R} K={K} B={B}: {int((~ok).sum())} outside"
+
+
+# Launches with enough 16-row tiles (on a 256-CU part: 2048 here) walk two tiles per step
+# with one shared x operand; a multi-matrix set does so only when every matrix but the
+# last starts at a multiple of 32 rows (else one tile per step).
+@pytest.mark.parametrize("Rs", [[32768], [32763], [16384, 16384], [16400, 16368]],
+                         ids=["plain", "ragged", "multi32", "multi16"])
+def test_tile_two_tiles_per_step(Rs):
+    say("tile two per step", Rs)
+    K, B = 1024, 8
+    x = synth.decode_x(B, K, 38, len(Rs))
+    n = oracle.col_norm(synth.calib_acts(K, 38, len(Rs)))
+    packed, refs = [], []
+    for i, R in enumerate(Rs):
+        W = synth.weights(R, K, 38, len(Rs), i)
+        mref, vref = oracle.prune_pack(W, n, 4, 8)
+        refs.append(oracle.spmv(mref, vref, x, K, nthreads=8))
+        packed.append((dev_u32(mref), dev_bf16(vref)))
+    ys = nm.nm_spmv_multi(packed, dev_bf16(x)) if len(Rs) > 1 else [nm.nm_spmv(*packed[0], dev_bf16(x))]
+    for i, (y, (yref, absum)) in enumerate(zip(ys, refs)):
+        assert y.shape == (B, Rs[i])
+        assert_within(host_bf16(y), yref, absum, f"two per step {Rs} matrix {i}")
+
+
+@pytest.mark.parametrize("R,B", [(16384, 8), (16377, 6)])
+def test_tile_swiglu_two_tiles_per_step(R, B):
+    """Gated MLP with two 16-row tiles (gate and up rows i..i+15) per step."""
+    say("tile swiglu two per step", R, B)
+    K = 1024
+    n = oracle.col_norm(synth.calib_acts(K, 39, R))
+    Wg, Wu = synth.weights(R, K, 39, 1, R), synth.weights(R, K, 39, 2, R)
+    gm, gv = oracle.prune_pack(Wg, n, 8, 16)
+    um, uv = oracle.prune_pack(Wu, n, 8, 16)
+    x = synth.decode_x(B, K, 39, R, B)
+    h = host_bf16(nm.nm_spmv_swiglu((dev_u32(gm), dev_bf16(gv)), (dev_u32(um), dev_bf16(uv)), dev_bf16(x)))
+    g, ag = oracle.spmv(gm, gv, x, K, nthreads=8)
+    u, au = oracle.spmv(um, uv, x, K, nthreads=8)
+    ref = oracle.swiglu(g, u)
+    ok = np.abs(bf16_as_f64(h) - ref) <= oracle.swiglu_tolerance(g, ag, u, au)
+    assert ok.all(), f"swiglu two per step R={R} B={B}: {int((~ok).sum())} outside"
