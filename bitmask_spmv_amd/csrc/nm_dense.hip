@@ -191,21 +191,26 @@ __global__ __launch_bounds__(NT, NT == 1024 ? 8 : 1) void dense_kernel(const Den
     // Stage x; the first round of x loads goes out before batch A's weight loads so that
     // waiting for x never waits for the weights queued behind it.
     {
+        // (unconditional loads -- a thread past the end re-reads the last chunk -- and
+        // the parts of a round beyond x skipped by a uniform test, as in the sparse
+        // kernel's staging: loads under a lane condition were issued one at a time)
         constexpr int kStage = 4;
         const int chunks = B * ncs;
+        const int rounds = (chunks + NT - 1) / NT;
         for (int i0 = 0; i0 < chunks || i0 == 0; i0 += NT * kStage) {
+            const int left = rounds - i0 / NT;
             u32x4 r[kStage];
 #pragma unroll
             for (int j = 0; j < kStage; ++j) {
-                const int i = i0 + j * NT + (int)threadIdx.x;
-                if (i < chunks) {
-                    const int b = i / ncs;
-                    r[j] = reinterpret_cast<const u32x4 *>(x + (int64_t)b * ldx)[c0 + (i - b * ncs)];
-                }
+                if (j > 0 && j >= left) break;
+                const int i = min(i0 + j * NT + (int)threadIdx.x, chunks - 1);
+                const int b = i / ncs;
+                r[j] = reinterpret_cast<const u32x4 *>(x + (int64_t)b * ldx)[c0 + (i - b * ncs)];
             }
             if (i0 == 0) load_row_dbatch<U, EPI>(bufA, set, min(rowA, R - 1), c0, total > 0 ? ncs : 0, 0, lane);
 #pragma unroll
             for (int j = 0; j < kStage; ++j) {
+                if (j > 0 && j >= left) break;
                 const int i = i0 + j * NT + (int)threadIdx.x;
                 if (i < chunks) xs4[i] = r[j];
             }

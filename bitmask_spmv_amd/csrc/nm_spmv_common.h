@@ -120,26 +120,33 @@ __device__ __forceinline__ void stage_x(uint32_t *xs, const uint16_t *__restrict
     } else {
         // Eight columns per thread and round: one 16-byte load of every token, transposed
         // with byte permutes into the interleaved per-column layout (the eight columns'
-        // 4*S dwords are contiguous in LDS: S 16-byte stores).
+        // 4*S dwords are contiguous in LDS: S 16-byte stores).  The loads are
+        // unconditional (a thread past the slice re-reads its last eight columns) and the
+        // parts of a round beyond the slice are skipped by a uniform test: loads under a
+        // lane condition were issued one or two at a time, each waiting for the previous.
         constexpr int S = XLayout<B>::S;
         constexpr int kStage = 8 / S;  // 8 x 16-byte loads in flight per thread and round
         const int octs = nws * 4;
+        const int rounds = (octs + NT - 1) / NT;  // loads per thread and token (uniform)
         const uint16_t *xw = x + (int64_t)w0 * 32;
         for (int i0 = 0; i0 < octs || i0 == 0; i0 += NT * kStage) {
+            const int left = rounds - i0 / NT;
             u32x4 r[kStage][S];
 #pragma unroll
             for (int j = 0; j < kStage; ++j) {
-                const int i = i0 + j * NT + (int)threadIdx.x;
+                if (j > 0 && j >= left) break;
+                const int i = min(i0 + j * NT + (int)threadIdx.x, octs - 1);
 #pragma unroll
                 for (int b = 0; b < S; ++b)
-                    r[j][b] = (b < B && i < octs) ? *reinterpret_cast<const u32x4 *>(xw + (int64_t)b * ldx + 8 * i)
-                                                  : u32x4{0u, 0u, 0u, 0u};
+                    r[j][b] = b < B ? *reinterpret_cast<const u32x4 *>(xw + (int64_t)b * ldx + 8 * i)
+                                    : u32x4{0u, 0u, 0u, 0u};
             }
             if (i0 == 0) first_round();
 #pragma unroll
             for (int j = 0; j < kStage; ++j) {
-                const int i = i0 + j * NT + (int)threadIdx.x;
-                if (i < octs) {
+                if (j > 0 && j >= left) break;
+                const int i = min(i0 + j * NT + (int)threadIdx.x, octs - 1);
+                {
                     const int c = 8 * i;  // first column of the eight, within the slice
                     u32x4 *d = reinterpret_cast<u32x4 *>(xs + (c >> 5) * XLayout<B>::kBlk + (c & 31) * (S / 2));
                     uint32_t col[4 * S];  // column c+k: dwords k*S/2 .. k*S/2 + S/2 - 1
