@@ -613,9 +613,14 @@ def main():
             den = (Wf @ Xf.T).pow(2).sum()
             return float(num / den)
 
-        flops = 2.0 * K_s * K_s * T_s
+        # H is symmetric: the kernel computes the 64x64 tiles on and above the diagonal
+        # (g(g+1)/2 of them, g = ceil(K/64)) on the fp64 matrix cores; those are the flops
+        # it executes and the ones held against the peak.
+        g_t = -(-K_s // 64)
+        flops = 2.0 * (g_t * (g_t + 1) // 2) * 64 * 64 * T_s
         solver = {"shape": f"{name_s} {R_s}x{K_s}", "pattern": f"{N}:{M}", "tokens": T_s,
                   "hessian_ms": round(h_ms, 3), "hessian_TFLOPs": round(flops / h_ms / 1e9, 2),
+                  "hessian_tflop_executed": round(flops / 1e12, 4),
                   "hessian_frac_fp64_mfma_peak": round(flops / h_ms / 1e9 / FP64_MFMA_PEAK_TFLOPS, 4),
                   "inverse_factor_ms": round(f_ms, 2), "prune_pack_ms": round(sg_ms, 2),
                   "rel_recon_error": {"wanda": rel_err(mw, vw), "sparsegpt": rel_err(m_s, v_s)}}

@@ -71,18 +71,28 @@ __device__ __forceinline__ uint16_t f64_to_bf16_rne(double v) {
 
 // ---------------------------------------------------------------- Hessian
 // H = 2 X^T X.  64x64 tile of H per workgroup (4 waves, 32x32 each = 2x2 MFMA tiles);
-// 16 tokens per LDS stage.
+// H is symmetric, so only the tiles on and above the diagonal are computed (workgroup
+// blockIdx.x walks them row by row) and each is written to both halves.  16 tokens per
+// LDS stage, two stage buffers: the next stage's elements of X are loaded into registers
+// before the current stage's MFMAs, and one barrier per stage separates the writes of a
+// buffer from the reads of the stage before.
 constexpr int kHT = 64;
 constexpr int kHS = 16;
 
 __global__ __launch_bounds__(256) void hessian_kernel(const uint16_t *__restrict__ X, int64_t T, int64_t K,
-                                                      int64_t ldx, double *__restrict__ H, int64_t ldh) {
-    __shared__ double As[kHS][kHT];
-    __shared__ double Bs[kHS][kHT];
+                                                      int64_t ldx, double *__restrict__ H, int64_t ldh, int g) {
+    __shared__ double As[2][kHS][kHT];
+    __shared__ double Bs[2][kHS][kHT];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int64_t i0 = (int64_t)blockIdx.y * kHT, j0 = (int64_t)blockIdx.x * kHT;
+    int bi = 0, rem = (int)blockIdx.x;
+    while (rem >= g - bi) {  // row bi of the upper triangle holds g - bi tiles
+        rem -= g - bi;
+        ++bi;
+    }
+    const int bj = bi + rem;
+    const int64_t i0 = (int64_t)bi * kHT, j0 = (int64_t)bj * kHT;
     const int wi = (wave >> 1) * 32, wj = (wave & 1) * 32;
     v4f64 acc[2][2];
 #pragma unroll
@@ -91,29 +101,40 @@ __global__ __launch_bounds__(256) void hessian_kernel(const uint16_t *__restrict
         for (int b = 0; b < 2; ++b) acc[a][b] = v4f64{0.0, 0.0, 0.0, 0.0};
     const int lt = tid >> 4;         // token within the stage
     const int lc = (tid & 15) * 4;   // first of 4 columns
-    for (int64_t t0 = 0; t0 < T; t0 += kHS) {
+    double ra[4], rb[4];
+    auto fetch = [&](int64_t t0) {
         const int64_t t = t0 + lt;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int64_t ci = i0 + lc + e, cj = j0 + lc + e;
-            As[lt][lc + e] = (t < T && ci < K) ? bf16_to_f64(X[t * ldx + ci]) : 0.0;
-            Bs[lt][lc + e] = (t < T && cj < K) ? bf16_to_f64(X[t * ldx + cj]) : 0.0;
+            ra[e] = (t < T && ci < K) ? bf16_to_f64(X[t * ldx + ci]) : 0.0;
+            rb[e] = (t < T && cj < K) ? bf16_to_f64(X[t * ldx + cj]) : 0.0;
+        }
+    };
+    fetch(0);
+    int buf = 0;
+    for (int64_t t0 = 0; t0 < T; t0 += kHS) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            As[buf][lt][lc + e] = ra[e];
+            Bs[buf][lt][lc + e] = rb[e];
         }
         __syncthreads();
+        if (t0 + kHS < T) fetch(t0 + kHS);
 #pragma unroll
         for (int s = 0; s < kHS / 4; ++s) {
             const int tk = 4 * s + (lane >> 4);
 #pragma unroll
             for (int a = 0; a < 2; ++a) {
-                const double av = As[tk][wi + 16 * a + (lane & 15)];
+                const double av = As[buf][tk][wi + 16 * a + (lane & 15)];
 #pragma unroll
                 for (int b = 0; b < 2; ++b) {
-                    const double bv = Bs[tk][wj + 16 * b + (lane & 15)];
+                    const double bv = Bs[buf][tk][wj + 16 * b + (lane & 15)];
                     acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc[a][b], 0, 0, 0);
                 }
             }
         }
-        __syncthreads();
+        buf ^= 1;
     }
     // D layout of the 16x16 f64 tile: lane l, element r -> row l/16 + 4*r, column l%16
 #pragma unroll
@@ -124,7 +145,11 @@ __global__ __launch_bounds__(256) void hessian_kernel(const uint16_t *__restrict
             for (int r = 0; r < 4; ++r) {
                 const int64_t i = i0 + wi + 16 * a + (lane >> 4) + 4 * r;
                 const int64_t j = j0 + wj + 16 * b + (lane & 15);
-                if (i < K && j < K) H[i * ldh + j] = 2.0 * acc[a][b][r];
+                if (i < K && j < K) {
+                    const double v = 2.0 * acc[a][b][r];
+                    H[i * ldh + j] = v;
+                    if (bi != bj) H[j * ldh + i] = v;
+                }
             }
 }
 
@@ -499,8 +524,9 @@ size_t sparsegpt_workspace(int64_t R, int64_t K) {
 
 hipError_t launch_hessian(const uint16_t *X, int64_t T, int64_t K, int64_t ldx, double *H, int64_t ldh,
                           hipStream_t st) {
-    const unsigned g = (unsigned)((K + kHT - 1) / kHT);
-    hipLaunchKernelGGL(hessian_kernel, dim3(g, g), dim3(256), 0, st, X, T, K, ldx, H, ldh);
+    const int g = (int)((K + kHT - 1) / kHT);
+    const unsigned tiles = (unsigned)((int64_t)g * (g + 1) / 2);  // on and above the diagonal
+    hipLaunchKernelGGL(hessian_kernel, dim3(tiles), dim3(256), 0, st, X, T, K, ldx, H, ldh, g);
     return hipGetLastError();
 }
 
