@@ -27,8 +27,10 @@
 //   * the column loop works in 32-column blocks (one mask word): one thread per row
 //     keeps the block's 32 weights in registers, selects, compensates inside the block
 //     against U's 32x32 diagonal block in LDS, writes the mask word, the 16 kept values
-//     (rounded once to bf16) and the 32 errors; a tiled fp64 kernel then applies the
-//     block's errors to all later columns at once (SparseGPT's lazy batch update).
+//     (rounded once to bf16) and the 32 errors.  SparseGPT's lazy batch update, in
+//     batches of 128 columns on the fp64 matrix cores: a block's errors compensate the
+//     rest of its batch, and a batch's 128 errors per row compensate every later column
+//     in one rank-128 update (one pass over those columns per 128 instead of per 32).
 #include "nm_device.h"
 #include "nm_kernels.h"
 
@@ -37,7 +39,8 @@ namespace {
 
 typedef double v4f64 __attribute__((ext_vector_type(4)));
 typedef double v2f64 __attribute__((ext_vector_type(2)));
-constexpr int kNB = 32;  // panel / column-block width
+constexpr int kNB = 32;   // panel / column-block width
+constexpr int kLB = 128;  // lazy batch: columns whose compensation of the later columns is applied at once
 
 __device__ __forceinline__ double bf16_to_f64(uint16_t b) { return (double)__uint_as_float((uint32_t)b << 16); }
 
@@ -232,7 +235,7 @@ __global__ __launch_bounds__(64) void trsm_panel_kernel(double *__restrict__ A, 
 
 // Tiled fp64 update C[i][j] -= sum_{k<32} P[i][k] * Q[j][k] over a 64x64 tile per
 // workgroup (each thread 4x4 outputs); P, Q, C row-major with the given strides.  Used
-// for the Cholesky trailing update (lower tiles only) and for the solver's lazy update.
+// for the Cholesky trailing update (lower tiles only).
 __device__ __forceinline__ void tile_update(double *__restrict__ C, int64_t ldc, const double *__restrict__ P,
                                             int64_t ldp, const double *__restrict__ Q, int64_t ldq, int64_t m0,
                                             int64_t n0, int64_t mend, int64_t nend) {
@@ -449,7 +452,7 @@ __global__ __launch_bounds__(kBlkThreads) void sgpt_block_kernel(const double *_
             w[a] = 0.0;
             for (int a2 = a + 1; a2 < kNB; ++a2) w[a2] = fma(-e, Ub[a][a2], w[a2]);
         }
-        Err[r * kNB + a] = e;
+        Err[r * kLB + c0 % kLB + a] = e;
     }
     const int64_t word = c0 / kNB;
     masks[r * (K / kNB) + word] = keep;
@@ -468,58 +471,72 @@ __global__ __launch_bounds__(kBlkThreads) void sgpt_block_kernel(const double *_
     v4[1] = make_uint4(out[4], out[5], out[6], out[7]);
 }
 
-// Lazy update of the later columns: Wd[r][j] -= sum_a Err[r][a] * U[c0 + a][j], j >= c0 + 32.
-// U rows are read as Q[j][a] = U[c0 + a][j]: staged transposed through a strided view.
-__global__ __launch_bounds__(256) void sgpt_trailing_kernel(double *__restrict__ Wd, int64_t R, int64_t K,
-                                                            const double *__restrict__ U, int64_t ldu, int64_t c0,
-                                                            const double *__restrict__ Err) {
-    __shared__ double Ps[64][kNB + 1];
-    __shared__ double Qs[64][kNB + 1];
+// Compensation of later columns: Wd[r][n0 + j] -= sum_k Err[r][e0 + k] * U[u0 + k][n0 + j]
+// for r < R, j < ncols, k < kw (kw a multiple of 16).  On the fp64 matrix cores: a 64x64
+// tile of Wd per workgroup (4 waves, 32x32 each = 2x2 MFMA tiles), 16 k per LDS stage.
+__global__ __launch_bounds__(256) void sgpt_update_kernel(double *__restrict__ Wd, int64_t R, int64_t K, int64_t n0,
+                                                          int64_t ncols, const double *__restrict__ Err, int e0,
+                                                          const double *__restrict__ U, int64_t ldu, int64_t u0,
+                                                          int kw) {
+    __shared__ double As[16][64];  // As[k][m] = Err[m0 + m][e0 + k0 + k]
+    __shared__ double Bs[16][64];  // Bs[k][n] = U[u0 + k0 + k][n0 + nb0 + n]
     const int tid = threadIdx.x;
-    const int64_t m0 = (int64_t)blockIdx.y * 64;
-    const int64_t n0 = c0 + kNB + (int64_t)blockIdx.x * 64;
-    for (int e = tid; e < 64 * kNB; e += 256) {
-        const int rr = e / kNB, kk = e % kNB;
-        Ps[rr][kk] = m0 + rr < R ? Err[(m0 + rr) * kNB + kk] : 0.0;
-    }
-    for (int e = tid; e < 64 * kNB; e += 256) {
-        const int kk = e / 64, jj = e % 64;  // coalesced along the U row
-        Qs[jj][kk] = n0 + jj < K ? U[(c0 + kk) * ldu + n0 + jj] : 0.0;
-    }
-    __syncthreads();
-    const int ti = (tid >> 4) * 4, tj = (tid & 15) * 4;
-    double acc[4][4] = {};
-#pragma unroll 8
-    for (int k = 0; k < kNB; ++k) {
-        double p[4], q[4];
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int64_t m0 = (int64_t)blockIdx.y * 64, nb0 = (int64_t)blockIdx.x * 64;
+    const int wi = (wave >> 1) * 32, wj = (wave & 1) * 32;
+    v4f64 acc[2][2];
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            p[a] = Ps[ti + a][k];
-            q[a] = Qs[tj + a][k];
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) acc[a][b] = v4f64{0.0, 0.0, 0.0, 0.0};
+    for (int k0 = 0; k0 < kw; k0 += 16) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int idx = tid + 256 * e;
+            const int m = idx >> 4, k = idx & 15;  // 16 consecutive k of one row of Err per 16 threads
+            As[k][m] = m0 + m < R ? Err[(m0 + m) * kLB + e0 + k0 + k] : 0.0;
+            const int kb = idx >> 6, n = idx & 63;  // one row of U, 64 consecutive columns
+            Bs[kb][n] = nb0 + n < ncols ? U[(u0 + k0 + kb) * ldu + n0 + nb0 + n] : 0.0;
         }
+        __syncthreads();
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
+        for (int st = 0; st < 4; ++st) {
+            const int tk = 4 * st + (lane >> 4);
 #pragma unroll
-            for (int b = 0; b < 4; ++b) acc[a][b] = fma(p[a], q[b], acc[a][b]);
-    }
+            for (int a = 0; a < 2; ++a) {
+                const double av = As[tk][wi + 16 * a + (lane & 15)];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const int64_t i = m0 + ti + a, j = n0 + tj + b;
-            if (i < R && j < K) Wd[i * K + j] -= acc[a][b];
+                for (int b = 0; b < 2; ++b) {
+                    const double bv = Bs[tk][wj + 16 * b + (lane & 15)];
+                    acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc[a][b], 0, 0, 0);
+                }
+            }
         }
+        __syncthreads();
+    }
+    // D layout of the 16x16 f64 tile: lane l, element r -> row l/16 + 4*r, column l%16
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t i = m0 + wi + 16 * a + (lane >> 4) + 4 * r;
+                const int64_t j = nb0 + wj + 16 * b + (lane & 15);
+                if (i < R && j < ncols) Wd[i * K + n0 + j] -= acc[a][b][r];
+            }
 }
 
 unsigned blocks_for(int64_t n) { return (unsigned)((n + 255) / 256); }
 
 }  // namespace
 
-// Workspace layout (bytes): [A/U: K*K fp64][Cinv: K*K fp64][Wd: R*K fp64][Err: R*32 fp64][lambda]
+// Workspace layout (bytes): [A/U: K*K fp64][Cinv: K*K fp64][lambda: 32 fp64][Wd: R*K fp64][Err: R*128 fp64]
 size_t sparsegpt_factor_workspace(int64_t K) { return (size_t)(2 * K * K + 32) * sizeof(double); }
 
 size_t sparsegpt_workspace(int64_t R, int64_t K) {
-    return sparsegpt_factor_workspace(K) + (size_t)(R * K + R * kNB) * sizeof(double);
+    return sparsegpt_factor_workspace(K) + (size_t)(R * K + R * kLB) * sizeof(double);
 }
 
 hipError_t launch_hessian(const uint16_t *X, int64_t T, int64_t K, int64_t ldx, double *H, int64_t ldh,
@@ -564,19 +581,26 @@ hipError_t launch_sparsegpt(const uint16_t *W, int64_t ldw, int64_t R, int64_t K
     hipError_t e = launch_inverse_factor(H, ldh, K, damp, A, K, ws, st);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(widen_kernel, dim3(blocks_for(R * K)), dim3(256), 0, st, W, ldw, R, K, Wd);
-    for (int64_t c0 = 0; c0 < K; c0 += kNB) {
-        const unsigned g = (unsigned)((R + kBlkThreads - 1) / kBlkThreads);
-        switch (M) {
-        case 4: hipLaunchKernelGGL(sgpt_block_kernel<4>, dim3(g), dim3(kBlkThreads), 0, st, Wd, R, K, A, K, c0, Err, masks, values); break;
-        case 8: hipLaunchKernelGGL(sgpt_block_kernel<8>, dim3(g), dim3(kBlkThreads), 0, st, Wd, R, K, A, K, c0, Err, masks, values); break;
-        case 16: hipLaunchKernelGGL(sgpt_block_kernel<16>, dim3(g), dim3(kBlkThreads), 0, st, Wd, R, K, A, K, c0, Err, masks, values); break;
-        case 32: hipLaunchKernelGGL(sgpt_block_kernel<32>, dim3(g), dim3(kBlkThreads), 0, st, Wd, R, K, A, K, c0, Err, masks, values); break;
-        default: return hipErrorInvalidValue;
+    // Column blocks of 32 in lazy batches of 128: a block's errors compensate the rest of its
+    // batch at once; a batch's errors compensate every later column in one rank-128 update.
+    auto update = [&](int64_t n0, int64_t ncols, int e0, int64_t u0, int kw) {
+        hipLaunchKernelGGL(sgpt_update_kernel, dim3((unsigned)((ncols + 63) / 64), (unsigned)((R + 63) / 64)),
+                           dim3(256), 0, st, Wd, R, K, n0, ncols, Err, e0, A, K, u0, kw);
+    };
+    for (int64_t b0 = 0; b0 < K; b0 += kLB) {
+        const int64_t b1 = b0 + kLB < K ? b0 + kLB : K;
+        for (int64_t c0 = b0; c0 < b1; c0 += kNB) {
+            const unsigned g = (unsigned)((R + kBlkThreads - 1) / kBlkThreads);
+            switch (M) {
+            case 4: hipLaunchKernelGGL(sgpt_block_kernel<4>, dim3(g), dim3(kBlkThreads), 0, st, Wd, R, K, A, K, c0, Err, masks, values); break;
+            case 8: hipLaunchKernelGGL(sgpt_block_kernel<8>, dim3(g), dim3(kBlkThreads), 0, st, Wd, R, K, A, K, c0, Err, masks, values); break;
+            case 16: hipLaunchKernelGGL(sgpt_block_kernel<16>, dim3(g), dim3(kBlkThreads), 0, st, Wd, R, K, A, K, c0, Err, masks, values); break;
+            case 32: hipLaunchKernelGGL(sgpt_block_kernel<32>, dim3(g), dim3(kBlkThreads), 0, st, Wd, R, K, A, K, c0, Err, masks, values); break;
+            default: return hipErrorInvalidValue;
+            }
+            if (c0 + kNB < b1) update(c0 + kNB, b1 - c0 - kNB, (int)(c0 - b0), c0, kNB);
         }
-        const int64_t rest = K - c0 - kNB;
-        if (rest > 0)
-            hipLaunchKernelGGL(sgpt_trailing_kernel, dim3((unsigned)((rest + 63) / 64), (unsigned)((R + 63) / 64)),
-                               dim3(256), 0, st, Wd, R, K, A, K, c0, Err);
+        if (b1 < K) update(b1, K - b1, 0, b0, (int)(b1 - b0));
     }
     return hipGetLastError();
 }
