@@ -122,7 +122,8 @@ def parse():
     ap.add_argument("--batch", type=int, default=1, help="tokens per step (B)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-reps", type=int, default=12)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="wall time of the oracle sample on all host cores (half of it again on one core)")
     ap.add_argument("--skip-check", action="store_true", help="skip the oracle spot check")
     ap.add_argument("--no-meta-formats", action="store_true",
                     help="skip the bitmask vs uint8-offset vs int32-index comparison table")
@@ -674,27 +675,26 @@ def main():
             host.append((masks.cpu().numpy().view(np.uint32), values.contiguous().view(torch.int16).cpu().numpy()
                          .view(np.uint16), xs[group][0].contiguous().view(torch.int16).cpu().numpy().view(np.uint16), K))
             sb += sparse_bytes(R, K, B)
-        t1 = time.time()
-        for _ in range(args.cpu_reps):
-            for m_h, v_h, x_h, K in host:
-                oracle.spmv(m_h, v_h, x_h, K, nthreads=cores)
-        dt = time.time() - t1
-        # the same sample on one core (fewer repetitions: it is ~cores times slower)
-        reps1 = max(1, args.cpu_reps // 6)
-        t1 = time.time()
-        for _ in range(reps1):
-            for m_h, v_h, x_h, K in host:
-                oracle.spmv(m_h, v_h, x_h, K, nthreads=1)
-        dt1 = time.time() - t1
+        def run_for(seconds, nthreads):
+            """Whole passes over the layer until `seconds` of wall time have gone by."""
+            reps, t1 = 0, time.time()
+            while reps == 0 or time.time() - t1 < seconds:
+                for m_h, v_h, x_h, K in host:
+                    oracle.spmv(m_h, v_h, x_h, K, nthreads=nthreads)
+                reps += 1
+            return reps, time.time() - t1
+
+        reps, dt = run_for(args.cpu_seconds, cores)
+        reps1, dt1 = run_for(args.cpu_seconds / 2, 1)  # the same sample on one core
         model = ""
         try:
             with open("/proc/cpuinfo") as f:
                 model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
         except OSError:
             pass
-        cpu = {"value": round(sb * args.cpu_reps / dt / 1e9, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
+        cpu = {"value": round(sb * reps / dt / 1e9, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
                "sample": f"layer 0 of the set ({', '.join(p[0] for p in projs)}), {N}:{M}, B={B}, "
-                         f"x{args.cpu_reps} reps, {dt:.1f}s wall",
+                         f"x{reps} reps, {dt:.1f}s wall",
                "one_core": {"value": round(sb * reps1 / dt1 / 1e9, 3), "unit": "GB/s",
                             "sample": f"the same layer, x{reps1} reps, {dt1:.1f}s wall"},
                "cpu_model": model}
