@@ -68,11 +68,19 @@ nmk::MvPlan spmv_plan(int64_t R, int64_t K, int B, int fmt = nmk::kMetaBitmask) 
 }
 
 // Plan of one launch over a validated set: the matrix-core tile kernel where it applies
-// (bitmask, B >= 5, K a multiple of 1024), else the word-per-lane kernel.
+// (bitmask, B >= 5, K a multiple of 1024), else the word-per-lane kernel.  At B = 3 or 4
+// the tile kernel replaces the word-per-lane one only where the latter would cut K into
+// slices for LDS on a matrix with rows for every CU (e.g. 4096 x 14336 at B = 4:
+// 17.3 vs 19.7 us); elsewhere it is the slower of the two at these batch sizes.
 nmk::MvPlan spmv_set_plan(const nmk::SpmvSet &set, int fmt, int64_t K, int64_t ldx, int B, int epi) {
-    if (nmk::spmv_tile_ok(set, K, ldx, B, fmt, epi))
-        return nmk::plan_spmv_tile(set, K, B, device_info(), epi);
-    return spmv_plan(set.row0[set.P], K, B, fmt);
+    const int64_t R = set.row0[set.P];
+    const nmk::MvPlan word = spmv_plan(R, K, B, fmt);
+    if (nmk::spmv_tile_ok(set, K, ldx, B, fmt, epi)) {
+        const int64_t cu = device_info().num_cu > 0 ? device_info().num_cu : 256;
+        if (B >= nmk::kTileMinB || (word.splits > 1 && R >= 2 * cu))
+            return nmk::plan_spmv_tile(set, K, B, device_info(), epi);
+    }
+    return word;
 }
 
 nmk::MvPlan spmv_unstructured_plan(int64_t R, int64_t K, int B) {

@@ -106,12 +106,16 @@ hipError_t launch_spmv(const MvPlan &p, const SpmvSet &set, int fmt, int64_t K, 
 // silu(gate x) * (up x).  Plan for 2R rows.
 hipError_t launch_spmv_swiglu(const MvPlan &p, const SpmvSet &set, int64_t K, const uint16_t *x, int64_t ldx, int B,
                               float *ws, hipStream_t st);
-// Bitmask launches with B >= kTileMinB tokens can run on the matrix cores: each 16-row
-// tile of mask words is expanded into a dense tile in LDS and multiplied by the inputs
-// with MFMA.  spmv_tile_ok says whether a set qualifies (K a multiple of 1024, matrices
-// of a plain set starting at multiples of 16 rows, 32-bit buffer ranges); the tile plan
-// needs no workspace.  R = rows of the launch (gated MLP: 2 x the rows of each matrix).
+// Bitmask launches with B >= kTileMinB tokens run on the matrix cores: each 16-row tile
+// of mask words is expanded into a dense tile in LDS and multiplied by the inputs with
+// MFMA.  spmv_tile_ok says whether a set qualifies (K a multiple of 1024, matrices of a
+// plain set starting at multiples of 16 rows, 32-bit buffer ranges); the tile plan needs
+// no workspace.  R = rows of the launch (gated MLP: 2 x the rows of each matrix).  With
+// kTileLowB <= B < kTileMinB the tile kernel is taken only where the word-per-lane
+// kernel would cut K into slices (a row's x too large for LDS): it reads x from L2 and
+// needs neither the partial sums nor the second pass.
 constexpr int kTileMinB = 5;
+constexpr int kTileLowB = 3;
 bool spmv_tile_ok(const SpmvSet &set, int64_t K, int64_t ldx, int B, int fmt, int epi);
 MvPlan plan_spmv_tile(const SpmvSet &set, int64_t K, int B, const DeviceInfo &dev, int epi);
 hipError_t launch_spmv_tile(const MvPlan &p, const SpmvSet &set, int64_t K, const uint16_t *x, int64_t ldx, int B,

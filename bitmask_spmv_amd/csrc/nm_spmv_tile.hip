@@ -400,6 +400,8 @@ template <int EPI>
 hipError_t launch_te(const MvPlan &p, const SpmvSet &set, int64_t K, const uint16_t *x, int64_t ldx, int B,
                      hipStream_t st) {
     switch (B) {
+    case 3: return launch_tb<3, EPI>(p, set, K, x, ldx, st);
+    case 4: return launch_tb<4, EPI>(p, set, K, x, ldx, st);
     case 5: return launch_tb<5, EPI>(p, set, K, x, ldx, st);
     case 6: return launch_tb<6, EPI>(p, set, K, x, ldx, st);
     case 7: return launch_tb<7, EPI>(p, set, K, x, ldx, st);
@@ -411,7 +413,7 @@ hipError_t launch_te(const MvPlan &p, const SpmvSet &set, int64_t K, const uint1
 }  // namespace
 
 bool spmv_tile_ok(const SpmvSet &set, int64_t K, int64_t ldx, int B, int fmt, int epi) {
-    if (fmt != kMetaBitmask || B < kTileMinB || B > 8) return false;
+    if (fmt != kMetaBitmask || B < kTileLowB || B > 8) return false;
     if (K % (32 * 8 * kTStep) != 0) return false;  // every wave of an 8-wave workgroup gets whole steps
     // 32-bit buffer offsets: 8 rows of values, and the x rows of all tokens
     if ((int64_t)8 * K > ((int64_t)1 << 30) || (int64_t)(B - 1) * ldx * 2 + K * 2 > ((int64_t)1 << 30)) return false;

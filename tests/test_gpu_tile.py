@@ -1,6 +1,7 @@
 """GPU parity of the matrix-core path of the bitmask SpMV (5 <= B <= 8 tokens, K a
-multiple of 1024): each 16-row tile of mask words is expanded into a dense tile in LDS
-by the fixed 16-step walk and multiplied by the inputs with MFMA.  Held to the same
+multiple of 1024; at B = 3 or 4 where a row's x is too large for the word-per-lane
+kernel's LDS): each 16-row tile of mask words is expanded into a dense tile in LDS by
+the fixed 16-step walk and multiplied by the inputs with MFMA.  Held to the same
 bars as the word-per-lane path: the oracle's tolerance element by element, exact
 equality where the result is an integer or a single weight."""
 from __future__ import annotations
@@ -187,3 +188,40 @@ def test_tile_swiglu_two_tiles_per_step(R, B):
     ref = oracle.swiglu(g, u)
     ok = np.abs(bf16_as_f64(h) - ref) <= oracle.swiglu_tolerance(g, ag, u, au)
     assert ok.all(), f"swiglu two per step R={R} B={B}: {int((~ok).sum())} outside"
+
+
+# B = 3 or 4 with K above 8192 columns (a row's x exceeds the word-per-lane kernel's LDS
+# slice) and at least 512 rows: these launches run on the tile path too.
+@pytest.mark.parametrize("R,K,B", [(4096, 14336, 4), (1000, 9216, 3), (513, 12288, 4), (2048, 28672, 3)])
+def test_tile_small_batch_wide_rows(R, K, B):
+    say("tile small batch wide", R, K, B)
+    W = synth.weights(R, K, 40, R, K, B)
+    mref, vref = oracle.prune_pack(W, oracle.col_norm(synth.calib_acts(K, 40, R)), 8, 16)
+    x = synth.decode_x(B, K, 40, R, K, B)
+    y = nm.nm_spmv(dev_u32(mref), dev_bf16(vref), dev_bf16(x))
+    yref, absum = oracle.spmv(mref, vref, x, K, nthreads=8)
+    assert_within(host_bf16(y), yref, absum, f"tile R={R} K={K} B={B}")
+
+
+@pytest.mark.parametrize("B", [3, 4])
+def test_tile_small_batch_multi_and_swiglu(B):
+    say("tile small batch multi+swiglu", B)
+    K = 10240
+    x = synth.decode_x(B, K, 41, B)
+    n = oracle.col_norm(synth.calib_acts(K, 41, B))
+    packed, refs = [], []
+    for i, R in enumerate([512, 256, 250]):
+        mref, vref = oracle.prune_pack(synth.weights(R, K, 41, B, i), n, 2, 4)
+        refs.append(oracle.spmv(mref, vref, x, K, nthreads=8))
+        packed.append((dev_u32(mref), dev_bf16(vref)))
+    ys = nm.nm_spmv_multi(packed, dev_bf16(x))
+    for i, (y, (yref, absum)) in enumerate(zip(ys, refs)):
+        assert_within(host_bf16(y), yref, absum, f"multi B={B} matrix {i}")
+    R = 600
+    gm, gv = oracle.prune_pack(synth.weights(R, K, 41, B, 10), n, 4, 8)
+    um, uv = oracle.prune_pack(synth.weights(R, K, 41, B, 11), n, 4, 8)
+    h = host_bf16(nm.nm_spmv_swiglu((dev_u32(gm), dev_bf16(gv)), (dev_u32(um), dev_bf16(uv)), dev_bf16(x)))
+    g, ag = oracle.spmv(gm, gv, x, K, nthreads=8)
+    u, au = oracle.spmv(um, uv, x, K, nthreads=8)
+    ok = np.abs(bf16_as_f64(h) - oracle.swiglu(g, u)) <= oracle.swiglu_tolerance(g, ag, u, au)
+    assert ok.all(), f"swiglu B={B}: {int((~ok).sum())} outside"
