@@ -43,7 +43,7 @@ constexpr int kThreads = 512;     // default workgroup: 8 waves (256 for matrice
 // whose x slice leaves room for only two workgroups per CU: the bitmask kernel at B = 3
 // and 4 fits that register budget without spilling (measured 4-9% faster on the 70B
 // shapes at B = 4); B >= 5 and the index formats would spill.
-constexpr bool wide_ok(int fmt, int B) { return fmt == kMetaBitmask && (B == 3 || B == 4); }
+constexpr bool wide_ok(int fmt, int B) { return fmt == kMetaBitmask && B <= 4; }
 constexpr size_t kLdsCap = 80 * 1024;     // keeps two workgroups resident per CU
 constexpr size_t kLdsPerCu = 160 * 1024;  // gfx950 LDS per compute unit
 
@@ -441,6 +441,16 @@ MvPlan plan_spmv(int64_t R, int64_t K, int B, const DeviceInfo &dev, int fmt) {
         p.threads = 256;
     else if (per_cu <= 2 && wide_ok(fmt, B))
         p.threads = 1024;  // x large enough to allow only two workgroups: twice the waves per CU
+    else if (B <= 2 && KW >= 256 && wide_ok(fmt, B) && splits == 1) {
+        // Rows of 8192+ columns at B <= 2: two 16-wave workgroups per CU stage x half as
+        // often as four 8-wave ones, where every wave still gets the same number of rows
+        // (an uneven split costs more with the larger workgroups).
+        const int64_t g16 = std::min<int64_t>((R + 15) / 16, 2 * cu);
+        if (R % (16 * g16) == 0) {
+            p.threads = 1024;
+            per_cu = 2;
+        }
+    }
     const int64_t waves = p.threads / kWave;
     int64_t gx = (R + waves - 1) / waves;
     int64_t cap_x = (per_cu * cu + splits - 1) / splits;

@@ -170,8 +170,9 @@ def test_spmv_every_batch_size(B):
 
 # x slices large enough that only two workgroups fit per CU at B = 3 and 4: the bitmask
 # kernel and the dense GEMV then run 1024-thread workgroups (incl. split rows for
-# K = 28672).
-WIDE = [(3000, 8192, 3), (2100, 8192, 4), (700, 28672, 4), (2049, 9216, 3)]
+# K = 28672); at B = 1 and 2 the bitmask kernel does so for rows of 8192+ columns too.
+WIDE = [(3000, 8192, 3), (2100, 8192, 4), (700, 28672, 4), (2049, 9216, 3), (1024, 8192, 1), (2048, 16384, 2),
+        (1000, 28672, 1)]
 
 
 @pytest.mark.parametrize("R,K,B", WIDE)
