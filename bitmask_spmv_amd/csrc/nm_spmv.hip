@@ -439,14 +439,15 @@ MvPlan plan_spmv(int64_t R, int64_t K, int B, const DeviceInfo &dev, int fmt) {
     // workgroups, which spreads them over twice as many CUs.
     if ((R + kThreads / kWave - 1) / (kThreads / kWave) * splits < cu)
         p.threads = 256;
-    else if (per_cu <= 2 && wide_ok(fmt, B))
+    else if (per_cu <= 2 && wide_ok(fmt, B) && B >= 3)
         p.threads = 1024;  // x large enough to allow only two workgroups: twice the waves per CU
-    else if (B <= 2 && KW >= 256 && wide_ok(fmt, B) && splits == 1) {
+    else if (B <= 2 && wide_ok(fmt, B) && (per_cu <= 2 || (KW >= 256 && splits == 1))) {
         // Rows of 8192+ columns at B <= 2: two 16-wave workgroups per CU stage x half as
-        // often as four 8-wave ones, where every wave still gets the same number of rows
-        // (an uneven split costs more with the larger workgroups).
-        const int64_t g16 = std::min<int64_t>((R + 15) / 16, 2 * cu);
-        if (R % (16 * g16) == 0) {
+        // often as four 8-wave ones, where the larger workgroups still split evenly -- the
+        // same number of rows for every wave and the same number of workgroups on every
+        // CU (5120 rows: 320 workgroups on 256 CUs made the launch 10-14% slower).
+        const int64_t g16 = std::min<int64_t>((R + 15) / 16, (2 * cu + splits - 1) / splits);
+        if (R % (16 * g16) == 0 && (g16 * splits) % cu == 0) {
             p.threads = 1024;
             per_cu = 2;
         }
