@@ -160,11 +160,10 @@ __device__ __forceinline__ uint32_t tpair_swap(uint32_t v) {
 // walk the word from its lowest set bit up, odd lanes from its highest set bit down (the
 // lowest set bit of the bit-reversed mask, the values taken in reverse order): at each
 // of the 16 steps the lanes then write near opposite ends of their words, which spreads
-// the writes of lanes whose words start on the same LDS bank.  A word whose mask runs out
-// of set bits (only rows past the matrix, whose loads read zero) writes one column before
-// the word (even lanes) or one after it (odd lanes): the row's lead pad, the neighbouring
-// word of the same row, the next row's lead pad or the tile's tail pad -- never another
-// row's data or another wave's tile.  The zeroing writes of lanes with rows 8..15 take
+// the writes of lanes whose words start on the same LDS bank.  A word without exactly 16
+// set bits (rows past the matrix, whose loads read zero, or a malformed mask) walks the
+// mask 0xFFFF instead, so every one of the 16 bit scans has a set bit to find and the
+// writes stay inside the lane's own word.  The zeroing writes of lanes with rows 8..15 take
 // the word's 16-byte chunks in the order 2, 3, 0, 1, so the 16 lanes of each group of a
 // 16-byte write cover distinct banks.  The wave's LDS operations execute in issue order,
 // so the expansion is complete before the operand reads that follow it, and the operand
@@ -183,6 +182,7 @@ __device__ __forceinline__ void walk_tile(const u32x4 &va, const u32x4 &vb, uint
 #pragma unroll
     for (int d = 0; d < 8; ++d) v[d] = odd ? __builtin_amdgcn_alignbit(od[d], od[d], 16) : ev[d];
     uint32_t m = odd ? __builtin_bitreverse32(mb) : ma;
+    m = __builtin_popcount(m) == 16 ? m : 0xFFFFu;
     uint8_t *ub = tw + ((lane & 1) * 8 + (lane >> 3)) * kTRowBytes + 16 + ((lane & 7) >> 1) * 64;
     uint8_t *wb = odd ? ub + 62 : ub;  // column c of the walk order sits at wb + step * c
     const int step = odd ? -2 : 2;
