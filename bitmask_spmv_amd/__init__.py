@@ -27,12 +27,15 @@ __all__ = [
     "dense_gemv_swiglu_workspace_bytes", "nm_prune_pack_unstructured", "nm_spmv_unstructured",
     "nm_spmv_unstructured_workspace_bytes", "nm_unpack_unstructured", "nm_hessian", "nm_obs_inverse_factor",
     "nm_obs_inverse_factor_workspace_bytes", "nm_sparsegpt_prune_pack", "nm_sparsegpt_workspace_bytes",
-    "nm_stream_read", "nm_stream_read_sink_words",
+    "nm_stream_read", "nm_stream_read_sink_words", "nm_spmv_plan", "nm_spmv_multi_plan", "NM_EPI_NONE",
+    "NM_EPI_SWIGLU", "NM_KERNEL_WORD", "NM_KERNEL_TILE",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnmspmv.so")
 NM_PATTERNS = ((2, 4), (4, 8), (8, 16), (16, 32))
 NM_META_BITMASK, NM_META_U8_OFFSET, NM_META_I32_INDEX = 0, 1, 2
+NM_EPI_NONE, NM_EPI_SWIGLU = 0, 1
+NM_KERNEL_WORD, NM_KERNEL_TILE = 0, 1
 
 _STATUS = {0: "NM_OK", 1: "NM_ERR_NULL", 2: "NM_ERR_SHAPE", 3: "NM_ERR_PATTERN", 4: "NM_ERR_ALIGN",
            5: "NM_ERR_WORKSPACE", 6: "NM_ERR_HIP"}
@@ -47,6 +50,12 @@ class NmError(RuntimeError):
 class _SpmvMatrix(ctypes.Structure):
     _fields_ = [("masks", ctypes.c_void_p), ("values", ctypes.c_void_p), ("R", ctypes.c_int64),
                 ("y", ctypes.c_void_p), ("ldy", ctypes.c_int64)]
+
+
+class _LaunchPlan(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int), ("threads", ctypes.c_int), ("grid_x", ctypes.c_int),
+                ("splits", ctypes.c_int), ("tiles_per_step", ctypes.c_int), ("reserved", ctypes.c_int),
+                ("lds_bytes", ctypes.c_size_t), ("workspace_bytes", ctypes.c_size_t)]
 
 
 class _DenseMatrix(ctypes.Structure):
@@ -98,6 +107,8 @@ def _load() -> ctypes.CDLL:
     L.dense_gemv_multi.argtypes = [p, i32, i64, p, i64, i32, p, sz, p]
     L.nm_stream_read_sink_words.argtypes, L.nm_stream_read_sink_words.restype = [sz], sz
     L.nm_stream_read.argtypes, L.nm_stream_read.restype = [p, sz, p, sz, p], i32
+    L.nm_spmv_plan.argtypes, L.nm_spmv_plan.restype = [i64, i64, i32, i32, p], i32
+    L.nm_spmv_multi_plan.argtypes, L.nm_spmv_multi_plan.restype = [p, i32, i64, i32, p], i32
     for f in (L.nm_col_norm, L.nm_prune_pack, L.nm_spmv, L.dense_gemv, L.nm_unpack, L.nm_spmv_multi,
               L.dense_gemv_multi):
         f.restype = i32
@@ -549,3 +560,24 @@ def nm_stream_read(buf: torch.Tensor, sink: torch.Tensor | None = None) -> torch
     _dev(sink, "sink", torch.int32, 1)
     _check(lib.nm_stream_read(_ptr(buf), nbytes, _ptr(sink), sink.numel(), _stream(buf)))
     return sink
+
+
+def _plan_dict(pl: _LaunchPlan) -> dict:
+    return {f: getattr(pl, f) for f, _ in _LaunchPlan._fields_ if f != "reserved"}
+
+
+def nm_spmv_plan(R: int, K: int, B: int, epilogue: int = NM_EPI_NONE) -> dict:
+    """Launch plan of nm_spmv (or nm_spmv_swiglu with epilogue=NM_EPI_SWIGLU, R rows each)
+    on the current device: kernel, threads, grid_x, splits, tiles_per_step, lds_bytes,
+    workspace_bytes.  Host only."""
+    pl = _LaunchPlan()
+    _check(lib.nm_spmv_plan(int(R), int(K), int(B), int(epilogue), ctypes.byref(pl)))
+    return _plan_dict(pl)
+
+
+def nm_spmv_multi_plan(rows, K: int, B: int) -> dict:
+    """Launch plan of nm_spmv_multi over matrices with the given row counts.  Host only."""
+    arr = (ctypes.c_int64 * len(rows))(*[int(r) for r in rows])
+    pl = _LaunchPlan()
+    _check(lib.nm_spmv_multi_plan(arr, len(rows), int(K), int(B), ctypes.byref(pl)))
+    return _plan_dict(pl)

@@ -19,7 +19,10 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{os.path.join(ROOT, 'include')}"]
-HIP_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Leading kernel arguments are preloaded into scalar registers at wave launch (gfx950), so
+# a kernel's first loads need not wait for a kernel-argument read.
+HIP_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-mllvm", "-amdgpu-kernarg-preload-count=16"]
 
 
 def _hipcc() -> str:

@@ -353,6 +353,67 @@ nm_status nm_spmv_swiglu(const uint32_t *gate_masks, const nm_bf16 *gate_values,
     }
 }
 
+static void fill_plan(const nmk::MvPlan &p, nm_launch_plan *out) {
+    out->kernel = p.tile ? NM_KERNEL_TILE : NM_KERNEL_WORD;
+    out->threads = p.threads;
+    out->grid_x = p.grid_x;
+    out->splits = p.splits;
+    out->tiles_per_step = p.tile ? p.unroll : 0;
+    out->reserved = 0;
+    out->lds_bytes = p.tile ? 0 : p.lds_bytes;
+    out->workspace_bytes = p.ws_bytes;
+}
+
+nm_status nm_spmv_plan(int64_t R, int64_t K, int B, int epilogue, nm_launch_plan *plan) {
+    try {
+        g_err[0] = 0;
+        if (!plan) return fail(NM_ERR_NULL, "nm_spmv_plan: NULL plan");
+        if (epilogue != NM_EPI_NONE && epilogue != NM_EPI_SWIGLU)
+            return fail(NM_ERR_PATTERN, "nm_spmv_plan: unknown epilogue %d", epilogue);
+        const int64_t rmax = epilogue == NM_EPI_SWIGLU ? kMaxDim / 2 : kMaxDim;
+        if (R < 1 || R > rmax || K < 32 || K > kMaxDim || K % 32 != 0 || B < 1 || B > 8)
+            return fail(NM_ERR_SHAPE, "nm_spmv_plan: bad sizes R=%lld K=%lld B=%d", (long long)R, (long long)K, B);
+        nmk::SpmvSet set;
+        if (epilogue == NM_EPI_SWIGLU) {
+            set.P = 2;
+            set.row0[1] = (int)R;
+            set.row0[2] = (int)(2 * R);
+        } else {
+            set.P = 1;
+            set.row0[1] = (int)R;
+        }
+        const int epi = epilogue == NM_EPI_SWIGLU ? nmk::kEpiSwiGLU : nmk::kEpiNone;
+        fill_plan(spmv_set_plan(set, NM_META_BITMASK, K, K, B, epi), plan);
+        return NM_OK;
+    } catch (...) {
+        return fail(NM_ERR_HIP, "nm_spmv_plan: internal error");
+    }
+}
+
+nm_status nm_spmv_multi_plan(const int64_t *rows, int P, int64_t K, int B, nm_launch_plan *plan) {
+    try {
+        g_err[0] = 0;
+        if (!plan || !rows) return fail(NM_ERR_NULL, "nm_spmv_multi_plan: NULL pointer");
+        if (P < 1 || P > nmk::kMaxMats || K < 32 || K > kMaxDim || K % 32 != 0 || B < 1 || B > 8)
+            return fail(NM_ERR_SHAPE, "nm_spmv_multi_plan: bad sizes P=%d K=%lld B=%d", P, (long long)K, B);
+        nmk::SpmvSet set;
+        int64_t total = 0;
+        set.P = P;
+        for (int i = 0; i < P; ++i) {
+            if (rows[i] < 1 || rows[i] > kMaxDim)
+                return fail(NM_ERR_SHAPE, "nm_spmv_multi_plan: matrix %d has R=%lld", i, (long long)rows[i]);
+            set.row0[i] = (int)total;
+            total += rows[i];
+            if (total > kMaxDim) return fail(NM_ERR_SHAPE, "nm_spmv_multi_plan: more than 2^30 rows in total");
+        }
+        set.row0[P] = (int)total;
+        fill_plan(spmv_set_plan(set, NM_META_BITMASK, K, K, B, nmk::kEpiNone), plan);
+        return NM_OK;
+    } catch (...) {
+        return fail(NM_ERR_HIP, "nm_spmv_multi_plan: internal error");
+    }
+}
+
 nm_status nm_prune_pack_unstructured(const nm_bf16 *W, int64_t ldw, int64_t R, int64_t K, const float *col_norm,
                                      uint32_t *masks, nm_bf16 *values, void *hip_stream) {
     try {
@@ -661,7 +722,7 @@ nm_status nm_unpack(const uint32_t *masks, const nm_bf16 *values, int64_t R, int
     }
 }
 
-size_t nm_stream_read_sink_words(size_t bytes) { return nmk::stream_read_groups(bytes); }
+size_t nm_stream_read_sink_words(size_t bytes) { return nmk::stream_read_waves(bytes); }
 
 nm_status nm_stream_read(const void *buf, size_t bytes, uint32_t *sink, size_t sink_words, void *hip_stream) {
     try {
@@ -671,7 +732,7 @@ nm_status nm_stream_read(const void *buf, size_t bytes, uint32_t *sink, size_t s
             return fail(NM_ERR_SHAPE, "nm_stream_read: bytes=%zu must be a multiple of 16 in [16, 2^31]", bytes);
         if (!aligned(buf, 16) || !aligned(sink, 4))
             return fail(NM_ERR_ALIGN, "nm_stream_read: buf needs 16-byte alignment");
-        const size_t need = nmk::stream_read_groups(bytes);
+        const size_t need = nmk::stream_read_waves(bytes);
         if (sink_words < need)
             return fail(NM_ERR_WORKSPACE, "nm_stream_read: sink of %zu words required, %zu given", need, sink_words);
         hipError_t e = nmk::launch_stream_read(buf, bytes, sink, (hipStream_t)hip_stream);

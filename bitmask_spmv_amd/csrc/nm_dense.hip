@@ -92,6 +92,9 @@ __device__ __forceinline__ void locate(const DenseSet &set, int r, int &p, int &
     if constexpr (EPI == kEpiSwiGLU) {
         p = r & 1;
         local = r >> 1;
+    } else if constexpr (EPI == kEpiOne) {
+        p = 0;
+        local = r;
     } else {
         p = owner(set, r);
         local = r - set.row0[p];
@@ -150,19 +153,37 @@ __device__ __forceinline__ void hold(uint32_t (&held)[B]) {
     for (int b = 0; b < B; ++b) asm volatile("" : "+v"(held[b]));
 }
 
+// Matrix 0's array and row stride come in as kernel arguments (W0, ldw0), as in the
+// sparse kernel: a one-matrix launch uses only those, and the gated MLP (one shared row
+// stride) picks between them and matrix 1's array at a fixed argument offset.
 template <int U, int EPI>
-__device__ __forceinline__ void load_row_dbatch(DBatch<U> &bt, const DenseSet &set, int r, int c0, int chunks,
-                                                int base, int lane) {
+__device__ __forceinline__ void load_row_dbatch(DBatch<U> &bt, const DenseSet &set, const uint16_t *W0, int64_t ldw0,
+                                                int r, int c0, int chunks, int base, int lane) {
     int p, local;
     locate<EPI>(set, r, p, local);
-    const u32x4 *wrow = reinterpret_cast<const u32x4 *>(set.W[p]) + (int64_t)local * (set.ldw[p] / 8) + c0;
+    const uint16_t *wp;
+    int64_t ldw;
+    if constexpr (EPI == kEpiOne) {
+        wp = W0;
+        ldw = ldw0;
+    } else if constexpr (EPI == kEpiSwiGLU) {
+        wp = p ? set.W[1] : W0;
+        ldw = ldw0;
+    } else {
+        wp = set.W[p];
+        ldw = set.ldw[p];
+    }
+    const u32x4 *wrow = reinterpret_cast<const u32x4 *>(wp) + (int64_t)local * (ldw / 8) + c0;
     load_dbatch<U>(bt, wrow, chunks, base, lane);
 }
 
+// Leading arguments as in the sparse kernel: what the first batch of loads depends on.
 template <int B, int U, int EPI, int NT>
-__global__ __launch_bounds__(NT, NT == 1024 ? 8 : 1) void dense_kernel(const DenseSet set, int KC, const uint16_t *__restrict__ x,
-                                                         int64_t ldx, float *__restrict__ partial, int slice) {
-    const int R = set.row0[set.P];
+__global__ __launch_bounds__(NT, NT == 1024 ? 8 : 1) void dense_kernel(const uint16_t *W0, int64_t ldw0, int R, int KC,
+                                                                       int gx, int split,
+                                                                       const uint16_t *__restrict__ x, int64_t ldx,
+                                                                       int slice, float *__restrict__ partial,
+                                                                       const DenseSet set) {
     extern __shared__ u32x4 xs4[];  // [B][ncs]
     const int s = blockIdx.y;
     const int c0 = s * slice;
@@ -174,8 +195,7 @@ __global__ __launch_bounds__(NT, NT == 1024 ? 8 : 1) void dense_kernel(const Den
     // Same flat, software-pipelined walk over (row, batch) as the sparse kernel, with the
     // same row order (row pairs for the gated MLP).
     const int unit = blockIdx.x * kWaves + wave;
-    const int row_step = gridDim.x * kWaves;
-    const int split = gridDim.y != 1 ? 1 : 0;
+    const int row_step = gx * kWaves;
     const int first_row = EPI == kEpiSwiGLU ? 2 * unit : unit;
     const int units = EPI == kEpiSwiGLU ? R / 2 : R;
     const int my_rows = (unit < units ? (units - 1 - unit) / row_step + 1 : 0) * (EPI == kEpiSwiGLU ? 2 : 1);
@@ -207,7 +227,7 @@ __global__ __launch_bounds__(NT, NT == 1024 ? 8 : 1) void dense_kernel(const Den
                 const int b = i / ncs;
                 r[j] = reinterpret_cast<const u32x4 *>(x + (int64_t)b * ldx)[c0 + (i - b * ncs)];
             }
-            if (i0 == 0) load_row_dbatch<U, EPI>(bufA, set, min(rowA, R - 1), c0, total > 0 ? ncs : 0, 0, lane);
+            if (i0 == 0) load_row_dbatch<U, EPI>(bufA, set, W0, ldw0, min(rowA, R - 1), c0, total > 0 ? ncs : 0, 0, lane);
 #pragma unroll
             for (int j = 0; j < kStage; ++j) {
                 if (j > 0 && j >= left) break;
@@ -239,7 +259,7 @@ __global__ __launch_bounds__(NT, NT == 1024 ? 8 : 1) void dense_kernel(const Den
         rowB = rowA;
         biB = biA;
         step(rowB, biB);
-        load_row_dbatch<U, EPI>(bufB, set, min(rowB, R - 1), c0, ncs, biB * kWave * U, lane);
+        load_row_dbatch<U, EPI>(bufB, set, W0, ldw0, min(rowB, R - 1), c0, ncs, biB * kWave * U, lane);
         hold(held);
         __builtin_amdgcn_sched_barrier(0);
         dot_dbatch<B, U>(bufA, xs4, ncs, acc);
@@ -247,7 +267,7 @@ __global__ __launch_bounds__(NT, NT == 1024 ? 8 : 1) void dense_kernel(const Den
         rowA = rowB;
         biA = biB;
         step(rowA, biA);
-        load_row_dbatch<U, EPI>(bufA, set, min(rowA, R - 1), c0, t + 2 < total ? ncs : 0, biA * kWave * U, lane);
+        load_row_dbatch<U, EPI>(bufA, set, W0, ldw0, min(rowA, R - 1), c0, t + 2 < total ? ncs : 0, biA * kWave * U, lane);
         hold(held);
         __builtin_amdgcn_sched_barrier(0);
         dot_dbatch<B, U>(bufB, xs4, ncs, acc);
@@ -315,8 +335,9 @@ hipError_t launch_bun(const MvPlan &p, const DenseSet &set, int64_t K, const uin
     if (e != hipSuccess) return e;
     DenseSet padded = set;  // row0 past the last matrix = the total (see owner())
     for (int q = set.P + 1; q <= kMaxMats; ++q) padded.row0[q] = set.row0[set.P];
-    hipLaunchKernelGGL((dense_kernel<B, U, EPI, NT>), dim3(p.grid_x, p.splits), dim3(NT), p.lds_bytes, st, padded,
-                       (int)(K / 8), x, ldx, ws, p.slice);
+    hipLaunchKernelGGL((dense_kernel<B, U, EPI, NT>), dim3(p.grid_x, p.splits), dim3(NT), p.lds_bytes, st, set.W[0],
+                       set.ldw[0], set.row0[set.P], (int)(K / 8), p.grid_x, p.splits > 1 ? 1 : 0, x, ldx, p.slice, ws,
+                       padded);
     e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;
     const int R = set.row0[set.P];
@@ -409,6 +430,7 @@ MvPlan plan_dense(int64_t R, int64_t K, int B, const DeviceInfo &dev, int epi) {
 
 hipError_t launch_dense(const MvPlan &p, const DenseSet &set, int64_t K, const uint16_t *x, int64_t ldx, int B,
                         float *ws, hipStream_t st) {
+    if (set.P == 1) return launch_e<kEpiOne>(p, set, K, x, ldx, B, ws, st);
     return launch_e<kEpiNone>(p, set, K, x, ldx, B, ws, st);
 }
 

@@ -38,6 +38,10 @@ struct MvPlan {
 // matrix 0's output.
 constexpr int kEpiNone = 0;
 constexpr int kEpiSwiGLU = 1;
+// kEpiOne: a launch over a single matrix (set.P == 1).  Same rows and outputs as kEpiNone;
+// the matrix's pointers come straight from the kernel arguments, with no row-to-matrix
+// lookup, so a wave can issue its first loads from preloaded argument registers.
+constexpr int kEpiOne = 2;
 
 // Matrices that read the same input x (q, k, v; gate, up) walked by one launch: global
 // row r belongs to matrix p when row0[p] <= r < row0[p + 1]; x is staged once.
@@ -125,8 +129,9 @@ hipError_t launch_dense(const MvPlan &p, const DenseSet &set, int64_t K, const u
 hipError_t launch_dense_swiglu(const MvPlan &p, const DenseSet &set, int64_t K, const uint16_t *x, int64_t ldx, int B,
                                float *ws, hipStream_t st);
 // Measurement aid: one streaming read of `bytes` bytes (multiple of 16, <= 2^31), one
-// XOR-fold per workgroup into sink[0 .. stream_read_groups(bytes)).
+// XOR-fold per wave into sink[0 .. stream_read_waves(bytes)).
 size_t stream_read_groups(size_t bytes);
+size_t stream_read_waves(size_t bytes);
 hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t st);
 
 }  // namespace nmk

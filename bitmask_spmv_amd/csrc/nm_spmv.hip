@@ -118,7 +118,9 @@ __device__ __forceinline__ uint32_t pair_swap(uint32_t v) {
 //
 // A padding lane (past the slice) holds zero values and walks fixed columns of block 0
 // (bitmask: the low 16 columns; index formats: zero metadata, column 0), so every LDS
-// address stays inside the staged x.
+// address stays inside the staged x.  A bitmask word without exactly 16 set bits (outside
+// the input contract) walks the low 16 columns of its own block instead, so each of the
+// 16 bit scans finds a set bit.
 template <int FMT, int B>
 __device__ __forceinline__ void walk_batch(const Batch<FMT> &bt, const uint32_t *xs, int nws, float (&acc)[B]) {
     constexpr int kBlk = XLayout<B>::kBlk;
@@ -143,7 +145,7 @@ __device__ __forceinline__ void walk_batch(const Batch<FMT> &bt, const uint32_t 
         const uint32_t v[8] = {odd ? r_x : bt.va.x, odd ? r_y : bt.va.y, odd ? r_z : bt.va.z, odd ? r_w : bt.va.w,
                                odd ? bt.vb.x : r_x, odd ? bt.vb.y : r_y, odd ? bt.vb.z : r_z, odd ? bt.vb.w : r_w};
         const uint32_t *blk = xs + (ok ? bt.lw : 0) * kBlk;  // this word's 32 columns
-        uint32_t mm = ok ? bt.meta[0].x : 0xFFFFu;
+        uint32_t mm = ok && __builtin_popcount(bt.meta[0].x) == 16 ? bt.meta[0].x : 0xFFFFu;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             int c0, c1;
@@ -168,6 +170,9 @@ __device__ __forceinline__ void locate(const SpmvSet &set, int r, int &p, int &l
     if constexpr (EPI == kEpiSwiGLU) {
         p = r & 1;
         local = r >> 1;
+    } else if constexpr (EPI == kEpiOne) {
+        p = 0;
+        local = r;
     } else {
         p = owner(set, r);
         local = r - set.row0[p];
@@ -208,21 +213,44 @@ __device__ __forceinline__ void finish_row(float (&acc)[B], float (&gsave)[B], c
     for (int b = 0; b < B; ++b) set.y[p][(int64_t)b * set.ldy[p] + local] = f32_to_bf16_rne(val[b]);
 }
 
-// Batch loads of launch row r, word offset `base` within the slice.
+// Batch loads of launch row r, word offset `base` within the slice.  meta0 / values0 are
+// matrix 0's arrays as kernel arguments: a one-matrix launch reads only those, and the
+// gated MLP picks between them and matrix 1's at a fixed argument offset, so neither
+// waits for an argument load that depends on another before its first batch goes out.
 template <int FMT, int EPI>
-__device__ __forceinline__ void load_row_batch(Batch<FMT> &bt, const SpmvSet &set, int r, int KW, int w0, int words,
-                                               int base, int lane) {
+__device__ __forceinline__ void load_row_batch(Batch<FMT> &bt, const SpmvSet &set, const void *meta0,
+                                               const uint16_t *values0, int r, int KW, int w0, int words, int base,
+                                               int lane) {
     int p, local;
     locate<EPI>(set, r, p, local);
     const int64_t off = (int64_t)local * KW + w0;  // in words
-    load_batch<FMT>(bt, reinterpret_cast<const uint8_t *>(set.meta[p]) + off * meta_bytes(FMT),
-                    reinterpret_cast<const u32x4 *>(set.values[p]) + off * 2, words, base, lane);
+    const void *mp;
+    const uint16_t *vp;
+    if constexpr (EPI == kEpiOne) {
+        mp = meta0;
+        vp = values0;
+    } else if constexpr (EPI == kEpiSwiGLU) {
+        mp = p ? set.meta[1] : meta0;
+        vp = p ? set.values[1] : values0;
+    } else {
+        mp = set.meta[p];
+        vp = set.values[p];
+    }
+    load_batch<FMT>(bt, reinterpret_cast<const uint8_t *>(mp) + off * meta_bytes(FMT),
+                    reinterpret_cast<const u32x4 *>(vp) + off * 2, words, base, lane);
 }
 
+// The scalars that the first batch of loads depends on lead the argument list (matrix 0's
+// arrays, the launch's row count R, the words per row KW, the grid width gx and whether
+// rows are split): the library is built to preload leading kernel arguments into scalar
+// registers, so a wave can issue its first weight loads without waiting for an argument
+// load, and no dispatch-packet read is needed for the grid size.
 template <int FMT, int B, int NT, int EPI>
-__global__ __launch_bounds__(NT, NT == 1024 ? 8 : 1) void spmv_kernel(const SpmvSet set, int KW, const uint16_t *__restrict__ x,
-                                                  int64_t ldx, float *__restrict__ partial, int slice) {
-    const int R = set.row0[set.P];
+__global__ __launch_bounds__(NT, NT == 1024 ? 8 : 1) void spmv_kernel(const void *meta0, const uint16_t *values0, int R,
+                                                                      int KW, int gx, int split,
+                                                                      const uint16_t *__restrict__ x, int64_t ldx,
+                                                                      int slice, float *__restrict__ partial,
+                                                                      const SpmvSet set) {
     extern __shared__ uint32_t xs[];  // [nws][XLayout<B>::kBlk]
     const int s = blockIdx.y;
     const int w0 = s * slice;
@@ -238,8 +266,7 @@ __global__ __launch_bounds__(NT, NT == 1024 ? 8 : 1) void spmv_kernel(const Spmv
     // into nb strips of 64 words, walked as one flat sequence so the next strip's loads
     // are in flight while the current one is computed, across row boundaries too.
     const int unit = blockIdx.x * kWaves + wave;
-    const int split = gridDim.y != 1 ? 1 : 0;
-    const int row_step = gridDim.x * kWaves;
+    const int row_step = gx * kWaves;
     const int first_row = EPI == kEpiSwiGLU ? 2 * unit : unit;
     const int units = EPI == kEpiSwiGLU ? R / 2 : R;
     const int my_rows = (unit < units ? (units - 1 - unit) / row_step + 1 : 0) * (EPI == kEpiSwiGLU ? 2 : 1);
@@ -265,7 +292,7 @@ __global__ __launch_bounds__(NT, NT == 1024 ? 8 : 1) void spmv_kernel(const Spmv
     // of x loads, so waiting for x (an L2 hit after the first workgroup of an XCD) never
     // waits for the weights queued behind it.
     stage_x<B, NT>(xs, x, ldx, w0, nws, [&] {
-        load_row_batch<FMT, EPI>(bufA, set, min(rowA, R - 1), KW, w0, total > 0 ? nws : 0, 0, lane);
+        load_row_batch<FMT, EPI>(bufA, set, meta0, values0, min(rowA, R - 1), KW, w0, total > 0 ? nws : 0, 0, lane);
     });
     __syncthreads();
 
@@ -283,7 +310,7 @@ __global__ __launch_bounds__(NT, NT == 1024 ? 8 : 1) void spmv_kernel(const Spmv
         rowB = rowA;
         biB = biA;
         step(rowB, biB);
-        load_row_batch<FMT, EPI>(bufB, set, min(rowB, R - 1), KW, w0, nws, biB * kWave, lane);  // batch t+1
+        load_row_batch<FMT, EPI>(bufB, set, meta0, values0, min(rowB, R - 1), KW, w0, nws, biB * kWave, lane);  // batch t+1
         // keep the walk (which waits for batch A) after the issue of these loads
         __builtin_amdgcn_sched_barrier(0);
         walk_batch<FMT, B>(bufA, xs, nws, acc);  // batch t
@@ -291,7 +318,7 @@ __global__ __launch_bounds__(NT, NT == 1024 ? 8 : 1) void spmv_kernel(const Spmv
         rowA = rowB;
         biA = biB;
         step(rowA, biA);
-        load_row_batch<FMT, EPI>(bufA, set, min(rowA, R - 1), KW, w0, t + 2 < total ? nws : 0, biA * kWave, lane);
+        load_row_batch<FMT, EPI>(bufA, set, meta0, values0, min(rowA, R - 1), KW, w0, t + 2 < total ? nws : 0, biA * kWave, lane);
         __builtin_amdgcn_sched_barrier(0);
         walk_batch<FMT, B>(bufB, xs, nws, acc);  // batch t+1
         if (biB == nb - 1) finish_row<B, EPI>(acc, gsave, set, rowB, split, s, R, lane, partial);
@@ -361,8 +388,9 @@ hipError_t launch_fbn(const MvPlan &p, const SpmvSet &set, int64_t K, const uint
     if (e != hipSuccess) return e;
     SpmvSet padded = set;
     for (int q = set.P + 1; q <= kMaxMats; ++q) padded.row0[q] = set.row0[set.P];
-    hipLaunchKernelGGL((spmv_kernel<FMT, B, NT, EPI>), dim3(p.grid_x, p.splits), dim3(NT), p.lds_bytes, st, padded,
-                       (int)(K / 32), x, ldx, ws, p.slice);
+    hipLaunchKernelGGL((spmv_kernel<FMT, B, NT, EPI>), dim3(p.grid_x, p.splits), dim3(NT), p.lds_bytes, st,
+                       set.meta[0], set.values[0], set.row0[set.P], (int)(K / 32), p.grid_x, p.splits > 1 ? 1 : 0, x,
+                       ldx, p.slice, ws, padded);
     e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;
     const int R = set.row0[set.P];
@@ -403,6 +431,7 @@ hipError_t launch_f(const MvPlan &p, const SpmvSet &set, int64_t K, const uint16
 }  // namespace
 
 size_t spmv_lds_per_word(int B) { return (size_t)blk_dwords(B) * 4; }
+
 
 MvPlan plan_spmv(int64_t R, int64_t K, int B, const DeviceInfo &dev, int fmt) {
     MvPlan p;
@@ -466,9 +495,15 @@ MvPlan plan_spmv(int64_t R, int64_t K, int B, const DeviceInfo &dev, int fmt) {
 hipError_t launch_spmv(const MvPlan &p, const SpmvSet &set, int fmt, int64_t K, const uint16_t *x, int64_t ldx, int B,
                        float *ws, hipStream_t st) {
     switch (fmt) {
-    case kMetaBitmask: return launch_f<kMetaBitmask, kEpiNone>(p, set, K, x, ldx, B, ws, st);
-    case kMetaU8: return launch_f<kMetaU8, kEpiNone>(p, set, K, x, ldx, B, ws, st);
-    case kMetaI32: return launch_f<kMetaI32, kEpiNone>(p, set, K, x, ldx, B, ws, st);
+    case kMetaBitmask:
+        return set.P == 1 ? launch_f<kMetaBitmask, kEpiOne>(p, set, K, x, ldx, B, ws, st)
+                          : launch_f<kMetaBitmask, kEpiNone>(p, set, K, x, ldx, B, ws, st);
+    case kMetaU8:
+        return set.P == 1 ? launch_f<kMetaU8, kEpiOne>(p, set, K, x, ldx, B, ws, st)
+                          : launch_f<kMetaU8, kEpiNone>(p, set, K, x, ldx, B, ws, st);
+    case kMetaI32:
+        return set.P == 1 ? launch_f<kMetaI32, kEpiOne>(p, set, K, x, ldx, B, ws, st)
+                          : launch_f<kMetaI32, kEpiNone>(p, set, K, x, ldx, B, ws, st);
     default: return hipErrorInvalidValue;
     }
 }

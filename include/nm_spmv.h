@@ -177,6 +177,32 @@ nm_status nm_spmv_swiglu(const uint32_t *gate_masks, const nm_bf16 *gate_values,
                          const nm_bf16 *up_values, int64_t R, int64_t K, const nm_bf16 *x, int64_t ldx, int B,
                          nm_bf16 *h, int64_t ldh, void *workspace, size_t workspace_bytes, void *hip_stream);
 
+/*
+ * nm_spmv_plan / nm_spmv_multi_plan -- the launch plan that nm_spmv (epilogue
+ * NM_EPI_NONE, R rows) or nm_spmv_swiglu (NM_EPI_SWIGLU, R rows of gate and of up)
+ * would use on the current device, or nm_spmv_multi for P matrices of rows[0..P-1]
+ * rows, with a contiguous x (ldx = K).  A test and tuning aid: host only, launches
+ * nothing, and the same planner as the compute calls, so a test can check which kernel
+ * instance a shape reaches.  With no visible device the planner assumes 256 compute
+ * units and 160 KiB of LDS per workgroup.  Returns NM_ERR_NULL for a NULL plan (or
+ * rows), NM_ERR_SHAPE / NM_ERR_PATTERN for sizes or an epilogue the compute call would
+ * reject; *plan is written only on NM_OK.
+ */
+typedef enum { NM_EPI_NONE = 0, NM_EPI_SWIGLU = 1 } nm_epilogue;
+typedef enum { NM_KERNEL_WORD = 0, NM_KERNEL_TILE = 1 } nm_kernel_kind;
+typedef struct {
+    int kernel;             /* nm_kernel_kind: word-per-lane walk, or the matrix-core tile walk */
+    int threads;            /* workgroup size */
+    int grid_x;             /* workgroups per row slice (word) / resident workgroups (tile) */
+    int splits;             /* row slices; > 1: fp32 partial sums and an ordered second pass */
+    int tiles_per_step;     /* tile walk: 16-row tiles sharing one x operand (1 or 2); 0 otherwise */
+    int reserved;
+    size_t lds_bytes;       /* dynamic LDS of the word-per-lane walk per workgroup */
+    size_t workspace_bytes; /* what the compute call requires */
+} nm_launch_plan;
+nm_status nm_spmv_plan(int64_t R, int64_t K, int B, int epilogue, nm_launch_plan *plan);
+nm_status nm_spmv_multi_plan(const int64_t *rows, int P, int64_t K, int B, nm_launch_plan *plan);
+
 /* dense_gemv_swiglu -- the dense baseline of nm_spmv_swiglu: unpruned bf16 gate and up
  * matrices W_gate, W_up [R][ldw], same epilogue and conventions. */
 size_t dense_gemv_swiglu_workspace_bytes(int64_t R, int64_t K, int B);
@@ -321,7 +347,7 @@ nm_status nm_unpack(const uint32_t *masks, const nm_bf16 *values, int64_t R, int
 /*
  * nm_stream_read -- measurement aid, not part of the method: reads `bytes` bytes at `buf`
  * once, with the same 16-byte non-temporal loads and 512-thread workgroups as the
- * matrix-vector kernels, and writes one XOR-fold of the dwords per workgroup to
+ * matrix-vector kernels, and writes one XOR-fold of the dwords per wave to
  * sink[0 .. nm_stream_read_sink_words(bytes)).  Timed under the same rotation of
  * distinct buffers as the SpMV, it gives the rate a kernel that only streams reaches --
  * the achievable figure the SpMV's % of the 8 TB/s peak is read against.  The XOR of all

@@ -270,10 +270,12 @@ def test_stream_read_rejects_bad_arguments(L):
     p, sz = ctypes.c_void_p, ctypes.c_size_t
     L.nm_stream_read_sink_words.argtypes, L.nm_stream_read_sink_words.restype = [sz], sz
     L.nm_stream_read.argtypes, L.nm_stream_read.restype = [p, sz, p, sz, p], ctypes.c_int
-    assert L.nm_stream_read_sink_words(16) == 1
-    assert L.nm_stream_read_sink_words(1 << 31) == 1024  # one fold per workgroup, at most 1024
-    assert L.nm_stream_read_sink_words(512 * 64 * 3) == 3  # at least four 16-byte chunks per thread
-    assert L.nm_stream_read_sink_words(512 * 64 * 3 + 16) == 4
+    # one fold per wave: 8 per 512-thread workgroup, at most 1024 workgroups, and at least
+    # one 2 KiB unit per wave (16 KiB per workgroup)
+    assert L.nm_stream_read_sink_words(16) == 8
+    assert L.nm_stream_read_sink_words(1 << 31) == 1024 * 8
+    assert L.nm_stream_read_sink_words(16384 * 3) == 3 * 8
+    assert L.nm_stream_read_sink_words(16384 * 3 + 16) == 4 * 8
     words = L.nm_stream_read_sink_words(1 << 20)
     assert L.nm_stream_read(None, 1 << 20, A16, words, None) == NM_ERR_NULL
     assert L.nm_stream_read(A16, 1 << 20, None, words, None) == NM_ERR_NULL

@@ -29,14 +29,21 @@ def _assert_h(h_bits, g, ag, u, au, what):
 
 
 SHAPES = [(256, 512), (1000, 4096), (513, 5120), (17, 8192), (3, 28672), (1, 32)]
-# 2R launch rows with an x slice that leaves room for two workgroups per CU at B = 3/4:
-# the 1024-thread workgroup variant of the gated-MLP kernel
-WIDE = [(1500, 8192, 4), (1100, 9216, 3)]
+# Larger launch forms of the gated-MLP kernel, each with the plan it must get (kernel 0
+# word-per-lane / 1 tile, workgroup size): 1024-thread workgroups at B = 1/2 (rows of
+# 8192 columns) and B = 4 (x allows two workgroups per CU), the tile kernel at B = 3 for a
+# row of x beyond the word-per-lane LDS slice.
+WIDE = [(2048, 8192, 1, (0, 1024)), (2048, 8192, 2, (0, 1024)), (1500, 8192, 4, (0, 1024)),
+        (1100, 9216, 3, (1, 512))]
 
 
-@pytest.mark.parametrize("R,K,B", [(R, K, B) for R, K in SHAPES for B in (1, 3, 8)] + WIDE)
+@pytest.mark.parametrize("R,K,B", [(R, K, B) for R, K in SHAPES for B in (1, 3, 8)] + [w[:3] for w in WIDE])
 def test_swiglu_sparse_and_dense(R, K, B):
-    say("swiglu", R, K, B)
+    p = nm.nm_spmv_plan(R, K, B, nm.NM_EPI_SWIGLU)
+    say("swiglu", R, K, B, p)
+    for wr, wk, wb, plan in WIDE:
+        if (wr, wk, wb) == (R, K, B):
+            assert (p["kernel"], p["threads"]) == plan
     n = oracle.col_norm(synth.calib_acts(K, 8, R, K))
     Wg, Wu = synth.weights(R, K, 8, 1, R, K), synth.weights(R, K, 8, 2, R, K)
     gm, gv = oracle.prune_pack(Wg, n, 4, 8)
@@ -74,28 +81,3 @@ def test_swiglu_large_gate_values_and_zero_up():
     assert (hf[32:] == 0).all()
     assert (hf[0:32:2] == 64.0 * 4.0).all()  # silu(64) = 64 in fp32, u = 4
     assert (np.abs(hf[1:32:2]) < 1e-20).all()
-
-
-def test_swiglu_full_size_sampled():
-    """Llama-3.1-8B MLP shape: gate and up 14336 x 4096, 2:4, generated and packed on the device."""
-    R, K, B = 14336, 4096, 1
-    say("swiglu full", R, K)
-    Xd = synth.device_calib_acts(K, 4, K)
-    n = nm.nm_col_norm(Xd)
-    Wg, Wu = synth.device_weights(R, K, 4, 1), synth.device_weights(R, K, 4, 2)
-    gate, up = nm.nm_prune_pack(Wg, n, 2, 4), nm.nm_prune_pack(Wu, n, 2, 4)
-    xd = synth.device_decode_x(B, K, 4, K)
-    h = nm.nm_spmv_swiglu(gate, up, xd)
-    hd = nm.dense_gemv_swiglu(Wg, Wu, xd)
-    torch.cuda.synchronize()
-    rows = np.unique(np.concatenate([[0, R - 1], np.random.default_rng(3).choice(R, 160, replace=False)]))
-    ridx = torch.from_numpy(rows).cuda()
-    xh = host_bf16(xd)
-    gs = (host_u32(gate[0].index_select(0, ridx)), host_bf16(gate[1].index_select(0, ridx)))
-    us = (host_u32(up[0].index_select(0, ridx)), host_bf16(up[1].index_select(0, ridx)))
-    g, ag = oracle.spmv(*gs, xh, K, nthreads=4)
-    u, au = oracle.spmv(*us, xh, K, nthreads=4)
-    _assert_h(host_bf16(h)[:, rows], g, ag, u, au, "sparse 8b mlp")
-    g, ag = oracle.dense(host_bf16(Wg.index_select(0, ridx)), xh, nthreads=4)
-    u, au = oracle.dense(host_bf16(Wu.index_select(0, ridx)), xh, nthreads=4)
-    _assert_h(host_bf16(hd)[:, rows], g, ag, u, au, "dense 8b mlp")
