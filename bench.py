@@ -2,26 +2,35 @@
 """Decode-step benchmark of the N:M bitmask SpMV against the same-GPU dense bf16 GEMV.
 
 A step is one decode token (batch B, default 1) through a stack of synthetic decoder
-layers -- every projection of every layer is one nm_spmv call on its own packed
+layers -- every projection of every layer is one pruned linear on its own packed
 weights -- for each N:M pattern of the workload.  The dense baseline runs the same
 stack with dense_gemv on the unpruned weights.  Inputs are generated and packed on
 the GPU before the timed region (column norms -> N:M select + pack), spot-checked
 against the CPU oracle, and every timed launch reads weights already resident in HBM.
 
-The headline step runs the projections that read the same x as one launch each --
-q|k|v through nm_spmv_multi, gate|up through nm_spmv_swiglu (silu(g) * u written by the
-epilogue), o and down alone -- against the same grouping of dense launches; the step
-with one nm_spmv call per projection is reported beside it.
+The headline (value, roofline) is the Llama-3.1-8B layer set at B = 1 with 2:4 and 16:32:
+the projections that read the same x run as one launch each -- q|k|v through
+nm_spmv_multi, gate|up through nm_spmv_swiglu (silu(g) * u written by the epilogue), o
+and down alone -- against the same grouping of dense launches; the step with one
+nm_spmv call per projection is reported beside it.
+
+Beside it, in the same JSON line (`configs`), the other workloads: the 8B set swept over
+the four 50% patterns with 32 decoder layers of distinct buffers, Qwen3-14B/32B layers
+at 4:8, and Llama-3.3-70B layers at 8:16 with 1, 2, 4 and 8 tokens.
+
+Per-layer timing (every projection and every fused launch): one HIP graph of whole
+passes over a pool of distinct buffers (>= 512 MB, twice the 256 MB Infinity Cache, and
+at least 64 launches), replayed 10 times untimed (>= 50 warmup launches), then 50 timed
+replays; the per-launch time of each replay gives the median and its p10/p90 (the
+pages' protocol times the median of 50 iterations after 50 warmup ones).
 
 Printed (one JSON line on stdout): effective GB/s of the step (algorithmic bytes:
-packed values + masks of every matrix, x once per launch, the launch's outputs), a
-per-projection and per-fused-launch table (us, GB/s, % of the 8 TB/s HBM peak, dense
-us, speedup, hipBLASLt us), the bitmask / uint8-offset / int32-index comparison, the
-roofline of the step's dominant launch and the CPU oracle timed on the host cores.
-
-Cache defeat: every per-projection timing rotates over >= 512 MB of distinct buffers
-(twice the 256 MB Infinity Cache), and the step itself walks all layers of all
-patterns in decode order (several GB between reuses).
+packed values + masks of every matrix, x once per launch, the launch's outputs), the
+per-layer tables (us with p10/p90, GB/s, % of the 8 TB/s HBM peak, dense us, speedup,
+hipBLASLt us, the achievable streaming read of the same bytes), the per-layer check
+against >= 70 % of peak and >= 1.5x dense, the bitmask / uint8-offset / int32-index
+comparison, the roofline of the step's dominant launch and the CPU oracle timed on the
+host cores.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config 8b] [--layers 8]
 """
@@ -42,11 +51,12 @@ HBM_PEAK_GBS = 8000.0
 FP64_MFMA_PEAK_TFLOPS = 78.6
 ROTATE_BYTES = 512e6
 # Launches per timed graph: a rotation pool is cycled (buffer i % pool) in whole passes
-# up to at least this many launches, so the cost of starting a graph replay is spread
-# over as many dispatches as the pages' protocol times (50), and every buffer -- also
-# across back-to-back replays -- is re-read only after the whole pool (>= 512 MB).
+# up to at least this many launches, and every buffer -- also across back-to-back
+# replays -- is re-read only after the whole pool (>= 512 MB) has been.
 TIMED_LAUNCHES = 64
-TIMED_REPLAYS = 5
+WARM_REPLAYS = 10
+TIMED_REPLAYS = 50
+TARGET_PCT, TARGET_SPEEDUP = 70.0, 1.5
 METRIC = "nm_spmv GB/s and % HBM peak per layer; speedup vs dense bf16 GEMV, batch 1"
 
 # Layer shapes (rows R = outputs, K = inputs) of the models the pages evaluate.
@@ -72,6 +82,9 @@ CONFIGS = {
                        ("o", 8192, 8192, "attn_out"), ("gate", 28672, 8192, "mlp"), ("up", 28672, 8192, "mlp"),
                        ("down", 8192, 28672, "mlp_mid")], patterns=[(8, 16)], batch=(1, 2, 4, 8)),
 }
+# The other workloads measured beside the headline in the default run: (config, decoder
+# layers in the step, batch sizes).
+OTHER_CONFIGS = [("8b-sweep", 32, (1,)), ("qwen14b", 4, (1,)), ("qwen32b", 4, (1,)), ("70b", 4, (1, 2, 4, 8))]
 
 
 def log(*a):
@@ -100,16 +113,33 @@ def is_glu(grp):
 
 
 def group_label(grp):
-    return "|".join(pr[0] for pr in grp) + ("+swiglu" if is_glu(grp) else "")
+    return grp[0][0] if len(grp) == 1 else "|".join(pr[0] for pr in grp) + ("+swiglu" if is_glu(grp) else "")
 
 
 def group_bytes(grp, B, dense):
-    """Algorithmic bytes of one fused launch: every matrix of the group once, x once, and
+    """Algorithmic bytes of one (fused) launch: every matrix of the group once, x once, and
     the outputs (one h of R rows for the gated MLP, else every matrix's y)."""
     K = grp[0][2]
     w = sum((2 if dense else 1.125) * R * K for _, R, _, _ in grp)
     outs = grp[0][1] if is_glu(grp) else sum(R for _, R, _, _ in grp)
     return int(w) + 2 * B * K + 2 * B * outs
+
+
+def layer_groups(projs):
+    """Projections in layer order, consecutive ones that share x grouped into one launch."""
+    groups = []
+    for proj in projs:
+        if groups and groups[-1][0][3] == proj[3]:
+            groups[-1].append(proj)
+        else:
+            groups.append([proj])
+    return groups
+
+
+def pctl(v, q):
+    """Nearest-rank percentile."""
+    s = sorted(v)
+    return s[min(len(s) - 1, max(0, int(math.ceil(q / 100 * len(s))) - 1))]
 
 
 def parse():
@@ -131,6 +161,8 @@ def parse():
     ap.add_argument("--solver-tokens", type=int, default=4096, help="calibration tokens for the solver")
     ap.add_argument("--no-unstructured", action="store_true",
                     help="skip the 50%% unstructured vs N:M comparison table")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="measure only the headline workload (skip the 8B pattern sweep, Qwen3 and 70B sets)")
     ap.add_argument("--profile-proj", default=None,
                     help="with --profile-kernel: launch this projection alone through nm_spmv (e.g. gate) "
                          "instead of the dominant launch")
@@ -144,35 +176,6 @@ def parse():
                     help="host-only: print a per-kernel / per-launch-shape summary of a rocprofv3 "
                          "--kernel-trace --stats run")
     return ap.parse_args()
-
-
-class Timer:
-    """HIP events on the current stream."""
-
-    def __init__(self, torch):
-        self.torch = torch
-
-    def time_graph(self, g, reps):
-        t = self.torch
-        e0, e1 = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            g.replay()
-        e1.record()
-        t.cuda.synchronize()
-        return e0.elapsed_time(e1) / reps  # ms per replay
-
-
-def time_launches(torch, timer, fns):
-    """Average µs per launch of a rotation: one graph of whole passes over the pool's
-    launches (at least TIMED_LAUNCHES), replayed once untimed, then the median of
-    TIMED_REPLAYS event-timed replays."""
-    n = -(-TIMED_LAUNCHES // len(fns)) * len(fns)
-    g = capture(torch, [fns[i % len(fns)] for i in range(n)])
-    g.replay()
-    t = sorted(timer.time_graph(g, 1) for _ in range(TIMED_REPLAYS))
-    del g
-    return t[len(t) // 2] * 1e3 / n
 
 
 def capture(torch, fns):
@@ -192,6 +195,295 @@ def capture(torch, fns):
     return g
 
 
+def time_graph(torch, g, reps):
+    """Average ms per replay over `reps` back-to-back replays (HIP events on the stream the
+    graph replays on)."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def time_launches(torch, fns):
+    """Per-launch µs of a rotation: one graph of whole passes over the pool's launches (at
+    least TIMED_LAUNCHES), WARM_REPLAYS untimed replays, then TIMED_REPLAYS replays timed one
+    by one; returns the median and p10/p90 of the per-launch time of a replay."""
+    n = -(-TIMED_LAUNCHES // len(fns)) * len(fns)
+    g = capture(torch, [fns[i % len(fns)] for i in range(n)])
+    for _ in range(WARM_REPLAYS):
+        g.replay()
+    e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(TIMED_REPLAYS)]
+    for e0, e1 in e:
+        e0.record()
+        g.replay()
+        e1.record()
+    torch.cuda.synchronize()
+    t = [e0.elapsed_time(e1) * 1e3 / n for e0, e1 in e]
+    del g
+    return {"us": round(pctl(t, 50), 3), "p10": round(pctl(t, 10), 3), "p90": round(pctl(t, 90), 3),
+            "launches": n * TIMED_REPLAYS}
+
+
+def rate(nbytes, t):
+    """GB/s and % of the HBM peak of nbytes per t['us']."""
+    gbs = nbytes / t["us"] / 1e3
+    return {"GBs": round(gbs, 1), "pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1)}
+
+
+class Ctx:
+    """Device, library handles and one shared workspace (grown on demand)."""
+
+    def __init__(self, args):
+        import numpy as np
+        import torch
+
+        import bitmask_spmv_amd as nm
+        import synth
+
+        self.np, self.torch, self.nm, self.synth, self.args = np, torch, nm, synth, args
+        self.dev = torch.device("cuda", 0)
+        self.ws = torch.empty(1, dtype=torch.float32, device=self.dev)
+
+    def workspace(self, projs, B):
+        nm = self.nm
+        need = max([nm.nm_spmv_workspace_bytes(R, K, B) for _, R, K, _ in projs]
+                   + [nm.dense_gemv_workspace_bytes(R, K, B) for _, R, K, _ in projs]
+                   + [nm.nm_spmv_swiglu_workspace_bytes(R, K, B) for _, R, K, _ in projs]
+                   + [nm.dense_gemv_swiglu_workspace_bytes(R, K, B) for _, R, K, _ in projs]
+                   + [nm.nm_spmv_multi_workspace_bytes([R] * 3, K, B) for _, R, K, _ in projs]
+                   + [nm.dense_gemv_multi_workspace_bytes([R] * 3, K, B) for _, R, K, _ in projs]
+                   + [nm.nm_spmv_unstructured_workspace_bytes(R, K, B) for _, R, K, _ in projs] + [4])
+        if self.ws.numel() * 4 < need:
+            self.ws = self.torch.empty((need + 3) // 4, dtype=self.torch.float32, device=self.dev)
+        return self.ws
+
+
+def build_pools(c, projs, patterns, L, seed, with_dense=True):
+    """Per projection a pool of distinct packed buffers of >= 512 MB (and >= L) per pattern,
+    and the same for the dense weights; the step uses the first L of each pool as its L
+    decoder layers.  Returns (pool_sparse, pool_dense, stats)."""
+    torch, nm, synth = c.torch, c.nm, c.synth
+    pool_sparse, pool_dense = {}, {}
+    pack_ms = norm_ms = 0.0
+    pack_bytes = 0
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for pi, (name, R, K, group) in enumerate(projs):
+        ns = max(L, math.ceil(ROTATE_BYTES / sparse_bytes(R, K, 1)))
+        nd = max(L, math.ceil(ROTATE_BYTES / dense_bytes(R, K, 1))) if with_dense else 0
+        for (N, M) in patterns:
+            pool_sparse[(N, M), name] = []
+        pool_dense[name] = []
+        for i in range(max(ns, nd)):
+            W = synth.device_weights(R, K, seed, 100 + pi, i)
+            X = synth.device_calib_acts(K, seed, 200 + pi, i)
+            ev0.record()
+            n = nm.nm_col_norm(X)
+            ev1.record()
+            torch.cuda.synchronize()
+            norm_ms += ev0.elapsed_time(ev1)
+            for (N, M) in patterns:
+                if i < ns:
+                    ev0.record()
+                    pk = nm.nm_prune_pack(W, n, N, M)
+                    ev1.record()
+                    torch.cuda.synchronize()
+                    pack_ms += ev0.elapsed_time(ev1)
+                    pack_bytes += 2 * R * K + sparse_bytes(R, K, 0)
+                    pool_sparse[(N, M), name].append(pk)
+            if i < nd:
+                pool_dense[name].append(W)
+            del X, n, W
+    return pool_sparse, pool_dense, {"pack_ms": pack_ms, "pack_bytes": pack_bytes, "norm_ms": norm_ms}
+
+
+def make_inputs(c, projs, B, L, seed):
+    """L decode inputs per activation group (one per decoder layer) and one output per
+    projection."""
+    synth, torch = c.synth, c.torch
+    xs = {}
+    for gi, group in enumerate(sorted({p[3] for p in projs})):
+        K = [p[2] for p in projs if p[3] == group][0]
+        xs[group] = [synth.device_decode_x(B, K, seed, 300 + gi, B, l) for l in range(L)]
+    ys = {name: torch.empty((B, R), dtype=torch.bfloat16, device=c.dev) for name, R, K, _ in projs}
+    return xs, ys
+
+
+def spot_check(c, projs, patterns, pool_sparse, pool_dense, xs, seed):
+    """Column norms, masks and values bit-exact and spmv / dense within tolerance on a
+    sample of rows of layer 0 of every projection, against the CPU oracle."""
+    import oracle
+
+    np, torch, nm, synth = c.np, c.torch, c.nm, c.synth
+
+    def host_u16(t):
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+    g = np.random.default_rng(seed)
+    for pi, (name, R, K, group) in enumerate(projs):
+        rows = np.unique(np.concatenate([[0, R - 1], g.choice(R, size=min(R, 6), replace=False)]))
+        ridx = torch.from_numpy(rows).to(c.dev)
+        X = synth.device_calib_acts(K, seed, 200 + pi, 0)
+        nref = oracle.col_norm(host_u16(X))
+        assert (nm.nm_col_norm(X).cpu().numpy().view(np.uint32) == nref.view(np.uint32)).all(), "col_norm"
+        W = pool_dense[name][0] if pool_dense.get(name) else synth.device_weights(R, K, seed, 100 + pi, 0)
+        Ws = host_u16(W.index_select(0, ridx))
+        x = xs[group][0]
+        xh = host_u16(x)
+        for (N, M) in patterns:
+            masks, values = pool_sparse[(N, M), name][0]
+            mref, vref = oracle.prune_pack(Ws, nref, N, M)
+            assert (masks.index_select(0, ridx).cpu().numpy().view(np.uint32) == mref).all(), f"masks {name}"
+            assert (host_u16(values.index_select(0, ridx)) == vref).all(), f"values {name}"
+            y = nm.nm_spmv(masks, values, x, workspace=c.ws)
+            yref, absum = oracle.spmv(mref, vref, xh, K)
+            yg = (host_u16(y)[:, rows].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+            assert oracle.within_tolerance(yg, yref, absum).all(), f"spmv {name} {N}:{M}"
+        yd = nm.dense_gemv(W, x, workspace=c.ws)
+        ydref, dabs = oracle.dense(Ws, xh)
+        ydg = (host_u16(yd)[:, rows].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        assert oracle.within_tolerance(ydg, ydref, dabs).all(), f"dense {name}"
+
+
+def group_call(c, grp, pk, x, ys, dense=False):
+    """One launch of a group: nm_spmv / nm_spmv_multi / nm_spmv_swiglu (pk: packs), or the
+    dense counterparts (pk: weights)."""
+    nm, ws = c.nm, c.ws
+    if dense:
+        if len(grp) == 1:
+            return lambda: nm.dense_gemv(pk[0], x, out=ys[grp[0][0]], workspace=ws)
+        if is_glu(grp):
+            return lambda: nm.dense_gemv_swiglu(pk[0], pk[1], x, out=ys["gate"], workspace=ws)
+        outs = [ys[pr[0]] for pr in grp]
+        return lambda: nm.dense_gemv_multi(pk, x, outs=outs, workspace=ws)
+    if len(grp) == 1:
+        m, v = pk[0]
+        return lambda: nm.nm_spmv(m, v, x, out=ys[grp[0][0]], workspace=ws)
+    if is_glu(grp):
+        return lambda: nm.nm_spmv_swiglu(pk[0], pk[1], x, out=ys["gate"], workspace=ws)
+    outs = [ys[pr[0]] for pr in grp]
+    return lambda: nm.nm_spmv_multi(pk, x, outs=outs, workspace=ws)
+
+
+def step_graphs(c, projs, patterns, pool_sparse, pool_dense, xs, ys, L, B):
+    """The fused decode step: L decoder layers of every pattern in decode order, each layer
+    its groups as one launch each; the dense step runs the same grouping once."""
+    groups = layer_groups(projs)
+    sparse, dense = [], []
+    for (N, M) in patterns:
+        for l in range(L):
+            for grp in groups:
+                sparse.append(group_call(c, grp, [pool_sparse[(N, M), pr[0]][l] for pr in grp], xs[grp[0][3]][l], ys))
+    for l in range(L):
+        for grp in groups:
+            dense.append(group_call(c, grp, [pool_dense[pr[0]][l] for pr in grp], xs[grp[0][3]][l], ys, dense=True))
+    sb = L * len(patterns) * sum(group_bytes(grp, B, False) for grp in groups)
+    db = L * sum(group_bytes(grp, B, True) for grp in groups)
+    return sparse, dense, sb, db
+
+
+def time_step(c, fns, steps, warmup):
+    g = capture(c.torch, fns)
+    for _ in range(warmup):
+        g.replay()
+    c.torch.cuda.synchronize()
+    ms = time_graph(c.torch, g, steps)
+    del g
+    return ms
+
+
+def per_layer_table(c, projs, patterns, pool_sparse, pool_dense, xs, ys, L, B, hipblaslt=False):
+    """Every projection and every fused group timed alone over its rotation pool: sparse per
+    pattern, dense, speedup (and hipBLASLt's torch.nn.functional.linear for single
+    projections when asked)."""
+    torch = c.torch
+    per = {}
+    for grp in [[p] for p in projs] + [grp for grp in layer_groups(projs) if len(grp) > 1]:
+        label = group_label(grp)
+        K = grp[0][2]
+        d = per.setdefault(label, {"R": grp[0][1] if len(grp) == 1 else [pr[1] for pr in grp], "K": K})
+        nb, ndb = group_bytes(grp, B, False), group_bytes(grp, B, True)
+        for (N, M) in patterns:
+            n_rot = min(len(pool_sparse[(N, M), pr[0]]) for pr in grp)
+            fns = [group_call(c, grp, [pool_sparse[(N, M), pr[0]][i] for pr in grp], xs[grp[0][3]][i % L], ys)
+                   for i in range(n_rot)]
+            t = time_launches(torch, fns)
+            d[f"{N}:{M}"] = dict(t, **rate(nb, t), rotation_MB=round(n_rot * nb / 1e6))
+        if pool_dense.get(grp[0][0]):
+            n_rot = min(len(pool_dense[pr[0]]) for pr in grp)
+            fns = [group_call(c, grp, [pool_dense[pr[0]][i] for pr in grp], xs[grp[0][3]][i % L], ys, dense=True)
+                   for i in range(n_rot)]
+            t = time_launches(torch, fns)
+            d["dense_us"], d["dense_p10"], d["dense_p90"] = t["us"], t["p10"], t["p90"]
+            d["dense_GBs"] = rate(ndb, t)["GBs"]
+            for (N, M) in patterns:
+                d[f"{N}:{M}"]["speedup_vs_dense"] = round(t["us"] / d[f"{N}:{M}"]["us"], 3)
+            if hipblaslt and len(grp) == 1:
+                lin = [(lambda W=pool_dense[grp[0][0]][i], x=xs[grp[0][3]][i % L]: torch.nn.functional.linear(x, W))
+                       for i in range(n_rot)]
+                tl = time_launches(torch, lin)
+                d["hipblaslt_us"] = tl["us"]
+                for (N, M) in patterns:
+                    d[f"{N}:{M}"]["speedup_vs_hipblaslt"] = round(tl["us"] / d[f"{N}:{M}"]["us"], 3)
+        torch.cuda.synchronize()
+    return per
+
+
+def target_check(per, patterns):
+    """Each launch of the table against the per-layer target: >= 70 % of the HBM peak and
+    >= 1.5x the same-GPU dense GEMV; with the achievable streaming read of its bytes."""
+    out = {}
+    for label, d in per.items():
+        for (N, M) in patterns:
+            e = d.get(f"{N}:{M}")
+            if not e or "speedup_vs_dense" not in e:
+                continue
+            row = {"pct_peak": e["pct_peak"], "speedup_vs_dense": e["speedup_vs_dense"],
+                   "pct_ok": e["pct_peak"] >= TARGET_PCT, "speedup_ok": e["speedup_vs_dense"] >= TARGET_SPEEDUP}
+            if "stream_read" in d:
+                row["stream_read_pct_peak"] = d["stream_read"]["pct_peak"]
+            out[f"{label} {N}:{M}"] = row
+    return out
+
+
+def measure_other(c, name, L, batches, steps, warmup, seed, check):
+    """One of the other workloads: per-layer table and fused step for each batch size."""
+    torch = c.torch
+    cfg = dict(CONFIGS[name])
+    projs = cfg.get("projs") or CONFIGS[cfg["base"]]["projs"]
+    patterns = cfg["patterns"]
+    t0 = time.time()
+    pool_sparse, pool_dense, _ = build_pools(c, projs, patterns, L, seed + 17)
+    out = {"workload": cfg["workload"], "layers": L, "patterns": [f"{N}:{M}" for N, M in patterns], "by_batch": {}}
+    for B in batches:
+        xs, ys = make_inputs(c, projs, B, L, seed + 17)
+        c.workspace(projs, B)
+        if check and B == batches[0]:
+            spot_check(c, projs, patterns, pool_sparse, pool_dense, xs, seed + 17)
+        sparse, dense, sb, db = step_graphs(c, projs, patterns, pool_sparse, pool_dense, xs, ys, L, B)
+        ms = time_step(c, sparse, steps, warmup)
+        msd = time_step(c, dense, steps, warmup)
+        per = per_layer_table(c, projs, patterns, pool_sparse, pool_dense, xs, ys, L, B)
+        gbs = sb / (ms * 1e-3) / 1e9
+        out["by_batch"][f"B{B}"] = {
+            "step": {"launches": len(sparse), "ms": round(ms, 4), "GBs": round(gbs, 1),
+                     "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1), "dense_ms": round(msd, 4),
+                     "speedup_vs_dense": round(msd * len(patterns) / ms, 3)},
+            "per_layer": per}
+        log(f"{name} B={B}: step {ms * 1e3:.1f} us ({100 * gbs / HBM_PEAK_GBS:.1f}% of peak, "
+            f"{msd * len(patterns) / ms:.2f}x dense); " + ", ".join(
+                f"{k} {v[p]['us']} us ({v[p]['pct_peak']}%)" for k, v in per.items()
+                for p in [f"{N}:{M}" for N, M in patterns[:1]]))
+        del xs, ys, sparse, dense
+    del pool_sparse, pool_dense
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    out["seconds"] = round(time.time() - t0, 1)
+    return out
+
+
 def main():
     args = parse()
     if args.ingest_pmc:
@@ -203,15 +495,12 @@ def main():
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
-
-    import bitmask_spmv_amd as nm
-    import synth
 
     assert torch.cuda.is_available(), "bench.py needs a HIP GPU"
     torch.cuda.set_device(0)
-    dev = torch.device("cuda", 0)
+    c = Ctx(args)
+    np, nm, synth = c.np, c.nm, c.synth
     cfg = dict(CONFIGS[args.config])
     if cfg.get("projs") is None:
         cfg["projs"] = CONFIGS[cfg["base"]]["projs"]
@@ -221,271 +510,83 @@ def main():
     props = torch.cuda.get_device_properties(0)
     log(f"device {props.name} CUs={props.multi_processor_count} config={args.config} layers={L} B={B}")
     if args.profile_kernel:
-        return profile_kernel(args, torch, nm, synth, cfg, dev)
+        return profile_kernel(args, torch, nm, synth, cfg, c.dev)
 
     # ---------------------------------------------------------------- inputs
-    # Per projection a pool of distinct weight buffers of >= 512 MB (and >= L); the
-    # step uses the first L of each pool as the L decoder layers.
     t0 = time.time()
-    pool_sparse = {}  # (pattern, proj) -> list of (masks, values)
-    pool_dense = {}   # proj -> list of W
-    pack_ms = 0.0
-    pack_bytes = 0
-    norm_ms = 0.0
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    for pi, (name, R, K, group) in enumerate(projs):
-        ns = max(L, math.ceil(ROTATE_BYTES / sparse_bytes(R, K, B)))
-        nd = max(L, math.ceil(ROTATE_BYTES / dense_bytes(R, K, B)))
-        for (N, M) in patterns:
-            pool_sparse[(N, M), name] = []
-        pool_dense[name] = []
-        for c in range(max(ns, nd)):
-            W = synth.device_weights(R, K, args.seed, 100 + pi, c)
-            X = synth.device_calib_acts(K, args.seed, 200 + pi, c)
-            ev0.record()
-            n = nm.nm_col_norm(X)
-            ev1.record()
-            torch.cuda.synchronize()
-            norm_ms += ev0.elapsed_time(ev1)
-            for (N, M) in patterns:
-                if c < ns:
-                    ev0.record()
-                    pk = nm.nm_prune_pack(W, n, N, M)
-                    ev1.record()
-                    torch.cuda.synchronize()
-                    pack_ms += ev0.elapsed_time(ev1)
-                    pack_bytes += 2 * R * K + sparse_bytes(R, K, 0)
-                    pool_sparse[(N, M), name].append(pk)
-            if c < nd:
-                pool_dense[name].append(W)
-            del X, n
-    xs = {}
-    for gi, group in enumerate(sorted({p[3] for p in projs})):
-        K = [p[2] for p in projs if p[3] == group][0]
-        xs[group] = [synth.device_decode_x(B, K, args.seed, 300 + gi, l) for l in range(L)]
-    ys = {name: torch.empty((B, R), dtype=torch.bfloat16, device=dev) for name, R, K, _ in projs}
-    ws_bytes = max([nm.nm_spmv_workspace_bytes(R, K, B) for _, R, K, _ in projs]
-                   + [nm.dense_gemv_workspace_bytes(R, K, B) for _, R, K, _ in projs]
-                   + [nm.nm_spmv_swiglu_workspace_bytes(R, K, B) for _, R, K, _ in projs]
-                   + [nm.dense_gemv_swiglu_workspace_bytes(R, K, B) for _, R, K, _ in projs]
-                   + [nm.nm_spmv_multi_workspace_bytes([R] * 3, K, B) for _, R, K, _ in projs]
-                   + [nm.dense_gemv_multi_workspace_bytes([R] * 3, K, B) for _, R, K, _ in projs]
-                   + [nm.nm_spmv_unstructured_workspace_bytes(R, K, B) for _, R, K, _ in projs] + [4])
-    ws = torch.empty((ws_bytes + 3) // 4, dtype=torch.float32, device=dev)
+    pool_sparse, pool_dense, st = build_pools(c, projs, patterns, L, args.seed)
+    xs, ys = make_inputs(c, projs, B, L, args.seed)
+    ws = c.workspace(projs, B)
     torch.cuda.synchronize()
     log(f"inputs generated and packed in {time.time() - t0:.1f}s "
-        f"(pack {pack_bytes / pack_ms / 1e6:.0f} GB/s, col_norm {norm_ms:.2f} ms total)")
+        f"(pack {st['pack_bytes'] / st['pack_ms'] / 1e6:.0f} GB/s, col_norm {st['norm_ms']:.2f} ms total)")
 
     # ---------------------------------------------------------------- oracle spot check
     parity = "skipped"
     if not args.skip_check:
-        import oracle
-
-        def host_u16(t):
-            return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
-
-        g = np.random.default_rng(args.seed)
-        for pi, (name, R, K, group) in enumerate(projs):
-            rows = np.unique(np.concatenate([[0, R - 1], g.choice(R, size=min(R, 6), replace=False)]))
-            ridx = torch.from_numpy(rows).to(dev)
-            W = pool_dense[name][0]
-            X = synth.device_calib_acts(K, args.seed, 200 + pi, 0)
-            nref = oracle.col_norm(host_u16(X))
-            assert (nm.nm_col_norm(X).cpu().numpy().view(np.uint32) == nref.view(np.uint32)).all(), "col_norm"
-            Ws = host_u16(W.index_select(0, ridx))
-            x = xs[group][0]
-            xh = host_u16(x)
-            for (N, M) in patterns:
-                masks, values = pool_sparse[(N, M), name][0]
-                mref, vref = oracle.prune_pack(Ws, nref, N, M)
-                assert (masks.index_select(0, ridx).cpu().numpy().view(np.uint32) == mref).all(), f"masks {name}"
-                assert (host_u16(values.index_select(0, ridx)) == vref).all(), f"values {name}"
-                y = nm.nm_spmv(masks, values, x, workspace=ws)
-                yref, absum = oracle.spmv(mref, vref, xh, K)
-                yg = (host_u16(y)[:, rows].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-                assert oracle.within_tolerance(yg, yref, absum).all(), f"spmv {name} {N}:{M}"
-            yd = nm.dense_gemv(W, x, workspace=ws)
-            ydref, dabs = oracle.dense(Ws, xh)
-            ydg = (host_u16(yd)[:, rows].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-            assert oracle.within_tolerance(ydg, ydref, dabs).all(), f"dense {name}"
+        spot_check(c, projs, patterns, pool_sparse, pool_dense, xs, args.seed)
         parity = "ok"
         log("oracle spot check ok (col_norm, masks, values bit-exact; spmv/dense within tolerance)")
 
-    # ---------------------------------------------------------------- step graphs
-    def spmv_call(pk, x, y):
-        m, v = pk
-        return lambda: nm.nm_spmv(m, v, x, out=y, workspace=ws)
-
-    def dense_call(W, x, y):
-        return lambda: nm.dense_gemv(W, x, out=y, workspace=ws)
-
-    sparse_fns, dense_fns = [], []
-    step_sparse_bytes = 0
-    step_dense_bytes = 0
-    for (N, M) in patterns:
-        for l in range(L):
-            for name, R, K, group in projs:
-                sparse_fns.append(spmv_call(pool_sparse[(N, M), name][l], xs[group][l], ys[name]))
-                step_sparse_bytes += sparse_bytes(R, K, B)
-    for l in range(L):
-        for name, R, K, group in projs:
-            dense_fns.append(dense_call(pool_dense[name][l], xs[group][l], ys[name]))
-            step_dense_bytes += dense_bytes(R, K, B)
-    g_sparse = capture(torch, sparse_fns)
-    g_dense = capture(torch, dense_fns)
-    timer = Timer(torch)
-
-    # The same step with projections that read the same x (q|k|v, gate|up) fused into one
-    # launch each (nm_spmv_multi / dense_gemv_multi): x is staged once per group.
-    groups = []  # list of lists of projection tuples, in layer order
-    for proj in projs:
-        if groups and groups[-1][0][3] == proj[3]:
-            groups[-1].append(proj)
-        else:
-            groups.append([proj])
-    fused_fns, fused_dense_fns = [], []
-    fused_sparse_bytes = L * len(patterns) * sum(group_bytes(grp, B, False) for grp in groups)
-    fused_dense_bytes = L * sum(group_bytes(grp, B, True) for grp in groups)
-    for (N, M) in patterns:
-        for l in range(L):
-            for grp in groups:
-                if len(grp) == 1:
-                    name = grp[0][0]
-                    fused_fns.append(spmv_call(pool_sparse[(N, M), name][l], xs[grp[0][3]][l], ys[name]))
-                elif [pr[0] for pr in grp] == ["gate", "up"]:
-                    # gated MLP: h = silu(gate x) * (up x) written by the launch's epilogue
-                    fused_fns.append(lambda g=pool_sparse[(N, M), "gate"][l], u=pool_sparse[(N, M), "up"][l],
-                                     x=xs[grp[0][3]][l]: nm.nm_spmv_swiglu(g, u, x, out=ys["gate"], workspace=ws))
-                else:
-                    pk = [pool_sparse[(N, M), pr[0]][l] for pr in grp]
-                    outs = [ys[pr[0]] for pr in grp]
-                    fused_fns.append(lambda pk=pk, x=xs[grp[0][3]][l], outs=outs:
-                                     nm.nm_spmv_multi(pk, x, outs=outs, workspace=ws))
-    for l in range(L):
-        for grp in groups:
-            if [pr[0] for pr in grp] == ["gate", "up"]:
-                fused_dense_fns.append(lambda g=pool_dense["gate"][l], u=pool_dense["up"][l], x=xs[grp[0][3]][l]:
-                                       nm.dense_gemv_swiglu(g, u, x, out=ys["gate"], workspace=ws))
-                continue
-            Wl = [pool_dense[pr[0]][l] for pr in grp]
-            outs = [ys[pr[0]] for pr in grp]
-            fused_dense_fns.append(lambda Wl=Wl, x=xs[grp[0][3]][l], outs=outs:
-                                   nm.dense_gemv_multi(Wl, x, outs=outs, workspace=ws))
-    g_fused = capture(torch, fused_fns)
-    g_fused_dense = capture(torch, fused_dense_fns)
-
-    for _ in range(args.warmup):
-        g_sparse.replay()
-        g_dense.replay()
-    torch.cuda.synchronize()
-    ms_sparse = timer.time_graph(g_sparse, args.steps)
-    ms_dense = timer.time_graph(g_dense, args.steps)
-    for _ in range(args.warmup):
-        g_fused.replay()
-        g_fused_dense.replay()
-    torch.cuda.synchronize()
-    ms_fused = timer.time_graph(g_fused, args.steps)
-    ms_fused_dense = timer.time_graph(g_fused_dense, args.steps)
+    # ---------------------------------------------------------------- steps
+    groups = layer_groups(projs)
+    fused_fns, fused_dense_fns, fused_sparse_bytes, fused_dense_bytes = step_graphs(
+        c, projs, patterns, pool_sparse, pool_dense, xs, ys, L, B)
+    ms_fused = time_step(c, fused_fns, args.steps, args.warmup)
+    ms_fused_dense = time_step(c, fused_dense_fns, args.steps, args.warmup)
+    # the same step with one nm_spmv call per projection
+    single = [[p] for p in projs]
+    sparse_fns = [group_call(c, grp, [pool_sparse[(N, M), grp[0][0]][l]], xs[grp[0][3]][l], ys)
+                  for (N, M) in patterns for l in range(L) for grp in single]
+    dense_fns = [group_call(c, grp, [pool_dense[grp[0][0]][l]], xs[grp[0][3]][l], ys, dense=True)
+                 for l in range(L) for grp in single]
+    step_sparse_bytes = L * len(patterns) * sum(sparse_bytes(R, K, B) for _, R, K, _ in projs)
+    ms_sparse = time_step(c, sparse_fns, args.steps, args.warmup)
+    ms_dense = time_step(c, dense_fns, args.steps, args.warmup)
     log(f"fused step: sparse {ms_fused * 1e3:.1f} us ({len(fused_fns)} launches), dense "
         f"{ms_fused_dense * 1e3:.1f} us ({len(fused_dense_fns)} launches)")
     log(f"step: sparse {ms_sparse * 1e3:.1f} us ({len(sparse_fns)} launches), dense {ms_dense * 1e3:.1f} us "
         f"({len(dense_fns)} launches, {len(patterns)} pattern(s) share it)")
 
-    # ---------------------------------------------------------------- per projection
-    per = {}
-    for (N, M) in patterns:
-        for name, R, K, group in projs:
-            pool = pool_sparse[(N, M), name]
-            fns = [spmv_call(pk, xs[group][i % L], ys[name]) for i, pk in enumerate(pool)]
-            us = time_launches(torch, timer, fns)
-            per.setdefault(name, {"R": R, "K": K})[f"{N}:{M}"] = {
-                "us": round(us, 2), "GBs": round(sparse_bytes(R, K, B) / us / 1e3, 1),
-                "pct_peak": round(100 * sparse_bytes(R, K, B) / us / 1e3 / HBM_PEAK_GBS, 1),
-                "rotation_MB": round(len(fns) * sparse_bytes(R, K, B) / 1e6)}
-    for name, R, K, group in projs:
-        pool = pool_dense[name]
-        fns = [dense_call(W, xs[group][i % L], ys[name]) for i, W in enumerate(pool)]
-        us = time_launches(torch, timer, fns)
-        lin = [(lambda W=W, x=xs[group][i % L]: torch.nn.functional.linear(x, W)) for i, W in enumerate(pool)]
-        us_lin = time_launches(torch, timer, lin)
-        d = per[name]
-        d["dense_us"] = round(us, 2)
-        d["dense_GBs"] = round(dense_bytes(R, K, B) / us / 1e3, 1)
-        d["hipblaslt_us"] = round(us_lin, 2)
-        for (N, M) in patterns:
-            d[f"{N}:{M}"]["speedup_vs_dense"] = round(us / d[f"{N}:{M}"]["us"], 3)
-            d[f"{N}:{M}"]["speedup_vs_hipblaslt"] = round(us_lin / d[f"{N}:{M}"]["us"], 3)
-    torch.cuda.synchronize()
-
-    # ---------------------------------------------------------------- fused launches
-    # Every group of projections that read the same x as one launch (q|k|v through
-    # nm_spmv_multi, gate|up through nm_spmv_swiglu whose epilogue writes silu(g) * u),
-    # timed over >= 512 MB of distinct buffers like the table above.
-    def fused_call(grp, i, N=None, M=None):
-        x = xs[grp[0][3]][i % L]
-        if N is None:
-            Ws = [pool_dense[pr[0]][i % len(pool_dense[pr[0]])] for pr in grp]
-            if is_glu(grp):
-                return lambda: nm.dense_gemv_swiglu(Ws[0], Ws[1], x, out=ys["gate"], workspace=ws)
-            outs = [ys[pr[0]] for pr in grp]
-            return lambda: nm.dense_gemv_multi(Ws, x, outs=outs, workspace=ws)
-        pk = [pool_sparse[(N, M), pr[0]][i % len(pool_sparse[(N, M), pr[0]])] for pr in grp]
-        if is_glu(grp):
-            return lambda: nm.nm_spmv_swiglu(pk[0], pk[1], x, out=ys["gate"], workspace=ws)
-        outs = [ys[pr[0]] for pr in grp]
-        return lambda: nm.nm_spmv_multi(pk, x, outs=outs, workspace=ws)
-
-    for grp in groups:
-        if len(grp) == 1:
-            continue
-        label = group_label(grp)
-        fb, fdb = group_bytes(grp, B, False), group_bytes(grp, B, True)
-        d = per.setdefault(label, {"R": [pr[1] for pr in grp], "K": grp[0][2]})
-        for (N, M) in patterns:
-            n_rot = min(len(pool_sparse[(N, M), pr[0]]) for pr in grp)
-            us = time_launches(torch, timer, [fused_call(grp, i, N, M) for i in range(n_rot)])
-            d[f"{N}:{M}"] = {"us": round(us, 2), "GBs": round(fb / us / 1e3, 1),
-                             "pct_peak": round(100 * fb / us / 1e3 / HBM_PEAK_GBS, 1),
-                             "rotation_MB": round(n_rot * fb / 1e6)}
-        n_rot = min(len(pool_dense[pr[0]]) for pr in grp)
-        us = time_launches(torch, timer, [fused_call(grp, i) for i in range(n_rot)])
-        d["dense_us"] = round(us, 2)
-        d["dense_GBs"] = round(fdb / us / 1e3, 1)
-        for (N, M) in patterns:
-            d[f"{N}:{M}"]["speedup_vs_dense"] = round(us / d[f"{N}:{M}"]["us"], 3)
-        torch.cuda.synchronize()
-        log(f"{label}: " + ", ".join(f"{k} {v['us']} us ({v['pct_peak']}%)" for k, v in d.items()
-                                     if isinstance(v, dict)) + f"; dense {d['dense_us']} us")
+    # ---------------------------------------------------------------- per layer
+    per = per_layer_table(c, projs, patterns, pool_sparse, pool_dense, xs, ys, L, B, hipblaslt=True)
+    for label, d in per.items():
+        log(f"{label}: " + ", ".join(f"{k} {v['us']} us [{v['p10']}-{v['p90']}] ({v['pct_peak']}%, "
+                                     f"x{v.get('speedup_vs_dense')})" for k, v in d.items()
+                                     if isinstance(v, dict)) + f"; dense {d.get('dense_us')} us")
 
     # ---------------------------------------------------------------- achievable read
     # What a launch that only streams reaches on the same byte count under the same
     # rotation (nm_stream_read over >= 512 MB of distinct buffers of that size): the rate
     # each launch's % of the 8 TB/s peak is read against.
-    stream_us = {}
+    stream_t = {}
 
     def time_stream_read(nbytes):
         nbytes = (int(nbytes) + 15) // 16 * 16
-        if nbytes not in stream_us:
+        if nbytes not in stream_t:
             cnt = max(2, math.ceil(ROTATE_BYTES / nbytes))
-            bufs = [torch.empty(nbytes // 4, dtype=torch.int32, device=dev) for _ in range(cnt)]
-            sink = torch.empty(nm.nm_stream_read_sink_words(nbytes), dtype=torch.int32, device=dev)
-            stream_us[nbytes] = time_launches(torch, timer, [(lambda b=b: nm.nm_stream_read(b, sink=sink))
-                                                             for b in bufs])
+            g = torch.Generator(device=c.dev)
+            g.manual_seed(nbytes)
+            bufs = [torch.randint(-(1 << 31), 1 << 31, (nbytes // 4,), dtype=torch.int32, device=c.dev, generator=g)
+                    for _ in range(cnt)]
+            sink = torch.empty(nm.nm_stream_read_sink_words(nbytes), dtype=torch.int32, device=c.dev)
+            stream_t[nbytes] = time_launches(torch, [(lambda b=b: nm.nm_stream_read(b, sink=sink)) for b in bufs])
             del bufs
-        return nbytes, stream_us[nbytes]
+        return nbytes, stream_t[nbytes]
 
     first_pat = f"{patterns[0][0]}:{patterns[0][1]}"
     stream_log = []
     for grp in [[pr] for pr in projs] + [grp for grp in groups if len(grp) > 1]:
-        label = grp[0][0] if len(grp) == 1 else group_label(grp)
-        nbytes, us = time_stream_read(group_bytes(grp, B, False))
+        label = group_label(grp)
+        nbytes, t = time_stream_read(group_bytes(grp, B, False))
         d = per[label]
-        d["stream_read"] = {"us": round(us, 2), "GBs": round(nbytes / us / 1e3, 1),
-                            "pct_peak": round(100 * nbytes / us / 1e3 / HBM_PEAK_GBS, 1),
-                            "spmv_over_stream_time": round(d[first_pat]["us"] / us, 3)}
-        stream_log.append(f"{label} {round(us, 2)} us ({d['stream_read']['pct_peak']}%)")
+        d["stream_read"] = dict(t, **rate(nbytes, t), spmv_over_stream_time=round(d[first_pat]["us"] / t["us"], 3))
+        stream_log.append(f"{label} {t['us']} us ({d['stream_read']['pct_peak']}%)")
     torch.cuda.synchronize()
     log("stream read of the same bytes (achievable): " + ", ".join(stream_log))
+    check = target_check(per, patterns)
+    log("per-layer target (>= 70% of peak, >= 1.5x dense): " + ", ".join(
+        f"{k} {'pass' if v['pct_ok'] and v['speedup_ok'] else 'FAIL'}" for k, v in check.items()))
 
     # ---------------------------------------------------------------- metadata formats
     # The same product over the first pattern's packs with the metadata as uint8 offsets
@@ -511,17 +612,16 @@ def main():
                     mk0, v0 = pool_sparse[(N, M), name][0]
                     yb = nm.nm_spmv(mk0, v0, xs[group][0], workspace=ws)
                     ym = nm.nm_spmv_meta(pool[0][0], fmt, v0, xs[group][0], workspace=ws)
-                    if B < 5 or K % 1024:
+                    if nm.nm_spmv_plan(R, K, B)["kernel"] == nm.NM_KERNEL_WORD:
                         assert torch.equal(yb.view(torch.int16), ym.view(torch.int16)), f"{key} {name} != bitmask"
                     else:
                         yf, mf = yb.float(), ym.float()
                         assert float((yf - mf).abs().max()) <= 1e-2 * float(yf.abs().max()), f"{key} {name} != bitmask"
                 fns = [(lambda mt=mt, v=v, x=xs[group][i % L]:
                         nm.nm_spmv_meta(mt, fmt, v, x, out=ys[name], workspace=ws)) for i, (mt, v) in enumerate(pool)]
-                us = time_launches(torch, timer, fns)
-                d[key] = {"us": round(us, 2), "GBs": round(nb / us / 1e3, 1), "bytes": nb,
-                          "slowdown_vs_bitmask": round(us / bm["us"], 3),
-                          "rotation_MB": round(len(fns) * nb / 1e6)}
+                t = time_launches(torch, fns)
+                d[key] = dict(t, GBs=rate(nb, t)["GBs"], bytes=nb, slowdown_vs_bitmask=round(t["us"] / bm["us"], 3),
+                              rotation_MB=round(len(fns) * nb / 1e6))
                 del pool, fns
             torch.cuda.synchronize()
         log("metadata formats (us): " + "; ".join(
@@ -542,17 +642,17 @@ def main():
             nb_ = sparse_bytes(R, K, B)
             cnt = max(2, math.ceil(ROTATE_BYTES / nb_))
             pool = []
-            for c in range(cnt):
-                W = synth.device_weights(R, K, args.seed, 100 + pi, c)
-                n = nm.nm_col_norm(synth.device_calib_acts(K, args.seed, 200 + pi, c))
+            for i in range(cnt):
+                W = synth.device_weights(R, K, args.seed, 100 + pi, i)
+                n = nm.nm_col_norm(synth.device_calib_acts(K, args.seed, 200 + pi, i))
                 pool.append(nm.nm_prune_pack_unstructured(W, n))
-                if c == 0:
+                if i == 0:
                     # spot check: masks/values bit-exact and the product within tolerance on sampled rows
                     g = np.random.default_rng(args.seed + pi)
                     rows = np.unique(np.concatenate([[0, R - 1], g.choice(R, size=min(R, 6), replace=False)]))
-                    ridx = torch.from_numpy(rows).to(dev)
-                    hu = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
-                    nref = oracle.col_norm(hu(synth.device_calib_acts(K, args.seed, 200 + pi, c)))
+                    ridx = torch.from_numpy(rows).to(c.dev)
+                    hu = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)  # noqa: E731
+                    nref = oracle.col_norm(hu(synth.device_calib_acts(K, args.seed, 200 + pi, i)))
                     ms, vs = oracle.prune_pack_unstructured(hu(W.index_select(0, ridx)), nref)
                     mk, vl = pool[0]
                     assert (mk.index_select(0, ridx).cpu().numpy().view(np.uint32) == ms).all(), f"u masks {name}"
@@ -564,13 +664,12 @@ def main():
                 del W, n
             fns = [(lambda mk=mk, vl=vl, x=xs[group][i % L]:
                     nm.nm_spmv_unstructured(mk, vl, x, out=ys[name], workspace=ws)) for i, (mk, vl) in enumerate(pool)]
-            us = time_launches(torch, timer, fns)
+            t = time_launches(torch, fns)
             nmus = per[name][f"{N}:{M}"]["us"]
-            unstructured[name] = {"R": R, "K": K, "us": round(us, 2), "GBs": round(nb_ / us / 1e3, 1),
-                                  "pct_peak": round(100 * nb_ / us / 1e3 / HBM_PEAK_GBS, 1),
-                                  f"nm_{N}:{M}_us": nmus, "slowdown_vs_nm": round(us / nmus, 3),
-                                  "speedup_vs_dense": round(per[name]["dense_us"] / us, 3),
-                                  "rotation_MB": round(len(fns) * nb_ / 1e6)}
+            unstructured[name] = dict(t, R=R, K=K, **rate(nb_, t), **{f"nm_{N}:{M}_us": nmus},
+                                      slowdown_vs_nm=round(t["us"] / nmus, 3),
+                                      speedup_vs_dense=round(per[name]["dense_us"] / t["us"], 3),
+                                      rotation_MB=round(len(fns) * nb_ / 1e6))
             del pool, fns
             torch.cuda.synchronize()
         log("unstructured 50% (us): " + "; ".join(f"{n} {d['us']} (N:M {d[f'nm_{N}:{M}_us']}, dense "
@@ -633,13 +732,12 @@ def main():
         torch.cuda.synchronize()
 
     # Dominant kernel: the launch of the (fused) step whose launches take the largest share
-    # of it; its algorithmic bytes over its average launch time is the roofline's achieved.
+    # of it; its algorithmic bytes over its median launch time is the roofline's achieved.
     share = {}
     for grp in groups:
-        label = grp[0][0] if len(grp) == 1 else group_label(grp)
-        share[label] = sum(per[label][f"{N}:{M}"]["us"] for (N, M) in patterns)
+        share[group_label(grp)] = sum(per[group_label(grp)][f"{N}:{M}"]["us"] for (N, M) in patterns)
     dom = max(share, key=share.get)
-    dom_grp = next(grp for grp in groups if (grp[0][0] if len(grp) == 1 else group_label(grp)) == dom)
+    dom_grp = next(grp for grp in groups if group_label(grp) == dom)
     dom_us = share[dom] / len(patterns)
     dom_bytes = group_bytes(dom_grp, B, False)
     achieved = dom_bytes / dom_us / 1e3  # GB/s
@@ -659,7 +757,7 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": dom_desc, "algorithmic_bytes_per_launch": dom_bytes,
-                "avg_launch_us": round(dom_us, 3)}
+                "avg_launch_us": round(dom_us, 3), "timing": "median of 50 replays of a >= 64-launch graph"}
 
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
@@ -675,6 +773,7 @@ def main():
             host.append((masks.cpu().numpy().view(np.uint32), values.contiguous().view(torch.int16).cpu().numpy()
                          .view(np.uint16), xs[group][0].contiguous().view(torch.int16).cpu().numpy().view(np.uint16), K))
             sb += sparse_bytes(R, K, B)
+
         def run_for(seconds, nthreads):
             """Whole passes over the layer until `seconds` of wall time have gone by."""
             reps, t1 = 0, time.time()
@@ -699,6 +798,18 @@ def main():
                             "sample": f"the same layer, x{reps1} reps, {dt1:.1f}s wall"},
                "cpu_model": model}
 
+    # ---------------------------------------------------------------- the other workloads
+    n_fused, n_unfused = len(fused_fns), len(sparse_fns)
+    others = None
+    if not args.no_other_configs and args.config == "8b":
+        del pool_sparse, pool_dense, fused_fns, fused_dense_fns, sparse_fns, dense_fns
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        others = {}
+        for name, layers, batches in OTHER_CONFIGS:
+            others[name] = measure_other(c, name, layers, batches, args.steps, args.warmup, args.seed,
+                                         not args.skip_check)
+
     value = fused_sparse_bytes / (ms_fused * 1e-3) / 1e9
     out = {
         "metric": METRIC,
@@ -716,21 +827,26 @@ def main():
         "config": {"workload": cfg["workload"], "layers": L, "batch": B,
                    "patterns": [f"{N}:{M}" for N, M in patterns], "parallelism": "single GPU"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1),
-        "step": {"launches": len(fused_fns), "groups": [group_label(grp) for grp in groups],
+        "step": {"launches": n_fused,
+                 "groups": [group_label(grp) for grp in groups],
                  "bytes": fused_sparse_bytes,
                  "dense_ms": round(ms_fused_dense, 4),
                  "dense_GBs": round(fused_dense_bytes / (ms_fused_dense * 1e-3) / 1e9, 1),
                  "speedup_vs_dense": round(ms_fused_dense * len(patterns) / ms_fused, 3)},
-        "unfused_step": {"launches": len(sparse_fns), "ms": round(ms_sparse, 4), "bytes": step_sparse_bytes,
+        "unfused_step": {"launches": n_unfused, "ms": round(ms_sparse, 4),
+                         "bytes": step_sparse_bytes,
                          "GBs": round(step_sparse_bytes / (ms_sparse * 1e-3) / 1e9, 1),
                          "pct_hbm_peak": round(100 * step_sparse_bytes / (ms_sparse * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
                          "dense_ms": round(ms_dense, 4),
                          "speedup_vs_dense": round(ms_dense * len(patterns) / ms_sparse, 3)},
         "per_layer": per,
+        "per_layer_target": {"criterion": f">= {TARGET_PCT:.0f}% of the 8 TB/s HBM peak and >= {TARGET_SPEEDUP}x "
+                                          "the same-GPU dense GEMV, per launch", "launches": check},
+        "configs": others,
         "metadata_formats": meta_table,
         "unstructured_50": unstructured,
         "solver": solver,
-        "pack_GBs": round(pack_bytes / pack_ms / 1e6, 1),
+        "pack_GBs": round(st["pack_bytes"] / st["pack_ms"] / 1e6, 1),
         "parity": parity,
         "roofline": roofline,
         "cpu_baseline": cpu,
