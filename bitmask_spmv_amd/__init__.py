@@ -28,7 +28,7 @@ __all__ = [
     "nm_spmv_unstructured_workspace_bytes", "nm_unpack_unstructured", "nm_hessian", "nm_obs_inverse_factor",
     "nm_obs_inverse_factor_workspace_bytes", "nm_sparsegpt_prune_pack", "nm_sparsegpt_workspace_bytes",
     "nm_stream_read", "nm_stream_read_sink_words", "nm_spmv_plan", "nm_spmv_multi_plan", "NM_EPI_NONE",
-    "NM_EPI_SWIGLU", "NM_KERNEL_WORD", "NM_KERNEL_TILE",
+    "NM_EPI_SWIGLU", "NM_KERNEL_WORD", "NM_KERNEL_TILE", "nm_spmv_noalloc",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnmspmv.so")
@@ -77,6 +77,7 @@ def _load() -> ctypes.CDLL:
     L.nm_prune_pack.argtypes = [p, i64, i64, i64, p, i32, i32, p, p, p]
     L.nm_spmv_workspace_bytes.argtypes, L.nm_spmv_workspace_bytes.restype = [i64, i64, i32], sz
     L.nm_spmv.argtypes = [p, p, i64, i64, p, i64, i32, p, i64, p, sz, p]
+    L.nm_spmv_noalloc.argtypes, L.nm_spmv_noalloc.restype = [p, p, i64, i64, p, i64, i32, p, i64, p], i32
     L.dense_gemv_workspace_bytes.argtypes, L.dense_gemv_workspace_bytes.restype = [i64, i64, i32], sz
     L.dense_gemv.argtypes = [p, i64, i64, i64, p, i64, i32, p, i64, p, sz, p]
     L.nm_unpack.argtypes = [p, p, i64, i64, p, i64, p]
@@ -236,6 +237,24 @@ def nm_spmv(masks: torch.Tensor, values: torch.Tensor, x: torch.Tensor, out: tor
     ws, ws_bytes = _workspace(nm_spmv_workspace_bytes(R, K, B), x2, workspace)
     _check(lib.nm_spmv(_ptr(masks), _ptr(values), R, K, _ptr(x2), _ld(x2), B, _ptr(o2), _ld(o2), _ptr(ws),
                        ws_bytes, _stream(x2)))
+    return out[0] if squeeze and out.dim() == 2 else out
+
+
+def nm_spmv_noalloc(masks: torch.Tensor, values: torch.Tensor, x: torch.Tensor,
+                    out: torch.Tensor | None = None) -> torch.Tensor:
+    """nm_spmv without a workspace: split rows use the library's fixed per-device scratch.
+    Allocates nothing when `out` is given."""
+    _dev(masks, "masks", torch.int32, 2)
+    _dev(values, "values", torch.bfloat16, 2)
+    if not (masks.is_contiguous() and values.is_contiguous()):
+        raise ValueError("masks and values must be contiguous")
+    R = masks.shape[0]
+    K = masks.shape[1] * 32
+    if values.shape != (R, K // 2):
+        raise ValueError("values must be [R, K/2] with K = 32 * masks.shape[1]")
+    x2, B, o2, out, squeeze = _x_y(x, R, K, out)
+    _check(lib.nm_spmv_noalloc(_ptr(masks), _ptr(values), R, K, _ptr(x2), _ld(x2), B, _ptr(o2), _ld(o2),
+                               _stream(x2)))
     return out[0] if squeeze and out.dim() == 2 else out
 
 

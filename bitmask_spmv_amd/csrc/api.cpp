@@ -217,6 +217,44 @@ nm_status nm_spmv(const uint32_t *masks, const nm_bf16 *values, int64_t R, int64
     }
 }
 
+nm_status nm_spmv_noalloc(const uint32_t *masks, const nm_bf16 *values, int64_t R, int64_t K, const nm_bf16 *x,
+                          int64_t ldx, int B, nm_bf16 *y, int64_t ldy, void *hip_stream) {
+    try {
+        g_err[0] = 0;
+        const char *who = "nm_spmv_noalloc";
+        if (!masks || !values || !x || !y) return fail(NM_ERR_NULL, "%s: NULL pointer", who);
+        if (K < 32 || K > kMaxDim || K % 32 != 0)
+            return fail(NM_ERR_SHAPE, "%s: K=%lld must be a positive multiple of 32", who, (long long)K);
+        nm_status st = check_mv_common(R, K, B, ldx, ldy, x, y);
+        if (st != NM_OK) return st;
+        if (!aligned(masks, 4) || !aligned(values, 16))
+            return fail(NM_ERR_ALIGN, "%s: masks need 4-byte and values 16-byte alignment", who);
+        nmk::SpmvSet set;
+        set.P = 1;
+        set.row0[1] = (int)R;
+        set.meta[0] = masks;
+        set.values[0] = values;
+        set.y[0] = y;
+        set.ldy[0] = ldy;
+        const nmk::MvPlan p = spmv_set_plan(set, NM_META_BITMASK, K, ldx, B, nmk::kEpiNone);
+        if (p.ws_bytes > nmk::kSpmvScratchBytes)
+            return fail(NM_ERR_WORKSPACE, "%s: this shape needs %zu bytes of scratch, above the fixed %zu", who,
+                        p.ws_bytes, nmk::kSpmvScratchBytes);
+        void *scratch = nullptr;
+        if (p.ws_bytes > 0) {
+            hipError_t e = nmk::spmv_scratch(&scratch);
+            if (e != hipSuccess) return hip_fail("nm_spmv_noalloc scratch lookup", e);
+        }
+        hipError_t e = p.tile ? nmk::launch_spmv_tile(p, set, K, x, ldx, B, nmk::kEpiNone, (hipStream_t)hip_stream)
+                              : nmk::launch_spmv(p, set, NM_META_BITMASK, K, x, ldx, B, (float *)scratch,
+                                                 (hipStream_t)hip_stream);
+        if (e != hipSuccess) return hip_fail(who, e);
+        return NM_OK;
+    } catch (...) {
+        return fail(NM_ERR_HIP, "nm_spmv_noalloc: internal error");
+    }
+}
+
 nm_status nm_spmv_meta(const void *meta, int format, const nm_bf16 *values, int64_t R, int64_t K, const nm_bf16 *x,
                        int64_t ldx, int B, nm_bf16 *y, int64_t ldy, void *workspace, size_t workspace_bytes,
                        void *hip_stream) {

@@ -75,6 +75,10 @@ struct DenseSet {
 // kernels that fit them without spilling).
 MvPlan plan_spmv(int64_t R, int64_t K, int B, const DeviceInfo &dev, int fmt = kMetaBitmask);
 size_t spmv_lds_per_word(int B);  // LDS bytes of x per 32-column block
+// Fixed device scratch for callers that cannot allocate (nm_spmv_noalloc): its device
+// address on the current device (looked up once per device), kSpmvScratchBytes long.
+constexpr size_t kSpmvScratchBytes = (size_t)4 << 20;
+hipError_t spmv_scratch(void **ptr);
 // epi: the launch's epilogue, which decides whether the 1024-thread workgroup variant
 // fits without spilling.
 MvPlan plan_dense(int64_t R, int64_t K, int B, const DeviceInfo &dev, int epi = kEpiNone);

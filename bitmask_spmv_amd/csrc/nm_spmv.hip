@@ -29,6 +29,7 @@
 //   * one kernel serves every 50% pattern (2:4 ... 16:32): the M of the pattern never
 //     enters the traversal.  Several matrices that share x run in one launch (SpmvSet).
 #include <atomic>
+#include <mutex>
 
 #include "nm_device.h"
 #include "nm_kernels.h"
@@ -432,6 +433,31 @@ hipError_t launch_f(const MvPlan &p, const SpmvSet &set, int64_t K, const uint16
 
 size_t spmv_lds_per_word(int B) { return (size_t)blk_dwords(B) * 4; }
 
+// Device-resident scratch of the no-allocation entry point: the fp32 partial sums of split
+// rows, in a fixed array of kSpmvScratchBytes on every device the library runs on (held
+// until the process ends).  In host code `scratch` only names the symbol; its device
+// address comes from hipGetSymbolAddress, looked up once per device with that device
+// current and kept per device, and only that address is passed to kernels.
+static __device__ __align__(256) unsigned char scratch[kSpmvScratchBytes];
+
+hipError_t spmv_scratch(void **ptr) {
+    static std::mutex mu;
+    static void *addr[64] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 MvPlan plan_spmv(int64_t R, int64_t K, int B, const DeviceInfo &dev, int fmt) {
     MvPlan p;

@@ -126,6 +126,23 @@ nm_status nm_spmv(const uint32_t *masks, const nm_bf16 *values, int64_t R, int64
                   void *hip_stream);
 
 /*
+ * nm_spmv_noalloc -- nm_spmv without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same product, same kernels and bit-identical results; the fp32
+ * partial sums of split rows live in a fixed scratch array of 4 MiB that the library holds
+ * on every device it runs on until the process ends.  The call allocates nothing and calls
+ * no allocating routine; its first call on a device looks up that device's scratch
+ * address (a host-side lookup, no allocation).
+ * A shape whose split rows need more than 4 MiB of partial sums (as nm_spmv_workspace_bytes
+ * would report) is rejected with NM_ERR_WORKSPACE before any HIP call; every other shape
+ * of nm_spmv is accepted.  All calls on one device share its scratch: calls that overlap
+ * in time on one device (different streams or threads) race and must be serialised by the
+ * caller.  Arguments and the remaining conditions as for nm_spmv.
+ */
+nm_status nm_spmv_noalloc(const uint32_t *masks, const nm_bf16 *values, int64_t R, int64_t K, const nm_bf16 *x,
+                          int64_t ldx, int B, nm_bf16 *y, int64_t ldy, void *hip_stream);
+
+/*
  * dense_gemv -- same-GPU dense baseline for the same product with an unpruned bf16
  * matrix (decode is a memory-bound matrix-vector product [SD-cn, 前置知识 Prefill 与
  * Decoding]):  y[b][i] = sum_j W[i][j] * x[b][j], fp32 accumulate, bf16 RNE store.

@@ -284,3 +284,22 @@ def test_stream_read_rejects_bad_arguments(L):
     assert L.nm_stream_read(A16, (1 << 31) + 16, A16, 1024, None) == NM_ERR_SHAPE
     assert L.nm_stream_read(A4, 1 << 20, A16, words, None) == NM_ERR_ALIGN
     assert L.nm_stream_read(A16, 1 << 20, A16, words - 1, None) == NM_ERR_WORKSPACE
+
+
+def test_noalloc_rejects_bad_arguments_and_oversized_scratch(L):
+    """nm_spmv_noalloc validates like nm_spmv and rejects, before any HIP call, a shape whose
+    split-row partial sums exceed its fixed 4 MiB scratch (B = 2, K = 28672 splits every row
+    in two: 2 * 2 * R * 4 bytes)."""
+    p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    L.nm_spmv_noalloc.argtypes = [p, p, i64, i64, p, i64, i32, p, i64, p]
+    L.nm_spmv_noalloc.restype = i32
+    assert L.nm_spmv_noalloc(None, A16, 4, 64, A16, 64, 1, A16, 4, None) == NM_ERR_NULL
+    assert L.nm_spmv_noalloc(A4, A16, 4, 48, A16, 64, 1, A16, 4, None) == NM_ERR_SHAPE
+    assert L.nm_spmv_noalloc(A4, A16, 4, 64, A16, 64, 9, A16, 4, None) == NM_ERR_SHAPE
+    assert L.nm_spmv_noalloc(A4, A4, 4, 64, A16, 64, 1, A16, 4, None) == NM_ERR_ALIGN
+    K = 28672
+    assert L.nm_spmv_noalloc(A4, A16, 300000, K, A16, K, 2, A16, 300000, None) == NM_ERR_WORKSPACE
+    assert b"scratch" in L.nm_last_error()
+    # exactly at the limit (262144 rows: 4 MiB) the shape is accepted; without a GPU the
+    # call then fails at the device lookup, not at the size check
+    assert L.nm_spmv_noalloc(A4, A16, 262144, K, A16, K, 2, A16, 262144, None) not in (NM_ERR_WORKSPACE, NM_OK)
