@@ -18,8 +18,8 @@
 // holds tokens 0..B-1 in its first B lanes of each row group and zeros in the others.
 //
 // Layout of the work:
-//   * a workgroup (8 waves) owns a tile of 16 rows at a time; wave w walks words
-//     [w*KW/8, (w+1)*KW/8) of those rows in steps of 4 words, one word per lane;
+//   * a workgroup (8 or 16 waves) owns a unit of 16-row tiles at a time; its steps of
+//     4 words go round-robin to the waves (wave w: steps w, w + W, ...), one word per lane;
 //   * tile rows 0-7 and 8-15 are 8 consecutive rows of one matrix each (plain launch:
 //     the same matrix; gated MLP: gate rows i..i+7, then up rows i..i+7);
 //   * a step loads 128 bytes of values per row (two 16-byte loads per lane, rows 0-7
@@ -276,9 +276,13 @@ __device__ __forceinline__ void finish_tile(f32x4 (&acc)[TT], float *red, const 
     }
 }
 
-// W waves per workgroup share a unit of TT tiles (16*TT rows) at a time: wave w walks
-// words [w*KW/W, (w+1)*KW/W) of the unit's rows in steps of 4 words, one word of each
-// tile per lane, all TT tiles of a step multiplied by the same x operand.
+// W waves per workgroup share a unit of TT tiles (16*TT rows) at a time: the unit's
+// steps of 4 words are dealt round-robin to the waves (wave w walks steps w, w + W,
+// w + 2W, ...), one word of each tile per lane, all TT tiles of a step multiplied by the
+// same x operand.  With the steps interleaved, the W waves read W consecutive 128-byte
+// pieces of every row at about the same time -- runs of W*128 bytes per row instead of W
+// pieces K/W columns apart -- which keeps the memory's row buffers busier (measured
+// 4-13% faster at 8 tokens than contiguous quarters of K per wave).
 template <int B, int EPI, int TT, int W>
 __global__ __launch_bounds__(W * kWave, 4) void spmv_tile_kernel(const SpmvSet set, int KW,
                                                                  const uint16_t *__restrict__ x, int64_t ldx,
@@ -291,7 +295,6 @@ __global__ __launch_bounds__(W * kWave, 4) void spmv_tile_kernel(const SpmvSet s
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int nwp = KW / W;  // words per wave and row; a multiple of kTStep
     const int steps = nwp / kTStep;
-    const int wa = wave * nwp;
     const int my_units = (int)blockIdx.x < units ? (units - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
     const int total = my_units * steps;
     const uint32_t vo = (uint32_t)((lane >> 3) * KW * 32 + (lane & 7) * 16);
@@ -310,7 +313,7 @@ __global__ __launch_bounds__(W * kWave, 4) void spmv_tile_kernel(const SpmvSet s
     TBatch<TT> bA, bB;
     int tA = blockIdx.x, sA = 0, tB = tA, sB = 0;
     TileRows<TT> rA = tile_rows<EPI, TT>(set, min(tA, units - 1), KW), rB = rA;
-    load_tbatch<B, TT>(bA, rA, wa, KW, x, ldx, vo, mo, xo, total > 0);
+    load_tbatch<B, TT>(bA, rA, wave * kTStep, KW, x, ldx, vo, mo, xo, total > 0);
     f32x4 acc[TT];
 #pragma unroll
     for (int t = 0; t < TT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -326,7 +329,7 @@ __global__ __launch_bounds__(W * kWave, 4) void spmv_tile_kernel(const SpmvSet s
         } else {
             rB = rA;
         }
-        load_tbatch<B, TT>(bB, rB, wa + kTStep * sB, KW, x, ldx, vo, mo, xo, true);
+        load_tbatch<B, TT>(bB, rB, (sB * W + wave) * kTStep, KW, x, ldx, vo, mo, xo, true);
         __builtin_amdgcn_sched_barrier(0);
         walk_tbatch<TT>(bA, tw, lane, acc);
         if (sA == steps - 1) {
@@ -342,7 +345,7 @@ __global__ __launch_bounds__(W * kWave, 4) void spmv_tile_kernel(const SpmvSet s
         } else {
             rA = rB;
         }
-        load_tbatch<B, TT>(bA, rA, wa + kTStep * sA, KW, x, ldx, vo, mo, xo, k + 2 < total);
+        load_tbatch<B, TT>(bA, rA, (sA * W + wave) * kTStep, KW, x, ldx, vo, mo, xo, k + 2 < total);
         __builtin_amdgcn_sched_barrier(0);
         walk_tbatch<TT>(bB, tw, lane, acc);
         if (sB == steps - 1) {
