@@ -54,7 +54,7 @@ class _SpmvMatrix(ctypes.Structure):
 
 class _LaunchPlan(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int), ("threads", ctypes.c_int), ("grid_x", ctypes.c_int),
-                ("splits", ctypes.c_int), ("tiles_per_step", ctypes.c_int), ("reserved", ctypes.c_int),
+                ("splits", ctypes.c_int), ("tiles_per_step", ctypes.c_int), ("x_steps_in_registers", ctypes.c_int),
                 ("lds_bytes", ctypes.c_size_t), ("workspace_bytes", ctypes.c_size_t)]
 
 
@@ -582,13 +582,13 @@ def nm_stream_read(buf: torch.Tensor, sink: torch.Tensor | None = None) -> torch
 
 
 def _plan_dict(pl: _LaunchPlan) -> dict:
-    return {f: getattr(pl, f) for f, _ in _LaunchPlan._fields_ if f != "reserved"}
+    return {f: getattr(pl, f) for f, _ in _LaunchPlan._fields_}
 
 
 def nm_spmv_plan(R: int, K: int, B: int, epilogue: int = NM_EPI_NONE) -> dict:
     """Launch plan of nm_spmv (or nm_spmv_swiglu with epilogue=NM_EPI_SWIGLU, R rows each)
-    on the current device: kernel, threads, grid_x, splits, tiles_per_step, lds_bytes,
-    workspace_bytes.  Host only."""
+    on the current device: kernel, threads, grid_x, splits, tiles_per_step,
+    x_steps_in_registers, lds_bytes, workspace_bytes.  Host only."""
     pl = _LaunchPlan()
     _check(lib.nm_spmv_plan(int(R), int(K), int(B), int(epilogue), ctypes.byref(pl)))
     return _plan_dict(pl)

@@ -397,7 +397,7 @@ static void fill_plan(const nmk::MvPlan &p, nm_launch_plan *out) {
     out->grid_x = p.grid_x;
     out->splits = p.splits;
     out->tiles_per_step = p.tile ? p.unroll : 0;
-    out->reserved = 0;
+    out->x_steps_in_registers = p.tile ? p.xreg : 0;
     out->lds_bytes = p.tile ? 0 : p.lds_bytes;
     out->workspace_bytes = p.ws_bytes;
 }

@@ -29,6 +29,7 @@ struct MvPlan {
     size_t ws_bytes = 0;    // workspace bytes (0 when splits == 1)
     int tile = 0;           // 1: the matrix-core tile kernel (nm_spmv_tile.hip), 16-row tiles (threads / 64 waves)
     int tiles = 0;          // tile kernel: number of units (16 or 32 rows; unroll = tiles per unit)
+    int xreg = 0;           // tile kernel: steps per wave and unit whose x operand stays in registers (0: none)
 };
 
 // Row epilogues of the matrix-vector kernels.  kEpiNone: every row's total is one

@@ -25,8 +25,11 @@
 //   * a step loads 128 bytes of values per row (two 16-byte loads per lane, rows 0-7
 //     then rows 8-15, 8 lanes per row, contiguous), the lane's mask word of both row
 //     halves, and the step's 4 x 32 columns of x straight into the MFMA operand
-//     registers (x is re-read by every tile: an L2 hit); a swap of 16-byte halves between
-//     lane pairs gives each lane the 16 values of its word, as in nm_spmv.hip;
+//     registers (x is re-read by every tile: an L2 hit -- except where every wave has
+//     exactly four steps per unit, K = 4096 with 8 waves or 8192 with 16: a wave's x
+//     columns are then the same in every unit and stay in registers after its first);
+//     a swap of 16-byte halves between lane pairs gives each lane the 16 values of its
+//     word, as in nm_spmv.hip;
 //   * the lane zeroes its word's 32 columns of the wave's dense tile and writes its 16
 //     kept values at their columns; four MFMAs then add the step into the wave's 16xB
 //     accumulator (lane l: rows 4*(l/16)..+3 of token l%16);
@@ -118,8 +121,9 @@ __device__ __forceinline__ TileRows<TT> tile_rows(const SpmvSet &set, int unit, 
     return t;
 }
 
-// Loads of one step at word column cw (live = false: the same loads with empty ranges).
-template <int B, int TT>
+// Loads of one step at word column cw (live = false: the same loads with empty ranges);
+// LX = false leaves out the x operand (kept in registers by the caller).
+template <int B, int TT, bool LX = true>
 __device__ __forceinline__ void load_tbatch(TBatch<TT> &bt, const TileRows<TT> &tr, int cw, int KW,
                                             const uint16_t *x, int64_t ldx, uint32_t vo, uint32_t mo, uint32_t xo,
                                             bool live) {
@@ -142,10 +146,12 @@ __device__ __forceinline__ void load_tbatch(TBatch<TT> &bt, const TileRows<TT> &
             bt.ma[q >> 1] = m;
         }
     }
-    const int64_t xn = live ? (int64_t)(B - 1) * ldx * 2 + (int64_t)(KW - cw) * 64 : 0;
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + (int64_t)cw * 32, xn);
+    if constexpr (LX) {
+        const int64_t xn = live ? (int64_t)(B - 1) * ldx * 2 + (int64_t)(KW - cw) * 64 : 0;
+        const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + (int64_t)cw * 32, xn);
 #pragma unroll
-    for (int j = 0; j < kTStep / 2; ++j) bt.xp[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, xo + j * 128u, 0, 0);
+        for (int j = 0; j < kTStep / 2; ++j) bt.xp[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, xo + j * 128u, 0, 0);
+    }
 }
 
 // Swap one dword with the neighbouring lane of the pair (lane ^ 1).
@@ -220,12 +226,13 @@ __device__ __forceinline__ u32x4 swap_row_halves(const u32x4 &v) {
 // the lanes of tokens 8..15 hold x of other tokens or columns: they only feed output
 // columns 8..15 of the product, which no one reads.
 template <int TT>
-__device__ __forceinline__ void walk_tbatch(const TBatch<TT> &bt, uint8_t *tw, int lane, f32x4 (&acc)[TT]) {
+__device__ __forceinline__ void walk_tbatch(const TBatch<TT> &bt, const u32x4 (&xp)[kTStep / 2], uint8_t *tw, int lane,
+                                            f32x4 (&acc)[TT]) {
     u32x4 xq[kTStep];
 #pragma unroll
     for (int j = 0; j < kTStep / 2; ++j) {
-        xq[2 * j] = bt.xp[j];
-        xq[2 * j + 1] = swap_row_halves(bt.xp[j]);
+        xq[2 * j] = xp[j];
+        xq[2 * j + 1] = swap_row_halves(xp[j]);
     }
 #pragma unroll
     for (int t = 0; t < TT; ++t) walk_tile(bt.va[t], bt.vb[t], bt.ma[t], bt.mb[t], xq, tw, lane, acc[t]);
@@ -331,7 +338,7 @@ __global__ __launch_bounds__(W * kWave, 4) void spmv_tile_kernel(const SpmvSet s
         }
         load_tbatch<B, TT>(bB, rB, (sB * W + wave) * kTStep, KW, x, ldx, vo, mo, xo, true);
         __builtin_amdgcn_sched_barrier(0);
-        walk_tbatch<TT>(bA, tw, lane, acc);
+        walk_tbatch<TT>(bA, bA.xp, tw, lane, acc);
         if (sA == steps - 1) {
             finish_tile<B, EPI, TT, W>(acc, buf ? red1 : red0, rA, set, wave, lane);
             buf ^= 1;
@@ -347,22 +354,104 @@ __global__ __launch_bounds__(W * kWave, 4) void spmv_tile_kernel(const SpmvSet s
         }
         load_tbatch<B, TT>(bA, rA, (sA * W + wave) * kTStep, KW, x, ldx, vo, mo, xo, k + 2 < total);
         __builtin_amdgcn_sched_barrier(0);
-        walk_tbatch<TT>(bB, tw, lane, acc);
+        walk_tbatch<TT>(bB, bB.xp, tw, lane, acc);
         if (sB == steps - 1) {
             finish_tile<B, EPI, TT, W>(acc, buf ? red1 : red0, rB, set, wave, lane);
             buf ^= 1;
         }
     }
     if (k < total) {  // odd count: the last step is in A
-        walk_tbatch<TT>(bA, tw, lane, acc);
+        walk_tbatch<TT>(bA, bA.xp, tw, lane, acc);
         if (sA == steps - 1) finish_tile<B, EPI, TT, W>(acc, buf ? red1 : red0, rA, set, wave, lane);
     }
 }
 
+// One unit of the walk below.  Step s of the unit reads buffer A for even s and B for
+// odd s; the last step loads the next unit's first step into A.  FIRST: the steps load
+// their x operand with their weights, as in spmv_tile_kernel, and keep it in xc for the
+// later units, which load weights only.
+template <int B, int EPI, int TT, int W, int XC, bool FIRST>
+__device__ __forceinline__ void xc_unit(TBatch<TT> &bA, TBatch<TT> &bB, u32x4 (&xc)[XC][kTStep / 2],
+                                        const TileRows<TT> &r, const TileRows<TT> &rn, bool next_live, int KW,
+                                        const uint16_t *x, int64_t ldx, uint32_t vo, uint32_t mo, uint32_t xo,
+                                        int wave, uint8_t *tw, int lane, f32x4 (&acc)[TT]) {
+#pragma unroll
+    for (int s = 0; s < XC; s += 2) {
+        load_tbatch<B, TT, FIRST>(bB, r, ((s + 1) * W + wave) * kTStep, KW, x, ldx, vo, mo, xo, true);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (FIRST) {
+#pragma unroll
+            for (int j = 0; j < kTStep / 2; ++j) xc[s][j] = bA.xp[j];
+        }
+        walk_tbatch<TT>(bA, xc[s], tw, lane, acc);
+        if (s + 2 < XC)
+            load_tbatch<B, TT, FIRST>(bA, r, ((s + 2) * W + wave) * kTStep, KW, x, ldx, vo, mo, xo, true);
+        else
+            load_tbatch<B, TT, false>(bA, rn, wave * kTStep, KW, x, ldx, vo, mo, xo, next_live);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (FIRST) {
+#pragma unroll
+            for (int j = 0; j < kTStep / 2; ++j) xc[s + 1][j] = bB.xp[j];
+        }
+        walk_tbatch<TT>(bB, xc[s + 1], tw, lane, acc);
+    }
+}
+
+// The same walk where every wave has exactly XC steps per unit (K = 128 * W * XC
+// columns, XC even): a wave's x columns are then the same in every unit, so it keeps
+// them in registers (XC x 8 per lane) after its first unit, and the steps of its later
+// units load weights only -- half the load instructions and L2 traffic of a one-tile
+// step.  The first unit loads x step by step with the weights, so a workgroup with a
+// single unit waits no longer for its first step than spmv_tile_kernel does.
+template <int B, int EPI, int TT, int W, int XC>
+__global__ __launch_bounds__(W * kWave, 4) void spmv_tile_xc_kernel(const SpmvSet set, int KW,
+                                                                    const uint16_t *__restrict__ x, int64_t ldx,
+                                                                    int units) {
+    static_assert(XC % 2 == 0, "steps per unit alternate between the two buffers");
+    extern __shared__ __attribute__((aligned(16))) uint8_t tlds[];
+    uint8_t *dense = tlds;
+    float *red0 = reinterpret_cast<float *>(tlds + (size_t)W * kTWaveBytes);
+    float *red1 = red0 + W * B * kTRows * TT;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const uint32_t vo = (uint32_t)((lane >> 3) * KW * 32 + (lane & 7) * 16);
+    const uint32_t mo = (uint32_t)((lane >> 3) * KW * 4 + ((lane & 7) >> 1) * 4);
+    const int n = lane & 7;  // x operand lanes as in spmv_tile_kernel
+    const uint32_t xo = n < B ? (uint32_t)(n * ldx * 2 + (lane >> 4) * 16 + ((lane >> 3) & 1) * 64) : kXOut;
+    uint8_t *tw = dense + wave * kTWaveBytes;
+
+    // the wave's x operand of each of its XC steps (word column (s * W + wave) * 4)
+    u32x4 xc[XC][kTStep / 2];
+    TBatch<TT> bA, bB;
+    f32x4 acc[TT];
+#pragma unroll
+    for (int t = 0; t < TT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // the grid never exceeds the units, so every workgroup has at least one
+    int u = blockIdx.x;
+    TileRows<TT> r = tile_rows<EPI, TT>(set, u, KW);
+    load_tbatch<B, TT, true>(bA, r, wave * kTStep, KW, x, ldx, vo, mo, xo, true);
+    {
+        const int un = u + gridDim.x;
+        const TileRows<TT> rn = tile_rows<EPI, TT>(set, min(un, units - 1), KW);
+        xc_unit<B, EPI, TT, W, XC, true>(bA, bB, xc, r, rn, un < units, KW, x, ldx, vo, mo, xo, wave, tw, lane, acc);
+        finish_tile<B, EPI, TT, W>(acc, red0, r, set, wave, lane);
+        r = rn;
+        u = un;
+    }
+    int buf = 1;
+    for (; u < units; u += gridDim.x) {
+        const int un = u + gridDim.x;
+        const TileRows<TT> rn = tile_rows<EPI, TT>(set, min(un, units - 1), KW);
+        xc_unit<B, EPI, TT, W, XC, false>(bA, bB, xc, r, rn, un < units, KW, x, ldx, vo, mo, xo, wave, tw, lane, acc);
+        finish_tile<B, EPI, TT, W>(acc, buf ? red1 : red0, r, set, wave, lane);
+        buf ^= 1;
+        r = rn;
+    }
+}
+
 // Raise the dynamic-LDS limit of one kernel instance once per device.
-template <int B, int EPI, int TT, int W>
-hipError_t allow_tile_lds() {
-    static std::atomic<uint64_t> done{0};
+template <int B, int TT, int W>
+hipError_t allow_tile_lds(const void *kernel, std::atomic<uint64_t> &done) {
     constexpr size_t bytes = tile_lds_bytes<B, TT, W>();
     if (bytes <= 64 * 1024) return hipSuccess;
     int dev = 0;
@@ -370,21 +459,35 @@ hipError_t allow_tile_lds() {
     if (e != hipSuccess) return e;
     const uint64_t bit = 1ull << (dev & 63);
     if (done.load(std::memory_order_acquire) & bit) return hipSuccess;
-    e = hipFuncSetAttribute((const void *)spmv_tile_kernel<B, EPI, TT, W>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)bytes);
+    e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
     if (e == hipSuccess) done.fetch_or(bit, std::memory_order_acq_rel);
     return e;
 }
 
+// Steps per wave and unit for which the x operand is held in registers.
+constexpr int kTileXC = 4;
+
 template <int B, int EPI, int TT, int W>
 hipError_t launch_tbw(const MvPlan &p, const SpmvSet &set, int64_t K, const uint16_t *x, int64_t ldx,
                       hipStream_t st) {
-    hipError_t e = allow_tile_lds<B, EPI, TT, W>();
-    if (e != hipSuccess) return e;
     SpmvSet padded = set;
     for (int q = set.P + 1; q <= kMaxMats; ++q) padded.row0[q] = set.row0[set.P];
+    const int KW = (int)(K / 32);
+    if (p.xreg) {
+        if (p.xreg != kTileXC || KW != W * kTStep * kTileXC) return hipErrorInvalidValue;
+        static std::atomic<uint64_t> done{0};
+        const void *kern = (const void *)spmv_tile_xc_kernel<B, EPI, TT, W, kTileXC>;
+        hipError_t e = allow_tile_lds<B, TT, W>(kern, done);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((spmv_tile_xc_kernel<B, EPI, TT, W, kTileXC>), dim3((unsigned)p.grid_x), dim3(W * kWave),
+                           (tile_lds_bytes<B, TT, W>()), st, padded, KW, x, ldx, p.tiles);
+        return hipGetLastError();
+    }
+    static std::atomic<uint64_t> done{0};
+    hipError_t e = allow_tile_lds<B, TT, W>((const void *)spmv_tile_kernel<B, EPI, TT, W>, done);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL((spmv_tile_kernel<B, EPI, TT, W>), dim3((unsigned)p.grid_x), dim3(W * kWave),
-                       (tile_lds_bytes<B, TT, W>()), st, padded, (int)(K / 32), x, ldx, p.tiles);
+                       (tile_lds_bytes<B, TT, W>()), st, padded, KW, x, ldx, p.tiles);
     return hipGetLastError();
 }
 
@@ -427,16 +530,25 @@ bool spmv_tile_ok(const SpmvSet &set, int64_t K, int64_t ldx, int B, int fmt, in
 }
 
 MvPlan plan_spmv_tile(const SpmvSet &set, int64_t K, int B, const DeviceInfo &dev, int epi) {
-    (void)B;
     MvPlan p;
     p.tile = 1;
     const int64_t R = set.row0[set.P];
     const int64_t cu = dev.num_cu > 0 ? dev.num_cu : 256;
     const int64_t tiles = epi == kEpiSwiGLU ? (R / 2 + 7) / 8 : (R + kTRows - 1) / kTRows;
-    // Two 8-wave workgroups per CU (LDS and register budget).  With fewer tiles than
-    // that, one 16-wave workgroup per CU keeps as many waves in flight, where K still
-    // gives every wave at least four steps per tile.
-    const int w = (tiles < 2 * cu && K % (32 * 16 * kTStep) == 0 && K / (32 * 16 * kTStep) >= 4) ? 16 : 8;
+    // Two 8-wave workgroups per CU (LDS and register budget), or one 16-wave workgroup
+    // per CU -- as many waves in flight -- where K gives every one of 16 waves at least
+    // four steps per tile and
+    //   * there are fewer tiles than 8-wave workgroups, or
+    //   * every wave of 16 then has exactly kTileXC steps (x stays in registers), there
+    //     are at least 4 tiles per CU to amortise the first unit's x loads, and 7 or 8
+    //     tokens make x a large share of the loads (28672 x 8192, 8 tokens: 54.8 -> 51.2
+    //     us; 5 tokens: 48.9 -> 52.4 us, so not there), or
+    //   * K is long (8 or more steps per wave of 16): the x operand, re-read every step,
+    //     is then shared by two tiles from as few as 2 tiles per CU on (8 tokens,
+    //     8192 x 28672: 60.2 -> 53.7 us).
+    const int64_t s16 = K % (32 * 16 * kTStep) == 0 ? K / (32 * 16 * kTStep) : 0;  // steps per wave of 16
+    const bool w16 = s16 >= 4 && (tiles < 2 * cu || (s16 == kTileXC && tiles >= 4 * cu && B >= 7) || s16 >= 8);
+    const int w = w16 ? 16 : 8;
     const int64_t slots = cu * (16 / w);  // resident workgroups
     // Two tiles per step (one x operand for 32 rows, half the x loads per weight byte)
     // when that leaves the CUs as evenly loaded as one tile per step does: the units of
@@ -458,6 +570,7 @@ MvPlan plan_spmv_tile(const SpmvSet &set, int64_t K, int B, const DeviceInfo &de
     p.tiles = (int)units;
     p.unroll = tt;
     p.threads = w * kWave;
+    p.xreg = K / 32 == (int64_t)w * kTStep * kTileXC ? kTileXC : 0;
     p.splits = 1;
     p.ws_bytes = 0;
     return p;

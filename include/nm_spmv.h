@@ -213,7 +213,8 @@ typedef struct {
     int grid_x;             /* workgroups per row slice (word) / resident workgroups (tile) */
     int splits;             /* row slices; > 1: fp32 partial sums and an ordered second pass */
     int tiles_per_step;     /* tile walk: 16-row tiles sharing one x operand (1 or 2); 0 otherwise */
-    int reserved;
+    int x_steps_in_registers; /* tile walk: steps whose x operand each wave holds in registers for the
+                                 whole launch (its steps then load weights only); 0: x re-read per step */
     size_t lds_bytes;       /* dynamic LDS of the word-per-lane walk per workgroup */
     size_t workspace_bytes; /* what the compute call requires */
 } nm_launch_plan;

@@ -78,6 +78,15 @@ def ternary(shape, seed: int = 0, *ids: int) -> np.ndarray:
     return to_bf16_bits(g.integers(-1, 2, size=shape).astype(np.float32))
 
 
+def ternary_sparse(shape, density: float, seed: int = 0, *ids: int) -> np.ndarray:
+    """Like ternary, with each entry kept nonzero only with probability `density`: long
+    rows whose sums of products still stay small integers (bf16-exact up to 256)."""
+    g = rng(seed, 6, *ids)
+    v = g.integers(-1, 2, size=shape).astype(np.float32)
+    v[g.random(size=shape) >= density] = 0.0
+    return to_bf16_bits(v)
+
+
 def tie_stress(R: int, K: int, seed: int = 0, *ids: int):
     """Weights drawn from {0, +-2^-4, +-2^-3} (and -0.0) and column norms from {1, 2}:
     many exactly equal scores inside every group, so the tie rule decides."""

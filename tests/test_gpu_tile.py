@@ -225,3 +225,48 @@ def test_tile_small_batch_multi_and_swiglu(B):
     u, au = oracle.spmv(um, uv, x, K, nthreads=8)
     ok = np.abs(bf16_as_f64(h) - oracle.swiglu(g, u)) <= oracle.swiglu_tolerance(g, ag, u, au)
     assert ok.all(), f"swiglu B={B}: {int((~ok).sum())} outside"
+
+
+# Shapes where every wave keeps its x operand in registers for the whole launch (exactly
+# four steps per wave and unit: K = 4096 with 8-wave workgroups, 8192 with 16-wave ones),
+# with more units than workgroups and with two tiles per step, beside shapes that re-read
+# x every step.  Integer-valued operands, so the result must equal the oracle exactly.
+# xreg None: the planner may take either walk.
+XREG = [(300, 4096, 8, 4), (9000, 4096, 5, 4), (1000, 8192, 8, 4), (5000, 8192, 6, 4), (9000, 8192, 7, None),
+        (300, 2048, 6, 0), (3000, 14336, 8, 0)]
+
+
+@pytest.mark.parametrize("R,K,B,xreg", XREG)
+def test_tile_x_in_registers_integer_exact(R, K, B, xreg):
+    say("tile x in registers", R, K, B)
+    plan = nm.nm_spmv_plan(R, K, B)
+    assert plan["kernel"] == nm.NM_KERNEL_TILE
+    if xreg is not None:
+        assert plan["x_steps_in_registers"] == xreg
+    W = synth.ternary((R, K), 44, R, K, B)
+    x = synth.ternary_sparse((B, K), 1024 / K, 45, R, K, B)
+    mref, vref = oracle.prune_pack(W, oracle.col_norm(synth.calib_acts(K, 44, R)), 8, 16)
+    y = nm.nm_spmv(dev_u32(mref), dev_bf16(vref), dev_bf16(x))
+    yref, _ = oracle.spmv(mref, vref, x, K, nthreads=8)
+    assert np.abs(yref).max() <= 256
+    got = bf16_as_f64(host_bf16(y))
+    assert (got == yref).all(), f"{int((got != yref).sum())} of {got.size} differ"
+
+
+def test_tile_x_in_registers_two_tiles_swiglu():
+    """Gated MLP, 16384 rows each, K = 4096, 8 tokens: two tiles per step, x in registers."""
+    R, K, B = 16384, 4096, 8
+    say("tile x in registers swiglu", R, K, B)
+    plan = nm.nm_spmv_plan(R, K, B, nm.NM_EPI_SWIGLU)
+    assert (plan["kernel"], plan["tiles_per_step"], plan["x_steps_in_registers"]) == (nm.NM_KERNEL_TILE, 2, 4)
+    n = oracle.col_norm(synth.calib_acts(K, 46, R))
+    Wg, Wu = synth.weights(R, K, 46, 1), synth.weights(R, K, 46, 2)
+    gm, gv = oracle.prune_pack(Wg, n, 2, 4)
+    um, uv = oracle.prune_pack(Wu, n, 2, 4)
+    x = synth.decode_x(B, K, 46, B)
+    h = host_bf16(nm.nm_spmv_swiglu((dev_u32(gm), dev_bf16(gv)), (dev_u32(um), dev_bf16(uv)), dev_bf16(x)))
+    g, ag = oracle.spmv(gm, gv, x, K, nthreads=8)
+    u, au = oracle.spmv(um, uv, x, K, nthreads=8)
+    ref = oracle.swiglu(g, u)
+    ok = np.abs(bf16_as_f64(h) - ref) <= oracle.swiglu_tolerance(g, ag, u, au)
+    assert ok.all(), f"swiglu x in registers: {int((~ok).sum())} outside"
