@@ -52,6 +52,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "nm_oracle.c")
 _LIB = os.path.join(_HERE, "libnmoracle.so")
+# NM_ORACLE_LIB: another build of nm_oracle.c to load (the host-sanitizer run points it
+# at an instrumented one); build() always writes _LIB
+_LOAD = os.environ.get("NM_ORACLE_LIB") or _LIB
 
 _lib = None
 
@@ -79,9 +82,9 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB):
+    if _LOAD == _LIB and not os.path.exists(_LIB):
         build(force=True)
-    lib = ctypes.CDLL(_LIB)
+    lib = ctypes.CDLL(_LOAD)
     i64, p = ctypes.c_int64, ctypes.c_void_p
     lib.nmo_col_norm.argtypes = [p, i64, i64, i64, p]
     lib.nmo_prune_pack.argtypes = [p, i64, i64, i64, p, ctypes.c_int, ctypes.c_int, p, p]

@@ -12,7 +12,8 @@ import subprocess
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-LIB = os.path.join(ROOT, "bitmask_spmv_amd", "libnmspmv.so")
+# NM_SPMV_LIB: another build of the same ABI (the host-sanitizer run points it at its own)
+LIB = os.environ.get("NM_SPMV_LIB") or os.path.join(ROOT, "bitmask_spmv_amd", "libnmspmv.so")
 
 NM_OK, NM_ERR_NULL, NM_ERR_SHAPE, NM_ERR_PATTERN, NM_ERR_ALIGN, NM_ERR_WORKSPACE, NM_ERR_HIP = range(7)
 
@@ -303,3 +304,50 @@ def test_noalloc_rejects_bad_arguments_and_oversized_scratch(L):
     # exactly at the limit (262144 rows: 4 MiB) the shape is accepted; without a GPU the
     # call then fails at the device lookup, not at the size check
     assert L.nm_spmv_noalloc(A4, A16, 262144, K, A16, K, 2, A16, 262144, None) not in (NM_ERR_WORKSPACE, NM_OK)
+
+
+class _Plan(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int), ("threads", ctypes.c_int), ("grid_x", ctypes.c_int),
+                ("splits", ctypes.c_int), ("tiles_per_step", ctypes.c_int), ("x_steps_in_registers", ctypes.c_int),
+                ("lds_bytes", ctypes.c_size_t), ("workspace_bytes", ctypes.c_size_t)]
+
+
+def test_launch_plans_host_only(L):
+    """nm_spmv_plan / nm_spmv_multi_plan run the planners on the host (256 compute units
+    assumed without a GPU): word-per-lane walk at 1-2 tokens, matrix-core tiles at 8, x
+    kept in registers where each wave has exactly four steps per unit, workspace only with
+    split rows; invalid sizes, a NULL plan and an unknown epilogue are rejected."""
+    p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    L.nm_spmv_plan.argtypes, L.nm_spmv_plan.restype = [i64, i64, i32, i32, p], i32
+    L.nm_spmv_multi_plan.argtypes, L.nm_spmv_multi_plan.restype = [p, i32, i64, i32, p], i32
+    pl = _Plan()
+    for R, K in [(4096, 4096), (1024, 4096), (14336, 4096), (4096, 14336), (8192, 8192), (28672, 8192),
+                 (8192, 28672), (1, 32), (3, 28672)]:
+        for B in (1, 2, 4, 8):
+            for epi in (0, 1):
+                assert L.nm_spmv_plan(R, K, B, epi, ctypes.byref(pl)) == NM_OK, (R, K, B, epi)
+                assert pl.threads in (256, 512, 1024) and pl.grid_x >= 1 and pl.splits >= 1
+                assert (pl.workspace_bytes > 0) == (pl.splits > 1)
+                if pl.kernel == 1:
+                    assert pl.splits == 1 and pl.tiles_per_step in (1, 2) and pl.lds_bytes == 0
+                    assert pl.x_steps_in_registers in (0, 4)
+                else:
+                    assert pl.tiles_per_step == 0 and pl.x_steps_in_registers == 0 and pl.lds_bytes > 0
+                if B <= 2:
+                    assert pl.kernel == 0
+    assert L.nm_spmv_plan(14336, 4096, 8, 0, ctypes.byref(pl)) == NM_OK
+    assert (pl.kernel, pl.threads, pl.x_steps_in_registers) == (1, 512, 4)
+    assert L.nm_spmv_plan(28672, 8192, 8, 0, ctypes.byref(pl)) == NM_OK
+    assert (pl.kernel, pl.threads, pl.x_steps_in_registers) == (1, 1024, 4)
+    assert L.nm_spmv_plan(8192, 28672, 8, 0, ctypes.byref(pl)) == NM_OK
+    assert (pl.kernel, pl.tiles_per_step, pl.x_steps_in_registers) == (1, 2, 0)
+    rows = (ctypes.c_int64 * 3)(4096, 1024, 1024)
+    assert L.nm_spmv_multi_plan(rows, 3, 4096, 1, ctypes.byref(pl)) == NM_OK and pl.kernel == 0
+    assert L.nm_spmv_multi_plan(rows, 3, 4096, 8, ctypes.byref(pl)) == NM_OK and pl.kernel == 1
+    assert L.nm_spmv_plan(4096, 4096, 1, 0, None) == NM_ERR_NULL
+    assert L.nm_spmv_plan(4096, 4096, 1, 2, ctypes.byref(pl)) == NM_ERR_PATTERN
+    for R, K, B in [(0, 64, 1), (4, 48, 1), (4, 64, 0), (4, 64, 9), (1 << 31, 64, 1)]:
+        assert L.nm_spmv_plan(R, K, B, 0, ctypes.byref(pl)) == NM_ERR_SHAPE
+    assert L.nm_spmv_multi_plan(None, 3, 4096, 1, ctypes.byref(pl)) == NM_ERR_NULL
+    assert L.nm_spmv_multi_plan(rows, 0, 4096, 1, ctypes.byref(pl)) == NM_ERR_SHAPE
+    assert L.nm_spmv_multi_plan(rows, 9, 4096, 1, ctypes.byref(pl)) == NM_ERR_SHAPE
