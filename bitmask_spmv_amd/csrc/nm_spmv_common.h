@@ -94,19 +94,28 @@ template <int B, int NT, class F>
 __device__ __forceinline__ void stage_x(uint32_t *xs, const uint16_t *__restrict__ x, int64_t ldx, int w0, int nws,
                                         F &&first_round) {
     if constexpr (XLayout<B>::S == 1) {
-        // 16-byte loads; 8 bf16 per chunk, 4 chunks per 32-column block
+        // 16-byte loads; 8 bf16 per chunk, 4 chunks per 32-column block.  No load sits under
+        // a lane condition: the part of a round beyond the slice is skipped by a uniform
+        // test, and a thread whose chunk lies past the slice loads the slice's last chunk
+        // again (and stores nothing).  Each loaded register is then consumed by an empty
+        // asm statement outside the store's lane condition.  Otherwise the compiler is left
+        // unsure whether an x load is still in flight, and it waits for every load -- the
+        // first weight batch included -- before the next batch's loads go out: a memory
+        // round trip per wave.
         constexpr int kStage = 4;
         const int chunks = nws * 4;
+        const u32x4 *xc = reinterpret_cast<const u32x4 *>(x + (int64_t)w0 * 32);
         for (int i0 = 0; i0 < chunks || i0 == 0; i0 += NT * kStage) {
             u32x4 r[kStage];
 #pragma unroll
             for (int j = 0; j < kStage; ++j) {
-                const int i = i0 + j * NT + (int)threadIdx.x;
-                if (i < chunks) r[j] = reinterpret_cast<const u32x4 *>(x + (int64_t)w0 * 32)[i];
+                if (j > 0 && i0 + j * NT >= chunks) break;
+                r[j] = xc[min(i0 + j * NT + (int)threadIdx.x, chunks - 1)];
             }
             if (i0 == 0) first_round();
 #pragma unroll
             for (int j = 0; j < kStage; ++j) {
+                if (j > 0 && i0 + j * NT >= chunks) break;
                 const int i = i0 + j * NT + (int)threadIdx.x;
                 if (i < chunks) {
                     uint32_t *d = xs + (i >> 2) * XLayout<B>::kBlk + (i & 3) * 4;
@@ -115,6 +124,7 @@ __device__ __forceinline__ void stage_x(uint32_t *xs, const uint16_t *__restrict
                     d[2] = r[j].z;
                     d[3] = r[j].w;
                 }
+                asm volatile("" ::"v"(r[j].x), "v"(r[j].y), "v"(r[j].z), "v"(r[j].w));
             }
         }
     } else {
