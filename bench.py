@@ -167,8 +167,9 @@ def parse():
                     help="with --profile-kernel: launch this projection alone through nm_spmv (e.g. gate) "
                          "instead of the dominant launch")
     ap.add_argument("--profile-kernel", action="store_true",
-                    help="counter-collection mode: only the dominant launch shape (eager, rotated) plus a "
-                         "plain 256 MiB device copy used to calibrate the byte counters")
+                    help="profiling mode: only the dominant launch shape, rotated and timed as the "
+                         "per-launch tables time it, plus a plain 256 MiB device copy used to calibrate the "
+                         "byte counters")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="host-only: turn two rocprofv3 --pmc runs of --profile-kernel (FETCH_SIZE, "
                          "WRITE_SIZE) into profiles/traffic.json")
@@ -858,10 +859,11 @@ COPY_BYTES = 256 << 20
 
 
 def profile_kernel(args, torch, nm, synth, cfg, dev):
-    """Eager launches of the step's dominant launch (gate|up through nm_spmv_swiglu when the
-    layer set has them, else the largest single projection), first pattern, rotated over
-    >= 512 MB of distinct packed buffers, then one plain device-to-device copy of
-    COPY_BYTES: the reference for the counters."""
+    """The step's dominant launch (gate|up through nm_spmv_swiglu when the layer set has
+    them, else the largest single projection), first pattern, rotated over >= 512 MB of
+    distinct packed buffers and timed exactly as the per-launch tables time it (printed:
+    per-launch µs by HIP events), then one plain device-to-device copy of COPY_BYTES: the
+    reference for the counters."""
     projs = cfg["projs"]
     names = [p[0] for p in projs]
     N, M = cfg["patterns"][0]
@@ -896,17 +898,19 @@ def profile_kernel(args, torch, nm, synth, cfg, dev):
     src = torch.empty(COPY_BYTES // 2, dtype=torch.int16, device=dev).random_()
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
-    for i in range(args.steps):
-        packs = pool[i % n_pool]
+
+    def launch(packs):
         if glu:
-            nm.nm_spmv_swiglu(packs[0], packs[1], x, out=y, workspace=ws)
-        else:
-            nm.nm_spmv(*packs[0], x, out=y, workspace=ws)
-    torch.cuda.synchronize()
+            return lambda: nm.nm_spmv_swiglu(packs[0], packs[1], x, out=y, workspace=ws)
+        return lambda: nm.nm_spmv(*packs[0], x, out=y, workspace=ws)
+
+    # the bench's own timing of this launch (one graph of whole passes over the pool,
+    # warm-up and timed replays): the dispatches a profiler sees are those of the table
+    t = time_launches(torch, [launch(p) for p in pool])
     dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"profile_kernel": f"{label} {mats}x {R}x{K} {N}:{M} B={B}", "label": label,
-                      "launches": args.steps, "copy_bytes": COPY_BYTES}), flush=True)
+                      "per_launch_us_events": t, "copy_bytes": COPY_BYTES}), flush=True)
 
 
 def _pmc_rows(d):
@@ -942,12 +946,15 @@ def ingest_pmc(args, fetch_dir, write_dir):
     out = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         per = _pmc_rows(d)
-        spmv = [v for (disp, kn, grid, cn), v in per.items() if cn == counter and "spmv_kernel" in kn]
-        copies = [v for (disp, kn, grid, cn), v in per.items()
-                  if cn == counter and "copy" in kn.lower() and "nmk" not in kn]
+        spmv = [v for (disp, kn, grid, cn), v in per.items()
+                if cn == counter and ("spmv_kernel" in kn or "spmv_tile" in kn)]
+        # the calibration copy: the runtime's buffer copy, the last dispatch of the command
+        # (torch's own elementwise copy kernels, e.g. dtype conversions, do not count)
+        copies = [(int(disp), v) for (disp, kn, grid, cn), v in per.items()
+                  if cn == counter and "rocclr_copybuffer" in kn.lower()]
         if not spmv or not copies:
             raise SystemExit(f"{counter}: missing spmv ({len(spmv)}) or copy ({len(copies)}) dispatches")
-        copy_kib = max(copies)  # the 256 MiB copy is the largest copy dispatch
+        copy_kib = max(copies)[1]
         factor = COPY_BYTES / (copy_kib * 1024.0)
         spmv.sort()
         med = spmv[len(spmv) // 2]
@@ -1007,7 +1014,7 @@ def kernel_fingerprint() -> str:
     import hashlib
 
     h = hashlib.sha256()
-    for f in ("nm_spmv.hip", "nm_spmv_common.h", "nm_device.h"):
+    for f in ("nm_spmv.hip", "nm_spmv_tile.hip", "nm_spmv_common.h", "nm_device.h"):
         with open(os.path.join(ROOT, "bitmask_spmv_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
