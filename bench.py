@@ -287,8 +287,11 @@ def build_pools(c, projs, patterns, L, seed, with_dense=True):
             norm_ms += ev0.elapsed_time(ev1)
             for (N, M) in patterns:
                 if i < ns:
+                    # outputs allocated first: the events time the pack kernel, not the allocator
+                    mk = torch.empty((R, K // 32), dtype=torch.int32, device=c.dev)
+                    vl = torch.empty((R, K // 2), dtype=torch.bfloat16, device=c.dev)
                     ev0.record()
-                    pk = nm.nm_prune_pack(W, n, N, M)
+                    pk = nm.nm_prune_pack(W, n, N, M, masks=mk, values=vl)
                     ev1.record()
                     torch.cuda.synchronize()
                     pack_ms += ev0.elapsed_time(ev1)
@@ -398,7 +401,8 @@ def time_step(c, fns, steps, warmup):
 def per_layer_table(c, projs, patterns, pool_sparse, pool_dense, xs, ys, L, B, hipblaslt=False):
     """Every projection and every fused group timed alone over its rotation pool: sparse per
     pattern, dense, speedup (and hipBLASLt's torch.nn.functional.linear for single
-    projections when asked)."""
+    projections when asked, with the speedup against the faster of the two dense
+    baselines)."""
     torch = c.torch
     per = {}
     for grp in [[p] for p in projs] + [grp for grp in layer_groups(projs) if len(grp) > 1]:
@@ -428,6 +432,8 @@ def per_layer_table(c, projs, patterns, pool_sparse, pool_dense, xs, ys, L, B, h
                 d["hipblaslt_us"] = tl["us"]
                 for (N, M) in patterns:
                     d[f"{N}:{M}"]["speedup_vs_hipblaslt"] = round(tl["us"] / d[f"{N}:{M}"]["us"], 3)
+                    # against the faster of the two dense baselines
+                    d[f"{N}:{M}"]["speedup_vs_best_dense"] = round(min(tl["us"], t["us"]) / d[f"{N}:{M}"]["us"], 3)
         torch.cuda.synchronize()
     return per
 
@@ -466,7 +472,7 @@ def measure_other(c, name, L, batches, steps, warmup, seed, check):
         sparse, dense, sb, db = step_graphs(c, projs, patterns, pool_sparse, pool_dense, xs, ys, L, B)
         ms = time_step(c, sparse, steps, warmup)
         msd = time_step(c, dense, steps, warmup)
-        per = per_layer_table(c, projs, patterns, pool_sparse, pool_dense, xs, ys, L, B)
+        per = per_layer_table(c, projs, patterns, pool_sparse, pool_dense, xs, ys, L, B, hipblaslt=True)
         gbs = sb / (ms * 1e-3) / 1e9
         out["by_batch"][f"B{B}"] = {
             "step": {"launches": len(sparse), "ms": round(ms, 4), "GBs": round(gbs, 1),
