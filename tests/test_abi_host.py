@@ -275,8 +275,8 @@ def test_stream_read_rejects_bad_arguments(L):
     # one 2 KiB unit per wave (16 KiB per workgroup)
     assert L.nm_stream_read_sink_words(16) == 8
     assert L.nm_stream_read_sink_words(1 << 31) == 1024 * 8
-    assert L.nm_stream_read_sink_words(16384 * 3) == 3 * 8
-    assert L.nm_stream_read_sink_words(16384 * 3 + 16) == 4 * 8
+    assert L.nm_stream_read_sink_words(32768 * 3) == 3 * 8  # two 2 KiB units per wave at least
+    assert L.nm_stream_read_sink_words(32768 * 3 + 16) == 4 * 8
     words = L.nm_stream_read_sink_words(1 << 20)
     assert L.nm_stream_read(None, 1 << 20, A16, words, None) == NM_ERR_NULL
     assert L.nm_stream_read(A16, 1 << 20, None, words, None) == NM_ERR_NULL
