@@ -1,11 +1,13 @@
-// nm_spmv_tile.hip -- N:M sparse matrix times a small batch of input vectors (5..8 tokens)
-// with the products on the matrix cores of gfx950.
+// nm_spmv_tile.hip -- N:M sparse matrix times a small batch of input vectors (5..8 tokens,
+// and 3..4 on rows too wide for the other kernel's LDS) with the products on the matrix
+// cores of gfx950.
 //
 // What it computes: the same product as nm_spmv.hip, over the same packed operands --
 // one 32-bit mask word per 32 columns whose set bits pair, in increasing column order,
 // with the stored values ("SparseDecoding: Decoding-Aware Pruning ..." (ai.info summary),
 // Methodology Steps 2-3; "SparseDecoding:解码感知的准确高效大模型剪枝框架"
-// (paper.rainbus.top), 方法步骤详情 第四步) -- for B = 5..8 input vectors.
+// (paper.rainbus.top), 方法步骤详情 第四步) -- for B = 5..8 input vectors, and for B = 3..4
+// where a row's x no longer fits the word-per-lane kernel's LDS slice (K > 8192).
 //
 // Why a second kernel: with one lane per mask word, every kept weight costs a gather of
 // its input column for all B tokens from LDS (16 bytes at B = 8, at a data-dependent
@@ -33,7 +35,7 @@
 //   * the lane zeroes its word's 32 columns of the wave's dense tile and writes its 16
 //     kept values at their columns; four MFMAs then add the step into the wave's 16xB
 //     accumulator (lane l: rows 4*(l/16)..+3 of token l%16);
-//   * at the end of a tile the 8 waves' partial sums meet in LDS and are added in wave
+//   * at the end of a unit the W waves' partial sums meet in LDS and are added in wave
 //     order (deterministic), then rounded once to bf16 -- for the gated MLP combined
 //     first as silu(gate) * up.
 // Every load goes through a raw buffer descriptor whose base carries the step's column
