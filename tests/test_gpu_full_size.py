@@ -183,7 +183,7 @@ def plan_signature(kind, rows, K, B):
         p = nm.nm_spmv_multi_plan(list(rows), K, B)
     else:
         p = nm.nm_spmv_plan(rows[0], K, B, nm.NM_EPI_SWIGLU if kind == "swiglu" else nm.NM_EPI_NONE)
-    return (kind, B, p["kernel"], p["threads"], p["splits"] > 1, p["tiles_per_step"])
+    return (kind, B, p["kernel"], p["threads"], p["splits"] > 1, p["tiles_per_step"], p["x_steps_in_registers"])
 
 
 def coverage_cases():
