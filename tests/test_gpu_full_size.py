@@ -235,3 +235,36 @@ def test_bench_launch_class_parity(case):
     else:
         for i, (y, (yref, absum)) in enumerate(zip(outs, refs)):
             assert_within(host_bf16(y), yref, absum, f"class {sig} matrix {i}")
+
+
+@pytest.mark.parametrize("B", [1, 8])
+def test_values_beyond_2gib(B):
+    """A matrix whose packed values pass 2^31 bytes (270000 x 8192: 2.2 GB of values, 4.4 GB
+    of dense weights), so row offsets need more than 32 bits in the pack and in both walks
+    (B = 1: word-per-lane; B = 8: matrix cores, 16875 tiles, several units per workgroup):
+    masks and values bit-exact and outputs within tolerance on sampled rows, the first and
+    last rows included."""
+    R, K = 270000, 8192
+    say("beyond 2 GiB", R, K, B)
+    plan = nm.nm_spmv_plan(R, K, B)
+    assert plan["kernel"] == (nm.NM_KERNEL_TILE if B == 8 else nm.NM_KERNEL_WORD)
+    Wd = synth.device_weights(R, K, 0, 61, R, K)
+    Xd = synth.device_calib_acts(K, 0, 61, K)
+    n = nm.nm_col_norm(Xd)
+    masks, values = nm.nm_prune_pack(Wd, n, 8, 16)
+    assert values.numel() * 2 > 2 ** 31
+    xd = synth.device_decode_x(B, K, 0, 61, B)
+    y = nm.nm_spmv(masks, values, xd)
+    torch.cuda.synchronize()
+    g = np.random.default_rng(61)
+    rows = np.unique(np.concatenate([[0, 1, R // 2, R - 2, R - 1], g.choice(R, size=250, replace=False)]))
+    ridx = torch.from_numpy(rows).cuda()
+    W = host_bf16(Wd.index_select(0, ridx))
+    del Wd
+    nref = oracle.col_norm(host_bf16(Xd))
+    assert (host_f32(n).view(np.uint32) == nref.view(np.uint32)).all(), "column norms"
+    mref, vref = oracle.prune_pack(W, nref, 8, 16)
+    assert (host_u32(masks.index_select(0, ridx)) == mref).all(), "masks"
+    assert (host_bf16(values.index_select(0, ridx)) == vref).all(), "values"
+    yref, absum = oracle.spmv(mref, vref, host_bf16(xd), K, nthreads=THREADS)
+    assert_within(host_bf16(y)[:, rows], yref, absum, f"{R}x{K} B={B}")
