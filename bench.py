@@ -136,6 +136,26 @@ def layer_groups(projs):
     return groups
 
 
+def best_dense_launch_sum(per, projs, patterns):
+    """The fused step's launches from the per-launch table, against the faster dense
+    baseline per launch: for each launch group, min(this repository's dense launch,
+    hipBLASLt's single projections summed -- no fused equivalent there, so the gated MLP's
+    SiLU-multiply is left out in its favour).  Returns {"sparse_us", "best_dense_us",
+    "speedup"} for the first pattern, or None when hipBLASLt was not measured."""
+    N, M = patterns[0]
+    sp = bd = 0.0
+    for grp in layer_groups(projs):
+        d = per.get(group_label(grp))
+        if not d or f"{N}:{M}" not in d or "dense_us" not in d:
+            return None
+        hip = [per.get(pr[0], {}).get("hipblaslt_us") for pr in grp]
+        if any(h is None for h in hip):
+            return None
+        sp += d[f"{N}:{M}"]["us"]
+        bd += min(d["dense_us"], sum(hip))
+    return {"sparse_us": round(sp, 3), "best_dense_us": round(bd, 3), "speedup": round(bd / sp, 3)}
+
+
 def pctl(v, q):
     """Nearest-rank percentile."""
     s = sorted(v)
@@ -477,10 +497,13 @@ def measure_other(c, name, L, batches, steps, warmup, seed, check):
         out["by_batch"][f"B{B}"] = {
             "step": {"launches": len(sparse), "ms": round(ms, 4), "GBs": round(gbs, 1),
                      "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1), "dense_ms": round(msd, 4),
-                     "speedup_vs_dense": round(msd * len(patterns) / ms, 3)},
+                     "speedup_vs_dense": round(msd * len(patterns) / ms, 3),
+                     "launch_sum_vs_best_dense": best_dense_launch_sum(per, projs, patterns)},
             "per_layer": per}
+        lsum = out["by_batch"][f"B{B}"]["step"]["launch_sum_vs_best_dense"]
         log(f"{name} B={B}: step {ms * 1e3:.1f} us ({100 * gbs / HBM_PEAK_GBS:.1f}% of peak, "
-            f"{msd * len(patterns) / ms:.2f}x dense); " + ", ".join(
+            f"{msd * len(patterns) / ms:.2f}x dense"
+            + (f", launches {lsum['speedup']:.2f}x the faster dense per launch" if lsum else "") + "); " + ", ".join(
                 f"{k} {v[p]['us']} us ({v[p]['pct_peak']}%)" for k, v in per.items()
                 for p in [f"{N}:{M}" for N, M in patterns[:1]]))
         del xs, ys, sparse, dense
@@ -839,7 +862,8 @@ def main():
                  "bytes": fused_sparse_bytes,
                  "dense_ms": round(ms_fused_dense, 4),
                  "dense_GBs": round(fused_dense_bytes / (ms_fused_dense * 1e-3) / 1e9, 1),
-                 "speedup_vs_dense": round(ms_fused_dense * len(patterns) / ms_fused, 3)},
+                 "speedup_vs_dense": round(ms_fused_dense * len(patterns) / ms_fused, 3),
+                 "launch_sum_vs_best_dense": best_dense_launch_sum(per, projs, patterns)},
         "unfused_step": {"launches": n_unfused, "ms": round(ms_sparse, 4),
                          "bytes": step_sparse_bytes,
                          "GBs": round(step_sparse_bytes / (ms_sparse * 1e-3) / 1e9, 1),
