@@ -28,14 +28,14 @@ __all__ = [
     "nm_spmv_unstructured_workspace_bytes", "nm_unpack_unstructured", "nm_hessian", "nm_obs_inverse_factor",
     "nm_obs_inverse_factor_workspace_bytes", "nm_sparsegpt_prune_pack", "nm_sparsegpt_workspace_bytes",
     "nm_stream_read", "nm_stream_read_sink_words", "nm_spmv_plan", "nm_spmv_multi_plan", "NM_EPI_NONE",
-    "NM_EPI_SWIGLU", "NM_KERNEL_WORD", "NM_KERNEL_TILE", "nm_spmv_noalloc",
+    "NM_EPI_SWIGLU", "NM_KERNEL_WORD", "NM_KERNEL_TILE", "NM_KERNEL_WORD_HALF_ROWS", "nm_spmv_noalloc",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnmspmv.so")
 NM_PATTERNS = ((2, 4), (4, 8), (8, 16), (16, 32))
 NM_META_BITMASK, NM_META_U8_OFFSET, NM_META_I32_INDEX = 0, 1, 2
 NM_EPI_NONE, NM_EPI_SWIGLU = 0, 1
-NM_KERNEL_WORD, NM_KERNEL_TILE = 0, 1
+NM_KERNEL_WORD, NM_KERNEL_TILE, NM_KERNEL_WORD_HALF_ROWS = 0, 1, 2
 
 _STATUS = {0: "NM_OK", 1: "NM_ERR_NULL", 2: "NM_ERR_SHAPE", 3: "NM_ERR_PATTERN", 4: "NM_ERR_ALIGN",
            5: "NM_ERR_WORKSPACE", 6: "NM_ERR_HIP"}

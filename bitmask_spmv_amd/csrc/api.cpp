@@ -80,6 +80,8 @@ nmk::MvPlan spmv_set_plan(const nmk::SpmvSet &set, int fmt, int64_t K, int64_t l
         if (B >= nmk::kTileMinB || (word.splits > 1 && R >= 2 * cu))
             return nmk::plan_spmv_tile(set, K, B, device_info(), epi);
     }
+    if (set.P == 1 && epi == nmk::kEpiNone && fmt == nmk::kMetaBitmask)
+        return nmk::plan_spmv_half(word, R, K, B, device_info());
     return word;
 }
 
@@ -392,7 +394,7 @@ nm_status nm_spmv_swiglu(const uint32_t *gate_masks, const nm_bf16 *gate_values,
 }
 
 static void fill_plan(const nmk::MvPlan &p, nm_launch_plan *out) {
-    out->kernel = p.tile ? NM_KERNEL_TILE : NM_KERNEL_WORD;
+    out->kernel = p.tile ? NM_KERNEL_TILE : (p.half ? NM_KERNEL_WORD_HALF_ROWS : NM_KERNEL_WORD);
     out->threads = p.threads;
     out->grid_x = p.grid_x;
     out->splits = p.splits;

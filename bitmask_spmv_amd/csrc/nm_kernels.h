@@ -30,6 +30,7 @@ struct MvPlan {
     int tile = 0;           // 1: the matrix-core tile kernel (nm_spmv_tile.hip), 16-row tiles (threads / 64 waves)
     int tiles = 0;          // tile kernel: number of units (16 or 32 rows; unroll = tiles per unit)
     int xreg = 0;           // tile kernel: steps per wave and unit whose x operand stays in registers (0: none)
+    int half = 0;           // 1: the half-row walk (each row split between two waves of a 16-wave workgroup)
 };
 
 // Row epilogues of the matrix-vector kernels.  kEpiNone: every row's total is one
@@ -75,6 +76,10 @@ struct DenseSet {
 // fmt: the launchs metadata format (the planner picks 1024-thread workgroups only for
 // kernels that fit them without spilling).
 MvPlan plan_spmv(int64_t R, int64_t K, int B, const DeviceInfo &dev, int fmt = kMetaBitmask);
+// The half-row walk for a one-matrix bitmask launch where it applies (else `word` as is):
+// one token, rows of at least 7 strips of 64 words, one row per wave in `word`, and at
+// least two 16-wave workgroups per CU.
+MvPlan plan_spmv_half(const MvPlan &word, int64_t R, int64_t K, int B, const DeviceInfo &dev);
 size_t spmv_lds_per_word(int B);  // LDS bytes of x per 32-column block
 // Fixed device scratch for callers that cannot allocate (nm_spmv_noalloc): its device
 // address on the current device (looked up once per device), kSpmvScratchBytes long.

@@ -25,7 +25,9 @@
 //     dword and feeds v_dot2_f32_bf16 with the matching packed value pair.
 //   * each wave owns whole rows (or row slices); the row total is a wave64 reduction.
 //     Slices of a row (when splits > 1) go to fp32 workspace and are added in slice
-//     order by a second kernel (deterministic, no atomics).
+//     order by a second kernel (deterministic, no atomics).  One-token rows of 7 or more
+//     strips may instead be walked by two waves of a workgroup, half the strips each,
+//     the two totals added in LDS in half order.
 //   * one kernel serves every 50% pattern (2:4 ... 16:32): the M of the pattern never
 //     enters the traversal.  Several matrices that share x run in one launch (SpmvSet).
 #include <atomic>
@@ -330,6 +332,70 @@ __global__ __launch_bounds__(NT, NT == 1024 ? 8 : 1) void spmv_kernel(const void
     }
 }
 
+// Half-row walk (one matrix, bitmask, one token; rows of at least 7 strips, one row per
+// wave pair).  The 16 waves of a workgroup cover 8 rows: wave w walks the first (w < 8)
+// or the second half of the strips of row blockIdx.x * 8 + w % 8, so a CU holds twice the
+// waves it would with one row per wave and each wave's chain of strips is half as long.
+// The halves' totals meet in LDS without a barrier: lane 0 of each wave stores its total
+// and then increments the row's counter (workgroup-scope release/acquire); the second to
+// arrive adds the two totals in half order (deterministic) and stores the row.
+constexpr int kHalfThreads = 1024;
+constexpr int kHalfRows = kHalfThreads / kWave / 2;  // rows per workgroup
+
+template <int B, int EPI>
+__global__ __launch_bounds__(kHalfThreads, 8) void spmv_half_kernel(const void *meta0, const uint16_t *values0, int R,
+                                                                    int KW, const uint16_t *__restrict__ x,
+                                                                    int64_t ldx, const SpmvSet set) {
+    static_assert(EPI == kEpiOne, "one matrix per launch");
+    extern __shared__ uint32_t xs[];  // x [KW][kBlk], then totals [rows][2][B], then counters [rows]
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int half = wave / kHalfRows, rl = wave - half * kHalfRows;
+    const int nb = (KW + kWave - 1) / kWave, h0 = (nb + 1) / 2;
+    const int first = half ? h0 : 0, ns = half ? nb - h0 : h0;  // this wave's strips
+    const int row = blockIdx.x * kHalfRows + rl;
+    const int live = row < R ? KW : 0;  // words to load: none for rows past the matrix
+    const int rr = min(row, R - 1);
+    float *tot = reinterpret_cast<float *>(xs + (size_t)KW * XLayout<B>::kBlk);
+    uint32_t *cnt = reinterpret_cast<uint32_t *>(tot + kHalfRows * 2 * B);
+    if ((int)threadIdx.x < kHalfRows) cnt[threadIdx.x] = 0u;
+
+    Batch<kMetaBitmask> bufA, bufB;
+    stage_x<B, kHalfThreads>(xs, x, ldx, 0, KW, [&] {
+        load_row_batch<kMetaBitmask, EPI>(bufA, set, meta0, values0, rr, KW, 0, live, first * kWave, lane);
+    });
+    __syncthreads();
+    float acc[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) acc[b] = 0.f;
+    // two buffers in turn, whole pairs in the loop and the odd last strip after it, as in
+    // spmv_kernel; the strip loaded past this half has no words (no memory traffic)
+    int t = 0;
+    for (; t + 1 < ns; t += 2) {
+        load_row_batch<kMetaBitmask, EPI>(bufB, set, meta0, values0, rr, KW, 0, live, (first + t + 1) * kWave, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        walk_batch<kMetaBitmask, B>(bufA, xs, KW, acc);
+        load_row_batch<kMetaBitmask, EPI>(bufA, set, meta0, values0, rr, KW, 0, t + 2 < ns ? live : 0,
+                                          (first + t + 2) * kWave, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        walk_batch<kMetaBitmask, B>(bufB, xs, KW, acc);
+    }
+    if (t < ns) walk_batch<kMetaBitmask, B>(bufA, xs, KW, acc);
+    float v[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) v[b] = wave_sum(acc[b]);
+    if (lane != 0 || row >= R) return;
+#pragma unroll
+    for (int b = 0; b < B; ++b) tot[(rl * 2 + half) * B + b] = v[b];
+    const uint32_t prev = __hip_atomic_fetch_add(&cnt[rl], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (prev != 1u) return;  // the other half is still walking: it stores the row
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+        const float o = tot[(rl * 2 + (half ^ 1)) * B + b];
+        set.y[0][(int64_t)b * set.ldy[0] + row] = f32_to_bf16_rne(half ? o + v[b] : v[b] + o);
+    }
+}
+
 // Second pass of split rows: add the slices in order, round once to bf16.
 template <int B>
 __global__ __launch_bounds__(256) void split_finish_kernel(const float *__restrict__ partial, int S,
@@ -404,9 +470,33 @@ hipError_t launch_fbn(const MvPlan &p, const SpmvSet &set, int64_t K, const uint
     return hipGetLastError();
 }
 
+template <int B>
+hipError_t launch_half(const MvPlan &p, const SpmvSet &set, int64_t K, const uint16_t *x, int64_t ldx,
+                       hipStream_t st) {
+    static std::atomic<uint64_t> done{0};
+    if (p.lds_bytes > 64 * 1024) {
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return e;
+        const uint64_t bit = 1ull << (dev & 63);
+        if (!(done.load(std::memory_order_acquire) & bit)) {
+            e = hipFuncSetAttribute((const void *)spmv_half_kernel<B, kEpiOne>,
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsCap);
+            if (e != hipSuccess) return e;
+            done.fetch_or(bit, std::memory_order_acq_rel);
+        }
+    }
+    hipLaunchKernelGGL((spmv_half_kernel<B, kEpiOne>), dim3(p.grid_x), dim3(kHalfThreads), p.lds_bytes, st,
+                       set.meta[0], set.values[0], set.row0[set.P], (int)(K / 32), x, ldx, set);
+    return hipGetLastError();
+}
+
 template <int FMT, int B, int EPI>
 hipError_t launch_fb(const MvPlan &p, const SpmvSet &set, int64_t K, const uint16_t *x, int64_t ldx, float *ws,
                      hipStream_t st) {
+    if constexpr (FMT == kMetaBitmask && B == 1 && EPI == kEpiOne)
+        if (p.half) return launch_half<B>(p, set, K, x, ldx, st);
+    if (p.half) return hipErrorInvalidValue;
     if constexpr (wide_ok(FMT, B))
         if (p.threads == 1024) return launch_fbn<FMT, B, 1024, EPI>(p, set, K, x, ldx, ws, st);
     if (p.threads == 256) return launch_fbn<FMT, B, 256, EPI>(p, set, K, x, ldx, ws, st);
@@ -515,6 +605,25 @@ MvPlan plan_spmv(int64_t R, int64_t K, int B, const DeviceInfo &dev, int fmt) {
     p.grid_x = (int)gx;
     p.unroll = 1;
     p.ws_bytes = splits > 1 ? (size_t)splits * B * R * sizeof(float) : 0;
+    return p;
+}
+
+MvPlan plan_spmv_half(const MvPlan &word, int64_t R, int64_t K, int B, const DeviceInfo &dev) {
+    // Rows of 7+ strips that the one-row-per-wave plan gives a wave at most one of, and
+    // enough of them for two 16-wave workgroups per CU: split each row between two waves
+    // (8B down 4096 x 14336: 12.61 -> 12.40 us; Qwen3-14B down 5120 x 17408: 19.58 ->
+    // 19.19 us; rows of 4 strips and B = 2 were slower, 70B down even).
+    const int64_t cu = dev.num_cu > 0 ? dev.num_cu : 256;
+    const int64_t KW = K / 32, nb = (KW + kWave - 1) / kWave;
+    const size_t extra = (size_t)kHalfRows * 2 * B * 4 + kHalfRows * 4;
+    if (B != 1 || word.tile || word.splits != 1 || nb < 7 || R < 2 * cu * kHalfRows ||
+        R > (int64_t)word.grid_x * (word.threads / kWave) || word.lds_bytes + extra > kLdsCap)
+        return word;
+    MvPlan p = word;
+    p.half = 1;
+    p.threads = kHalfThreads;
+    p.grid_x = (int)((R + kHalfRows - 1) / kHalfRows);
+    p.lds_bytes = word.lds_bytes + extra;
     return p;
 }
 

@@ -206,9 +206,12 @@ nm_status nm_spmv_swiglu(const uint32_t *gate_masks, const nm_bf16 *gate_values,
  * reject; *plan is written only on NM_OK.
  */
 typedef enum { NM_EPI_NONE = 0, NM_EPI_SWIGLU = 1 } nm_epilogue;
-typedef enum { NM_KERNEL_WORD = 0, NM_KERNEL_TILE = 1 } nm_kernel_kind;
+/* NM_KERNEL_WORD_HALF_ROWS: the word-per-lane walk with every row split between two
+   waves of a workgroup (one matrix, one token, rows of 7+ strips of 64 words). */
+typedef enum { NM_KERNEL_WORD = 0, NM_KERNEL_TILE = 1, NM_KERNEL_WORD_HALF_ROWS = 2 } nm_kernel_kind;
 typedef struct {
-    int kernel;             /* nm_kernel_kind: word-per-lane walk, or the matrix-core tile walk */
+    int kernel;             /* nm_kernel_kind: word-per-lane walk (whole or half rows per wave), or the
+                               matrix-core tile walk */
     int threads;            /* workgroup size */
     int grid_x;             /* workgroups per row slice (word) / resident workgroups (tile) */
     int splits;             /* row slices; > 1: fp32 partial sums and an ordered second pass */

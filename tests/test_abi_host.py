@@ -333,14 +333,20 @@ def test_launch_plans_host_only(L):
                     assert pl.x_steps_in_registers in (0, 4)
                 else:
                     assert pl.tiles_per_step == 0 and pl.x_steps_in_registers == 0 and pl.lds_bytes > 0
+                if pl.kernel == 2:  # half rows: one matrix, one token, no split
+                    assert B == 1 and epi == 0 and pl.splits == 1 and pl.threads == 1024
                 if B <= 2:
-                    assert pl.kernel == 0
+                    assert pl.kernel in (0, 2)
     assert L.nm_spmv_plan(14336, 4096, 8, 0, ctypes.byref(pl)) == NM_OK
     assert (pl.kernel, pl.threads, pl.x_steps_in_registers) == (1, 512, 4)
     assert L.nm_spmv_plan(28672, 8192, 8, 0, ctypes.byref(pl)) == NM_OK
     assert (pl.kernel, pl.threads, pl.x_steps_in_registers) == (1, 1024, 4)
     assert L.nm_spmv_plan(8192, 28672, 8, 0, ctypes.byref(pl)) == NM_OK
     assert (pl.kernel, pl.tiles_per_step, pl.x_steps_in_registers) == (1, 2, 0)
+    assert L.nm_spmv_plan(4096, 14336, 1, 0, ctypes.byref(pl)) == NM_OK
+    assert (pl.kernel, pl.threads, pl.grid_x) == (2, 1024, 512)
+    assert L.nm_spmv_plan(4096, 14336, 2, 0, ctypes.byref(pl)) == NM_OK and pl.kernel == 0
+    assert L.nm_spmv_plan(4096, 14336, 1, 1, ctypes.byref(pl)) == NM_OK and pl.kernel == 0  # gated MLP
     rows = (ctypes.c_int64 * 3)(4096, 1024, 1024)
     assert L.nm_spmv_multi_plan(rows, 3, 4096, 1, ctypes.byref(pl)) == NM_OK and pl.kernel == 0
     assert L.nm_spmv_multi_plan(rows, 3, 4096, 8, ctypes.byref(pl)) == NM_OK and pl.kernel == 1

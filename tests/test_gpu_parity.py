@@ -205,6 +205,55 @@ def test_spmv_wide_workgroups(R, K, B, plan):
     assert_within(host_bf16(yd), ydref, adabs, f"dense wide R={R} K={K} B={B}")
 
 
+# One token, one matrix, rows of 7+ strips of 64 words and at least 4096 of them: each row
+# is split between two waves of a 16-wave workgroup (the half-row walk), whose totals
+# meet in LDS.  Ragged last workgroup (4097 rows), a ragged last strip (K = 17408: 8.5
+# strips per row), every pattern, integer-exact and random data, repeat runs identical,
+# a one-matrix nm_spmv_multi identical to nm_spmv, and the plan at the boundaries.
+HALF = [(4096, 14336, 2, 4), (4097, 14336, 8, 16), (5000, 17408, 16, 32), (4096, 28672, 4, 8)]
+
+
+@pytest.mark.parametrize("R,K,N,M", HALF)
+def test_spmv_half_rows(R, K, N, M):
+    p = nm.nm_spmv_plan(R, K, 1)
+    say("spmv half rows", R, K, N, M, p)
+    assert (p["kernel"], p["threads"], p["grid_x"], p["splits"]) == (nm.NM_KERNEL_WORD_HALF_ROWS, 1024, (R + 7) // 8, 1)
+    n = oracle.col_norm(synth.calib_acts(K, 62, R, K))
+    # integer-valued operands: the result equals the oracle exactly
+    Wt = synth.ternary((R, K), 62, R, K)
+    xt = synth.ternary_sparse((1, K), 1024 / K, 63, R, K)
+    mt, vt = oracle.prune_pack(Wt, n, N, M)
+    yt = host_bf16(nm.nm_spmv(dev_u32(mt), dev_bf16(vt), dev_bf16(xt)))
+    ytref, _ = oracle.spmv(mt, vt, xt, K, nthreads=8)
+    assert np.abs(ytref).max() <= 256
+    got = bf16_as_f64(yt)
+    assert (got == ytref).all(), f"{int((got != ytref).sum())} of {got.size} differ"
+    # random data within tolerance; repeats and the one-matrix multi launch identical
+    W = synth.weights(R, K, 64, R, K)
+    mref, vref = oracle.prune_pack(W, n, N, M)
+    x = synth.decode_x(1, K, 64, R, K)
+    md, vd, xd = dev_u32(mref), dev_bf16(vref), dev_bf16(x)
+    y = nm.nm_spmv(md, vd, xd)
+    y2 = nm.nm_spmv(md, vd, xd)
+    ym = nm.nm_spmv_multi([(md, vd)], xd)[0]
+    yref, absum = oracle.spmv(mref, vref, x, K, nthreads=8)
+    assert_within(host_bf16(y), yref, absum, f"half rows R={R} K={K} {N}:{M}")
+    assert (host_bf16(y) == host_bf16(y2)).all()
+    assert (host_bf16(y) == host_bf16(ym)).all()
+
+
+def test_spmv_half_rows_plan_boundaries():
+    """The half-row walk is taken only at one token, one matrix, 7+ strips per row and
+    4096+ rows; neighbouring shapes keep the whole-row walk."""
+    say("spmv half rows plan boundaries")
+    assert nm.nm_spmv_plan(4096, 14336, 1)["kernel"] == nm.NM_KERNEL_WORD_HALF_ROWS
+    assert nm.nm_spmv_plan(4095, 14336, 1)["kernel"] == nm.NM_KERNEL_WORD
+    assert nm.nm_spmv_plan(4096, 14336, 2)["kernel"] == nm.NM_KERNEL_WORD
+    assert nm.nm_spmv_plan(8192, 8192, 1)["kernel"] == nm.NM_KERNEL_WORD  # 4 strips per row
+    assert nm.nm_spmv_plan(4096, 14336, 1, nm.NM_EPI_SWIGLU)["kernel"] == nm.NM_KERNEL_WORD
+    assert nm.nm_spmv_multi_plan([2048, 2048], 14336, 1)["kernel"] == nm.NM_KERNEL_WORD
+
+
 @pytest.mark.parametrize("N,M", PATTERNS)
 def test_spmv_integer_exact(N, M):
     """Ternary weights and inputs: every partial sum is an integer <= K/2 in
