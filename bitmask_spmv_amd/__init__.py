@@ -28,14 +28,15 @@ __all__ = [
     "nm_spmv_unstructured_workspace_bytes", "nm_unpack_unstructured", "nm_hessian", "nm_obs_inverse_factor",
     "nm_obs_inverse_factor_workspace_bytes", "nm_sparsegpt_prune_pack", "nm_sparsegpt_workspace_bytes",
     "nm_stream_read", "nm_stream_read_sink_words", "nm_spmv_plan", "nm_spmv_multi_plan", "NM_EPI_NONE",
-    "NM_EPI_SWIGLU", "NM_KERNEL_WORD", "NM_KERNEL_TILE", "NM_KERNEL_WORD_HALF_ROWS", "nm_spmv_noalloc",
+    "NM_EPI_SWIGLU", "NM_KERNEL_WORD", "NM_KERNEL_TILE", "NM_KERNEL_WORD_HALF_ROWS", "NM_KERNEL_WORD_STRIPS",
+    "nm_spmv_noalloc",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnmspmv.so")
 NM_PATTERNS = ((2, 4), (4, 8), (8, 16), (16, 32))
 NM_META_BITMASK, NM_META_U8_OFFSET, NM_META_I32_INDEX = 0, 1, 2
 NM_EPI_NONE, NM_EPI_SWIGLU = 0, 1
-NM_KERNEL_WORD, NM_KERNEL_TILE, NM_KERNEL_WORD_HALF_ROWS = 0, 1, 2
+NM_KERNEL_WORD, NM_KERNEL_TILE, NM_KERNEL_WORD_HALF_ROWS, NM_KERNEL_WORD_STRIPS = 0, 1, 2, 3
 
 _STATUS = {0: "NM_OK", 1: "NM_ERR_NULL", 2: "NM_ERR_SHAPE", 3: "NM_ERR_PATTERN", 4: "NM_ERR_ALIGN",
            5: "NM_ERR_WORKSPACE", 6: "NM_ERR_HIP"}
@@ -55,7 +56,7 @@ class _SpmvMatrix(ctypes.Structure):
 class _LaunchPlan(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int), ("threads", ctypes.c_int), ("grid_x", ctypes.c_int),
                 ("splits", ctypes.c_int), ("tiles_per_step", ctypes.c_int), ("x_steps_in_registers", ctypes.c_int),
-                ("lds_bytes", ctypes.c_size_t), ("workspace_bytes", ctypes.c_size_t)]
+                ("rows_per_group", ctypes.c_int), ("lds_bytes", ctypes.c_size_t), ("workspace_bytes", ctypes.c_size_t)]
 
 
 class _DenseMatrix(ctypes.Structure):
@@ -588,7 +589,7 @@ def _plan_dict(pl: _LaunchPlan) -> dict:
 def nm_spmv_plan(R: int, K: int, B: int, epilogue: int = NM_EPI_NONE) -> dict:
     """Launch plan of nm_spmv (or nm_spmv_swiglu with epilogue=NM_EPI_SWIGLU, R rows each)
     on the current device: kernel, threads, grid_x, splits, tiles_per_step,
-    x_steps_in_registers, lds_bytes, workspace_bytes.  Host only."""
+    x_steps_in_registers, rows_per_group, lds_bytes, workspace_bytes.  Host only."""
     pl = _LaunchPlan()
     _check(lib.nm_spmv_plan(int(R), int(K), int(B), int(epilogue), ctypes.byref(pl)))
     return _plan_dict(pl)

@@ -81,7 +81,7 @@ nmk::MvPlan spmv_set_plan(const nmk::SpmvSet &set, int fmt, int64_t K, int64_t l
             return nmk::plan_spmv_tile(set, K, B, device_info(), epi);
     }
     if (set.P == 1 && epi == nmk::kEpiNone && fmt == nmk::kMetaBitmask)
-        return nmk::plan_spmv_half(word, R, K, B, device_info());
+        return nmk::plan_spmv_one(word, R, K, B, device_info());
     return word;
 }
 
@@ -394,12 +394,16 @@ nm_status nm_spmv_swiglu(const uint32_t *gate_masks, const nm_bf16 *gate_values,
 }
 
 static void fill_plan(const nmk::MvPlan &p, nm_launch_plan *out) {
-    out->kernel = p.tile ? NM_KERNEL_TILE : (p.half ? NM_KERNEL_WORD_HALF_ROWS : NM_KERNEL_WORD);
+    out->kernel = p.tile                             ? NM_KERNEL_TILE
+                  : p.walk == nmk::kWalkHalf   ? NM_KERNEL_WORD_HALF_ROWS
+                  : p.walk == nmk::kWalkStrips ? NM_KERNEL_WORD_STRIPS
+                                               : NM_KERNEL_WORD;
     out->threads = p.threads;
     out->grid_x = p.grid_x;
     out->splits = p.splits;
     out->tiles_per_step = p.tile ? p.unroll : 0;
     out->x_steps_in_registers = p.tile ? p.xreg : 0;
+    out->rows_per_group = p.walk == nmk::kWalkStrips ? p.rows_per_group : 0;
     out->lds_bytes = p.tile ? 0 : p.lds_bytes;
     out->workspace_bytes = p.ws_bytes;
 }

@@ -30,8 +30,17 @@ struct MvPlan {
     int tile = 0;           // 1: the matrix-core tile kernel (nm_spmv_tile.hip), 16-row tiles (threads / 64 waves)
     int tiles = 0;          // tile kernel: number of units (16 or 32 rows; unroll = tiles per unit)
     int xreg = 0;           // tile kernel: steps per wave and unit whose x operand stays in registers (0: none)
-    int half = 0;           // 1: the half-row walk (each row split between two waves of a 16-wave workgroup)
+    int walk = 0;           // one-token single-matrix walks (nm_spmv.hip): kWalkRows, kWalkHalf, kWalkStrips
+    int rows_per_group = 0; // kWalkStrips: consecutive rows owned by one workgroup
 };
+
+// Word-per-lane walks of a launch.  kWalkRows: each wave walks whole rows (any batch
+// size, any set of matrices).  kWalkHalf: one matrix, one token; each row is split
+// between two waves of a 16-wave workgroup.  kWalkStrips: one matrix, one token; a
+// workgroup owns consecutive rows and deals their strips to its waves in turn.
+constexpr int kWalkRows = 0;
+constexpr int kWalkHalf = 1;
+constexpr int kWalkStrips = 2;
 
 // Row epilogues of the matrix-vector kernels.  kEpiNone: every row's total is one
 // output.  kEpiSwiGLU: the set is the gate (matrix 0) and up (matrix 1) projections of a
@@ -76,10 +85,9 @@ struct DenseSet {
 // fmt: the launchs metadata format (the planner picks 1024-thread workgroups only for
 // kernels that fit them without spilling).
 MvPlan plan_spmv(int64_t R, int64_t K, int B, const DeviceInfo &dev, int fmt = kMetaBitmask);
-// The half-row walk for a one-matrix bitmask launch where it applies (else `word` as is):
-// one token, rows of at least 7 strips of 64 words, one row per wave in `word`, and at
-// least two 16-wave workgroups per CU.
-MvPlan plan_spmv_half(const MvPlan &word, int64_t R, int64_t K, int B, const DeviceInfo &dev);
+// The walk of a one-matrix bitmask launch: the half-row or the strip walk where one of
+// them applies (one token, no split rows), else `word` as is.
+MvPlan plan_spmv_one(const MvPlan &word, int64_t R, int64_t K, int B, const DeviceInfo &dev);
 size_t spmv_lds_per_word(int B);  // LDS bytes of x per 32-column block
 // Fixed device scratch for callers that cannot allocate (nm_spmv_noalloc): its device
 // address on the current device (looked up once per device), kSpmvScratchBytes long.

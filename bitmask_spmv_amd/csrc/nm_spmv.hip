@@ -396,6 +396,96 @@ __global__ __launch_bounds__(kHalfThreads, 8) void spmv_half_kernel(const void *
     }
 }
 
+// Strip walk (one matrix, bitmask, one token).  A workgroup of NT threads owns rpw
+// consecutive rows; their strips, taken row by row as one sequence, are dealt to the
+// waves in turn (wave w walks strips w, w + W, w + 2W, ... of the sequence), so every
+// wave of every workgroup has the same number of strips to within one whatever R, and the
+// W waves of a workgroup read W adjacent pieces of one contiguous stretch of the matrix
+// at about the same time.  Each strip's total (a wave reduction) goes to LDS; after a
+// barrier every row adds its strips in strip order (deterministic) and stores.  The
+// planner takes it where whole rows or half rows per wave would leave the CUs unevenly
+// loaded, or for long matrices of rows of few strips.
+template <int B, int EPI, int NT>
+__global__ __launch_bounds__(NT, NT == 1024 ? 8 : 1) void spmv_strip_kernel(const void *meta0, const uint16_t *values0,
+                                                                            int R, int KW, int rpw,
+                                                                            const uint16_t *__restrict__ x,
+                                                                            int64_t ldx, const SpmvSet set) {
+    static_assert(EPI == kEpiOne, "one matrix per launch");
+    constexpr int W = NT / kWave;
+    extern __shared__ uint32_t xs[];  // x [KW][kBlk], then strip totals [rpw * nb][B]
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int nb = (KW + kWave - 1) / kWave;
+    const int r0 = blockIdx.x * rpw;
+    const int nr = min(rpw, R - r0);  // >= 1: the grid is ceil(R / rpw)
+    const int T = nr * nb;            // strips of this workgroup
+    float *part = reinterpret_cast<float *>(xs + (size_t)KW * XLayout<B>::kBlk);
+    const int n = T > wave ? (T - 1 - wave) / W + 1 : 0;  // strips of this wave
+    // strip j of the sequence is strip j % nb of row r0 + j / nb; a step of W strips
+    // moves dq rows and dr strips
+    const int dq = W / nb, dr = W - dq * nb;
+    auto advance = [&](int &r, int &s) {
+        s += dr;
+        r += dq;
+        if (s >= nb) {
+            s -= nb;
+            ++r;
+        }
+    };
+    int rowA = r0 + wave / nb, sA = wave - (wave / nb) * nb, jA = wave;
+    int rowB = rowA, sB = sA, jB = jA;
+    Batch<kMetaBitmask> bufA, bufB;
+    stage_x<B, NT>(xs, x, ldx, 0, KW, [&] {
+        load_row_batch<kMetaBitmask, EPI>(bufA, set, meta0, values0, min(rowA, R - 1), KW, 0, n > 0 ? KW : 0,
+                                          sA * kWave, lane);
+    });
+    __syncthreads();
+    float acc[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) acc[b] = 0.f;
+    auto strip_done = [&](int j) {
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            const float tsum = wave_sum(acc[b]);
+            acc[b] = 0.f;
+            if (lane == 0) part[j * B + b] = tsum;
+        }
+    };
+    // two buffers in turn, whole pairs in the loop and the odd last strip after it, as in
+    // spmv_kernel; the strip loaded past this wave's last has no words (no memory traffic)
+    int t = 0;
+    for (; t + 1 < n; t += 2) {
+        rowB = rowA;
+        sB = sA;
+        advance(rowB, sB);
+        jB = jA + W;
+        load_row_batch<kMetaBitmask, EPI>(bufB, set, meta0, values0, min(rowB, R - 1), KW, 0, KW, sB * kWave, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        walk_batch<kMetaBitmask, B>(bufA, xs, KW, acc);
+        strip_done(jA);
+        rowA = rowB;
+        sA = sB;
+        advance(rowA, sA);
+        jA = jB + W;
+        load_row_batch<kMetaBitmask, EPI>(bufA, set, meta0, values0, min(rowA, R - 1), KW, 0, t + 2 < n ? KW : 0,
+                                          sA * kWave, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        walk_batch<kMetaBitmask, B>(bufB, xs, KW, acc);
+        strip_done(jB);
+    }
+    if (t < n) {
+        walk_batch<kMetaBitmask, B>(bufA, xs, KW, acc);
+        strip_done(jA);
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < nr * B; i += NT) {
+        const int rl = i / B, b = i - rl * B;
+        float s = 0.f;
+        for (int k = 0; k < nb; ++k) s += part[(rl * nb + k) * B + b];
+        set.y[0][(int64_t)b * set.ldy[0] + r0 + rl] = f32_to_bf16_rne(s);
+    }
+}
+
 // Second pass of split rows: add the slices in order, round once to bf16.
 template <int B>
 __global__ __launch_bounds__(256) void split_finish_kernel(const float *__restrict__ partial, int S,
@@ -491,12 +581,37 @@ hipError_t launch_half(const MvPlan &p, const SpmvSet &set, int64_t K, const uin
     return hipGetLastError();
 }
 
+template <int B, int NT>
+hipError_t launch_strip(const MvPlan &p, const SpmvSet &set, int64_t K, const uint16_t *x, int64_t ldx,
+                        hipStream_t st) {
+    static std::atomic<uint64_t> done{0};
+    if (p.lds_bytes > 64 * 1024) {
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return e;
+        const uint64_t bit = 1ull << (dev & 63);
+        if (!(done.load(std::memory_order_acquire) & bit)) {
+            e = hipFuncSetAttribute((const void *)spmv_strip_kernel<B, kEpiOne, NT>,
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsCap);
+            if (e != hipSuccess) return e;
+            done.fetch_or(bit, std::memory_order_acq_rel);
+        }
+    }
+    hipLaunchKernelGGL((spmv_strip_kernel<B, kEpiOne, NT>), dim3(p.grid_x), dim3(NT), p.lds_bytes, st, set.meta[0],
+                       set.values[0], set.row0[set.P], (int)(K / 32), p.rows_per_group, x, ldx, set);
+    return hipGetLastError();
+}
+
 template <int FMT, int B, int EPI>
 hipError_t launch_fb(const MvPlan &p, const SpmvSet &set, int64_t K, const uint16_t *x, int64_t ldx, float *ws,
                      hipStream_t st) {
     if constexpr (FMT == kMetaBitmask && B == 1 && EPI == kEpiOne)
-        if (p.half) return launch_half<B>(p, set, K, x, ldx, st);
-    if (p.half) return hipErrorInvalidValue;
+        if (p.walk != kWalkRows) {
+            if (p.walk == kWalkHalf) return launch_half<B>(p, set, K, x, ldx, st);
+            if (p.walk == kWalkStrips && p.threads == 1024) return launch_strip<B, 1024>(p, set, K, x, ldx, st);
+            if (p.walk == kWalkStrips && p.threads == 512) return launch_strip<B, 512>(p, set, K, x, ldx, st);
+        }
+    if (p.walk != kWalkRows) return hipErrorInvalidValue;
     if constexpr (wide_ok(FMT, B))
         if (p.threads == 1024) return launch_fbn<FMT, B, 1024, EPI>(p, set, K, x, ldx, ws, st);
     if (p.threads == 256) return launch_fbn<FMT, B, 256, EPI>(p, set, K, x, ldx, ws, st);
@@ -608,23 +723,47 @@ MvPlan plan_spmv(int64_t R, int64_t K, int B, const DeviceInfo &dev, int fmt) {
     return p;
 }
 
-MvPlan plan_spmv_half(const MvPlan &word, int64_t R, int64_t K, int B, const DeviceInfo &dev) {
-    // Rows of 7+ strips that the one-row-per-wave plan gives a wave at most one of, and
-    // enough of them for two 16-wave workgroups per CU: split each row between two waves
-    // (8B down 4096 x 14336: 12.61 -> 12.40 us; Qwen3-14B down 5120 x 17408: 19.58 ->
-    // 19.19 us; rows of 4 strips and B = 2 were slower, 70B down even).
+MvPlan plan_spmv_one(const MvPlan &word, int64_t R, int64_t K, int B, const DeviceInfo &dev) {
     const int64_t cu = dev.num_cu > 0 ? dev.num_cu : 256;
     const int64_t KW = K / 32, nb = (KW + kWave - 1) / kWave;
-    const size_t extra = (size_t)kHalfRows * 2 * B * 4 + kHalfRows * 4;
-    if (B != 1 || word.tile || word.splits != 1 || nb < 7 || R < 2 * cu * kHalfRows ||
-        R > (int64_t)word.grid_x * (word.threads / kWave) || word.lds_bytes + extra > kLdsCap)
-        return word;
-    MvPlan p = word;
-    p.half = 1;
-    p.threads = kHalfThreads;
-    p.grid_x = (int)((R + kHalfRows - 1) / kHalfRows);
-    p.lds_bytes = word.lds_bytes + extra;
-    return p;
+    if (B != 1 || word.tile || word.splits != 1) return word;
+    const size_t xb = (size_t)KW * spmv_lds_per_word(B);  // x of a whole row
+    auto strips = [&](int threads, int64_t groups_per_cu) {
+        const int64_t rpw = (R + groups_per_cu * cu - 1) / (groups_per_cu * cu);
+        const size_t lds = xb + (size_t)rpw * nb * B * sizeof(float);
+        if (lds * groups_per_cu > kLdsPerCu || lds > kLdsCap) return word;
+        MvPlan p = word;
+        p.walk = kWalkStrips;
+        p.threads = threads;
+        p.rows_per_group = (int)rpw;
+        p.grid_x = (int)((R + rpw - 1) / rpw);
+        p.lds_bytes = lds;
+        return p;
+    };
+    if (nb >= 7 && R >= 2 * cu * kHalfRows) {
+        // Rows of 7+ strips, at least 16 per CU.  Where the rows fill whole rounds of two
+        // 16-wave workgroups per CU, split each row between two waves (8B down 4096 x
+        // 14336: 12.61 -> 12.40 us; 70B down 8192 x 28672: 41.98 -> 41.41 us).  Otherwise
+        // (5120 rows: 640 half-row workgroups, or 1.25 rows per wave) deal the strips of
+        // 10 rows per workgroup to its 16 waves (Qwen3-14B down 5120 x 17408: 19.87 ->
+        // 17.92 us; Qwen3-32B down 5120 x 25600: 26.42 -> 25.78 us).
+        if (R % (2 * cu * kHalfRows) != 0) return strips(1024, 2);
+        const size_t extra = (size_t)kHalfRows * 2 * B * 4 + kHalfRows * 4;
+        if (R > (int64_t)word.grid_x * (word.threads / kWave) || word.lds_bytes + extra > kLdsCap) return word;
+        MvPlan p = word;
+        p.walk = kWalkHalf;
+        p.threads = kHalfThreads;
+        p.grid_x = (int)((R + kHalfRows - 1) / kHalfRows);
+        p.lds_bytes = word.lds_bytes + extra;
+        return p;
+    }
+    // Rows of 8192-12288 columns (4-6 strips) and at least 4 strips for every wave of four
+    // 8-wave workgroups per CU: deal the strips of consecutive rows to the waves, which
+    // then sweep one contiguous stretch of the matrix together (70B q 8192 x 8192: 14.15
+    // -> 13.68 us; 70B gate 28672 x 8192: 42.61 -> 41.71 us).  Shorter rows keep whole
+    // rows per wave: the strip walk was 1-9% slower on the 8B shapes.
+    if (KW >= 256 && nb <= 6 && R * nb >= 4 * (4 * cu * (kThreads / kWave))) return strips(kThreads, 4);
+    return word;
 }
 
 hipError_t launch_spmv(const MvPlan &p, const SpmvSet &set, int fmt, int64_t K, const uint16_t *x, int64_t ldx, int B,

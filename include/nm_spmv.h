@@ -207,17 +207,25 @@ nm_status nm_spmv_swiglu(const uint32_t *gate_masks, const nm_bf16 *gate_values,
  */
 typedef enum { NM_EPI_NONE = 0, NM_EPI_SWIGLU = 1 } nm_epilogue;
 /* NM_KERNEL_WORD_HALF_ROWS: the word-per-lane walk with every row split between two
-   waves of a workgroup (one matrix, one token, rows of 7+ strips of 64 words). */
-typedef enum { NM_KERNEL_WORD = 0, NM_KERNEL_TILE = 1, NM_KERNEL_WORD_HALF_ROWS = 2 } nm_kernel_kind;
+   waves of a workgroup (one matrix, one token, rows of 7+ strips of 64 words).
+   NM_KERNEL_WORD_STRIPS: the word-per-lane walk with each workgroup owning consecutive
+   rows and dealing their 64-word strips to its waves in turn (one matrix, one token). */
+typedef enum {
+    NM_KERNEL_WORD = 0,
+    NM_KERNEL_TILE = 1,
+    NM_KERNEL_WORD_HALF_ROWS = 2,
+    NM_KERNEL_WORD_STRIPS = 3
+} nm_kernel_kind;
 typedef struct {
-    int kernel;             /* nm_kernel_kind: word-per-lane walk (whole or half rows per wave), or the
-                               matrix-core tile walk */
+    int kernel;             /* nm_kernel_kind: word-per-lane walk (whole rows, half rows or strips per
+                               wave), or the matrix-core tile walk */
     int threads;            /* workgroup size */
     int grid_x;             /* workgroups per row slice (word) / resident workgroups (tile) */
     int splits;             /* row slices; > 1: fp32 partial sums and an ordered second pass */
     int tiles_per_step;     /* tile walk: 16-row tiles sharing one x operand (1 or 2); 0 otherwise */
     int x_steps_in_registers; /* tile walk: steps whose x operand each wave holds in registers for the
                                  whole launch (its steps then load weights only); 0: x re-read per step */
+    int rows_per_group;     /* strip walk: consecutive rows owned by one workgroup; 0 otherwise */
     size_t lds_bytes;       /* dynamic LDS of the word-per-lane walk per workgroup */
     size_t workspace_bytes; /* what the compute call requires */
 } nm_launch_plan;

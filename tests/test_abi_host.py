@@ -309,20 +309,21 @@ def test_noalloc_rejects_bad_arguments_and_oversized_scratch(L):
 class _Plan(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int), ("threads", ctypes.c_int), ("grid_x", ctypes.c_int),
                 ("splits", ctypes.c_int), ("tiles_per_step", ctypes.c_int), ("x_steps_in_registers", ctypes.c_int),
-                ("lds_bytes", ctypes.c_size_t), ("workspace_bytes", ctypes.c_size_t)]
+                ("rows_per_group", ctypes.c_int), ("lds_bytes", ctypes.c_size_t), ("workspace_bytes", ctypes.c_size_t)]
 
 
 def test_launch_plans_host_only(L):
     """nm_spmv_plan / nm_spmv_multi_plan run the planners on the host (256 compute units
-    assumed without a GPU): word-per-lane walk at 1-2 tokens, matrix-core tiles at 8, x
-    kept in registers where each wave has exactly four steps per unit, workspace only with
-    split rows; invalid sizes, a NULL plan and an unknown epilogue are rejected."""
+    assumed without a GPU): word-per-lane walk at 1-2 tokens (whole rows, half rows or
+    strips per wave at one token), matrix-core tiles at 8, x kept in registers where each
+    wave has exactly four steps per unit, workspace only with split rows; invalid sizes, a
+    NULL plan and an unknown epilogue are rejected."""
     p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     L.nm_spmv_plan.argtypes, L.nm_spmv_plan.restype = [i64, i64, i32, i32, p], i32
     L.nm_spmv_multi_plan.argtypes, L.nm_spmv_multi_plan.restype = [p, i32, i64, i32, p], i32
     pl = _Plan()
     for R, K in [(4096, 4096), (1024, 4096), (14336, 4096), (4096, 14336), (8192, 8192), (28672, 8192),
-                 (8192, 28672), (1, 32), (3, 28672)]:
+                 (8192, 28672), (5120, 17408), (5121, 25600), (1, 32), (3, 28672)]:
         for B in (1, 2, 4, 8):
             for epi in (0, 1):
                 assert L.nm_spmv_plan(R, K, B, epi, ctypes.byref(pl)) == NM_OK, (R, K, B, epi)
@@ -333,10 +334,14 @@ def test_launch_plans_host_only(L):
                     assert pl.x_steps_in_registers in (0, 4)
                 else:
                     assert pl.tiles_per_step == 0 and pl.x_steps_in_registers == 0 and pl.lds_bytes > 0
-                if pl.kernel == 2:  # half rows: one matrix, one token, no split
-                    assert B == 1 and epi == 0 and pl.splits == 1 and pl.threads == 1024
+                if pl.kernel in (2, 3):  # half rows / strips: one matrix, one token, no split
+                    assert B == 1 and epi == 0 and pl.splits == 1 and pl.threads in (512, 1024)
+                if pl.kernel == 3:  # every row in exactly one workgroup
+                    assert pl.rows_per_group >= 1 and (pl.grid_x - 1) * pl.rows_per_group < R <= pl.grid_x * pl.rows_per_group
+                else:
+                    assert pl.rows_per_group == 0
                 if B <= 2:
-                    assert pl.kernel in (0, 2)
+                    assert pl.kernel in (0, 2, 3)
     assert L.nm_spmv_plan(14336, 4096, 8, 0, ctypes.byref(pl)) == NM_OK
     assert (pl.kernel, pl.threads, pl.x_steps_in_registers) == (1, 512, 4)
     assert L.nm_spmv_plan(28672, 8192, 8, 0, ctypes.byref(pl)) == NM_OK
@@ -346,6 +351,21 @@ def test_launch_plans_host_only(L):
     assert L.nm_spmv_plan(4096, 14336, 1, 0, ctypes.byref(pl)) == NM_OK
     assert (pl.kernel, pl.threads, pl.grid_x) == (2, 1024, 512)
     assert L.nm_spmv_plan(4096, 14336, 2, 0, ctypes.byref(pl)) == NM_OK and pl.kernel == 0
+    assert L.nm_spmv_plan(8192, 28672, 1, 0, ctypes.byref(pl)) == NM_OK and (pl.kernel, pl.grid_x) == (2, 1024)
+    # 5120 rows of 7+ strips: strips of 10 rows per 16-wave workgroup, one workgroup round
+    assert L.nm_spmv_plan(5120, 17408, 1, 0, ctypes.byref(pl)) == NM_OK
+    assert (pl.kernel, pl.threads, pl.grid_x, pl.rows_per_group) == (3, 1024, 512, 10)
+    assert L.nm_spmv_plan(5121, 17408, 1, 0, ctypes.byref(pl)) == NM_OK
+    assert (pl.kernel, pl.grid_x, pl.rows_per_group) == (3, 466, 11)
+    # rows of 8192 columns: strips of consecutive rows per 8-wave workgroup
+    assert L.nm_spmv_plan(8192, 8192, 1, 0, ctypes.byref(pl)) == NM_OK
+    assert (pl.kernel, pl.threads, pl.grid_x, pl.rows_per_group) == (3, 512, 1024, 8)
+    assert L.nm_spmv_plan(28672, 8192, 1, 0, ctypes.byref(pl)) == NM_OK
+    assert (pl.kernel, pl.threads, pl.rows_per_group) == (3, 512, 28)
+    for R, K in [(14336, 4096), (4096, 4096), (1024, 8192), (6000, 8192), (17408, 5120)]:  # whole rows
+        assert L.nm_spmv_plan(R, K, 1, 0, ctypes.byref(pl)) == NM_OK and pl.kernel == 0, (R, K)
+    assert L.nm_spmv_plan(8192, 8192, 2, 0, ctypes.byref(pl)) == NM_OK and pl.kernel == 0
+    assert L.nm_spmv_plan(8192, 8192, 1, 1, ctypes.byref(pl)) == NM_OK and pl.kernel == 0
     assert L.nm_spmv_plan(4096, 14336, 1, 1, ctypes.byref(pl)) == NM_OK and pl.kernel == 0  # gated MLP
     rows = (ctypes.c_int64 * 3)(4096, 1024, 1024)
     assert L.nm_spmv_multi_plan(rows, 3, 4096, 1, ctypes.byref(pl)) == NM_OK and pl.kernel == 0

@@ -237,17 +237,17 @@ def test_bench_launch_class_parity(case):
             assert_within(host_bf16(y), yref, absum, f"class {sig} matrix {i}")
 
 
-@pytest.mark.parametrize("B", [1, 8])
+@pytest.mark.parametrize("B", [1, 2, 8])
 def test_values_beyond_2gib(B):
     """A matrix whose packed values pass 2^31 bytes (270000 x 8192: 2.2 GB of values, 4.4 GB
-    of dense weights), so row offsets need more than 32 bits in the pack and in both walks
-    (B = 1: word-per-lane; B = 8: matrix cores, 16875 tiles, several units per workgroup):
-    masks and values bit-exact and outputs within tolerance on sampled rows, the first and
-    last rows included."""
+    of dense weights), so row offsets need more than 32 bits in the pack and in every walk
+    (B = 1: strips of consecutive rows per workgroup; B = 2: whole rows per wave; B = 8:
+    matrix cores, 16875 tiles, several units per workgroup): masks and values bit-exact and
+    outputs within tolerance on sampled rows, the first and last rows included."""
     R, K = 270000, 8192
     say("beyond 2 GiB", R, K, B)
     plan = nm.nm_spmv_plan(R, K, B)
-    assert plan["kernel"] == (nm.NM_KERNEL_TILE if B == 8 else nm.NM_KERNEL_WORD)
+    assert plan["kernel"] == {1: nm.NM_KERNEL_WORD_STRIPS, 2: nm.NM_KERNEL_WORD, 8: nm.NM_KERNEL_TILE}[B]
     Wd = synth.device_weights(R, K, 0, 61, R, K)
     Xd = synth.device_calib_acts(K, 0, 61, K)
     n = nm.nm_col_norm(Xd)

@@ -210,14 +210,16 @@ def test_spmv_wide_workgroups(R, K, B, plan):
 # meet in LDS.  Ragged last workgroup (4097 rows), a ragged last strip (K = 17408: 8.5
 # strips per row), every pattern, integer-exact and random data, repeat runs identical,
 # a one-matrix nm_spmv_multi identical to nm_spmv, and the plan at the boundaries.
-HALF = [(4096, 14336, 2, 4), (4097, 14336, 8, 16), (5000, 17408, 16, 32), (4096, 28672, 4, 8)]
+HALF = [(4096, 14336, 2, 4), (8192, 14336, 16, 32), (4096, 28672, 4, 8)]
+# (rows, columns, pattern, workgroup size, rows per workgroup)
+STRIPS = [(4097, 14336, 8, 16, 1024, 9), (5000, 17408, 16, 32, 1024, 10), (5120, 25600, 2, 4, 1024, 10),
+          (8192, 8192, 4, 8, 512, 8), (8193, 8192, 2, 4, 512, 9), (9000, 12288, 16, 32, 512, 9)]
 
 
-@pytest.mark.parametrize("R,K,N,M", HALF)
-def test_spmv_half_rows(R, K, N, M):
-    p = nm.nm_spmv_plan(R, K, 1)
-    say("spmv half rows", R, K, N, M, p)
-    assert (p["kernel"], p["threads"], p["grid_x"], p["splits"]) == (nm.NM_KERNEL_WORD_HALF_ROWS, 1024, (R + 7) // 8, 1)
+def _check_one_token_walk(R, K, N, M, what):
+    """One-token launch of a single matrix against the oracle: ternary integer inputs
+    exactly, random inputs within tolerance; repeats bit-identical; the same matrix as a
+    one-matrix nm_spmv_multi launch (whole rows per wave) within tolerance."""
     n = oracle.col_norm(synth.calib_acts(K, 62, R, K))
     # integer-valued operands: the result equals the oracle exactly
     Wt = synth.ternary((R, K), 62, R, K)
@@ -237,21 +239,49 @@ def test_spmv_half_rows(R, K, N, M):
     y2 = nm.nm_spmv(md, vd, xd)
     ym = nm.nm_spmv_multi([(md, vd)], xd)[0]
     yref, absum = oracle.spmv(mref, vref, x, K, nthreads=8)
-    assert_within(host_bf16(y), yref, absum, f"half rows R={R} K={K} {N}:{M}")
+    assert_within(host_bf16(y), yref, absum, f"{what} R={R} K={K} {N}:{M}")
+    assert_within(host_bf16(ym), yref, absum, f"{what} (multi) R={R} K={K} {N}:{M}")
     assert (host_bf16(y) == host_bf16(y2)).all()
-    assert (host_bf16(y) == host_bf16(ym)).all()
 
 
-def test_spmv_half_rows_plan_boundaries():
-    """The half-row walk is taken only at one token, one matrix, 7+ strips per row and
-    4096+ rows; neighbouring shapes keep the whole-row walk."""
-    say("spmv half rows plan boundaries")
-    assert nm.nm_spmv_plan(4096, 14336, 1)["kernel"] == nm.NM_KERNEL_WORD_HALF_ROWS
-    assert nm.nm_spmv_plan(4095, 14336, 1)["kernel"] == nm.NM_KERNEL_WORD
-    assert nm.nm_spmv_plan(4096, 14336, 2)["kernel"] == nm.NM_KERNEL_WORD
-    assert nm.nm_spmv_plan(8192, 8192, 1)["kernel"] == nm.NM_KERNEL_WORD  # 4 strips per row
-    assert nm.nm_spmv_plan(4096, 14336, 1, nm.NM_EPI_SWIGLU)["kernel"] == nm.NM_KERNEL_WORD
-    assert nm.nm_spmv_multi_plan([2048, 2048], 14336, 1)["kernel"] == nm.NM_KERNEL_WORD
+@pytest.mark.parametrize("R,K,N,M", HALF)
+def test_spmv_half_rows(R, K, N, M):
+    p = nm.nm_spmv_plan(R, K, 1)
+    say("spmv half rows", R, K, N, M, p)
+    assert (p["kernel"], p["threads"], p["grid_x"], p["splits"]) == (nm.NM_KERNEL_WORD_HALF_ROWS, 1024, (R + 7) // 8, 1)
+    _check_one_token_walk(R, K, N, M, "half rows")
+
+
+@pytest.mark.parametrize("R,K,N,M,nt,rpw", STRIPS)
+def test_spmv_strips(R, K, N, M, nt, rpw):
+    """The strip walk: consecutive rows per workgroup, strips dealt to the waves in turn,
+    ragged last workgroups (R not a multiple of the rows per workgroup) included."""
+    p = nm.nm_spmv_plan(R, K, 1)
+    say("spmv strips", R, K, N, M, p)
+    assert (p["kernel"], p["threads"], p["rows_per_group"], p["splits"]) == (nm.NM_KERNEL_WORD_STRIPS, nt, rpw, 1)
+    assert p["grid_x"] == (R + rpw - 1) // rpw
+    _check_one_token_walk(R, K, N, M, "strips")
+
+
+def test_spmv_one_token_walk_plan_boundaries():
+    """Half rows and strips are taken only at one token and one matrix: half rows for
+    7+ strips per row on whole rounds of 4096 rows (on 256 CUs; the GPU here may have
+    another count, so the row counts scale with it), strips for other row counts from
+    16 per CU and for rows of 4-6 strips with 4+ strips per wave; other shapes keep the
+    whole-row walk."""
+    say("spmv one-token walk plan boundaries")
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    rnd = 2 * cu * 8
+    assert nm.nm_spmv_plan(rnd, 14336, 1)["kernel"] == nm.NM_KERNEL_WORD_HALF_ROWS
+    assert nm.nm_spmv_plan(rnd + 64, 14336, 1)["kernel"] == nm.NM_KERNEL_WORD_STRIPS
+    assert nm.nm_spmv_plan(rnd - 1, 14336, 1)["kernel"] == nm.NM_KERNEL_WORD
+    assert nm.nm_spmv_plan(rnd, 12288, 1)["kernel"] == nm.NM_KERNEL_WORD  # 6 strips, 4 per wave: no
+    assert nm.nm_spmv_plan(2 * rnd, 12288, 1)["kernel"] == nm.NM_KERNEL_WORD_STRIPS
+    assert nm.nm_spmv_plan(4 * cu * 8, 4096, 1)["kernel"] == nm.NM_KERNEL_WORD  # rows of 2 strips
+    assert nm.nm_spmv_plan(rnd, 14336, 2)["kernel"] == nm.NM_KERNEL_WORD
+    assert nm.nm_spmv_plan(2 * rnd, 8192, 2)["kernel"] == nm.NM_KERNEL_WORD
+    assert nm.nm_spmv_plan(rnd, 14336, 1, nm.NM_EPI_SWIGLU)["kernel"] == nm.NM_KERNEL_WORD
+    assert nm.nm_spmv_multi_plan([rnd // 2, rnd // 2], 14336, 1)["kernel"] == nm.NM_KERNEL_WORD
 
 
 @pytest.mark.parametrize("N,M", PATTERNS)
