@@ -55,6 +55,8 @@ ROTATE_BYTES = 512e6
 # replays -- is re-read only after the whole pool (>= 512 MB) has been.
 TIMED_LAUNCHES = 64
 WARM_REPLAYS = 10
+WARM_MS = 25.0  # and at least this much replay time before the timed replays
+SETTLE_S = 0.5   # step replays before each further workload's timings (see settle)
 TIMED_REPLAYS = 50
 TARGET_PCT, TARGET_SPEEDUP = 70.0, 1.5
 METRIC = "nm_spmv GB/s and % HBM peak per layer; speedup vs dense bf16 GEMV, batch 1"
@@ -230,11 +232,17 @@ def time_graph(torch, g, reps):
 
 def time_launches(torch, fns):
     """Per-launch µs of a rotation: one graph of whole passes over the pool's launches (at
-    least TIMED_LAUNCHES), WARM_REPLAYS untimed replays, then TIMED_REPLAYS replays timed one
-    by one; returns the median and p10/p90 of the per-launch time of a replay."""
+    least TIMED_LAUNCHES), untimed replays (WARM_REPLAYS and at least WARM_MS of them, so
+    that clocks settle after host-side work whatever ran before), then TIMED_REPLAYS replays
+    timed one by one; returns the median and p10/p90 of the per-launch time of a replay."""
     n = -(-TIMED_LAUNCHES // len(fns)) * len(fns)
     g = capture(torch, [fns[i % len(fns)] for i in range(n)])
-    for _ in range(WARM_REPLAYS):
+    w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0.record()
+    g.replay()
+    w1.record()
+    torch.cuda.synchronize()
+    for _ in range(max(WARM_REPLAYS - 1, math.ceil(WARM_MS / max(w0.elapsed_time(w1), 1e-3)))):
         g.replay()
     e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(TIMED_REPLAYS)]
     for e0, e1 in e:
@@ -408,6 +416,19 @@ def step_graphs(c, projs, patterns, pool_sparse, pool_dense, xs, ys, L, B):
     return sparse, dense, sb, db
 
 
+def settle(c, fns, seconds=SETTLE_S):
+    """Replays of one step for about `seconds` before a workload's timings.  After the
+    pools of a workload are rebuilt in a process that has already measured another, the
+    first ~0.35 s of launches ran up to 8% slow (70B q at B = 1: 14.6 us, then 13.5 us),
+    whatever was launched; a first workload in a fresh process showed no such window."""
+    g = capture(c.torch, fns)
+    t0 = time.time()
+    while time.time() - t0 < seconds:
+        g.replay()
+        c.torch.cuda.synchronize()
+    del g
+
+
 def time_step(c, fns, steps, warmup):
     g = capture(c.torch, fns)
     for _ in range(warmup):
@@ -490,6 +511,7 @@ def measure_other(c, name, L, batches, steps, warmup, seed, check):
         if check and B == batches[0]:
             spot_check(c, projs, patterns, pool_sparse, pool_dense, xs, seed + 17)
         sparse, dense, sb, db = step_graphs(c, projs, patterns, pool_sparse, pool_dense, xs, ys, L, B)
+        settle(c, sparse)
         ms = time_step(c, sparse, steps, warmup)
         msd = time_step(c, dense, steps, warmup)
         per = per_layer_table(c, projs, patterns, pool_sparse, pool_dense, xs, ys, L, B, hipblaslt=True)
