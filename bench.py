@@ -417,10 +417,11 @@ def step_graphs(c, projs, patterns, pool_sparse, pool_dense, xs, ys, L, B):
 
 
 def settle(c, fns, seconds=SETTLE_S):
-    """Replays of one step for about `seconds` before a workload's timings.  After the
-    pools of a workload are rebuilt in a process that has already measured another, the
-    first ~0.35 s of launches ran up to 8% slow (70B q at B = 1: 14.6 us, then 13.5 us),
-    whatever was launched; a first workload in a fresh process showed no such window."""
+    """Replays of one step for about `seconds` (untimed) before a workload's timings, so
+    that they start from the clocks of sustained decoding.  After the pools of a workload
+    are built the first ~0.35 s of launches ran up to 8% slow (70B q at B = 1: 14.6 us,
+    then 13.5 us), whatever was launched; after a pause of 1 s the 8B step read 2% slow
+    again (0.761 ms against 0.746 ms right after these replays)."""
     g = capture(c.torch, fns)
     t0 = time.time()
     while time.time() - t0 < seconds:
@@ -584,6 +585,8 @@ def main():
     groups = layer_groups(projs)
     fused_fns, fused_dense_fns, fused_sparse_bytes, fused_dense_bytes = step_graphs(
         c, projs, patterns, pool_sparse, pool_dense, xs, ys, L, B)
+    # steady state first (untimed): then the W warm-up steps and exactly K timed steps
+    settle(c, fused_fns)
     ms_fused = time_step(c, fused_fns, args.steps, args.warmup)
     ms_fused_dense = time_step(c, fused_dense_fns, args.steps, args.warmup)
     # the same step with one nm_spmv call per projection
