@@ -218,8 +218,9 @@ STRIPS = [(4097, 14336, 8, 16, 1024, 9), (5000, 17408, 16, 32, 1024, 10), (5120,
 
 def _check_one_token_walk(R, K, N, M, what):
     """One-token launch of a single matrix against the oracle: ternary integer inputs
-    exactly, random inputs within tolerance; repeats bit-identical; the same matrix as a
-    one-matrix nm_spmv_multi launch (whole rows per wave) within tolerance."""
+    exactly, random inputs within tolerance; repeats bit-identical; the same matrix cut
+    into two nm_spmv_multi matrices (which the planner gives whole rows per wave) within
+    tolerance."""
     n = oracle.col_norm(synth.calib_acts(K, 62, R, K))
     # integer-valued operands: the result equals the oracle exactly
     Wt = synth.ternary((R, K), 62, R, K)
@@ -237,10 +238,12 @@ def _check_one_token_walk(R, K, N, M, what):
     md, vd, xd = dev_u32(mref), dev_bf16(vref), dev_bf16(x)
     y = nm.nm_spmv(md, vd, xd)
     y2 = nm.nm_spmv(md, vd, xd)
-    ym = nm.nm_spmv_multi([(md, vd)], xd)[0]
+    h = R // 2
+    assert nm.nm_spmv_multi_plan([h, R - h], K, 1)["kernel"] == nm.NM_KERNEL_WORD
+    ym = torch.cat(nm.nm_spmv_multi([(md[:h], vd[:h]), (md[h:], vd[h:])], xd), dim=1)
     yref, absum = oracle.spmv(mref, vref, x, K, nthreads=8)
     assert_within(host_bf16(y), yref, absum, f"{what} R={R} K={K} {N}:{M}")
-    assert_within(host_bf16(ym), yref, absum, f"{what} (multi) R={R} K={K} {N}:{M}")
+    assert_within(host_bf16(ym), yref, absum, f"{what} (whole rows) R={R} K={K} {N}:{M}")
     assert (host_bf16(y) == host_bf16(y2)).all()
 
 

@@ -54,9 +54,11 @@ def test_noalloc_matches_nm_spmv_on_two_calls(first, second):
     _check(*a, f"first again {first}")
 
 
-@pytest.mark.parametrize("R,K,B", [(1024, 4096, 1), (512, 4096, 8)])
-def test_noalloc_without_split_rows(R, K, B):
-    """Shapes that need no scratch (whole rows; the matrix-core path at B = 8)."""
+@pytest.mark.parametrize("R,K,B,kind", [(1024, 4096, 1, 0), (512, 4096, 8, 1), (4096, 14336, 1, 2), (4160, 14336, 1, 3)])
+def test_noalloc_without_split_rows(R, K, B, kind):
+    """Shapes that need no scratch: whole rows, the matrix-core path at B = 8, and the
+    one-token half-row and strip walks."""
     say("noalloc no split", R, K, B)
-    assert nm.nm_spmv_plan(R, K, B)["workspace_bytes"] == 0
+    p = nm.nm_spmv_plan(R, K, B)
+    assert p["workspace_bytes"] == 0 and p["kernel"] == kind
     _check(*_case(R, K, B, 3), f"{R}x{K} B={B}")
