@@ -204,15 +204,17 @@ def test_bench_launch_classes_listed():
     assert kinds == {"one", "multi", "swiglu"}
 
 
-@pytest.mark.parametrize("case", range(48))
-def test_bench_launch_class_parity(case):
+CLASSES = coverage_cases()  # the planner runs on the host: known at collection time
+
+
+@pytest.mark.parametrize("sig,case", CLASSES,
+                         ids=[f"{s[0]}-B{s[1]}-k{s[2]}-t{s[3]}{'-split' if s[4] else ''}-tt{s[5]}-x{s[6]}"
+                              for s, _ in CLASSES])
+def test_bench_launch_class_parity(sig, case):
     """One launch of each distinct plan the bench times, at its own shape, all rows: the
     product against the oracle's matvec of the GPU-packed operands (the pack itself is
     held bit-exact by the tests above)."""
-    cases = coverage_cases()
-    if case >= len(cases):
-        pytest.skip(f"only {len(cases)} launch classes")
-    sig, (kind, rows, K, B) = cases[case]
+    kind, rows, K, B = case
     say("launch class", sig, kind, rows, K, B)
     n = nm.nm_col_norm(synth.device_calib_acts(K, 0, 60, K))
     mats = []
