@@ -377,3 +377,43 @@ def test_launch_plans_host_only(L):
     assert L.nm_spmv_multi_plan(None, 3, 4096, 1, ctypes.byref(pl)) == NM_ERR_NULL
     assert L.nm_spmv_multi_plan(rows, 0, 4096, 1, ctypes.byref(pl)) == NM_ERR_SHAPE
     assert L.nm_spmv_multi_plan(rows, 9, 4096, 1, ctypes.byref(pl)) == NM_ERR_SHAPE
+
+
+C_CLIENT = r"""
+#include "nm_spmv.h"
+#include <stdio.h>
+
+int main(void) {
+    nm_launch_plan plan;
+    const nm_status s = nm_spmv_plan(4096, 14336, 1, NM_EPI_NONE, &plan);
+    if (s != NM_OK) { printf("plan: %s\n", nm_status_str(s)); return 1; }
+    /* argument errors come back synchronously, before any HIP call */
+    if (nm_spmv(NULL, NULL, 4096, 14336, NULL, 14336, 1, NULL, 4096, NULL, 0, NULL) != NM_ERR_NULL) return 2;
+    if (nm_last_error()[0] == '\0') return 3;
+    printf("version %d kernel %d threads %d grid %d\n", nm_version(), plan.kernel, plan.threads, plan.grid_x);
+    return 0;
+}
+"""
+
+
+def test_plain_c_client_builds_and_runs(tmp_path):
+    """The header is plain C (C99, no C++ or HIP types): a C program includes it, links the
+    library and calls the host-only entry points; the header also compiles as C++."""
+    if os.environ.get("NM_SPMV_LIB"):
+        pytest.skip("the C client links the regular build (a sanitized one needs its runtimes)")
+    src = tmp_path / "client.c"
+    src.write_text(C_CLIENT)
+    exe = tmp_path / "client"
+    libdir = os.path.dirname(LIB)
+    cc = ["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", f"-I{os.path.join(ROOT, 'include')}",
+          str(src), "-o", str(exe), f"-L{libdir}", f"-l:{os.path.basename(LIB)}", f"-Wl,-rpath,{libdir}"]
+    r = subprocess.run(cc, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, (r.returncode, r.stdout, r.stderr)
+    assert re.match(r"version \d+ kernel 2 threads 1024 grid 512", r.stdout), r.stdout
+    cxx = tmp_path / "client.cpp"
+    cxx.write_text('#include "nm_spmv.h"\nint main() { return nm_version() > 0 ? 0 : 1; }\n')
+    r = subprocess.run(["g++", "-std=c++11", "-Wall", "-Wextra", "-pedantic", "-Werror", "-fsyntax-only",
+                        f"-I{os.path.join(ROOT, 'include')}", str(cxx)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
