@@ -124,6 +124,17 @@ __device__ __forceinline__ uint32_t pair_swap(uint32_t v) {
 // address stays inside the staged x.  A bitmask word without exactly 16 set bits (outside
 // the input contract) walks the low 16 columns of its own block instead, so each of the
 // 16 bit scans finds a set bit.
+//
+// One or two tokens (bitmask and uint8 offsets): no value exchange between the lanes of
+// a pair.  Lane 2i holds values 0..7 of words i and 32+i of the strip (the first halves
+// of its two 16-byte chunks), lane 2i+1 values 8..15 of the same two words, and each
+// walks its eight values of both words: even lanes from the lowest kept column up, odd
+// lanes from the highest down (the lowest set bits of the bit-reversed mask word; for
+// uint8 the offset bytes in reverse order).  Only the partner's metadata crosses lanes
+// (one or two DPP moves), and each lane runs two independent chains of eight steps.  The
+// bitmask and uint8 walks visit the same kept weights in the same order on the same
+// lane, so their fp32 sums agree bit for bit.  At three or four tokens the exchange of
+// value halves below is the faster of the two.
 template <int FMT, int B>
 __device__ __forceinline__ void walk_batch(const Batch<FMT> &bt, const uint32_t *xs, int nws, float (&acc)[B]) {
     constexpr int kBlk = XLayout<B>::kBlk;
@@ -135,6 +146,61 @@ __device__ __forceinline__ void walk_batch(const Batch<FMT> &bt, const uint32_t 
             const uint32_t *blk = xs + (w < nws ? w : 0) * kBlk;
             dot_pair<B>(v[2 * q], blk, (int)(bt.meta[q].x & 31u), (int)(bt.meta[q].y & 31u), acc);
             dot_pair<B>(v[2 * q + 1], blk, (int)(bt.meta[q].z & 31u), (int)(bt.meta[q].w & 31u), acc);
+        }
+    } else if constexpr (B <= 2) {
+        constexpr int kCol = XLayout<B>::S * 2;  // LDS bytes of one column (its token slots)
+        const bool odd = threadIdx.x & 1;
+        const int wa = odd ? bt.lw - 32 : bt.lw, wb = wa + 32;  // words i and 32+i of the strip
+        const bool oka = wa < nws, okb = wb < nws;
+        const uint8_t *x8 = reinterpret_cast<const uint8_t *>(xs);
+        const int ba = (oka ? wa : 0) * kBlk * 4, bb = (okb ? wb : 0) * kBlk * 4;  // block byte offsets
+        // value pair k of the walk: even lanes dword k of a chunk; odd lanes dword 3 - k
+        // with its halves swapped (the downward walk meets the higher column first)
+        const uint32_t vsel = odd ? 0x01000302u : 0x07060504u;
+        const uint32_t av[4] = {bt.va.x, bt.va.y, bt.va.z, bt.va.w}, bv[4] = {bt.vb.x, bt.vb.y, bt.vb.z, bt.vb.w};
+        if constexpr (FMT == kMetaBitmask) {
+            const uint32_t own = bt.meta[0].x, oth = pair_swap(own);
+            uint32_t ma = odd ? oth : own, mb = odd ? own : oth;
+            ma = oka && __builtin_popcount(ma) == 16 ? ma : 0xFFFFu;
+            mb = okb && __builtin_popcount(mb) == 16 ? mb : 0xFFFFu;
+            ma = odd ? __builtin_bitreverse32(ma) : ma;
+            mb = odd ? __builtin_bitreverse32(mb) : mb;
+            // byte address of the column at walk position p: base + dir * p (odd lanes: column 31 - p)
+            const int dir = odd ? -kCol : kCol, flip = odd ? 31 * kCol : 0;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int a0 = __builtin_ctz(ma);
+                ma &= ma - 1;
+                const int a1 = __builtin_ctz(ma);
+                ma &= ma - 1;
+                const int b0 = __builtin_ctz(mb);
+                mb &= mb - 1;
+                const int b1 = __builtin_ctz(mb);
+                mb &= mb - 1;
+                dot_pair_at<B>(__builtin_amdgcn_perm(av[k], av[3 - k], vsel), x8 + ba + flip + dir * a0,
+                               x8 + ba + flip + dir * a1, acc);
+                dot_pair_at<B>(__builtin_amdgcn_perm(bv[k], bv[3 - k], vsel), x8 + bb + flip + dir * b0,
+                               x8 + bb + flip + dir * b1, acc);
+            }
+        } else {
+            // offsets of the lane's eight values of each word: even lanes bytes 0..7 of
+            // words i (own) and 32+i (partner's); odd lanes bytes 8..15 of word i (partner's)
+            // and of 32+i (own), then byte-reversed so that byte 2k is the walk's first
+            const u32x4 own = bt.meta[0];
+            const uint32_t r0 = pair_swap(odd ? own.x : own.z), r1 = pair_swap(odd ? own.y : own.w);
+            const uint32_t a0 = odd ? r0 : own.x, a1 = odd ? r1 : own.y;
+            const uint32_t b0 = odd ? own.z : r0, b1 = odd ? own.w : r1;
+            const uint32_t rsel = odd ? 0x00010203u : 0x07060504u;  // odd: the other dword, bytes reversed
+            const uint32_t oa[2] = {__builtin_amdgcn_perm(a0, a1, rsel), __builtin_amdgcn_perm(a1, a0, rsel)};
+            const uint32_t ob[2] = {__builtin_amdgcn_perm(b0, b1, rsel), __builtin_amdgcn_perm(b1, b0, rsel)};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t pa = oa[k >> 1] >> (16 * (k & 1)), pb = ob[k >> 1] >> (16 * (k & 1));
+                dot_pair_at<B>(__builtin_amdgcn_perm(av[k], av[3 - k], vsel), x8 + ba + kCol * (int)(pa & 31u),
+                               x8 + ba + kCol * (int)((pa >> 8) & 31u), acc);
+                dot_pair_at<B>(__builtin_amdgcn_perm(bv[k], bv[3 - k], vsel), x8 + bb + kCol * (int)(pb & 31u),
+                               x8 + bb + kCol * (int)((pb >> 8) & 31u), acc);
+            }
         }
     } else {
         const bool ok = bt.lw < nws;

@@ -73,6 +73,22 @@ __device__ __forceinline__ void dot_pair(uint32_t v, const uint32_t *blk, int c0
     }
 }
 
+// The same with the two columns given by the LDS byte addresses of their token slots
+// (one or two tokens).
+template <int B>
+__device__ __forceinline__ void dot_pair_at(uint32_t v, const uint8_t *p0, const uint8_t *p1, float (&acc)[B]) {
+    static_assert(B <= 2, "one or two tokens");
+    if constexpr (B == 1) {
+        const uint32_t pr = (uint32_t)*reinterpret_cast<const uint16_t *>(p0) |
+                            ((uint32_t)*reinterpret_cast<const uint16_t *>(p1) << 16);
+        acc[0] = dot2_bf16(v, pr, acc[0]);
+    } else {
+        const uint32_t d0 = *reinterpret_cast<const uint32_t *>(p0), d1 = *reinterpret_cast<const uint32_t *>(p1);
+        acc[0] = dot2_bf16(v, __builtin_amdgcn_perm(d1, d0, 0x05040100u), acc[0]);
+        acc[1] = dot2_bf16(v, __builtin_amdgcn_perm(d1, d0, 0x07060302u), acc[1]);
+    }
+}
+
 // Matrix of the set that owns global row r (0 <= r < R).  The launcher pads row0 past
 // the last matrix with the total row count, so p counts the bounds row0[q] <= r.  The
 // test is the sign of row0[q] - 1 - r (no overflow for 0 <= r, row0[q] <= INT_MAX),

@@ -52,7 +52,7 @@ SHAPES = [(256, 512), (129, 4096), (1000, 1024), (7, 14336), (1, 32), (3, 28672)
 
 @pytest.mark.parametrize("fmt,ofmt", FMTS)
 @pytest.mark.parametrize("R,K", SHAPES)
-@pytest.mark.parametrize("B", [1, 3, 8])
+@pytest.mark.parametrize("B", [1, 2, 3, 8])
 def test_spmv_meta_matches_oracle_and_bitmask(fmt, ofmt, R, K, B):
     say("spmv_meta", fmt, R, K, B)
     m, v = _pack(R, K, 8, R, K, B)
