@@ -541,15 +541,17 @@ MvPlan plan_spmv_tile(const SpmvSet &set, int64_t K, int B, const DeviceInfo &de
     // per CU -- as many waves in flight -- where K gives every one of 16 waves at least
     // four steps per tile and
     //   * there are fewer tiles than 8-wave workgroups, or
-    //   * every wave of 16 then has exactly kTileXC steps (x stays in registers), there
-    //     are at least 4 tiles per CU to amortise the first unit's x loads, and 7 or 8
-    //     tokens make x a large share of the loads (28672 x 8192, 8 tokens: 54.8 -> 51.2
-    //     us; 5 tokens: 48.9 -> 52.4 us, so not there), or
+    //   * every wave of 16 then has exactly kTileXC steps (x stays in registers after a
+    //     workgroup's first unit) and either 7 or 8 tokens make x a large share of the
+    //     loads (28672 x 8192, 8 tokens: 56.7 -> 52.1 us; 12288 x 8192, 7 tokens: 25.0 ->
+    //     24.5 us; 5 and 6 tokens on 3 or more tiles per CU: 2-6% slower, so not there) or
+    //     there are at most two tiles per CU (8192 x 8192: 18.7 -> 17.7 us at 8 tokens,
+    //     17.8 -> 17.3 at 5), or
     //   * K is long (8 or more steps per wave of 16): the x operand, re-read every step,
     //     is then shared by two tiles from as few as 2 tiles per CU on (8 tokens,
     //     8192 x 28672: 60.2 -> 53.7 us).
     const int64_t s16 = K % (32 * 16 * kTStep) == 0 ? K / (32 * 16 * kTStep) : 0;  // steps per wave of 16
-    const bool w16 = s16 >= 4 && (tiles < 2 * cu || (s16 == kTileXC && tiles >= 4 * cu && B >= 7) || s16 >= 8);
+    const bool w16 = s16 >= 4 && (tiles < 2 * cu || (s16 == kTileXC && (B >= 7 || tiles <= 2 * cu)) || s16 >= 8);
     const int w = w16 ? 16 : 8;
     const int64_t slots = cu * (16 / w);  // resident workgroups
     // Two tiles per step (one x operand for 32 rows, half the x loads per weight byte)
@@ -563,6 +565,10 @@ MvPlan plan_spmv_tile(const SpmvSet &set, int64_t K, int B, const DeviceInfo &de
         const int64_t u1 = tiles, u2 = (tiles + 1) / 2;
         // ceil(u / cu) / (u / cu): compare ceil(u2/cu) * u1 with ceil(u1/cu) * u2
         if ((u2 + cu - 1) / cu * u1 > (u1 + cu - 1) / cu * u2) two = false;
+        // with x kept in registers, a workgroup's later units reuse its x operand: one
+        // tile per step and two units per workgroup beat two tiles and a single unit
+        // (8192 x 8192, 16 waves, 8 tokens: 17.8 vs 18.4 us)
+        if (K / 32 == (int64_t)w * kTStep * kTileXC && u2 <= slots) two = false;
     }
     const int tt = two ? 2 : 1;
     const int64_t units = (tiles + tt - 1) / tt;
