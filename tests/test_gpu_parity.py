@@ -362,6 +362,32 @@ def test_spmv_strided_x_and_y():
     assert (yh[:, R:] == 0).all()  # nothing written past ldy's row
 
 
+# Mask words without exactly 16 set bits are outside the input contract: every walk then
+# reads fixed columns of the word's own block (no access outside the staged x or the
+# dense tile), so the other rows of the launch are unaffected and every output is finite.
+BAD_WORDS = [(3, 5, 0x00000000), (77, 40, 0xFFFFFFFF), (150, 100, 0x00010001), (299, 127, 0x7FFFFFFF)]
+
+
+@pytest.mark.parametrize("R,K,B", [(300, 4096, 1), (300, 4096, 2), (300, 4096, 4), (300, 4096, 8),
+                                   (4096, 14336, 1)])
+def test_spmv_malformed_mask_words_stay_in_their_rows(R, K, B):
+    say("spmv malformed words", R, K, B)
+    W = synth.weights(R, K, 14, R, K)
+    mref, vref = oracle.prune_pack(W, oracle.col_norm(synth.calib_acts(K, 14, R)), 4, 8)
+    bad = mref.copy()
+    rows = sorted({r for r, _, _ in BAD_WORDS if r < R})
+    for r, w, word in BAD_WORDS:
+        if r < R:
+            bad[r, w] = word
+    x = synth.decode_x(B, K, 14, R, K, B)
+    y = bf16_as_f64(host_bf16(nm.nm_spmv(dev_u32(bad), dev_bf16(vref), dev_bf16(x))))
+    assert np.isfinite(y).all()
+    yref, absum = oracle.spmv(mref, vref, x, K, nthreads=8)
+    keep = np.setdiff1d(np.arange(R), rows)
+    ok = oracle.within_tolerance(y[:, keep], yref[:, keep], absum[:, keep], RTOL, ATOL_FRAC)
+    assert ok.all(), f"{int((~ok).sum())} of {ok.size} rows outside tolerance next to malformed words"
+
+
 def test_spmv_workspace_errors():
     say("spmv workspace errors")
     R, K = 64, 8192
