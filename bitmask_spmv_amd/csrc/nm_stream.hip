@@ -2,8 +2,8 @@
 //
 // The matrix-vector kernels are judged against the memory system's bandwidth; this
 // kernel shows what a launch that only reads delivers under the same conditions (the
-// same 16-byte non-temporal buffer loads, the same grid of 512-thread workgroups, the
-// same rotation over distinct buffers).  Every dword read is XOR-folded and one fold per
+// same 16-byte non-temporal buffer loads of 512-thread workgroups, the same rotation over
+// distinct buffers), in the grid shape that reads fastest.  Every dword read is XOR-folded and one fold per
 // wave is written, so the loads cannot be dropped and the result is checkable: the XOR of
 // all folds equals the XOR of all dwords of the buffer.
 #include "nm_device.h"
@@ -14,58 +14,46 @@ namespace {
 
 constexpr int kSThreads = 512;
 constexpr int kSWaves = kSThreads / kWave;
-constexpr int kSUnroll = 2;         // 1 KiB wave loads per unit; two units in flight per wave
-constexpr int kSMaxGroups = 1024;   // four 512-thread workgroups per CU on 256 CUs
-constexpr uint32_t kSUnitBytes = 2048; // one unit = two 1 KiB wave loads
+constexpr uint32_t kSUnitBytes = 1024;  // one unit = one 16-byte load per lane, 1 KiB per wave
+constexpr int kSMaxGroups = 256;        // one 8-wave workgroup per CU on 256 CUs
 
-template <int U>
-__device__ __forceinline__ void load_group(u32x4 (&v)[U], __amdgpu_buffer_rsrc_t rs, uint32_t off) {
-#pragma unroll
-    for (int u = 0; u < U; ++u)  // past the buffer: zeros, which leave the fold as it is
-        v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, off + u * 1024u, 0, kLoadNT);
-}
-
-template <int U>
-__device__ __forceinline__ uint32_t fold_group(const u32x4 (&v)[U]) {
-    uint32_t f = 0;
-#pragma unroll
-    for (int u = 0; u < U; ++u) f ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
-    return f;
-}
-
-// The buffer is cut into 2 KiB units (one 16-byte load per lane for each KiB); wave gw of
-// W takes units gw, gw + W, gw + 2W, ..., so the waves of a workgroup sweep adjacent
-// units, as the matrix-vector kernels' waves sweep adjacent rows.  The grid gives every
-// wave at least two units, up to four 512-thread workgroups per CU.  Two units are in
-// flight per wave: the next unit of a buffer is issued right after that buffer is
-// folded.  The loop has a single exit at its top (the second buffer past the end reads
-// zeros, which leave the fold as it is), and the wave index is made wave-uniform, so
-// the loop runs on scalar registers and every wait covers one unit only.  The grid size
-// is an argument (preloaded with the others) rather than a dispatch-packet read, and each
-// wave writes its own fold (no workgroup barrier at the end).
+// The buffer is cut into 1 KiB units; wave gw of W takes units gw, gw + W, gw + 2W, ...,
+// so the waves of a workgroup read adjacent units.  D units are in flight per wave: the
+// next unit of a register set is issued right after that set is folded.  One 8-wave
+// workgroup per CU with 3 or 4 units in flight per wave (24-32 KiB per CU) reads faster
+// than more, fuller workgroups: a sweep of 256-1024-thread workgroups, 1-4 KiB units, 2-4
+// units in flight and 1-8 workgroups per CU put this shape first at 19, 66, 132 and
+// 264 MB (66 MB: 75.5% of 8 TB/s against 73.9% with four 8-wave workgroups per CU and
+// two 2 KiB units in flight per wave; 264 MB: 86.5% against 82.5%).  The loop has a single
+// exit at its top (loads past the end read zeros, which leave the fold as it is), and the
+// wave index is wave-uniform, so the loop runs on scalar registers and every wait covers
+// one unit only.  The grid size is an argument (preloaded with the others), and each wave
+// writes its own fold (no workgroup barrier at the end).
+template <int D>
 __global__ __launch_bounds__(kSThreads) void stream_read_kernel(const uint8_t *__restrict__ buf, uint32_t bytes,
                                                                 uint32_t *__restrict__ sink, uint32_t grid) {
     const int lane = threadIdx.x & (kWave - 1);
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const uint32_t gw = blockIdx.x * kSWaves + wave;
     const uint32_t W = grid * kSWaves;
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(buf, bytes);  // past the end: zeros
-    constexpr uint32_t U = kSUnroll * 1024u;                   // one unit
-    const uint32_t units = (bytes + U - 1) / U;                // offsets stay below 2^31 + 2^25
-    uint32_t ua = gw, ub = gw + W;
-    u32x4 a[kSUnroll], b[kSUnroll];
-    load_group(a, rs, ua * U + lane * 16u);
-    load_group(b, rs, ub * U + lane * 16u);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(buf, bytes);       // past the end: zeros
+    const uint32_t units = (bytes + kSUnitBytes - 1) / kSUnitBytes;  // offsets stay below 2^31 + 2^24
+    u32x4 v[D];
+    uint32_t u[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        u[d] = gw + d * W;
+        v[d] = __builtin_amdgcn_raw_buffer_load_b128(rs, u[d] * kSUnitBytes + lane * 16u, 0, kLoadNT);
+    }
     uint32_t fold = 0;
-    while (ua < units) {
-        fold ^= fold_group(a);
-        ua = ub + W;
-        load_group(a, rs, ua * U + lane * 16u);
-        __builtin_amdgcn_sched_barrier(0);
-        fold ^= fold_group(b);
-        ub = ua + W;
-        load_group(b, rs, ub * U + lane * 16u);
-        __builtin_amdgcn_sched_barrier(0);
+    while (u[0] < units) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            fold ^= v[d].x ^ v[d].y ^ v[d].z ^ v[d].w;
+            u[d] = u[d == 0 ? D - 1 : d - 1] + W;
+            v[d] = __builtin_amdgcn_raw_buffer_load_b128(rs, u[d] * kSUnitBytes + lane * 16u, 0, kLoadNT);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
     // XOR over the wave: within rows of 16 lanes by DPP, then the four row results (a
     // cross-lane shuffle through LDS here cost 0.2 us at the end of every launch)
@@ -81,10 +69,9 @@ __global__ __launch_bounds__(kSThreads) void stream_read_kernel(const uint8_t *_
 }  // namespace
 
 size_t stream_read_groups(size_t bytes) {
-    // two units per wave at least: a launch over a small buffer runs fewer, fuller waves
-    // (19 MB: 5.60 -> 4.98 us; 66 MB and up within 1%)
-    const size_t per_group = (size_t)kSWaves * kSUnitBytes * 2;
-    size_t g = (bytes + per_group - 1) / per_group;
+    // at least two units per wave: a launch over a small buffer runs fewer, fuller waves
+    const size_t units = (bytes + kSUnitBytes - 1) / kSUnitBytes;
+    size_t g = units / (2 * kSWaves);
     if (g > (size_t)kSMaxGroups) g = kSMaxGroups;
     return g < 1 ? 1 : g;
 }
@@ -93,8 +80,14 @@ size_t stream_read_waves(size_t bytes) { return stream_read_groups(bytes) * kSWa
 
 hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t st) {
     const unsigned grid = (unsigned)stream_read_groups(bytes);
-    hipLaunchKernelGGL(stream_read_kernel, dim3(grid), dim3(kSThreads), 0, st, static_cast<const uint8_t *>(buf),
-                       (uint32_t)bytes, sink, grid);
+    // four units in flight per wave for 40-200 MB (the MLP layers' sizes), three otherwise
+    // (19 MB: 4.80 vs 4.95 us; 66 MB: 10.94 vs 11.17 us; 264 MB: 38.2 vs 38.5 us)
+    if (bytes >= (size_t)40e6 && bytes <= (size_t)200e6)
+        hipLaunchKernelGGL(stream_read_kernel<4>, dim3(grid), dim3(kSThreads), 0, st, static_cast<const uint8_t *>(buf),
+                           (uint32_t)bytes, sink, grid);
+    else
+        hipLaunchKernelGGL(stream_read_kernel<3>, dim3(grid), dim3(kSThreads), 0, st, static_cast<const uint8_t *>(buf),
+                           (uint32_t)bytes, sink, grid);
     return hipGetLastError();
 }
 

@@ -376,7 +376,8 @@ nm_status nm_unpack(const uint32_t *masks, const nm_bf16 *values, int64_t R, int
 /*
  * nm_stream_read -- measurement aid, not part of the method: reads `bytes` bytes at `buf`
  * once, with the same 16-byte non-temporal loads and 512-thread workgroups as the
- * matrix-vector kernels, and writes one XOR-fold of the dwords per wave to
+ * matrix-vector kernels (one workgroup per CU, 3-4 KiB in flight per wave: the fastest
+ * plain read found), and writes one XOR-fold of the dwords per wave to
  * sink[0 .. nm_stream_read_sink_words(bytes)).  Timed under the same rotation of
  * distinct buffers as the SpMV, it gives the rate a kernel that only streams reaches --
  * the achievable figure the SpMV's % of the 8 TB/s peak is read against.  The XOR of all

@@ -274,9 +274,10 @@ def test_stream_read_rejects_bad_arguments(L):
     # one fold per wave: 8 per 512-thread workgroup, at most 1024 workgroups, and at least
     # one 2 KiB unit per wave (16 KiB per workgroup)
     assert L.nm_stream_read_sink_words(16) == 8
-    assert L.nm_stream_read_sink_words(1 << 31) == 1024 * 8
-    assert L.nm_stream_read_sink_words(32768 * 3) == 3 * 8  # two 2 KiB units per wave at least
-    assert L.nm_stream_read_sink_words(32768 * 3 + 16) == 4 * 8
+    assert L.nm_stream_read_sink_words(1 << 31) == 256 * 8  # one 8-wave workgroup per CU of 256
+    assert L.nm_stream_read_sink_words(16384 * 3) == 3 * 8  # two 1 KiB units per wave at least
+    assert L.nm_stream_read_sink_words(16384 * 3 + 16) == 3 * 8
+    assert L.nm_stream_read_sink_words(16384 * 4) == 4 * 8
     words = L.nm_stream_read_sink_words(1 << 20)
     assert L.nm_stream_read(None, 1 << 20, A16, words, None) == NM_ERR_NULL
     assert L.nm_stream_read(A16, 1 << 20, None, words, None) == NM_ERR_NULL
