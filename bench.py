@@ -492,7 +492,10 @@ def target_check(per, patterns):
             row = {"pct_peak": e["pct_peak"], "speedup_vs_dense": e["speedup_vs_dense"],
                    "pct_ok": e["pct_peak"] >= TARGET_PCT, "speedup_ok": e["speedup_vs_dense"] >= TARGET_SPEEDUP}
             if "stream_read" in d:
+                # a plain read of the launch's bytes below the bar: no kernel of this size
+                # can reach it, whatever its walk costs
                 row["stream_read_pct_peak"] = d["stream_read"]["pct_peak"]
+                row["pct_reachable_by_plain_read"] = d["stream_read"]["pct_peak"] >= TARGET_PCT
             out[f"{label} {N}:{M}"] = row
     return out
 
@@ -641,7 +644,9 @@ def main():
     log("stream read of the same bytes (achievable): " + ", ".join(stream_log))
     check = target_check(per, patterns)
     log("per-layer target (>= 70% of peak, >= 1.5x dense): " + ", ".join(
-        f"{k} {'pass' if v['pct_ok'] and v['speedup_ok'] else 'FAIL'}" for k, v in check.items()))
+        f"{k} {'pass' if v['pct_ok'] and v['speedup_ok'] else 'FAIL'}"
+        + ("" if v.get("pct_reachable_by_plain_read", True) else f" (plain read {v['stream_read_pct_peak']}%)")
+        for k, v in check.items()))
 
     # ---------------------------------------------------------------- metadata formats
     # The same product over the first pattern's packs with the metadata as uint8 offsets
