@@ -88,7 +88,7 @@ MvPlan plan_spmv(int64_t R, int64_t K, int B, const DeviceInfo &dev, int fmt = k
 // The walk of a one-matrix bitmask launch: the half-row or the strip walk where one of
 // them applies (one token, no split rows), else `word` as is.
 MvPlan plan_spmv_one(const MvPlan &word, int64_t R, int64_t K, int B, const DeviceInfo &dev);
-size_t spmv_lds_per_word(int B);  // LDS bytes of x per 32-column block
+size_t spmv_lds_per_word(int B);  // LDS bytes of x per 32-column block, blocked layout (unstructured kernel)
 // Fixed device scratch for callers that cannot allocate (nm_spmv_noalloc): its device
 // address on the current device (looked up once per device), kSpmvScratchBytes long.
 constexpr size_t kSpmvScratchBytes = (size_t)4 << 20;

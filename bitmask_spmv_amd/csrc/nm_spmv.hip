@@ -125,30 +125,35 @@ __device__ __forceinline__ uint32_t pair_swap(uint32_t v) {
 // the input contract) walks the low 16 columns of its own block instead, so each of the
 // 16 bit scans finds a set bit.
 //
-// One or two tokens (bitmask and uint8 offsets): no value exchange between the lanes of
-// a pair.  Lane 2i holds values 0..7 of words i and 32+i of the strip (the first halves
-// of its two 16-byte chunks), lane 2i+1 values 8..15 of the same two words, and each
-// walks its eight values of both words: even lanes from the lowest kept column up, odd
-// lanes from the highest down (the lowest set bits of the bit-reversed mask word; for
+// One token (bitmask and uint8 offsets; blocked x): no value exchange between the lanes
+// of a pair.  Lane 2i holds values 0..7 of words i and 32+i of the strip (the first
+// halves of its two 16-byte chunks), lane 2i+1 values 8..15 of the same two words, and
+// each walks its eight values of both words: even lanes from the lowest kept column up,
+// odd lanes from the highest down (the lowest set bits of the bit-reversed mask word; for
 // uint8 the offset bytes in reverse order).  Only the partner's metadata crosses lanes
 // (one or two DPP moves), and each lane runs two independent chains of eight steps.  The
 // bitmask and uint8 walks visit the same kept weights in the same order on the same
-// lane, so their fp32 sums agree bit for bit.  At three or four tokens the exchange of
-// value halves below is the faster of the two.
+// lane, so their fp32 sums agree bit for bit.
+//
+// Two or more tokens (panel x): the exchange of value halves below gives every lane one
+// whole word, lane 2i word i and lane 2i+1 word 32+i, and the panel layout gives each
+// lane's block LDS banks of its own (measured against the walk without exchange on
+// blocked x at two tokens: 1-6% faster on the Llama-3.1-8B and -3.3-70B shapes).
 template <int FMT, int B>
 __device__ __forceinline__ void walk_batch(const Batch<FMT> &bt, const uint32_t *xs, int nws, float (&acc)[B]) {
     constexpr int kBlk = XLayout<B>::kBlk;
+    constexpr bool kPanel = B >= 2;  // x in the panel layout (else blocked)
     if constexpr (FMT == kMetaI32) {
         const uint32_t v[8] = {bt.va.x, bt.va.y, bt.va.z, bt.va.w, bt.vb.x, bt.vb.y, bt.vb.z, bt.vb.w};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int w = bt.lw + 16 * q;
-            const uint32_t *blk = xs + (w < nws ? w : 0) * kBlk;
-            dot_pair<B>(v[2 * q], blk, (int)(bt.meta[q].x & 31u), (int)(bt.meta[q].y & 31u), acc);
-            dot_pair<B>(v[2 * q + 1], blk, (int)(bt.meta[q].z & 31u), (int)(bt.meta[q].w & 31u), acc);
+            const int w = bt.lw + 16 * q < nws ? bt.lw + 16 * q : 0;
+            const uint32_t *blk = kPanel ? xs + panel_block<B>(w) : xs + w * kBlk;
+            dot_pair<B, kPanel>(v[2 * q], blk, (int)(bt.meta[q].x & 31u), (int)(bt.meta[q].y & 31u), acc);
+            dot_pair<B, kPanel>(v[2 * q + 1], blk, (int)(bt.meta[q].z & 31u), (int)(bt.meta[q].w & 31u), acc);
         }
-    } else if constexpr (B <= 2) {
-        constexpr int kCol = XLayout<B>::S * 2;  // LDS bytes of one column (its token slots)
+    } else if constexpr (B == 1) {
+        constexpr int kCol = 2;  // LDS bytes of one column
         const bool odd = threadIdx.x & 1;
         const int wa = odd ? bt.lw - 32 : bt.lw, wb = wa + 32;  // words i and 32+i of the strip
         const bool oka = wa < nws, okb = wb < nws;
@@ -177,10 +182,10 @@ __device__ __forceinline__ void walk_batch(const Batch<FMT> &bt, const uint32_t 
                 mb &= mb - 1;
                 const int b1 = __builtin_ctz(mb);
                 mb &= mb - 1;
-                dot_pair_at<B>(__builtin_amdgcn_perm(av[k], av[3 - k], vsel), x8 + ba + flip + dir * a0,
-                               x8 + ba + flip + dir * a1, acc);
-                dot_pair_at<B>(__builtin_amdgcn_perm(bv[k], bv[3 - k], vsel), x8 + bb + flip + dir * b0,
-                               x8 + bb + flip + dir * b1, acc);
+                dot_pair_at(__builtin_amdgcn_perm(av[k], av[3 - k], vsel), x8 + ba + flip + dir * a0,
+                            x8 + ba + flip + dir * a1, acc[0]);
+                dot_pair_at(__builtin_amdgcn_perm(bv[k], bv[3 - k], vsel), x8 + bb + flip + dir * b0,
+                            x8 + bb + flip + dir * b1, acc[0]);
             }
         } else {
             // offsets of the lane's eight values of each word: even lanes bytes 0..7 of
@@ -196,10 +201,10 @@ __device__ __forceinline__ void walk_batch(const Batch<FMT> &bt, const uint32_t 
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const uint32_t pa = oa[k >> 1] >> (16 * (k & 1)), pb = ob[k >> 1] >> (16 * (k & 1));
-                dot_pair_at<B>(__builtin_amdgcn_perm(av[k], av[3 - k], vsel), x8 + ba + kCol * (int)(pa & 31u),
-                               x8 + ba + kCol * (int)((pa >> 8) & 31u), acc);
-                dot_pair_at<B>(__builtin_amdgcn_perm(bv[k], bv[3 - k], vsel), x8 + bb + kCol * (int)(pb & 31u),
-                               x8 + bb + kCol * (int)((pb >> 8) & 31u), acc);
+                dot_pair_at(__builtin_amdgcn_perm(av[k], av[3 - k], vsel), x8 + ba + kCol * (int)(pa & 31u),
+                            x8 + ba + kCol * (int)((pa >> 8) & 31u), acc[0]);
+                dot_pair_at(__builtin_amdgcn_perm(bv[k], bv[3 - k], vsel), x8 + bb + kCol * (int)(pb & 31u),
+                            x8 + bb + kCol * (int)((pb >> 8) & 31u), acc[0]);
             }
         }
     } else {
@@ -213,7 +218,13 @@ __device__ __forceinline__ void walk_batch(const Batch<FMT> &bt, const uint32_t 
         const uint32_t r_x = pair_swap(s_x), r_y = pair_swap(s_y), r_z = pair_swap(s_z), r_w = pair_swap(s_w);
         const uint32_t v[8] = {odd ? r_x : bt.va.x, odd ? r_y : bt.va.y, odd ? r_z : bt.va.z, odd ? r_w : bt.va.w,
                                odd ? bt.vb.x : r_x, odd ? bt.vb.y : r_y, odd ? bt.vb.z : r_z, odd ? bt.vb.w : r_w};
-        const uint32_t *blk = xs + (ok ? bt.lw : 0) * kBlk;  // this word's 32 columns
+        // this word's 32 columns: word bt.lw is the lane's own word of its strip, so its
+        // panel and stripe follow from the lane (panel_block for that word, without the
+        // per-batch arithmetic); a lane past the slice reads block 0 (staged, finite x)
+        using P = XPanel<B>;
+        const int ln = threadIdx.x & (kWave - 1);
+        const uint32_t *blk = ok ? xs + ((bt.lw >> 6) * P::kColDw + ln / P::kGroup) * P::kPanelDw + (ln % P::kGroup) * P::kColDw
+                                 : xs;
         uint32_t mm = ok && __builtin_popcount(bt.meta[0].x) == 16 ? bt.meta[0].x : 0xFFFFu;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
@@ -228,7 +239,7 @@ __device__ __forceinline__ void walk_batch(const Batch<FMT> &bt, const uint32_t 
                 c0 = (int)(o & 31u);
                 c1 = (int)((o >> 8) & 31u);
             }
-            dot_pair<B>(v[k], blk, c0, c1, acc);
+            dot_pair<B, kPanel>(v[k], blk, c0, c1, acc);
         }
     }
 }
@@ -320,7 +331,7 @@ __global__ __launch_bounds__(NT, NT == 1024 ? 8 : 1) void spmv_kernel(const void
                                                                       const uint16_t *__restrict__ x, int64_t ldx,
                                                                       int slice, float *__restrict__ partial,
                                                                       const SpmvSet set) {
-    extern __shared__ uint32_t xs[];  // [nws][XLayout<B>::kBlk]
+    extern __shared__ uint32_t xs[];  // x: [nws][XLayout<1>::kBlk] at one token, else whole strips of panels
     const int s = blockIdx.y;
     const int w0 = s * slice;
     const int nws = min(slice, KW - w0);
@@ -360,7 +371,7 @@ __global__ __launch_bounds__(NT, NT == 1024 ? 8 : 1) void spmv_kernel(const void
     // Stage this slice of x into LDS; batch 0's loads go out right after the first round
     // of x loads, so waiting for x (an L2 hit after the first workgroup of an XCD) never
     // waits for the weights queued behind it.
-    stage_x<B, NT>(xs, x, ldx, w0, nws, [&] {
+    stage_x<B, NT, (B >= 2)>(xs, x, ldx, w0, nws, [&] {
         load_row_batch<FMT, EPI>(bufA, set, meta0, values0, min(rowA, R - 1), KW, w0, total > 0 ? nws : 0, 0, lane);
     });
     __syncthreads();
@@ -412,7 +423,7 @@ template <int B, int EPI>
 __global__ __launch_bounds__(kHalfThreads, 8) void spmv_half_kernel(const void *meta0, const uint16_t *values0, int R,
                                                                     int KW, const uint16_t *__restrict__ x,
                                                                     int64_t ldx, const SpmvSet set) {
-    static_assert(EPI == kEpiOne, "one matrix per launch");
+    static_assert(EPI == kEpiOne && B == 1, "one matrix and one token per launch (blocked x)");
     extern __shared__ uint32_t xs[];  // x [KW][kBlk], then totals [rows][2][B], then counters [rows]
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -476,7 +487,7 @@ __global__ __launch_bounds__(NT, NT == 1024 ? 8 : 1) void spmv_strip_kernel(cons
                                                                             int R, int KW, int rpw,
                                                                             const uint16_t *__restrict__ x,
                                                                             int64_t ldx, const SpmvSet set) {
-    static_assert(EPI == kEpiOne, "one matrix per launch");
+    static_assert(EPI == kEpiOne && B == 1, "one matrix and one token per launch (blocked x)");
     constexpr int W = NT / kWave;
     extern __shared__ uint32_t xs[];  // x [KW][kBlk], then strip totals [rpw * nb][B]
     const int lane = threadIdx.x & (kWave - 1);
@@ -704,6 +715,13 @@ hipError_t launch_f(const MvPlan &p, const SpmvSet &set, int64_t K, const uint16
 
 size_t spmv_lds_per_word(int B) { return (size_t)blk_dwords(B) * 4; }
 
+// x of the N:M word walk: blocked at one token; at two or more tokens the panel layout,
+// 64*S bytes per word in whole 64-word strips (S = 2, 4 or 8 token slots per column).
+static size_t spmv_x_bytes_per_word(int B) { return B == 1 ? (size_t)blk_dwords(1) * 4 : (size_t)64 * (B <= 2 ? 2 : B <= 4 ? 4 : 8); }
+static size_t spmv_x_lds_bytes(int64_t nws, int B) {
+    return spmv_x_bytes_per_word(B) * (size_t)(B == 1 ? nws : (nws + kWave - 1) / kWave * kWave);
+}
+
 // Device-resident scratch of the no-allocation entry point: the fp32 partial sums of split
 // rows, in a fixed array of kSpmvScratchBytes on every device the library runs on (held
 // until the process ends).  In host code `scratch` only names the symbol; its device
@@ -734,7 +752,7 @@ MvPlan plan_spmv(int64_t R, int64_t K, int B, const DeviceInfo &dev, int fmt) {
     MvPlan p;
     p.threads = kThreads;
     const int64_t KW = K / 32;
-    const int64_t bytes_per_word = (int64_t)blk_dwords(B) * 4;
+    const int64_t bytes_per_word = (int64_t)spmv_x_bytes_per_word(B);
     size_t cap = kLdsCap;
     if (dev.max_lds_per_block > 0 && (size_t)dev.max_lds_per_block < cap) cap = (size_t)dev.max_lds_per_block;
     int64_t max_slice = (int64_t)cap / bytes_per_word;
@@ -757,7 +775,7 @@ MvPlan plan_spmv(int64_t R, int64_t K, int B, const DeviceInfo &dev, int fmt) {
     splits = (KW + slice - 1) / slice;
     p.splits = (int)splits;
     p.slice = (int)slice;
-    p.lds_bytes = (size_t)slice * bytes_per_word;
+    p.lds_bytes = spmv_x_lds_bytes(slice, B);
     int per_cu = (int)(kLdsPerCu / (p.lds_bytes > 0 ? p.lds_bytes : 1));
     if (per_cu > 4) per_cu = 4;
     if (per_cu < 1) per_cu = 1;

@@ -9,11 +9,12 @@
 namespace nmk {
 namespace {
 
-// LDS layout of x.  B = 1: each 32-column block is 16 dwords of bf16 pairs plus one pad
-// dword (17 dwords), so lanes walking different words spread over the banks.  B > 1:
-// tokens are interleaved per column -- column c holds S bf16 (S = B rounded up to 2, 4
-// or 8, zero-filled) -- so one 4/8/16-byte LDS load gathers a column for every token;
-// blocks are 16*S dwords plus S/2 pad dwords (keeping 8/16-byte alignment).
+// Blocked LDS layout of x (the one-token word walk, and the unstructured kernel at every
+// B).  B = 1: each 32-column block is 16 dwords of bf16 pairs plus one pad dword (17
+// dwords), so lanes walking different words spread over the banks.  B > 1: tokens are
+// interleaved per column -- column c holds S bf16 (S = B rounded up to 2, 4 or 8,
+// zero-filled) -- so one 4/8/16-byte LDS load gathers a column for every token; blocks
+// are 16*S dwords plus S/2 pad dwords (keeping 8/16-byte alignment).
 template <int B>
 struct XLayout {
     static constexpr int S = B == 1 ? 1 : (B <= 2 ? 2 : (B <= 4 ? 4 : 8));
@@ -24,6 +25,35 @@ constexpr int blk_dwords(int B) {
     return B == 1 ? 17 : (B <= 2 ? 33 : (B <= 4 ? 66 : 132));
 }
 
+// Panel LDS layout of x (the N:M word walk at B >= 2).  Columns hold the same S
+// interleaved token slots (S/2 dwords), but a block's 32 columns are stacked at a stride
+// of 64 dwords: a panel is 32 rows of 64 dwords, and the 128/S blocks side by side in it
+// each own one stripe of S/2 dwords of every row.  In the word walk lane 2i walks word i
+// of its 64-word strip and lane 2i+1 word 32+i; block j of a strip goes to the panel and
+// stripe of that lane, L = 2j (j < 32) or 2j - 63, so every lane gathers from LDS banks
+// that no other lane of its group of 128/S lanes touches, whatever columns the masks
+// pick (the blocked layout puts the columns of different lanes' words on shared banks at
+// random: about half the LDS cycles of the walk went to bank conflicts at 2-4 tokens).
+// A 64-word strip takes S/2 panels (64*S bytes per word); the layout is defined for
+// every word index, so a lane may gather from any block.
+template <int B>
+struct XPanel {
+    static constexpr int S = XLayout<B>::S;
+    static constexpr int kColDw = S / 2;           // dwords per column (the token slots)
+    static constexpr int kGroup = 128 / S;         // blocks side by side in one panel
+    static constexpr int kRowDw = 64;              // dwords per panel row (column stride)
+    static constexpr int kPanelDw = 32 * kRowDw;   // dwords per panel
+    static constexpr int kWordBytes = 64 * S;      // LDS bytes per word, in whole strips
+};
+
+// Dword offset of column 0 of block w (w counted from the slice start) in the panel layout.
+template <int B>
+__device__ __forceinline__ int panel_block(int w) {
+    using P = XPanel<B>;
+    const int j = w & 63, L = j < 32 ? 2 * j : 2 * j - 63;
+    return ((w >> 6) * P::kColDw + L / P::kGroup) * P::kPanelDw + (L % P::kGroup) * P::kColDw;
+}
+
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -32,17 +62,18 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
 }
 
-// Gather of one column for the S token slots (S/2 dwords: token pairs).
-template <int S>
+// Gather of one column for the S token slots (S/2 dwords: token pairs); CS is the
+// column stride in dwords (S/2 in the blocked layout, 64 in the panel layout).
+template <int S, int CS>
 __device__ __forceinline__ void gather_col(const uint32_t *blk, int c, uint32_t (&d)[S / 2]) {
     if constexpr (S == 2) {
-        d[0] = blk[c];
+        d[0] = blk[CS * c];
     } else if constexpr (S == 4) {
-        const u32x2 t = *reinterpret_cast<const u32x2 *>(blk + 2 * c);
+        const u32x2 t = *reinterpret_cast<const u32x2 *>(blk + CS * c);
         d[0] = t.x;
         d[1] = t.y;
     } else {
-        const u32x4 t = *reinterpret_cast<const u32x4 *>(blk + 4 * c);
+        const u32x4 t = *reinterpret_cast<const u32x4 *>(blk + CS * c);
         d[0] = t.x;
         d[1] = t.y;
         d[2] = t.z;
@@ -51,18 +82,21 @@ __device__ __forceinline__ void gather_col(const uint32_t *blk, int c, uint32_t 
 }
 
 // One pair of kept weights: the inputs of columns c0 and c1 of the word's block (per
-// token) meet the packed value pair v in one v_dot2_f32_bf16.
-template <int B>
+// token) meet the packed value pair v in one v_dot2_f32_bf16.  PANEL: blk is the block's
+// column 0 in the panel layout (B >= 2), else in the blocked layout.
+template <int B, bool PANEL = false>
 __device__ __forceinline__ void dot_pair(uint32_t v, const uint32_t *blk, int c0, int c1, float (&acc)[B]) {
     constexpr int S = XLayout<B>::S;
+    static_assert(!PANEL || S > 1, "the panel layout holds two or more token slots");
+    constexpr int CS = PANEL ? XPanel<B>::kRowDw : S / 2;
     if constexpr (S == 1) {
         const uint16_t *xw = reinterpret_cast<const uint16_t *>(blk);
         const uint32_t pr = (uint32_t)xw[c0] | ((uint32_t)xw[c1] << 16);
         acc[0] = dot2_bf16(v, pr, acc[0]);
     } else {
         uint32_t d0[S / 2], d1[S / 2];
-        gather_col<S>(blk, c0, d0);
-        gather_col<S>(blk, c1, d1);
+        gather_col<S, CS>(blk, c0, d0);
+        gather_col<S, CS>(blk, c1, d1);
 #pragma unroll
         for (int j = 0; j < S / 2; ++j) {
             // (token 2j of column c0, token 2j of column c1), then the same for 2j+1
@@ -73,20 +107,11 @@ __device__ __forceinline__ void dot_pair(uint32_t v, const uint32_t *blk, int c0
     }
 }
 
-// The same with the two columns given by the LDS byte addresses of their token slots
-// (one or two tokens).
-template <int B>
-__device__ __forceinline__ void dot_pair_at(uint32_t v, const uint8_t *p0, const uint8_t *p1, float (&acc)[B]) {
-    static_assert(B <= 2, "one or two tokens");
-    if constexpr (B == 1) {
-        const uint32_t pr = (uint32_t)*reinterpret_cast<const uint16_t *>(p0) |
-                            ((uint32_t)*reinterpret_cast<const uint16_t *>(p1) << 16);
-        acc[0] = dot2_bf16(v, pr, acc[0]);
-    } else {
-        const uint32_t d0 = *reinterpret_cast<const uint32_t *>(p0), d1 = *reinterpret_cast<const uint32_t *>(p1);
-        acc[0] = dot2_bf16(v, __builtin_amdgcn_perm(d1, d0, 0x05040100u), acc[0]);
-        acc[1] = dot2_bf16(v, __builtin_amdgcn_perm(d1, d0, 0x07060302u), acc[1]);
-    }
+// The same at one token, with the two columns given by their LDS byte addresses.
+__device__ __forceinline__ void dot_pair_at(uint32_t v, const uint8_t *p0, const uint8_t *p1, float &acc) {
+    const uint32_t pr = (uint32_t)*reinterpret_cast<const uint16_t *>(p0) |
+                        ((uint32_t)*reinterpret_cast<const uint16_t *>(p1) << 16);
+    acc = dot2_bf16(v, pr, acc);
 }
 
 // Matrix of the set that owns global row r (0 <= r < R).  The launcher pads row0 past
@@ -103,12 +128,14 @@ __device__ __forceinline__ int owner(const SpmvSet &set, int r) {
 }
 
 // Stages columns [32*w0, 32*(w0+nws)) of x (B tokens, row stride ldx) into LDS in the
-// XLayout<B> layout, all NT threads of the workgroup taking part; first_round() runs
-// once, right after the first round of x loads has been issued (callers put their first
-// weight loads there).  The caller synchronises the workgroup afterwards.
-template <int B, int NT, class F>
+// blocked layout, or in the panel layout (PANEL, B >= 2), all NT threads of the workgroup
+// taking part; first_round() runs once, right after the first round of x loads has been
+// issued (callers put their first weight loads there).  The caller synchronises the
+// workgroup afterwards.
+template <int B, int NT, bool PANEL = false, class F>
 __device__ __forceinline__ void stage_x(uint32_t *xs, const uint16_t *__restrict__ x, int64_t ldx, int w0, int nws,
                                         F &&first_round) {
+    static_assert(!PANEL || XLayout<B>::S > 1, "the panel layout holds two or more token slots");
     if constexpr (XLayout<B>::S == 1) {
         // 16-byte loads; 8 bf16 per chunk, 4 chunks per 32-column block.  No load sits under
         // a lane condition: the part of a round beyond the slice is skipped by a uniform
@@ -174,7 +201,6 @@ __device__ __forceinline__ void stage_x(uint32_t *xs, const uint16_t *__restrict
                 const int i = min(i0 + j * NT + (int)threadIdx.x, octs - 1);
                 {
                     const int c = 8 * i;  // first column of the eight, within the slice
-                    u32x4 *d = reinterpret_cast<u32x4 *>(xs + (c >> 5) * XLayout<B>::kBlk + (c & 31) * (S / 2));
                     uint32_t col[4 * S];  // column c+k: dwords k*S/2 .. k*S/2 + S/2 - 1
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
@@ -185,8 +211,25 @@ __device__ __forceinline__ void stage_x(uint32_t *xs, const uint16_t *__restrict
                                 __builtin_amdgcn_perm(r[j][2 * t + 1][q], r[j][2 * t][q], 0x07060302u);
                         }
                     }
+                    if constexpr (PANEL) {
+                        // eight columns of one block: one S/2-dword store per column, 64 dwords apart
+                        uint32_t *d = xs + panel_block<B>(c >> 5) + (c & 31) * XPanel<B>::kRowDw;
 #pragma unroll
-                    for (int v = 0; v < S; ++v) d[v] = u32x4{col[4 * v], col[4 * v + 1], col[4 * v + 2], col[4 * v + 3]};
+                        for (int k = 0; k < 8; ++k) {
+                            if constexpr (S == 2) {
+                                d[k * XPanel<B>::kRowDw] = col[k];
+                            } else if constexpr (S == 4) {
+                                *reinterpret_cast<u32x2 *>(d + k * XPanel<B>::kRowDw) = u32x2{col[2 * k], col[2 * k + 1]};
+                            } else {
+                                *reinterpret_cast<u32x4 *>(d + k * XPanel<B>::kRowDw) =
+                                    u32x4{col[4 * k], col[4 * k + 1], col[4 * k + 2], col[4 * k + 3]};
+                            }
+                        }
+                    } else {
+                        u32x4 *d = reinterpret_cast<u32x4 *>(xs + (c >> 5) * XLayout<B>::kBlk + (c & 31) * (S / 2));
+#pragma unroll
+                        for (int v = 0; v < S; ++v) d[v] = u32x4{col[4 * v], col[4 * v + 1], col[4 * v + 2], col[4 * v + 3]};
+                    }
                 }
             }
         }

@@ -7,7 +7,7 @@
 // with the stored values ("SparseDecoding: Decoding-Aware Pruning ..." (ai.info summary),
 // Methodology Steps 2-3; "SparseDecoding:解码感知的准确高效大模型剪枝框架"
 // (paper.rainbus.top), 方法步骤详情 第四步) -- for B = 5..8 input vectors, and for B = 3..4
-// where a row's x no longer fits the word-per-lane kernel's LDS slice (K > 8192).
+// where a row's x no longer fits the word-per-lane kernel's LDS slice (K > 10240).
 //
 // Why a second kernel: with one lane per mask word, every kept weight costs a gather of
 // its input column for all B tokens from LDS (16 bytes at B = 8, at a data-dependent

@@ -107,7 +107,7 @@ nm_status nm_prune_pack(const nm_bf16 *W, int64_t ldw, int64_t R, int64_t K, con
  * clear it), pairing the t-th set bit with values[16w+t].  The kernel does not depend
  * on M: every 50% pattern has 16 set bits per word.  Products and sums are fp32; y is
  * rounded to nearest even bf16.  For 5 <= B <= 8 and K a multiple of 1024 (and for
- * B = 3 or 4 with such a K above 8192 on at least two rows per compute unit) the walk
+ * B = 3 or 4 with such a K above 10240 on at least two rows per compute unit) the walk
  * writes each kept value into a dense 16-row tile in LDS and the tile is multiplied by
  * the B inputs on the matrix cores (bf16 products, fp32 sums); that path uses no
  * workspace (the size query covers both paths).

@@ -156,6 +156,25 @@ def test_spmv_within_tolerance(R, K, B):
     assert_within(host_bf16(y), yref, absum, f"spmv R={R} K={K} B={B}")
 
 
+@pytest.mark.parametrize("B", [2, 3, 4, 5, 8])
+def test_spmv_word_walk_ragged_strips(B):
+    # 4160 columns = 130 words: two whole 64-word strips and a 2-word strip, and K is no
+    # multiple of 1024, so every B takes the word-per-lane walk (x in whole strips of LDS
+    # panels at B >= 2, the last one mostly unused).  600 rows keep whole rows in one
+    # slice up to four tokens (at 5-8 tokens the x of 130 words exceeds one slice: slices
+    # of 128 and 2 words); 9 rows are cut into the same two slices to spread the work.
+    say("spmv ragged strips", B)
+    for R, splits in ((600, 1 if B <= 4 else 2), (9, 2)):
+        p = nm.nm_spmv_plan(R, 4160, B)
+        assert p["kernel"] == 0 and p["splits"] == splits, p
+        W = synth.weights(R, 4160, 23, R, B)
+        mref, vref = oracle.prune_pack(W, oracle.col_norm(synth.calib_acts(4160, 23, R)), 4, 8)
+        x = synth.decode_x(B, 4160, 23, R, B)
+        y = nm.nm_spmv(dev_u32(mref), dev_bf16(vref), dev_bf16(x))
+        yref, absum = oracle.spmv(mref, vref, x, 4160, nthreads=4)
+        assert_within(host_bf16(y), yref, absum, f"spmv ragged strips R={R} B={B}")
+
+
 @pytest.mark.parametrize("B", [3, 4, 5, 6, 7])
 def test_spmv_every_batch_size(B):
     say("spmv batch", B)
@@ -178,8 +197,8 @@ def test_spmv_every_batch_size(B):
 # * the tile kernel at B = 3/4 where a row's x exceeds the word-per-lane LDS slice.
 WIDE = [(3000, 8192, 3, (0, 1024, 1)), (2100, 8192, 4, (0, 1024, 1)), (4096, 8192, 1, (0, 1024, 1)),
         (4096, 16384, 2, (0, 1024, 1)), (2048, 28672, 2, (0, 1024, 2)), (1000, 28672, 1, (0, 256, 1)),
-        (300, 28672, 3, (0, 256, 4)), (1024, 8192, 1, (0, 256, 1)), (700, 28672, 4, (1, 1024, 1)),
-        (2049, 9216, 3, (1, 512, 1))]
+        (300, 28672, 3, (0, 256, 3)), (1024, 8192, 1, (0, 256, 1)), (700, 28672, 4, (1, 1024, 1)),
+        (2049, 11264, 3, (1, 512, 1))]
 
 
 @pytest.mark.parametrize("R,K,B,plan", WIDE)

@@ -34,7 +34,7 @@ SHAPES = [(256, 512), (1000, 4096), (513, 5120), (17, 8192), (3, 28672), (1, 32)
 # 8192 columns) and B = 4 (x allows two workgroups per CU), the tile kernel at B = 3 for a
 # row of x beyond the word-per-lane LDS slice.
 WIDE = [(2048, 8192, 1, (0, 1024)), (2048, 8192, 2, (0, 1024)), (1500, 8192, 4, (0, 1024)),
-        (1100, 9216, 3, (1, 512))]
+        (1100, 11264, 3, (1, 512))]
 
 
 @pytest.mark.parametrize("R,K,B", [(R, K, B) for R, K in SHAPES for B in (1, 3, 8)] + [w[:3] for w in WIDE])

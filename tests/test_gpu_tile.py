@@ -190,10 +190,11 @@ def test_tile_swiglu_two_tiles_per_step(R, B):
     assert ok.all(), f"swiglu two per step R={R} B={B}: {int((~ok).sum())} outside"
 
 
-# B = 3 or 4 with K above 8192 columns (a row's x exceeds the word-per-lane kernel's LDS
-# slice) and at least 512 rows: these launches run on the tile path too.
-@pytest.mark.parametrize("R,K,B", [(4096, 14336, 4), (1000, 9216, 3), (513, 12288, 4), (2048, 28672, 3)])
+# B = 3 or 4 with K above 10240 columns (a row's x exceeds the word-per-lane kernel's
+# LDS slice) and at least 512 rows: these launches run on the tile path too.
+@pytest.mark.parametrize("R,K,B", [(4096, 14336, 4), (1000, 11264, 3), (513, 12288, 4), (2048, 28672, 3)])
 def test_tile_small_batch_wide_rows(R, K, B):
+    assert nm.nm_spmv_plan(R, K, B)["kernel"] == nm.NM_KERNEL_TILE
     say("tile small batch wide", R, K, B)
     W = synth.weights(R, K, 40, R, K, B)
     mref, vref = oracle.prune_pack(W, oracle.col_norm(synth.calib_acts(K, 40, R)), 8, 16)
@@ -206,7 +207,7 @@ def test_tile_small_batch_wide_rows(R, K, B):
 @pytest.mark.parametrize("B", [3, 4])
 def test_tile_small_batch_multi_and_swiglu(B):
     say("tile small batch multi+swiglu", B)
-    K = 10240
+    K = 11264
     x = synth.decode_x(B, K, 41, B)
     n = oracle.col_norm(synth.calib_acts(K, 41, B))
     packed, refs = [], []
