@@ -89,11 +89,23 @@ __device__ __forceinline__ double sqrt_rn_f64(double s) {
 
 // Sum over the 64 lanes of a wavefront, returned in every lane.  Four DPP steps
 // (quad swaps, half-row and row mirrors) leave each 16-lane row holding its row sum;
-// the four row sums are then read out and added in a fixed order, so the result does
-// not depend on timing.
+// the rows then meet through the gfx950 lane swaps (rows 0+1 and 2+3, then the two
+// halves), added in a fixed order in every lane, so the result does not depend on
+// timing: (r0 + r1) + (r2 + r3).
 template <int kCtrl>
 __device__ __forceinline__ float dpp_add(float v) {
     return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+
+// Lanes at the same position of the four 16-lane rows added, (r0 + r1) + (r2 + r3), the
+// result in all four of them.
+__device__ __forceinline__ float cross_rows_sum(float v) {
+    const uint32_t u = __float_as_uint(v);
+    const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);  // [r0 r0 r2 r2], [r1 r1 r3 r3]
+    const float w = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    const uint32_t uw = __float_as_uint(w);
+    const auto q = __builtin_amdgcn_permlane32_swap(uw, uw, false, false);  // [lo lo], [hi hi]
+    return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -101,11 +113,7 @@ __device__ __forceinline__ float wave_sum(float v) {
     v = dpp_add<0x4E>(v);   // quad_perm(2,3,0,1)
     v = dpp_add<0x141>(v);  // row_half_mirror
     v = dpp_add<0x140>(v);  // row_mirror
-    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-    return (r0 + r1) + (r2 + r3);
+    return cross_rows_sum(v);
 }
 
 // Gated-MLP epilogue (kEpiSwiGLU, nm_kernels.h): h = silu(g) * u in fp32.

@@ -33,6 +33,8 @@
 #include <atomic>
 #include <mutex>
 
+#include <type_traits>
+
 #include "nm_device.h"
 #include "nm_kernels.h"
 #include "nm_spmv_common.h"
@@ -106,9 +108,11 @@ __device__ __forceinline__ void load_batch(Batch<FMT> &bt, const uint8_t *mrow, 
     }
 }
 
-// Swap one dword with the neighbouring lane of the pair (lane ^ 1).
+// Swap one dword with the neighbouring lane of the pair (lane ^ 1).  Every lane has a
+// source lane, so the "old" operand is never read; passing v itself saves the compiler a
+// register set to zero where v is not needed afterwards.
 __device__ __forceinline__ uint32_t pair_swap(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);  // quad_perm(1,0,3,2)
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xF, 0xF, false);  // quad_perm(1,0,3,2)
 }
 
 // Walk of one batch: 8 pairs of kept weights per lane.
@@ -259,9 +263,57 @@ __device__ __forceinline__ void locate(const SpmvSet &set, int r, int &p, int &l
     }
 }
 
-// Row finished: wave reduction (uniform across the wave), then lane 0 writes the output
-// -- the bf16 row; for the gated MLP h = silu(g) * u once the up row of a pair is done,
-// the gate total kept in gsave until then; for a split launch the row's fp32 partial.
+// Token whose row total lane `lane` holds after wave_sum_tokens<B> (2 <= B <= 4): lanes
+// 0..3 hold tokens 0, 2, 1, 3 at B = 3-4, lanes 0..1 tokens 0, 1 at B = 2 (and every
+// further lane repeats the pattern of its lane % 4).
+template <int B>
+__device__ __forceinline__ int token_of_lane(int lane) {
+    return B == 2 ? (lane & 1) : 2 * (lane & 1) + ((lane >> 1) & 1);
+}
+
+// Row totals of B = 2..4 tokens at once: the first exchanges halve the tokens per lane
+// (lane pairs swap half of their partial sums, then lane pairs two apart), so each lane
+// adds one token's partials from then on: rotations by 4 and 8 within each 16-lane row
+// and the cross-row sum.  Lane i ends with the total of token token_of_lane<B>(i); a
+// fixed order of additions, so the result does not depend on timing.  The partial sums
+// are cleared.
+template <int B>
+__device__ __forceinline__ float wave_sum_tokens(float (&a)[B], int lane) {
+    static_assert(B >= 2 && B <= 4, "two to four tokens");
+    auto dpp = [](float v, auto ctrl) {
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), decltype(ctrl)::value, 0xF, 0xF, false));
+    };
+    using X1 = std::integral_constant<int, 0xB1>;   // quad_perm(1,0,3,2): lane ^ 1
+    using X2 = std::integral_constant<int, 0x4E>;   // quad_perm(2,3,0,1): lane ^ 2
+    using R4 = std::integral_constant<int, 0x124>;  // row_ror:4
+    using R8 = std::integral_constant<int, 0x128>;  // row_ror:8
+    const bool odd = lane & 1;
+    float c;
+    if constexpr (B == 2) {
+        c = (odd ? a[1] : a[0]) + dpp(odd ? a[0] : a[1], X1{});  // even lanes token 0, odd lanes token 1
+        c = c + dpp(c, X2{});
+    } else {
+        float t3 = 0.f;
+        if constexpr (B == 4) t3 = a[B - 1];
+        // even lanes keep tokens 0 and 1, odd lanes 2 and 3
+        const float b0 = (odd ? a[2] : a[0]) + dpp(odd ? a[0] : a[2], X1{});
+        const float b1 = (odd ? t3 : a[1]) + dpp(odd ? a[1] : t3, X1{});
+        const bool hi = lane & 2;  // lanes 2, 3 of a quad keep the second of the two
+        c = (hi ? b1 : b0) + dpp(hi ? b0 : b1, X2{});
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) a[b] = 0.f;
+    c = c + dpp(c, R4{});
+    c = c + dpp(c, R8{});
+    return cross_rows_sum(c);
+}
+
+// Row finished: wave reduction (uniform across the wave), then one lane per token writes
+// the output -- the bf16 row; for the gated MLP h = silu(g) * u once the up row of a
+// pair is done, the gate total kept in gsave until then; for a split launch the row's
+// fp32 partial.  At one token and at 5..8 lane 0 writes every token; at 2..4 tokens the
+// totals come from wave_sum_tokens and lanes 0..B-1 (B = 2) or 0..3 (B = 3-4; lane 3 has
+// no token at B = 3) each write their own token (gsave[0] holds that token's gate total).
 // `split` (0 or 1) and the row parity are integers: a boolean here would be materialised
 // through a vector register, and the reuse of that register can make the wave wait for
 // its in-flight loads.
@@ -270,6 +322,24 @@ __device__ __forceinline__ void finish_row(float (&acc)[B], float (&gsave)[B], c
                                            int s, int R, int lane, float *partial) {
     const int glu = EPI == kEpiSwiGLU ? 1 - split : 0;  // gated MLP without a split
     const int up = row & 1;
+    if constexpr (B >= 2 && B <= 4) {
+        const float tot = wave_sum_tokens<B>(acc, lane);
+        float val = tot;
+        if constexpr (EPI == kEpiSwiGLU) {
+            gsave[0] = up ? gsave[0] : tot;
+            val = glu ? silu_mul(gsave[0], tot) : tot;
+        }
+        const int t = token_of_lane<B>(lane);
+        if ((glu & (up ^ 1)) | (lane >= (B == 2 ? 2 : 4)) | (t >= B)) return;
+        if (split) {
+            partial[((int64_t)s * B + t) * R + row] = val;
+            return;
+        }
+        int p, local;
+        locate<EPI>(set, row, p, local);
+        set.y[p][(int64_t)t * set.ldy[p] + local] = f32_to_bf16_rne(val);
+        return;
+    }
     float val[B];
 #pragma unroll
     for (int b = 0; b < B; ++b) {

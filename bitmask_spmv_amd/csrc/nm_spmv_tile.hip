@@ -158,7 +158,8 @@ __device__ __forceinline__ void load_tbatch(TBatch<TT> &bt, const TileRows<TT> &
 
 // Swap one dword with the neighbouring lane of the pair (lane ^ 1).
 __device__ __forceinline__ uint32_t tpair_swap(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);  // quad_perm(1,0,3,2)
+    // every lane has a source lane: "old" is never read (v itself: no zeroed register)
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xF, 0xF, false);  // quad_perm(1,0,3,2)
 }
 
 // One tile of one step: expand the lane's word into the wave's dense tile, then four MFMAs.
