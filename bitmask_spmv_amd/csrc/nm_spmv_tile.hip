@@ -184,12 +184,14 @@ __device__ __forceinline__ void walk_tile(const u32x4 &va, const u32x4 &vb, uint
     const uint32_t s_z = odd ? va.z : vb.z, s_w = odd ? va.w : vb.w;
     const uint32_t r_x = tpair_swap(s_x), r_y = tpair_swap(s_y), r_z = tpair_swap(s_z), r_w = tpair_swap(s_w);
     // the word's 16 values in walk order: even lanes ascending, odd lanes descending
-    // (dword d of the odd lane = the two values of dword 7 - d, halves swapped)
+    // (dword d of the odd lane = the two values of dword 7 - d, halves swapped); one byte
+    // permute per dword picks the lane's dword and, on odd lanes, swaps its halves
     const uint32_t od[8] = {vb.w, vb.z, vb.y, vb.x, r_w, r_z, r_y, r_x};
     const uint32_t ev[8] = {va.x, va.y, va.z, va.w, r_x, r_y, r_z, r_w};
+    const uint32_t sel = odd ? 0x05040706u : 0x03020100u;  // odd: od[d] halves swapped; even: ev[d]
     uint32_t v[8];
 #pragma unroll
-    for (int d = 0; d < 8; ++d) v[d] = odd ? __builtin_amdgcn_alignbit(od[d], od[d], 16) : ev[d];
+    for (int d = 0; d < 8; ++d) v[d] = __builtin_amdgcn_perm(od[d], ev[d], sel);
     uint32_t m = odd ? __builtin_bitreverse32(mb) : ma;
     m = __builtin_popcount(m) == 16 ? m : 0xFFFFu;
     uint8_t *ub = tw + ((lane & 1) * 8 + (lane >> 3)) * kTRowBytes + 16 + ((lane & 7) >> 1) * 64;
