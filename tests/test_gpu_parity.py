@@ -322,13 +322,16 @@ def test_spmv_integer_exact(N, M):
     assert (bf16_as_f64(host_bf16(y)) == yref).all()
 
 
-def test_spmv_one_hot_reads_columns():
-    say("spmv one-hot")
+# 6 tokens: the matrix-core walk; 2-4 tokens: the word walk, whose row totals of the
+# tokens are reduced together and stored by one lane per token (a token routed to the
+# wrong output row, or a column of another lane's block, shows here exactly).
+@pytest.mark.parametrize("cols", [[0, 1, 31, 32, 2047, 4095], [33, 4095], [0, 2047, 4064], [5, 1000, 31, 4090]])
+def test_spmv_one_hot_reads_columns(cols):
+    say("spmv one-hot", cols)
     R, K = 512, 4096
     W = synth.weights(R, K, 10)
     mref, vref = oracle.prune_pack(W, oracle.col_norm(synth.calib_acts(K, 10)), 2, 4)
     Wp = oracle.unpack(mref, vref, K)
-    cols = [0, 1, 31, 32, 2047, 4095]
     x = np.zeros((len(cols), K), np.uint16)
     for b, j in enumerate(cols):
         x[b, j] = 0x3F80
@@ -337,13 +340,14 @@ def test_spmv_one_hot_reads_columns():
         assert (y[b] == Wp[:, j]).all()
 
 
-def test_spmv_power_of_two_scaling_and_determinism():
-    say("spmv scaling + determinism")
+@pytest.mark.parametrize("B", [1, 2, 4])
+def test_spmv_power_of_two_scaling_and_determinism(B):
+    say("spmv scaling + determinism", B)
     R, K = 2048, 4096
     W = synth.weights(R, K, 11)
     mref, vref = oracle.prune_pack(W, oracle.col_norm(synth.calib_acts(K, 11)), 4, 8)
     m, v = dev_u32(mref), dev_bf16(vref)
-    x = synth.decode_x(1, K, 11)
+    x = synth.decode_x(B, K, 11)
     x4 = synth.to_bf16_bits(synth.bf16_bits_to_f32(x) * 4.0)
     y1 = host_bf16(nm.nm_spmv(m, v, dev_bf16(x)))
     y1b = host_bf16(nm.nm_spmv(m, v, dev_bf16(x)))
